@@ -1,0 +1,138 @@
+"""CPU oracle for the W4A16 matmul (int4 GPTQ-packed weights x bf16 activations).
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT: only ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package. The HIP library never
+imports, links or calls it, and it shares no code with the HIP library.
+
+The arithmetic lives in ``w4a16_oracle.c`` (plain C, fp32 exact dequantisation, fp64
+accumulation); this module only builds that file with gcc and marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w4a16_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libw4a16_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP over output columns)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.w4o_fp16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.w4o_fp16_to_f32.restype = ctypes.c_float
+        lib.w4o_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.w4o_bf16_to_f32.restype = ctypes.c_float
+        lib.w4o_unpack_qweight.argtypes = [P, I64, I64, P]
+        lib.w4o_unpack_qzeros.argtypes = [P, I64, I64, P]
+        lib.w4o_dequant.argtypes = [P, P, P, I64, I64, I64, P]
+        lib.w4o_gemm.argtypes = [P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
+        lib.w4o_argmax_rows_f32.argtypes = [P, I64, I64, P]
+        for f in (lib.w4o_unpack_qweight, lib.w4o_unpack_qzeros, lib.w4o_dequant,
+                  lib.w4o_gemm, lib.w4o_argmax_rows_f32):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (status {rc})")
+
+
+def fp16_to_f32(bits: int) -> float:
+    return _load().w4o_fp16_to_f32(int(bits))
+
+
+def bf16_to_f32(bits: int) -> float:
+    return _load().w4o_bf16_to_f32(int(bits))
+
+
+def unpack_qweight(qweight: np.ndarray) -> np.ndarray:
+    """Codes [K, N] (uint8) from qweight [K/8, N]."""
+    qw = _c(qweight, np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    q = np.empty((K, N), dtype=np.uint8)
+    _check(_load().w4o_unpack_qweight(_ptr(qw), K, N, _ptr(q)), "unpack_qweight")
+    return q
+
+
+def unpack_qzeros(qzeros: Optional[np.ndarray], groups: int, N: int) -> np.ndarray:
+    """Zeros [G, N] (uint8) from qzeros [G, N/8]; all 8 when qzeros is None."""
+    qz = _c(qzeros, np.uint32)
+    if qz is not None:
+        assert qz.shape == (groups, N // 8)
+    z = np.empty((groups, N), dtype=np.uint8)
+    _check(_load().w4o_unpack_qzeros(_ptr(qz), groups, N, _ptr(z)), "unpack_qzeros")
+    return z
+
+
+def dequant(qweight, scales, qzeros, group: int) -> np.ndarray:
+    """Dequantised weights [K, N] in fp32."""
+    qw = _c(qweight, np.uint32)
+    sc = _c(scales, np.uint16)
+    qz = _c(qzeros, np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    w = np.empty((K, N), dtype=np.float32)
+    _check(_load().w4o_dequant(_ptr(qw), _ptr(sc), _ptr(qz), group, K, N, _ptr(w)), "dequant")
+    return w
+
+
+def gemm(act, qweight, scales, qzeros, group: int, cols: Optional[Sequence[int]] = None,
+         with_bound: bool = True):
+    """y (fp64 [M, C]) and bound (fp64 [M, C]) for columns ``cols`` (all when None).
+
+    ``act`` is bf16 bits [M, K] (uint16)."""
+    a = _c(act, np.uint16)
+    qw = _c(qweight, np.uint32)
+    sc = _c(scales, np.uint16)
+    qz = _c(qzeros, np.uint32)
+    M, K = a.shape
+    N = qw.shape[1]
+    assert qw.shape[0] * 8 == K
+    cc = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    C = N if cc is None else cc.shape[0]
+    y = np.empty((M, C), dtype=np.float64)
+    b = np.empty((M, C), dtype=np.float64) if with_bound else None
+    _check(_load().w4o_gemm(_ptr(a), _ptr(qw), _ptr(sc), _ptr(qz), group, M, N, K,
+                            _ptr(cc), C, _ptr(y), _ptr(b)), "gemm")
+    return (y, b) if with_bound else y
+
+
+def argmax_rows_f32(v: np.ndarray) -> np.ndarray:
+    """Per-row argmax (ties -> lowest index) of fp32 values [M, N]."""
+    x = _c(v, np.float32)
+    M, N = x.shape
+    idx = np.empty(M, dtype=np.int64)
+    _check(_load().w4o_argmax_rows_f32(_ptr(x), M, N, _ptr(idx)), "argmax")
+    return idx
+
