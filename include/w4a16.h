@@ -1,0 +1,119 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so: group-quantised int4-weight x bf16-activation matmul for
+ * LLM decode on AMD Instinct MI355X (gfx950).
+ *
+ *   out[M, N] = A[M, K] x W[K, N],   W[k][n] = (q[k][n] - z[k/g][n]) * scale[k/g][n]
+ *
+ * The operation is the int4 path of the GRIMOIRE v1.7 release notes ('What changed'): int4
+ * weights and bf16 activations, an exact (q - z) * scale dequantisation, one kernel for a
+ * single decoding row (M = 1) and a matrix-core kernel for the 2-16 rows that several users
+ * or a speculative verify pass produce. GRIMOIRE v1.8 ('What changed') checks its 1 + 4
+ * drafted MTP rows through that small-M path and scores the output layer in one pass; the
+ * 248k-row output layer of strix-llama.cpp PR #105 is such a call. lucebox PR #823 moves the
+ * greedy pick over a vocabulary row onto the GPU (w4a16_argmax_rows).
+ *
+ * Storage (the GPTQ convention):
+ *   qweight  uint32 [K/8, N]    nibble j (bits 4j..4j+3) of word [i][n] is the code of row 8i+j
+ *   scales   fp16   [K/g, N]    IEEE binary16 bit patterns
+ *   qzeros   uint32 [K/g, N/8]  nibble j of word [gi][c] is the zero point of column 8c+j, used
+ *                               as stored (no +1 offset); NULL means every zero point is 8
+ *   A        bf16   [M, K]      row-major
+ *   out      fp32 or bf16 [M, N] row-major, fully overwritten
+ * All tensors are dense with the row strides implied by their shapes.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers (memory the caller owns; the library never frees or keeps
+ *     them). Calls are asynchronous on `stream` (0 = the null stream); results are valid once
+ *     the stream has reached the call. Inputs and outputs must not overlap.
+ *   - Arguments are checked on the host before any device work; a non-OK status means no
+ *     device work was enqueued. The library never aborts and never prints: w4a16_last_error()
+ *     returns a description of the last non-OK status of the calling thread.
+ *   - The library owns one scratch buffer per (device, stream) for split-K partial sums and
+ *     completion counters. It is allocated on the first call that needs it on that stream
+ *     (and grown if a later call needs more), so warm a stream up before timing or capturing
+ *     it. Calls on different streams never share scratch; calls on one stream are ordered.
+ *   - Results are deterministic: the same inputs and launch give bit-identical outputs (the
+ *     split-K partials are summed in a fixed order, never with float atomics).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = -1,   /* null pointer, size or divisibility violation, bad dtype */
+    W4A16_ERR_UNSUPPORTED = -2,   /* pointer not 16-byte aligned */
+    W4A16_ERR_HIP = -3,           /* a HIP runtime call failed; see w4a16_last_error() */
+    W4A16_ERR_NO_MEMORY = -4      /* the scratch buffer could not be allocated */
+} w4a16_status;
+
+typedef enum { W4A16_OUT_F32 = 0, W4A16_OUT_BF16 = 1 } w4a16_out_dtype;
+
+/*
+ * out = A x dequant(qweight, scales, qzeros).
+ *   A         bf16 [M, K], 16-byte aligned
+ *   qweight   uint32 [K/8, N], 16-byte aligned
+ *   scales    fp16 bits [K/g, N], 16-byte aligned
+ *   qzeros    uint32 [K/g, N/8], 16-byte aligned, or NULL for the symmetric zero point 8
+ *   group_size g: a positive multiple of 32 that divides K
+ *   M in 1..16; N > 0 and a multiple of 8; K > 0 and a multiple of g
+ *   out       [M, N] fp32 (out_dtype W4A16_OUT_F32) or bf16 (W4A16_OUT_BF16, round to
+ *             nearest even), 16-byte aligned
+ * M = 1 runs the single-row GEMV; M = 2..16 run the matrix-core GEMM. Accuracy: every output
+ * is within 4e-3 * sum_k |a_k * w_kn| + 1e-6 of the exact value for finite inputs whose
+ * nonzero activations within one row span less than 2^30 in magnitude (activations enter the
+ * fp16 matrix cores through an exact power-of-two rescale per row and K-slice).
+ */
+int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales,
+               const uint32_t *qzeros, int group_size, int M, int N, int K,
+               void *out, int out_dtype, hipStream_t stream);
+
+/*
+ * Same as w4a16_gemm with an explicit split-K factor: `splits` K-slices (1..K/32) whose fp32
+ * partial sums are added in slice order; 0 picks the factor w4a16_gemm uses. Every factor
+ * meets the same accuracy contract; different factors round differently. Meant for tests and
+ * tuning sweeps.
+ */
+int w4a16_gemm_splits(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                      const uint32_t *qzeros, int group_size, int M, int N, int K,
+                      void *out, int out_dtype, int splits, hipStream_t stream);
+
+/* The split-K factor w4a16_gemm picks for a shape (>= 1), or a negative status. */
+int w4a16_default_splits(int M, int N, int K, int group_size);
+
+/*
+ * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32
+ * comparison, -0 == +0, NaN entries ignored; an all-NaN row gives 0).
+ *   logits fp32 [M, N] device, 16-byte aligned; M in 1..65535; N in 1..2^31-1
+ *   idx    int32 [M] device
+ */
+int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream_t stream);
+
+/*
+ * Test hooks running the kernels' own unpack/dequant device code.
+ * w4a16_unpack_u8: q_out[k][n] (uint8 [K, N]) = code of row k, column n. K % 8 == 0, N % 4 == 0.
+ * w4a16_dequant_f32: w_out[k][n] (fp32 [K, N]) = (q - z) * scale, exact. Same size rules as
+ * w4a16_gemm for group_size, K and N. All pointers 16-byte aligned.
+ */
+int w4a16_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q_out, hipStream_t stream);
+int w4a16_dequant_f32(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                      int group_size, int K, int N, float *w_out, hipStream_t stream);
+
+/* Release every scratch buffer the library holds (all devices, all streams). The caller
+ * must ensure no library work is still running. Returns W4A16_OK or W4A16_ERR_HIP. */
+int w4a16_release_scratch(void);
+
+const char *w4a16_status_string(int status);
+const char *w4a16_last_error(void);
+int w4a16_version(void);   /* 100 * major + minor */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

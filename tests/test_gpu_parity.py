@@ -1,0 +1,174 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Bar (floating-point outputs): |y_gpu - y_oracle| <= 4e-3 * sum_k |a_k w_kn| + 1e-6 on every
+output (tests/parity.py). Integer stages (unpack, dequantisation, argmax) are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import verify_matmul_amd as vm
+from tests import parity
+from tests.golden import hand
+from verify_matmul_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gu():
+    from tests import gpu_util
+    vm.load()
+    return gpu_util
+
+
+# ---- stage checks: the kernels' own unpack and dequantisation, bit-exact ------------------
+
+@pytest.mark.parametrize("name", ["tiny", "attn", "ffn_up", "ffn_down", "lm_head"])
+def test_unpack_and_dequant_bit_exact(gu, name):
+    wl = synth.WORKLOADS[name]
+    gu.say(f"[dequant] {name}")
+    inp = synth.make_inputs(wl, N=min(wl.N, 8192))   # the stage is per column: a slice suffices
+    d = gu.DevInputs(inp)
+    q = torch.empty((inp.K, inp.N), dtype=torch.uint8, device=gu.DEV)
+    vm.w4a16_unpack_u8(d.qweight, q)
+    w = torch.empty((inp.K, inp.N), dtype=torch.float32, device=gu.DEV)
+    vm.w4a16_dequant_f32(d.qweight, d.scales, d.qzeros, inp.group, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), oracle.unpack_qweight(inp.qweight))
+    w_ref = oracle.dequant(inp.qweight, inp.scales, inp.qzeros, inp.group)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+
+
+def test_dequant_all_codes_zeros_scales(gu):
+    """Every (q, z) pair against every finite fp16 scale, through the device dequantiser."""
+    fin = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = fin[np.isfinite(fin.view(np.float16))]
+    N = 63488
+    g = 32
+    K = 16 * g * 2     # 32 groups: zero gi % 16, codes cycle 0..15 down the rows
+    qweight = np.empty((K // 8, N), dtype=np.uint32)
+    qweight[0::2] = 0x76543210
+    qweight[1::2] = 0xFEDCBA98
+    scales = np.broadcast_to(fin[:N], (K // g, N)).copy()
+    qzeros = np.repeat(((np.arange(K // g, dtype=np.uint32) % 16) * 0x11111111)[:, None], N // 8, axis=1)
+    w = torch.empty((K, N), dtype=torch.float32, device=gu.DEV)
+    vm.w4a16_dequant_f32(gu.dev_u32(qweight), gu.dev_u16(scales), gu.dev_u32(qzeros), g, w)
+    torch.cuda.synchronize()
+    w_ref = oracle.dequant(qweight, scales, qzeros, g)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+
+
+# ---- hand-derived examples ---------------------------------------------------------------
+
+def test_hand_examples(gu):
+    for c in hand.cases():
+        inp = synth.Inputs(c["qweight"], c["scales"], c["qzeros"], c["act"], c["group"])
+        y = gu.DevInputs(inp).run(c["M"])
+        assert np.array_equal(y, c["y"]), c["name"]
+
+
+# ---- sweeps over shapes, rows, zero points and split-K factors -----------------------------
+
+SHAPES = [   # (K, N, group, symmetric): several tiles, ragged column tails, uneven slices
+    (512, 256, 128, True),
+    (768, 264, 64, False),
+    (1024, 1000, 128, True),
+    (1088, 520, 32, False),
+    (2048, 8, 64, True),
+    (4096, 776, 4096, False),
+]
+
+
+def lds_fits(M, K, splits):
+    # the activations of one K-slice must fit the LDS a workgroup may stage (64 KiB - 256)
+    max_steps = -(-(K // 32) // splits)
+    return 64 + max_steps * 4 * M * 16 <= 65536 - 256
+
+
+@pytest.mark.parametrize("K,N,g,sym", SHAPES)
+def test_parity_sweep_rows_and_splits(gu, K, N, g, sym):
+    inp = synth.make_random(K * 7 + N, 16, K, N, g, sym)
+    d = gu.DevInputs(inp)
+    steps = K // 32
+    for M in range(1, 17):
+        y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
+        for splits in sorted({0, 1, 2, 3, min(7, steps), steps}):
+            if splits and not lds_fits(M, K, splits):
+                with pytest.raises(vm.W4A16Error):
+                    d.run(M, splits=splits)
+                continue
+            gu.say(f"[sweep] K={K} N={N} g={g} sym={sym} M={M} splits={splits}")
+            y = d.run(M, splits=splits)
+            parity.check_close(y, y_ref, bound, f"K={K} N={N} g={g} M={M} splits={splits}")
+
+
+# ---- the workloads at full size, in the default launch configuration --------------------------
+
+_WL_CASES = [("tiny", 1), ("attn", 1)] + [("ffn_up", m) for m in (1, 2, 4, 8, 16)] + \
+            [("ffn_down", m) for m in (1, 4, 8, 16)]
+
+
+@pytest.fixture(scope="module")
+def wl_cache():
+    return {}
+
+
+def _wl(gu, cache, name):
+    if name not in cache:
+        cache.clear()   # keep one workload resident at a time
+        inp = synth.make_inputs(name)
+        cache[name] = (inp, gu.DevInputs(inp))
+    return cache[name]
+
+
+@pytest.mark.parametrize("name,M", _WL_CASES)
+def test_parity_workloads(gu, wl_cache, name, M):
+    inp, d = _wl(gu, wl_cache, name)
+    gu.say(f"[workload] {name} M={M} K={inp.K} N={inp.N} g={inp.group} splits="
+           f"{vm.w4a16_default_splits(M, inp.N, inp.K, inp.group)}")
+    y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)
+    y = d.run(M)
+    frac = parity.check_close(y, y_ref, bound, f"{name} M={M} fp32")
+    gu.say(f"  fp32 worst err/tol {frac:.3e}")
+    if name in ("attn", "tiny") or M in (1, 16):
+        yb = d.run(M, out_dtype=torch.bfloat16)
+        frac = parity.check_close(yb, y_ref, bound, f"{name} M={M} bf16")
+        gu.say(f"  bf16 worst err/tol {frac:.3e}")
+        # bf16 output is the fp32 output rounded once
+        assert np.array_equal(yb, torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).double().numpy())
+
+
+@pytest.mark.parametrize("M", [5, 1])
+def test_parity_lm_head_and_argmax(gu, wl_cache, M):
+    inp, d = _wl(gu, wl_cache, "lm_head")
+    gu.say(f"[lm_head] M={M} N={inp.N}")
+    a = d.act[:M]
+    logits = torch.empty((M, inp.N), dtype=torch.float32, device=gu.DEV)
+    vm.w4a16_gemm(a, d.qweight, d.scales, None, inp.group, logits)
+    idx = torch.empty((M,), dtype=torch.int32, device=gu.DEV)
+    vm.w4a16_argmax_rows(logits, idx)
+    torch.cuda.synchronize()
+    y = logits.cpu().numpy()
+    got = idx.cpu().numpy().astype(np.int64)
+    # the argmax step itself: bit-exact against a host argmax of the same fp32 logits
+    assert np.array_equal(got, oracle.argmax_rows_f32(y))
+    y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, None, inp.group)
+    frac = parity.check_close(y.astype(np.float64), y_ref, bound, f"lm_head M={M}")
+    gu.say(f"  worst err/tol {frac:.3e}")
+    # end to end: the oracle's choice, decided in fp32 like the kernel's
+    # The pick must equal the oracle's whenever the oracle's top-2 gap exceeds what the GPU's
+    # measured error on that row (plus the fp32 rounding of both sides) could reorder.
+    ref_idx = oracle.argmax_rows_f32(y_ref.astype(np.float32))
+    for m in range(M):
+        top2 = np.sort(y_ref[m])[-2:]
+        gap = top2[1] - top2[0]
+        err = float(np.max(np.abs(y[m].astype(np.float64) - y_ref[m])))
+        slack = 2 * err + 4 * np.spacing(np.float32(abs(top2[1])))
+        gu.say(f"  row {m}: argmax {got[m]} (oracle {ref_idx[m]}), top-2 gap {gap:.4f}, "
+               f"max row error {err:.2e}")
+        if gap > slack:
+            assert got[m] == ref_idx[m], (m, got[m], ref_idx[m], gap, err)
+        else:   # near-tie: the pick must be a column whose exact value is within reach of the max
+            assert y_ref[m, got[m]] >= top2[1] - slack

@@ -1,0 +1,106 @@
+"""The HIP library builds, loads, exports every declared symbol, and rejects bad arguments on
+the host before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import verify_matmul_amd as vm
+    if not os.path.exists(vm.lib_path):
+        from verify_matmul_amd import _build
+        _build.build()
+    return vm.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("w4a16_gemm", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    import verify_matmul_amd as vm
+    names = declared_functions()
+    assert sorted(vm.EXPORTS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", vm.lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(w4a16_\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+A = 0x10000   # fake, 16-byte-aligned device addresses: the checks below fail before any use
+Q = 0x20000
+S = 0x30000
+Z = 0x40000
+O = 0x50000
+
+
+def gemm(lib, a=A, q=Q, s=S, z=None, g=128, M=1, N=256, K=512, o=O, dt=0):
+    return lib.w4a16_gemm(a, q, s, z, g, M, N, K, o, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=None), -1), (dict(q=None), -1), (dict(s=None), -1), (dict(o=None), -1),
+    (dict(M=0), -1), (dict(M=17), -1), (dict(N=0), -1), (dict(K=0), -1), (dict(g=0), -1),
+    (dict(N=-8), -1), (dict(g=48), -1), (dict(g=96), -1), (dict(K=520, g=32), -1),
+    (dict(N=260), -1), (dict(a=A + 2), -2), (dict(q=Q + 4), -2), (dict(s=S + 8), -2),
+    (dict(z=Z + 4), -2), (dict(o=O + 8), -2), (dict(dt=2), -1), (dict(dt=-1), -1),
+])
+def test_gemm_rejects_bad_arguments(lib, kw, status):
+    assert gemm(lib, **kw) == status
+    assert lib.w4a16_last_error().decode()
+
+
+def test_validation_order_is_fixed(lib):
+    # null pointer is reported before a bad M, bad M before a bad group, group before alignment
+    assert gemm(lib, a=None, M=0) == -1 and b"null" in lib.w4a16_last_error()
+    assert gemm(lib, M=0, g=48) == -1 and b"M=0" in lib.w4a16_last_error()
+    assert gemm(lib, g=48, a=A + 2) == -1 and b"multiple of 32" in lib.w4a16_last_error()
+
+
+def test_explicit_splits_are_checked(lib):
+    # K=512 has 16 steps of 32
+    assert lib.w4a16_gemm_splits(A, Q, S, None, 128, 1, 256, 512, O, 0, 17, None) == -1
+    assert lib.w4a16_gemm_splits(A, Q, S, None, 128, 1, 256, 512, O, 0, -1, None) == -1
+
+
+def test_default_splits_host_only(lib):
+    for M in (1, 2, 4, 8, 16):
+        s = lib.w4a16_default_splits(M, 17408, 5120, 128)
+        assert 1 <= s <= 5120 // 32
+    assert lib.w4a16_default_splits(1, 248320, 5120, 128) >= 1
+    assert lib.w4a16_default_splits(16, 5120, 17408, 64) >= 1
+    assert lib.w4a16_default_splits(0, 256, 512, 128) == -1
+
+
+def test_aux_entry_points_reject_bad_arguments(lib):
+    assert lib.w4a16_argmax_rows(None, 1, 10, O, None) == -1
+    assert lib.w4a16_argmax_rows(A, 0, 10, O, None) == -1
+    assert lib.w4a16_argmax_rows(A, 1, 0, O, None) == -1
+    assert lib.w4a16_argmax_rows(A + 4, 1, 10, O, None) == -2
+    assert lib.w4a16_unpack_u8(Q, 12, 8, O, None) == -1
+    assert lib.w4a16_unpack_u8(Q, 16, 6, O, None) == -1
+    assert lib.w4a16_dequant_f32(Q, S, None, 64, 96, 8, O, None) == -1
+    assert lib.w4a16_dequant_f32(Q, S, None, 32, 64, 12, O, None) == -1
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, 7):
+        assert lib.w4a16_status_string(st)
+    assert lib.w4a16_version() >= 100

@@ -1,0 +1,171 @@
+"""Python binding of libw4a16.so: group-quantised int4 x bf16 matmul on AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP library. PyTorch
+provides the device buffers and the stream; tensors are passed by pointer to the C ABI in
+``include/w4a16.h``. There is no CPU fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_splits", "w4a16_default_splits",
+    "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
+    "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libw4a16.so")
+_lib = None
+
+# every symbol the header declares
+EXPORTS = (
+    "w4a16_gemm", "w4a16_gemm_splits", "w4a16_default_splits", "w4a16_argmax_rows",
+    "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_last_error", "w4a16_version",
+)
+
+OUT_F32 = 0
+OUT_BF16 = 1
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+def load():
+    """Load libw4a16.so (built in-tree by ``__graft_entry__.build()``); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with __graft_entry__.build() "
+                          f"(hipcc --offload-arch=gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(lib_path)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_splits.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P]
+    lib.w4a16_default_splits.argtypes = [I, I, I, I]
+    lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
+    lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
+    lib.w4a16_dequant_f32.argtypes = [P, P, P, I, I, I, P, P]
+    lib.w4a16_release_scratch.argtypes = []
+    lib.w4a16_status_string.argtypes = [I]
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    lib.w4a16_last_error.argtypes = []
+    lib.w4a16_last_error.restype = ctypes.c_char_p
+    lib.w4a16_version.argtypes = []
+    for f in ("w4a16_gemm", "w4a16_gemm_splits", "w4a16_default_splits", "w4a16_argmax_rows",
+              "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, where: str):
+    if rc < 0:
+        lib = load()
+        raise W4A16Error(rc, where, f"{lib.w4a16_status_string(rc).decode()}: "
+                                    f"{lib.w4a16_last_error().decode()}")
+    return rc
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_I32 = (torch.int32, torch.uint32)
+_I16 = (torch.float16, torch.int16, torch.uint16)
+
+
+def _gemm_args(A, qweight, scales, qzeros, group_size, out):
+    M, K = A.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != K:
+        raise ValueError(f"qweight {tuple(qweight.shape)} does not match K={K}")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out {tuple(out.shape)} is not [{M}, {N}]")
+    if tuple(scales.shape) != (K // group_size, N):
+        raise ValueError(f"scales {tuple(scales.shape)} is not [{K // group_size}, {N}]")
+    if qzeros is not None and tuple(qzeros.shape) != (K // group_size, N // 8):
+        raise ValueError(f"qzeros {tuple(qzeros.shape)} is not [{K // group_size}, {N // 8}]")
+    dt = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}.get(out.dtype)
+    if dt is None:
+        raise TypeError("out must be float32 or bfloat16")
+    return (_ptr(A, "A", (torch.bfloat16, torch.int16, torch.uint16)), _ptr(qweight, "qweight", _I32),
+            _ptr(scales, "scales", _I16), _ptr(qzeros, "qzeros", _I32), int(group_size), M, N, K,
+            _ptr(out, "out", (torch.float32, torch.bfloat16)), dt)
+
+
+def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
+    """out[M,N] = A[M,K] (bf16) x dequant(qweight, scales, qzeros); qzeros None = symmetric 8."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    _check(load().w4a16_gemm(*args, _stream(stream)), "w4a16_gemm")
+    return out
+
+
+def w4a16_gemm_splits(A, qweight, scales, qzeros, group_size, out, splits, stream=None):
+    """w4a16_gemm with an explicit split-K factor (0 = the default choice)."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    _check(load().w4a16_gemm_splits(*args, int(splits), _stream(stream)), "w4a16_gemm_splits")
+    return out
+
+
+def w4a16_default_splits(M, N, K, group_size) -> int:
+    return _check(load().w4a16_default_splits(int(M), int(N), int(K), int(group_size)),
+                  "w4a16_default_splits")
+
+
+def w4a16_argmax_rows(logits, idx, stream=None):
+    M, N = logits.shape
+    if tuple(idx.shape) != (M,):
+        raise ValueError("idx must be [M]")
+    _check(load().w4a16_argmax_rows(_ptr(logits, "logits", (torch.float32,)), M, N,
+                                    _ptr(idx, "idx", (torch.int32,)), _stream(stream)),
+           "w4a16_argmax_rows")
+    return idx
+
+
+def w4a16_unpack_u8(qweight, q_out, stream=None):
+    K, N = qweight.shape[0] * 8, qweight.shape[1]
+    if tuple(q_out.shape) != (K, N):
+        raise ValueError("q_out must be [K, N]")
+    _check(load().w4a16_unpack_u8(_ptr(qweight, "qweight", _I32), K, N,
+                                  _ptr(q_out, "q_out", (torch.uint8,)), _stream(stream)),
+           "w4a16_unpack_u8")
+    return q_out
+
+
+def w4a16_dequant_f32(qweight, scales, qzeros, group_size, w_out, stream=None):
+    K, N = qweight.shape[0] * 8, qweight.shape[1]
+    if tuple(w_out.shape) != (K, N):
+        raise ValueError("w_out must be [K, N]")
+    _check(load().w4a16_dequant_f32(_ptr(qweight, "qweight", _I32), _ptr(scales, "scales", _I16),
+                                    _ptr(qzeros, "qzeros", _I32), int(group_size), K, N,
+                                    _ptr(w_out, "w_out", (torch.float32,)), _stream(stream)),
+           "w4a16_dequant_f32")
+    return w_out
+
+
+def w4a16_release_scratch():
+    _check(load().w4a16_release_scratch(), "w4a16_release_scratch")

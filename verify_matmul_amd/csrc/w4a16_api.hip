@@ -1,0 +1,276 @@
+// C ABI of libw4a16.so: argument checks, kernel choice, split-K factor and per-stream scratch.
+// The declarations and the contract live in include/w4a16.h.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+#include <utility>
+
+#include "../../include/w4a16.h"
+#include "w4a16_launch.h"
+
+using namespace w4a16;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(W4A16_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- per-(device, stream) scratch -------------------------------------------------------------
+// Layout of one scratch block: [counters: uint32 x n_counters][pad to 256][partials: float ...].
+// Counters are zeroed once at allocation; every kernel that uses one leaves it at zero again.
+struct Scratch {
+    void *base = nullptr;
+    size_t counter_bytes = 0;
+    size_t partial_bytes = 0;
+};
+
+struct Key {
+    int device;
+    hipStream_t stream;
+    bool operator<(const Key &o) const
+    {
+        return device != o.device ? device < o.device : (uintptr_t)stream < (uintptr_t)o.stream;
+    }
+};
+
+std::mutex g_scratch_mu;
+std::map<Key, Scratch> g_scratch;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Returns W4A16_OK and fills counters/partials with pointers into a block of at least the
+// requested sizes, allocating or growing the stream's block when needed.
+int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, uint32_t **counters,
+                float **partials)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    Scratch &s = g_scratch[Key{dev, stream}];
+    if (s.base == nullptr || s.counter_bytes < counter_bytes || s.partial_bytes < partial_bytes) {
+        const size_t cb = round_up(std::max(counter_bytes, std::max(s.counter_bytes, (size_t)4096)), 256);
+        const size_t pb = round_up(std::max(partial_bytes, s.partial_bytes), 256);
+        if (s.base) {
+            // the old block may still be in use by earlier work on this stream
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            e = hipFree(s.base);
+            s.base = nullptr;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        void *p = nullptr;
+        e = hipMalloc(&p, cb + pb);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", cb + pb, hipGetErrorString(e));
+        }
+        e = hipMemsetAsync(p, 0, cb, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "hipMemsetAsync");
+        }
+        s.base = p;
+        s.counter_bytes = cb;
+        s.partial_bytes = pb;
+    }
+    *counters = static_cast<uint32_t *>(s.base);
+    *partials = reinterpret_cast<float *>(static_cast<char *>(s.base) + s.counter_bytes);
+    return W4A16_OK;
+}
+
+// Split-K factor: enough workgroups to keep every CU streaming, while keeping the fp32
+// partials (splits x M x N x 4 bytes, written and read once) small against the weights.
+int pick_splits(int M, int N, int K)
+{
+    const int steps = K / kStepK;
+    const int tiles = (N + kTileN - 1) / kTileN;
+    // activations of one slice must fit the LDS budget
+    int s = 1;
+    while (s < steps && gemm_lds_bytes(M, K, s) > (size_t)kMaxLds) ++s;
+    // aim for about 1024 workgroups (4 per CU on 256 CUs)
+    int want = (1024 + tiles - 1) / tiles;
+    // partial traffic 8*splits*M*N bytes against K*N/2 bytes of weights: keep under ~1/8
+    int cap = (K / 2) / (8 * 8 * M);
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want > s) s = want;
+    if (s > steps) s = steps;
+    if (s > 65535) s = 65535;
+    return s;
+}
+
+int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                    int g, int M, int N, int K, void *out, int out_dtype)
+{
+    if (!A || !qweight || !scales || !out)
+        return fail(W4A16_ERR_INVALID_ARG, "null pointer (A=%p qweight=%p scales=%p out=%p)", A,
+                    (const void *)qweight, (const void *)scales, out);
+    if (M < 1 || M > 16) return fail(W4A16_ERR_INVALID_ARG, "M=%d outside 1..16", M);
+    if (N <= 0 || K <= 0 || g <= 0)
+        return fail(W4A16_ERR_INVALID_ARG, "sizes must be positive (N=%d K=%d group_size=%d)", N, K, g);
+    if (g % 32) return fail(W4A16_ERR_INVALID_ARG, "group_size=%d is not a multiple of 32", g);
+    if (K % g) return fail(W4A16_ERR_INVALID_ARG, "K=%d is not a multiple of group_size=%d", K, g);
+    if (N % 8) return fail(W4A16_ERR_INVALID_ARG, "N=%d is not a multiple of 8", N);
+    if (!aligned16(A) || !aligned16(qweight) || !aligned16(scales) || (qzeros && !aligned16(qzeros)) ||
+        !aligned16(out))
+        return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
+    if (out_dtype != W4A16_OUT_F32 && out_dtype != W4A16_OUT_BF16)
+        return fail(W4A16_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_splits(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                      int group_size, int M, int N, int K, void *out, int out_dtype, int splits,
+                      hipStream_t stream)
+{
+    int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
+    if (rc != W4A16_OK) return rc;
+    const int steps = K / kStepK;
+    if (splits < 0 || splits > steps || splits > 65535)
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d outside 0..%d", splits, steps < 65535 ? steps : 65535);
+    if (splits == 0) splits = pick_splits(M, N, K);
+    if (gemm_lds_bytes(M, K, splits) > (size_t)kMaxLds)
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d leaves %zu bytes of activations per workgroup (max %d)",
+                    splits, gemm_lds_bytes(M, K, splits), kMaxLds);
+
+    GemmArgs a{};
+    a.A = static_cast<const uint16_t *>(A);
+    a.qweight = qweight;
+    a.scales = scales;
+    a.qzeros = qzeros;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.g = group_size;
+    a.splits = splits;
+    a.out_bf16 = out_dtype == W4A16_OUT_BF16;
+    if (splits > 1) {
+        const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
+        rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)splits * M * N * sizeof(float), &a.counters,
+                         &a.partials);
+        if (rc != W4A16_OK) return rc;
+    }
+    const hipError_t e = launch_gemm(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "GEMM launch");
+    return W4A16_OK;
+}
+
+int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+               int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
+{
+    return w4a16_gemm_splits(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, stream);
+}
+
+int w4a16_default_splits(int M, int N, int K, int group_size)
+{
+    if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
+        return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
+    return pick_splits(M, N, K);
+}
+
+int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream_t stream)
+{
+    if (!logits || !idx) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (M < 1 || M > 65535 || N < 1) return fail(W4A16_ERR_INVALID_ARG, "M=%d or N=%d out of range", M, N);
+    if (!aligned16(logits)) return fail(W4A16_ERR_UNSUPPORTED, "logits must be 16-byte aligned");
+    ArgmaxArgs a{};
+    a.logits = logits;
+    a.idx = idx;
+    a.M = M;
+    a.N = N;
+    a.chunks = (int)(((long long)N + kArgmaxChunk - 1) / kArgmaxChunk);
+    uint32_t *ctr = nullptr;
+    float *part = nullptr;
+    // counters: M uint32 counters followed by M 64-bit keys, all zero between calls
+    const size_t need = round_up((size_t)M * 4, 8) + (size_t)M * 8;
+    int rc = get_scratch(stream, need, 0, &ctr, &part);
+    if (rc != W4A16_OK) return rc;
+    a.counters = ctr;
+    a.keys = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ctr) + round_up((size_t)M * 4, 8));
+    const hipError_t e = launch_argmax(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "argmax launch");
+    return W4A16_OK;
+}
+
+int w4a16_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q_out, hipStream_t stream)
+{
+    if (!qweight || !q_out) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (K <= 0 || N <= 0 || K % 8 || N % 4) return fail(W4A16_ERR_INVALID_ARG, "K=%d N=%d", K, N);
+    if (!aligned16(qweight) || !aligned16(q_out)) return fail(W4A16_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    const hipError_t e = launch_unpack_u8(qweight, K, N, q_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "unpack launch");
+    return W4A16_OK;
+}
+
+int w4a16_dequant_f32(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros, int group_size,
+                      int K, int N, float *w_out, hipStream_t stream)
+{
+    if (!qweight || !scales || !w_out) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (K <= 0 || N <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
+        return fail(W4A16_ERR_INVALID_ARG, "K=%d N=%d group_size=%d", K, N, group_size);
+    if (!aligned16(qweight) || !aligned16(scales) || (qzeros && !aligned16(qzeros)) || !aligned16(w_out))
+        return fail(W4A16_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    const hipError_t e = launch_dequant_f32(qweight, scales, qzeros, group_size, K, N, w_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    return W4A16_OK;
+}
+
+int w4a16_release_scratch(void)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    int rc = W4A16_OK;
+    for (auto &kv : g_scratch) {
+        if (!kv.second.base) continue;
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(kv.first.device);
+        const hipError_t e = hipFree(kv.second.base);
+        (void)hipSetDevice(cur);
+        if (e != hipSuccess) rc = hip_fail(e, "hipFree");
+    }
+    g_scratch.clear();
+    return rc;
+}
+
+const char *w4a16_status_string(int status)
+{
+    switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported (alignment)";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    case W4A16_ERR_NO_MEMORY: return "out of device memory";
+    default: return "unknown status";
+    }
+}
+
+const char *w4a16_last_error(void) { return g_last_error; }
+
+int w4a16_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Per-row greedy argmax over fp32 logits, and the unpack/dequant test hooks (gfx950).
+#include "w4a16_device.h"
+#include "w4a16_launch.h"
+
+namespace w4a16 {
+namespace {
+
+// Greedy selection on the device, as lucebox PR #823 (PR description) does to avoid reading a
+// whole vocabulary row back to the host. A (value, index) pair is packed into one 64-bit key
+// whose unsigned order is "larger value first, then smaller index": the high word is the fp32
+// bit pattern mapped to an unsigned total order (-0 folded onto +0), the low word is
+// 0xFFFFFFFF - index. The maximum key over a row is therefore unique and independent of the
+// order in which workgroups combine it, so the result is deterministic.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t n)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if ((u & 0x7FFFFFFFu) == 0) u = 0;                       // -0 == +0
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - n);
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
+{
+    const uint32_t lo = __shfl_xor((uint32_t)v, m);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+constexpr int kArgmaxThreads = 256;
+
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_rows_kernel(ArgmaxArgs p)
+{
+    __shared__ unsigned long long s_key[kArgmaxThreads / 64];
+    __shared__ int s_last;
+    const int m = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const float *row = p.logits + (size_t)m * p.N;
+    const long long begin = (long long)chunk * kArgmaxChunk;
+    const long long end = min((long long)p.N, begin + kArgmaxChunk);
+
+    unsigned long long best = 0;   // 0 = nothing seen (every real key has a nonzero high word)
+    for (long long n = begin + threadIdx.x; n < end; n += kArgmaxThreads) {
+        const float v = row[n];
+        if (v != v) continue;   // NaN
+        const unsigned long long k = argmax_key(v, (uint32_t)n);
+        best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long other = shfl_xor_u64(best, o);
+        best = other > best ? other : best;
+    }
+    if ((threadIdx.x & 63) == 0) s_key[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kArgmaxThreads / 64; ++w) best = s_key[w] > best ? s_key[w] : best;
+        if (best) atomicMax(&p.keys[m], best);
+        __threadfence();
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[m], 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned)(p.chunks - 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0 && s_last) {
+        __threadfence();
+        const unsigned long long k = atomicExch(&p.keys[m], 0ull);
+        p.idx[m] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
+        __hip_atomic_store(&p.counters[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// q[k][n] through the kernels' own dequantiser with zero point 0: the exact fp16 value is q.
+__global__ void unpack_u8_kernel(const uint32_t *qweight, int K, int N, uint8_t *q)
+{
+    const long long quads = (long long)(K / 8) * (N / 4);
+    const Masks mk = make_masks();
+    const ZeroSub z0 = zero_sub(0);
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < quads;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long wr = i / (N / 4);
+        const int n = (int)(i - wr * (N / 4)) * 4;
+        const uint4 w = *reinterpret_cast<const uint4 *>(qweight + wr * N + n);
+        const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+        constexpr int kRowOfSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const half8_t d = dequant_word(words[j], z0, mk);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                q[(wr * 8 + kRowOfSlot[s]) * N + n + j] = (uint8_t)(int)(float)d[s];
+        }
+    }
+}
+
+// w[k][n] = (q - z) * scale through the kernels' dequantiser: exact fp16 (q - z), widened to
+// fp32 and multiplied by the widened scale (a 5-bit by 11-bit product, exact in fp32).
+__global__ void dequant_f32_kernel(const uint32_t *qweight, const uint16_t *scales,
+                                   const uint32_t *qzeros, int g, int K, int N, float *w)
+{
+    const long long quads = (long long)(K / 8) * (N / 4);
+    const Masks mk = make_masks();
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < quads;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long wr = i / (N / 4);
+        const int n = (int)(i - wr * (N / 4)) * 4;
+        const long long gi = wr * 8 / g;
+        const uint4 v = *reinterpret_cast<const uint4 *>(qweight + wr * N + n);
+        const uint2 sc = *reinterpret_cast<const uint2 *>(scales + gi * N + n);
+        const float s4[4] = {half_bits_to_float(sc.x & 0xFFFFu), half_bits_to_float(sc.x >> 16),
+                             half_bits_to_float(sc.y & 0xFFFFu), half_bits_to_float(sc.y >> 16)};
+        const uint32_t zw = qzeros ? qzeros[gi * (N / 8) + n / 8] : 0u;
+        const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+        constexpr int kRowOfSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const ZeroSub zs = qzeros ? zero_sub(zero_of(zw, (uint32_t)(n + j))) : zero_sub_sym();
+            const half8_t d = dequant_word(words[j], zs, mk);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                w[(wr * 8 + kRowOfSlot[s]) * N + n + j] = (float)d[s] * s4[j];
+        }
+    }
+}
+
+unsigned grid_for(long long items, int threads)
+{
+    long long b = (items + threads - 1) / threads;
+    if (b > 65536) b = 65536;
+    if (b < 1) b = 1;
+    return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(argmax_rows_kernel, dim3((unsigned)a.chunks, (unsigned)a.M), dim3(kArgmaxThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q, hipStream_t s)
+{
+    const long long quads = (long long)(K / 8) * (N / 4);
+    hipLaunchKernelGGL(unpack_u8_kernel, dim3(grid_for(quads, 256)), dim3(256), 0, s, qweight, K, N, q);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_f32(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                              int g, int K, int N, float *w, hipStream_t s)
+{
+    const long long quads = (long long)(K / 8) * (N / 4);
+    hipLaunchKernelGGL(dequant_f32_kernel, dim3(grid_for(quads, 256)), dim3(256), 0, s, qweight, scales,
+                       qzeros, g, K, N, w);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -1,0 +1,140 @@
+// Device-side code readers shared by every W4A16 kernel (gfx950).
+//
+// One header holds the unpack and dequantisation so the GEMV, the MFMA GEMM and the test hooks
+// cannot drift apart (TensorFold PR #859 keeps its code readers in one header shared by its
+// GEMV and GEMM for the same reason).
+//
+// Exact dequantisation in fp16. The pages keep the dequantisation exact, (q - z) * scale
+// (GRIMOIRE v1.7 release notes, 'What changed'). d = q - z is an integer in [-15, 15], exact in
+// fp16, so the kernels build d directly as packed fp16 pairs with two VALU operations per pair:
+//   (word & 0x000F000F) | 0x64006400  ->  fp16 pair (1024 + q_j, 1024 + q_{j+4})
+//   (word & 0x00F000F0) | 0x54005400  ->  fp16 pair (  64 + q_j,   64 + q_{j+4})
+// (0x6400 is 1024 with a unit of 1 in the low fraction bits, 0x5400 is 64 with a unit of 1/16,
+// so a nibble sitting at bit 4 still reads as q), and one v_pk_add_f16 with the packed
+// constant -(1024 + z) or -(64 + z) leaves q - z exactly in both halves. The scale is applied
+// once per group to fp32 sums, so the product d * scale never rounds before accumulation.
+//
+// A word of column n holds rows 8i..8i+7; the dequantised pairs come out in the slot order
+//   slot:  0   1   2   3   4   5   6   7
+//   row :  k0  k4  k1  k5  k2  k6  k3  k7      (relative to 8i)
+// Activations are staged in the same slot order so that slot t of A meets slot t of B in the
+// dot products and in the MFMA K dimension.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half2_t as_half2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+__device__ __forceinline__ uint32_t as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Packed fp16 constants that subtract the zero point from the two magic encodings.
+struct ZeroSub {
+    uint32_t even;  // -(1024 + z) in both halves, for nibbles read at bit 0 of a half
+    uint32_t odd;   // -(64 + z) in both halves, for nibbles read at bit 4 of a half
+};
+
+__device__ __forceinline__ ZeroSub zero_sub(uint32_t z)
+{
+    const uint32_t e = 0xE400u | z;          // fp16 -(1024 + z)
+    const uint32_t o = 0xD400u | (z << 4);   // fp16 -(64 + z)
+    return ZeroSub{e | (e << 16), o | (o << 16)};
+}
+
+// The symmetric zero point 8.
+__device__ __forceinline__ ZeroSub zero_sub_sym() { return ZeroSub{0xE408E408u, 0xD480D480u}; }
+
+// Nibble masks kept in VGPRs so the and/or pair fuses into one v_and_or_b32 (gfx950's VOP3 has
+// no literal operand, and two SGPR sources would break the constant-bus limit).
+struct Masks {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ Masks make_masks()
+{
+    Masks m{0x000F000Fu, 0x00F000F0u};
+    asm volatile("" : "+v"(m.lo), "+v"(m.hi));
+    return m;
+}
+
+// One packed word -> 8 exact fp16 values (q - z) in slot order.
+__device__ __forceinline__ half8_t dequant_word(uint32_t w, ZeroSub zs, Masks mk)
+{
+    const uint32_t h = w >> 8;
+    const half2_t p0 = as_half2((w & mk.lo) | 0x64006400u) + as_half2(zs.even);   // k0, k4
+    const half2_t p1 = as_half2((w & mk.hi) | 0x54005400u) + as_half2(zs.odd);    // k1, k5
+    const half2_t p2 = as_half2((h & mk.lo) | 0x64006400u) + as_half2(zs.even);   // k2, k6
+    const half2_t p3 = as_half2((h & mk.hi) | 0x54005400u) + as_half2(zs.odd);    // k3, k7
+    half8_t r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// Zero point of column n from its packed word (nibble n % 8).
+__device__ __forceinline__ uint32_t zero_of(uint32_t zword, uint32_t n)
+{
+    return (zword >> (4u * (n & 7u))) & 0xFu;
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// bf16 bits -> fp32 (exact: bf16 is the upper half of a binary32).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits)
+{
+    return __builtin_bit_cast(float, bits << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Exponent field of a bf16 value (0..255).
+__device__ __forceinline__ uint32_t bf16_exp_field(uint32_t bits) { return (bits >> 7) & 0xFFu; }
+
+// Per-row rescale of activations into fp16. With e_max the largest bf16 exponent field of the
+// row's slice, the slice is multiplied by 2^-shift with shift = e_max - 141 so that every
+// magnitude lands below 2^15 (fp16 tops out at 65504). A bf16 value keeps all 8 significant
+// bits in fp16 as long as it stays above 2^-17 after the rescale, i.e. within 2^31 of the
+// slice's largest magnitude; the rescale itself is exact.
+__device__ __forceinline__ int act_shift(uint32_t e_max) { return (int)e_max - 141; }
+
+// 8 bf16 activations of one word's rows (k order) -> fp16 in slot order, times 2^-shift.
+__device__ __forceinline__ half8_t act8_to_slots(uint4 raw, int shift)
+{
+    const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __builtin_amdgcn_ldexpf(bf16_bits_to_float(v[i] & 0xFFFFu), -shift);
+        f[2 * i + 1] = __builtin_amdgcn_ldexpf(bf16_bits_to_float(v[i] >> 16), -shift);
+    }
+    half8_t r;
+    r[0] = (_Float16)f[0]; r[1] = (_Float16)f[4]; r[2] = (_Float16)f[1]; r[3] = (_Float16)f[5];
+    r[4] = (_Float16)f[2]; r[5] = (_Float16)f[6]; r[6] = (_Float16)f[3]; r[7] = (_Float16)f[7];
+    return r;
+}
+
+__device__ __forceinline__ uint32_t max_exp8(uint4 raw)
+{
+    const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t e = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        e = max(e, bf16_exp_field(v[i] & 0xFFFFu));
+        e = max(e, bf16_exp_field(v[i] >> 16));
+    }
+    return e;
+}
+
+}  // namespace w4a16
