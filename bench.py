@@ -1,0 +1,229 @@
+"""Benchmark: W4A16 GEMV / small-M GEMM achieved HBM bandwidth and microseconds per call.
+
+Default workload: the FFN up/gate projection (K=5120, N=17408, group 128, symmetric zero
+point) swept over M = 1, 2, 4, 8, 16 rows; one step is one call at each M. Inputs are seeded
+synthetic tensors with the value distributions of an int4 GPTQ checkpoint and bf16
+activations (no checkpoint is loaded). Every call reads a different copy of the weights
+from a rotating pool far larger than the 256 MB last-level cache, so the weights stream from
+HBM as they do in decode, where each layer's weights are read once per token.
+
+Algorithmic bytes per call = qweight (K*N/2) + scales (2*K*N/g) + qzeros (K*N/(2g), if any)
++ activations (2*M*K) + outputs (4*M*N for fp32). Re-reads, padding and split-K scratch are
+not counted.
+
+Prints one JSON line (rank 0; this build runs on one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+POOL_BYTES = 768 * 2 ** 20      # rotating weight pool, 3x the 256 MB last-level cache
+
+
+def algorithmic_bytes(M, K, N, g, symmetric, out_bytes=4):
+    b = K * N // 2 + 2 * (K // g) * N + 2 * M * K + out_bytes * M * N
+    if not symmetric:
+        b += (K // g) * N // 2
+    return b
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="ffn_up",
+                   choices=["tiny", "attn", "ffn_up", "ffn_down", "lm_head"])
+    p.add_argument("--ms", default=None, help="comma-separated row counts (default: the workload's)")
+    p.add_argument("--splits", type=int, default=0, help="workgroups per column tile along K (0 = default)")
+    p.add_argument("--waves-k", type=int, default=0, help="waves per workgroup along K (0 = default)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def cpu_baseline(wl, inp, ms, seconds):
+    """The CPU oracle, as it is, on this host's cores: the whole step repeated for ~`seconds`."""
+    import oracle
+    oracle._load()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    reps, elapsed, nbytes = 0, 0.0, 0
+    while elapsed < seconds or reps == 0:
+        for M in ms:
+            t = time.perf_counter()
+            oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)
+            elapsed += time.perf_counter() - t
+            nbytes += algorithmic_bytes(M, wl.K, wl.N, wl.group, wl.symmetric)
+        reps += 1
+    return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full step(s) of the workload (M={','.join(map(str, ms))}, all {wl.N} columns), "
+                      f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)"}
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it still matches the
+    kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        from verify_matmul_amd import _build
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_hash") != _build.source_hash():
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the column-sharded multi-GPU layout is described in DESIGN.md)", file=sys.stderr)
+        return 2
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if world != 1:
+        print("bench.py: run as a single process on one GPU", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import verify_matmul_amd as vm
+    from verify_matmul_amd import synth
+
+    lib = vm.load()
+    wl = synth.WORKLOADS[args.workload]
+    ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
+    inp = synth.make_inputs(wl)
+    K, N, g = wl.K, wl.N, wl.group
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    per_copy = algorithmic_bytes(1, K, N, g, wl.symmetric)
+    R = max(2, math.ceil(POOL_BYTES / per_copy))
+    qw0 = torch.from_numpy(inp.qweight.view(np.int32)).to(dev)
+    sc0 = torch.from_numpy(inp.scales.view(np.int16)).to(dev)
+    qz0 = None if inp.qzeros is None else torch.from_numpy(inp.qzeros.view(np.int32)).to(dev)
+    a0 = torch.from_numpy(inp.act.view(np.int16)).to(dev)
+    pool = []
+    for r in range(R):
+        qw = qw0.clone()
+        sc = sc0.clone()
+        qz = None if qz0 is None else qz0.clone()
+        a = a0.clone()
+        outs = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}
+        pool.append((qw, sc, qz, a, outs))
+    del qw0, sc0, qz0
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    # pre-marshalled calls: (M, args) per rotation slot
+    calls = []
+    for (qw, sc, qz, a, outs) in pool:
+        row = []
+        for M in ms:
+            row.append((M, (ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(qw.data_ptr()),
+                            ctypes.c_void_p(sc.data_ptr()), None if qz is None else ctypes.c_void_p(qz.data_ptr()),
+                            g, M, N, K, ctypes.c_void_p(outs[M].data_ptr()), 0, args.splits, args.waves_k, sp)))
+        calls.append(row)
+    fn = lib.w4a16_gemm_ex
+
+    def step(i, evs=None):
+        for j, (M, cargs) in enumerate(calls[i % R]):
+            if evs is not None:
+                evs[i][j][0].record(stream)
+            rc = fn(*cargs)
+            if evs is not None:
+                evs[i][j][1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm_ex failed: {lib.w4a16_last_error().decode()}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
+           for _ in range(args.steps)]
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(i, evs)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall = t1 - t0
+    gpu_span = g0.elapsed_time(g1) / 1e3
+    step_bytes = sum(algorithmic_bytes(M, K, N, g, wl.symmetric) for M in ms)
+    value = step_bytes * args.steps / wall / 1e9
+
+    per_m = {}
+    kern_time = {"gemv": 0.0, "gemm": 0.0}
+    kern_bytes = {"gemv": 0, "gemm": 0}
+    kern_launches = {"gemv": 0, "gemm": 0}
+    for j, M in enumerate(ms):
+        d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
+        b = algorithmic_bytes(M, K, N, g, wl.symmetric)
+        us = float(np.mean(d))
+        kern, spl, wk = vm.w4a16_plan(M, N, K, g)
+        per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+                         "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
+                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b,
+                         "kernel": "gemv" if kern == 0 else "mfma",
+                         "splits": args.splits or spl, "waves_k": args.waves_k or wk}
+        k = "gemv" if M == 1 else "gemm"
+        kern_time[k] += float(np.sum(d))
+        kern_bytes[k] += b * args.steps
+        kern_launches[k] += args.steps
+    dom = max(kern_time, key=kern_time.get)
+    achieved = kern_bytes[dom] / kern_time[dom] / 1e3   # GB/s
+    traffic = load_traffic(args.workload, dom)
+
+    kernel_name = {"gemv": "w4a16_gemm_kernel<gemv>", "gemm": "w4a16_gemm_kernel<mfma>"}[dom]
+    rec = {
+        "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}, M in {','.join(map(str, ms))} (one call each per step)",
+                   "K": K, "N": N, "group": g, "symmetric_zero": wl.symmetric, "ms": list(ms), "out": "fp32",
+                   "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20),
+                   "launch": "default" if not (args.splits or args.waves_k) else
+                   f"splits={args.splits or 'default'} waves_k={args.waves_k or 'default'}"},
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "launches": kern_launches[dom],
+                     "bytes_per_launch": kern_bytes[dom] // max(1, kern_launches[dom])},
+        "per_m": per_m,
+        "gpu_span_ms_per_step": round(gpu_span / args.steps * 1e3, 4),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

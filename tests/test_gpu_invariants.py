@@ -33,10 +33,10 @@ def test_codes_equal_zeros_give_zero(gu):
     sym = synth.Inputs(np.full((K // 8, N), 0x88888888, np.uint32), inp.scales, None, inp.act, g)
     ds = gu.DevInputs(sym)
     for M in ROWS:
-        for splits in (1, 3):
-            gu.say(f"[q==z] M={M} splits={splits}")
-            assert np.all(d.run(M, splits=splits) == 0.0)
-            assert np.all(ds.run(M, splits=splits) == 0.0)
+        for splits, wk in ((1, 1), (3, 2), (0, 0)):
+            gu.say(f"[q==z] M={M} splits={splits} waves_k={wk}")
+            assert np.all(d.run(M, splits=splits, waves_k=wk) == 0.0)
+            assert np.all(ds.run(M, splits=splits, waves_k=wk) == 0.0)
 
 
 def test_integer_matmul_is_exact(gu):
@@ -51,9 +51,9 @@ def test_integer_matmul_is_exact(gu):
     for M in ROWS:
         ref = (ai[:M].astype(np.int64) @ codes.astype(np.int64)).astype(np.float64)
         assert np.abs(ref).max() < 2 ** 24
-        for splits in (0, 17, 40):
-            gu.say(f"[integer] M={M} splits={splits}")
-            assert np.array_equal(d.run(M, splits=splits), ref)
+        for splits, wk in ((0, 0), (17, 2), (40, 8), (1, 16)):
+            gu.say(f"[integer] M={M} splits={splits} waves_k={wk}")
+            assert np.array_equal(d.run(M, splits=splits, waves_k=wk), ref)
 
 
 def test_scaling_negation_permutation_and_repeat(gu):
@@ -107,9 +107,9 @@ def test_wide_dynamic_range_rows(gu):
     d = gu.DevInputs(inp)
     for M in (1, 5, 16):
         y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
-        for splits in (2, 4):
-            gu.say(f"[range] M={M} splits={splits}")
-            parity.check_close(d.run(M, splits=splits), y_ref, bound, f"range M={M}")
+        for splits, wk in ((1, 1), (2, 4), (0, 0)):
+            gu.say(f"[range] M={M} splits={splits} waves_k={wk}")
+            parity.check_close(d.run(M, splits=splits, waves_k=wk), y_ref, bound, f"range M={M}")
 
 
 def test_argmax_edge_cases(gu):
@@ -142,6 +142,6 @@ def test_errors_do_not_touch_the_device(gu):
     d = gu.DevInputs(inp)
     out = torch.zeros((1, 256), dtype=torch.float32, device=gu.DEV)
     with pytest.raises(vm.W4A16Error):
-        vm.w4a16_gemm_splits(d.act[:1], d.qweight, d.scales, None, 128, out, 999)
+        vm.w4a16_gemm_ex(d.act[:1], d.qweight, d.scales, None, 128, out, 999, 1)
     torch.cuda.synchronize()
     assert torch.all(out == 0)

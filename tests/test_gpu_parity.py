@@ -81,27 +81,22 @@ SHAPES = [   # (K, N, group, symmetric): several tiles, ragged column tails, une
 ]
 
 
-def lds_fits(M, K, splits):
-    # the activations of one K-slice must fit the LDS a workgroup may stage (64 KiB - 256)
-    max_steps = -(-(K // 32) // splits)
-    return 64 + max_steps * 4 * M * 16 <= 65536 - 256
+LAUNCHES = [(0, 0), (1, 1), (1, 2), (2, 1), (3, 4), (1, 16), (5, 8)]   # (splits, waves_k); 0 = default
 
 
 @pytest.mark.parametrize("K,N,g,sym", SHAPES)
-def test_parity_sweep_rows_and_splits(gu, K, N, g, sym):
+def test_parity_sweep_rows_and_launches(gu, K, N, g, sym):
     inp = synth.make_random(K * 7 + N, 16, K, N, g, sym)
     d = gu.DevInputs(inp)
     steps = K // 32
     for M in range(1, 17):
         y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
-        for splits in sorted({0, 1, 2, 3, min(7, steps), steps}):
-            if splits and not lds_fits(M, K, splits):
-                with pytest.raises(vm.W4A16Error):
-                    d.run(M, splits=splits)
+        for splits, wk in LAUNCHES + [(steps, 1), (steps // 16, 16)]:
+            if (splits or 1) * (wk or 1) > steps or (wk == 16 and splits == 0):
                 continue
-            gu.say(f"[sweep] K={K} N={N} g={g} sym={sym} M={M} splits={splits}")
-            y = d.run(M, splits=splits)
-            parity.check_close(y, y_ref, bound, f"K={K} N={N} g={g} M={M} splits={splits}")
+            gu.say(f"[sweep] K={K} N={N} g={g} sym={sym} M={M} splits={splits} waves_k={wk}")
+            y = d.run(M, splits=splits, waves_k=wk)
+            parity.check_close(y, y_ref, bound, f"K={K} N={N} g={g} M={M} splits={splits} waves_k={wk}")
 
 
 # ---- the workloads at full size, in the default launch configuration --------------------------
@@ -126,8 +121,8 @@ def _wl(gu, cache, name):
 @pytest.mark.parametrize("name,M", _WL_CASES)
 def test_parity_workloads(gu, wl_cache, name, M):
     inp, d = _wl(gu, wl_cache, name)
-    gu.say(f"[workload] {name} M={M} K={inp.K} N={inp.N} g={inp.group} splits="
-           f"{vm.w4a16_default_splits(M, inp.N, inp.K, inp.group)}")
+    gu.say(f"[workload] {name} M={M} K={inp.K} N={inp.N} g={inp.group} plan (kernel, splits, waves_k)="
+           f"{vm.w4a16_plan(M, inp.N, inp.K, inp.group)}")
     y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)
     y = d.run(M)
     frac = parity.check_close(y, y_ref, bound, f"{name} M={M} fp32")

@@ -74,19 +74,30 @@ def test_validation_order_is_fixed(lib):
     assert gemm(lib, g=48, a=A + 2) == -1 and b"multiple of 32" in lib.w4a16_last_error()
 
 
-def test_explicit_splits_are_checked(lib):
-    # K=512 has 16 steps of 32
-    assert lib.w4a16_gemm_splits(A, Q, S, None, 128, 1, 256, 512, O, 0, 17, None) == -1
-    assert lib.w4a16_gemm_splits(A, Q, S, None, 128, 1, 256, 512, O, 0, -1, None) == -1
+def ex(lib, splits, wk, K=512):
+    return lib.w4a16_gemm_ex(A, Q, S, None, 128, 1, 256, K, O, 0, splits, wk, None)
 
 
-def test_default_splits_host_only(lib):
-    for M in (1, 2, 4, 8, 16):
-        s = lib.w4a16_default_splits(M, 17408, 5120, 128)
-        assert 1 <= s <= 5120 // 32
-    assert lib.w4a16_default_splits(1, 248320, 5120, 128) >= 1
-    assert lib.w4a16_default_splits(16, 5120, 17408, 64) >= 1
-    assert lib.w4a16_default_splits(0, 256, 512, 128) == -1
+def test_explicit_launch_is_checked(lib):
+    # K=512 has 16 steps of 32: splits * waves_k may not exceed 16; waves_k in {1,2,4,8,16}
+    assert ex(lib, 17, 1) == -1
+    assert ex(lib, 4, 8) == -1
+    assert ex(lib, -1, 0) == -1
+    assert ex(lib, 0, -1) == -1
+    assert ex(lib, 1, 3) == -1
+    assert ex(lib, 1, 32) == -1
+
+
+def test_plan_host_only(lib):
+    import ctypes
+    k, s, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    for M, N, K, g in ((1, 17408, 5120, 128), (16, 17408, 5120, 128), (5, 248320, 5120, 128),
+                       (1, 5120, 5120, 128), (16, 5120, 17408, 64), (1, 256, 512, 128), (16, 8, 64, 32)):
+        assert lib.w4a16_plan(M, N, K, g, ctypes.byref(k), ctypes.byref(s), ctypes.byref(w)) == 0
+        assert k.value == (0 if M == 1 else 1)
+        assert s.value >= 1 and w.value in (1, 2, 4, 8, 16) and s.value * w.value <= K // 32
+    assert lib.w4a16_plan(0, 256, 512, 128, None, None, None) == -1
+    assert lib.w4a16_plan(1, 256, 512, 48, None, None, None) == -1
 
 
 def test_aux_entry_points_reject_bad_arguments(lib):

@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_splits", "w4a16_default_splits",
+    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "EXPORTS",
 ]
@@ -24,7 +24,7 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = (
-    "w4a16_gemm", "w4a16_gemm_splits", "w4a16_default_splits", "w4a16_argmax_rows",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_plan", "w4a16_argmax_rows",
     "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
@@ -50,8 +50,8 @@ def load():
     lib = ctypes.CDLL(lib_path)
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
-    lib.w4a16_gemm_splits.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P]
-    lib.w4a16_default_splits.argtypes = [I, I, I, I]
+    lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, P]
+    lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
     lib.w4a16_dequant_f32.argtypes = [P, P, P, I, I, I, P, P]
@@ -61,7 +61,7 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_splits", "w4a16_default_splits", "w4a16_argmax_rows",
+    for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -124,16 +124,19 @@ def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
     return out
 
 
-def w4a16_gemm_splits(A, qweight, scales, qzeros, group_size, out, splits, stream=None):
-    """w4a16_gemm with an explicit split-K factor (0 = the default choice)."""
+def w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, out, splits=0, waves_k=0, stream=None):
+    """w4a16_gemm with an explicit launch (0 = the default choice for that knob)."""
     args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
-    _check(load().w4a16_gemm_splits(*args, int(splits), _stream(stream)), "w4a16_gemm_splits")
+    _check(load().w4a16_gemm_ex(*args, int(splits), int(waves_k), _stream(stream)), "w4a16_gemm_ex")
     return out
 
 
-def w4a16_default_splits(M, N, K, group_size) -> int:
-    return _check(load().w4a16_default_splits(int(M), int(N), int(K), int(group_size)),
-                  "w4a16_default_splits")
+def w4a16_plan(M, N, K, group_size):
+    """(kernel, splits, waves_k) that w4a16_gemm uses for a shape; kernel 0 = GEMV, 1 = MFMA GEMM."""
+    k, s, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().w4a16_plan(int(M), int(N), int(K), int(group_size), ctypes.byref(k), ctypes.byref(s),
+                             ctypes.byref(w)), "w4a16_plan")
+    return k.value, s.value, w.value
 
 
 def w4a16_argmax_rows(logits, idx, stream=None):

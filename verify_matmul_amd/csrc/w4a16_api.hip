@@ -2,6 +2,7 @@
 // The declarations and the contract live in include/w4a16.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <stdarg.h>
@@ -98,25 +99,45 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
     return W4A16_OK;
 }
 
-// Split-K factor: enough workgroups to keep every CU streaming, while keeping the fp32
-// partials (splits x M x N x 4 bytes, written and read once) small against the weights.
-int pick_splits(int M, int N, int K)
+int pow2_floor(int x)
+{
+    int p = 1;
+    while (p * 2 <= x) p *= 2;
+    return p;
+}
+
+// The launch plan of a shape. Goals, in order: (1) enough waves in flight to cover HBM latency
+// on 256 CUs (about 2-3 thousand), (2) a column tile per workgroup when there are enough tiles,
+// so no partial sum leaves the CU, (3) split K across workgroups only for narrow matrices.
+// `splits` / `wk` > 0 override the choice (tuning and tests).
+int make_plan(int M, int N, int K, int splits, int wk, GemmPlan *plan)
 {
     const int steps = K / kStepK;
     const int tiles = (N + kTileN - 1) / kTileN;
-    // activations of one slice must fit the LDS budget
-    int s = 1;
-    while (s < steps && gemm_lds_bytes(M, K, s) > (size_t)kMaxLds) ++s;
-    // aim for about 1024 workgroups (4 per CU on 256 CUs)
-    int want = (1024 + tiles - 1) / tiles;
-    // partial traffic 8*splits*M*N bytes against K*N/2 bytes of weights: keep under ~1/8
-    int cap = (K / 2) / (8 * 8 * M);
-    if (cap < 1) cap = 1;
-    if (want > cap) want = cap;
-    if (want > s) s = want;
-    if (s > steps) s = steps;
-    if (s > 65535) s = 65535;
-    return s;
+    const int kTargetWaves = 2560;
+    if (splits == 0) splits = tiles >= 256 ? 1 : std::min(steps, (320 + tiles - 1) / tiles);
+    if (wk == 0) {
+        wk = pow2_floor(std::max(1, kTargetWaves / (tiles * splits)));
+        if (wk > 8) wk = 8;
+        while (wk > 1 && splits * wk > steps) wk /= 2;
+    }
+    if (wk != 1 && wk != 2 && wk != 4 && wk != 8 && wk != 16)
+        return fail(W4A16_ERR_INVALID_ARG, "waves_k=%d is not 1, 2, 4, 8 or 16", wk);
+    if (splits < 1 || splits > 65535 || (long long)splits * wk > steps)
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d x waves_k=%d exceeds the %d K-steps of 32", splits, wk, steps);
+    plan->mfma = M > 1;
+    plan->wk = wk;
+    plan->splits = splits;
+    // stage activations in LDS when that is cheaper than converting fragments every step and
+    // fits the budget; the GEMV always stages
+    int stride = 0;
+    const size_t staged = gemm_lds_bytes(M, K, splits, wk, true, &stride);
+    plan->lds_a = !plan->mfma || (M <= 8 && staged <= (size_t)kLdsStageBudget * wk);
+    plan->lds = gemm_lds_bytes(M, K, splits, wk, plan->lds_a, &plan->a_stride);
+    if (plan->lds > (size_t)kMaxLds)
+        return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",
+                    plan->lds, kMaxLds);
+    return W4A16_OK;
 }
 
 int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -143,19 +164,17 @@ int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scal
 
 extern "C" {
 
-int w4a16_gemm_splits(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
-                      int group_size, int M, int N, int K, void *out, int out_dtype, int splits,
-                      hipStream_t stream)
+int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                  int group_size, int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
+                  hipStream_t stream)
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
-    const int steps = K / kStepK;
-    if (splits < 0 || splits > steps || splits > 65535)
-        return fail(W4A16_ERR_INVALID_ARG, "splits=%d outside 0..%d", splits, steps < 65535 ? steps : 65535);
-    if (splits == 0) splits = pick_splits(M, N, K);
-    if (gemm_lds_bytes(M, K, splits) > (size_t)kMaxLds)
-        return fail(W4A16_ERR_INVALID_ARG, "splits=%d leaves %zu bytes of activations per workgroup (max %d)",
-                    splits, gemm_lds_bytes(M, K, splits), kMaxLds);
+    if (splits < 0 || waves_k < 0)
+        return fail(W4A16_ERR_INVALID_ARG, "splits=%d waves_k=%d must be >= 0", splits, waves_k);
+    GemmPlan plan{};
+    rc = make_plan(M, N, K, splits, waves_k, &plan);
+    if (rc != W4A16_OK) return rc;
 
     GemmArgs a{};
     a.A = static_cast<const uint16_t *>(A);
@@ -167,15 +186,16 @@ int w4a16_gemm_splits(const void *A, const uint32_t *qweight, const uint16_t *sc
     a.N = N;
     a.K = K;
     a.g = group_size;
-    a.splits = splits;
+    a.splits = plan.splits;
     a.out_bf16 = out_dtype == W4A16_OUT_BF16;
-    if (splits > 1) {
+    a.a_stride = plan.a_stride;
+    if (plan.splits > 1) {
         const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
-        rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)splits * M * N * sizeof(float), &a.counters,
-                         &a.partials);
+        rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)plan.splits * M * N * sizeof(float),
+                         &a.counters, &a.partials);
         if (rc != W4A16_OK) return rc;
     }
-    const hipError_t e = launch_gemm(a, stream);
+    const hipError_t e = launch_gemm(a, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     return W4A16_OK;
 }
@@ -183,14 +203,20 @@ int w4a16_gemm_splits(const void *A, const uint32_t *qweight, const uint16_t *sc
 int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
 {
-    return w4a16_gemm_splits(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, stream);
+    return w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, stream);
 }
 
-int w4a16_default_splits(int M, int N, int K, int group_size)
+int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k)
 {
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
-    return pick_splits(M, N, K);
+    GemmPlan plan{};
+    const int rc = make_plan(M, N, K, 0, 0, &plan);
+    if (rc != W4A16_OK) return rc;
+    if (kernel) *kernel = plan.mfma ? 1 : 0;
+    if (splits) *splits = plan.splits;
+    if (waves_k) *waves_k = plan.wk;
+    return W4A16_OK;
 }
 
 int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream_t stream)

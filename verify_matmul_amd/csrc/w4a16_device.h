@@ -106,24 +106,36 @@ __device__ __forceinline__ uint32_t bf16_exp_field(uint32_t bits) { return (bits
 // row's slice, the slice is multiplied by 2^-shift with shift = e_max - 141 so that every
 // magnitude lands below 2^15 (fp16 tops out at 65504). A bf16 value keeps all 8 significant
 // bits in fp16 as long as it stays above 2^-17 after the rescale, i.e. within 2^31 of the
-// slice's largest magnitude; the rescale itself is exact.
-__device__ __forceinline__ int act_shift(uint32_t e_max) { return (int)e_max - 141; }
-
-// 8 bf16 activations of one word's rows (k order) -> fp16 in slot order, times 2^-shift.
-__device__ __forceinline__ half8_t act8_to_slots(uint4 raw, int shift)
+// slice's largest magnitude; the rescale itself is exact. The shift is kept >= -126 so that
+// 2^-shift stays a finite fp32 (that only affects rows whose largest magnitude is below 2^-112).
+__device__ __forceinline__ int act_shift(uint32_t e_max)
 {
-    const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __builtin_amdgcn_ldexpf(bf16_bits_to_float(v[i] & 0xFFFFu), -shift);
-        f[2 * i + 1] = __builtin_amdgcn_ldexpf(bf16_bits_to_float(v[i] >> 16), -shift);
-    }
+    const int s = (int)e_max - 141;
+    return s < -126 ? -126 : s;
+}
+
+// 8 bf16 activations of one word's rows (k order: raw.x = k0,k1 ... raw.w = k6,k7) -> fp16 in
+// slot order, times `mul` (= 2^-shift, so the product is exact). The fp32 -> fp16 step rounds
+// toward zero; it is exact for every value inside fp16's range, which the rescale guarantees
+// for all but the smallest magnitudes of a row.
+__device__ __forceinline__ half8_t act8_to_slots(uint4 raw, float mul)
+{
+    const float k0 = bf16_bits_to_float(raw.x & 0xFFFFu) * mul, k1 = __builtin_bit_cast(float, raw.x & 0xFFFF0000u) * mul;
+    const float k2 = bf16_bits_to_float(raw.y & 0xFFFFu) * mul, k3 = __builtin_bit_cast(float, raw.y & 0xFFFF0000u) * mul;
+    const float k4 = bf16_bits_to_float(raw.z & 0xFFFFu) * mul, k5 = __builtin_bit_cast(float, raw.z & 0xFFFF0000u) * mul;
+    const float k6 = bf16_bits_to_float(raw.w & 0xFFFFu) * mul, k7 = __builtin_bit_cast(float, raw.w & 0xFFFF0000u) * mul;
+    const half2_t p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(k0, k4));
+    const half2_t p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(k1, k5));
+    const half2_t p2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(k2, k6));
+    const half2_t p3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(k3, k7));
     half8_t r;
-    r[0] = (_Float16)f[0]; r[1] = (_Float16)f[4]; r[2] = (_Float16)f[1]; r[3] = (_Float16)f[5];
-    r[4] = (_Float16)f[2]; r[5] = (_Float16)f[6]; r[6] = (_Float16)f[3]; r[7] = (_Float16)f[7];
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
     return r;
 }
+
+// 2^-shift as a float (shift within [-126, 114]).
+__device__ __forceinline__ float pow2_neg(int shift) { return __builtin_amdgcn_ldexpf(1.0f, -shift); }
 
 __device__ __forceinline__ uint32_t max_exp8(uint4 raw)
 {

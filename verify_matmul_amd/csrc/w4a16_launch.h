@@ -6,14 +6,15 @@
 
 namespace w4a16 {
 
-// Columns covered by one GEMM/GEMV workgroup (4 waves x 64 columns).
-constexpr int kTileN = 256;
+// Columns covered by one wave and by one workgroup (the waves of a workgroup split K).
+constexpr int kTileN = 64;
 // K rows consumed per step (4 packed word rows = one 16x16x32 MFMA K step).
 constexpr int kStepK = 32;
-// Largest dynamic LDS a GEMM workgroup may ask for.
-constexpr int kMaxLds = 64 * 1024 - 256;   // leaves room for the static LDS
-// LDS bytes before the staged activations (per-row shifts).
-constexpr int kLdsHeader = 64;
+// Largest dynamic LDS a GEMM workgroup may ask for (gfx950: 160 KiB per workgroup).
+constexpr int kMaxLds = 160 * 1024 - 256;
+// Staged activations per wave beyond which converting fragments per step is preferred (keeps
+// about 8 waves per CU resident).
+constexpr int kLdsStageBudget = 16 * 1024;
 
 struct GemmArgs {
     const uint16_t *A;
@@ -24,19 +25,42 @@ struct GemmArgs {
     float *partials;          // [splits, M, N] when splits > 1
     uint32_t *counters;       // one per column tile, zero between calls
     int M, N, K, g;
-    int splits;
+    int splits;               // workgroups along K per column tile
     int out_bf16;
+    int a_stride;             // staged activations per wave, in 16-byte units
 };
 
-// LDS bytes a GEMM workgroup needs for the given rows and split.
-inline size_t gemm_lds_bytes(int M, int K, int splits)
+// How one call is launched.
+struct GemmPlan {
+    bool mfma;     // false: the M = 1 dot-product GEMV
+    bool lds_a;    // activations staged once per wave in LDS (else converted per step)
+    int wk;        // waves per workgroup, each a contiguous K range (1, 2, 4, 8 or 16)
+    int splits;    // workgroups per column tile, reduced through the scratch buffer
+    size_t lds;    // dynamic LDS bytes per workgroup
+    int a_stride;  // see GemmArgs
+};
+
+// Steps (of kStepK rows) of the largest K range a single wave gets under a plan.
+inline int max_wave_steps(int K, int splits, int wk)
 {
     const int steps = K / kStepK;
-    const int max_steps = (steps + splits - 1) / splits;
-    return (size_t)kLdsHeader + (size_t)max_steps * 4 * (size_t)M * 16;
+    const int per_split = (steps + splits - 1) / splits;
+    return (per_split + wk - 1) / wk;
 }
 
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+// Dynamic LDS of a plan: per-wave row exponents, then either the staged activations or the
+// cross-wave reduction buffer (the two never live at the same time).
+inline size_t gemm_lds_bytes(int M, int K, int splits, int wk, bool lds_a, int *a_stride)
+{
+    const size_t header = (size_t)wk * 16 * sizeof(int);
+    const size_t stride = lds_a ? (size_t)max_wave_steps(K, splits, wk) * 4 * M : 0;   // 16-byte units
+    if (a_stride) *a_stride = (int)stride;
+    const size_t staged = (size_t)wk * stride * 16;
+    const size_t red = (wk > 1 || splits > 1) ? (size_t)wk * M * kTileN * sizeof(float) : 0;
+    return header + (staged > red ? staged : red);
+}
+
+hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream);
 
 struct ArgmaxArgs {
     const float *logits;
