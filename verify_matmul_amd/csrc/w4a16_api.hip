@@ -10,7 +10,7 @@
 #include <string.h>
 #include <utility>
 
-#include "../../include/w4a16.h"
+#include "w4a16.h"
 #include "w4a16_launch.h"
 
 using namespace w4a16;
@@ -110,7 +110,7 @@ int pow2_floor(int x)
 // on 256 CUs (about 2-3 thousand), (2) a column tile per workgroup when there are enough tiles,
 // so no partial sum leaves the CU, (3) split K across workgroups only for narrow matrices.
 // `splits` / `wk` > 0 override the choice (tuning and tests).
-int make_plan(int M, int N, int K, int splits, int wk, GemmPlan *plan)
+int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan *plan)
 {
     const int steps = K / kStepK;
     const int tiles = (N + kTileN - 1) / kTileN;
@@ -128,12 +128,14 @@ int make_plan(int M, int N, int K, int splits, int wk, GemmPlan *plan)
     plan->mfma = M > 1;
     plan->wk = wk;
     plan->splits = splits;
-    // stage activations in LDS when that is cheaper than converting fragments every step and
-    // fits the budget; the GEMV always stages
-    int stride = 0;
-    const size_t staged = gemm_lds_bytes(M, K, splits, wk, true, &stride);
-    plan->lds_a = !plan->mfma || (M <= 8 && staged <= (size_t)kLdsStageBudget * wk);
-    plan->lds = gemm_lds_bytes(M, K, splits, wk, plan->lds_a, &plan->a_stride);
+    // Stage activations in LDS when that fits the per-wave budget (keeps ~8 waves per CU) and
+    // rows are few enough that converting them once beats converting fragments every step.
+    // The GEMV always stages.
+    GemmPlan staged{};
+    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, true, sym, &staged);
+    plan->lds_a = !plan->mfma || (M <= 8 && (size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
+                                   lds_staged <= (size_t)kMaxLds);
+    plan->lds = gemm_lds_layout(M, K, g, splits, wk, plan->lds_a, sym, plan);
     if (plan->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",
                     plan->lds, kMaxLds);
@@ -173,7 +175,7 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     if (splits < 0 || waves_k < 0)
         return fail(W4A16_ERR_INVALID_ARG, "splits=%d waves_k=%d must be >= 0", splits, waves_k);
     GemmPlan plan{};
-    rc = make_plan(M, N, K, splits, waves_k, &plan);
+    rc = make_plan(M, N, K, group_size, qzeros == nullptr, splits, waves_k, &plan);
     if (rc != W4A16_OK) return rc;
 
     GemmArgs a{};
@@ -188,7 +190,9 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     a.g = group_size;
     a.splits = plan.splits;
     a.out_bf16 = out_dtype == W4A16_OUT_BF16;
-    a.a_stride = plan.a_stride;
+    a.wave_lds = plan.wave_lds;
+    a.scale_off = plan.scale_off;
+    a.zero_off = plan.zero_off;
     if (plan.splits > 1) {
         const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
         rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)plan.splits * M * N * sizeof(float),
@@ -211,7 +215,7 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
     GemmPlan plan{};
-    const int rc = make_plan(M, N, K, 0, 0, &plan);
+    const int rc = make_plan(M, N, K, group_size, true, 0, 0, &plan);
     if (rc != W4A16_OK) return rc;
     if (kernel) *kernel = plan.mfma ? 1 : 0;
     if (splits) *splits = plan.splits;

@@ -14,37 +14,53 @@
 //     not an L2 write-back. The pages reduce split-K through per-slice partials too on GPUs
 //     without thread-block clusters (TensorFold PR #859, commit messages).
 //
+// Latency first. A wave lives for a few microseconds, only a handful of HBM round trips, so it
+// starts all its memory traffic at once:
+//   1. direct global->LDS loads (global_load_lds) of everything small the wave will need: its
+//      activations (raw bf16), and the scales and zero points of its groups;
+//   2. a ring of kPf steps of packed weights into registers;
+//   3. a wait for (1) only: loads retire in order, so "at most the ring outstanding" suffices;
+//   4. activations are converted in place in LDS while the weights are still in flight.
+// The ring then issues exactly one step per iteration (clamped past the wave's end), so the
+// compiler waits for the oldest step only.
+//
 // Per step (32 K rows x 64 columns per wave)
-//   * a ring of kPf steps of loads is kept in flight: every iteration issues exactly one step of
-//     loads (clamped to the wave's last step past the end) so the in-order load counter lets
-//     the compiler wait for the oldest step only;
 //   * each packed word becomes 8 exact fp16 values (q - z) (w4a16_device.h);
 //   * GEMV: v_dot2c_f32_f16 into one fp32 sum per column; the four word rows of a step are
 //     added across lanes at the end. GEMM: one v_mfma_f32_16x16x32_f16 per word column
 //     (16 rows x 16 columns x 32 K), activations padded with zero rows up to 16;
 //   * sums are kept per quantisation group and scaled once at the group's end.
 //
-// Activations: fp16 after an exact per-row power-of-two rescale chosen from the row's largest
-// exponent over the wave's K range. With few rows they are converted once into the wave's own
-// LDS; with many rows each lane converts its MFMA fragment as it arrives.
+// Activations are fp16 after an exact per-row power-of-two rescale chosen from the row's largest
+// exponent over the wave's K range. With up to 8 rows they are staged in LDS as above; with more
+// rows (whose staging would not fit) each lane converts its MFMA fragment as it arrives through
+// the ring, after a first pass that only finds the exponents.
 //
 // Why this shape (GRIMOIRE v1.7 release notes, 'What changed': a GEMV for one user and a
 // matrix-engine GEMM for 2-16 rows; GRIMOIRE v1.8, 'What changed': the small-row kernel got
 // faster from register budgeting and from splitting work over more threads): every
 // configuration is bound by streaming the packed weights from HBM, so the VALU work is only
-// the exact dequantisation and the loads stay in flight from the first instruction on.
+// the exact dequantisation and the weight loads stay in flight from the first instructions on.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
 namespace w4a16 {
 namespace {
 
-struct Slot {
-    uint4 w;      // packed words of 4 columns, one word row
-    uint2 s;      // fp16 scales of the 4 columns for the step's group
-    uint32_t z;   // packed zero word of the columns (asymmetric only)
-    uint4 a;      // raw bf16 activation fragment (per-step conversion only)
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt encoding (gfx9): wait until at most `n` vector memory operations are outstanding.
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ void load_to_lds16(const void *src, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ void load_to_lds4(const void *src, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds_base), 4, 0, 0);
+}
 
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf>
 __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
@@ -68,53 +84,118 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     const int se = (int)((long long)(split + 1) * steps / p.splits);
     const int wb = sb + (int)((long long)wave * (se - sb) / kWK);
     const int we = sb + (int)((long long)(wave + 1) * (se - sb) / kWK);   // we > wb (host)
+    const int g0 = wb / spg;                  // first group of the wave
+    const int ng = (we - 1) / spg - g0 + 1;   // groups touched by the wave
 
-    int *shift_lds = reinterpret_cast<int *>(smem) + wave * 16;   // this wave's per-row shifts
+    // LDS: [kWK x 16 row shifts][per wave: activations | scales | zeros]
+    int *shift_lds = reinterpret_cast<int *>(smem) + wave * 16;
     unsigned char *region = smem + kWK * 16 * sizeof(int);
-    half8_t *a_lds = reinterpret_cast<half8_t *>(region) + (size_t)wave * p.a_stride;
+    unsigned char *wreg = region + (size_t)wave * p.wave_lds;
+    uint4 *a_lds = reinterpret_cast<uint4 *>(wreg);                                // [word row][M]
+    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(wreg + p.scale_off);           // [group][64]
+    uint32_t *z_lds = reinterpret_cast<uint32_t *>(wreg + p.zero_off);             // [group][8]
 
     const int n0 = tile * kTileN + cl * 4;
     const bool col_ok = n0 < N;
-    const int nc = col_ok ? n0 : 0;            // clamped column for loads of dead lanes
-    const int arow = cl < M ? cl : 0;          // clamped activation row (MFMA fragments)
+    const int nc = col_ok ? n0 : 0;       // clamped column for loads of dead lanes
+    const int arow = cl < M ? cl : 0;     // clamped activation row (MFMA fragments)
     const uint32_t *qw_lane = p.qweight + (size_t)rl * N + nc;
-    const uint16_t *sc_lane = p.scales + nc;
-    const uint32_t *qz_lane = kSym ? nullptr : p.qzeros + nc / 8;
     const uint16_t *a_lane = p.A + (size_t)arow * K + rl * 8;
 
-    auto load_slot = [&](int t) {
-        Slot s;
-        s.w = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)t * 4 * N);
-        const int gi = t / spg;
-        s.s = *reinterpret_cast<const uint2 *>(sc_lane + (size_t)gi * N);
-        s.z = kSym ? 0u : qz_lane[(size_t)gi * (N / 8)];
-        if (!kLdsA) s.a = *reinterpret_cast<const uint4 *>(a_lane + (size_t)t * kStepK);
-        return s;
-    };
-
-    // ---- the weight stream starts first ---------------------------------------------------
-    Slot ring[kPf];
-#pragma unroll
-    for (int u = 0; u < kPf; ++u) ring[u] = load_slot(min(wb + u, we - 1));
-
-    // ---- per-row exponent of the activations over this wave's K range --------------------
     const int nwr = (we - wb) * 4;   // packed word rows in the wave's range
-    const int items = M * nwr;       // 8-value activation items
+    const int items = M * nwr;       // 16-byte activation items, item = word row * M + row
+    int pre_loads = 0;               // vector memory operations issued before the ring
+
+    // ---- 1. small operands straight into LDS ------------------------------------------------
+    if (kLdsA) {
+        for (int b = 0; b < items; b += 64) {
+            int it = b + lane;
+            if (it >= items) it = items - 1;
+            const int wr = it / M;
+            const int m = it - wr * M;
+            load_to_lds16(p.A + (size_t)m * K + (size_t)(wb * 4 + wr) * 8, a_lds + b);
+            ++pre_loads;
+        }
+    }
+    {   // scales: 8 lanes x 8 columns per group
+        const int sitems = ng * 8;
+        for (int b = 0; b < sitems; b += 64) {
+            int it = b + lane;
+            if (it >= sitems) it = sitems - 1;
+            const int gi = g0 + it / 8;
+            int c = tile * kTileN + (it & 7) * 8;
+            if (c >= N) c = 0;
+            load_to_lds16(p.scales + (size_t)gi * N + c, sc_lds + (size_t)b * 8);
+            ++pre_loads;
+        }
+    }
+    if (!kSym) {   // zero words: 8 per group (64 columns)
+        const int zitems = ng * 8;
+        for (int b = 0; b < zitems; b += 64) {
+            int it = b + lane;
+            if (it >= zitems) it = zitems - 1;
+            const int gi = g0 + it / 8;
+            int c = tile * kTileN + (it & 7) * 8;
+            if (c >= N) c = 0;
+            load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
+            ++pre_loads;
+        }
+    }
+
+    // ---- exponent pass for per-step conversion (many rows): loads finish before the ring ------
     if (lane < 16) shift_lds[lane] = 0;
-    for (int it = lane; it < items; it += 64) {
-        const int m = it / nwr;
-        const int wr = it - m * nwr;
-        const uint4 raw = *reinterpret_cast<const uint4 *>(p.A + (size_t)m * K + (size_t)(wb * 4 + wr) * 8);
-        const uint32_t e = max_exp8(raw);
-        if (e) atomicMax(&shift_lds[m], (int)e);
+    if (!kLdsA) {
+        constexpr int kBatch = 8;
+        for (int b = 0; b < items; b += 64 * kBatch) {
+            uint4 raw[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                int it = b + u * 64 + lane;
+                if (it >= items) it = items - 1;
+                const int wr = it / M;
+                const int m = it - wr * M;
+                raw[u] = *reinterpret_cast<const uint4 *>(p.A + (size_t)m * K + (size_t)(wb * 4 + wr) * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int it = b + u * 64 + lane;
+                if (it < items) {
+                    const int wr = it / M;
+                    const uint32_t e = max_exp8(raw[u]);
+                    if (e) atomicMax(&shift_lds[it - wr * M], (int)e);
+                }
+            }
+        }
+    }
+    asm volatile("" ::: "memory");
+
+    // ---- 2. the weight ring -------------------------------------------------------------------
+    uint4 ring_w[kPf];
+    uint4 ring_a[kLdsA ? 1 : kPf];
+#pragma unroll
+    for (int u = 0; u < kPf; ++u) {
+        const int t = min(wb + u, we - 1);
+        ring_w[u] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)t * 4 * N);
+        if (!kLdsA) ring_a[u] = *reinterpret_cast<const uint4 *>(a_lane + (size_t)t * kStepK);
+    }
+    asm volatile("" ::: "memory");
+
+    // ---- 3./4. wait for the LDS operands only, convert activations in place ---------------------
+    if (pre_loads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLdsA ? kPf : 2 * kPf));
+    asm volatile("" ::: "memory");
+    if (kLdsA) {
+        for (int it = lane; it < items; it += 64) {
+            const int wr = it / M;
+            const uint32_t e = max_exp8(a_lds[it]);
+            if (e) atomicMax(&shift_lds[it - wr * M], (int)e);
+        }
     }
     if (lane < 16) shift_lds[lane] = act_shift((uint32_t)shift_lds[lane]);
     if (kLdsA) {
         for (int it = lane; it < items; it += 64) {
-            const int m = it / nwr;
-            const int wr = it - m * nwr;
-            const uint4 raw = *reinterpret_cast<const uint4 *>(p.A + (size_t)m * K + (size_t)(wb * 4 + wr) * 8);
-            a_lds[wr * M + m] = act8_to_slots(raw, pow2_neg(shift_lds[m]));
+            const int wr = it / M;
+            const uint4 raw = a_lds[it];
+            a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(raw, pow2_neg(shift_lds[it - wr * M])));
         }
     }
     const float a_mul = pow2_neg(shift_lds[arow]);   // per-step conversion of this lane's row
@@ -129,7 +210,6 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
         tot[j] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-
     ZeroSub zs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) zs[j] = zero_sub_sym();
@@ -140,29 +220,28 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         for (int u = 0; u < kPf; ++u) {
             const int t = t0 + u;
             if (t < we) {
-                const Slot &cur = ring[u];
+                const int gi = t / spg;
                 half8_t a;
                 if (kLdsA) {
                     const int wrow = (t - wb) * 4 + rl;
                     if (kMfma) {
                         a = zero8;
-                        if (cl < M) a = a_lds[wrow * M + cl];
+                        if (cl < M) a = __builtin_bit_cast(half8_t, a_lds[wrow * M + cl]);
                     } else {
-                        a = a_lds[wrow];
+                        a = __builtin_bit_cast(half8_t, a_lds[wrow]);
                     }
                 } else {
-                    a = act8_to_slots(cur.a, a_mul);
+                    a = act8_to_slots(ring_a[u], a_mul);
                     if (cl >= M) a = zero8;
                 }
-                if (!kSym) {   // zero points change once per group (uniform branch)
-                    const int gi = t / spg;
-                    if (gi != zs_group) {
-                        zs_group = gi;
+                if (!kSym && gi != zs_group) {   // zero points change once per group (uniform)
+                    zs_group = gi;
+                    const uint32_t zw = z_lds[(gi - g0) * 8 + cl / 2];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(cur.z, (uint32_t)(nc + j)));
-                    }
+                    for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
                 }
-                const uint32_t words[4] = {cur.w.x, cur.w.y, cur.w.z, cur.w.w};
+                const uint4 wv = ring_w[u];
+                const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const half8_t b = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
@@ -178,8 +257,9 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
                     }
                 }
                 if (((t + 1) % spg == 0) || (t + 1 == we)) {
-                    const float s4[4] = {half_bits_to_float(cur.s.x & 0xFFFFu), half_bits_to_float(cur.s.x >> 16),
-                                         half_bits_to_float(cur.s.y & 0xFFFFu), half_bits_to_float(cur.s.y >> 16)};
+                    const uint2 sc = *reinterpret_cast<const uint2 *>(sc_lds + (gi - g0) * kTileN + cl * 4);
+                    const float s4[4] = {half_bits_to_float(sc.x & 0xFFFFu), half_bits_to_float(sc.x >> 16),
+                                         half_bits_to_float(sc.y & 0xFFFFu), half_bits_to_float(sc.y >> 16)};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if (kMfma) {
@@ -193,7 +273,9 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
                     }
                 }
             }
-            ring[u] = load_slot(min(t + kPf, we - 1));
+            const int tn = min(t + kPf, we - 1);
+            ring_w[u] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)tn * 4 * N);
+            if (!kLdsA) ring_a[u] = *reinterpret_cast<const uint4 *>(a_lane + (size_t)tn * kStepK);
         }
     }
 
@@ -247,34 +329,19 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     }
 
     // ---- cross-wave reduction in LDS, in wave order ---------------------------------------
-    float *red = reinterpret_cast<float *>(region);   // [kWK][M][64]; the staged activations are dead
-    if (kWK > 1) {
-        __syncthreads();
-        if (holder) {
+    float *red = reinterpret_cast<float *>(region);   // [kWK][M][64] over the dead staging areas
+    __syncthreads();
+    if (holder) {
 #pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                const int m = row_base + r;
-                if (m < M) {
-                    float *dst = red + ((size_t)wave * M + m) * kTileN + cl * 4;
-                    *reinterpret_cast<float4_t *>(dst) = float4_t{tot[0][r], tot[1][r], tot[2][r], tot[3][r]};
-                }
+        for (int r = 0; r < kRows; ++r) {
+            const int m = row_base + r;
+            if (m < M) {
+                float *dst = red + ((size_t)wave * M + m) * kTileN + cl * 4;
+                *reinterpret_cast<float4_t *>(dst) = float4_t{tot[0][r], tot[1][r], tot[2][r], tot[3][r]};
             }
         }
-        __syncthreads();
-    } else {
-        // one wave: stage its sums the same way so the split-K path below has one layout
-        if (holder) {
-#pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                const int m = row_base + r;
-                if (m < M) {
-                    float *dst = red + (size_t)m * kTileN + cl * 4;
-                    *reinterpret_cast<float4_t *>(dst) = float4_t{tot[0][r], tot[1][r], tot[2][r], tot[3][r]};
-                }
-            }
-        }
-        __syncthreads();
     }
+    __syncthreads();
     constexpr int kThreads = kWK * 64;
     for (int idx = tid; idx < M * kTileN; idx += kThreads) {
         const int m = idx / kTileN;
@@ -318,11 +385,10 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kPf = 4;
-
 template <bool kMfma, bool kSym, bool kLdsA, int kWK>
 hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
+    constexpr int kPf = kLdsA ? kRingStaged : kRingConvert;
     const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf>;
     if (plan.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

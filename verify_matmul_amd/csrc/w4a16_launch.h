@@ -16,6 +16,12 @@ constexpr int kMaxLds = 160 * 1024 - 256;
 // about 8 waves per CU resident).
 constexpr int kLdsStageBudget = 16 * 1024;
 
+// Ring depth (steps of packed weights in flight per wave): deeper when activations are staged
+// in LDS (a slot is one 16-byte load), shallower when each slot also carries an activation
+// fragment.
+constexpr int kRingStaged = 16;
+constexpr int kRingConvert = 8;
+
 struct GemmArgs {
     const uint16_t *A;
     const uint32_t *qweight;
@@ -27,7 +33,9 @@ struct GemmArgs {
     int M, N, K, g;
     int splits;               // workgroups along K per column tile
     int out_bf16;
-    int a_stride;             // staged activations per wave, in 16-byte units
+    int wave_lds;             // LDS bytes of one wave's staging area
+    int scale_off;            // offset of the scales within a wave's area
+    int zero_off;             // offset of the zero words within a wave's area
 };
 
 // How one call is launched.
@@ -37,7 +45,7 @@ struct GemmPlan {
     int wk;        // waves per workgroup, each a contiguous K range (1, 2, 4, 8 or 16)
     int splits;    // workgroups per column tile, reduced through the scratch buffer
     size_t lds;    // dynamic LDS bytes per workgroup
-    int a_stride;  // see GemmArgs
+    int wave_lds, scale_off, zero_off;
 };
 
 // Steps (of kStepK rows) of the largest K range a single wave gets under a plan.
@@ -48,16 +56,29 @@ inline int max_wave_steps(int K, int splits, int wk)
     return (per_split + wk - 1) / wk;
 }
 
-// Dynamic LDS of a plan: per-wave row exponents, then either the staged activations or the
-// cross-wave reduction buffer (the two never live at the same time).
-inline size_t gemm_lds_bytes(int M, int K, int splits, int wk, bool lds_a, int *a_stride)
+inline size_t round_up_sz(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// LDS layout of a plan: per-wave row shifts, then one staging area per wave (activations if
+// staged, the scales and the zero words of the wave's groups; each filled by whole 64-lane
+// direct loads), and, after the main loop, the cross-wave reduction buffer over the same bytes.
+inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, bool lds_a, bool sym, GemmPlan *pl)
 {
+    const int ws = max_wave_steps(K, splits, wk);
+    const int spg = g / kStepK;
+    const size_t groups = (size_t)(ws + spg - 1) / spg + 1;
+    const size_t a_bytes = lds_a ? round_up_sz((size_t)M * ws * 4, 64) * 16 : 0;
+    const size_t s_bytes = round_up_sz(groups * 8, 64) * 16;
+    const size_t z_bytes = sym ? 0 : round_up_sz(groups * 8, 64) * 4;
+    const size_t wave = a_bytes + s_bytes + z_bytes;
     const size_t header = (size_t)wk * 16 * sizeof(int);
-    const size_t stride = lds_a ? (size_t)max_wave_steps(K, splits, wk) * 4 * M : 0;   // 16-byte units
-    if (a_stride) *a_stride = (int)stride;
-    const size_t staged = (size_t)wk * stride * 16;
     const size_t red = (wk > 1 || splits > 1) ? (size_t)wk * M * kTileN * sizeof(float) : 0;
-    return header + (staged > red ? staged : red);
+    const size_t body = (size_t)wk * wave > red ? (size_t)wk * wave : red;
+    if (pl) {
+        pl->wave_lds = (int)wave;
+        pl->scale_off = (int)a_bytes;
+        pl->zero_off = (int)(a_bytes + s_bytes);
+    }
+    return header + body;
 }
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream);
