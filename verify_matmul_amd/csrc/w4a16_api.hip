@@ -99,27 +99,31 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
     return W4A16_OK;
 }
 
-int pow2_floor(int x)
-{
-    int p = 1;
-    while (p * 2 <= x) p *= 2;
-    return p;
-}
-
-// The launch plan of a shape. Goals, in order: (1) enough waves in flight to cover HBM latency
-// on 256 CUs (about 2-3 thousand), (2) a column tile per workgroup when there are enough tiles,
-// so no partial sum leaves the CU, (3) split K across workgroups only for narrow matrices.
-// `splits` / `wk` > 0 override the choice (tuning and tests).
+// The launch plan of a shape. Measured on MI355X, the weights stream best from many short
+// waves (5-20 K steps each) with a shallow ring, 4-16 thousand waves in all: they keep HBM
+// busy from the first microsecond and the hardware dispatcher balances them. Each 64-column
+// tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
+// `splits` workgroups (summed through scratch). The MFMA path keeps P at 32 or below because its
+// partial sums are M rows wide. `splits` / `wk` > 0 override the choice (tuning and tests).
 int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan *plan)
 {
     const int steps = K / kStepK;
     const int tiles = (N + kTileN - 1) / kTileN;
-    const int kTargetWaves = 2560;
-    if (splits == 0) splits = tiles >= 256 ? 1 : std::min(steps, (320 + tiles - 1) / tiles);
-    if (wk == 0) {
-        wk = pow2_floor(std::max(1, kTargetWaves / (tiles * splits)));
-        if (wk > 8) wk = 8;
-        while (wk > 1 && splits * wk > steps) wk /= 2;
+    if (splits == 0 || wk == 0) {
+        int P, w, s;
+        if (M == 1) {
+            P = std::max(8, std::min(steps / 8, (4352 + tiles - 1) / tiles));
+            w = P >= 16 ? 4 : std::min(8, P);
+            s = (P + w - 1) / w;
+        } else {
+            P = std::max(8, std::min(std::min(32, steps / 5), (8192 + tiles - 1) / tiles));
+            w = 8;
+            s = (P + w - 1) / w;
+        }
+        while (w > 1 && w > steps) w /= 2;
+        s = std::max(1, std::min(s, steps / w));
+        if (wk == 0) wk = w;
+        if (splits == 0) splits = std::max(1, std::min(s, steps / wk));
     }
     if (wk != 1 && wk != 2 && wk != 4 && wk != 8 && wk != 16)
         return fail(W4A16_ERR_INVALID_ARG, "waves_k=%d is not 1, 2, 4, 8 or 16", wk);

@@ -16,11 +16,12 @@ constexpr int kMaxLds = 160 * 1024 - 256;
 // about 8 waves per CU resident).
 constexpr int kLdsStageBudget = 16 * 1024;
 
-// Ring depth (steps of packed weights in flight per wave): deeper when activations are staged
-// in LDS (a slot is one 16-byte load), shallower when each slot also carries an activation
-// fragment.
-constexpr int kRingStaged = 16;
-constexpr int kRingConvert = 8;
+// Ring depth (steps of packed weights in flight per wave). Shallow rings measure best: with
+// thousands of short waves in flight, HBM is kept busy by the number of waves, and a deep ring
+// only lengthens each wave's start. One step deeper when activations are staged in LDS (a slot
+// is one 16-byte load) than when each slot also carries an activation fragment.
+constexpr int kRingStaged = 3;
+constexpr int kRingConvert = 2;
 
 struct GemmArgs {
     const uint16_t *A;
