@@ -4,12 +4,22 @@ Default workload: the FFN up/gate projection (K=5120, N=17408, group 128, symmet
 point) swept over M = 1, 2, 4, 8, 16 rows; one step is one call at each M. Inputs are seeded
 synthetic tensors with the value distributions of an int4 GPTQ checkpoint and bf16
 activations (no checkpoint is loaded). Every call reads a different copy of the weights
-from a rotating pool far larger than the 256 MB last-level cache, so the weights stream from
-HBM as they do in decode, where each layer's weights are read once per token.
+(consecutive calls included) from a rotating pool far larger than the 256 MB last-level cache,
+so the weights stream from HBM as they do in decode, where each layer's weights are read once
+per token.
 
 Algorithmic bytes per call = qweight (K*N/2) + scales (2*K*N/g) + qzeros (K*N/(2g), if any)
 + activations (2*M*K) + outputs (4*M*N for fp32). Re-reads, padding and split-K scratch are
 not counted.
+
+Timed regions (all on the library's stream, inputs resident in HBM):
+  1. K steps back to back -> `value` (whole-step throughput, wall clock between synchronizes);
+  2. the same K steps with a HIP event pair around every launch -> `per_m` (us per call);
+  3. the step's dominant call alone, K launches back to back between one event pair ->
+     `roofline.achieved` (algorithmic bytes per launch / average launch duration).
+`roofline.traffic` is the HBM bytes per launch of that call from the committed rocprofv3 counter
+summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or null when the
+kernel sources changed since the counters were taken.
 
 Prints one JSON line (rank 0; this build runs on one GPU).
 """
@@ -48,6 +58,9 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="workgroups per column tile along K (0 = default)")
     p.add_argument("--waves-k", type=int, default=0, help="waves per workgroup along K (0 = default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate", type=int, default=0, metavar="MIB",
+                   help="only run a plain elementwise kernel (y = 2x, fp32) over MIB MiB five times: the "
+                        "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
 
@@ -70,10 +83,10 @@ def cpu_baseline(wl, inp, ms, seconds):
                       f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)"}
 
 
-def load_traffic(workload, kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it still matches the
-    kernel source; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def load_traffic(workload, M):
+    """HBM bytes per launch of the M-row call, from the committed rocprofv3 counter summary, if it
+    still matches the kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_w4a16_gemm_kernel_{workload}_M{M}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -102,6 +115,17 @@ def main():
     import torch
     import verify_matmul_amd as vm
     from verify_matmul_amd import synth
+
+    if args.calibrate:
+        n = args.calibrate * 2 ** 20 // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            torch.mul(x, 2.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "torch.mul(x, 2.0, out=y) fp32", "bytes_read": 4 * n,
+                          "bytes_written": 4 * n, "launches": 5}), flush=True)
+        return 0
 
     lib = vm.load()
     wl = synth.WORKLOADS[args.workload]
@@ -141,7 +165,10 @@ def main():
     fn = lib.w4a16_gemm_ex
 
     def step(i, evs=None):
-        for j, (M, cargs) in enumerate(calls[i % R]):
+        # every call of every step reads its own weight copy: consecutive calls never find the
+        # previous call's weights in the last-level cache
+        for j, M in enumerate(ms):
+            cargs = calls[(i * len(ms) + j) % R][j][1]
             if evs is not None:
                 evs[i][j][0].record(stream)
             rc = fn(*cargs)
@@ -154,27 +181,27 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
-           for _ in range(args.steps)]
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region 1: the steps back to back, as a decode loop issues them -> value
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g0.record(stream)
     for i in range(args.steps):
-        step(i, evs)
-    g1.record(stream)
+        step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    wall = t1 - t0
-    gpu_span = g0.elapsed_time(g1) / 1e3
+    wall = time.perf_counter() - t0
     step_bytes = sum(algorithmic_bytes(M, K, N, g, wl.symmetric) for M in ms)
     value = step_bytes * args.steps / wall / 1e9
 
+    # timed region 2: the same steps with a HIP event pair around every launch, on the stream the
+    # kernels run on -> per-row-count duration and the roofline of the dominant launch
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs)
+    torch.cuda.synchronize()
+
     per_m = {}
-    kern_time = {"gemv": 0.0, "gemm": 0.0}
-    kern_bytes = {"gemv": 0, "gemm": 0}
-    kern_launches = {"gemv": 0, "gemm": 0}
+    dom, dom_time = None, -1.0
     for j, M in enumerate(ms):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
         b = algorithmic_bytes(M, K, N, g, wl.symmetric)
@@ -185,15 +212,26 @@ def main():
                          "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b,
                          "kernel": "gemv" if kern == 0 else "mfma",
                          "splits": args.splits or spl, "waves_k": args.waves_k or wk}
-        k = "gemv" if M == 1 else "gemm"
-        kern_time[k] += float(np.sum(d))
-        kern_bytes[k] += b * args.steps
-        kern_launches[k] += args.steps
-    dom = max(kern_time, key=kern_time.get)
-    achieved = kern_bytes[dom] / kern_time[dom] / 1e3   # GB/s
+        if float(np.sum(d)) > dom_time:
+            dom, dom_time = M, float(np.sum(d))
+    # the dominant launch: the row count whose calls take the most time in a step
+    dm = per_m[str(dom)]
+
+    # timed region 3: the dominant launch alone, K times back to back (rotating weight copies)
+    # between one HIP event pair on its stream -> its average duration without the per-launch
+    # dispatch gap that a lone event pair adds
+    jd = list(ms).index(dom)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        fn(*calls[i % R][jd][1])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
+    achieved = dm["bytes"] / us_dom / 1e3   # GB/s
     traffic = load_traffic(args.workload, dom)
 
-    kernel_name = {"gemv": "w4a16_gemm_kernel<gemv>", "gemm": "w4a16_gemm_kernel<mfma>"}[dom]
     rec = {
         "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
         "value": round(value, 1),
@@ -212,12 +250,12 @@ def main():
                    "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20),
                    "launch": "default" if not (args.splits or args.waves_k) else
                    f"splits={args.splits or 'default'} waves_k={args.waves_k or 'default'}"},
-        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "launches": kern_launches[dom],
-                     "bytes_per_launch": kern_bytes[dom] // max(1, kern_launches[dom])},
+        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel ({dm['kernel']}, M={dom})", "M": dom,
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "launches": args.steps, "bytes_per_launch": dm["bytes"],
+                     "us_per_launch": round(us_dom, 3), "us_per_launch_lone_event_pair": dm["us_per_call"]},
         "per_m": per_m,
-        "gpu_span_ms_per_step": round(gpu_span / args.steps * 1e3, 4),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds)
