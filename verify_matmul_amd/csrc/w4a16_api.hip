@@ -103,8 +103,9 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
 // waves (5-20 K steps each) with a shallow ring, 4-16 thousand waves in all: they keep HBM
 // busy from the first microsecond and the hardware dispatcher balances them. Each 64-column
 // tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
-// `splits` workgroups (summed through scratch). The MFMA path keeps P at 32 or below because its
-// partial sums are M rows wide. `splits` / `wk` > 0 override the choice (tuning and tests).
+// `splits` workgroups (summed through scratch). More than 8 rows want twice the waves (shorter
+// waves keep each wave's staged activations small). `splits` / `wk` > 0 override the choice
+// (tuning and tests).
 int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan *plan)
 {
     const int steps = K / kStepK;
@@ -116,7 +117,8 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan
             w = P >= 16 ? 4 : std::min(8, P);
             s = (P + w - 1) / w;
         } else {
-            P = std::max(8, std::min(std::min(32, steps / 5), (8192 + tiles - 1) / tiles));
+            const int want_waves = M > 8 ? 8192 : 4352;
+            P = std::max(8, std::min(steps / 5, (want_waves + tiles - 1) / tiles));
             w = 8;
             s = (P + w - 1) / w;
         }
@@ -132,13 +134,14 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan
     plan->mfma = M > 1;
     plan->wk = wk;
     plan->splits = splits;
-    // Stage activations in LDS when that fits the per-wave budget (keeps ~8 waves per CU) and
-    // rows are few enough that converting them once beats converting fragments every step.
-    // The GEMV always stages.
+    // Stage activations in LDS when a wave's slice fits the per-wave budget: then they arrive by
+    // direct loads issued with the weights and are converted once. Past the budget the LDS a
+    // workgroup needs would cut the waves per CU, and converting each fragment as it streams in
+    // (after an exponent pass) measures faster. The GEMV always stages.
     GemmPlan staged{};
     const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, true, sym, &staged);
-    plan->lds_a = !plan->mfma || (M <= 8 && (size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
-                                   lds_staged <= (size_t)kMaxLds);
+    plan->lds_a = !plan->mfma || ((size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
+                                  lds_staged <= (size_t)kMaxLds);
     plan->lds = gemm_lds_layout(M, K, g, splits, wk, plan->lds_a, sym, plan);
     if (plan->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",

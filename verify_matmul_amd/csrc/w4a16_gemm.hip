@@ -371,15 +371,28 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     }
     __syncthreads();
     if (!s_last) return;
+    // Slices are fetched kBatch at a time (all loads in flight together, one round trip per
+    // batch) and added in slice order.
+    constexpr int kBatch = 16;
     for (int idx = tid; idx < M * kTileN; idx += kThreads) {
         const int m = idx / kTileN;
         const int c = idx - m * kTileN;
         const int n = tile * kTileN + c;
         if (n >= N) continue;
+        const float *col = p.partials + (size_t)m * N + n;
+        const size_t slice = (size_t)M * N;
         float v = 0.f;
-        for (int sp = 0; sp < p.splits; ++sp)
-            v += __hip_atomic_load(p.partials + ((size_t)sp * M + m) * N + n, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
+            const int cnt = min(kBatch, p.splits - sp0);
+            float part[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                part[i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (i < cnt) v += part[i];
+        }
         store_out(m, n, v);
     }
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -12,9 +12,9 @@ constexpr int kTileN = 64;
 constexpr int kStepK = 32;
 // Largest dynamic LDS a GEMM workgroup may ask for (gfx950: 160 KiB per workgroup).
 constexpr int kMaxLds = 160 * 1024 - 256;
-// Staged activations per wave beyond which converting fragments per step is preferred (keeps
-// about 8 waves per CU resident).
-constexpr int kLdsStageBudget = 16 * 1024;
+// Staged activations (plus scales and zero words) per wave beyond which converting fragments
+// per step is preferred: larger staging areas cost more waves per CU than they save.
+constexpr int kLdsStageBudget = 8 * 1024;
 
 // Ring depth (steps of packed weights in flight per wave). Shallow rings measure best: with
 // thousands of short waves in flight, HBM is kept busy by the number of waves, and a deep ring
