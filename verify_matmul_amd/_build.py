@@ -18,6 +18,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # keep a one-lane atomic a single atomic whose result is waited for where it is used (the
+    # split-K arrival count is read only at the end of the kernel), not a wave-aggregated one
+    # waited for on the spot
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

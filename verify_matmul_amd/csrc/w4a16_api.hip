@@ -36,12 +36,15 @@ int hip_fail(hipError_t e, const char *what)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- per-(device, stream) scratch -------------------------------------------------------------
-// Layout of one scratch block: [counters: uint32 x n_counters][pad to 256][partials: float ...].
-// Counters are zeroed once at allocation; every kernel that uses one leaves it at zero again.
+// One block per (device, stream): [counters: zero between calls][flags: uint64][partials: float].
+// The whole block is zeroed when it is allocated. Kernels leave every counter at zero; flags
+// keep the epoch of the call that last set them, and each split-K call takes a fresh epoch.
 struct Scratch {
     void *base = nullptr;
     size_t counter_bytes = 0;
+    size_t flag_bytes = 0;
     size_t partial_bytes = 0;
+    uint64_t epoch = 0;
 };
 
 struct Key {
@@ -58,18 +61,27 @@ std::map<Key, Scratch> g_scratch;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Returns W4A16_OK and fills counters/partials with pointers into a block of at least the
-// requested sizes, allocating or growing the stream's block when needed.
-int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, uint32_t **counters,
-                float **partials)
+struct ScratchView {
+    uint32_t *counters;
+    uint64_t *flags;
+    float *partials;
+    uint64_t epoch;   // a value no earlier call on this stream has used (0 if not asked for)
+};
+
+// Returns W4A16_OK and fills `view` with pointers into a block of at least the requested sizes,
+// allocating or growing the stream's block when needed. `new_epoch` takes a fresh epoch.
+int get_scratch(hipStream_t stream, size_t counter_bytes, size_t flag_bytes, size_t partial_bytes, bool new_epoch,
+                ScratchView *view)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch &s = g_scratch[Key{dev, stream}];
-    if (s.base == nullptr || s.counter_bytes < counter_bytes || s.partial_bytes < partial_bytes) {
+    if (s.base == nullptr || s.counter_bytes < counter_bytes || s.flag_bytes < flag_bytes ||
+        s.partial_bytes < partial_bytes) {
         const size_t cb = round_up(std::max(counter_bytes, std::max(s.counter_bytes, (size_t)4096)), 256);
+        const size_t fb = round_up(std::max(flag_bytes, s.flag_bytes), 256);
         const size_t pb = round_up(std::max(partial_bytes, s.partial_bytes), 256);
         if (s.base) {
             // the old block may still be in use by earlier work on this stream
@@ -80,22 +92,27 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
             if (e != hipSuccess) return hip_fail(e, "hipFree");
         }
         void *p = nullptr;
-        e = hipMalloc(&p, cb + pb);
+        e = hipMalloc(&p, cb + fb + pb);
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", cb + pb, hipGetErrorString(e));
+            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", cb + fb + pb,
+                        hipGetErrorString(e));
         }
-        e = hipMemsetAsync(p, 0, cb, stream);
+        e = hipMemsetAsync(p, 0, cb + fb + pb, stream);
         if (e != hipSuccess) {
             (void)hipFree(p);
             return hip_fail(e, "hipMemsetAsync");
         }
         s.base = p;
         s.counter_bytes = cb;
+        s.flag_bytes = fb;
         s.partial_bytes = pb;
     }
-    *counters = static_cast<uint32_t *>(s.base);
-    *partials = reinterpret_cast<float *>(static_cast<char *>(s.base) + s.counter_bytes);
+    char *b = static_cast<char *>(s.base);
+    view->counters = reinterpret_cast<uint32_t *>(b);
+    view->flags = reinterpret_cast<uint64_t *>(b + s.counter_bytes);
+    view->partials = reinterpret_cast<float *>(b + s.counter_bytes + s.flag_bytes);
+    view->epoch = new_epoch ? ++s.epoch : 0;
     return W4A16_OK;
 }
 
@@ -202,9 +219,14 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     a.zero_off = plan.zero_off;
     if (plan.splits > 1) {
         const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
-        rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)plan.splits * M * N * sizeof(float),
-                         &a.counters, &a.partials);
+        ScratchView v{};
+        rc = get_scratch(stream, tiles * sizeof(uint32_t), tiles * plan.splits * sizeof(uint64_t),
+                         (size_t)plan.splits * M * N * sizeof(float), true, &v);
         if (rc != W4A16_OK) return rc;
+        a.counters = v.counters;
+        a.flags = v.flags;
+        a.partials = v.partials;
+        a.epoch = v.epoch;
     }
     const hipError_t e = launch_gemm(a, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
@@ -241,12 +263,12 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
     a.M = M;
     a.N = N;
     a.chunks = (int)(((long long)N + kArgmaxChunk - 1) / kArgmaxChunk);
-    uint32_t *ctr = nullptr;
-    float *part = nullptr;
     // counters: M uint32 counters followed by M 64-bit keys, all zero between calls
     const size_t need = round_up((size_t)M * 4, 8) + (size_t)M * 8;
-    int rc = get_scratch(stream, need, 0, &ctr, &part);
+    ScratchView v{};
+    int rc = get_scratch(stream, need, 0, 0, false, &v);
     if (rc != W4A16_OK) return rc;
+    uint32_t *ctr = v.counters;
     a.counters = ctr;
     a.keys = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ctr) + round_up((size_t)M * 4, 8));
     const hipError_t e = launch_argmax(a, stream);

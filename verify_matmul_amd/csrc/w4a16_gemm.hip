@@ -41,6 +41,8 @@
 // faster from register budgeting and from splitting work over more threads): every
 // configuration is bound by streaming the packed weights from HBM, so the VALU work is only
 // the exact dequantisation and the weight loads stay in flight from the first instructions on.
+#include <type_traits>
+
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -52,14 +54,25 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt encoding (gfx9): wait until at most `n` vector memory operations are outstanding.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// Direct global->LDS loads: lane i's 16 (or 4) bytes land at lds_base + 16 i (4 i). They are
+// written as inline assembly on purpose. Had the compiler seen these LDS writes, it would guard
+// every LDS read that follows any later global load with a full vmcnt(0) wait -- one per
+// iteration of the main loop, draining the weight ring. The kernel instead waits for them
+// itself, once, with an explicit vmcnt before the staged data is first read. (Vector-memory
+// operations the compiler cannot see only make its own wait counts stricter, never looser.)
+__device__ __forceinline__ uint32_t lds_offset(void *lds_base)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)(lds_base));
+}
+
 __device__ __forceinline__ void load_to_lds16(const void *src, void *lds_base)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds_base), 16, 0, 0);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_offset(lds_base)) : "memory");
 }
 
 __device__ __forceinline__ void load_to_lds4(const void *src, void *lds_base)
 {
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds_base), 4, 0, 0);
+    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_offset(lds_base)) : "memory");
 }
 
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf>
@@ -67,6 +80,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last;
+    __shared__ int s_timeout;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -79,6 +93,11 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     const int spg = p.g / kStepK;   // steps per quantisation group
     const int tile = blockIdx.x;
     const int split = blockIdx.y;
+    // Split-K: count this workgroup in at the start; the answer is needed only at the end, and
+    // the workgroup that starts last becomes the one that adds the slices.
+    uint32_t arrival = 0;
+    if (p.splits > 1 && tid == 0)
+        arrival = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int steps = K / kStepK;
     const int sb = (int)((long long)split * steps / p.splits);
     const int se = (int)((long long)(split + 1) * steps / p.splits);
@@ -215,69 +234,80 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     for (int j = 0; j < 4; ++j) zs[j] = zero_sub_sym();
     int zs_group = -1;
 
-    for (int t0 = wb; t0 < we; t0 += kPf) {
+    // One step: dequantise the ring slot's words, multiply, and scale at a group's end.
+    auto step = [&](int t, const uint4 wv, const uint4 av) {
+        const int gi = t / spg;
+        half8_t a;
+        if (kLdsA) {
+            const int wrow = (t - wb) * 4 + rl;
+            if (kMfma) {
+                a = zero8;
+                if (cl < M) a = __builtin_bit_cast(half8_t, a_lds[wrow * M + cl]);
+            } else {
+                a = __builtin_bit_cast(half8_t, a_lds[wrow]);
+            }
+        } else {
+            a = act8_to_slots(av, a_mul);
+            if (cl >= M) a = zero8;
+        }
+        if (!kSym && gi != zs_group) {   // zero points change once per group (uniform)
+            zs_group = gi;
+            const uint32_t zw = z_lds[(gi - g0) * 8 + cl / 2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
+        }
+        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const half8_t b = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
+            if (kMfma) {
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+            } else {
+                float s = acc[j][0];
+                s = __builtin_amdgcn_fdot2(b.lo.lo, a.lo.lo, s, false);
+                s = __builtin_amdgcn_fdot2(b.lo.hi, a.lo.hi, s, false);
+                s = __builtin_amdgcn_fdot2(b.hi.lo, a.hi.lo, s, false);
+                s = __builtin_amdgcn_fdot2(b.hi.hi, a.hi.hi, s, false);
+                acc[j][0] = s;
+            }
+        }
+        if (((t + 1) % spg == 0) || (t + 1 == we)) {
+            const uint2 sc = *reinterpret_cast<const uint2 *>(sc_lds + (gi - g0) * kTileN + cl * 4);
+            const float s4[4] = {half_bits_to_float(sc.x & 0xFFFFu), half_bits_to_float(sc.x >> 16),
+                                 half_bits_to_float(sc.y & 0xFFFFu), half_bits_to_float(sc.y >> 16)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (kMfma) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tot[j][r] = __builtin_fmaf(acc[j][r], s4[j], tot[j][r]);
+                    acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    tot[j][0] = __builtin_fmaf(acc[j][0], s4[j], tot[j][0]);
+                    acc[j][0] = 0.f;
+                }
+            }
+        }
+    };
+
+    // Whole rounds of the ring: every step computes and reissues its slot unconditionally, so
+    // the compiler's wait before each step covers exactly that slot (a skipped step would leave
+    // a load in flight into the registers being reloaded and force a full wait).
+    const int full_end = wb + (we - wb) / kPf * kPf;
+    int t0 = wb;
+    for (; t0 < full_end; t0 += kPf) {
 #pragma unroll
         for (int u = 0; u < kPf; ++u) {
             const int t = t0 + u;
-            if (t < we) {
-                const int gi = t / spg;
-                half8_t a;
-                if (kLdsA) {
-                    const int wrow = (t - wb) * 4 + rl;
-                    if (kMfma) {
-                        a = zero8;
-                        if (cl < M) a = __builtin_bit_cast(half8_t, a_lds[wrow * M + cl]);
-                    } else {
-                        a = __builtin_bit_cast(half8_t, a_lds[wrow]);
-                    }
-                } else {
-                    a = act8_to_slots(ring_a[u], a_mul);
-                    if (cl >= M) a = zero8;
-                }
-                if (!kSym && gi != zs_group) {   // zero points change once per group (uniform)
-                    zs_group = gi;
-                    const uint32_t zw = z_lds[(gi - g0) * 8 + cl / 2];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
-                }
-                const uint4 wv = ring_w[u];
-                const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const half8_t b = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
-                    if (kMfma) {
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
-                    } else {
-                        float s = acc[j][0];
-                        s = __builtin_amdgcn_fdot2(b.lo.lo, a.lo.lo, s, false);
-                        s = __builtin_amdgcn_fdot2(b.lo.hi, a.lo.hi, s, false);
-                        s = __builtin_amdgcn_fdot2(b.hi.lo, a.hi.lo, s, false);
-                        s = __builtin_amdgcn_fdot2(b.hi.hi, a.hi.hi, s, false);
-                        acc[j][0] = s;
-                    }
-                }
-                if (((t + 1) % spg == 0) || (t + 1 == we)) {
-                    const uint2 sc = *reinterpret_cast<const uint2 *>(sc_lds + (gi - g0) * kTileN + cl * 4);
-                    const float s4[4] = {half_bits_to_float(sc.x & 0xFFFFu), half_bits_to_float(sc.x >> 16),
-                                         half_bits_to_float(sc.y & 0xFFFFu), half_bits_to_float(sc.y >> 16)};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (kMfma) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) tot[j][r] = __builtin_fmaf(acc[j][r], s4[j], tot[j][r]);
-                            acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-                        } else {
-                            tot[j][0] = __builtin_fmaf(acc[j][0], s4[j], tot[j][0]);
-                            acc[j][0] = 0.f;
-                        }
-                    }
-                }
-            }
+            step(t, ring_w[u], kLdsA ? ring_w[u] : ring_a[kLdsA ? 0 : u]);
             const int tn = min(t + kPf, we - 1);
             ring_w[u] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)tn * 4 * N);
             if (!kLdsA) ring_a[u] = *reinterpret_cast<const uint4 *>(a_lane + (size_t)tn * kStepK);
         }
     }
+    // The last (we - wb) % kPf steps are already in the ring's first slots.
+#pragma unroll
+    for (int u = 0; u + 1 < kPf; ++u)
+        if (t0 + u < we) step(t0 + u, ring_w[u], kLdsA ? ring_w[u] : ring_a[kLdsA ? 0 : u]);
 
     // ---- this wave's sums: add the word rows (GEMV), undo the activation rescale ---------------
     // GEMM: lane holds rows 4*rl + r of its 4 columns. GEMV: lanes with rl == 0 hold row 0.
@@ -341,60 +371,95 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             }
         }
     }
+    if (p.splits > 1 && tid == 0) s_last = arrival == (uint32_t)(p.splits - 1);
     __syncthreads();
     constexpr int kThreads = kWK * 64;
-    for (int idx = tid; idx < M * kTileN; idx += kThreads) {
-        const int m = idx / kTileN;
-        const int c = idx - m * kTileN;
+    auto wg_sum = [&](int m, int c) {
         float v = red[(size_t)m * kTileN + c];
 #pragma unroll
         for (int w = 1; w < kWK; ++w) v += red[((size_t)w * M + m) * kTileN + c];
-        const int n = tile * kTileN + c;
-        if (n >= N) continue;
-        if (p.splits == 1)
-            store_out(m, n, v);
-        else
-            __hip_atomic_store(p.partials + ((size_t)split * M + m) * N + n, v, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (p.splits == 1) return;
-
-    // ---- split-K across workgroups: the last to arrive adds the slices in order -------------
-    // The partials above are agent-scope atomic stores: once complete (waitcnt) they are
-    // visible to every CU, so the counter increment after the barrier publishes them.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned)(p.splits - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // Slices are fetched kBatch at a time (all loads in flight together, one round trip per
-    // batch) and added in slice order.
-    constexpr int kBatch = 16;
-    for (int idx = tid; idx < M * kTileN; idx += kThreads) {
-        const int m = idx / kTileN;
-        const int c = idx - m * kTileN;
-        const int n = tile * kTileN + c;
-        if (n >= N) continue;
-        const float *col = p.partials + (size_t)m * N + n;
-        const size_t slice = (size_t)M * N;
-        float v = 0.f;
-        for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
-            const int cnt = min(kBatch, p.splits - sp0);
-            float part[kBatch];
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i)
-                part[i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i)
-                if (i < cnt) v += part[i];
+        return v;
+    };
+    if (p.splits == 1) {
+        for (int idx = tid; idx < M * kTileN; idx += kThreads) {
+            const int m = idx / kTileN;
+            const int c = idx - m * kTileN;
+            const int n = tile * kTileN + c;
+            if (n < N) store_out(m, n, wg_sum(m, c));
         }
-        store_out(m, n, v);
+        return;
     }
+
+    // ---- split-K across workgroups ---------------------------------------------------------
+    // Every workgroup of the tile bumped the tile's counter when it started; the last one to
+    // start reduces. The others publish their slice with agent-scope atomic stores (visible to
+    // every CU once complete), wait for completion, then raise their flag to this call's
+    // epoch. The reducer waits for the flags of the other slices -- their workgroups are
+    // already running, so the wait ends -- and adds all slices in slice order.
+    uint64_t *flags = p.flags + (size_t)tile * p.splits;
+    if (!s_last) {
+        for (int idx = tid; idx < M * kTileN; idx += kThreads) {
+            const int m = idx / kTileN;
+            const int c = idx - m * kTileN;
+            const int n = tile * kTileN + c;
+            if (n < N)
+                __hip_atomic_store(p.partials + ((size_t)split * M + m) * N + n, wg_sum(m, c), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(&flags[split], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (tid == 0) s_timeout = 0;
+    __syncthreads();
+    for (int sp = tid; sp < p.splits; sp += kThreads) {
+        if (sp == split) continue;
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                s_timeout = 1;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const bool failed = s_timeout != 0;
+    // Slices are fetched a batch at a time (all loads of a batch in flight together) and added
+    // in slice order, this workgroup's own slice taken from LDS. The batch is the smallest of
+    // 4, 8 or 16 that covers the slices, so few slices do not fetch padding.
+    auto reduce = [&](auto batch_tag) {
+        constexpr int kBatch = decltype(batch_tag)::value;
+        for (int idx = tid; idx < M * kTileN; idx += kThreads) {
+            const int m = idx / kTileN;
+            const int c = idx - m * kTileN;
+            const int n = tile * kTileN + c;
+            if (n >= N) continue;
+            const float own = wg_sum(m, c);
+            const float *col = p.partials + (size_t)m * N + n;
+            const size_t slice = (size_t)M * N;
+            float v = 0.f;
+            for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
+                const int cnt = min(kBatch, p.splits - sp0);
+                float part[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    part[i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < cnt) v += sp0 + i == split ? own : part[i];
+            }
+            store_out(m, n, failed ? __builtin_nanf("") : v);
+        }
+    };
+    if (p.splits <= 4)
+        reduce(std::integral_constant<int, 4>{});
+    else if (p.splits <= 8)
+        reduce(std::integral_constant<int, 8>{});
+    else
+        reduce(std::integral_constant<int, 16>{});
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

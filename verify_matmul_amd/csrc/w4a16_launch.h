@@ -16,6 +16,11 @@ constexpr int kMaxLds = 160 * 1024 - 256;
 // per step is preferred: larger staging areas cost more waves per CU than they save.
 constexpr int kLdsStageBudget = 8 * 1024;
 
+// Bound on the split-K reducer's wait for another slice (each try sleeps about 128 cycles).
+// Only reached if a workgroup never finished, which a correct launch rules out; the outputs
+// of the tile are then NaN instead of a hang.
+constexpr uint32_t kSpinLimit = 1u << 24;
+
 // Ring depth (steps of packed weights in flight per wave). Shallow rings measure best: with
 // thousands of short waves in flight, HBM is kept busy by the number of waves, and a deep ring
 // only lengthens each wave's start. One step deeper when activations are staged in LDS (a slot
@@ -31,6 +36,8 @@ struct GemmArgs {
     void *out;
     float *partials;          // [splits, M, N] when splits > 1
     uint32_t *counters;       // one per column tile, zero between calls
+    uint64_t *flags;          // [tiles][splits] slice-ready flags (hold old epochs between calls)
+    uint64_t epoch;           // this call's flag value, never reused on a stream
     int M, N, K, g;
     int splits;               // workgroups along K per column tile
     int out_bf16;
