@@ -29,9 +29,11 @@
  *     device work was enqueued. The library never aborts and never prints: w4a16_last_error()
  *     returns a description of the last non-OK status of the calling thread.
  *   - The library owns one scratch buffer per (device, stream) for split-K partial sums and
- *     completion counters. It is allocated on the first call that needs it on that stream
- *     (and grown if a later call needs more), so warm a stream up before timing or capturing
- *     it. Calls on different streams never share scratch; calls on one stream are ordered.
+ *     tile counters. It is allocated on the first call that needs it on that stream (and grown
+ *     if a later call needs more), so warm a stream up before timing or capturing it. Calls on
+ *     different streams never share scratch; calls on one stream are ordered, and calls that
+ *     run concurrently on one stream's scratch (e.g. the same stream used from two graphs
+ *     replayed at once) are not supported.
  *   - Results are deterministic: the same inputs and launch give bit-identical outputs (the
  *     split-K partials are summed in a fixed order, never with float atomics).
  */

@@ -36,15 +36,15 @@ int hip_fail(hipError_t e, const char *what)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- per-(device, stream) scratch -------------------------------------------------------------
-// One block per (device, stream): [counters: zero between calls][flags: uint64][partials: float].
-// The whole block is zeroed when it is allocated. Kernels leave every counter at zero; flags
-// keep the epoch of the call that last set them, and each split-K call takes a fresh epoch.
+// One block per (device, stream): [counters][stamped partials]. The block is zeroed when it is
+// allocated. Kernels leave every counter at zero. Split-K partials carry the stamp of the call
+// that wrote them; each split-K call takes the next stamp, and when the 32-bit stamps run out
+// the partials are zeroed again, so an old stamp never matches a new one.
 struct Scratch {
     void *base = nullptr;
     size_t counter_bytes = 0;
-    size_t flag_bytes = 0;
     size_t partial_bytes = 0;
-    uint64_t epoch = 0;
+    uint32_t stamp = 0;
 };
 
 struct Key {
@@ -63,25 +63,21 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct ScratchView {
     uint32_t *counters;
-    uint64_t *flags;
-    float *partials;
-    uint64_t epoch;   // a value no earlier call on this stream has used (0 if not asked for)
+    uint64_t *partials;
+    uint32_t stamp;   // 0 unless a stamp was asked for
 };
 
 // Returns W4A16_OK and fills `view` with pointers into a block of at least the requested sizes,
-// allocating or growing the stream's block when needed. `new_epoch` takes a fresh epoch.
-int get_scratch(hipStream_t stream, size_t counter_bytes, size_t flag_bytes, size_t partial_bytes, bool new_epoch,
-                ScratchView *view)
+// allocating or growing the stream's block when needed. `new_stamp` takes the next stamp.
+int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, bool new_stamp, ScratchView *view)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch &s = g_scratch[Key{dev, stream}];
-    if (s.base == nullptr || s.counter_bytes < counter_bytes || s.flag_bytes < flag_bytes ||
-        s.partial_bytes < partial_bytes) {
+    if (s.base == nullptr || s.counter_bytes < counter_bytes || s.partial_bytes < partial_bytes) {
         const size_t cb = round_up(std::max(counter_bytes, std::max(s.counter_bytes, (size_t)4096)), 256);
-        const size_t fb = round_up(std::max(flag_bytes, s.flag_bytes), 256);
         const size_t pb = round_up(std::max(partial_bytes, s.partial_bytes), 256);
         if (s.base) {
             // the old block may still be in use by earlier work on this stream
@@ -92,27 +88,32 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t flag_bytes, siz
             if (e != hipSuccess) return hip_fail(e, "hipFree");
         }
         void *p = nullptr;
-        e = hipMalloc(&p, cb + fb + pb);
+        e = hipMalloc(&p, cb + pb);
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", cb + fb + pb,
-                        hipGetErrorString(e));
+            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", cb + pb, hipGetErrorString(e));
         }
-        e = hipMemsetAsync(p, 0, cb + fb + pb, stream);
+        e = hipMemsetAsync(p, 0, cb + pb, stream);
         if (e != hipSuccess) {
             (void)hipFree(p);
             return hip_fail(e, "hipMemsetAsync");
         }
         s.base = p;
         s.counter_bytes = cb;
-        s.flag_bytes = fb;
         s.partial_bytes = pb;
     }
     char *b = static_cast<char *>(s.base);
     view->counters = reinterpret_cast<uint32_t *>(b);
-    view->flags = reinterpret_cast<uint64_t *>(b + s.counter_bytes);
-    view->partials = reinterpret_cast<float *>(b + s.counter_bytes + s.flag_bytes);
-    view->epoch = new_epoch ? ++s.epoch : 0;
+    view->partials = reinterpret_cast<uint64_t *>(b + s.counter_bytes);
+    view->stamp = 0;
+    if (new_stamp) {
+        if (++s.stamp == 0) {   // every stamp used once: clear the partials and start over
+            e = hipMemsetAsync(b + s.counter_bytes, 0, s.partial_bytes, stream);
+            if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+            s.stamp = 1;
+        }
+        view->stamp = s.stamp;
+    }
     return W4A16_OK;
 }
 
@@ -120,27 +121,19 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t flag_bytes, siz
 // waves (5-20 K steps each) with a shallow ring, 4-16 thousand waves in all: they keep HBM
 // busy from the first microsecond and the hardware dispatcher balances them. Each 64-column
 // tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
-// `splits` workgroups (summed through scratch). More than 8 rows want twice the waves (shorter
-// waves keep each wave's staged activations small). `splits` / `wk` > 0 override the choice
-// (tuning and tests).
+// `splits` workgroups (summed through scratch): 4 waves per workgroup up to 32 pieces, 8 beyond
+// and for more than 8 rows (shorter waves keep their activation slice within the LDS staging
+// budget). `splits` / `wk` > 0 override the choice (tuning and tests).
 int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan *plan)
 {
     const int steps = K / kStepK;
     const int tiles = (N + kTileN - 1) / kTileN;
     if (splits == 0 || wk == 0) {
-        int P, w, s;
-        if (M == 1) {
-            P = std::max(8, std::min(steps / 8, (4352 + tiles - 1) / tiles));
-            w = P >= 16 ? 4 : std::min(8, P);
-            s = (P + w - 1) / w;
-        } else {
-            const int want_waves = M > 8 ? 8192 : 4352;
-            P = std::max(8, std::min(steps / 5, (want_waves + tiles - 1) / tiles));
-            w = 8;
-            s = (P + w - 1) / w;
-        }
+        // P pieces per tile: about 4352 waves in all, at least 8 pieces, at least 5 steps each
+        const int P = std::max(8, std::min(steps / 5, (4352 + tiles - 1) / tiles));
+        int w = P <= 8 ? P : (P < 32 && M <= 8 ? 4 : 8);   // 8 keeps 16-row slices small enough to stage
         while (w > 1 && w > steps) w /= 2;
-        s = std::max(1, std::min(s, steps / w));
+        const int s = std::max(1, std::min((P + w - 1) / w, steps / w));
         if (wk == 0) wk = w;
         if (splits == 0) splits = std::max(1, std::min(s, steps / wk));
     }
@@ -220,13 +213,12 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     if (plan.splits > 1) {
         const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
         ScratchView v{};
-        rc = get_scratch(stream, tiles * sizeof(uint32_t), tiles * plan.splits * sizeof(uint64_t),
-                         (size_t)plan.splits * M * N * sizeof(float), true, &v);
+        rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)plan.splits * M * N * sizeof(uint64_t), true,
+                         &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.counters;
-        a.flags = v.flags;
         a.partials = v.partials;
-        a.epoch = v.epoch;
+        a.stamp = v.stamp;
     }
     const hipError_t e = launch_gemm(a, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
@@ -266,7 +258,7 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
     // counters: M uint32 counters followed by M 64-bit keys, all zero between calls
     const size_t need = round_up((size_t)M * 4, 8) + (size_t)M * 8;
     ScratchView v{};
-    int rc = get_scratch(stream, need, 0, 0, false, &v);
+    int rc = get_scratch(stream, need, 0, false, &v);
     if (rc != W4A16_OK) return rc;
     uint32_t *ctr = v.counters;
     a.counters = ctr;

@@ -80,7 +80,6 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last;
-    __shared__ int s_timeout;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -392,43 +391,27 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
 
     // ---- split-K across workgroups ---------------------------------------------------------
     // Every workgroup of the tile bumped the tile's counter when it started; the last one to
-    // start reduces. The others publish their slice with agent-scope atomic stores (visible to
-    // every CU once complete), wait for completion, then raise their flag to this call's
-    // epoch. The reducer waits for the flags of the other slices -- their workgroups are
-    // already running, so the wait ends -- and adds all slices in slice order.
-    uint64_t *flags = p.flags + (size_t)tile * p.splits;
+    // start adds the slices. The others store each element of their slice as one 64-bit word,
+    // the value in the low half and this call's stamp in the high half: a single agent-scope
+    // atomic store, so value and stamp become visible together, and nothing to wait for. The
+    // reducer reads the other slices and re-reads any element whose stamp is not yet this
+    // call's (those workgroups are already running, so every wait ends), adding the slices in
+    // slice order with its own slice taken from LDS.
+    const uint64_t stamp_hi = (uint64_t)p.stamp << 32;
     if (!s_last) {
         for (int idx = tid; idx < M * kTileN; idx += kThreads) {
             const int m = idx / kTileN;
             const int c = idx - m * kTileN;
             const int n = tile * kTileN + c;
             if (n < N)
-                __hip_atomic_store(p.partials + ((size_t)split * M + m) * N + n, wg_sum(m, c), __ATOMIC_RELAXED,
+                __hip_atomic_store(p.partials + ((size_t)split * M + m) * N + n,
+                                   stamp_hi | __builtin_bit_cast(uint32_t, wg_sum(m, c)), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(&flags[split], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    if (tid == 0) s_timeout = 0;
-    __syncthreads();
-    for (int sp = tid; sp < p.splits; sp += kThreads) {
-        if (sp == split) continue;
-        uint32_t spins = 0;
-        while (__hip_atomic_load(&flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
-                s_timeout = 1;
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    const bool failed = s_timeout != 0;
-    // Slices are fetched a batch at a time (all loads of a batch in flight together) and added
-    // in slice order, this workgroup's own slice taken from LDS. The batch is the smallest of
-    // 4, 8 or 16 that covers the slices, so few slices do not fetch padding.
+    // Slices are fetched a batch at a time (all loads of a batch in flight together). The batch
+    // is the smallest of 4, 8 or 16 that covers the slices, so few slices fetch no padding.
     auto reduce = [&](auto batch_tag) {
         constexpr int kBatch = decltype(batch_tag)::value;
         for (int idx = tid; idx < M * kTileN; idx += kThreads) {
@@ -437,19 +420,37 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             const int n = tile * kTileN + c;
             if (n >= N) continue;
             const float own = wg_sum(m, c);
-            const float *col = p.partials + (size_t)m * N + n;
+            const uint64_t *col = p.partials + (size_t)m * N + n;
             const size_t slice = (size_t)M * N;
             float v = 0.f;
+            bool failed = false;
             for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
                 const int cnt = min(kBatch, p.splits - sp0);
-                float part[kBatch];
+                uint64_t part[kBatch];
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i)
                     part[i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    if (i < cnt) v += sp0 + i == split ? own : part[i];
+                for (int i = 0; i < kBatch; ++i) {
+                    if (i >= cnt) continue;
+                    const int sp = sp0 + i;
+                    if (sp == split) {
+                        v += own;
+                        continue;
+                    }
+                    uint64_t w = part[i];
+                    uint32_t spins = 0;
+                    while ((w & 0xFFFFFFFF00000000ull) != stamp_hi) {   // not yet stored in this call
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                            failed = true;
+                            break;
+                        }
+                        w = __hip_atomic_load(col + (size_t)sp * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    v += __builtin_bit_cast(float, (uint32_t)w);
+                }
             }
             store_out(m, n, failed ? __builtin_nanf("") : v);
         }

@@ -16,7 +16,8 @@ constexpr int kMaxLds = 160 * 1024 - 256;
 // per step is preferred: larger staging areas cost more waves per CU than they save.
 constexpr int kLdsStageBudget = 8 * 1024;
 
-// Bound on the split-K reducer's wait for another slice (each try sleeps about 128 cycles).
+// Bound on the split-K reducer's wait for another slice's element (each try sleeps about 128
+// cycles).
 // Only reached if a workgroup never finished, which a correct launch rules out; the outputs
 // of the tile are then NaN instead of a hang.
 constexpr uint32_t kSpinLimit = 1u << 24;
@@ -34,10 +35,9 @@ struct GemmArgs {
     const uint16_t *scales;
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
     void *out;
-    float *partials;          // [splits, M, N] when splits > 1
+    uint64_t *partials;       // [splits, M, N] stamped fp32 partial sums when splits > 1
     uint32_t *counters;       // one per column tile, zero between calls
-    uint64_t *flags;          // [tiles][splits] slice-ready flags (hold old epochs between calls)
-    uint64_t epoch;           // this call's flag value, never reused on a stream
+    uint32_t stamp;           // this call's stamp (nonzero, not used by the last 2^32 - 1 calls)
     int M, N, K, g;
     int splits;               // workgroups along K per column tile
     int out_bf16;
