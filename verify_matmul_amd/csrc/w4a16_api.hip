@@ -122,16 +122,19 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
 // busy from the first microsecond and the hardware dispatcher balances them. Each 64-column
 // tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
 // `splits` workgroups (summed through scratch): 4 waves per workgroup up to 32 pieces, 8 beyond
-// and for more than 8 rows (shorter waves keep their activation slice within the LDS staging
-// budget). `splits` / `wk` > 0 override the choice (tuning and tests).
+// and for more than 8 rows. `splits` / `wk` > 0 override the choice (tuning and tests).
 int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan *plan)
 {
     const int steps = K / kStepK;
     const int tiles = (N + kTileN - 1) / kTileN;
     if (splits == 0 || wk == 0) {
-        // P pieces per tile: about 4352 waves in all, at least 8 pieces, at least 5 steps each
-        const int P = std::max(8, std::min(steps / 5, (4352 + tiles - 1) / tiles));
-        int w = P <= 8 ? P : (P < 32 && M <= 8 ? 4 : 8);   // 8 keeps 16-row slices small enough to stage
+        // P pieces per tile: about 4352 waves in all (8192 for more than 8 rows, whose shorter
+        // pieces keep their activation slices within the LDS staging budget, at most 64 pieces
+        // there), at least 8 pieces, at least 5 steps each
+        const int want = M > 8 ? 8192 : 4352;
+        const int cap = M > 8 ? std::min(64, steps / 5) : steps / 5;
+        const int P = std::max(8, std::min(cap, (want + tiles - 1) / tiles));
+        int w = P <= 8 ? P : (P < 32 && M <= 8 ? 4 : 8);
         while (w > 1 && w > steps) w /= 2;
         const int s = std::max(1, std::min((P + w - 1) / w, steps / w));
         if (wk == 0) wk = w;
