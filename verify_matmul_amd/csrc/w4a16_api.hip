@@ -36,14 +36,14 @@ int hip_fail(hipError_t e, const char *what)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- per-(device, stream) scratch -------------------------------------------------------------
-// One block per (device, stream): [counters][stamped partials]. The block is zeroed when it is
-// allocated. Kernels leave every counter at zero. Split-K partials carry the stamp of the call
-// that wrote them; each split-K call takes the next stamp, and when the 32-bit stamps run out
-// the partials are zeroed again, so an old stamp never matches a new one.
+// One block per (device, stream): [counters][stamped partials][prepared activations]. The block
+// is zeroed when it is allocated. Kernels leave every counter at zero. Split-K partials carry
+// the stamp of the call that wrote them; each split-K call takes the next stamp, and when the
+// 32-bit stamps run out the partials are zeroed again, so an old stamp never matches a new one.
+// Prepared activations are rewritten by every matrix-core call before its GEMM reads them.
 struct Scratch {
     void *base = nullptr;
-    size_t counter_bytes = 0;
-    size_t partial_bytes = 0;
+    size_t bytes[3] = {0, 0, 0};
     uint32_t stamp = 0;
 };
 
@@ -64,21 +64,28 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct ScratchView {
     uint32_t *counters;
     uint64_t *partials;
+    void *act;
     uint32_t stamp;   // 0 unless a stamp was asked for
 };
 
-// Returns W4A16_OK and fills `view` with pointers into a block of at least the requested sizes,
-// allocating or growing the stream's block when needed. `new_stamp` takes the next stamp.
-int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, bool new_stamp, ScratchView *view)
+// Returns W4A16_OK and fills `view` with pointers into a block whose regions hold at least the
+// requested bytes, allocating or growing the stream's block when needed. `new_stamp` takes the
+// next stamp.
+int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, size_t act_bytes, bool new_stamp,
+                ScratchView *view)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch &s = g_scratch[Key{dev, stream}];
-    if (s.base == nullptr || s.counter_bytes < counter_bytes || s.partial_bytes < partial_bytes) {
-        const size_t cb = round_up(std::max(counter_bytes, std::max(s.counter_bytes, (size_t)4096)), 256);
-        const size_t pb = round_up(std::max(partial_bytes, s.partial_bytes), 256);
+    const size_t need[3] = {std::max(counter_bytes, (size_t)4096), partial_bytes, act_bytes};
+    if (s.base == nullptr || s.bytes[0] < need[0] || s.bytes[1] < need[1] || s.bytes[2] < need[2]) {
+        size_t nb[3], total = 0;
+        for (int r = 0; r < 3; ++r) {
+            nb[r] = round_up(std::max(need[r], s.bytes[r]), 256);
+            total += nb[r];
+        }
         if (s.base) {
             // the old block may still be in use by earlier work on this stream
             e = hipStreamSynchronize(stream);
@@ -88,27 +95,27 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
             if (e != hipSuccess) return hip_fail(e, "hipFree");
         }
         void *p = nullptr;
-        e = hipMalloc(&p, cb + pb);
+        e = hipMalloc(&p, total);
         if (e != hipSuccess) {
             (void)hipGetLastError();
-            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", cb + pb, hipGetErrorString(e));
+            return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", total, hipGetErrorString(e));
         }
-        e = hipMemsetAsync(p, 0, cb + pb, stream);
+        e = hipMemsetAsync(p, 0, total, stream);
         if (e != hipSuccess) {
             (void)hipFree(p);
             return hip_fail(e, "hipMemsetAsync");
         }
         s.base = p;
-        s.counter_bytes = cb;
-        s.partial_bytes = pb;
+        for (int r = 0; r < 3; ++r) s.bytes[r] = nb[r];
     }
     char *b = static_cast<char *>(s.base);
     view->counters = reinterpret_cast<uint32_t *>(b);
-    view->partials = reinterpret_cast<uint64_t *>(b + s.counter_bytes);
+    view->partials = reinterpret_cast<uint64_t *>(b + s.bytes[0]);
+    view->act = b + s.bytes[0] + s.bytes[1];
     view->stamp = 0;
     if (new_stamp) {
         if (++s.stamp == 0) {   // every stamp used once: clear the partials and start over
-            e = hipMemsetAsync(b + s.counter_bytes, 0, s.partial_bytes, stream);
+            e = hipMemsetAsync(view->partials, 0, s.bytes[1], stream);
             if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
             s.stamp = 1;
         }
@@ -155,6 +162,10 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan
     const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, true, sym, &staged);
     plan->lds_a = !plan->mfma || ((size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
                                   lds_staged <= (size_t)kMaxLds);
+    // Activations a wave cannot stage are prepared once per call by a separate kernel: without
+    // it each wave would run an exponent pass over its slice and convert every fragment as it
+    // streams in. Staged slices are converted in the wave (cheaper than the extra launch).
+    plan->prep_a = plan->mfma && !plan->lds_a;
     plan->lds = gemm_lds_layout(M, K, g, splits, wk, plan->lds_a, sym, plan);
     if (plan->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",
@@ -213,15 +224,20 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     a.wave_lds = plan.wave_lds;
     a.scale_off = plan.scale_off;
     a.zero_off = plan.zero_off;
-    if (plan.splits > 1) {
+    const bool split_k = plan.splits > 1;
+    if (split_k || plan.prep_a) {
         const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
+        const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
+        const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
-        rc = get_scratch(stream, tiles * sizeof(uint32_t), (size_t)plan.splits * M * N * sizeof(uint64_t), true,
-                         &v);
+        rc = get_scratch(stream, split_k ? tiles * sizeof(uint32_t) : 0,
+                         split_k ? (size_t)plan.splits * M * N * sizeof(uint64_t) : 0, act_bytes, split_k, &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.counters;
         a.partials = v.partials;
         a.stamp = v.stamp;
+        a.A16 = static_cast<uint16_t *>(v.act);
+        a.ashift = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
     }
     const hipError_t e = launch_gemm(a, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
@@ -261,7 +277,7 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
     // counters: M uint32 counters followed by M 64-bit keys, all zero between calls
     const size_t need = round_up((size_t)M * 4, 8) + (size_t)M * 8;
     ScratchView v{};
-    int rc = get_scratch(stream, need, 0, false, &v);
+    int rc = get_scratch(stream, need, 0, 0, false, &v);
     if (rc != W4A16_OK) return rc;
     uint32_t *ctr = v.counters;
     a.counters = ctr;

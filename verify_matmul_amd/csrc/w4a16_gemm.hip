@@ -75,9 +75,89 @@ __device__ __forceinline__ void load_to_lds4(const void *src, void *lds_base)
     asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_offset(lds_base)) : "memory");
 }
 
+// The K range [wb, we) (in steps) of piece `wave` of split `split`: splits cut K into
+// contiguous slices, the waves of a workgroup cut each slice again. The activation preparation
+// kernel and the GEMM compute the same ranges.
+__device__ __forceinline__ void piece_range(int steps, int splits, int wk, int split, int wave, int &wb, int &we)
+{
+    const int sb = (int)((long long)split * steps / splits);
+    const int se = (int)((long long)(split + 1) * steps / splits);
+    wb = sb + (int)((long long)wave * (se - sb) / wk);
+    we = sb + (int)((long long)(wave + 1) * (se - sb) / wk);
+}
+
+// Activation preparation for the matrix-core path, once per call instead of once per column
+// tile: for each K piece of the launch and each row, the largest bf16 exponent gives the
+// power-of-two rescale (see act_shift), and the piece's activations are stored as fp16 in the
+// packed-word slot order with that rescale applied. One workgroup per piece.
+constexpr int kPrepThreads = 256;
+constexpr int kPrepHeld = 4;   // granules a thread keeps in registers between the two phases
+
+__global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
+{
+    __shared__ uint32_t s_emax[16];
+    __shared__ int s_shift[16];
+    const int piece = blockIdx.x;
+    const int split = piece / p.wk;
+    const int wave = piece - split * p.wk;
+    int wb, we;
+    piece_range(p.K / kStepK, p.splits, p.wk, split, wave, wb, we);
+    const int M = p.M;
+    const int items = M * (we - wb) * 4;   // 16-byte granules, item = word row * M + row
+    auto offset = [&](int it) {
+        const int wr = it / M;
+        return (size_t)(it - wr * M) * p.K + (size_t)(wb * 4 + wr) * 8;
+    };
+    if (threadIdx.x < 16) s_emax[threadIdx.x] = 0;
+    __syncthreads();
+    // Exponents: the first kPrepHeld granules of each thread stay in registers for the
+    // conversion; a piece larger than kPrepHeld x 256 granules reads the rest twice.
+    uint4 held[kPrepHeld];
+#pragma unroll
+    for (int u = 0; u < kPrepHeld; ++u) {
+        const int it = threadIdx.x + u * kPrepThreads;
+        held[u] = *reinterpret_cast<const uint4 *>(p.A + offset(min(it, items - 1)));
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepHeld; ++u) {
+        const int it = threadIdx.x + u * kPrepThreads;
+        if (it < items) {
+            const uint32_t e = max_exp8(held[u]);
+            if (e) atomicMax(&s_emax[it % M], e);
+        }
+    }
+    for (int it = threadIdx.x + kPrepHeld * kPrepThreads; it < items; it += kPrepThreads) {
+        const uint32_t e = max_exp8(*reinterpret_cast<const uint4 *>(p.A + offset(it)));
+        if (e) atomicMax(&s_emax[it % M], e);
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        const int sh = act_shift(s_emax[threadIdx.x]);
+        s_shift[threadIdx.x] = sh;
+        p.shifts[(size_t)piece * M + threadIdx.x] = sh;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPrepHeld; ++u) {
+        const int it = threadIdx.x + u * kPrepThreads;
+        if (it < items)
+            *reinterpret_cast<uint4 *>(p.A16 + offset(it)) =
+                __builtin_bit_cast(uint4, act8_to_slots(held[u], pow2_neg(s_shift[it % M])));
+    }
+    for (int it = threadIdx.x + kPrepHeld * kPrepThreads; it < items; it += kPrepThreads) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(p.A + offset(it));
+        *reinterpret_cast<uint4 *>(p.A16 + offset(it)) =
+            __builtin_bit_cast(uint4, act8_to_slots(raw, pow2_neg(s_shift[it % M])));
+    }
+}
+
+// kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
+// slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
+// order, rescaled per piece and row -- and stream in with the weights, one fragment per step.
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf>
 __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
 {
+    constexpr bool kPreA = !kLdsA;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last;
 
@@ -98,10 +178,9 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     if (p.splits > 1 && tid == 0)
         arrival = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int steps = K / kStepK;
-    const int sb = (int)((long long)split * steps / p.splits);
-    const int se = (int)((long long)(split + 1) * steps / p.splits);
-    const int wb = sb + (int)((long long)wave * (se - sb) / kWK);
-    const int we = sb + (int)((long long)(wave + 1) * (se - sb) / kWK);   // we > wb (host)
+    int wb, we;   // we > wb (host)
+    piece_range(steps, p.splits, kWK, split, wave, wb, we);
+    const int piece = split * kWK + wave;
     const int g0 = wb / spg;                  // first group of the wave
     const int ng = (we - 1) / spg - g0 + 1;   // groups touched by the wave
 
@@ -118,7 +197,10 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     const int nc = col_ok ? n0 : 0;       // clamped column for loads of dead lanes
     const int arow = cl < M ? cl : 0;     // clamped activation row (MFMA fragments)
     const uint32_t *qw_lane = p.qweight + (size_t)rl * N + nc;
-    const uint16_t *a_lane = p.A + (size_t)arow * K + rl * 8;
+    const uint16_t *asrc = kPreA ? p.A16 : p.A;   // prepared fp16 or raw bf16
+    const uint16_t *a_lane = asrc + (size_t)arow * K + rl * 8;
+    int pre_shift = 0;   // prepared path: this piece's rescale of row `lane`
+    if (kPreA && lane < M) pre_shift = p.ashift[(size_t)piece * M + lane];
 
     const int nwr = (we - wb) * 4;   // packed word rows in the wave's range
     const int items = M * nwr;       // 16-byte activation items, item = word row * M + row
@@ -131,7 +213,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             if (it >= items) it = items - 1;
             const int wr = it / M;
             const int m = it - wr * M;
-            load_to_lds16(p.A + (size_t)m * K + (size_t)(wb * 4 + wr) * 8, a_lds + b);
+            load_to_lds16(asrc + (size_t)m * K + (size_t)(wb * 4 + wr) * 8, a_lds + b);
             ++pre_loads;
         }
     }
@@ -160,31 +242,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         }
     }
 
-    // ---- exponent pass for per-step conversion (many rows): loads finish before the ring ------
     if (lane < 16) shift_lds[lane] = 0;
-    if (!kLdsA) {
-        constexpr int kBatch = 8;
-        for (int b = 0; b < items; b += 64 * kBatch) {
-            uint4 raw[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                int it = b + u * 64 + lane;
-                if (it >= items) it = items - 1;
-                const int wr = it / M;
-                const int m = it - wr * M;
-                raw[u] = *reinterpret_cast<const uint4 *>(p.A + (size_t)m * K + (size_t)(wb * 4 + wr) * 8);
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int it = b + u * 64 + lane;
-                if (it < items) {
-                    const int wr = it / M;
-                    const uint32_t e = max_exp8(raw[u]);
-                    if (e) atomicMax(&shift_lds[it - wr * M], (int)e);
-                }
-            }
-        }
-    }
     asm volatile("" ::: "memory");
 
     // ---- 2. the weight ring -------------------------------------------------------------------
@@ -201,22 +259,21 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     // ---- 3./4. wait for the LDS operands only, convert activations in place ---------------------
     if (pre_loads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLdsA ? kPf : 2 * kPf));
     asm volatile("" ::: "memory");
-    if (kLdsA) {
+    if (kLdsA && !kPreA) {
         for (int it = lane; it < items; it += 64) {
             const int wr = it / M;
             const uint32_t e = max_exp8(a_lds[it]);
             if (e) atomicMax(&shift_lds[it - wr * M], (int)e);
         }
     }
-    if (lane < 16) shift_lds[lane] = act_shift((uint32_t)shift_lds[lane]);
-    if (kLdsA) {
+    if (lane < 16) shift_lds[lane] = kPreA ? pre_shift : act_shift((uint32_t)shift_lds[lane]);
+    if (kLdsA && !kPreA) {
         for (int it = lane; it < items; it += 64) {
             const int wr = it / M;
             const uint4 raw = a_lds[it];
             a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(raw, pow2_neg(shift_lds[it - wr * M])));
         }
     }
-    const float a_mul = pow2_neg(shift_lds[arow]);   // per-step conversion of this lane's row
 
     // ---- stream ------------------------------------------------------------------------
     const Masks mk = make_masks();
@@ -246,7 +303,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
                 a = __builtin_bit_cast(half8_t, a_lds[wrow]);
             }
         } else {
-            a = act8_to_slots(av, a_mul);
+            a = __builtin_bit_cast(half8_t, av);   // prepared fragment
             if (cl >= M) a = zero8;
         }
         if (!kSym && gi != zs_group) {   // zero points change once per group (uniform)
@@ -469,6 +526,12 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
 {
     constexpr int kPf = kLdsA ? kRingStaged : kRingConvert;
     const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf>;
+    if (!kLdsA) {
+        ActPrepArgs pa{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK};
+        hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(a.splits * kWK)), dim3(kPrepThreads), 0, stream, pa);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (plan.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
@@ -492,17 +555,19 @@ hipError_t launch_wk(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream
     }
 }
 
+template <bool kMfma, bool kLdsA>
+hipError_t launch_sym(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
+{
+    return a.qzeros == nullptr ? launch_wk<kMfma, true, kLdsA>(a, plan, stream)
+                               : launch_wk<kMfma, false, kLdsA>(a, plan, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
-    const bool sym = a.qzeros == nullptr;
-    if (!plan.mfma) {   // GEMV: one row, activations always staged
-        return sym ? launch_wk<false, true, true>(a, plan, stream) : launch_wk<false, false, true>(a, plan, stream);
-    }
-    if (plan.lds_a)
-        return sym ? launch_wk<true, true, true>(a, plan, stream) : launch_wk<true, false, true>(a, plan, stream);
-    return sym ? launch_wk<true, true, false>(a, plan, stream) : launch_wk<true, false, false>(a, plan, stream);
+    if (!plan.mfma) return launch_sym<false, true>(a, plan, stream);   // GEMV: always staged
+    return plan.lds_a ? launch_sym<true, true>(a, plan, stream) : launch_sym<true, false>(a, plan, stream);
 }
 
 }  // namespace w4a16

@@ -35,6 +35,8 @@ struct GemmArgs {
     const uint16_t *scales;
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
     void *out;
+    uint16_t *A16;            // [M, K] prepared activations (matrix-core path)
+    int *ashift;              // [splits * waves_k, M] their rescale per K piece and row
     uint64_t *partials;       // [splits, M, N] stamped fp32 partial sums when splits > 1
     uint32_t *counters;       // one per column tile, zero between calls
     uint32_t stamp;           // this call's stamp (nonzero, not used by the last 2^32 - 1 calls)
@@ -50,6 +52,7 @@ struct GemmArgs {
 struct GemmPlan {
     bool mfma;     // false: the M = 1 dot-product GEMV
     bool lds_a;    // activations staged once per wave in LDS (else converted per step)
+    bool prep_a;   // activations prepared once per call by act_prep_kernel (matrix-core path)
     int wk;        // waves per workgroup, each a contiguous K range (1, 2, 4, 8 or 16)
     int splits;    // workgroups per column tile, reduced through the scratch buffer
     size_t lds;    // dynamic LDS bytes per workgroup
@@ -88,6 +91,14 @@ inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, bool lds_
     }
     return header + body;
 }
+
+// Activation preparation (matrix-core path): one workgroup per K piece of the launch.
+struct ActPrepArgs {
+    const uint16_t *A;
+    uint16_t *A16;
+    int *shifts;
+    int M, K, splits, wk;
+};
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream);
 
