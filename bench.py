@@ -217,6 +217,24 @@ def main():
     # the dominant launch: the row count whose calls take the most time in a step
     dm = per_m[str(dom)]
 
+    # output layer: the greedy pick over each row of logits, timed on its own (it re-reads the
+    # logits; not part of the algorithmic bytes of the matmul)
+    if wl.argmax:
+        for j, M in enumerate(ms):
+            logits = pool[0][4][M]
+            idx = torch.empty((M,), dtype=torch.int32, device=dev)
+            vm.w4a16_argmax_rows(logits, idx)
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(args.steps):
+                vm.w4a16_argmax_rows(logits, idx)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            us = a0.elapsed_time(a1) * 1e3 / args.steps
+            per_m[str(M)]["argmax_us_per_call"] = round(us, 3)
+            per_m[str(M)]["argmax_GBps"] = round(4 * M * N / us / 1e3, 1)
+
     # timed region 3: the dominant launch alone, K times back to back (rotating weight copies)
     # between one HIP event pair on its stream -> its average duration without the per-launch
     # dispatch gap that a lone event pair adds

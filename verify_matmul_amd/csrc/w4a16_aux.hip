@@ -27,11 +27,17 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 }
 
 constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxPerThread = kArgmaxChunk / kArgmaxThreads;   // 16 logits
+static_assert(kArgmaxPerThread % 4 == 0, "whole 16-byte loads per thread");
 
+// One workgroup per chunk of a row: every logit of the chunk is loaded at once (16-byte loads
+// when rows are 16-byte aligned), reduced to one key in the workgroup, and merged into the
+// row's key with an atomic max. The atomic completes (waitcnt) before the chunk is counted in,
+// so the last chunk of the row, which takes the key and resets the row's scratch, sees every
+// other chunk's maximum.
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows_kernel(ArgmaxArgs p)
 {
     __shared__ unsigned long long s_key[kArgmaxThreads / 64];
-    __shared__ int s_last;
     const int m = blockIdx.y;
     const int chunk = blockIdx.x;
     const float *row = p.logits + (size_t)m * p.N;
@@ -39,11 +45,36 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows_kernel(ArgmaxArgs 
     const long long end = min((long long)p.N, begin + kArgmaxChunk);
 
     unsigned long long best = 0;   // 0 = nothing seen (every real key has a nonzero high word)
-    for (long long n = begin + threadIdx.x; n < end; n += kArgmaxThreads) {
-        const float v = row[n];
-        if (v != v) continue;   // NaN
-        const unsigned long long k = argmax_key(v, (uint32_t)n);
-        best = k > best ? k : best;
+    auto consider = [&](float v, long long n) {
+        if (n < end && v == v) {   // NaN never wins
+            const unsigned long long k = argmax_key(v, (uint32_t)n);
+            best = k > best ? k : best;
+        }
+    };
+    if ((p.N & 3) == 0) {
+        float4 v[kArgmaxPerThread / 4];
+#pragma unroll
+        for (int u = 0; u < kArgmaxPerThread / 4; ++u) {
+            const long long n = begin + ((long long)u * kArgmaxThreads + threadIdx.x) * 4;
+            v[u] = n < end ? *reinterpret_cast<const float4 *>(row + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kArgmaxPerThread / 4; ++u) {
+            const long long n = begin + ((long long)u * kArgmaxThreads + threadIdx.x) * 4;
+            consider(v[u].x, n);
+            consider(v[u].y, n + 1);
+            consider(v[u].z, n + 2);
+            consider(v[u].w, n + 3);
+        }
+    } else {
+        float v[kArgmaxPerThread];
+#pragma unroll
+        for (int u = 0; u < kArgmaxPerThread; ++u) {
+            const long long n = begin + (long long)u * kArgmaxThreads + threadIdx.x;
+            v[u] = n < end ? row[n] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kArgmaxPerThread; ++u) consider(v[u], begin + (long long)u * kArgmaxThreads + threadIdx.x);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -54,18 +85,15 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows_kernel(ArgmaxArgs 
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int w = 1; w < kArgmaxThreads / 64; ++w) best = s_key[w] > best ? s_key[w] : best;
-        if (best) atomicMax(&p.keys[m], best);
-        __threadfence();
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[m], 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned)(p.chunks - 1);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && s_last) {
-        __threadfence();
-        const unsigned long long k = atomicExch(&p.keys[m], 0ull);
-        p.idx[m] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
-        __hip_atomic_store(&p.counters[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (best) __hip_atomic_fetch_max(&p.keys[m], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // the max is performed before this chunk counts in
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == (unsigned)(p.chunks - 1)) {
+            const unsigned long long k =
+                __hip_atomic_exchange(&p.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            p.idx[m] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
+            __hip_atomic_store(&p.counters[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

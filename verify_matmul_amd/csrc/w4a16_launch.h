@@ -111,7 +111,7 @@ struct ArgmaxArgs {
     int chunks;                 // workgroups per row
 };
 
-constexpr int kArgmaxChunk = 16384;   // logits per argmax workgroup
+constexpr int kArgmaxChunk = 4096;   // logits per argmax workgroup
 
 hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t stream);
 hipError_t launch_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q, hipStream_t s);
