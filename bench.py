@@ -57,6 +57,7 @@ def parse():
     p.add_argument("--ms", default=None, help="comma-separated row counts (default: the workload's)")
     p.add_argument("--splits", type=int, default=0, help="workgroups per column tile along K (0 = default)")
     p.add_argument("--waves-k", type=int, default=0, help="waves per workgroup along K (0 = default)")
+    p.add_argument("--tile-cols", type=int, default=0, help="column tile width, 64 or 128 (0 = default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise kernel (y = 2x, fp32) over MIB MiB five times: the "
@@ -160,7 +161,8 @@ def main():
         for M in ms:
             row.append((M, (ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(qw.data_ptr()),
                             ctypes.c_void_p(sc.data_ptr()), None if qz is None else ctypes.c_void_p(qz.data_ptr()),
-                            g, M, N, K, ctypes.c_void_p(outs[M].data_ptr()), 0, args.splits, args.waves_k, sp)))
+                            g, M, N, K, ctypes.c_void_p(outs[M].data_ptr()), 0, args.splits, args.waves_k,
+                            args.tile_cols, sp)))
         calls.append(row)
     fn = lib.w4a16_gemm_ex
 
@@ -206,12 +208,13 @@ def main():
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
         b = algorithmic_bytes(M, K, N, g, wl.symmetric)
         us = float(np.mean(d))
-        kern, spl, wk = vm.w4a16_plan(M, N, K, g)
+        kern, spl, wk, tcols = vm.w4a16_plan(M, N, K, g)
         per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
                          "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b,
                          "kernel": "gemv" if kern == 0 else "mfma",
-                         "splits": args.splits or spl, "waves_k": args.waves_k or wk}
+                         "splits": args.splits or spl, "waves_k": args.waves_k or wk,
+                         "tile_cols": args.tile_cols or tcols}
         if float(np.sum(d)) > dom_time:
             dom, dom_time = M, float(np.sum(d))
     # the dominant launch: the row count whose calls take the most time in a step
@@ -266,8 +269,9 @@ def main():
         "config": {"workload": f"{wl.name}, M in {','.join(map(str, ms))} (one call each per step)",
                    "K": K, "N": N, "group": g, "symmetric_zero": wl.symmetric, "ms": list(ms), "out": "fp32",
                    "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20),
-                   "launch": "default" if not (args.splits or args.waves_k) else
-                   f"splits={args.splits or 'default'} waves_k={args.waves_k or 'default'}"},
+                   "launch": "default" if not (args.splits or args.waves_k or args.tile_cols) else
+                   f"splits={args.splits or 'default'} waves_k={args.waves_k or 'default'} "
+                   f"tile_cols={args.tile_cols or 'default'}"},
         "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel ({dm['kernel']}, M={dom})", "M": dom,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,

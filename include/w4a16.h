@@ -77,20 +77,24 @@ int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales,
                void *out, int out_dtype, hipStream_t stream);
 
 /*
- * w4a16_gemm with an explicit launch: `splits` workgroups share each 64-column tile along K
- * (their fp32 partials are added in slice order through the library's scratch buffer) and
- * `waves_k` waves of each workgroup split that workgroup's K range (1, 2, 4, 8 or 16); 0 picks
- * what w4a16_gemm picks. splits * waves_k must not exceed K/32. Every launch meets the same
- * accuracy contract and is deterministic; different launches round differently. Meant for tests
- * and tuning sweeps.
+ * w4a16_gemm with an explicit launch: `splits` workgroups share each column tile along K
+ * (their fp32 partials are added in slice order through the library's scratch buffer),
+ * `waves_k` waves of each workgroup split that workgroup's K range (1, 2, 4, 8 or 16), and
+ * `tile_cols` is the tile width (64 or 128 columns: 4 or 8 adjacent columns per lane). 0 picks
+ * what w4a16_gemm picks for that knob. splits * waves_k must not exceed K/32. Every launch meets
+ * the same accuracy contract and is deterministic; different launches round differently. Meant
+ * for tests and tuning sweeps.
  */
 int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales,
                   const uint32_t *qzeros, int group_size, int M, int N, int K,
-                  void *out, int out_dtype, int splits, int waves_k, hipStream_t stream);
+                  void *out, int out_dtype, int splits, int waves_k, int tile_cols,
+                  hipStream_t stream);
 
 /* The launch w4a16_gemm picks for a shape: *kernel = 0 for the one-row GEMV, 1 for the MFMA
- * GEMM; *splits and *waves_k as in w4a16_gemm_ex. Any output pointer may be NULL. Host only. */
-int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k);
+ * GEMM; *splits, *waves_k and *tile_cols as in w4a16_gemm_ex. Any output pointer may be NULL.
+ * Host only. */
+int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k,
+               int *tile_cols);
 
 /*
  * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32

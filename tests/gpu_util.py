@@ -26,13 +26,14 @@ class DevInputs:
         self.act = dev_u16(inp.act)
         self.K, self.N, self.group = inp.K, inp.N, inp.group
 
-    def run(self, M: int, out_dtype=torch.float32, splits=None, waves_k=0, act=None) -> np.ndarray:
+    def run(self, M: int, out_dtype=torch.float32, splits=None, waves_k=0, act=None, tile_cols=0) -> np.ndarray:
         a = self.act[:M] if act is None else act
         out = torch.empty((M, self.N), dtype=out_dtype, device=DEV)
-        if splits is None and not waves_k:
+        if splits is None and not waves_k and not tile_cols:
             vm.w4a16_gemm(a, self.qweight, self.scales, self.qzeros, self.group, out)
         else:
-            vm.w4a16_gemm_ex(a, self.qweight, self.scales, self.qzeros, self.group, out, splits or 0, waves_k)
+            vm.w4a16_gemm_ex(a, self.qweight, self.scales, self.qzeros, self.group, out, splits or 0, waves_k,
+                             tile_cols)
         torch.cuda.synchronize()
         return out.float().cpu().numpy().astype(np.float64)
 

@@ -33,10 +33,10 @@ def test_codes_equal_zeros_give_zero(gu):
     sym = synth.Inputs(np.full((K // 8, N), 0x88888888, np.uint32), inp.scales, None, inp.act, g)
     ds = gu.DevInputs(sym)
     for M in ROWS:
-        for splits, wk in ((1, 1), (3, 2), (0, 0)):
-            gu.say(f"[q==z] M={M} splits={splits} waves_k={wk}")
-            assert np.all(d.run(M, splits=splits, waves_k=wk) == 0.0)
-            assert np.all(ds.run(M, splits=splits, waves_k=wk) == 0.0)
+        for splits, wk, cols in ((1, 1, 0), (3, 2, 0), (0, 0, 0), (3, 2, 128)):
+            gu.say(f"[q==z] M={M} splits={splits} waves_k={wk} tile_cols={cols}")
+            assert np.all(d.run(M, splits=splits, waves_k=wk, tile_cols=cols) == 0.0)
+            assert np.all(ds.run(M, splits=splits, waves_k=wk, tile_cols=cols) == 0.0)
 
 
 def test_integer_matmul_is_exact(gu):
@@ -51,9 +51,9 @@ def test_integer_matmul_is_exact(gu):
     for M in ROWS:
         ref = (ai[:M].astype(np.int64) @ codes.astype(np.int64)).astype(np.float64)
         assert np.abs(ref).max() < 2 ** 24
-        for splits, wk in ((0, 0), (17, 2), (40, 8), (1, 16)):
-            gu.say(f"[integer] M={M} splits={splits} waves_k={wk}")
-            assert np.array_equal(d.run(M, splits=splits, waves_k=wk), ref)
+        for splits, wk, cols in ((0, 0, 0), (17, 2, 0), (40, 8, 0), (1, 16, 0), (0, 0, 128), (17, 2, 128)):
+            gu.say(f"[integer] M={M} splits={splits} waves_k={wk} tile_cols={cols}")
+            assert np.array_equal(d.run(M, splits=splits, waves_k=wk, tile_cols=cols), ref)
 
 
 def test_scaling_negation_permutation_and_repeat(gu):

@@ -81,7 +81,9 @@ SHAPES = [   # (K, N, group, symmetric): several tiles, ragged column tails, une
 ]
 
 
-LAUNCHES = [(0, 0), (1, 1), (1, 2), (2, 1), (3, 4), (1, 16), (5, 8)]   # (splits, waves_k); 0 = default
+# (splits, waves_k, tile_cols); 0 = the default for that knob
+LAUNCHES = [(0, 0, 0), (1, 1, 0), (1, 2, 0), (2, 1, 0), (3, 4, 0), (1, 16, 0), (5, 8, 0),
+            (0, 0, 128), (1, 1, 128), (3, 2, 128), (2, 8, 128)]
 
 
 @pytest.mark.parametrize("K,N,g,sym", SHAPES)
@@ -91,12 +93,13 @@ def test_parity_sweep_rows_and_launches(gu, K, N, g, sym):
     steps = K // 32
     for M in range(1, 17):
         y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
-        for splits, wk in LAUNCHES + [(steps, 1), (steps // 16, 16)]:
+        for splits, wk, cols in LAUNCHES + [(steps, 1, 0), (steps // 16, 16, 0), (steps, 1, 128)]:
             if (splits or 1) * (wk or 1) > steps or (wk == 16 and splits == 0):
                 continue
-            gu.say(f"[sweep] K={K} N={N} g={g} sym={sym} M={M} splits={splits} waves_k={wk}")
-            y = d.run(M, splits=splits, waves_k=wk)
-            parity.check_close(y, y_ref, bound, f"K={K} N={N} g={g} M={M} splits={splits} waves_k={wk}")
+            gu.say(f"[sweep] K={K} N={N} g={g} sym={sym} M={M} splits={splits} waves_k={wk} tile_cols={cols}")
+            y = d.run(M, splits=splits, waves_k=wk, tile_cols=cols)
+            parity.check_close(y, y_ref, bound,
+                               f"K={K} N={N} g={g} M={M} splits={splits} waves_k={wk} tile_cols={cols}")
 
 
 # ---- the workloads at full size, in the default launch configuration --------------------------
@@ -121,7 +124,7 @@ def _wl(gu, cache, name):
 @pytest.mark.parametrize("name,M", _WL_CASES)
 def test_parity_workloads(gu, wl_cache, name, M):
     inp, d = _wl(gu, wl_cache, name)
-    gu.say(f"[workload] {name} M={M} K={inp.K} N={inp.N} g={inp.group} plan (kernel, splits, waves_k)="
+    gu.say(f"[workload] {name} M={M} K={inp.K} N={inp.N} g={inp.group} plan (kernel, splits, waves_k, tile_cols)="
            f"{vm.w4a16_plan(M, inp.N, inp.K, inp.group)}")
     y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)
     y = d.run(M)

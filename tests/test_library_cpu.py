@@ -74,8 +74,8 @@ def test_validation_order_is_fixed(lib):
     assert gemm(lib, g=48, a=A + 2) == -1 and b"multiple of 32" in lib.w4a16_last_error()
 
 
-def ex(lib, splits, wk, K=512):
-    return lib.w4a16_gemm_ex(A, Q, S, None, 128, 1, 256, K, O, 0, splits, wk, None)
+def ex(lib, splits, wk, K=512, cols=0):
+    return lib.w4a16_gemm_ex(A, Q, S, None, 128, 1, 256, K, O, 0, splits, wk, cols, None)
 
 
 def test_explicit_launch_is_checked(lib):
@@ -86,18 +86,21 @@ def test_explicit_launch_is_checked(lib):
     assert ex(lib, 0, -1) == -1
     assert ex(lib, 1, 3) == -1
     assert ex(lib, 1, 32) == -1
+    assert ex(lib, 1, 1, cols=96) == -1 and b"tile_cols" in lib.w4a16_last_error()
+    assert ex(lib, 1, 1, cols=-64) == -1
 
 
 def test_plan_host_only(lib):
     import ctypes
-    k, s, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    k, s, w, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     for M, N, K, g in ((1, 17408, 5120, 128), (16, 17408, 5120, 128), (5, 248320, 5120, 128),
                        (1, 5120, 5120, 128), (16, 5120, 17408, 64), (1, 256, 512, 128), (16, 8, 64, 32)):
-        assert lib.w4a16_plan(M, N, K, g, ctypes.byref(k), ctypes.byref(s), ctypes.byref(w)) == 0
+        assert lib.w4a16_plan(M, N, K, g, ctypes.byref(k), ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)) == 0
         assert k.value == (0 if M == 1 else 1)
         assert s.value >= 1 and w.value in (1, 2, 4, 8, 16) and s.value * w.value <= K // 32
-    assert lib.w4a16_plan(0, 256, 512, 128, None, None, None) == -1
-    assert lib.w4a16_plan(1, 256, 512, 48, None, None, None) == -1
+        assert c.value in (64, 128)
+    assert lib.w4a16_plan(0, 256, 512, 128, None, None, None, None) == -1
+    assert lib.w4a16_plan(1, 256, 512, 48, None, None, None, None) == -1
 
 
 def test_aux_entry_points_reject_bad_arguments(lib):

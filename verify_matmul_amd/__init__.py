@@ -50,8 +50,8 @@ def load():
     lib = ctypes.CDLL(lib_path)
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
-    lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, P]
-    lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P]
+    lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
+    lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
     lib.w4a16_dequant_f32.argtypes = [P, P, P, I, I, I, P, P]
@@ -124,19 +124,21 @@ def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
     return out
 
 
-def w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, out, splits=0, waves_k=0, stream=None):
+def w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, out, splits=0, waves_k=0, tile_cols=0, stream=None):
     """w4a16_gemm with an explicit launch (0 = the default choice for that knob)."""
     args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
-    _check(load().w4a16_gemm_ex(*args, int(splits), int(waves_k), _stream(stream)), "w4a16_gemm_ex")
+    _check(load().w4a16_gemm_ex(*args, int(splits), int(waves_k), int(tile_cols), _stream(stream)),
+           "w4a16_gemm_ex")
     return out
 
 
 def w4a16_plan(M, N, K, group_size):
-    """(kernel, splits, waves_k) that w4a16_gemm uses for a shape; kernel 0 = GEMV, 1 = MFMA GEMM."""
-    k, s, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    """(kernel, splits, waves_k, tile_cols) that w4a16_gemm uses for a shape; kernel 0 = GEMV,
+    1 = MFMA GEMM."""
+    k, s, w, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(load().w4a16_plan(int(M), int(N), int(K), int(group_size), ctypes.byref(k), ctypes.byref(s),
-                             ctypes.byref(w)), "w4a16_plan")
-    return k.value, s.value, w.value
+                             ctypes.byref(w), ctypes.byref(c)), "w4a16_plan")
+    return k.value, s.value, w.value, c.value
 
 
 def w4a16_argmax_rows(logits, idx, stream=None):

@@ -130,10 +130,16 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
 // tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
 // `splits` workgroups (summed through scratch): 4 waves per workgroup up to 32 pieces, 8 beyond
 // and for more than 8 rows. `splits` / `wk` > 0 override the choice (tuning and tests).
-int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan *plan)
+int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile_cols, GemmPlan *plan)
 {
     const int steps = K / kStepK;
-    const int tiles = (N + kTileN - 1) / kTileN;
+    if (tile_cols != 0 && tile_cols != 64 && tile_cols != 128)
+        return fail(W4A16_ERR_INVALID_ARG, "tile_cols=%d is not 0, 64 or 128", tile_cols);
+    // 128-column tiles for wide matrices: each wave then converts its activation slice once
+    // for twice the columns (measured on the 248320-column output layer: 148 -> 130 us at
+    // M = 5); narrower matrices keep 64-column tiles and the larger wave count they give.
+    const int cols = tile_cols != 0 ? tile_cols / 16 : (N >= kWideTileMinN ? 8 : 4);
+    const int tiles = (N + tile_columns(cols) - 1) / tile_columns(cols);
     if (splits == 0 || wk == 0) {
         // P pieces per tile: about 4352 waves in all (8192 for more than 8 rows, whose shorter
         // pieces keep their activation slices within the LDS staging budget, at most 64 pieces
@@ -152,6 +158,7 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan
     if (splits < 1 || splits > 65535 || (long long)splits * wk > steps)
         return fail(W4A16_ERR_INVALID_ARG, "splits=%d x waves_k=%d exceeds the %d K-steps of 32", splits, wk, steps);
     plan->mfma = M > 1;
+    plan->cols = cols;
     plan->wk = wk;
     plan->splits = splits;
     // Stage activations in LDS when a wave's slice fits the per-wave budget: then they arrive by
@@ -159,14 +166,14 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, GemmPlan
     // workgroup needs would cut the waves per CU, and converting each fragment as it streams in
     // (after an exponent pass) measures faster. The GEMV always stages.
     GemmPlan staged{};
-    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, true, sym, &staged);
+    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, sym, &staged);
     plan->lds_a = !plan->mfma || ((size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
                                   lds_staged <= (size_t)kMaxLds);
     // Activations a wave cannot stage are prepared once per call by a separate kernel: without
     // it each wave would run an exponent pass over its slice and convert every fragment as it
     // streams in. Staged slices are converted in the wave (cheaper than the extra launch).
     plan->prep_a = plan->mfma && !plan->lds_a;
-    plan->lds = gemm_lds_layout(M, K, g, splits, wk, plan->lds_a, sym, plan);
+    plan->lds = gemm_lds_layout(M, K, g, splits, wk, cols, plan->lds_a, sym, plan);
     if (plan->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",
                     plan->lds, kMaxLds);
@@ -199,14 +206,14 @@ extern "C" {
 
 int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                   int group_size, int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
-                  hipStream_t stream)
+                  int tile_cols, hipStream_t stream)
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
     if (splits < 0 || waves_k < 0)
         return fail(W4A16_ERR_INVALID_ARG, "splits=%d waves_k=%d must be >= 0", splits, waves_k);
     GemmPlan plan{};
-    rc = make_plan(M, N, K, group_size, qzeros == nullptr, splits, waves_k, &plan);
+    rc = make_plan(M, N, K, group_size, qzeros == nullptr, splits, waves_k, tile_cols, &plan);
     if (rc != W4A16_OK) return rc;
 
     GemmArgs a{};
@@ -226,7 +233,8 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
     if (split_k || plan.prep_a) {
-        const size_t tiles = (size_t)(N + kTileN - 1) / kTileN;
+        const size_t tile = (size_t)tile_columns(plan.cols);
+        const size_t tiles = ((size_t)N + tile - 1) / tile;
         const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
         const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
@@ -247,19 +255,20 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
 int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
 {
-    return w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, stream);
+    return w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, stream);
 }
 
-int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k)
+int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k, int *tile_cols)
 {
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
     GemmPlan plan{};
-    const int rc = make_plan(M, N, K, group_size, true, 0, 0, &plan);
+    const int rc = make_plan(M, N, K, group_size, true, 0, 0, 0, &plan);
     if (rc != W4A16_OK) return rc;
     if (kernel) *kernel = plan.mfma ? 1 : 0;
     if (splits) *splits = plan.splits;
     if (waves_k) *waves_k = plan.wk;
+    if (tile_cols) *tile_cols = tile_columns(plan.cols);
     return W4A16_OK;
 }
 

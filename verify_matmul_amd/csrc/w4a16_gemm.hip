@@ -154,17 +154,20 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
 // kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
 // slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
 // order, rescaled per piece and row -- and stream in with the weights, one fragment per step.
-template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf>
+template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf, int kC>
 __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
 {
     constexpr bool kPreA = !kLdsA;
+    constexpr int kTile = 16 * kC;      // columns per tile: kC adjacent columns per lane
+    constexpr int kV = kC / 4;          // 16-byte weight loads per lane per step
+    constexpr int kZW = kTile / 8;      // zero words (and 8-scale items) per group
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: K-range math stays scalar
-    const int cl = lane & 15;   // column quad (and MFMA A row) of this lane
+    const int cl = lane & 15;   // column block (and MFMA A row) of this lane
     const int rl = lane >> 4;   // word row within the step
     const int M = p.M;
     const int N = p.N;
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     uint16_t *sc_lds = reinterpret_cast<uint16_t *>(wreg + p.scale_off);           // [group][64]
     uint32_t *z_lds = reinterpret_cast<uint32_t *>(wreg + p.zero_off);             // [group][8]
 
-    const int n0 = tile * kTileN + cl * 4;
+    const int n0 = tile * kTile + cl * kC;
     const bool col_ok = n0 < N;
     const int nc = col_ok ? n0 : 0;       // clamped column for loads of dead lanes
     const int arow = cl < M ? cl : 0;     // clamped activation row (MFMA fragments)
@@ -217,25 +220,25 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             ++pre_loads;
         }
     }
-    {   // scales: 8 lanes x 8 columns per group
-        const int sitems = ng * 8;
+    {   // scales: kZW items of 8 columns per group
+        const int sitems = ng * kZW;
         for (int b = 0; b < sitems; b += 64) {
             int it = b + lane;
             if (it >= sitems) it = sitems - 1;
-            const int gi = g0 + it / 8;
-            int c = tile * kTileN + (it & 7) * 8;
+            const int gi = g0 + it / kZW;
+            int c = tile * kTile + (it % kZW) * 8;
             if (c >= N) c = 0;
             load_to_lds16(p.scales + (size_t)gi * N + c, sc_lds + (size_t)b * 8);
             ++pre_loads;
         }
     }
-    if (!kSym) {   // zero words: 8 per group (64 columns)
-        const int zitems = ng * 8;
+    if (!kSym) {   // zero words: kZW per group (8 columns each)
+        const int zitems = ng * kZW;
         for (int b = 0; b < zitems; b += 64) {
             int it = b + lane;
             if (it >= zitems) it = zitems - 1;
-            const int gi = g0 + it / 8;
-            int c = tile * kTileN + (it & 7) * 8;
+            const int gi = g0 + it / kZW;
+            int c = tile * kTile + (it % kZW) * 8;
             if (c >= N) c = 0;
             load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
             ++pre_loads;
@@ -246,12 +249,16 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     asm volatile("" ::: "memory");
 
     // ---- 2. the weight ring -------------------------------------------------------------------
-    uint4 ring_w[kPf];
+    uint4 ring_w[kPf][kV];
     uint4 ring_a[kLdsA ? 1 : kPf];
+    auto load_w = [&](uint4 *dst, int t) {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) dst[v] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)t * 4 * N + 4 * v);
+    };
 #pragma unroll
     for (int u = 0; u < kPf; ++u) {
         const int t = min(wb + u, we - 1);
-        ring_w[u] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)t * 4 * N);
+        load_w(ring_w[u], t);
         if (!kLdsA) ring_a[u] = *reinterpret_cast<const uint4 *>(a_lane + (size_t)t * kStepK);
     }
     asm volatile("" ::: "memory");
@@ -278,20 +285,20 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     // ---- stream ------------------------------------------------------------------------
     const Masks mk = make_masks();
     const half8_t zero8 = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    float4_t acc[4];
-    float4_t tot[4];
+    float4_t acc[kC];
+    float4_t tot[kC];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kC; ++j) {
         acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
         tot[j] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-    ZeroSub zs[4];
+    ZeroSub zs[kC];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) zs[j] = zero_sub_sym();
+    for (int j = 0; j < kC; ++j) zs[j] = zero_sub_sym();
     int zs_group = -1;
 
     // One step: dequantise the ring slot's words, multiply, and scale at a group's end.
-    auto step = [&](int t, const uint4 wv, const uint4 av) {
+    auto step = [&](int t, const uint4 *wv, const uint4 av) {
         const int gi = t / spg;
         half8_t a;
         if (kLdsA) {
@@ -308,13 +315,20 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         }
         if (!kSym && gi != zs_group) {   // zero points change once per group (uniform)
             zs_group = gi;
-            const uint32_t zw = z_lds[(gi - g0) * 8 + cl / 2];
+            const uint32_t zw = z_lds[(gi - g0) * kZW + (cl * kC) / 8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
+            for (int j = 0; j < kC; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
         }
-        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t words[kC];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int v = 0; v < kV; ++v) {
+            words[4 * v] = wv[v].x;
+            words[4 * v + 1] = wv[v].y;
+            words[4 * v + 2] = wv[v].z;
+            words[4 * v + 3] = wv[v].w;
+        }
+#pragma unroll
+        for (int j = 0; j < kC; ++j) {
             const half8_t b = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
             if (kMfma) {
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
@@ -328,11 +342,27 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             }
         }
         if (((t + 1) % spg == 0) || (t + 1 == we)) {
-            const uint2 sc = *reinterpret_cast<const uint2 *>(sc_lds + (gi - g0) * kTileN + cl * 4);
-            const float s4[4] = {half_bits_to_float(sc.x & 0xFFFFu), half_bits_to_float(sc.x >> 16),
-                                 half_bits_to_float(sc.y & 0xFFFFu), half_bits_to_float(sc.y >> 16)};
+            const uint16_t *sp = sc_lds + (gi - g0) * kTile + cl * kC;
+            uint32_t sw[kC / 2];
+            if constexpr (kC == 4) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(sp);
+                sw[0] = v.x;
+                sw[1] = v.y;
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int v = 0; v < kV; ++v) {
+                    const uint4 q = *reinterpret_cast<const uint4 *>(sp + 8 * v);
+                    sw[4 * v] = q.x;
+                    sw[4 * v + 1] = q.y;
+                    sw[4 * v + 2] = q.z;
+                    sw[4 * v + 3] = q.w;
+                }
+            }
+            float s4[kC];
+#pragma unroll
+            for (int j = 0; j < kC; ++j) s4[j] = half_bits_to_float((sw[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+#pragma unroll
+            for (int j = 0; j < kC; ++j) {
                 if (kMfma) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) tot[j][r] = __builtin_fmaf(acc[j][r], s4[j], tot[j][r]);
@@ -354,23 +384,23 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
 #pragma unroll
         for (int u = 0; u < kPf; ++u) {
             const int t = t0 + u;
-            step(t, ring_w[u], kLdsA ? ring_w[u] : ring_a[kLdsA ? 0 : u]);
+            step(t, ring_w[u], ring_a[kLdsA ? 0 : u]);
             const int tn = min(t + kPf, we - 1);
-            ring_w[u] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)tn * 4 * N);
+            load_w(ring_w[u], tn);
             if (!kLdsA) ring_a[u] = *reinterpret_cast<const uint4 *>(a_lane + (size_t)tn * kStepK);
         }
     }
     // The last (we - wb) % kPf steps are already in the ring's first slots.
 #pragma unroll
     for (int u = 0; u + 1 < kPf; ++u)
-        if (t0 + u < we) step(t0 + u, ring_w[u], kLdsA ? ring_w[u] : ring_a[kLdsA ? 0 : u]);
+        if (t0 + u < we) step(t0 + u, ring_w[u], ring_a[kLdsA ? 0 : u]);
 
     // ---- this wave's sums: add the word rows (GEMV), undo the activation rescale ---------------
     // GEMM: lane holds rows 4*rl + r of its 4 columns. GEMV: lanes with rl == 0 hold row 0.
     constexpr int kRows = kMfma ? 4 : 1;
     if (!kMfma) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kC; ++j) {
             float v = tot[j][0];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
@@ -384,7 +414,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         const int m = row_base + r;
         const int sh = m < M ? shift_lds[m] : 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tot[j][r] = __builtin_amdgcn_ldexpf(tot[j][r], sh);
+        for (int j = 0; j < kC; ++j) tot[j][r] = __builtin_amdgcn_ldexpf(tot[j][r], sh);
     }
 
     auto store_out = [&](int m, int n, float v) {
@@ -401,29 +431,35 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             const int m = row_base + r;
             if (m >= M) break;
             const size_t o = (size_t)m * N + n0;
-            if (p.out_bf16) {
-                uint2 v;
-                v.x = float_to_bf16_bits(tot[0][r]) | (float_to_bf16_bits(tot[1][r]) << 16);
-                v.y = float_to_bf16_bits(tot[2][r]) | (float_to_bf16_bits(tot[3][r]) << 16);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o) = v;
-            } else {
-                *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o) =
-                    make_float4(tot[0][r], tot[1][r], tot[2][r], tot[3][r]);
+#pragma unroll
+            for (int v = 0; v < kV; ++v) {
+                const float x0 = tot[4 * v][r], x1 = tot[4 * v + 1][r], x2 = tot[4 * v + 2][r], x3 = tot[4 * v + 3][r];
+                if (p.out_bf16) {
+                    uint2 q;
+                    q.x = float_to_bf16_bits(x0) | (float_to_bf16_bits(x1) << 16);
+                    q.y = float_to_bf16_bits(x2) | (float_to_bf16_bits(x3) << 16);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o + 4 * v) = q;
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o + 4 * v) = make_float4(x0, x1, x2, x3);
+                }
             }
         }
         return;
     }
 
     // ---- cross-wave reduction in LDS, in wave order ---------------------------------------
-    float *red = reinterpret_cast<float *>(region);   // [kWK][M][64] over the dead staging areas
+    float *red = reinterpret_cast<float *>(region);   // [kWK][M][kTile] over the dead staging areas
     __syncthreads();
     if (holder) {
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const int m = row_base + r;
             if (m < M) {
-                float *dst = red + ((size_t)wave * M + m) * kTileN + cl * 4;
-                *reinterpret_cast<float4_t *>(dst) = float4_t{tot[0][r], tot[1][r], tot[2][r], tot[3][r]};
+                float *dst = red + ((size_t)wave * M + m) * kTile + cl * kC;
+#pragma unroll
+                for (int v = 0; v < kV; ++v)
+                    *reinterpret_cast<float4_t *>(dst + 4 * v) =
+                        float4_t{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
             }
         }
     }
@@ -431,16 +467,16 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     __syncthreads();
     constexpr int kThreads = kWK * 64;
     auto wg_sum = [&](int m, int c) {
-        float v = red[(size_t)m * kTileN + c];
+        float v = red[(size_t)m * kTile + c];
 #pragma unroll
-        for (int w = 1; w < kWK; ++w) v += red[((size_t)w * M + m) * kTileN + c];
+        for (int w = 1; w < kWK; ++w) v += red[((size_t)w * M + m) * kTile + c];
         return v;
     };
     if (p.splits == 1) {
-        for (int idx = tid; idx < M * kTileN; idx += kThreads) {
-            const int m = idx / kTileN;
-            const int c = idx - m * kTileN;
-            const int n = tile * kTileN + c;
+        for (int idx = tid; idx < M * kTile; idx += kThreads) {
+            const int m = idx / kTile;
+            const int c = idx - m * kTile;
+            const int n = tile * kTile + c;
             if (n < N) store_out(m, n, wg_sum(m, c));
         }
         return;
@@ -456,10 +492,10 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     // slice order with its own slice taken from LDS.
     const uint64_t stamp_hi = (uint64_t)p.stamp << 32;
     if (!s_last) {
-        for (int idx = tid; idx < M * kTileN; idx += kThreads) {
-            const int m = idx / kTileN;
-            const int c = idx - m * kTileN;
-            const int n = tile * kTileN + c;
+        for (int idx = tid; idx < M * kTile; idx += kThreads) {
+            const int m = idx / kTile;
+            const int c = idx - m * kTile;
+            const int n = tile * kTile + c;
             if (n < N)
                 __hip_atomic_store(p.partials + ((size_t)split * M + m) * N + n,
                                    stamp_hi | __builtin_bit_cast(uint32_t, wg_sum(m, c)), __ATOMIC_RELAXED,
@@ -471,10 +507,10 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     // is the smallest of 4, 8 or 16 that covers the slices, so few slices fetch no padding.
     auto reduce = [&](auto batch_tag) {
         constexpr int kBatch = decltype(batch_tag)::value;
-        for (int idx = tid; idx < M * kTileN; idx += kThreads) {
-            const int m = idx / kTileN;
-            const int c = idx - m * kTileN;
-            const int n = tile * kTileN + c;
+        for (int idx = tid; idx < M * kTile; idx += kThreads) {
+            const int m = idx / kTile;
+            const int c = idx - m * kTile;
+            const int n = tile * kTile + c;
             if (n >= N) continue;
             const float own = wg_sum(m, c);
             const uint64_t *col = p.partials + (size_t)m * N + n;
@@ -521,11 +557,11 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool kMfma, bool kSym, bool kLdsA, int kWK>
+template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kC>
 hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     constexpr int kPf = kLdsA ? kRingStaged : kRingConvert;
-    const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf>;
+    const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf, kC>;
     if (!kLdsA) {
         ActPrepArgs pa{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK};
         hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(a.splits * kWK)), dim3(kPrepThreads), 0, stream, pa);
@@ -537,29 +573,36 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
         if (e != hipSuccess) return e;
     }
-    const dim3 grid((unsigned)((a.N + kTileN - 1) / kTileN), (unsigned)a.splits);
+    const dim3 grid((unsigned)((a.N + 16 * kC - 1) / (16 * kC)), (unsigned)a.splits);
     hipLaunchKernelGGL(kern, grid, dim3(kWK * 64), plan.lds, stream, a);
     return hipGetLastError();
 }
 
-template <bool kMfma, bool kSym, bool kLdsA>
+template <bool kMfma, bool kSym, bool kLdsA, int kC>
 hipError_t launch_wk(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     switch (plan.wk) {
-    case 1: return launch_one<kMfma, kSym, kLdsA, 1>(a, plan, stream);
-    case 2: return launch_one<kMfma, kSym, kLdsA, 2>(a, plan, stream);
-    case 4: return launch_one<kMfma, kSym, kLdsA, 4>(a, plan, stream);
-    case 8: return launch_one<kMfma, kSym, kLdsA, 8>(a, plan, stream);
-    case 16: return launch_one<kMfma, kSym, kLdsA, 16>(a, plan, stream);
+    case 1: return launch_one<kMfma, kSym, kLdsA, 1, kC>(a, plan, stream);
+    case 2: return launch_one<kMfma, kSym, kLdsA, 2, kC>(a, plan, stream);
+    case 4: return launch_one<kMfma, kSym, kLdsA, 4, kC>(a, plan, stream);
+    case 8: return launch_one<kMfma, kSym, kLdsA, 8, kC>(a, plan, stream);
+    case 16: return launch_one<kMfma, kSym, kLdsA, 16, kC>(a, plan, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <bool kMfma, bool kSym, bool kLdsA>
+hipError_t launch_cols(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
+{
+    return plan.cols == 8 ? launch_wk<kMfma, kSym, kLdsA, 8>(a, plan, stream)
+                          : launch_wk<kMfma, kSym, kLdsA, 4>(a, plan, stream);
 }
 
 template <bool kMfma, bool kLdsA>
 hipError_t launch_sym(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
-    return a.qzeros == nullptr ? launch_wk<kMfma, true, kLdsA>(a, plan, stream)
-                               : launch_wk<kMfma, false, kLdsA>(a, plan, stream);
+    return a.qzeros == nullptr ? launch_cols<kMfma, true, kLdsA>(a, plan, stream)
+                               : launch_cols<kMfma, false, kLdsA>(a, plan, stream);
 }
 
 }  // namespace

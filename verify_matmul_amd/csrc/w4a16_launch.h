@@ -6,8 +6,11 @@
 
 namespace w4a16 {
 
-// Columns covered by one wave and by one workgroup (the waves of a workgroup split K).
-constexpr int kTileN = 64;
+// Columns of a column tile: one wave wide, 16 lanes x `cols` adjacent columns each (4 or 8). The
+// waves of a workgroup share the tile and split its K range.
+inline int tile_columns(int cols) { return 16 * cols; }
+// Matrices at least this wide get 128-column tiles by default (64 otherwise).
+constexpr int kWideTileMinN = 32768;
 // K rows consumed per step (4 packed word rows = one 16x16x32 MFMA K step).
 constexpr int kStepK = 32;
 // Largest dynamic LDS a GEMM workgroup may ask for (gfx950: 160 KiB per workgroup).
@@ -53,6 +56,7 @@ struct GemmPlan {
     bool mfma;     // false: the M = 1 dot-product GEMV
     bool lds_a;    // activations staged once per wave in LDS (else converted per step)
     bool prep_a;   // activations prepared once per call by act_prep_kernel (matrix-core path)
+    int cols;      // adjacent columns per lane (4 or 8): tiles of 64 or 128 columns
     int wk;        // waves per workgroup, each a contiguous K range (1, 2, 4, 8 or 16)
     int splits;    // workgroups per column tile, reduced through the scratch buffer
     size_t lds;    // dynamic LDS bytes per workgroup
@@ -72,17 +76,19 @@ inline size_t round_up_sz(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // LDS layout of a plan: per-wave row shifts, then one staging area per wave (activations if
 // staged, the scales and the zero words of the wave's groups; each filled by whole 64-lane
 // direct loads), and, after the main loop, the cross-wave reduction buffer over the same bytes.
-inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, bool lds_a, bool sym, GemmPlan *pl)
+inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols, bool lds_a, bool sym,
+                              GemmPlan *pl)
 {
+    const size_t tile = (size_t)tile_columns(cols);
     const int ws = max_wave_steps(K, splits, wk);
     const int spg = g / kStepK;
     const size_t groups = (size_t)(ws + spg - 1) / spg + 1;
     const size_t a_bytes = lds_a ? round_up_sz((size_t)M * ws * 4, 64) * 16 : 0;
-    const size_t s_bytes = round_up_sz(groups * 8, 64) * 16;
-    const size_t z_bytes = sym ? 0 : round_up_sz(groups * 8, 64) * 4;
+    const size_t s_bytes = round_up_sz(groups * (tile / 8), 64) * 16;       // 8 scales per item
+    const size_t z_bytes = sym ? 0 : round_up_sz(groups * (tile / 8), 64) * 4;   // 8 zeros per word
     const size_t wave = a_bytes + s_bytes + z_bytes;
     const size_t header = (size_t)wk * 16 * sizeof(int);
-    const size_t red = (wk > 1 || splits > 1) ? (size_t)wk * M * kTileN * sizeof(float) : 0;
+    const size_t red = (wk > 1 || splits > 1) ? (size_t)wk * M * tile * sizeof(float) : 0;
     const size_t body = (size_t)wk * wave > red ? (size_t)wk * wave : red;
     if (pl) {
         pl->wave_lds = (int)wave;
