@@ -237,6 +237,19 @@ def main():
             us = a0.elapsed_time(a1) * 1e3 / args.steps
             per_m[str(M)]["argmax_us_per_call"] = round(us, 3)
             per_m[str(M)]["argmax_GBps"] = round(4 * M * N / us / 1e3, 1)
+            # the same pick fused into the GEMM's epilogue (one launch, no logits re-read),
+            # a lone event pair around each call as for us_per_call
+            fd = []
+            for i in range(args.steps):
+                qw, sc, qz, a, outs = pool[(i * len(ms) + j) % R]
+                f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                f0.record(stream)
+                vm.w4a16_gemm_argmax(a[:M], qw, sc, qz, g, outs[M], idx)
+                f1.record(stream)
+                fd.append((f0, f1))
+            torch.cuda.synchronize()
+            per_m[str(M)]["fused_gemm_argmax_us_per_call"] = round(
+                float(np.mean([e0.elapsed_time(e1) * 1e3 for e0, e1 in fd])), 3)
 
     # timed region 3: the dominant launch alone, K times back to back (rotating weight copies)
     # between one HIP event pair on its stream -> its average duration without the per-launch

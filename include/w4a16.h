@@ -97,6 +97,16 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
                int *tile_cols);
 
 /*
+ * w4a16_gemm and the greedy pick in one launch (the output layer): out as in w4a16_gemm, and
+ * idx[m] = smallest n with out[m][n] (in fp32, before any bf16 rounding) equal to the row
+ * maximum, with the conventions of w4a16_argmax_rows. The pick is made in the GEMM's epilogue
+ * from the values it writes, so the logits are not read back. idx: int32 [M] device.
+ */
+int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                      const uint32_t *qzeros, int group_size, int M, int N, int K,
+                      void *out, int out_dtype, int32_t *idx, hipStream_t stream);
+
+/*
  * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32
  * comparison, -0 == +0, NaN entries ignored; an all-NaN row gives 0).
  *   logits fp32 [M, N] device, 16-byte aligned; M in 1..65535; N in 1..2^31-1

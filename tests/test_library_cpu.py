@@ -103,6 +103,13 @@ def test_plan_host_only(lib):
     assert lib.w4a16_plan(1, 256, 512, 48, None, None, None, None) == -1
 
 
+def test_fused_pick_checks_its_arguments(lib):
+    assert lib.w4a16_gemm_argmax(A, Q, S, None, 128, 1, 256, 512, O, 0, None, None) == -1
+    assert b"idx" in lib.w4a16_last_error()
+    assert lib.w4a16_gemm_argmax(A, Q, S, None, 128, 17, 256, 512, O, 0, O, None) == -1
+    assert lib.w4a16_gemm_argmax(A, Q, S, None, 48, 1, 256, 512, O, 0, O, None) == -1
+
+
 def test_aux_entry_points_reject_bad_arguments(lib):
     assert lib.w4a16_argmax_rows(None, 1, 10, O, None) == -1
     assert lib.w4a16_argmax_rows(A, 0, 10, O, None) == -1

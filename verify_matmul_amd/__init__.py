@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_plan",
+    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "EXPORTS",
 ]
@@ -24,7 +24,7 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = (
-    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_plan", "w4a16_argmax_rows",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_plan", "w4a16_argmax_rows",
     "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
@@ -51,6 +51,7 @@ def load():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
+    lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
     lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
@@ -61,7 +62,7 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_plan", "w4a16_argmax_rows",
+    for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -130,6 +131,16 @@ def w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, out, splits=0, waves_k
     _check(load().w4a16_gemm_ex(*args, int(splits), int(waves_k), int(tile_cols), _stream(stream)),
            "w4a16_gemm_ex")
     return out
+
+
+def w4a16_gemm_argmax(A, qweight, scales, qzeros, group_size, out, idx, stream=None):
+    """w4a16_gemm plus the greedy pick per row (fp32 values) in the same launch."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    if tuple(idx.shape) != (A.shape[0],):
+        raise ValueError("idx must be [M]")
+    _check(load().w4a16_gemm_argmax(*args, _ptr(idx, "idx", (torch.int32,)), _stream(stream)),
+           "w4a16_gemm_argmax")
+    return out, idx
 
 
 def w4a16_plan(M, N, K, group_size):

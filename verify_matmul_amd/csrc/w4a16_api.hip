@@ -130,7 +130,8 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
 // tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
 // `splits` workgroups (summed through scratch): 4 waves per workgroup up to 32 pieces, 8 beyond
 // and for more than 8 rows. `splits` / `wk` > 0 override the choice (tuning and tests).
-int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile_cols, GemmPlan *plan)
+int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile_cols, bool argmax,
+              GemmPlan *plan)
 {
     const int steps = K / kStepK;
     if (tile_cols != 0 && tile_cols != 64 && tile_cols != 128)
@@ -166,14 +167,14 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
     // workgroup needs would cut the waves per CU, and converting each fragment as it streams in
     // (after an exponent pass) measures faster. The GEMV always stages.
     GemmPlan staged{};
-    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, sym, &staged);
+    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, sym, argmax, &staged);
     plan->lds_a = !plan->mfma || ((size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
                                   lds_staged <= (size_t)kMaxLds);
     // Activations a wave cannot stage are prepared once per call by a separate kernel: without
     // it each wave would run an exponent pass over its slice and convert every fragment as it
     // streams in. Staged slices are converted in the wave (cheaper than the extra launch).
     plan->prep_a = plan->mfma && !plan->lds_a;
-    plan->lds = gemm_lds_layout(M, K, g, splits, wk, cols, plan->lds_a, sym, plan);
+    plan->lds = gemm_lds_layout(M, K, g, splits, wk, cols, plan->lds_a, sym, argmax, plan);
     if (plan->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",
                     plan->lds, kMaxLds);
@@ -200,20 +201,18 @@ int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scal
     return W4A16_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
-                  int group_size, int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
-                  int tile_cols, hipStream_t stream)
+// One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick.
+int gemm_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros, int group_size,
+              int M, int N, int K, void *out, int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx,
+              hipStream_t stream)
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
     if (splits < 0 || waves_k < 0)
         return fail(W4A16_ERR_INVALID_ARG, "splits=%d waves_k=%d must be >= 0", splits, waves_k);
     GemmPlan plan{};
-    rc = make_plan(M, N, K, group_size, qzeros == nullptr, splits, waves_k, tile_cols, &plan);
+    rc = make_plan(M, N, K, group_size, qzeros == nullptr, splits, waves_k, tile_cols, idx != nullptr, &plan);
     if (rc != W4A16_OK) return rc;
 
     GemmArgs a{};
@@ -232,24 +231,52 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
     a.scale_off = plan.scale_off;
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
-    if (split_k || plan.prep_a) {
+    if (split_k || plan.prep_a || idx) {
+        // counters: [tile counters][argmax row keys (M x 64 bit)]
         const size_t tile = (size_t)tile_columns(plan.cols);
         const size_t tiles = ((size_t)N + tile - 1) / tile;
+        const size_t key_off = round_up(tiles * sizeof(uint32_t), 8);
+        const size_t counter_bytes = key_off + 16 * sizeof(unsigned long long);
         const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
         const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
-        rc = get_scratch(stream, split_k ? tiles * sizeof(uint32_t) : 0,
-                         split_k ? (size_t)plan.splits * M * N * sizeof(uint64_t) : 0, act_bytes, split_k, &v);
+        rc = get_scratch(stream, counter_bytes, split_k ? (size_t)plan.splits * M * N * sizeof(uint64_t) : 0, act_bytes,
+                         split_k, &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.counters;
         a.partials = v.partials;
         a.stamp = v.stamp;
         a.A16 = static_cast<uint16_t *>(v.act);
         a.ashift = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
+        if (idx) {
+            char *c = reinterpret_cast<char *>(v.counters);
+            a.amax_keys = reinterpret_cast<unsigned long long *>(c + key_off);
+            a.amax_idx = idx;
+        }
     }
     const hipError_t e = launch_gemm(a, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "GEMM launch");
     return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                  int group_size, int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
+                  int tile_cols, hipStream_t stream)
+{
+    return gemm_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, splits, waves_k, tile_cols,
+                     nullptr, stream);
+}
+
+int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                      int group_size, int M, int N, int K, void *out, int out_dtype, int32_t *idx,
+                      hipStream_t stream)
+{
+    if (!idx) return fail(W4A16_ERR_INVALID_ARG, "null pointer (idx)");
+    return gemm_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, idx, stream);
 }
 
 int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -263,7 +290,7 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
     GemmPlan plan{};
-    const int rc = make_plan(M, N, K, group_size, true, 0, 0, 0, &plan);
+    const int rc = make_plan(M, N, K, group_size, true, 0, 0, 0, false, &plan);
     if (rc != W4A16_OK) return rc;
     if (kernel) *kernel = plan.mfma ? 1 : 0;
     if (splits) *splits = plan.splits;

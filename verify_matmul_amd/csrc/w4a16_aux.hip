@@ -5,27 +5,6 @@
 namespace w4a16 {
 namespace {
 
-// Greedy selection on the device, as lucebox PR #823 (PR description) does to avoid reading a
-// whole vocabulary row back to the host. A (value, index) pair is packed into one 64-bit key
-// whose unsigned order is "larger value first, then smaller index": the high word is the fp32
-// bit pattern mapped to an unsigned total order (-0 folded onto +0), the low word is
-// 0xFFFFFFFF - index. The maximum key over a row is therefore unique and independent of the
-// order in which workgroups combine it, so the result is deterministic.
-__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t n)
-{
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    if ((u & 0x7FFFFFFFu) == 0) u = 0;                       // -0 == +0
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - n);
-}
-
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
-{
-    const uint32_t lo = __shfl_xor((uint32_t)v, m);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
 constexpr int kArgmaxThreads = 256;
 constexpr int kArgmaxPerThread = kArgmaxChunk / kArgmaxThreads;   // 16 logits
 static_assert(kArgmaxPerThread % 4 == 0, "whole 16-byte loads per thread");

@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     constexpr int kZW = kTile / 8;      // zero words (and 8-scale items) per group
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last;
+    __shared__ unsigned long long s_rowkey[16];   // fused argmax: best key per row of the tile
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -424,7 +425,8 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             static_cast<float *>(p.out)[(size_t)m * N + n] = v;
     };
 
-    if (kWK == 1 && p.splits == 1) {
+    const bool amax = p.amax_keys != nullptr;   // fused greedy pick (output layer)
+    if (kWK == 1 && p.splits == 1 && !amax) {
         if (!holder || !col_ok) return;
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
@@ -464,6 +466,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         }
     }
     if (p.splits > 1 && tid == 0) s_last = arrival == (uint32_t)(p.splits - 1);
+    if (tid < 16) s_rowkey[tid] = 0;
     __syncthreads();
     constexpr int kThreads = kWK * 64;
     auto wg_sum = [&](int m, int c) {
@@ -472,13 +475,40 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         for (int w = 1; w < kWK; ++w) v += red[((size_t)w * M + m) * kTile + c];
         return v;
     };
+    // Fused greedy pick: every finished output of the tile folds into its row's key in LDS;
+    // the tile then merges its keys into the call's row keys and exits without waiting, and
+    // argmax_keys_finish_kernel, next on the stream, turns the keys into indices and clears
+    // them (the same keys as argmax_rows_kernel, so the result equals its pick over the fp32
+    // outputs). A tile that waited for its merge to land, or counted itself out on a shared
+    // counter, would hold its compute unit a memory round trip longer. All lanes of a wave hold outputs of one
+    // row (a tile's width is a multiple of 64), so the keys are first reduced across the wave
+    // and one LDS atomic per wave folds them in: emit is called by every lane of the wave
+    // together, with `ok` false for columns past N.
+    auto emit = [&](int m, int n, float v, bool ok) {
+        if (ok) store_out(m, n, v);
+        if (amax) {
+            unsigned long long k = ok && v == v ? argmax_key(v, (uint32_t)n) : 0ull;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const unsigned long long other = shfl_xor_u64(k, o);
+                k = other > k ? other : k;
+            }
+            if (lane == 0 && k) atomicMax(&s_rowkey[m], k);
+        }
+    };
+    auto finish_argmax = [&]() {
+        __syncthreads();
+        if (tid < M && s_rowkey[tid])
+            __hip_atomic_fetch_max(&p.amax_keys[tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     if (p.splits == 1) {
         for (int idx = tid; idx < M * kTile; idx += kThreads) {
             const int m = idx / kTile;
             const int c = idx - m * kTile;
             const int n = tile * kTile + c;
-            if (n < N) store_out(m, n, wg_sum(m, c));
+            emit(m, n, wg_sum(m, c), n < N);
         }
+        if (amax) finish_argmax();
         return;
     }
 
@@ -511,13 +541,13 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             const int m = idx / kTile;
             const int c = idx - m * kTile;
             const int n = tile * kTile + c;
-            if (n >= N) continue;
+            const bool in = n < N;
             const float own = wg_sum(m, c);
             const uint64_t *col = p.partials + (size_t)m * N + n;
             const size_t slice = (size_t)M * N;
             float v = 0.f;
             bool failed = false;
-            for (int sp0 = 0; sp0 < p.splits; sp0 += kBatch) {
+            for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
                 const int cnt = min(kBatch, p.splits - sp0);
                 uint64_t part[kBatch];
 #pragma unroll
@@ -545,7 +575,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
                     v += __builtin_bit_cast(float, (uint32_t)w);
                 }
             }
-            store_out(m, n, failed ? __builtin_nanf("") : v);
+            emit(m, n, failed ? __builtin_nanf("") : v, in);
         }
     };
     if (p.splits <= 4)
@@ -554,7 +584,19 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
         reduce(std::integral_constant<int, 8>{});
     else
         reduce(std::integral_constant<int, 16>{});
+    if (amax) finish_argmax();
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Ends a fused greedy pick: row m's index from its key, and the key cleared for the next call.
+// Runs after the GEMM on its stream, so every tile's merge has landed.
+__global__ __launch_bounds__(64) void argmax_keys_finish_kernel(unsigned long long *keys, int32_t *idx, int M)
+{
+    const int m = threadIdx.x;
+    if (m >= M) return;
+    const unsigned long long k = keys[m];
+    idx[m] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
+    keys[m] = 0;
 }
 
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kC>
@@ -575,6 +617,9 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
     }
     const dim3 grid((unsigned)((a.N + 16 * kC - 1) / (16 * kC)), (unsigned)a.splits);
     hipLaunchKernelGGL(kern, grid, dim3(kWK * 64), plan.lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.amax_keys) return e;
+    hipLaunchKernelGGL(argmax_keys_finish_kernel, dim3(1), dim3(64), 0, stream, a.amax_keys, a.amax_idx, a.M);
     return hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ struct GemmArgs {
     uint64_t *partials;       // [splits, M, N] stamped fp32 partial sums when splits > 1
     uint32_t *counters;       // one per column tile, zero between calls
     uint32_t stamp;           // this call's stamp (nonzero, not used by the last 2^32 - 1 calls)
+    unsigned long long *amax_keys;   // fused argmax: [M] row keys, zero between calls (nullptr: off)
+    int32_t *amax_idx;               // fused argmax: [M] output indices
     int M, N, K, g;
     int splits;               // workgroups along K per column tile
     int out_bf16;
@@ -77,7 +79,7 @@ inline size_t round_up_sz(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // staged, the scales and the zero words of the wave's groups; each filled by whole 64-lane
 // direct loads), and, after the main loop, the cross-wave reduction buffer over the same bytes.
 inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols, bool lds_a, bool sym,
-                              GemmPlan *pl)
+                              bool argmax, GemmPlan *pl)
 {
     const size_t tile = (size_t)tile_columns(cols);
     const int ws = max_wave_steps(K, splits, wk);
@@ -88,7 +90,7 @@ inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols,
     const size_t z_bytes = sym ? 0 : round_up_sz(groups * (tile / 8), 64) * 4;   // 8 zeros per word
     const size_t wave = a_bytes + s_bytes + z_bytes;
     const size_t header = (size_t)wk * 16 * sizeof(int);
-    const size_t red = (wk > 1 || splits > 1) ? (size_t)wk * M * tile * sizeof(float) : 0;
+    const size_t red = (wk > 1 || splits > 1 || argmax) ? (size_t)wk * M * tile * sizeof(float) : 0;
     const size_t body = (size_t)wk * wave > red ? (size_t)wk * wave : red;
     if (pl) {
         pl->wave_lds = (int)wave;
