@@ -99,9 +99,6 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Exponent field of a bf16 value (0..255).
-__device__ __forceinline__ uint32_t bf16_exp_field(uint32_t bits) { return (bits >> 7) & 0xFFu; }
-
 // Per-row rescale of activations into fp16. With e_max the largest bf16 exponent field of the
 // row's slice, the slice is multiplied by 2^-shift with shift = e_max - 141 so that every
 // magnitude lands below 2^15 (fp16 tops out at 65504). A bf16 value keeps all 8 significant
@@ -137,16 +134,18 @@ __device__ __forceinline__ half8_t act8_to_slots(uint4 raw, float mul)
 // 2^-shift as a float (shift within [-126, 114]).
 __device__ __forceinline__ float pow2_neg(int shift) { return __builtin_amdgcn_ldexpf(1.0f, -shift); }
 
-__device__ __forceinline__ uint32_t max_exp8(uint4 raw)
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+// Largest magnitude bits (sign cleared) of 8 bf16 values, in packed 16-bit halves. The largest
+// magnitude has the largest exponent field: result >> 7 is the largest exponent field of the 8.
+__device__ __forceinline__ uint32_t max_mag8(uint4 raw)
 {
-    const uint32_t v[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t e = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        e = max(e, bf16_exp_field(v[i] & 0xFFFFu));
-        e = max(e, bf16_exp_field(v[i] >> 16));
-    }
-    return e;
+    const ushort2_t a = __builtin_bit_cast(ushort2_t, raw.x & 0x7FFF7FFFu);
+    const ushort2_t b = __builtin_bit_cast(ushort2_t, raw.y & 0x7FFF7FFFu);
+    const ushort2_t c = __builtin_bit_cast(ushort2_t, raw.z & 0x7FFF7FFFu);
+    const ushort2_t d = __builtin_bit_cast(ushort2_t, raw.w & 0x7FFF7FFFu);
+    const ushort2_t r = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    return max((uint32_t)r.x, (uint32_t)r.y);
 }
 
 // Greedy selection on the device, as lucebox PR #823 (PR description) does to avoid reading a

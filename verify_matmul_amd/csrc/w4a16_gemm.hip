@@ -95,7 +95,7 @@ constexpr int kPrepHeld = 4;   // granules a thread keeps in registers between t
 
 __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
 {
-    __shared__ uint32_t s_emax[16];
+    __shared__ uint32_t s_mag[16];   // largest magnitude bits per row
     __shared__ int s_shift[16];
     const int piece = blockIdx.x;
     const int split = piece / p.wk;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
         const int wr = it / M;
         return (size_t)(it - wr * M) * p.K + (size_t)(wb * 4 + wr) * 8;
     };
-    if (threadIdx.x < 16) s_emax[threadIdx.x] = 0;
+    if (threadIdx.x < 16) s_mag[threadIdx.x] = 0;
     __syncthreads();
     // Exponents: the first kPrepHeld granules of each thread stay in registers for the
     // conversion; a piece larger than kPrepHeld x 256 granules reads the rest twice.
@@ -122,17 +122,17 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
     for (int u = 0; u < kPrepHeld; ++u) {
         const int it = threadIdx.x + u * kPrepThreads;
         if (it < items) {
-            const uint32_t e = max_exp8(held[u]);
-            if (e) atomicMax(&s_emax[it % M], e);
+            const uint32_t mag = max_mag8(held[u]);
+            if (mag) atomicMax(&s_mag[it % M], mag);
         }
     }
     for (int it = threadIdx.x + kPrepHeld * kPrepThreads; it < items; it += kPrepThreads) {
-        const uint32_t e = max_exp8(*reinterpret_cast<const uint4 *>(p.A + offset(it)));
-        if (e) atomicMax(&s_emax[it % M], e);
+        const uint32_t mag = max_mag8(*reinterpret_cast<const uint4 *>(p.A + offset(it)));
+        if (mag) atomicMax(&s_mag[it % M], mag);
     }
     __syncthreads();
     if (threadIdx.x < M) {
-        const int sh = act_shift(s_emax[threadIdx.x]);
+        const int sh = act_shift(s_mag[threadIdx.x] >> 7);
         s_shift[threadIdx.x] = sh;
         p.shifts[(size_t)piece * M + threadIdx.x] = sh;
     }
@@ -188,9 +188,10 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     const int g0 = wb / spg;                  // first group of the wave
     const int ng = (we - 1) / spg - g0 + 1;   // groups touched by the wave
 
-    // LDS: [kWK x 16 row shifts][per wave: activations | scales | zeros]
-    int *shift_lds = reinterpret_cast<int *>(smem) + wave * 16;
-    unsigned char *region = smem + kWK * 16 * sizeof(int);
+    // LDS: [kWK x (16 row shifts, 16 row multipliers)][per wave: activations | scales | zeros]
+    int *shift_lds = reinterpret_cast<int *>(smem) + wave * kRowHeader;
+    float *mul_lds = reinterpret_cast<float *>(shift_lds + 16);
+    unsigned char *region = smem + kWK * kRowHeader * sizeof(int);
     unsigned char *wreg = region + (size_t)wave * p.wave_lds;
     uint4 *a_lds = reinterpret_cast<uint4 *>(wreg);                                // [word row][M]
     uint16_t *sc_lds = reinterpret_cast<uint16_t *>(wreg + p.scale_off);           // [group][64]
@@ -209,16 +210,25 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     const int nwr = (we - wb) * 4;   // packed word rows in the wave's range
     const int items = M * nwr;       // 16-byte activation items, item = word row * M + row
     int pre_loads = 0;               // vector memory operations issued before the ring
+    // Lanes walk the items 64 at a time; each tracks the (word row, row) of its item with adds
+    // (64 items = dq word rows and dr rows), so no pass divides by M.
+    const int dq = 64 / M;
+    const int dr = 64 - dq * M;
+    const int wr_l = lane / M;
+    const int m_l = lane - wr_l * M;
 
     // ---- 1. small operands straight into LDS ------------------------------------------------
     if (kLdsA) {
+        int wr = wb * 4 + wr_l, m = m_l;
         for (int b = 0; b < items; b += 64) {
-            int it = b + lane;
-            if (it >= items) it = items - 1;
-            const int wr = it / M;
-            const int m = it - wr * M;
-            load_to_lds16(asrc + (size_t)m * K + (size_t)(wb * 4 + wr) * 8, a_lds + b);
+            if (b + lane < items) load_to_lds16(asrc + (size_t)m * K + (size_t)wr * 8, a_lds + b);
             ++pre_loads;
+            wr += dq;
+            m += dr;
+            if (m >= M) {
+                m -= M;
+                ++wr;
+            }
         }
     }
     {   // scales: kZW items of 8 columns per group
@@ -267,19 +277,31 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     // ---- 3./4. wait for the LDS operands only, convert activations in place ---------------------
     if (pre_loads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLdsA ? kPf : 2 * kPf));
     asm volatile("" ::: "memory");
-    if (kLdsA && !kPreA) {
+    if (kLdsA) {   // each row's largest magnitude (its largest exponent), then its rescale
+        uint32_t run = 0;
+        int m = m_l;
         for (int it = lane; it < items; it += 64) {
-            const int wr = it / M;
-            const uint32_t e = max_exp8(a_lds[it]);
-            if (e) atomicMax(&shift_lds[it - wr * M], (int)e);
+            run = max(run, max_mag8(a_lds[it]));
+            if (dr) {   // the row changes from one item of the lane to the next
+                if (run) atomicMax(&shift_lds[m], (int)run);
+                run = 0;
+                m += dr;
+                if (m >= M) m -= M;
+            }
         }
+        if (run) atomicMax(&shift_lds[m], (int)run);
     }
-    if (lane < 16) shift_lds[lane] = kPreA ? pre_shift : act_shift((uint32_t)shift_lds[lane]);
-    if (kLdsA && !kPreA) {
+    if (lane < M) {
+        const int sh = kPreA ? pre_shift : act_shift((uint32_t)shift_lds[lane] >> 7);
+        shift_lds[lane] = sh;
+        mul_lds[lane] = pow2_neg(sh);
+    }
+    if (kLdsA) {
+        int m = m_l;
         for (int it = lane; it < items; it += 64) {
-            const int wr = it / M;
-            const uint4 raw = a_lds[it];
-            a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(raw, pow2_neg(shift_lds[it - wr * M])));
+            a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(a_lds[it], mul_lds[m]));
+            m += dr;
+            if (m >= M) m -= M;
         }
     }
 

@@ -25,6 +25,9 @@ constexpr int kLdsStageBudget = 8 * 1024;
 // of the tile are then NaN instead of a hang.
 constexpr uint32_t kSpinLimit = 1u << 24;
 
+// Ints of per-row data at the start of a GEMM workgroup's LDS, per wave: 16 rescale exponents
+// and 16 rescale multipliers.
+constexpr int kRowHeader = 32;
 // Ring depth (steps of packed weights in flight per wave). Shallow rings measure best: with
 // thousands of short waves in flight, HBM is kept busy by the number of waves, and a deep ring
 // only lengthens each wave's start. One step deeper when activations are staged in LDS (a slot
@@ -89,7 +92,7 @@ inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols,
     const size_t s_bytes = round_up_sz(groups * (tile / 8), 64) * 16;       // 8 scales per item
     const size_t z_bytes = sym ? 0 : round_up_sz(groups * (tile / 8), 64) * 4;   // 8 zeros per word
     const size_t wave = a_bytes + s_bytes + z_bytes;
-    const size_t header = (size_t)wk * 16 * sizeof(int);
+    const size_t header = (size_t)wk * kRowHeader * sizeof(int);
     const size_t red = (wk > 1 || splits > 1 || argmax) ? (size_t)wk * M * tile * sizeof(float) : 0;
     const size_t body = (size_t)wk * wave > red ? (size_t)wk * wave : red;
     if (pl) {
