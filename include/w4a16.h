@@ -67,7 +67,8 @@ typedef enum { W4A16_OUT_F32 = 0, W4A16_OUT_BF16 = 1 } w4a16_out_dtype;
  *   M in 1..16; N > 0 and a multiple of 8; K > 0 and a multiple of g
  *   out       [M, N] fp32 (out_dtype W4A16_OUT_F32) or bf16 (W4A16_OUT_BF16, round to
  *             nearest even), 16-byte aligned
- * M = 1 runs the single-row GEMV; M = 2..16 run the matrix-core GEMM. Accuracy: every output
+ * M = 1 on 64-column tiles runs the single-row GEMV; everything else (M = 2..16, and M = 1 on
+ * the 128-column tiles of matrices with N >= 32768) runs the matrix-core GEMM. Accuracy: every output
  * is within 4e-3 * sum_k |a_k * w_kn| + 1e-6 of the exact value for finite inputs whose
  * nonzero activations within one row span less than 2^30 in magnitude (activations enter the
  * fp16 matrix cores through an exact power-of-two rescale per row and K-slice).

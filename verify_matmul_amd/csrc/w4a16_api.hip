@@ -158,14 +158,17 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
         return fail(W4A16_ERR_INVALID_ARG, "waves_k=%d is not 1, 2, 4, 8 or 16", wk);
     if (splits < 1 || splits > 65535 || (long long)splits * wk > steps)
         return fail(W4A16_ERR_INVALID_ARG, "splits=%d x waves_k=%d exceeds the %d K-steps of 32", splits, wk, steps);
-    plan->mfma = M > 1;
+    // One row takes the dot-product GEMV on 64-column tiles. On 128-column tiles its eight
+    // columns per lane make the VALU the tighter resource, and the matrix cores (16 rows of which
+    // one is used) measure faster: 248320-column output layer, 120.3 -> 116.1 us.
+    plan->mfma = M > 1 || cols == 8;
     plan->cols = cols;
     plan->wk = wk;
     plan->splits = splits;
     // Stage activations in LDS when a wave's slice fits the per-wave budget: then they arrive by
     // direct loads issued with the weights and are converted once. Past the budget the LDS a
-    // workgroup needs would cut the waves per CU, and converting each fragment as it streams in
-    // (after an exponent pass) measures faster. The GEMV always stages.
+    // workgroup needs would cut the waves per CU; those slices are prepared once per call
+    // instead (below). The GEMV always stages.
     GemmPlan staged{};
     const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, sym, argmax, &staged);
     plan->lds_a = !plan->mfma || ((size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&

@@ -658,11 +658,15 @@ hipError_t launch_wk(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream
     }
 }
 
+// The GEMV runs on 64-column tiles only (128-column tiles go to the matrix cores).
 template <bool kMfma, bool kSym, bool kLdsA>
 hipError_t launch_cols(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
-    return plan.cols == 8 ? launch_wk<kMfma, kSym, kLdsA, 8>(a, plan, stream)
-                          : launch_wk<kMfma, kSym, kLdsA, 4>(a, plan, stream);
+    if constexpr (kMfma)
+        return plan.cols == 8 ? launch_wk<kMfma, kSym, kLdsA, 8>(a, plan, stream)
+                              : launch_wk<kMfma, kSym, kLdsA, 4>(a, plan, stream);
+    else
+        return plan.cols == 4 ? launch_wk<kMfma, kSym, kLdsA, 4>(a, plan, stream) : hipErrorInvalidValue;
 }
 
 template <bool kMfma, bool kLdsA>
