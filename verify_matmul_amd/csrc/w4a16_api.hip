@@ -169,10 +169,13 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
     // direct loads issued with the weights and are converted once. Past the budget the LDS a
     // workgroup needs would cut the waves per CU; those slices are prepared once per call
     // instead (below). The GEMV always stages.
+    // On 128-column tiles, whose registers already limit the waves per CU, the test is whether the
+    // staged workgroups still fit that many waves (output layer, M = 5: 134.4 -> 127.7 us).
     GemmPlan staged{};
     const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, sym, argmax, &staged);
-    plan->lds_a = !plan->mfma || ((size_t)staged.wave_lds <= (size_t)kLdsStageBudget &&
-                                  lds_staged <= (size_t)kMaxLds);
+    const bool fits = cols == 8 ? (size_t)kLdsPerCu / lds_staged >= (size_t)std::max(1, kWideTileWavesPerCu / wk)
+                                : (size_t)staged.wave_lds <= (size_t)kLdsStageBudget;
+    plan->lds_a = !plan->mfma || (fits && lds_staged <= (size_t)kMaxLds);
     // Activations a wave cannot stage are prepared once per call by a separate kernel: without
     // it each wave would run an exponent pass over its slice and convert every fragment as it
     // streams in. Staged slices are converted in the wave (cheaper than the extra launch).

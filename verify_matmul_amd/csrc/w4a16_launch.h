@@ -15,9 +15,14 @@ constexpr int kWideTileMinN = 32768;
 constexpr int kStepK = 32;
 // Largest dynamic LDS a GEMM workgroup may ask for (gfx950: 160 KiB per workgroup).
 constexpr int kMaxLds = 160 * 1024 - 256;
-// Staged activations (plus scales and zero words) per wave beyond which converting fragments
-// per step is preferred: larger staging areas cost more waves per CU than they save.
+// Staged activations (plus scales and zero words) per wave beyond which a 64-column plan takes
+// prepared activations instead: larger staging areas cost more waves per CU than they save.
 constexpr int kLdsStageBudget = 8 * 1024;
+// LDS of one compute unit, and the waves per CU the 128-column matrix-core kernels reach (their
+// registers cap them at 4 waves per SIMD): staging that still leaves room for that many waves
+// costs them nothing.
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kWideTileWavesPerCu = 16;
 
 // Bound on the split-K reducer's wait for another slice's element (each try sleeps about 128
 // cycles).
