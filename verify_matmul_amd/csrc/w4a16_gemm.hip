@@ -318,11 +318,15 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     ZeroSub zs[kC];
 #pragma unroll
     for (int j = 0; j < kC; ++j) zs[j] = zero_sub_sym();
-    int zs_group = -1;
+    // Position in the quantisation groups, kept by counting (all wave-uniform): step t is step
+    // gpos of group gi, and `first` marks the first step of the wave's part of a group.
+    int gi = g0;
+    int gpos = wb - g0 * spg;
+    bool first = true;
 
     // One step: dequantise the ring slot's words, multiply, and scale at a group's end.
     auto step = [&](int t, const uint4 *wv, const uint4 av) {
-        const int gi = t / spg;
+        const bool last = gpos == spg - 1 || t + 1 == we;
         half8_t a;
         if (kLdsA) {
             const int wrow = (t - wb) * 4 + rl;
@@ -336,8 +340,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
             a = __builtin_bit_cast(half8_t, av);   // prepared fragment
             if (cl >= M) a = zero8;
         }
-        if (!kSym && gi != zs_group) {   // zero points change once per group (uniform)
-            zs_group = gi;
+        if (!kSym && first) {   // zero points change once per group (uniform)
             const uint32_t zw = z_lds[(gi - g0) * kZW + (cl * kC) / 8];
 #pragma unroll
             for (int j = 0; j < kC; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
                 acc[j][0] = s;
             }
         }
-        if (((t + 1) % spg == 0) || (t + 1 == we)) {
+        if (last) {
             const uint16_t *sp = sc_lds + (gi - g0) * kTile + cl * kC;
             uint32_t sw[kC / 2];
             if constexpr (kC == 4) {
@@ -395,6 +398,11 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
                     acc[j][0] = 0.f;
                 }
             }
+        }
+        first = last;
+        if (++gpos == spg) {
+            gpos = 0;
+            ++gi;
         }
     };
 
