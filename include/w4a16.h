@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_INVALID_ARG = -1,   /* null pointer, size or divisibility violation, bad dtype */
-    W4A16_ERR_UNSUPPORTED = -2,   /* pointer not 16-byte aligned */
+    W4A16_ERR_UNSUPPORTED = -2,   /* pointer not 16-byte aligned, or qweight of 2^32 words or more */
     W4A16_ERR_HIP = -3,           /* a HIP runtime call failed; see w4a16_last_error() */
     W4A16_ERR_NO_MEMORY = -4      /* the scratch buffer could not be allocated */
 } w4a16_status;
@@ -60,7 +60,7 @@ typedef enum { W4A16_OUT_F32 = 0, W4A16_OUT_BF16 = 1 } w4a16_out_dtype;
 /*
  * out = A x dequant(qweight, scales, qzeros).
  *   A         bf16 [M, K], 16-byte aligned
- *   qweight   uint32 [K/8, N], 16-byte aligned
+ *   qweight   uint32 [K/8, N], 16-byte aligned, fewer than 2^32 words (16 GiB)
  *   scales    fp16 bits [K/g, N], 16-byte aligned
  *   qzeros    uint32 [K/g, N/8], 16-byte aligned, or NULL for the symmetric zero point 8
  *   group_size g: a positive multiple of 32 that divides K

@@ -61,6 +61,7 @@ def gemm(lib, a=A, q=Q, s=S, z=None, g=128, M=1, N=256, K=512, o=O, dt=0):
     (dict(N=-8), -1), (dict(g=48), -1), (dict(g=96), -1), (dict(K=520, g=32), -1),
     (dict(N=260), -1), (dict(a=A + 2), -2), (dict(q=Q + 4), -2), (dict(s=S + 8), -2),
     (dict(z=Z + 4), -2), (dict(o=O + 8), -2), (dict(dt=2), -1), (dict(dt=-1), -1),
+    (dict(N=1 << 20, K=1 << 22), -2),   # qweight of 2^39 words: beyond the 32-bit word offsets
 ])
 def test_gemm_rejects_bad_arguments(lib, kw, status):
     assert gemm(lib, **kw) == status

@@ -199,6 +199,8 @@ int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scal
     if (g % 32) return fail(W4A16_ERR_INVALID_ARG, "group_size=%d is not a multiple of 32", g);
     if (K % g) return fail(W4A16_ERR_INVALID_ARG, "K=%d is not a multiple of group_size=%d", K, g);
     if (N % 8) return fail(W4A16_ERR_INVALID_ARG, "N=%d is not a multiple of 8", N);
+    if ((long long)(K / 8) * N > 0xFFFFFFFFLL)   // the kernels address qweight with 32-bit word offsets
+        return fail(W4A16_ERR_UNSUPPORTED, "qweight of %lld words exceeds 2^32 words", (long long)(K / 8) * N);
     if (!aligned16(A) || !aligned16(qweight) || !aligned16(scales) || (qzeros && !aligned16(qzeros)) ||
         !aligned16(out))
         return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");

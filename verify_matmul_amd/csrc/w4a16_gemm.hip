@@ -264,7 +264,8 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     uint4 ring_a[kLdsA ? 1 : kPf];
     auto load_w = [&](uint4 *dst, int t) {
 #pragma unroll
-        for (int v = 0; v < kV; ++v) dst[v] = *reinterpret_cast<const uint4 *>(qw_lane + (size_t)t * 4 * N + 4 * v);
+        for (int v = 0; v < kV; ++v)   // word offsets fit 32 bits (checked on the host)
+            dst[v] = *reinterpret_cast<const uint4 *>(qw_lane + (uint32_t)(t * 4 * N) + 4 * v);
     };
 #pragma unroll
     for (int u = 0; u < kPf; ++u) {
