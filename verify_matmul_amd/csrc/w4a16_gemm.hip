@@ -276,7 +276,8 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     asm volatile("" ::: "memory");
 
     // ---- 3./4. wait for the LDS operands only, convert activations in place ---------------------
-    if (pre_loads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLdsA ? kPf : 2 * kPf));
+    // (the ring holds kPf steps of kV weight loads, plus one activation fragment each when unstaged)
+    if (pre_loads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPf * (kV + (kLdsA ? 0 : 1))));
     asm volatile("" ::: "memory");
     if (kLdsA) {   // each row's largest magnitude (its largest exponent), then its rescale
         uint32_t run = 0;
