@@ -51,6 +51,9 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Activation items (16 bytes) a lane may stage through registers: 8 KB per wave.
+constexpr int kHeld = 8;
+
 // s_waitcnt encoding (gfx9): wait until at most `n` vector memory operations are outstanding.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
@@ -154,8 +157,15 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
 // kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
 // slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
 // order, rescaled per piece and row -- and stream in with the weights, one fragment per step.
+// Occupancy the register allocator must keep (waves per SIMD; 1 = no constraint). Left to
+// itself it moves the 64-column matrix-core kernels' accumulators into AGPRs whenever a
+// workgroup has at most 4 waves, which costs two waves per SIMD.
+template <bool kMfma, bool kSym, int kC>
+constexpr int gemm_min_waves() { return kMfma && kC == 4 ? (kSym ? 7 : 5) : 1; }
+
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf, int kC>
-__global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
+__global__ __launch_bounds__(kWK * 64)
+__attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a16_gemm_kernel(GemmArgs p)
 {
     constexpr bool kPreA = !kLdsA;
     constexpr int kTile = 16 * kC;      // columns per tile: kC adjacent columns per lane
@@ -217,17 +227,39 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     const int wr_l = lane / M;
     const int m_l = lane - wr_l * M;
 
-    // ---- 1. small operands straight into LDS ------------------------------------------------
+    // ---- 1. small operands: activations into registers, scales and zeros straight into LDS ---
+    // A slice of at most kHeld items per lane is loaded into registers, reduced and converted
+    // there, and written to LDS once as fp16. A longer slice (long one-row pieces) goes into
+    // LDS by direct loads and is reduced and converted in place.
+    const bool held = items <= kHeld * 64;   // uniform
+    uint4 held_a[kHeld];
     if (kLdsA) {
         int wr = wb * 4 + wr_l, m = m_l;
-        for (int b = 0; b < items; b += 64) {
-            if (b + lane < items) load_to_lds16(asrc + (size_t)m * K + (size_t)wr * 8, a_lds + b);
-            ++pre_loads;
-            wr += dq;
-            m += dr;
-            if (m >= M) {
-                m -= M;
-                ++wr;
+        if (held) {
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) {
+                held_a[i] = uint4{0u, 0u, 0u, 0u};
+                if (i * 64 < items) {
+                    if (i * 64 + lane < items)
+                        held_a[i] = *reinterpret_cast<const uint4 *>(asrc + (size_t)m * K + (size_t)wr * 8);
+                    wr += dq;
+                    m += dr;
+                    if (m >= M) {
+                        m -= M;
+                        ++wr;
+                    }
+                }
+            }
+        } else {
+            for (int b = 0; b < items; b += 64) {
+                if (b + lane < items) load_to_lds16(asrc + (size_t)m * K + (size_t)wr * 8, a_lds + b);
+                ++pre_loads;
+                wr += dq;
+                m += dr;
+                if (m >= M) {
+                    m -= M;
+                    ++wr;
+                }
             }
         }
     }
@@ -282,14 +314,21 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     if (kLdsA) {   // each row's largest magnitude (its largest exponent), then its rescale
         uint32_t run = 0;
         int m = m_l;
-        for (int it = lane; it < items; it += 64) {
-            run = max(run, max_mag8(a_lds[it]));
+        auto fold = [&](uint32_t mag) {
+            run = max(run, mag);
             if (dr) {   // the row changes from one item of the lane to the next
                 if (run) atomicMax(&shift_lds[m], (int)run);
                 run = 0;
                 m += dr;
                 if (m >= M) m -= M;
             }
+        };
+        if (held) {
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i)
+                if (i * 64 < items) fold(i * 64 + lane < items ? max_mag8(held_a[i]) : 0u);
+        } else {
+            for (int it = lane; it < items; it += 64) fold(max_mag8(a_lds[it]));
         }
         if (run) atomicMax(&shift_lds[m], (int)run);
     }
@@ -300,10 +339,22 @@ __global__ __launch_bounds__(kWK * 64) void w4a16_gemm_kernel(GemmArgs p)
     }
     if (kLdsA) {
         int m = m_l;
-        for (int it = lane; it < items; it += 64) {
-            a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(a_lds[it], mul_lds[m]));
-            m += dr;
-            if (m >= M) m -= M;
+        if (held) {
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) {
+                if (i * 64 < items) {
+                    if (i * 64 + lane < items)
+                        a_lds[i * 64 + lane] = __builtin_bit_cast(uint4, act8_to_slots(held_a[i], mul_lds[m]));
+                    m += dr;
+                    if (m >= M) m -= M;
+                }
+            }
+        } else {
+            for (int it = lane; it < items; it += 64) {
+                a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(a_lds[it], mul_lds[m]));
+                m += dr;
+                if (m >= M) m -= M;
+            }
         }
     }
 
