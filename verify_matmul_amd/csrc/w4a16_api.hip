@@ -142,15 +142,20 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
     const int cols = tile_cols != 0 ? tile_cols / 16 : (N >= kWideTileMinN ? 8 : 4);
     const int tiles = (N + tile_columns(cols) - 1) / tile_columns(cols);
     if (splits == 0 || wk == 0) {
-        // P pieces per tile: about 4352 waves in all (8192 for more than 8 rows, whose shorter
-        // pieces keep their activation slices within the LDS staging budget, at most 64 pieces
-        // there), at least 8 pieces, at least 5 steps each
+        // P pieces per tile: about 4352 waves in all, at least 8 pieces, of at least 10 steps
+        // up to 4 rows (attention, M = 1: 16 pieces of 10 steps 10.2 us, 32 of 5 10.6 us) and
+        // at least 5 steps beyond (attention, M = 8: 11.9 us with 5 steps, 12.6 with 10); for
+        // more than 8 rows 8192 waves, at most 64 pieces, whose shorter pieces keep their
+        // activation slices within the LDS staging budget. The workgroups per tile are rounded
+        // up to a power of two (FFN down, M = 1..8: 8 beat 7 by 0.5-1.2 us).
         const int want = M > 8 ? 8192 : 4352;
-        const int cap = M > 8 ? std::min(64, steps / 5) : steps / 5;
+        const int cap = M > 8 ? std::min(64, steps / 5) : M > 4 ? steps / 5 : steps / 10;
         const int P = std::max(8, std::min(cap, (want + tiles - 1) / tiles));
         int w = P <= 8 ? P : (P < 32 && M <= 8 ? 4 : 8);
         while (w > 1 && w > steps) w /= 2;
-        const int s = std::max(1, std::min((P + w - 1) / w, steps / w));
+        int s = 1;
+        while (s < (P + w - 1) / w) s *= 2;
+        s = std::max(1, std::min(s, steps / w));
         if (wk == 0) wk = w;
         if (splits == 0) splits = std::max(1, std::min(s, steps / wk));
     }
