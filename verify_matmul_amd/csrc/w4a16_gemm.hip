@@ -616,49 +616,75 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
         }
         return;
     }
-    // Slices are fetched a batch at a time (all loads of a batch in flight together). The batch
-    // is the smallest of 4, 8 or 16 that covers the slices, so few slices fetch no padding.
+    // Slices are fetched a batch at a time. The batch is the smallest of 4, 8 or 16 that covers
+    // the slices, so few slices fetch no padding, and a thread issues the first batch of up to
+    // 8 / batch of its outputs (two at 16 rows with 8 waves) before it adds any: one round trip
+    // for them, overlapped with its own slice's sum from LDS.
     auto reduce = [&](auto batch_tag) {
         constexpr int kBatch = decltype(batch_tag)::value;
-        for (int idx = tid; idx < M * kTile; idx += kThreads) {
-            const int m = idx / kTile;
-            const int c = idx - m * kTile;
-            const int n = tile * kTile + c;
-            const bool in = n < N;
-            const float own = wg_sum(m, c);
-            const uint64_t *col = p.partials + (size_t)m * N + n;
-            const size_t slice = (size_t)M * N;
-            float v = 0.f;
-            bool failed = false;
-            for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
-                const int cnt = min(kBatch, p.splits - sp0);
-                uint64_t part[kBatch];
+        constexpr int kOut = kBatch >= 8 ? 1 : 8 / kBatch;
+        const size_t slice = (size_t)M * N;
+        const int cnt0 = min(kBatch, p.splits);
+        for (int base = tid; base < M * kTile; base += kOut * kThreads) {
+            uint64_t part[kOut][kBatch];
 #pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    part[i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+            for (int o = 0; o < kOut; ++o) {
+                const int idx = base + o * kThreads;
+                const int m = idx / kTile;
+                const int n = tile * kTile + idx - m * kTile;
+                const bool ok = idx < M * kTile && n < N;
+                const uint64_t *col = p.partials + (ok ? (size_t)m * N + n : 0);
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
-                    if (i >= cnt) continue;
-                    const int sp = sp0 + i;
-                    if (sp == split) {
-                        v += own;
-                        continue;
-                    }
-                    uint64_t w = part[i];
-                    uint32_t spins = 0;
-                    while ((w & 0xFFFFFFFF00000000ull) != stamp_hi) {   // not yet stored in this call
-                        __builtin_amdgcn_s_sleep(2);
-                        if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
-                            failed = true;
-                            break;
-                        }
-                        w = __hip_atomic_load(col + (size_t)sp * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    v += __builtin_bit_cast(float, (uint32_t)w);
+                    part[o][i] = 0;
+                    if (ok)
+                        part[o][i] = __hip_atomic_load(col + (size_t)min(i, cnt0 - 1) * slice, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
-            emit(m, n, failed ? __builtin_nanf("") : v, in);
+#pragma unroll
+            for (int o = 0; o < kOut; ++o) {
+                const int idx = base + o * kThreads;
+                if (idx >= M * kTile) continue;   // wave-uniform: M * kTile is a multiple of 64
+                const int m = idx / kTile;
+                const int c = idx - m * kTile;
+                const int n = tile * kTile + c;
+                const bool in = n < N;
+                const float own = wg_sum(m, c);
+                const uint64_t *col = p.partials + (size_t)m * N + n;
+                float v = 0.f;
+                bool failed = false;
+                for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
+                    const int cnt = min(kBatch, p.splits - sp0);
+                    if (sp0 > 0) {   // more than 16 slices: the next batch of this output
+#pragma unroll
+                        for (int i = 0; i < kBatch; ++i)
+                            part[o][i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int i = 0; i < kBatch; ++i) {
+                        if (i >= cnt) continue;
+                        const int sp = sp0 + i;
+                        if (sp == split) {
+                            v += own;
+                            continue;
+                        }
+                        uint64_t w = part[o][i];
+                        uint32_t spins = 0;
+                        while ((w & 0xFFFFFFFF00000000ull) != stamp_hi) {   // not yet stored in this call
+                            __builtin_amdgcn_s_sleep(2);
+                            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                                failed = true;
+                                break;
+                            }
+                            w = __hip_atomic_load(col + (size_t)sp * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                        v += __builtin_bit_cast(float, (uint32_t)w);
+                    }
+                }
+                emit(m, n, failed ? __builtin_nanf("") : v, in);
+            }
         }
     };
     if (p.splits <= 4)
