@@ -148,6 +148,17 @@ __device__ __forceinline__ uint32_t max_mag8(uint4 raw)
     return max((uint32_t)r.x, (uint32_t)r.y);
 }
 
+// The same maximum kept packed (two 16-bit halves), folded into a running packed maximum.
+__device__ __forceinline__ uint32_t max_mag8_packed(uint4 raw, uint32_t run)
+{
+    const ushort2_t a = __builtin_bit_cast(ushort2_t, raw.x & 0x7FFF7FFFu);
+    const ushort2_t b = __builtin_bit_cast(ushort2_t, raw.y & 0x7FFF7FFFu);
+    const ushort2_t c = __builtin_bit_cast(ushort2_t, raw.z & 0x7FFF7FFFu);
+    const ushort2_t d = __builtin_bit_cast(ushort2_t, raw.w & 0x7FFF7FFFu);
+    const ushort2_t r = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(r, __builtin_bit_cast(ushort2_t, run)));
+}
+
 // Greedy selection on the device, as lucebox PR #823 (PR description) does to avoid reading a
 // whole vocabulary row back to the host. A (value, index) pair is packed into one 64-bit key
 // whose unsigned order is "larger value first, then smaller index": the high word is the fp32

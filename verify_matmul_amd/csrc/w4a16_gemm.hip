@@ -243,10 +243,12 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                     if (i * 64 + lane < items)
                         held_a[i] = *reinterpret_cast<const uint4 *>(asrc + (size_t)m * K + (size_t)wr * 8);
                     wr += dq;
-                    m += dr;
-                    if (m >= M) {
-                        m -= M;
-                        ++wr;
+                    if (dr) {   // uniform: rows change only when M does not divide 64
+                        m += dr;
+                        if (m >= M) {
+                            m -= M;
+                            ++wr;
+                        }
                     }
                 }
             }
@@ -323,7 +325,13 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                 if (m >= M) m -= M;
             }
         };
-        if (held) {
+        if (held && !dr) {   // fixed rows: a packed running maximum, its halves folded once
+            uint32_t pk = 0;
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i)
+                if (i * 64 < items && i * 64 + lane < items) pk = max_mag8_packed(held_a[i], pk);
+            run = max(pk & 0xFFFFu, pk >> 16);
+        } else if (held) {
 #pragma unroll
             for (int i = 0; i < kHeld; ++i)
                 if (i * 64 < items) fold(i * 64 + lane < items ? max_mag8(held_a[i]) : 0u);
@@ -339,7 +347,13 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     }
     if (kLdsA) {
         int m = m_l;
-        if (held) {
+        if (held && !dr) {   // fixed rows: one multiplier per lane
+            const float mul = mul_lds[m_l];
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i)
+                if (i * 64 < items && i * 64 + lane < items)
+                    a_lds[i * 64 + lane] = __builtin_bit_cast(uint4, act8_to_slots(held_a[i], mul));
+        } else if (held) {
 #pragma unroll
             for (int i = 0; i < kHeld; ++i) {
                 if (i * 64 < items) {
