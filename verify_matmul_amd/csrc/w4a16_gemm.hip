@@ -265,27 +265,26 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             }
         }
     }
-    {   // scales: kZW items of 8 columns per group
+    {   // scales: kZW items of 8 columns per group (lanes past the last item stay idle, so the
+        // LDS area holds exactly the wave's groups)
         const int sitems = ng * kZW;
         for (int b = 0; b < sitems; b += 64) {
-            int it = b + lane;
-            if (it >= sitems) it = sitems - 1;
+            const int it = b + lane;
             const int gi = g0 + it / kZW;
             int c = tile * kTile + (it % kZW) * 8;
             if (c >= N) c = 0;
-            load_to_lds16(p.scales + (size_t)gi * N + c, sc_lds + (size_t)b * 8);
+            if (it < sitems) load_to_lds16(p.scales + (size_t)gi * N + c, sc_lds + (size_t)b * 8);
             ++pre_loads;
         }
     }
     if (!kSym) {   // zero words: kZW per group (8 columns each)
         const int zitems = ng * kZW;
         for (int b = 0; b < zitems; b += 64) {
-            int it = b + lane;
-            if (it >= zitems) it = zitems - 1;
+            const int it = b + lane;
             const int gi = g0 + it / kZW;
             int c = tile * kTile + (it % kZW) * 8;
             if (c >= N) c = 0;
-            load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
+            if (it < zitems) load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
             ++pre_loads;
         }
     }

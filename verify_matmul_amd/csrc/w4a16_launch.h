@@ -84,8 +84,8 @@ inline int max_wave_steps(int K, int splits, int wk)
 inline size_t round_up_sz(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // LDS layout of a plan: per-wave row shifts, then one staging area per wave (activations if
-// staged, the scales and the zero words of the wave's groups; each filled by whole 64-lane
-// direct loads), and, after the main loop, the cross-wave reduction buffer over the same bytes.
+// staged, the scales and the zero words of the wave's groups, filled by direct loads), and,
+// after the main loop, the cross-wave reduction buffer over the same bytes.
 inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols, bool lds_a, bool sym,
                               bool argmax, GemmPlan *pl)
 {
@@ -94,8 +94,8 @@ inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols,
     const int spg = g / kStepK;
     const size_t groups = (size_t)(ws + spg - 1) / spg + 1;
     const size_t a_bytes = lds_a ? round_up_sz((size_t)M * ws * 4, 64) * 16 : 0;
-    const size_t s_bytes = round_up_sz(groups * (tile / 8), 64) * 16;       // 8 scales per item
-    const size_t z_bytes = sym ? 0 : round_up_sz(groups * (tile / 8), 64) * 4;   // 8 zeros per word
+    const size_t s_bytes = groups * (tile / 8) * 16;                         // 8 scales per item
+    const size_t z_bytes = sym ? 0 : round_up_sz(groups * (tile / 8) * 4, 16);   // 8 zeros per word
     const size_t wave = a_bytes + s_bytes + z_bytes;
     const size_t header = (size_t)wk * kRowHeader * sizeof(int);
     const size_t red = (wk > 1 || splits > 1 || argmax) ? (size_t)wk * M * tile * sizeof(float) : 0;
