@@ -92,65 +92,52 @@ __device__ __forceinline__ void piece_range(int steps, int splits, int wk, int s
 // Activation preparation for the matrix-core path, once per call instead of once per column
 // tile: for each K piece of the launch and each row, the largest bf16 exponent gives the
 // power-of-two rescale (see act_shift), and the piece's activations are stored as fp16 in the
-// packed-word slot order with that rescale applied. One workgroup per piece.
-constexpr int kPrepThreads = 256;
-constexpr int kPrepHeld = 4;   // granules a thread keeps in registers between the two phases
+// packed-word slot order with that rescale applied. One wave per (piece, row): its items stay
+// in registers, the row maximum is a wave reduction, and no LDS or barrier is involved.
+constexpr int kPrepWaves = 4;   // rows per workgroup
+constexpr int kPrepHeld = 4;    // items (16 bytes) a lane keeps in registers between the passes
 
-__global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(ActPrepArgs p)
+__global__ __launch_bounds__(kPrepWaves * 64) void act_prep_kernel(ActPrepArgs p)
 {
-    __shared__ uint32_t s_mag[16];   // largest magnitude bits per row
-    __shared__ int s_shift[16];
     const int piece = blockIdx.x;
+    const int m = blockIdx.y * kPrepWaves + (int)(threadIdx.x >> 6);
+    if (m >= p.M) return;   // whole waves: no barrier follows
+    const int lane = threadIdx.x & 63;
     const int split = piece / p.wk;
     const int wave = piece - split * p.wk;
     int wb, we;
     piece_range(p.K / kStepK, p.splits, p.wk, split, wave, wb, we);
-    const int M = p.M;
-    const int items = M * (we - wb) * 4;   // 16-byte granules, item = word row * M + row
-    auto offset = [&](int it) {
-        const int wr = it / M;
-        return (size_t)(it - wr * M) * p.K + (size_t)(wb * 4 + wr) * 8;
-    };
-    if (threadIdx.x < 16) s_mag[threadIdx.x] = 0;
-    __syncthreads();
-    // Exponents: the first kPrepHeld granules of each thread stay in registers for the
-    // conversion; a piece larger than kPrepHeld x 256 granules reads the rest twice.
+    const int nwr = (we - wb) * 4;   // word rows (16-byte items) of the row in this piece
+    const size_t base = (size_t)m * p.K + (size_t)wb * 4 * 8;
+    // Largest magnitude: the first kPrepHeld x 64 items stay in registers for the conversion;
+    // a longer piece reads the rest twice.
     uint4 held[kPrepHeld];
+    uint32_t mag = 0;
 #pragma unroll
     for (int u = 0; u < kPrepHeld; ++u) {
-        const int it = threadIdx.x + u * kPrepThreads;
-        held[u] = *reinterpret_cast<const uint4 *>(p.A + offset(min(it, items - 1)));
-    }
-#pragma unroll
-    for (int u = 0; u < kPrepHeld; ++u) {
-        const int it = threadIdx.x + u * kPrepThreads;
-        if (it < items) {
-            const uint32_t mag = max_mag8(held[u]);
-            if (mag) atomicMax(&s_mag[it % M], mag);
+        const int it = lane + 64 * u;
+        held[u] = uint4{0u, 0u, 0u, 0u};
+        if (it < nwr) {
+            held[u] = *reinterpret_cast<const uint4 *>(p.A + base + (size_t)it * 8);
+            mag = max(mag, max_mag8(held[u]));
         }
     }
-    for (int it = threadIdx.x + kPrepHeld * kPrepThreads; it < items; it += kPrepThreads) {
-        const uint32_t mag = max_mag8(*reinterpret_cast<const uint4 *>(p.A + offset(it)));
-        if (mag) atomicMax(&s_mag[it % M], mag);
-    }
-    __syncthreads();
-    if (threadIdx.x < M) {
-        const int sh = act_shift(s_mag[threadIdx.x] >> 7);
-        s_shift[threadIdx.x] = sh;
-        p.shifts[(size_t)piece * M + threadIdx.x] = sh;
-    }
-    __syncthreads();
+    for (int it = lane + 64 * kPrepHeld; it < nwr; it += 64)
+        mag = max(mag, max_mag8(*reinterpret_cast<const uint4 *>(p.A + base + (size_t)it * 8)));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, o));
+    const int sh = act_shift(mag >> 7);
+    if (lane == 0) p.shifts[(size_t)piece * p.M + m] = sh;
+    const float mul = pow2_neg(sh);
 #pragma unroll
     for (int u = 0; u < kPrepHeld; ++u) {
-        const int it = threadIdx.x + u * kPrepThreads;
-        if (it < items)
-            *reinterpret_cast<uint4 *>(p.A16 + offset(it)) =
-                __builtin_bit_cast(uint4, act8_to_slots(held[u], pow2_neg(s_shift[it % M])));
+        const int it = lane + 64 * u;
+        if (it < nwr)
+            *reinterpret_cast<uint4 *>(p.A16 + base + (size_t)it * 8) = __builtin_bit_cast(uint4, act8_to_slots(held[u], mul));
     }
-    for (int it = threadIdx.x + kPrepHeld * kPrepThreads; it < items; it += kPrepThreads) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(p.A + offset(it));
-        *reinterpret_cast<uint4 *>(p.A16 + offset(it)) =
-            __builtin_bit_cast(uint4, act8_to_slots(raw, pow2_neg(s_shift[it % M])));
+    for (int it = lane + 64 * kPrepHeld; it < nwr; it += 64) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(p.A + base + (size_t)it * 8);
+        *reinterpret_cast<uint4 *>(p.A16 + base + (size_t)it * 8) = __builtin_bit_cast(uint4, act8_to_slots(raw, mul));
     }
 }
 
@@ -728,7 +715,8 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
     const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf, kC>;
     if (!kLdsA) {
         ActPrepArgs pa{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK};
-        hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(a.splits * kWK)), dim3(kPrepThreads), 0, stream, pa);
+        hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(a.splits * kWK), (unsigned)((a.M + kPrepWaves - 1) / kPrepWaves)),
+                           dim3(kPrepWaves * 64), 0, stream, pa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
