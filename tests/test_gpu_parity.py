@@ -78,6 +78,8 @@ SHAPES = [   # (K, N, group, symmetric): several tiles, ragged column tails, une
     (1088, 520, 32, False),
     (2048, 8, 64, True),
     (4096, 776, 4096, False),
+    (8192, 136, 128, True),    # one workgroup per tile: slices past 8 items per lane (direct-to-LDS staging)
+    (8192, 72, 64, False),
 ]
 
 
