@@ -216,28 +216,22 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
 
     // ---- 1. small operands: activations into registers, scales and zeros straight into LDS ---
     // A slice of at most kHeld items per lane is loaded into registers, reduced and converted
-    // there, and written to LDS once as fp16. A longer slice (long one-row pieces) goes into
-    // LDS by direct loads and is reduced and converted in place.
-    const bool held = items <= kHeld * 64;   // uniform
+    // there, and written to LDS once as fp16. There every lane keeps one row: lane l takes row
+    // l % M and word rows l / M + i * dq, so item l + i * dq * M (lanes from dq * M on idle when M
+    // does not divide 64). A longer slice (long one-row pieces) goes into LDS by direct loads
+    // and is reduced and converted in place.
+    const bool held = (nwr + dq - 1) / dq <= kHeld;   // uniform
+    const bool lane_on = lane < dq * M;
     uint4 held_a[kHeld];
+    auto held_ok = [&](int i) { return lane_on && wr_l + i * dq < nwr; };
     if (kLdsA) {
         int wr = wb * 4 + wr_l, m = m_l;
         if (held) {
 #pragma unroll
             for (int i = 0; i < kHeld; ++i) {
                 held_a[i] = uint4{0u, 0u, 0u, 0u};
-                if (i * 64 < items) {
-                    if (i * 64 + lane < items)
-                        held_a[i] = *reinterpret_cast<const uint4 *>(asrc + (size_t)m * K + (size_t)wr * 8);
-                    wr += dq;
-                    if (dr) {   // uniform: rows change only when M does not divide 64
-                        m += dr;
-                        if (m >= M) {
-                            m -= M;
-                            ++wr;
-                        }
-                    }
-                }
+                if (i * dq < nwr && held_ok(i))   // (uniform, then per lane)
+                    held_a[i] = *reinterpret_cast<const uint4 *>(asrc + (size_t)m_l * K + (size_t)(wr + i * dq) * 8);
             }
         } else {
             for (int b = 0; b < items; b += 64) {
@@ -311,16 +305,12 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                 if (m >= M) m -= M;
             }
         };
-        if (held && !dr) {   // fixed rows: a packed running maximum, its halves folded once
+        if (held) {   // the lane's row is fixed: a packed running maximum, its halves folded once
             uint32_t pk = 0;
 #pragma unroll
             for (int i = 0; i < kHeld; ++i)
-                if (i * 64 < items && i * 64 + lane < items) pk = max_mag8_packed(held_a[i], pk);
+                if (i * dq < nwr && held_ok(i)) pk = max_mag8_packed(held_a[i], pk);
             run = max(pk & 0xFFFFu, pk >> 16);
-        } else if (held) {
-#pragma unroll
-            for (int i = 0; i < kHeld; ++i)
-                if (i * 64 < items) fold(i * 64 + lane < items ? max_mag8(held_a[i]) : 0u);
         } else {
             for (int it = lane; it < items; it += 64) fold(max_mag8(a_lds[it]));
         }
@@ -333,22 +323,12 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     }
     if (kLdsA) {
         int m = m_l;
-        if (held && !dr) {   // fixed rows: one multiplier per lane
-            const float mul = mul_lds[m_l];
+        if (held) {   // one multiplier per lane (its row)
+            const float mul = lane_on ? mul_lds[m_l] : 0.f;
 #pragma unroll
             for (int i = 0; i < kHeld; ++i)
-                if (i * 64 < items && i * 64 + lane < items)
-                    a_lds[i * 64 + lane] = __builtin_bit_cast(uint4, act8_to_slots(held_a[i], mul));
-        } else if (held) {
-#pragma unroll
-            for (int i = 0; i < kHeld; ++i) {
-                if (i * 64 < items) {
-                    if (i * 64 + lane < items)
-                        a_lds[i * 64 + lane] = __builtin_bit_cast(uint4, act8_to_slots(held_a[i], mul_lds[m]));
-                    m += dr;
-                    if (m >= M) m -= M;
-                }
-            }
+                if (i * dq < nwr && held_ok(i))
+                    a_lds[lane + i * dq * M] = __builtin_bit_cast(uint4, act8_to_slots(held_a[i], mul));
         } else {
             for (int it = lane; it < items; it += 64) {
                 a_lds[it] = __builtin_bit_cast(uint4, act8_to_slots(a_lds[it], mul_lds[m]));
