@@ -1,40 +1,41 @@
 // W4A16 GEMV (M = 1) and small-M MFMA GEMM (M = 1..16) for gfx950.
 //
 // Work layout
-//   * A column tile is 64 columns, one wave wide. Lane l owns 4 adjacent columns (one 128-bit
-//     load per packed word row) and word row l / 16 of every 4-row step, so one wave-wide load
-//     fetches 4 rows x 256 contiguous bytes.
+//   * A column tile is one wave wide: 64 columns (4 adjacent columns per lane), or 128 (8 per
+//     lane) for wide matrices. Lane l owns its columns' 16-byte loads of word row l / 16 of
+//     every 4-row step, so one wave-wide load fetches 4 rows x 256 contiguous bytes.
 //   * The `wk` waves of a workgroup share one column tile and split its K range into contiguous
-//     pieces; their sums meet in LDS at the end. With enough column tiles (N >= 16384) every
-//     workgroup owns a tile outright and no reduction ever leaves the CU.
-//   * Narrow matrices also split K across `splits` workgroups. Their fp32 partials are written
-//     with agent-scope atomic stores and the last workgroup to arrive (atomic counter) adds them
-//     in slice order, so results are bit-identical from run to run. Because the partials are
-//     themselves coherent atomic stores, publishing them needs only a wait for their completion,
-//     not an L2 write-back. The pages reduce split-K through per-slice partials too on GPUs
-//     without thread-block clusters (TensorFold PR #859, commit messages).
+//     pieces; their sums meet in LDS at the end.
+//   * `splits` workgroups per tile split K further. Their fp32 partials are written with
+//     agent-scope atomic stores and the workgroup that started last adds them in slice order,
+//     so results are bit-identical from run to run. Because the partials are themselves
+//     coherent atomic stores, publishing them needs no L2 write-back. The pages reduce split-K
+//     through per-slice partials too on GPUs without thread-block clusters (TensorFold PR #859,
+//     commit messages).
 //
 // Latency first. A wave lives for a few microseconds, only a handful of HBM round trips, so it
 // starts all its memory traffic at once:
-//   1. direct global->LDS loads (global_load_lds) of everything small the wave will need: its
-//      activations (raw bf16), and the scales and zero points of its groups;
+//   1. its activation slice into registers (or, for a long one-row slice, straight into LDS),
+//      and the scales and zero points of its groups straight into LDS (global_load_lds);
 //   2. a ring of kPf steps of packed weights into registers;
 //   3. a wait for (1) only: loads retire in order, so "at most the ring outstanding" suffices;
-//   4. activations are converted in place in LDS while the weights are still in flight.
+//   4. the activations are rescaled and converted to fp16 and written to LDS once, while the
+//      weights are still in flight.
 // The ring then issues exactly one step per iteration (clamped past the wave's end), so the
 // compiler waits for the oldest step only.
 //
-// Per step (32 K rows x 64 columns per wave)
+// Per step (32 K rows x one tile per wave)
 //   * each packed word becomes 8 exact fp16 values (q - z) (w4a16_device.h);
-//   * GEMV: v_dot2c_f32_f16 into one fp32 sum per column; the four word rows of a step are
-//     added across lanes at the end. GEMM: one v_mfma_f32_16x16x32_f16 per word column
-//     (16 rows x 16 columns x 32 K), activations padded with zero rows up to 16;
+//   * GEMV (one row, 64-column tiles): v_dot2c_f32_f16 into one fp32 sum per column; the four
+//     word rows of a step are added across lanes at the end. Otherwise one
+//     v_mfma_f32_16x16x32_f16 per word column (16 rows x 16 columns x 32 K), activations padded
+//     with zero rows up to 16;
 //   * sums are kept per quantisation group and scaled once at the group's end.
 //
 // Activations are fp16 after an exact per-row power-of-two rescale chosen from the row's largest
-// exponent over the wave's K range. With up to 8 rows they are staged in LDS as above; with more
-// rows (whose staging would not fit) each lane converts its MFMA fragment as it arrives through
-// the ring, after a first pass that only finds the exponents.
+// exponent over the wave's K range. A slice too large to stage without costing waves per CU is
+// prepared once per call by act_prep_kernel instead, and its fragments stream in with the
+// weights.
 //
 // Why this shape (GRIMOIRE v1.7 release notes, 'What changed': a GEMV for one user and a
 // matrix-engine GEMM for 2-16 rows; GRIMOIRE v1.8, 'What changed': the small-row kernel got
@@ -141,15 +142,15 @@ __global__ __launch_bounds__(kPrepWaves * 64) void act_prep_kernel(ActPrepArgs p
     }
 }
 
-// kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
-// slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
-// order, rescaled per piece and row -- and stream in with the weights, one fragment per step.
 // Occupancy the register allocator must keep (waves per SIMD; 1 = no constraint). Left to
 // itself it moves the 64-column matrix-core kernels' accumulators into AGPRs whenever a
 // workgroup has at most 4 waves, which costs two waves per SIMD.
 template <bool kMfma, bool kSym, int kC>
 constexpr int gemm_min_waves() { return kMfma && kC == 4 ? (kSym ? 7 : 5) : 1; }
 
+// kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
+// slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
+// order, rescaled per piece and row -- and stream in with the weights, one fragment per step.
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf, int kC>
 __global__ __launch_bounds__(kWK * 64)
 __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a16_gemm_kernel(GemmArgs p)
@@ -207,8 +208,9 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     const int nwr = (we - wb) * 4;   // packed word rows in the wave's range
     const int items = M * nwr;       // 16-byte activation items, item = word row * M + row
     int pre_loads = 0;               // vector memory operations issued before the ring
-    // Lanes walk the items 64 at a time; each tracks the (word row, row) of its item with adds
-    // (64 items = dq word rows and dr rows), so no pass divides by M.
+    // 64 items are dq word rows and dr rows: the register path gives each lane the fixed row
+    // m_l (below); the direct-to-LDS path walks the items 64 at a time and tracks each item's
+    // (word row, row) with adds. Neither divides by M per item.
     const int dq = 64 / M;
     const int dr = 64 - dq * M;
     const int wr_l = lane / M;
@@ -289,7 +291,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     }
     asm volatile("" ::: "memory");
 
-    // ---- 3./4. wait for the LDS operands only, convert activations in place ---------------------
+    // ---- 3./4. wait for the staged operands only, then rescale and convert the activations -------
     // (the ring holds kPf steps of kV weight loads, plus one activation fragment each when unstaged)
     if (pre_loads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPf * (kV + (kLdsA ? 0 : 1))));
     asm volatile("" ::: "memory");
@@ -543,10 +545,10 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     // argmax_keys_finish_kernel, next on the stream, turns the keys into indices and clears
     // them (the same keys as argmax_rows_kernel, so the result equals its pick over the fp32
     // outputs). A tile that waited for its merge to land, or counted itself out on a shared
-    // counter, would hold its compute unit a memory round trip longer. All lanes of a wave hold outputs of one
-    // row (a tile's width is a multiple of 64), so the keys are first reduced across the wave
-    // and one LDS atomic per wave folds them in: emit is called by every lane of the wave
-    // together, with `ok` false for columns past N.
+    // counter, would hold its compute unit a memory round trip longer. All lanes of a wave hold
+    // outputs of one row (a tile's width is a multiple of 64), so the keys are first reduced
+    // across the wave and one LDS atomic per wave folds them in: emit is called by every lane of
+    // the wave together, with `ok` false for columns past N.
     auto emit = [&](int m, int n, float v, bool ok) {
         if (ok) store_out(m, n, v);
         if (amax) {
