@@ -28,8 +28,9 @@
  *   - Arguments are checked on the host before any device work; a non-OK status means no
  *     device work was enqueued. The library never aborts and never prints: w4a16_last_error()
  *     returns a description of the last non-OK status of the calling thread.
- *   - The library owns one scratch buffer per (device, stream) for split-K partial sums and
- *     tile counters. It is allocated on the first call that needs it on that stream (and grown
+ *   - The library owns one scratch buffer per (device, stream) for split-K partial sums, tile
+ *     counters, prepared activations and the fused pick's row keys. It is allocated (with
+ *     hipMalloc, then zeroed) on the first call that needs it on that stream (and grown
  *     if a later call needs more), so warm a stream up before timing or capturing it. Calls on
  *     different streams never share scratch; calls on one stream are ordered, and calls that
  *     run concurrently on one stream's scratch (e.g. the same stream used from two graphs
