@@ -104,8 +104,8 @@ def load_traffic(workload, M):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              f"(the column-sharded multi-GPU layout is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(more GPUs would each take a column shard of the weights)", file=sys.stderr)
         return 2
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if world != 1:

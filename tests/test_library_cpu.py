@@ -126,3 +126,16 @@ def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.w4a16_status_string(st)
     assert lib.w4a16_version() >= 100
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the refusal comes before any GPU or torch import, so it runs on the CPU
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    r = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 2
+    assert "--gpus 2 is not supported" in r.stderr
+    assert r.stdout == ""
