@@ -112,6 +112,33 @@ def test_wide_dynamic_range_rows(gu):
             parity.check_close(d.run(M, splits=splits, waves_k=wk), y_ref, bound, f"range M={M}")
 
 
+def test_power_of_two_activation_scaling_is_exact(gu):
+    """Scaling every activation by 2^k scales every output by exactly 2^k: the per-slice rescale
+    into fp16 is exact, so it absorbs any power of two, from slices far below fp16's range to
+    slices above it, and for held and LDS-staged slices alike."""
+    rng = np.random.default_rng(27)
+    K, N, g = 2048, 520, 128
+    mag = np.exp2(rng.uniform(-6.0, 2.0, size=(16, K))).astype(np.float32)
+    a = np.where(rng.integers(0, 2, size=(16, K)) == 1, mag, -mag).astype(np.float32)
+    a[rng.random((16, K)) < 0.05] = 0.0       # exact zeros: must stay zero in either form
+    a[:, ::32] = 3.0                          # every slice's largest magnitude is in [2, 4)
+    a = a.view(np.uint32) & np.uint32(0xFFFF0000)   # already bf16: scaling by 2^k stays exact
+    base = synth.f32_to_bf16_bits(a.view(np.float32))
+    inp = synth.Inputs(synth.random_words(rng, (K // 8, N)), synth.draw_scales(rng, (K // g, N), 0.002, 0.02),
+                       synth.random_words(rng, (K // g, N // 8)), base, g)
+    d = gu.DevInputs(inp)
+    launches = ((0, 0, 0), (1, 1, 0), (4, 2, 0), (0, 0, 128))
+    for M in (1, 5, 16):
+        ys = {c: d.run(M, splits=c[0], waves_k=c[1], tile_cols=c[2]) for c in launches}
+        for k in (-90, -89, -40, 13, 14, 20):
+            scaled = synth.f32_to_bf16_bits(a.view(np.float32)[:M] * np.float32(2.0 ** k))
+            act = gu.dev_u16(scaled)
+            for c in launches:
+                gu.say(f"[2^k] M={M} k={k} splits={c[0]} waves_k={c[1]} tile_cols={c[2]}")
+                assert np.array_equal(d.run(M, act=act, splits=c[0], waves_k=c[1], tile_cols=c[2]),
+                                      ys[c] * 2.0 ** k)
+
+
 def test_argmax_edge_cases(gu):
     rows = []
     N = 40000                                   # more than two argmax chunks, ragged tail
