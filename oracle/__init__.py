@@ -49,8 +49,11 @@ def _load():
         lib.w4o_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         lib.w4o_gemm.argtypes = [P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
         lib.w4o_argmax_rows_f32.argtypes = [P, I64, I64, P]
+        lib.w4o_silu.argtypes = [ctypes.c_double]
+        lib.w4o_silu.restype = ctypes.c_double
+        lib.w4o_silu_mul.argtypes = [P, P, I64, P]
         for f in (lib.w4o_unpack_qweight, lib.w4o_unpack_qzeros, lib.w4o_dequant,
-                  lib.w4o_gemm, lib.w4o_argmax_rows_f32):
+                  lib.w4o_gemm, lib.w4o_argmax_rows_f32, lib.w4o_silu_mul):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -136,3 +139,28 @@ def argmax_rows_f32(v: np.ndarray) -> np.ndarray:
     _check(_load().w4o_argmax_rows_f32(_ptr(x), M, N, _ptr(idx)), "argmax")
     return idx
 
+
+
+def silu(x: float) -> float:
+    """x / (1 + e^-x) in fp64."""
+    return _load().w4o_silu(float(x))
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """silu(g) * u elementwise, fp64 (same shapes)."""
+    gg = _c(g, np.float64)
+    uu = _c(u, np.float64)
+    assert gg.shape == uu.shape
+    h = np.empty(gg.shape, dtype=np.float64)
+    _check(_load().w4o_silu_mul(_ptr(gg), _ptr(uu), gg.size, _ptr(h)), "silu_mul")
+    return h
+
+
+def gate_up(act, gate, up, group: int, cols: Optional[Sequence[int]] = None):
+    """Gated feed-forward input silu(A x W_gate) * (A x W_up) for columns ``cols`` (all when None).
+
+    ``gate`` and ``up`` are (qweight, scales, qzeros) triples of the same shape. Returns h, and
+    the two products with their bounds: (h, y_gate, bound_gate, y_up, bound_up), all fp64."""
+    yg, bg = gemm(act, gate[0], gate[1], gate[2], group, cols)
+    yu, bu = gemm(act, up[0], up[1], up[2], group, cols)
+    return silu_mul(yg, yu), yg, bg, yu, bu

@@ -193,3 +193,23 @@ int w4o_argmax_rows_f32(const float *v, int64_t M, int64_t N, int64_t *idx)
     }
     return 0;
 }
+
+/* ---- gated feed-forward input: SiLU(gate) * up ------------------------------------------ */
+
+/*
+ * The GRIMOIRE v1.8 release notes ('What changed', INT4 prompt processing) fuse the
+ * feed-forward gate into the int4 matmul path. The pages do not name the gate's nonlinearity;
+ * the Qwen-family feed-forward they run is the SiLU-gated one, so the gated product is
+ *   h[i] = silu(g[i]) * u[i],   silu(x) = x / (1 + e^-x),
+ * here with g = A x W_gate and u = A x W_up, both the fp64 products of w4o_gemm.
+ */
+double w4o_silu(double x) { return x / (1.0 + exp(-x)); }
+
+int w4o_silu_mul(const double *g, const double *u, int64_t n, double *h)
+{
+    if (!g || !u || !h || n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        h[i] = w4o_silu(g[i]) * u[i];
+    return 0;
+}

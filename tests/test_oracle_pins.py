@@ -244,3 +244,76 @@ def test_oracle_rejects_bad_arguments(orc):
         orc.gemm(inp.act, inp.qweight, inp.scales, None, 48)                 # K % g != 0
     with pytest.raises(ValueError):
         orc.gemm(inp.act, inp.qweight, inp.scales, None, 32, cols=[16])      # column out of range
+
+
+# ---- the gated feed-forward input: silu(A x W_gate) * (A x W_up) --------------------------
+
+def test_silu_closed_forms(orc):
+    """silu(x) = x * logistic(x): logistic(1) = e / (1 + e), silu(0) = 0, silu(x) -> x for large
+    x and -> 0 for large -x, and the odd part silu(x) - silu(-x) = x."""
+    e = float(np.e)
+    assert orc.silu(0.0) == 0.0
+    assert abs(orc.silu(1.0) - e / (1.0 + e)) <= 1e-16
+    assert abs(orc.silu(2.0) - 2.0 * e * e / (1.0 + e * e)) <= 1e-15
+    assert orc.silu(64.0) == 64.0
+    assert -1e-20 < orc.silu(-64.0) < 0.0
+    for x in (0.25, 1.5, 3.0, 7.0, 20.0):
+        assert abs((orc.silu(x) - orc.silu(-x)) - x) <= 4e-15 * max(1.0, x)
+
+
+def test_silu_slope_bound(orc):
+    """The test tolerance for the gated product uses max |silu'| <= 1.1 (the true maximum is
+    about 1.0998, reached near x = 2.4): checked by finite differences on a fine grid."""
+    x = np.linspace(-20.0, 20.0, 40001)
+    s = np.array([orc.silu(v) for v in x])
+    slope = np.abs(np.diff(s) / np.diff(x))
+    assert 1.09 < slope.max() < 1.1
+
+
+def test_silu_mul_elementwise(orc):
+    e = float(np.e)
+    g = np.array([[0.0, 1.0, -1.0], [64.0, 2.0, -64.0]])
+    u = np.array([[5.0, 2.0, 3.0], [-1.0, 0.5, 7.0]])
+    h = orc.silu_mul(g, u)
+    expect = np.array([[0.0, 2.0 * e / (1 + e), -3.0 / (1 + e)], [-64.0, e * e / (1 + e * e), 0.0]])
+    assert np.allclose(h, expect, rtol=1e-15, atol=1e-18)
+
+
+def test_gate_up_orientation(orc):
+    """All-ones activations, gate weights +1 and up weights -1 (unit scales): gate = K, up = -K
+    in every column, so h = silu(K) * (-K) = -K^2 exactly; with gate and up swapped the
+    result would be silu(-K) * K, about -K^2 e^-K."""
+    K, N, g = 64, 16, 32
+    ones = np.full((1, K), 0x3F80, np.uint16)            # bf16 1.0
+    unit = np.full((K // g, N), 0x3C00, np.uint16)       # fp16 1.0
+    gate = (synth.pack_rows(np.full((K, N), 9)), unit, None)   # 9 - 8 = +1
+    up = (synth.pack_rows(np.full((K, N), 7)), unit, None)     # 7 - 8 = -1
+    h, yg, bg, yu, bu = orc.gate_up(ones, gate, up, g)
+    assert np.all(yg == K) and np.all(yu == -K) and np.all(bg == K) and np.all(bu == K)
+    assert np.all(h == -float(K * K))
+    h2 = orc.gate_up(ones, up, gate, g)[0]
+    assert np.all((h2 < 0) & (h2 > -1e-20))
+
+
+def test_gate_up_column_subset(orc):
+    inp = synth.make_random(17, 3, 256, 64, 64, symmetric=False)
+    inp2 = synth.make_random(18, 3, 256, 64, 64, symmetric=False)
+    gate = (inp.qweight, inp.scales, inp.qzeros)
+    up = (inp2.qweight, inp2.scales, inp2.qzeros)
+    full = orc.gate_up(inp.act, gate, up, 64)[0]
+    cols = [0, 7, 8, 33, 63]
+    assert np.array_equal(orc.gate_up(inp.act, gate, up, 64, cols=cols)[0], full[:, cols])
+
+
+def test_gate_up_bar_rejects_plausible_mistakes(orc):
+    """The gated-product bar passes the exact product rounded to fp32 and rejects a missing
+    nonlinearity, swapped operands and a bare logistic gate."""
+    from tests import parity
+    inp = synth.make_random(19, 4, 512, 128, 128, symmetric=True)
+    inp2 = synth.make_random(20, 4, 512, 128, 128, symmetric=True)
+    h, yg, bg, yu, bu = orc.gate_up(inp.act, (inp.qweight, inp.scales, None), (inp2.qweight, inp2.scales, None), 128)
+    parity.check_gate_up(h.astype(np.float32), h, yg, bg, yu, bu, "fp32 rounding")
+    logistic = orc.silu_mul(yg, np.ones_like(yg)) / np.where(yg == 0, 1.0, yg)
+    for wrong in (yg * yu, orc.silu_mul(yu, yg), logistic * yu):
+        with pytest.raises(AssertionError):
+            parity.check_gate_up(wrong, h, yg, bg, yu, bu, "planted")

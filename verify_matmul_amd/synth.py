@@ -26,6 +26,8 @@ import numpy as np
 
 # tensor ids mixed into the seed: seed = 1000 * config_index + tensor_id
 _T_QWEIGHT, _T_SCALES, _T_ZEROS, _T_ACT = 1, 2, 3, 4
+# the second matrix of a gated pair (the gate beside the up projection): its own draws
+_T_QWEIGHT2, _T_SCALES2, _T_ZEROS2 = 5, 6, 7
 
 
 @dataclass(frozen=True)
@@ -133,6 +135,20 @@ def make_inputs(wl: Workload | str, N: Optional[int] = None) -> Inputs:
     act = draw_activations(_rng(wl.index, _T_ACT), MAX_ROWS, wl.K, wl.act_sigma,
                            wl.outlier_frac, wl.outlier_mul)
     return Inputs(qweight, scales, qzeros, act, wl.group)
+
+
+def make_gate_inputs(wl: Workload | str, N: Optional[int] = None) -> Inputs:
+    """The gate matrix that pairs with ``make_inputs(wl)`` (taken as the up projection) in a
+    gated feed-forward input: same shapes and distributions, its own draws, the same
+    activations."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    n = wl.N if N is None else N
+    up = make_inputs(wl, N)
+    qweight = random_words(_rng(wl.index, _T_QWEIGHT2), (wl.K // 8, n))
+    scales = draw_scales(_rng(wl.index, _T_SCALES2), (wl.groups, n), wl.scale_lo, wl.scale_hi)
+    qzeros = None if wl.symmetric else random_words(_rng(wl.index, _T_ZEROS2), (wl.groups, n // 8))
+    return Inputs(qweight, scales, qzeros, up.act, wl.group)
 
 
 def make_random(seed: int, M: int, K: int, N: int, group: int, symmetric: bool,
