@@ -109,6 +109,33 @@ int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *sc
                       void *out, int out_dtype, int32_t *idx, hipStream_t stream);
 
 /*
+ * Gated feed-forward input in one launch: two matrices of the same shape read against the same
+ * activations, combined as
+ *   out[m][n] = silu(g[m][n]) * u[m][n],   silu(x) = x / (1 + e^-x),
+ *   g = A x dequant(qweight_gate, scales_gate, qzeros_gate), u = A x dequant(qweight_up, ...)
+ * with g and u summed in fp32 exactly as w4a16_gemm sums them; silu and the product are
+ * evaluated in fp32, a bf16 out is that fp32 value rounded to nearest even. The GRIMOIRE v1.8
+ * release notes ('What changed', INT4 prompt processing) fuse the feed-forward gate into the
+ * int4 path; the pages do not name the gate's nonlinearity, and SiLU is the gate of the
+ * Qwen-family feed-forward they run. The activations are staged once for both matrices and
+ * only [M, N] is written.
+ * Every argument is as in w4a16_gemm, for each matrix; both matrices have the same N, K and
+ * group size, and qzeros_gate and qzeros_up are both NULL (symmetric) or both given
+ * (INVALID_ARG otherwise). out must not overlap any input.
+ * The _ex form fixes the launch as w4a16_gemm_ex does (0 = default), on 128-column tiles of the
+ * pair (64 output columns of each matrix): splits * waves_k must not exceed K/32.
+ */
+int w4a16_gemm_gate_up(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,
+                       const uint32_t *qzeros_gate, const uint32_t *qweight_up,
+                       const uint16_t *scales_up, const uint32_t *qzeros_up, int group_size,
+                       int M, int N, int K, void *out, int out_dtype, hipStream_t stream);
+int w4a16_gemm_gate_up_ex(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,
+                          const uint32_t *qzeros_gate, const uint32_t *qweight_up,
+                          const uint16_t *scales_up, const uint32_t *qzeros_up, int group_size,
+                          int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
+                          hipStream_t stream);
+
+/*
  * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32
  * comparison, -0 == +0, NaN entries ignored; an all-NaN row gives 0).
  *   logits fp32 [M, N] device, 16-byte aligned; M in 1..65535; N in 1..2^31-1

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("w4a16_gemm", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32"):
+    for n in ("w4a16_gemm", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_gemm_gate_up"):
         assert n in names
 
 
@@ -139,3 +139,23 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "--gpus 2 is not supported" in r.stderr
     assert r.stdout == ""
+
+
+Q2, S2, Z2 = 0x60000, 0x70000, 0x80000
+
+
+def gate_up(lib, q=Q, s=S, z=None, q2=Q2, s2=S2, z2=None, g=128, M=1, N=256, K=512, o=O, dt=0, splits=0, wk=0):
+    return lib.w4a16_gemm_gate_up_ex(A, q, s, z, q2, s2, z2, g, M, N, K, o, dt, splits, wk, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(s2=None), -1), (dict(q2=None), -1),
+    (dict(z=Z), -1), (dict(z2=Z2), -1),                 # zeros given for one matrix only
+    (dict(q2=Q2 + 4), -2), (dict(z=Z, z2=Z2 + 4), -2), (dict(M=17), -1), (dict(N=260), -1),
+    (dict(splits=17, wk=1), -1),                        # 17 x 1 > 512/32 steps
+    (dict(wk=3, splits=1), -1),
+])
+def test_gate_up_rejects_bad_arguments(lib, kw, status):
+    assert gate_up(lib, **kw) == status
+    assert lib.w4a16_last_error().decode()
+    assert lib.w4a16_gemm_gate_up(A, Q, S, None, None, S2, None, 128, 1, 256, 512, O, 0, None) == -1

@@ -215,17 +215,36 @@ int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scal
 }
 
 
-// One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick.
-int gemm_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros, int group_size,
-              int M, int N, int K, void *out, int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx,
-              hipStream_t stream)
+// One stored matrix: packed codes, fp16 scales, packed zeros (nullptr: symmetric).
+struct Matrix {
+    const uint32_t *qweight;
+    const uint16_t *scales;
+    const uint32_t *qzeros;
+};
+
+// One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick;
+// `up` non-null makes it a gated pair (w is the gate): out = silu(A x w) * (A x up), planned as
+// one 2N-column problem on 128-column tiles (64 output columns of each matrix).
+int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
+              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream)
 {
+    const uint32_t *qweight = w.qweight;
+    const uint16_t *scales = w.scales;
+    const uint32_t *qzeros = w.qzeros;
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
+    if (up) {
+        rc = check_gemm_args(A, up->qweight, up->scales, up->qzeros, group_size, M, N, K, out, out_dtype);
+        if (rc != W4A16_OK) return rc;
+        if ((qzeros == nullptr) != (up->qzeros == nullptr))
+            return fail(W4A16_ERR_INVALID_ARG, "qzeros_gate and qzeros_up must both be NULL or both be given");
+    }
     if (splits < 0 || waves_k < 0)
         return fail(W4A16_ERR_INVALID_ARG, "splits=%d waves_k=%d must be >= 0", splits, waves_k);
+    const int NV = up ? 2 * N : N;   // columns of the planned problem
+    if (up) tile_cols = 128;
     GemmPlan plan{};
-    rc = make_plan(M, N, K, group_size, qzeros == nullptr, splits, waves_k, tile_cols, idx != nullptr, &plan);
+    rc = make_plan(M, NV, K, group_size, qzeros == nullptr, splits, waves_k, tile_cols, idx != nullptr, &plan);
     if (rc != W4A16_OK) return rc;
 
     GemmArgs a{};
@@ -233,6 +252,11 @@ int gemm_call(const void *A, const uint32_t *qweight, const uint16_t *scales, co
     a.qweight = qweight;
     a.scales = scales;
     a.qzeros = qzeros;
+    if (up) {
+        a.qweight2 = up->qweight;
+        a.scales2 = up->scales;
+        a.qzeros2 = up->qzeros;
+    }
     a.out = out;
     a.M = M;
     a.N = N;
@@ -247,14 +271,14 @@ int gemm_call(const void *A, const uint32_t *qweight, const uint16_t *scales, co
     if (split_k || plan.prep_a || idx) {
         // counters: [tile counters][argmax row keys (M x 64 bit)]
         const size_t tile = (size_t)tile_columns(plan.cols);
-        const size_t tiles = ((size_t)N + tile - 1) / tile;
+        const size_t tiles = ((size_t)NV + tile - 1) / tile;
         const size_t key_off = round_up(tiles * sizeof(uint32_t), 8);
         const size_t counter_bytes = key_off + 16 * sizeof(unsigned long long);
         const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
         const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
-        rc = get_scratch(stream, counter_bytes, split_k ? (size_t)plan.splits * M * N * sizeof(uint64_t) : 0, act_bytes,
-                         split_k, &v);
+        rc = get_scratch(stream, counter_bytes, split_k ? (size_t)plan.splits * M * NV * sizeof(uint64_t) : 0,
+                         act_bytes, split_k, &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.counters;
         a.partials = v.partials;
@@ -280,8 +304,8 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
                   int group_size, int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
                   int tile_cols, hipStream_t stream)
 {
-    return gemm_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, splits, waves_k, tile_cols,
-                     nullptr, stream);
+    return gemm_call(A, Matrix{qweight, scales, qzeros}, nullptr, group_size, M, N, K, out, out_dtype, splits,
+                     waves_k, tile_cols, nullptr, stream);
 }
 
 int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -289,7 +313,27 @@ int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *sc
                       hipStream_t stream)
 {
     if (!idx) return fail(W4A16_ERR_INVALID_ARG, "null pointer (idx)");
-    return gemm_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, idx, stream);
+    return gemm_call(A, Matrix{qweight, scales, qzeros}, nullptr, group_size, M, N, K, out, out_dtype, 0, 0, 0, idx,
+                     stream);
+}
+
+int w4a16_gemm_gate_up_ex(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,
+                          const uint32_t *qzeros_gate, const uint32_t *qweight_up, const uint16_t *scales_up,
+                          const uint32_t *qzeros_up, int group_size, int M, int N, int K, void *out, int out_dtype,
+                          int splits, int waves_k, hipStream_t stream)
+{
+    const Matrix up{qweight_up, scales_up, qzeros_up};
+    return gemm_call(A, Matrix{qweight_gate, scales_gate, qzeros_gate}, &up, group_size, M, N, K, out, out_dtype,
+                     splits, waves_k, 0, nullptr, stream);
+}
+
+int w4a16_gemm_gate_up(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,
+                       const uint32_t *qzeros_gate, const uint32_t *qweight_up, const uint16_t *scales_up,
+                       const uint32_t *qzeros_up, int group_size, int M, int N, int K, void *out, int out_dtype,
+                       hipStream_t stream)
+{
+    return w4a16_gemm_gate_up_ex(A, qweight_gate, scales_gate, qzeros_gate, qweight_up, scales_up, qzeros_up,
+                                 group_size, M, N, K, out, out_dtype, 0, 0, stream);
 }
 
 int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,

@@ -131,6 +131,10 @@ __device__ __forceinline__ half8_t act8_to_slots(uint4 raw, float mul)
     return r;
 }
 
+// SiLU, the gate of a gated feed-forward pair: x * logistic(x) = x / (1 + e^-x). Large
+// negative x give e^-x = inf and a signed zero.
+__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+
 // 2^-shift as a float (shift within [-126, 114]).
 __device__ __forceinline__ float pow2_neg(int shift) { return __builtin_amdgcn_ldexpf(1.0f, -shift); }
 

@@ -151,12 +151,19 @@ constexpr int gemm_min_waves() { return kMfma && kC == 4 ? (kSym ? 7 : 5) : 1; }
 // kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
 // slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
 // order, rescaled per piece and row -- and stream in with the weights, one fragment per step.
-template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf, int kC>
+// kDual: a gated pair (gate in qweight, up in qweight2, same shape). A lane's 8 columns are 4
+// output columns of the gate followed by the same 4 of the up projection, so a tile covers 64
+// output columns of both, the activations are staged and converted once for the two, and the
+// epilogue writes silu(gate) * up. Internally the pair is a 2N-column problem whose column c of
+// a tile is output column (c / 8) * 4 + c % 4 of matrix (c / 4) % 2.
+template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf, int kC, bool kDual = false>
 __global__ __launch_bounds__(kWK * 64)
 __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a16_gemm_kernel(GemmArgs p)
 {
+    static_assert(!kDual || (kMfma && kC == 8), "gated pairs run on the matrix cores, 8 columns per lane");
     constexpr bool kPreA = !kLdsA;
     constexpr int kTile = 16 * kC;      // columns per tile: kC adjacent columns per lane
+    constexpr int kOutTile = kDual ? kTile / 2 : kTile;   // output columns per tile
     constexpr int kV = kC / 4;          // 16-byte weight loads per lane per step
     constexpr int kZW = kTile / 8;      // zero words (and 8-scale items) per group
     extern __shared__ __align__(16) unsigned char smem[];
@@ -195,11 +202,12 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     uint16_t *sc_lds = reinterpret_cast<uint16_t *>(wreg + p.scale_off);           // [group][64]
     uint32_t *z_lds = reinterpret_cast<uint32_t *>(wreg + p.zero_off);             // [group][8]
 
-    const int n0 = tile * kTile + cl * kC;
+    const int n0 = tile * kOutTile + cl * (kDual ? 4 : kC);   // the lane's first output column
     const bool col_ok = n0 < N;
     const int nc = col_ok ? n0 : 0;       // clamped column for loads of dead lanes
     const int arow = cl < M ? cl : 0;     // clamped activation row (MFMA fragments)
     const uint32_t *qw_lane = p.qweight + (size_t)rl * N + nc;
+    const uint32_t *qw2_lane = kDual ? p.qweight2 + (size_t)rl * N + nc : qw_lane;   // up columns
     const uint16_t *asrc = kPreA ? p.A16 : p.A;   // prepared fp16 or raw bf16
     const uint16_t *a_lane = asrc + (size_t)arow * K + rl * 8;
     int pre_shift = 0;   // prepared path: this piece's rescale of row `lane`
@@ -248,7 +256,17 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             }
         }
     }
-    {   // scales: kZW items of 8 columns per group (lanes past the last item stay idle, so the
+    if constexpr (kDual) {   // scales: 64 pairs per group, in lane order [cl][gate 4 | up 4]
+        const int sitems = ng * 64;
+        for (int b = 0; b < sitems; b += 64) {
+            const int gi = g0 + b / 64;
+            const int j = (2 * lane) & 7;   // first slot of the pair within the lane's 8
+            int c = tile * kOutTile + (lane >> 2) * 4 + (j & 3);
+            if (c >= N) c = 0;
+            load_to_lds4((j < 4 ? p.scales : p.scales2) + (size_t)gi * N + c, sc_lds + (size_t)b * 2);
+            ++pre_loads;
+        }
+    } else {   // scales: kZW items of 8 columns per group (lanes past the last item stay idle, so the
         // LDS area holds exactly the wave's groups)
         const int sitems = ng * kZW;
         for (int b = 0; b < sitems; b += 64) {
@@ -260,14 +278,16 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             ++pre_loads;
         }
     }
-    if (!kSym) {   // zero words: kZW per group (8 columns each)
+    if (!kSym) {   // zero words: kZW per group (8 columns each; a pair: 8 gate words, 8 up words)
         const int zitems = ng * kZW;
         for (int b = 0; b < zitems; b += 64) {
             const int it = b + lane;
             const int gi = g0 + it / kZW;
-            int c = tile * kTile + (it % kZW) * 8;
+            const int w = it % kZW;
+            int c = kDual ? tile * kOutTile + (w & 7) * 8 : tile * kTile + w * 8;
             if (c >= N) c = 0;
-            if (it < zitems) load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
+            const uint32_t *zsrc = kDual && w >= 8 ? p.qzeros2 : p.qzeros;
+            if (it < zitems) load_to_lds4(zsrc + (size_t)gi * (N / 8) + c / 8, z_lds + b);
             ++pre_loads;
         }
     }
@@ -281,7 +301,8 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     auto load_w = [&](uint4 *dst, int t) {
 #pragma unroll
         for (int v = 0; v < kV; ++v)   // word offsets fit 32 bits (checked on the host)
-            dst[v] = *reinterpret_cast<const uint4 *>(qw_lane + (uint32_t)(t * 4 * N) + 4 * v);
+            dst[v] = kDual ? *reinterpret_cast<const uint4 *>((v ? qw2_lane : qw_lane) + (uint32_t)(t * 4 * N))
+                           : *reinterpret_cast<const uint4 *>(qw_lane + (uint32_t)(t * 4 * N) + 4 * v);
     };
 #pragma unroll
     for (int u = 0; u < kPf; ++u) {
@@ -376,9 +397,19 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             if (cl >= M) a = zero8;
         }
         if (!kSym && first) {   // zero points change once per group (uniform)
-            const uint32_t zw = z_lds[(gi - g0) * kZW + (cl * kC) / 8];
+            if constexpr (kDual) {
+                const uint32_t *zg = z_lds + (gi - g0) * kZW + (cl >> 1);
+                const uint32_t zw0 = zg[0], zw1 = zg[8];   // gate, up
 #pragma unroll
-            for (int j = 0; j < kC; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
+                for (int j = 0; j < 4; ++j) {
+                    zs[j] = zero_sub(zero_of(zw0, (uint32_t)(nc + j)));
+                    zs[4 + j] = zero_sub(zero_of(zw1, (uint32_t)(nc + j)));
+                }
+            } else {
+                const uint32_t zw = z_lds[(gi - g0) * kZW + (cl * kC) / 8];
+#pragma unroll
+                for (int j = 0; j < kC; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(nc + j)));
+            }
         }
         uint32_t words[kC];
 #pragma unroll
@@ -409,15 +440,12 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                 const uint2 v = *reinterpret_cast<const uint2 *>(sp);
                 sw[0] = v.x;
                 sw[1] = v.y;
-            } else {
-#pragma unroll
-                for (int v = 0; v < kV; ++v) {
-                    const uint4 q = *reinterpret_cast<const uint4 *>(sp + 8 * v);
-                    sw[4 * v] = q.x;
-                    sw[4 * v + 1] = q.y;
-                    sw[4 * v + 2] = q.z;
-                    sw[4 * v + 3] = q.w;
-                }
+            } else {   // the lane's 8 scales
+                const uint4 q = *reinterpret_cast<const uint4 *>(sp);
+                sw[0] = q.x;
+                sw[1] = q.y;
+                sw[2] = q.z;
+                sw[3] = q.w;
             }
             float s4[kC];
 #pragma unroll
@@ -499,8 +527,14 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             if (m >= M) break;
             const size_t o = (size_t)m * N + n0;
 #pragma unroll
-            for (int v = 0; v < kV; ++v) {
-                const float x0 = tot[4 * v][r], x1 = tot[4 * v + 1][r], x2 = tot[4 * v + 2][r], x3 = tot[4 * v + 3][r];
+            for (int v = 0; v < (kDual ? 1 : kV); ++v) {
+                float x0 = tot[4 * v][r], x1 = tot[4 * v + 1][r], x2 = tot[4 * v + 2][r], x3 = tot[4 * v + 3][r];
+                if (kDual) {   // silu(gate) * up
+                    x0 = silu_f32(x0) * tot[4][r];
+                    x1 = silu_f32(x1) * tot[5][r];
+                    x2 = silu_f32(x2) * tot[6][r];
+                    x3 = silu_f32(x3) * tot[7][r];
+                }
                 if (p.out_bf16) {
                     uint2 q;
                     q.x = float_to_bf16_bits(x0) | (float_to_bf16_bits(x1) << 16);
@@ -566,13 +600,35 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
         if (tid < M && s_rowkey[tid])
             __hip_atomic_fetch_max(&p.amax_keys[tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
+    // Column c of the tile: its place in the split-K partials (2N wide for a gated pair),
+    // whether it holds an output, and where its finished sum goes -- out, or for a gated pair
+    // into LDS over the thread's own slot of wave 0's sums (only that thread reads the slot)
+    // until silu(gate) * up is formed.
+    const size_t NV = kDual ? 2 * (size_t)N : (size_t)N;
+    auto col_valid = [&](int c) { return kDual ? tile * kOutTile + (c >> 3) * 4 < N : tile * kTile + c < N; };
+    auto put = [&](int m, int c, float v, bool ok) {
+        if constexpr (kDual)
+            red[(size_t)m * kTile + c] = v;
+        else
+            emit(m, tile * kTile + c, v, ok);
+    };
+    auto finish_pair = [&]() {
+        __syncthreads();
+        for (int idx = tid; idx < M * kOutTile; idx += kThreads) {
+            const int m = idx / kOutTile;
+            const int oc = idx - m * kOutTile;
+            const int n = tile * kOutTile + oc;
+            const float *fin = red + (size_t)m * kTile + (oc >> 2) * 8 + (oc & 3);   // gate; up 4 further
+            if (n < N) store_out(m, n, silu_f32(fin[0]) * fin[4]);
+        }
+    };
     if (p.splits == 1) {
         for (int idx = tid; idx < M * kTile; idx += kThreads) {
             const int m = idx / kTile;
             const int c = idx - m * kTile;
-            const int n = tile * kTile + c;
-            emit(m, n, wg_sum(m, c), n < N);
+            put(m, c, wg_sum(m, c), col_valid(c));
         }
+        if (kDual) finish_pair();
         if (amax) finish_argmax();
         return;
     }
@@ -591,8 +647,8 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             const int m = idx / kTile;
             const int c = idx - m * kTile;
             const int n = tile * kTile + c;
-            if (n < N)
-                __hip_atomic_store(p.partials + ((size_t)split * M + m) * N + n,
+            if (col_valid(c))
+                __hip_atomic_store(p.partials + ((size_t)split * M + m) * NV + n,
                                    stamp_hi | __builtin_bit_cast(uint32_t, wg_sum(m, c)), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -605,7 +661,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     auto reduce = [&](auto batch_tag) {
         constexpr int kBatch = decltype(batch_tag)::value;
         constexpr int kOut = kBatch >= 8 ? 1 : 8 / kBatch;
-        const size_t slice = (size_t)M * N;
+        const size_t slice = (size_t)M * NV;
         const int cnt0 = min(kBatch, p.splits);
         for (int base = tid; base < M * kTile; base += kOut * kThreads) {
             uint64_t part[kOut][kBatch];
@@ -614,8 +670,8 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                 const int idx = base + o * kThreads;
                 const int m = idx / kTile;
                 const int n = tile * kTile + idx - m * kTile;
-                const bool ok = idx < M * kTile && n < N;
-                const uint64_t *col = p.partials + (ok ? (size_t)m * N + n : 0);
+                const bool ok = idx < M * kTile && col_valid(idx - m * kTile);
+                const uint64_t *col = p.partials + (ok ? (size_t)m * NV + n : 0);
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i) {
                     part[o][i] = 0;
@@ -631,9 +687,9 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                 const int m = idx / kTile;
                 const int c = idx - m * kTile;
                 const int n = tile * kTile + c;
-                const bool in = n < N;
+                const bool in = col_valid(c);
                 const float own = wg_sum(m, c);
-                const uint64_t *col = p.partials + (size_t)m * N + n;
+                const uint64_t *col = p.partials + (size_t)m * NV + n;
                 float v = 0.f;
                 bool failed = false;
                 for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
@@ -665,7 +721,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                         v += __builtin_bit_cast(float, (uint32_t)w);
                     }
                 }
-                emit(m, n, failed ? __builtin_nanf("") : v, in);
+                put(m, c, failed ? __builtin_nanf("") : v, in);
             }
         }
     };
@@ -675,6 +731,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
         reduce(std::integral_constant<int, 8>{});
     else
         reduce(std::integral_constant<int, 16>{});
+    if (kDual) finish_pair();
     if (amax) finish_argmax();
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -690,11 +747,12 @@ __global__ __launch_bounds__(64) void argmax_keys_finish_kernel(unsigned long lo
     keys[m] = 0;
 }
 
-template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kC>
+template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kC, bool kDual>
 hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     constexpr int kPf = kLdsA ? kRingStaged : kRingConvert;
-    const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf, kC>;
+    constexpr int kOutTile = kDual ? 8 * kC : 16 * kC;
+    const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf, kC, kDual>;
     if (!kLdsA) {
         ActPrepArgs pa{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK};
         hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(a.splits * kWK), (unsigned)((a.M + kPrepWaves - 1) / kPrepWaves)),
@@ -707,7 +765,7 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
         if (e != hipSuccess) return e;
     }
-    const dim3 grid((unsigned)((a.N + 16 * kC - 1) / (16 * kC)), (unsigned)a.splits);
+    const dim3 grid((unsigned)((a.N + kOutTile - 1) / kOutTile), (unsigned)a.splits);
     hipLaunchKernelGGL(kern, grid, dim3(kWK * 64), plan.lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_keys) return e;
@@ -715,15 +773,15 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
     return hipGetLastError();
 }
 
-template <bool kMfma, bool kSym, bool kLdsA, int kC>
+template <bool kMfma, bool kSym, bool kLdsA, int kC, bool kDual = false>
 hipError_t launch_wk(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     switch (plan.wk) {
-    case 1: return launch_one<kMfma, kSym, kLdsA, 1, kC>(a, plan, stream);
-    case 2: return launch_one<kMfma, kSym, kLdsA, 2, kC>(a, plan, stream);
-    case 4: return launch_one<kMfma, kSym, kLdsA, 4, kC>(a, plan, stream);
-    case 8: return launch_one<kMfma, kSym, kLdsA, 8, kC>(a, plan, stream);
-    case 16: return launch_one<kMfma, kSym, kLdsA, 16, kC>(a, plan, stream);
+    case 1: return launch_one<kMfma, kSym, kLdsA, 1, kC, kDual>(a, plan, stream);
+    case 2: return launch_one<kMfma, kSym, kLdsA, 2, kC, kDual>(a, plan, stream);
+    case 4: return launch_one<kMfma, kSym, kLdsA, 4, kC, kDual>(a, plan, stream);
+    case 8: return launch_one<kMfma, kSym, kLdsA, 8, kC, kDual>(a, plan, stream);
+    case 16: return launch_one<kMfma, kSym, kLdsA, 16, kC, kDual>(a, plan, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -746,10 +804,20 @@ hipError_t launch_sym(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
                                : launch_cols<kMfma, false, kLdsA>(a, plan, stream);
 }
 
+// A gated pair: matrix cores on 8 columns per lane (4 of each matrix).
+template <bool kLdsA>
+hipError_t launch_pair(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
+{
+    if (plan.cols != 8 || !plan.mfma) return hipErrorInvalidValue;
+    return a.qzeros == nullptr ? launch_wk<true, true, kLdsA, 8, true>(a, plan, stream)
+                               : launch_wk<true, false, kLdsA, 8, true>(a, plan, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
+    if (a.qweight2) return plan.lds_a ? launch_pair<true>(a, plan, stream) : launch_pair<false>(a, plan, stream);
     if (!plan.mfma) return launch_sym<false, true>(a, plan, stream);   // GEMV: always staged
     return plan.lds_a ? launch_sym<true, true>(a, plan, stream) : launch_sym<true, false>(a, plan, stream);
 }

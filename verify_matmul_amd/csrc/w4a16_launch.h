@@ -45,10 +45,15 @@ struct GemmArgs {
     const uint32_t *qweight;
     const uint16_t *scales;
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
+    // gated pair: the up projection (same shape as qweight, the gate); out = silu(gate) * up.
+    // qweight2 == nullptr: a single matrix.
+    const uint32_t *qweight2;
+    const uint16_t *scales2;
+    const uint32_t *qzeros2;
     void *out;
     uint16_t *A16;            // [M, K] prepared activations (matrix-core path)
     int *ashift;              // [splits * waves_k, M] their rescale per K piece and row
-    uint64_t *partials;       // [splits, M, N] stamped fp32 partial sums when splits > 1
+    uint64_t *partials;       // [splits, M, N] (gated pair: [splits, M, 2N]) stamped fp32 partial sums
     uint32_t *counters;       // one per column tile, zero between calls
     uint32_t stamp;           // this call's stamp (nonzero, not used by the last 2^32 - 1 calls)
     unsigned long long *amax_keys;   // fused argmax: [M] row keys, zero between calls (nullptr: off)
