@@ -21,6 +21,10 @@ Timed regions (all on the library's stream, inputs resident in HBM):
 summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or null when the
 kernel sources changed since the counters were taken.
 
+With --gate-up every call is instead the fused gated pair on the workload's shape,
+silu(A x W_gate) * (A x W_up) (w4a16_gemm_gate_up): two weight matrices per call, one [M, N]
+output, and the algorithmic bytes count both matrices.
+
 Prints one JSON line (rank 0; this build runs on one GPU).
 """
 from __future__ import annotations
@@ -40,11 +44,11 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 POOL_BYTES = 768 * 2 ** 20      # rotating weight pool, 3x the 256 MB last-level cache
 
 
-def algorithmic_bytes(M, K, N, g, symmetric, out_bytes=4):
-    b = K * N // 2 + 2 * (K // g) * N + 2 * M * K + out_bytes * M * N
+def algorithmic_bytes(M, K, N, g, symmetric, out_bytes=4, matrices=1):
+    w = K * N // 2 + 2 * (K // g) * N
     if not symmetric:
-        b += (K // g) * N // 2
-    return b
+        w += (K // g) * N // 2
+    return matrices * w + 2 * M * K + out_bytes * M * N
 
 
 def parse():
@@ -58,6 +62,8 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="workgroups per column tile along K (0 = default)")
     p.add_argument("--waves-k", type=int, default=0, help="waves per workgroup along K (0 = default)")
     p.add_argument("--tile-cols", type=int, default=0, help="column tile width, 64 or 128 (0 = default)")
+    p.add_argument("--gate-up", action="store_true",
+                   help="time the fused gated pair silu(A x W_gate) * (A x W_up) on the workload's shape")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise kernel (y = 2x, fp32) over MIB MiB five times: the "
@@ -66,7 +72,7 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(wl, inp, ms, seconds):
+def cpu_baseline(wl, inp, ms, seconds, gate=None):
     """The CPU oracle, as it is, on this host's cores: the whole step repeated for ~`seconds`."""
     import oracle
     oracle._load()
@@ -75,9 +81,13 @@ def cpu_baseline(wl, inp, ms, seconds):
     while elapsed < seconds or reps == 0:
         for M in ms:
             t = time.perf_counter()
-            oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)
+            if gate is None:
+                oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)
+            else:
+                oracle.gate_up(inp.act[:M], (gate.qweight, gate.scales, gate.qzeros),
+                               (inp.qweight, inp.scales, inp.qzeros), inp.group)
             elapsed += time.perf_counter() - t
-            nbytes += algorithmic_bytes(M, wl.K, wl.N, wl.group, wl.symmetric)
+            nbytes += algorithmic_bytes(M, wl.K, wl.N, wl.group, wl.symmetric, matrices=1 if gate is None else 2)
         reps += 1
     return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full step(s) of the workload (M={','.join(map(str, ms))}, all {wl.N} columns), "
@@ -132,17 +142,27 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
     inp = synth.make_inputs(wl)
+    pair = args.gate_up
+    gate_inp = synth.make_gate_inputs(wl) if pair else None
+    nmat = 2 if pair else 1
+    if pair and (wl.argmax or args.tile_cols):
+        print("bench.py: --gate-up takes no output-layer workload and no --tile-cols", file=sys.stderr)
+        return 2
     K, N, g = wl.K, wl.N, wl.group
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    per_copy = algorithmic_bytes(1, K, N, g, wl.symmetric)
+    per_copy = algorithmic_bytes(1, K, N, g, wl.symmetric, matrices=nmat)
     R = max(2, math.ceil(POOL_BYTES / per_copy))
     qw0 = torch.from_numpy(inp.qweight.view(np.int32)).to(dev)
     sc0 = torch.from_numpy(inp.scales.view(np.int16)).to(dev)
     qz0 = None if inp.qzeros is None else torch.from_numpy(inp.qzeros.view(np.int32)).to(dev)
     a0 = torch.from_numpy(inp.act.view(np.int16)).to(dev)
-    pool = []
+    if pair:
+        gw0 = torch.from_numpy(gate_inp.qweight.view(np.int32)).to(dev)
+        gs0 = torch.from_numpy(gate_inp.scales.view(np.int16)).to(dev)
+        gz0 = None if gate_inp.qzeros is None else torch.from_numpy(gate_inp.qzeros.view(np.int32)).to(dev)
+    pool, gates = [], []
     for r in range(R):
         qw = qw0.clone()
         sc = sc0.clone()
@@ -150,21 +170,29 @@ def main():
         a = a0.clone()
         outs = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}
         pool.append((qw, sc, qz, a, outs))
+        if pair:
+            gates.append((gw0.clone(), gs0.clone(), None if gz0 is None else gz0.clone()))
     del qw0, sc0, qz0
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
 
     # pre-marshalled calls: (M, args) per rotation slot
+    def vp(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
     calls = []
-    for (qw, sc, qz, a, outs) in pool:
+    for r, (qw, sc, qz, a, outs) in enumerate(pool):
         row = []
         for M in ms:
-            row.append((M, (ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(qw.data_ptr()),
-                            ctypes.c_void_p(sc.data_ptr()), None if qz is None else ctypes.c_void_p(qz.data_ptr()),
-                            g, M, N, K, ctypes.c_void_p(outs[M].data_ptr()), 0, args.splits, args.waves_k,
-                            args.tile_cols, sp)))
+            if pair:
+                gw, gs, gz = gates[r]
+                row.append((M, (vp(a), vp(gw), vp(gs), vp(gz), vp(qw), vp(sc), vp(qz), g, M, N, K, vp(outs[M]), 0,
+                                args.splits, args.waves_k, sp)))
+            else:
+                row.append((M, (vp(a), vp(qw), vp(sc), vp(qz), g, M, N, K, vp(outs[M]), 0, args.splits,
+                                args.waves_k, args.tile_cols, sp)))
         calls.append(row)
-    fn = lib.w4a16_gemm_ex
+    fn = lib.w4a16_gemm_gate_up_ex if pair else lib.w4a16_gemm_ex
 
     def step(i, evs=None):
         # every call of every step reads its own weight copy: consecutive calls never find the
@@ -177,7 +205,8 @@ def main():
             if evs is not None:
                 evs[i][j][1].record(stream)
             if rc != 0:
-                raise RuntimeError(f"w4a16_gemm_ex failed: {lib.w4a16_last_error().decode()}")
+                raise RuntimeError(f"{'w4a16_gemm_gate_up_ex' if pair else 'w4a16_gemm_ex'} failed: "
+                                   f"{lib.w4a16_last_error().decode()}")
 
     for i in range(args.warmup):
         step(i)
@@ -190,7 +219,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_bytes = sum(algorithmic_bytes(M, K, N, g, wl.symmetric) for M in ms)
+    step_bytes = sum(algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat) for M in ms)
     value = step_bytes * args.steps / wall / 1e9
 
     # timed region 2: the same steps with a HIP event pair around every launch, on the stream the
@@ -206,15 +235,19 @@ def main():
     dom, dom_time = None, -1.0
     for j, M in enumerate(ms):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
-        b = algorithmic_bytes(M, K, N, g, wl.symmetric)
+        b = algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat)
         us = float(np.mean(d))
         kern, spl, wk, tcols = vm.w4a16_plan(M, N, K, g)
         per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
-                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b,
-                         "kernel": "gemv" if kern == 0 else "mfma",
-                         "splits": args.splits or spl, "waves_k": args.waves_k or wk,
-                         "tile_cols": args.tile_cols or tcols}
+                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
+        if pair:   # 128-column tiles of the 2N-wide pair (64 output columns of each matrix)
+            per_m[str(M)].update({"kernel": "mfma, gated pair", "tile_cols": 128})
+            if args.splits or args.waves_k:
+                per_m[str(M)].update({"splits": args.splits or "default", "waves_k": args.waves_k or "default"})
+        else:
+            per_m[str(M)].update({"kernel": "gemv" if kern == 0 else "mfma", "splits": args.splits or spl,
+                                  "waves_k": args.waves_k or wk, "tile_cols": args.tile_cols or tcols})
         if float(np.sum(d)) > dom_time:
             dom, dom_time = M, float(np.sum(d))
     # the dominant launch: the row count whose calls take the most time in a step
@@ -264,7 +297,7 @@ def main():
     torch.cuda.synchronize()
     us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
     achieved = dm["bytes"] / us_dom / 1e3   # GB/s
-    traffic = load_traffic(args.workload, dom)
+    traffic = load_traffic(args.workload + ("_gate_up" if pair else ""), dom)
 
     rec = {
         "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
@@ -279,7 +312,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}, M in {','.join(map(str, ms))} (one call each per step)",
+        "config": {"workload": (f"{wl.name} gated pair silu(A x W_gate) * (A x W_up)" if pair else wl.name) +
+                               f", M in {','.join(map(str, ms))} (one call each per step)",
                    "K": K, "N": N, "group": g, "symmetric_zero": wl.symmetric, "ms": list(ms), "out": "fp32",
                    "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20),
                    "launch": "default" if not (args.splits or args.waves_k or args.tile_cols) else
@@ -293,7 +327,7 @@ def main():
         "per_m": per_m,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp)
     print(json.dumps(rec), flush=True)
     return 0
 
