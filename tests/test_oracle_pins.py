@@ -202,6 +202,22 @@ def test_unit_scale_zero_point_is_integer_matmul(orc):
     assert np.array_equal(y, ref.astype(np.float64))
 
 
+def test_many_rows_integer_matmul(orc):
+    """The prompt-sized case: 300 rows (more than any small-row launch), unit scales and zero
+    points drawn per group and column, integer activations: an exact int64 matmul of the codes
+    minus their zeros."""
+    rng = np.random.default_rng(16)
+    M, K, N, g = 300, 256, 72, 64
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)
+    ai = rng.integers(-8, 9, size=(M, K))
+    act = synth.f32_to_bf16_bits(ai.astype(np.float32))
+    scales = np.full((K // g, N), 0x3C00, dtype=np.uint16)
+    y, _ = orc.gemm(act, synth.pack_rows(codes), scales, synth.pack_cols(zeros), g)
+    d = codes.astype(np.int64) - np.repeat(zeros.astype(np.int64), g, axis=0)
+    assert np.array_equal(y, (ai.astype(np.int64) @ d).astype(np.float64))
+
+
 def test_scaling_and_negation(orc):
     inp = synth.make_random(13, 4, 384, 48, 128, symmetric=False)
     y, b = orc.gemm(inp.act, inp.qweight, inp.scales, inp.qzeros, inp.group)
