@@ -109,6 +109,22 @@ int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *sc
                       void *out, int out_dtype, int32_t *idx, hipStream_t stream);
 
 /*
+ * out[M,N] = A x W for many rows (prompt processing), on the matrix cores: the same operation,
+ * storage layout and argument rules as w4a16_gemm, with M in 1..W4A16_PREFILL_MAX_M. The GRIMOIRE
+ * v1.8 release notes ('What changed', INT4 prompt processing) run GPTQ int4 weights through a
+ * fast prompt path; with hundreds of rows each weight feeds hundreds of multiply-adds and the
+ * matrix cores, not HBM, set the pace. Each row of A is rescaled by one power of two over its
+ * whole K before the fp16 matrix cores (exact; a bf16 value keeps all its bits when it lies
+ * within 2^31 of its row's largest magnitude), so results match w4a16_gemm's accuracy
+ * contract. Uses M * K * 2 + M * 4 bytes of the stream's scratch for the prepared activations
+ * (allocated on the first call of a size on a stream). Meant for M well above 16; any M works.
+ */
+#define W4A16_PREFILL_MAX_M 65536
+int w4a16_gemm_prefill(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                       const uint32_t *qzeros, int group_size, int M, int N, int K,
+                       void *out, int out_dtype, hipStream_t stream);
+
+/*
  * Gated feed-forward input in one launch: two matrices of the same shape read against the same
  * activations, combined as
  *   out[m][n] = silu(g[m][n]) * u[m][n],   silu(x) = x / (1 + e^-x),

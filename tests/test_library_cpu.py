@@ -159,3 +159,11 @@ def test_gate_up_rejects_bad_arguments(lib, kw, status):
     assert gate_up(lib, **kw) == status
     assert lib.w4a16_last_error().decode()
     assert lib.w4a16_gemm_gate_up(A, Q, S, None, None, S2, None, 128, 1, 256, 512, O, 0, None) == -1
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    def pre(a=A, q=Q, s=S, z=None, g=128, M=300, N=256, K=512, o=O, dt=0):
+        return lib.w4a16_gemm_prefill(a, q, s, z, g, M, N, K, o, dt, None)
+    assert pre(M=0) == -1 and pre(M=65537) == -1 and pre(N=260) == -1 and pre(g=48) == -1
+    assert pre(q=None) == -1 and pre(a=A + 2) == -2 and pre(dt=3) == -1
+    assert pre(M=65537) == -1 and b"M=65537" in lib.w4a16_last_error()

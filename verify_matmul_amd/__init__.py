@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax",
-    "w4a16_gemm_gate_up", "w4a16_plan",
+    "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "EXPORTS",
 ]
@@ -25,8 +25,8 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = (
-    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex",
-    "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+    "w4a16_gemm_gate_up_ex", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
 
@@ -53,6 +53,7 @@ def load():
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
+    lib.w4a16_gemm_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_gate_up.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_gate_up_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
     lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
@@ -65,7 +66,8 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex",
+    for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+              "w4a16_gemm_gate_up_ex",
               "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
         getattr(lib, f).restype = ctypes.c_int
@@ -145,6 +147,13 @@ def w4a16_gemm_argmax(A, qweight, scales, qzeros, group_size, out, idx, stream=N
     _check(load().w4a16_gemm_argmax(*args, _ptr(idx, "idx", (torch.int32,)), _stream(stream)),
            "w4a16_gemm_argmax")
     return out, idx
+
+
+def w4a16_gemm_prefill(A, qweight, scales, qzeros, group_size, out, stream=None):
+    """w4a16_gemm for many rows (prompt processing, M up to 65536) on the matrix cores."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    _check(load().w4a16_gemm_prefill(*args, _stream(stream)), "w4a16_gemm_prefill")
+    return out
 
 
 def w4a16_gemm_gate_up(A, gate, up, group_size, out, splits=0, waves_k=0, stream=None):

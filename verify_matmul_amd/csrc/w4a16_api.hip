@@ -193,12 +193,12 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
 }
 
 int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
-                    int g, int M, int N, int K, void *out, int out_dtype)
+                    int g, int M, int N, int K, void *out, int out_dtype, int max_m = 16)
 {
     if (!A || !qweight || !scales || !out)
         return fail(W4A16_ERR_INVALID_ARG, "null pointer (A=%p qweight=%p scales=%p out=%p)", A,
                     (const void *)qweight, (const void *)scales, out);
-    if (M < 1 || M > 16) return fail(W4A16_ERR_INVALID_ARG, "M=%d outside 1..16", M);
+    if (M < 1 || M > max_m) return fail(W4A16_ERR_INVALID_ARG, "M=%d outside 1..%d", M, max_m);
     if (N <= 0 || K <= 0 || g <= 0)
         return fail(W4A16_ERR_INVALID_ARG, "sizes must be positive (N=%d K=%d group_size=%d)", N, K, g);
     if (g % 32) return fail(W4A16_ERR_INVALID_ARG, "group_size=%d is not a multiple of 32", g);
@@ -315,6 +315,26 @@ int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *sc
     if (!idx) return fail(W4A16_ERR_INVALID_ARG, "null pointer (idx)");
     return gemm_call(A, Matrix{qweight, scales, qzeros}, nullptr, group_size, M, N, K, out, out_dtype, 0, 0, 0, idx,
                      stream);
+}
+
+int w4a16_gemm_prefill(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                       int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
+{
+    int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, W4A16_PREFILL_MAX_M);
+    if (rc != W4A16_OK) return rc;
+    // scratch: the prepared activations (fp16, [M, K]) and one rescale per row
+    const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
+    ScratchView v{};
+    rc = get_scratch(stream, 0, 0, a16_bytes + (size_t)M * sizeof(int), false, &v);
+    if (rc != W4A16_OK) return rc;
+    uint16_t *a16 = static_cast<uint16_t *>(v.act);
+    int *shifts = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
+    hipError_t e = launch_act_prep(ActPrepArgs{static_cast<const uint16_t *>(A), a16, shifts, M, K, 1, 1}, stream);
+    if (e != hipSuccess) return hip_fail(e, "activation preparation launch");
+    PrefillArgs pa{a16, shifts, qweight, scales, qzeros, out, M, N, K, group_size, out_dtype == W4A16_OUT_BF16};
+    e = launch_prefill(pa, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
+    return W4A16_OK;
 }
 
 int w4a16_gemm_gate_up_ex(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,

@@ -747,6 +747,10 @@ __global__ __launch_bounds__(64) void argmax_keys_finish_kernel(unsigned long lo
     keys[m] = 0;
 }
 
+}  // namespace
+hipError_t launch_act_prep(const ActPrepArgs &pa, hipStream_t stream);
+namespace {
+
 template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kC, bool kDual>
 hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
@@ -754,10 +758,7 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
     constexpr int kOutTile = kDual ? 8 * kC : 16 * kC;
     const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf, kC, kDual>;
     if (!kLdsA) {
-        ActPrepArgs pa{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK};
-        hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(a.splits * kWK), (unsigned)((a.M + kPrepWaves - 1) / kPrepWaves)),
-                           dim3(kPrepWaves * 64), 0, stream, pa);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_act_prep(ActPrepArgs{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK}, stream);
         if (e != hipSuccess) return e;
     }
     if (plan.lds > 64 * 1024) {
@@ -814,6 +815,13 @@ hipError_t launch_pair(const GemmArgs &a, const GemmPlan &plan, hipStream_t stre
 }
 
 }  // namespace
+
+hipError_t launch_act_prep(const ActPrepArgs &pa, hipStream_t stream)
+{
+    hipLaunchKernelGGL(act_prep_kernel, dim3((unsigned)(pa.splits * pa.wk), (unsigned)((pa.M + kPrepWaves - 1) / kPrepWaves)),
+                       dim3(kPrepWaves * 64), 0, stream, pa);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {

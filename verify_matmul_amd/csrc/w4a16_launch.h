@@ -122,6 +122,26 @@ struct ActPrepArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream);
+// Activations to fp16 in slot order with one power-of-two rescale per (K piece, row); with
+// splits = wk = 1 a single piece covers the whole K of each row.
+hipError_t launch_act_prep(const ActPrepArgs &pa, hipStream_t stream);
+
+// Many-row GEMM (prompt processing): out[M, N] = A x W for any M, on the matrix cores, from
+// activations prepared by launch_act_prep with one piece per row (A16, shifts).
+struct PrefillArgs {
+    const uint16_t *A16;      // [M, K] fp16, slot order, rescaled per row
+    const int *shifts;        // [M] the rescale of each row (out = sum * 2^shift)
+    const uint32_t *qweight;
+    const uint16_t *scales;
+    const uint32_t *qzeros;   // nullptr: symmetric zero point 8
+    void *out;
+    int M, N, K, g;
+    int out_bf16;
+};
+// Output tile of one prefill workgroup (4 waves of 64 x 64).
+constexpr int kPrefillTileM = 128;
+constexpr int kPrefillTileN = 128;
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 struct ArgmaxArgs {
     const float *logits;
