@@ -50,34 +50,9 @@
 namespace w4a16 {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // Activation items (16 bytes) a lane may stage through registers: 8 KB per wave.
 constexpr int kHeld = 8;
 
-// s_waitcnt encoding (gfx9): wait until at most `n` vector memory operations are outstanding.
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-// Direct global->LDS loads: lane i's 16 (or 4) bytes land at lds_base + 16 i (4 i). They are
-// written as inline assembly on purpose. Had the compiler seen these LDS writes, it would guard
-// every LDS read that follows any later global load with a full vmcnt(0) wait -- one per
-// iteration of the main loop, draining the weight ring. The kernel instead waits for them
-// itself, once, with an explicit vmcnt before the staged data is first read. (Vector-memory
-// operations the compiler cannot see only make its own wait counts stricter, never looser.)
-__device__ __forceinline__ uint32_t lds_offset(void *lds_base)
-{
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)(lds_base));
-}
-
-__device__ __forceinline__ void load_to_lds16(const void *src, void *lds_base)
-{
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_offset(lds_base)) : "memory");
-}
-
-__device__ __forceinline__ void load_to_lds4(const void *src, void *lds_base)
-{
-    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_offset(lds_base)) : "memory");
-}
 
 // The K range [wb, we) (in steps) of piece `wave` of split `split`: splits cut K into
 // contiguous slices, the waves of a workgroup cut each slice again. The activation preparation

@@ -2,83 +2,100 @@
 //
 // The GRIMOIRE v1.8 release notes ('What changed', INT4 prompt processing) route GPTQ int4
 // weights through a fast prompt path. With hundreds of rows every packed weight feeds hundreds
-// of multiply-adds, so the bound is the matrix cores, not HBM, and the shape is a plain tiled
-// GEMM:
+// of multiply-adds, so the bound is the matrix cores, not HBM, and the shape is a tiled GEMM:
 //   * a workgroup owns a 128 x 128 output tile; its 4 waves own 64 x 64 quarters (4 x 4 blocks of
 //     one v_mfma_f32_16x16x32_f16 each per 32-row K step);
 //   * the activations come prepared once per call (act_prep_kernel with one piece per row):
 //     fp16 in the packed-word slot order after an exact power-of-two rescale of each row, so a
-//     lane's 16-byte load is an MFMA A fragment as is;
-//   * the packed weights are loaded as in the small-row kernel (lane: 4 adjacent columns of one
-//     word row, 256 contiguous bytes per 16 lanes) and dequantised exactly in registers into the
-//     B fragments of the wave's 4 column blocks (w4a16_device.h);
+//     16-byte read is an MFMA A fragment as is;
+//   * every operand of a step -- the 128 x 32 activation tile, the 32 x 128 packed weights, and
+//     the scales and zero words of the step's group -- is staged in LDS by direct global->LDS
+//     loads, kStages steps ahead, so the loads cost no registers and each step waits for its
+//     own stage only; one barrier per step both publishes a stage and frees the one before;
+//   * each wave dequantises its columns' packed words exactly in registers (w4a16_device.h)
+//     into the B fragments of its 4 column blocks;
 //   * sums are kept per quantisation group and scaled once at the group's end in fp32, so the
-//     exact (q - z) * scale product never rounds before accumulation;
-//   * each step's activation fragments, weight words, and the scales and zero word of its group
-//     travel in one ring slot: every load of the loop is unconditional, one step ahead per slot.
+//     exact (q - z) * scale product never rounds before accumulation.
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
 namespace w4a16 {
 namespace {
 
-constexpr int kPrefillPf = 2;   // ring depth in steps
+constexpr int kStages = 4;   // LDS ring depth in steps
+constexpr int kXcds = 8;     // gfx950 dies; workgroups are dispatched to them round-robin
 
-// One step's operands: the A fragments of the wave's 4 row blocks, 4 packed words (the lane's
-// 4 columns), and the fp16 scales and zero word of the step's group for those columns.
-struct PrefillSlot {
-    uint4 a[4];
-    uint4 w;
-    uint2 s;
-    uint32_t z;
-};
+// One stage of LDS: the activation tile [128 rows][4 chunks of 16 B] (a row's chunk c sits in
+// slot c ^ ((row / 4) % 4): the 16 rows a wave reads at once then fall into 16 different bank
+// groups), the packed weights [4 word rows][128 columns], 128 fp16 scales, 16 zero words.
+constexpr int kStA = kPrefillTileM * 64;
+constexpr int kStB = 4 * kPrefillTileN * 4;
+constexpr int kStS = kPrefillTileN * 2;
+constexpr int kStZ = kPrefillTileN / 8 * 4;
+constexpr int kStBytes = kStA + kStB + kStS + kStZ;
 
 template <bool kSym>
-__global__ __launch_bounds__(256) void w4a16_prefill_kernel(PrefillArgs p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w4a16_prefill_kernel(PrefillArgs p)
 {
+    __shared__ __align__(16) unsigned char lds[kStages * kStBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cl = lane & 15;   // A row / B column of the lane within a 16 x 16 block
     const int rl = lane >> 4;   // word row (8 K rows) of the lane within a 32-row step
+    const int wm = wave >> 1, wn = wave & 1;
     const int M = p.M;
     const int N = p.N;
     const int K = p.K;
-    const int n0 = blockIdx.x * kPrefillTileN + (wave & 1) * 64 + cl * 4;   // the lane's 4 columns
-    const bool col_ok = n0 < N;
-    const int nc = col_ok ? n0 : 0;
-    const int mb = blockIdx.y * kPrefillTileM + (wave >> 1) * 64;   // the wave's first row
+    // Tiles in row-major order, a contiguous range per die: workgroup w runs on die w % 8, so
+    // each die's L2 holds one or two row tiles' activations while its workgroups walk the
+    // column tiles (the dispatch order is a matter of speed only; any mapping is correct).
+    const int row_tiles = (M + kPrefillTileM - 1) / kPrefillTileM;
+    const int col_tiles = (N + kPrefillTileN - 1) / kPrefillTileN;
+    const int per_die = (row_tiles * col_tiles + kXcds - 1) / kXcds;
+    const int tile = (int)(blockIdx.x % kXcds) * per_die + (int)(blockIdx.x / kXcds);
+    if (tile >= row_tiles * col_tiles) return;   // padding of the grid to a multiple of 8
+    const int tm = tile / col_tiles * kPrefillTileM;   // the tile's first row
+    const int tn = tile % col_tiles * kPrefillTileN;   // the tile's first column
     const int steps = K / kStepK;
     const int spg = p.g / kStepK;
-    const int groups = K / p.g;
 
-    const uint32_t *wl = p.qweight + (size_t)rl * N + nc;
-    const uint16_t *al[4];
+    // ---- loads of one stage: every wave issues the same kLoads direct loads -------------------
+    constexpr int kLoads = kSym ? 4 : 5;
+    // activation tile: wave w fills slots [128 w, 128 w + 128) in two 64-slot loads
+    const uint16_t *a_src[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = min(mb + 16 * i + cl, M - 1);   // rows past M read the last row, never stored
-        al[i] = p.A16 + (size_t)m * K + rl * 8;
+    for (int h = 0; h < 2; ++h) {
+        const int slot = wave * 128 + h * 64 + lane;
+        const int row = slot >> 2;
+        const int chunk = (slot & 3) ^ ((row >> 2) & 3);
+        a_src[h] = p.A16 + (size_t)min(tm + row, M - 1) * K + chunk * 8;   // rows past M: the last row
     }
-    const uint16_t *sl = p.scales + nc;
-    const uint32_t *zl = kSym ? nullptr : p.qzeros + nc / 8;
-
-    // Loads run one slot ahead of use, in step order; their group is tracked by counting.
-    int lt = 0, lg = 0, lpos = 0;   // next step to load, its group and position in the group
-    auto load = [&](PrefillSlot &s) {
+    auto col = [&](int c) { return c < N ? c : 0; };   // columns past N read column 0, never stored
+    // packed weights: wave w loads word row w of the step, lanes 0..31 four columns each
+    const uint32_t *w_src = p.qweight + (size_t)wave * N + col(tn + (lane & 31) * 4);
+    // scales: wave w loads columns [32 w, 32 w + 32) as 16 pairs; zero words: wave w loads 4
+    const uint16_t *s_src = p.scales + col(tn + wave * 32 + (lane & 15) * 2);
+    const uint32_t *z_src = kSym ? nullptr : p.qzeros + col(tn + (wave * 4 + (lane & 3)) * 8) / 8;
+    int lt = 0, lg = 0, lpos = 0;   // next step to stage, its group and position in the group
+    auto issue = [&](int buf) {
+        unsigned char *st = lds + buf * kStBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s.a[i] = *reinterpret_cast<const uint4 *>(al[i] + (size_t)lt * kStepK);
-        s.w = *reinterpret_cast<const uint4 *>(wl + (uint32_t)(lt * 4 * N));   // < 2^32 words (host)
-        s.s = *reinterpret_cast<const uint2 *>(sl + (size_t)lg * N);
-        if (!kSym) s.z = zl[(size_t)lg * (N / 8)];
-        if (lt + 1 < steps) {   // past the last step the slot reloads it (uniform)
+        for (int h = 0; h < 2; ++h) load_to_lds16(a_src[h] + (size_t)lt * kStepK, st + (wave * 128 + h * 64) * 16);
+        if (lane < 32) load_to_lds16(w_src + (uint32_t)(lt * 4 * N), st + kStA + wave * 512);   // < 2^32 words
+        if (lane < 16) load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 64);
+        if (!kSym && lane < 4) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 16);
+        if (lt + 1 < steps) {   // past the last step the stage reloads it (uniform)
             ++lt;
             if (++lpos == spg) {
                 lpos = 0;
-                lg = min(lg + 1, groups - 1);
+                ++lg;
             }
         }
     };
 
+    // ---- compute ------------------------------------------------------------------------------
+    const int n0 = tn + wn * 64 + cl * 4;   // the lane's 4 columns
     const Masks mk = make_masks();
     float4_t acc[4][4];
     float4_t tot[4][4];
@@ -93,29 +110,42 @@ __global__ __launch_bounds__(256) void w4a16_prefill_kernel(PrefillArgs p)
 #pragma unroll
     for (int j = 0; j < 4; ++j) zs[j] = zero_sub_sym();
     int cpos = 0;   // position of the computed step in its group
-
-    auto step = [&](const PrefillSlot &s) {
-        if (!kSym && cpos == 0) {   // a new group's zero points (uniform)
+    int a_off[4];   // the lane's A fragment of each row block within a stage
 #pragma unroll
-            for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(s.z, (uint32_t)(nc + j)));
+    for (int i = 0; i < 4; ++i) {
+        const int row = wm * 64 + 16 * i + cl;
+        a_off[i] = row * 64 + ((rl ^ ((row >> 2) & 3)) * 16);
+    }
+    const int b_off = kStA + rl * 512 + (wn * 64 + cl * 4) * 4;
+    const int s_off = kStA + kStB + (wn * 64 + cl * 4) * 2;
+    const int z_off = kStA + kStB + kStS + (wn * 8 + (cl >> 1)) * 4;
+
+    auto step = [&](int buf) {
+        const unsigned char *st = lds + buf * kStBytes;
+        if (!kSym && cpos == 0) {   // a new group's zero points (uniform)
+            const uint32_t zw = *reinterpret_cast<const uint32_t *>(st + z_off);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(n0 + j)));
         }
-        const uint32_t words[4] = {s.w.x, s.w.y, s.w.z, s.w.w};
+        const uint4 w = *reinterpret_cast<const uint4 *>(st + b_off);
+        const uint32_t words[4] = {w.x, w.y, w.z, w.w};
         half8_t b[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const half8_t a = __builtin_bit_cast(half8_t, s.a[i]);
+            const half8_t a = *reinterpret_cast<const half8_t *>(st + a_off[i]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
         }
         if (++cpos == spg) {   // the group's end: scale its sums once (uniform)
             cpos = 0;
+            const uint2 sv = *reinterpret_cast<const uint2 *>(st + s_off);
             float sc[4];
-            sc[0] = half_bits_to_float(s.s.x & 0xFFFFu);
-            sc[1] = half_bits_to_float(s.s.x >> 16);
-            sc[2] = half_bits_to_float(s.s.y & 0xFFFFu);
-            sc[3] = half_bits_to_float(s.s.y >> 16);
+            sc[0] = half_bits_to_float(sv.x & 0xFFFFu);
+            sc[1] = half_bits_to_float(sv.x >> 16);
+            sc[2] = half_bits_to_float(sv.y & 0xFFFFu);
+            sc[3] = half_bits_to_float(sv.y >> 16);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -127,31 +157,25 @@ __global__ __launch_bounds__(256) void w4a16_prefill_kernel(PrefillArgs p)
         }
     };
 
-    PrefillSlot ring[kPrefillPf];
+    // Stages 0 .. kStages-2 first; at step t, after the wait for stage t and the barrier (every
+    // wave is past step t-1), stage t + kStages - 1 refills the buffer step t-1 used.
 #pragma unroll
-    for (int u = 0; u < kPrefillPf; ++u) load(ring[u]);
-    // Whole rounds of the ring, each slot computed and then reloaded unconditionally; the last
-    // steps % kPrefillPf steps are left in the first slots.
-    const int full_end = steps / kPrefillPf * kPrefillPf;
-    int t0 = 0;
-    for (; t0 < full_end; t0 += kPrefillPf) {
-#pragma unroll
-        for (int u = 0; u < kPrefillPf; ++u) {
-            step(ring[u]);
-            load(ring[u]);
-        }
+    for (int u = 0; u + 1 < kStages; ++u) issue(u);
+    for (int t = 0; t < steps; ++t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoads));
+        __syncthreads();
+        issue((t + kStages - 1) % kStages);
+        step(t % kStages);
     }
-#pragma unroll
-    for (int u = 0; u + 1 < kPrefillPf; ++u)
-        if (t0 + u < steps) step(ring[u]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last stages' reloads land before the wave ends
 
     // Lane holds rows 4 rl + r of each row block, its 4 columns: undo the row's rescale, store.
-    if (!col_ok) return;
+    if (n0 >= N) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = mb + 16 * i + 4 * rl + r;
+            const int m = tm + wm * 64 + 16 * i + 4 * rl + r;
             if (m >= M) continue;
             const int sh = p.shifts[m];
             const float x0 = __builtin_amdgcn_ldexpf(tot[i][0][r], sh), x1 = __builtin_amdgcn_ldexpf(tot[i][1][r], sh);
@@ -172,8 +196,8 @@ __global__ __launch_bounds__(256) void w4a16_prefill_kernel(PrefillArgs p)
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((a.N + kPrefillTileN - 1) / kPrefillTileN),
-                    (unsigned)((a.M + kPrefillTileM - 1) / kPrefillTileM));
+    const int tiles = ((a.M + kPrefillTileM - 1) / kPrefillTileM) * ((a.N + kPrefillTileN - 1) / kPrefillTileN);
+    const dim3 grid((unsigned)((tiles + kXcds - 1) / kXcds * kXcds));   // whole rounds of the 8 dies
     if (a.qzeros == nullptr)
         hipLaunchKernelGGL(w4a16_prefill_kernel<true>, grid, dim3(256), 0, stream, a);
     else
