@@ -138,9 +138,9 @@ struct PrefillArgs {
     int M, N, K, g;
     int out_bf16;
 };
-// Output tile of one prefill workgroup (4 waves of 64 x 64).
-constexpr int kPrefillTileM = 128;
-constexpr int kPrefillTileN = 128;
+// Output tile of one prefill workgroup (4 waves of 64 x 64 side by side).
+constexpr int kPrefillTileM = 64;
+constexpr int kPrefillTileN = 256;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 struct ArgmaxArgs {

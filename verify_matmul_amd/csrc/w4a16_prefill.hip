@@ -3,8 +3,12 @@
 // The GRIMOIRE v1.8 release notes ('What changed', INT4 prompt processing) route GPTQ int4
 // weights through a fast prompt path. With hundreds of rows every packed weight feeds hundreds
 // of multiply-adds, so the bound is the matrix cores, not HBM, and the shape is a tiled GEMM:
-//   * a workgroup owns a 128 x 128 output tile; its 4 waves own 64 x 64 quarters (4 x 4 blocks of
-//     one v_mfma_f32_16x16x32_f16 each per 32-row K step);
+//   * a workgroup owns a 64 x 256 output tile; each of its 4 waves owns 64 x 64 (4 x 4 blocks of
+//     one v_mfma_f32_16x16x32_f16 each per 32-row K step). The tile is wide because a step moves
+//     2 / width bytes of activations (re-read by every column tile) per multiply-add against
+//     0.5 / height of packed weights, and the global->LDS traffic is what bounds the kernel
+//     (64 x 256 measured 18% faster than 128 x 128 at 512 rows; 128 x 256 with 8 waves slower,
+//     one such workgroup per CU leaving no second one to run while it waits);
 //   * the activations come prepared once per call (act_prep_kernel with one piece per row):
 //     fp16 in the packed-word slot order after an exact power-of-two rescale of each row, so a
 //     16-byte read is an MFMA A fragment as is;
@@ -25,9 +29,9 @@ namespace {
 constexpr int kStages = 4;   // LDS ring depth in steps
 constexpr int kXcds = 8;     // gfx950 dies; workgroups are dispatched to them round-robin
 
-// One stage of LDS: the activation tile [128 rows][4 chunks of 16 B] (a row's chunk c sits in
+// One stage of LDS: the activation tile [64 rows][4 chunks of 16 B] (a row's chunk c sits in
 // slot c ^ ((row / 4) % 4): the 16 rows a wave reads at once then fall into 16 different bank
-// groups), the packed weights [4 word rows][128 columns], 128 fp16 scales, 16 zero words.
+// groups), the packed weights [4 word rows][256 columns], 256 fp16 scales, 32 zero words.
 constexpr int kStA = kPrefillTileM * 64;
 constexpr int kStB = 4 * kPrefillTileN * 4;
 constexpr int kStS = kPrefillTileN * 2;
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const int wave = tid >> 6;
     const int cl = lane & 15;   // A row / B column of the lane within a 16 x 16 block
     const int rl = lane >> 4;   // word row (8 K rows) of the lane within a 32-row step
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wn = wave;   // the wave's 64 columns
     const int M = p.M;
     const int N = p.N;
     const int K = p.K;
@@ -61,30 +65,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const int spg = p.g / kStepK;
 
     // ---- loads of one stage: every wave issues the same kLoads direct loads -------------------
-    constexpr int kLoads = kSym ? 4 : 5;
-    // activation tile: wave w fills slots [128 w, 128 w + 128) in two 64-slot loads
-    const uint16_t *a_src[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int slot = wave * 128 + h * 64 + lane;
+    constexpr int kLoads = kSym ? 3 : 4;
+    // activation tile: wave w fills slots [64 w, 64 w + 64), rows 16 w .. 16 w + 15
+    const uint16_t *a_src;
+    {
+        const int slot = wave * 64 + lane;
         const int row = slot >> 2;
         const int chunk = (slot & 3) ^ ((row >> 2) & 3);
-        a_src[h] = p.A16 + (size_t)min(tm + row, M - 1) * K + chunk * 8;   // rows past M: the last row
+        a_src = p.A16 + (size_t)min(tm + row, M - 1) * K + chunk * 8;   // rows past M: the last row
     }
     auto col = [&](int c) { return c < N ? c : 0; };   // columns past N read column 0, never stored
-    // packed weights: wave w loads word row w of the step, lanes 0..31 four columns each
-    const uint32_t *w_src = p.qweight + (size_t)wave * N + col(tn + (lane & 31) * 4);
-    // scales: wave w loads columns [32 w, 32 w + 32) as 16 pairs; zero words: wave w loads 4
-    const uint16_t *s_src = p.scales + col(tn + wave * 32 + (lane & 15) * 2);
-    const uint32_t *z_src = kSym ? nullptr : p.qzeros + col(tn + (wave * 4 + (lane & 3)) * 8) / 8;
+    // packed weights: wave w loads word row w of the step, four columns per lane
+    const uint32_t *w_src = p.qweight + (size_t)wave * N + col(tn + lane * 4);
+    // scales: wave w loads columns [64 w, 64 w + 64) as 32 pairs; zero words: wave w loads 8
+    const uint16_t *s_src = p.scales + col(tn + wave * 64 + (lane & 31) * 2);
+    const uint32_t *z_src = kSym ? nullptr : p.qzeros + col(tn + (wave * 8 + (lane & 7)) * 8) / 8;
     int lt = 0, lg = 0, lpos = 0;   // next step to stage, its group and position in the group
     auto issue = [&](int buf) {
         unsigned char *st = lds + buf * kStBytes;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) load_to_lds16(a_src[h] + (size_t)lt * kStepK, st + (wave * 128 + h * 64) * 16);
-        if (lane < 32) load_to_lds16(w_src + (uint32_t)(lt * 4 * N), st + kStA + wave * 512);   // < 2^32 words
-        if (lane < 16) load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 64);
-        if (!kSym && lane < 4) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 16);
+        load_to_lds16(a_src + (size_t)lt * kStepK, st + wave * 64 * 16);
+        load_to_lds16(w_src + (uint32_t)(lt * 4 * N), st + kStA + wave * 1024);   // < 2^32 words
+        if (lane < 32) load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
+        if (!kSym && lane < 8) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 32);
         if (lt + 1 < steps) {   // past the last step the stage reloads it (uniform)
             ++lt;
             if (++lpos == spg) {
@@ -113,10 +115,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     int a_off[4];   // the lane's A fragment of each row block within a stage
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + 16 * i + cl;
+        const int row = 16 * i + cl;
         a_off[i] = row * 64 + ((rl ^ ((row >> 2) & 3)) * 16);
     }
-    const int b_off = kStA + rl * 512 + (wn * 64 + cl * 4) * 4;
+    const int b_off = kStA + rl * 1024 + (wn * 64 + cl * 4) * 4;
     const int s_off = kStA + kStB + (wn * 64 + cl * 4) * 2;
     const int z_off = kStA + kStB + kStS + (wn * 8 + (cl >> 1)) * 4;
 
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = tm + wm * 64 + 16 * i + 4 * rl + r;
+            const int m = tm + 16 * i + 4 * rl + r;
             if (m >= M) continue;
             const int sh = p.shifts[m];
             const float x0 = __builtin_amdgcn_ldexpf(tot[i][0][r], sh), x1 = __builtin_amdgcn_ldexpf(tot[i][1][r], sh);
