@@ -21,6 +21,11 @@ Timed regions (all on the library's stream, inputs resident in HBM):
 summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or null when the
 kernel sources changed since the counters were taken.
 
+With --prefill every call is the many-row (prompt-processing) GEMM, w4a16_gemm_prefill, on the
+workload's matrix with M = 512 and 2048 rows by default (activations drawn with the workload's
+distribution): the bound is the fp16 matrix cores (2.5 PFLOP/s dense), and the line reports
+TFLOP/s (2*M*N*K per call) with an "mfma" roofline.
+
 With --gate-up every call is instead the fused gated pair on the workload's shape,
 silu(A x W_gate) * (A x W_up) (w4a16_gemm_gate_up): two weight matrices per call, one [M, N]
 output, and the algorithmic bytes count both matrices.
@@ -41,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16 matrix cores
 POOL_BYTES = 768 * 2 ** 20      # rotating weight pool, 3x the 256 MB last-level cache
 
 
@@ -62,6 +68,9 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="workgroups per column tile along K (0 = default)")
     p.add_argument("--waves-k", type=int, default=0, help="waves per workgroup along K (0 = default)")
     p.add_argument("--tile-cols", type=int, default=0, help="column tile width, 64 or 128 (0 = default)")
+    p.add_argument("--prefill", action="store_true",
+                   help="time the many-row GEMM (w4a16_gemm_prefill) on the workload's matrix, M = --ms "
+                        "(default 512,2048)")
     p.add_argument("--gate-up", action="store_true",
                    help="time the fused gated pair silu(A x W_gate) * (A x W_up) on the workload's shape")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,6 +148,8 @@ def main():
         return 0
 
     lib = vm.load()
+    if args.prefill:
+        return run_prefill(args, lib)
     wl = synth.WORKLOADS[args.workload]
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
     inp = synth.make_inputs(wl)
@@ -328,6 +339,126 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_prefill(args, lib):
+    """The many-row GEMM: one call per M per step, TFLOP/s against the fp16 matrix-core peak."""
+    import numpy as np
+    import torch
+    import verify_matmul_amd as vm
+    from verify_matmul_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    if wl.argmax or args.gate_up or args.splits or args.waves_k or args.tile_cols:
+        print("bench.py: --prefill takes an FFN or attention workload and no launch knobs", file=sys.stderr)
+        return 2
+    ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else (512, 2048)
+    inp = synth.make_inputs(wl)
+    K, N, g = wl.K, wl.N, wl.group
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    # prompt-sized activations with the workload's distribution (its own seeded draw)
+    rng = np.random.Generator(np.random.PCG64(1000 * wl.index + 8))
+    act = synth.draw_activations(rng, max(ms), K, wl.act_sigma, wl.outlier_frac, wl.outlier_mul)
+    per_copy = algorithmic_bytes(0, K, N, g, wl.symmetric)
+    R = max(2, math.ceil(POOL_BYTES / per_copy))
+    qw0 = torch.from_numpy(inp.qweight.view(np.int32)).to(dev)
+    sc = torch.from_numpy(inp.scales.view(np.int16)).to(dev)
+    qz = None if inp.qzeros is None else torch.from_numpy(inp.qzeros.view(np.int32)).to(dev)
+    pool = [qw0.clone() for _ in range(R)]
+    a = torch.from_numpy(act.view(np.int16)).to(dev)
+    outs = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}
+    stream = torch.cuda.current_stream()
+
+    def call(i, M):
+        vm.w4a16_gemm_prefill(a[:M], pool[i % R], sc, qz, g, outs[M], stream=stream)
+
+    def step(i, evs=None):
+        for j, M in enumerate(ms):
+            if evs is not None:
+                evs[i][j][0].record(stream)
+            call(i * len(ms) + j, M)
+            if evs is not None:
+                evs[i][j][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = sum(2.0 * M * N * K for M in ms)
+    value = flops * args.steps / wall / 1e12
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs)
+    torch.cuda.synchronize()
+    per_m, dom, dom_time = {}, None, -1.0
+    for j, M in enumerate(ms):
+        d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
+        us = float(np.mean(d))
+        f = 2.0 * M * N * K
+        per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+                         "us_p90": round(float(np.percentile(d, 90)), 3), "TFLOPs": round(f / us / 1e6, 1),
+                         "frac_of_peak": round(f / us / 1e6 / PEAK_F16_TFLOPS, 4), "flops": f,
+                         "hbm_GBps_weights_once": round(algorithmic_bytes(M, K, N, g, wl.symmetric) / us / 1e3, 1)}
+        if float(np.sum(d)) > dom_time:
+            dom, dom_time = M, float(np.sum(d))
+    # the dominant call alone, back to back between one event pair on its stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i, dom)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
+    f_dom = 2.0 * dom * N * K
+    rec = {
+        "metric": "W4A16 prefill GEMM TFLOP/s (% of fp16 matrix-core peak), us/call",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}, prompt rows M in {','.join(map(str, ms))} (one call each per step)",
+                   "K": K, "N": N, "group": g, "symmetric_zero": wl.symmetric, "ms": list(ms), "out": "fp32",
+                   "rotation_copies": R},
+        "roofline": {"bound": "mfma", "kernel": f"w4a16_prefill_kernel (M={dom})", "M": dom,
+                     "achieved": round(f_dom / us_dom / 1e6, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(f_dom / us_dom / 1e6 / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "launches": args.steps, "flops_per_launch": f_dom, "us_per_launch": round(us_dom, 3),
+                     "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
+        "per_m": per_m,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        M = min(ms)
+        cols = np.arange(0, N, max(1, N // 256))[:256]   # a bounded sample of columns
+        reps, elapsed = 0, 0.0
+        while elapsed < args.cpu_seconds or reps == 0:
+            t = time.perf_counter()
+            oracle.gemm(act[:M], inp.qweight, inp.scales, inp.qzeros, g, cols, with_bound=False)
+            elapsed += time.perf_counter() - t
+            reps += 1
+        rec["cpu_baseline"] = {"value": round(2.0 * M * len(cols) * K * reps / elapsed / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{reps} call(s) of M={M} rows on {len(cols)} of the {N} columns, "
+                                         f"{elapsed:.1f} s of oracle time"}
     print(json.dumps(rec), flush=True)
     return 0
 
