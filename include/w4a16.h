@@ -116,8 +116,11 @@ int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *sc
  * matrix cores, not HBM, set the pace. Each row of A is rescaled by one power of two over its
  * whole K before the fp16 matrix cores (exact; a bf16 value keeps all its bits when it lies
  * within 2^31 of its row's largest magnitude), so results match w4a16_gemm's accuracy
- * contract. Uses M * K * 2 + M * 4 bytes of the stream's scratch for the prepared activations
- * (allocated on the first call of a size on a stream). Meant for M well above 16; any M works.
+ * contract. Uses M * K * 2 + M * 4 bytes of the stream's scratch for the prepared activations,
+ * and when the output has fewer 64 x 256 tiles than the device runs at once, up to
+ * 16 * M * N * 4 more for fp32 sums of whole-group K slices, added in slice order (scratch is
+ * allocated on the first call of a size on a stream). Deterministic. Meant for M well above 16;
+ * any M works.
  */
 #define W4A16_PREFILL_MAX_M 65536
 int w4a16_gemm_prefill(const void *A, const uint32_t *qweight, const uint16_t *scales,

@@ -135,8 +135,10 @@ struct PrefillArgs {
     const uint16_t *scales;
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
     void *out;
+    float *partials;          // [splits, M, N] fp32 slices when splits > 1 (else unused)
     int M, N, K, g;
     int out_bf16;
+    int splits;               // workgroups per tile along K, each a contiguous range of groups
 };
 // Output tile of one prefill workgroup (4 waves of 64 x 64 side by side).
 constexpr int kPrefillTileM = 64;

@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kStages = 4;   // LDS ring depth in steps
 constexpr int kXcds = 8;     // gfx950 dies; workgroups are dispatched to them round-robin
+constexpr int kRowGroup = 4; // row tiles that visit the column tiles together
 
 // One stage of LDS: the activation tile [64 rows][4 chunks of 16 B] (a row's chunk c sits in
 // slot c ^ ((row / 4) % 4): the 16 rows a wave reads at once then fall into 16 different bank
@@ -51,18 +52,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const int M = p.M;
     const int N = p.N;
     const int K = p.K;
-    // Tiles in row-major order, a contiguous range per die: workgroup w runs on die w % 8, so
-    // each die's L2 holds one or two row tiles' activations while its workgroups walk the
-    // column tiles (the dispatch order is a matter of speed only; any mapping is correct).
+    // A contiguous range of tiles per die: workgroup w runs on die w % 8 (the dispatch order is a
+    // matter of speed only; any mapping is correct).
+    // Work units are (tile, K slice) pairs, the slices of a tile adjacent.
     const int row_tiles = (M + kPrefillTileM - 1) / kPrefillTileM;
     const int col_tiles = (N + kPrefillTileN - 1) / kPrefillTileN;
-    const int per_die = (row_tiles * col_tiles + kXcds - 1) / kXcds;
-    const int tile = (int)(blockIdx.x % kXcds) * per_die + (int)(blockIdx.x / kXcds);
-    if (tile >= row_tiles * col_tiles) return;   // padding of the grid to a multiple of 8
-    const int tm = tile / col_tiles * kPrefillTileM;   // the tile's first row
-    const int tn = tile % col_tiles * kPrefillTileN;   // the tile's first column
-    const int steps = K / kStepK;
+    const int units = row_tiles * col_tiles * p.splits;
+    const int per_die = (units + kXcds - 1) / kXcds;
+    const int unit = (int)(blockIdx.x % kXcds) * per_die + (int)(blockIdx.x / kXcds);
+    if (unit >= units) return;   // padding of the grid to a multiple of 8
+    const int tile = unit / p.splits;
+    const int slice = unit - tile * p.splits;
+    // Within that order, kRowGroup row tiles take each column tile in turn, so the row tiles of
+    // a group share a weight tile in L2 while their activations stay there.
+    const int grp = tile / (kRowGroup * col_tiles);
+    const int g_rows = min(kRowGroup, row_tiles - grp * kRowGroup);
+    const int idx = tile - grp * kRowGroup * col_tiles;
+    const int tm = (grp * kRowGroup + idx % g_rows) * kPrefillTileM;   // the tile's first row
+    const int tn = (idx / g_rows) * kPrefillTileN;                     // the tile's first column
     const int spg = p.g / kStepK;
+    // the slice's K range: whole quantisation groups [gb, ge), so every group is scaled once
+    const int groups = K / p.g;
+    const int gb = (int)((long long)slice * groups / p.splits);
+    const int ge = (int)((long long)(slice + 1) * groups / p.splits);
+    const int s0 = gb * spg;              // first step of the slice
+    const int steps = (ge - gb) * spg;    // steps of the slice (>= 1: splits <= groups)
 
     // ---- loads of one stage: every wave issues the same kLoads direct loads -------------------
     constexpr int kLoads = kSym ? 3 : 4;
@@ -80,14 +94,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     // scales: wave w loads columns [64 w, 64 w + 64) as 32 pairs; zero words: wave w loads 8
     const uint16_t *s_src = p.scales + col(tn + wave * 64 + (lane & 31) * 2);
     const uint32_t *z_src = kSym ? nullptr : p.qzeros + col(tn + (wave * 8 + (lane & 7)) * 8) / 8;
-    int lt = 0, lg = 0, lpos = 0;   // next step to stage, its group and position in the group
+    int lt = s0, lg = gb, lpos = 0;   // next step to stage, its group and position in the group
     auto issue = [&](int buf) {
         unsigned char *st = lds + buf * kStBytes;
         load_to_lds16(a_src + (size_t)lt * kStepK, st + wave * 64 * 16);
         load_to_lds16(w_src + (uint32_t)(lt * 4 * N), st + kStA + wave * 1024);   // < 2^32 words
         if (lane < 32) load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
         if (!kSym && lane < 8) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 32);
-        if (lt + 1 < steps) {   // past the last step the stage reloads it (uniform)
+        if (lt + 1 < s0 + steps) {   // past the slice's last step the stage reloads it (uniform)
             ++lt;
             if (++lpos == spg) {
                 lpos = 0;
@@ -171,8 +185,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last stages' reloads land before the wave ends
 
-    // Lane holds rows 4 rl + r of each row block, its 4 columns: undo the row's rescale, store.
+    // Lane holds rows 4 rl + r of each row block, its 4 columns: undo the row's rescale, store
+    // (or store the slice's fp32 sums for the slice reduction).
     if (n0 >= N) return;
+    if (p.splits > 1) {
+        float *part = p.partials + (size_t)slice * M * N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = tm + 16 * i + 4 * rl + r;
+                if (m >= M) continue;
+                const int sh = p.shifts[m];
+                *reinterpret_cast<float4 *>(part + (size_t)m * N + n0) =
+                    make_float4(__builtin_amdgcn_ldexpf(tot[i][0][r], sh), __builtin_amdgcn_ldexpf(tot[i][1][r], sh),
+                                __builtin_amdgcn_ldexpf(tot[i][2][r], sh), __builtin_amdgcn_ldexpf(tot[i][3][r], sh));
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -194,16 +224,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         }
 }
 
+// out = the sum of the K slices in slice order (deterministic), 4 outputs per thread.
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs p)
+{
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
+    const size_t mn = (size_t)p.M * p.N;
+    if (q * 4 >= mn) return;
+    float4 v = reinterpret_cast<const float4 *>(p.partials)[q];
+    for (int s = 1; s < p.splits; ++s) {
+        const float4 w = reinterpret_cast<const float4 *>(p.partials + (size_t)s * mn)[q];
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+    }
+    if (p.out_bf16) {
+        uint2 o;
+        o.x = float_to_bf16_bits(v.x) | (float_to_bf16_bits(v.y) << 16);
+        o.y = float_to_bf16_bits(v.z) | (float_to_bf16_bits(v.w) << 16);
+        reinterpret_cast<uint2 *>(p.out)[q] = o;
+    } else {
+        reinterpret_cast<float4 *>(p.out)[q] = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
-    const int tiles = ((a.M + kPrefillTileM - 1) / kPrefillTileM) * ((a.N + kPrefillTileN - 1) / kPrefillTileN);
-    const dim3 grid((unsigned)((tiles + kXcds - 1) / kXcds * kXcds));   // whole rounds of the 8 dies
+    const int units = ((a.M + kPrefillTileM - 1) / kPrefillTileM) * ((a.N + kPrefillTileN - 1) / kPrefillTileN) * a.splits;
+    const dim3 grid((unsigned)((units + kXcds - 1) / kXcds * kXcds));   // whole rounds of the 8 dies
     if (a.qzeros == nullptr)
         hipLaunchKernelGGL(w4a16_prefill_kernel<true>, grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(w4a16_prefill_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    const size_t quads = (size_t)a.M * a.N / 4;   // N % 8 == 0
+    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
