@@ -103,10 +103,10 @@ def cpu_baseline(wl, inp, ms, seconds, gate=None):
                       f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)"}
 
 
-def load_traffic(workload, M):
+def load_traffic(workload, M, kernel="w4a16_gemm_kernel"):
     """HBM bytes per launch of the M-row call, from the committed rocprofv3 counter summary, if it
     still matches the kernel source; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"traffic_w4a16_gemm_kernel_{workload}_M{M}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_M{M}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -438,7 +438,8 @@ def run_prefill(args, lib):
                    "rotation_copies": R},
         "roofline": {"bound": "mfma", "kernel": f"w4a16_prefill_kernel (M={dom})", "M": dom,
                      "achieved": round(f_dom / us_dom / 1e6, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(f_dom / us_dom / 1e6 / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "frac": round(f_dom / us_dom / 1e6 / PEAK_F16_TFLOPS, 4),
+                     "traffic": load_traffic(args.workload, dom, "w4a16_prefill_kernel"),
                      "launches": args.steps, "flops_per_launch": f_dom, "us_per_launch": round(us_dom, 3),
                      "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
         "per_m": per_m,

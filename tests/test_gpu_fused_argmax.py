@@ -87,3 +87,26 @@ def test_fused_pick_ties_take_the_lowest_index(gu):
     for m in range(16):
         if y[m, 7] == y[m].max():
             assert idx[m] == 7
+
+
+def test_draft_vocabulary_subset(gu):
+    """Drafted tokens scored against only the first n rows of the output layer: strix-llama.cpp
+    PR #105 (commit messages) copies those rows once at load time. In this layout that copy is a
+    [K/8, n] matrix of the head's first n columns, so the fused pick over it is the greedy choice
+    among those n tokens of the full head: its logits meet the bar against the full head's first
+    n columns, and its index is the oracle's wherever the top-2 gap exceeds the error bound."""
+    K, N_full, g, n, M = 2048, 40000, 128, 16384, 16
+    inp = synth.make_random(31, M, K, N_full, g, symmetric=True)
+    draft = synth.Inputs(np.ascontiguousarray(inp.qweight[:, :n]), np.ascontiguousarray(inp.scales[:, :n]), None,
+                         inp.act, g)
+    d = gu.DevInputs(draft)
+    logits, idx = fused_vs_separate(gu, d, M)
+    y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, None, g, cols=np.arange(n))
+    parity.check_close(logits, y_ref, bound, "draft head")
+    checked = 0
+    for m in range(M):
+        top, second = np.argsort(-y_ref[m], kind="stable")[:2]
+        if y_ref[m, top] - y_ref[m, second] > 2 * parity.tolerance(bound[m, [top, second]]).max():
+            assert idx[m] == top
+            checked += 1
+    assert checked >= 2
