@@ -92,3 +92,48 @@ def test_release_scratch_then_call_again(gu):
     second = d.run(4, splits=4, waves_k=4)
     parity.check_close(second, y_ref, bound, "after release")
     assert np.array_equal(first, second)
+
+
+def test_every_entry_point_interleaved_on_one_stream(gu):
+    """The small-row GEMM, the gated pair and the many-row GEMM share one stream's scratch
+    (counters, stamped slices, prepared activations, K-slice sums) and grow it in turn: each
+    call's result equals the same call made alone on a fresh scratch block."""
+    K, N, g = 2048, 1032, 64
+    gate = synth.make_random(41, 300, K, N, g, symmetric=False)
+    up = synth.make_random(42, 300, K, N, g, symmetric=False)
+    up = synth.Inputs(up.qweight, up.scales, up.qzeros, gate.act, g)
+    dg, du = gu.DevInputs(gate), gu.DevInputs(up)
+
+    def small(M):
+        out = torch.empty((M, N), dtype=torch.float32, device=gu.DEV)
+        vm.w4a16_gemm(du.act[:M], du.qweight, du.scales, du.qzeros, g, out)
+        return out
+
+    def pair(M):
+        out = torch.empty((M, N), dtype=torch.float32, device=gu.DEV)
+        vm.w4a16_gemm_gate_up(du.act[:M], (dg.qweight, dg.scales, dg.qzeros), (du.qweight, du.scales, du.qzeros),
+                              g, out)
+        return out
+
+    def many(M):
+        out = torch.empty((M, N), dtype=torch.float32, device=gu.DEV)
+        vm.w4a16_gemm_prefill(du.act[:M], du.qweight, du.scales, du.qzeros, g, out)
+        return out
+
+    calls = [(small, 16), (many, 300), (pair, 5), (small, 1), (many, 40), (pair, 16), (many, 300), (small, 16)]
+    alone = {}
+    for fn, M in set(calls):
+        torch.cuda.synchronize()
+        vm.w4a16_release_scratch()
+        r = fn(M)
+        torch.cuda.synchronize()
+        alone[(fn.__name__, M)] = r.cpu().numpy()
+    torch.cuda.synchronize()
+    vm.w4a16_release_scratch()
+    outs = [(fn.__name__, M, fn(M)) for fn, M in calls]   # queued back to back, one stream
+    torch.cuda.synchronize()
+    for i, (name, M, o) in enumerate(outs):
+        gu.say(f"[interleaved] call {i}: {name} M={M}")
+        assert np.array_equal(o.cpu().numpy(), alone[(name, M)]), (i, name, M)
+    y_ref, bound = oracle.gemm(up.act[:300], up.qweight, up.scales, up.qzeros, g)
+    parity.check_close(alone[("many", 300)].astype(np.float64), y_ref, bound, "many-row alone")
