@@ -504,7 +504,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
 #pragma unroll
             for (int v = 0; v < (kDual ? 1 : kV); ++v) {
                 float x0 = tot[4 * v][r], x1 = tot[4 * v + 1][r], x2 = tot[4 * v + 2][r], x3 = tot[4 * v + 3][r];
-                if (kDual) {   // silu(gate) * up
+                if constexpr (kDual) {   // silu(gate) * up
                     x0 = silu_f32(x0) * tot[4][r];
                     x1 = silu_f32(x1) * tot[5][r];
                     x2 = silu_f32(x2) * tot[6][r];
