@@ -155,6 +155,20 @@ int w4a16_gemm_gate_up_ex(const void *A, const uint32_t *qweight_gate, const uin
                           hipStream_t stream);
 
 /*
+ * The gated feed-forward input for many rows (prompt processing), on the matrix cores: the
+ * operation and argument rules of w4a16_gemm_gate_up with M in 1..W4A16_PREFILL_MAX_M, computed
+ * as w4a16_gemm_prefill computes a product (so g and u follow its accuracy contract), with
+ * silu(g) * u formed before the single [M, N] store. This is where the GRIMOIRE v1.8 release
+ * notes ('What changed', INT4 prompt processing) fuse the feed-forward gate. Scratch as
+ * w4a16_gemm_prefill, the K-slice sums being 2N wide.
+ */
+int w4a16_gemm_gate_up_prefill(const void *A, const uint32_t *qweight_gate,
+                               const uint16_t *scales_gate, const uint32_t *qzeros_gate,
+                               const uint32_t *qweight_up, const uint16_t *scales_up,
+                               const uint32_t *qzeros_up, int group_size, int M, int N, int K,
+                               void *out, int out_dtype, hipStream_t stream);
+
+/*
  * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32
  * comparison, -0 == +0, NaN entries ignored; an all-NaN row gives 0).
  *   logits fp32 [M, N] device, 16-byte aligned; M in 1..65535; N in 1..2^31-1

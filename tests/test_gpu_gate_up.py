@@ -128,3 +128,52 @@ def test_gate_up_ffn_workload(gu, M):
     h_ref, yg, bg, yu, bu = p.ref(M, cols)
     frac = parity.check_gate_up(h[:, cols], h_ref, yg, bg, yu, bu, f"ffn gate_up M={M}")
     gu.say(f"  worst err/tol {frac:.3e}")
+
+
+def run_prefill_pair(gu, p, M, out_dtype=torch.float32, act=None):
+    out = torch.empty((M, p.N), dtype=out_dtype, device=gu.DEV)
+    a = p.du.act[:M] if act is None else act
+    vm.w4a16_gemm_gate_up_prefill(a, (p.dg.qweight, p.dg.scales, p.dg.qzeros),
+                                  (p.du.qweight, p.du.scales, p.du.qzeros), p.group, out)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+# (M, K, N, g, sym): ragged M and N; few tiles (K slices, 2N-wide partials) and many (LDS hand-over)
+PREFILL_SHAPES = [(17, 512, 200, 128, True), (130, 2048, 264, 64, False), (300, 1024, 1032, 128, True),
+                  (640, 512, 5120, 64, False)]
+
+
+@pytest.mark.parametrize("M,K,N,g,sym", PREFILL_SHAPES)
+def test_gate_up_prefill_parity(gu, M, K, N, g, sym):
+    gate = synth.make_random(100 + M, M, K, N, g, symmetric=sym)
+    up = synth.make_random(101 + M, M, K, N, g, symmetric=sym)
+    up = synth.Inputs(up.qweight, up.scales, up.qzeros, gate.act, g)
+    p = Pair(gu, gate, up)
+    gu.say(f"[gate_up prefill] M={M} K={K} N={N} g={g} sym={sym}")
+    h = run_prefill_pair(gu, p, M)
+    h_ref, yg, bg, yu, bu = p.ref(M)
+    frac = parity.check_gate_up(h, h_ref, yg, bg, yu, bu, f"prefill pair M={M} K={K} N={N}")
+    gu.say(f"  worst err/tol {frac:.3e}")
+    hb = run_prefill_pair(gu, p, M, torch.bfloat16)
+    assert np.array_equal(hb, torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).double().numpy())
+    assert np.array_equal(run_prefill_pair(gu, p, M), h)   # deterministic
+
+
+def test_gate_up_prefill_ffn_workload(gu):
+    """The 5120 x 17408 FFN pair with 512 prompt rows, sampled columns."""
+    up = synth.make_inputs("ffn_up")
+    gate = synth.make_gate_inputs("ffn_up")
+    wl = synth.WORKLOADS["ffn_up"]
+    M = 512
+    rng = np.random.Generator(np.random.PCG64(1000 * wl.index + 9))
+    act = synth.draw_activations(rng, M, wl.K, wl.act_sigma, wl.outlier_frac, wl.outlier_mul)
+    gate = synth.Inputs(gate.qweight, gate.scales, gate.qzeros, act, gate.group)
+    up = synth.Inputs(up.qweight, up.scales, up.qzeros, act, up.group)
+    p = Pair(gu, gate, up)
+    gu.say(f"[gate_up prefill ffn] M={M}")
+    h = run_prefill_pair(gu, p, M)
+    cols = np.unique(np.concatenate([rng.choice(up.N, 400, replace=False), np.arange(up.N - 130, up.N)]))
+    h_ref, yg, bg, yu, bu = p.ref(M, cols)
+    frac = parity.check_gate_up(h[:, cols], h_ref, yg, bg, yu, bu, "ffn prefill pair")
+    gu.say(f"  worst err/tol {frac:.3e}")

@@ -167,3 +167,10 @@ def test_prefill_rejects_bad_arguments(lib):
     assert pre(M=0) == -1 and pre(M=65537) == -1 and pre(N=260) == -1 and pre(g=48) == -1
     assert pre(q=None) == -1 and pre(a=A + 2) == -2 and pre(dt=3) == -1
     assert pre(M=65537) == -1 and b"M=65537" in lib.w4a16_last_error()
+
+
+def test_gate_up_prefill_rejects_bad_arguments(lib):
+    def pre(q2=Q2, z=None, z2=None, M=300, N=256):
+        return lib.w4a16_gemm_gate_up_prefill(A, Q, S, z, q2, S2, z2, 128, M, N, 512, O, 0, None)
+    assert pre(q2=None) == -1 and pre(z=Z) == -1 and pre(z2=Z2) == -1
+    assert pre(M=65537) == -1 and pre(N=260) == -1 and pre(q2=Q2 + 4) == -2

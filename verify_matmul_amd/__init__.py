@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax",
-    "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_plan",
+    "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "EXPORTS",
 ]
@@ -26,7 +26,7 @@ _lib = None
 # every symbol the header declares
 EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
-    "w4a16_gemm_gate_up_ex", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
 
@@ -55,6 +55,7 @@ def load():
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
     lib.w4a16_gemm_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_gate_up.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_gate_up_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_gate_up_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
     lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
@@ -67,7 +68,7 @@ def load():
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
     for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
-              "w4a16_gemm_gate_up_ex",
+              "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill",
               "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
         getattr(lib, f).restype = ctypes.c_int
@@ -165,6 +166,15 @@ def w4a16_gemm_gate_up(A, gate, up, group_size, out, splits=0, waves_k=0, stream
     _check(load().w4a16_gemm_gate_up_ex(ga[0], ga[1], ga[2], ga[3], ua[1], ua[2], ua[3], *ga[4:],
                                         int(splits), int(waves_k), _stream(stream)),
            "w4a16_gemm_gate_up")
+    return out
+
+
+def w4a16_gemm_gate_up_prefill(A, gate, up, group_size, out, stream=None):
+    """silu(A x W_gate) * (A x W_up) for many rows (prompt processing) on the matrix cores."""
+    ga = _gemm_args(A, gate[0], gate[1], gate[2], group_size, out)
+    ua = _gemm_args(A, up[0], up[1], up[2], group_size, out)
+    _check(load().w4a16_gemm_gate_up_prefill(ga[0], ga[1], ga[2], ga[3], ua[1], ua[2], ua[3], *ga[4:],
+                                             _stream(stream)), "w4a16_gemm_gate_up_prefill")
     return out
 
 

@@ -296,6 +296,69 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     return W4A16_OK;
 }
 
+// A many-row call (prompt processing): check, choose the K slices, take scratch, prepare the
+// activations, launch. `up` non-null makes it a gated pair (w is the gate).
+int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
+                 int out_dtype, hipStream_t stream)
+{
+    int rc = check_gemm_args(A, w.qweight, w.scales, w.qzeros, group_size, M, N, K, out, out_dtype, W4A16_PREFILL_MAX_M);
+    if (rc != W4A16_OK) return rc;
+    if (up) {
+        rc = check_gemm_args(A, up->qweight, up->scales, up->qzeros, group_size, M, N, K, out, out_dtype,
+                             W4A16_PREFILL_MAX_M);
+        if (rc != W4A16_OK) return rc;
+        if ((w.qzeros == nullptr) != (up->qzeros == nullptr))
+            return fail(W4A16_ERR_INVALID_ARG, "qzeros_gate and qzeros_up must both be NULL or both be given");
+    }
+    const int out_cols = up ? kPrefillTileN / 2 : kPrefillTileN;   // output columns per tile
+    // K slices when the tiles cannot fill the compute units: about two 4-wave workgroups per CU
+    // run at once (`slots`), so fewer tiles than that are cut into S = slots / tiles whole-group
+    // K ranges (at most 16) whose fp32 sums are added in slice order. Measured on MI355X: FFN
+    // down 17408 x 5120 at M = 512, 160 tiles, 371 -> 207 us with 3 slices; at M = 128 12 slices
+    // 80 us. From one full round of tiles on, the slices' extra fp32 traffic costs more than
+    // the idle tail (attention 5120 x 5120 at M = 2048: 177 us whole, 213 us in 4 slices).
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    const long long tiles = (long long)((M + kPrefillTileM - 1) / kPrefillTileM) * ((N + out_cols - 1) / out_cols);
+    const long long slots = 2LL * std::max(cus, 1);
+    const int splits = tiles >= slots ? 1 : (int)std::min<long long>({16LL, (long long)(K / group_size), slots / tiles});
+    // scratch: the prepared activations (fp16, [M, K]), one rescale per row, the K slices
+    const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
+    const size_t part_bytes = splits > 1 ? (size_t)splits * M * N * (up ? 2 : 1) * sizeof(float) : 0;
+    ScratchView v{};
+    rc = get_scratch(stream, 0, part_bytes, a16_bytes + (size_t)M * sizeof(int), false, &v);
+    if (rc != W4A16_OK) return rc;
+    uint16_t *a16 = static_cast<uint16_t *>(v.act);
+    int *shifts = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
+    e = launch_act_prep(ActPrepArgs{static_cast<const uint16_t *>(A), a16, shifts, M, K, 1, 1}, stream);
+    if (e != hipSuccess) return hip_fail(e, "activation preparation launch");
+    PrefillArgs pa{};
+    pa.A16 = a16;
+    pa.shifts = shifts;
+    pa.qweight = w.qweight;
+    pa.scales = w.scales;
+    pa.qzeros = w.qzeros;
+    if (up) {
+        pa.qweight2 = up->qweight;
+        pa.scales2 = up->scales;
+        pa.qzeros2 = up->qzeros;
+    }
+    pa.out = out;
+    pa.partials = reinterpret_cast<float *>(v.partials);
+    pa.M = M;
+    pa.N = N;
+    pa.K = K;
+    pa.g = group_size;
+    pa.out_bf16 = out_dtype == W4A16_OUT_BF16;
+    pa.splits = splits;
+    e = launch_prefill(pa, stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
+    return W4A16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,37 +383,17 @@ int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *sc
 int w4a16_gemm_prefill(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                        int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
 {
-    int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, W4A16_PREFILL_MAX_M);
-    if (rc != W4A16_OK) return rc;
-    // K slices when the tiles cannot fill the compute units: about two 4-wave workgroups per CU
-    // run at once (`slots`), so fewer tiles than that are cut into S = slots / tiles whole-group
-    // K ranges (at most 16) whose fp32 sums are added in slice order. Measured on MI355X: FFN
-    // down 17408 x 5120 at M = 512, 160 tiles, 371 -> 207 us with 3 slices; at M = 128 12 slices
-    // 80 us. From one full round of tiles on, the slices' extra fp32 traffic costs more than
-    // the idle tail (attention 5120 x 5120 at M = 2048: 177 us whole, 213 us in 4 slices).
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    const long long tiles = (long long)((M + kPrefillTileM - 1) / kPrefillTileM) * ((N + kPrefillTileN - 1) / kPrefillTileN);
-    const long long slots = 2LL * std::max(cus, 1);
-    const int splits = tiles >= slots ? 1 : (int)std::min<long long>({16LL, (long long)(K / group_size), slots / tiles});
-    // scratch: the prepared activations (fp16, [M, K]), one rescale per row, the K slices
-    const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
-    const size_t part_bytes = splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
-    ScratchView v{};
-    rc = get_scratch(stream, 0, part_bytes, a16_bytes + (size_t)M * sizeof(int), false, &v);
-    if (rc != W4A16_OK) return rc;
-    uint16_t *a16 = static_cast<uint16_t *>(v.act);
-    int *shifts = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
-    e = launch_act_prep(ActPrepArgs{static_cast<const uint16_t *>(A), a16, shifts, M, K, 1, 1}, stream);
-    if (e != hipSuccess) return hip_fail(e, "activation preparation launch");
-    PrefillArgs pa{a16,    shifts, qweight, scales, qzeros, out, reinterpret_cast<float *>(v.partials),
-                   M,      N,      K,       group_size,     out_dtype == W4A16_OUT_BF16, splits};
-    e = launch_prefill(pa, stream);
-    if (e != hipSuccess) return hip_fail(e, "prefill GEMM launch");
-    return W4A16_OK;
+    return prefill_call(A, Matrix{qweight, scales, qzeros}, nullptr, group_size, M, N, K, out, out_dtype, stream);
+}
+
+int w4a16_gemm_gate_up_prefill(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,
+                               const uint32_t *qzeros_gate, const uint32_t *qweight_up, const uint16_t *scales_up,
+                               const uint32_t *qzeros_up, int group_size, int M, int N, int K, void *out,
+                               int out_dtype, hipStream_t stream)
+{
+    const Matrix up{qweight_up, scales_up, qzeros_up};
+    return prefill_call(A, Matrix{qweight_gate, scales_gate, qzeros_gate}, &up, group_size, M, N, K, out, out_dtype,
+                        stream);
 }
 
 int w4a16_gemm_gate_up_ex(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,

@@ -134,8 +134,13 @@ struct PrefillArgs {
     const uint32_t *qweight;
     const uint16_t *scales;
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
+    // gated pair: the up projection (same shape as qweight, the gate); out = silu(gate) * up.
+    // qweight2 == nullptr: a single matrix.
+    const uint32_t *qweight2;
+    const uint16_t *scales2;
+    const uint32_t *qzeros2;
     void *out;
-    float *partials;          // [splits, M, N] fp32 slices when splits > 1 (else unused)
+    float *partials;          // [splits, M, N] fp32 slices when splits > 1 ([splits, M, 2N] for a pair)
     int M, N, K, g;
     int out_bf16;
     int splits;               // workgroups per tile along K, each a contiguous range of groups

@@ -39,16 +39,22 @@ constexpr int kStS = kPrefillTileN * 2;
 constexpr int kStZ = kPrefillTileN / 8 * 4;
 constexpr int kStBytes = kStA + kStB + kStS + kStZ;
 
-template <bool kSym>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w4a16_prefill_kernel(PrefillArgs p)
+// kDual: a gated pair (gate in qweight, up in qweight2). The tile's 256 columns are then 128
+// output columns of the gate followed by the same 128 of the up projection: waves 0 and 1
+// compute the gate, waves 2 and 3 the up projection, and the up waves hand their sums to the
+// gate waves through LDS, which write silu(gate) * up. Everything up to the epilogue is the
+// single-matrix kernel over those 256 columns.
+template <bool kSym, bool kDual>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w4a16_prefill_kernel(PrefillArgs p)
 {
+    constexpr int kOutCols = kDual ? kPrefillTileN / 2 : kPrefillTileN;   // output columns per tile
     __shared__ __align__(16) unsigned char lds[kStages * kStBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cl = lane & 15;   // A row / B column of the lane within a 16 x 16 block
     const int rl = lane >> 4;   // word row (8 K rows) of the lane within a 32-row step
-    const int wn = wave;   // the wave's 64 columns
+    const int wn = wave;   // the wave's 64 columns of the tile
     const int M = p.M;
     const int N = p.N;
     const int K = p.K;
@@ -56,7 +62,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     // matter of speed only; any mapping is correct).
     // Work units are (tile, K slice) pairs, the slices of a tile adjacent.
     const int row_tiles = (M + kPrefillTileM - 1) / kPrefillTileM;
-    const int col_tiles = (N + kPrefillTileN - 1) / kPrefillTileN;
+    const int col_tiles = (N + kOutCols - 1) / kOutCols;
     const int units = row_tiles * col_tiles * p.splits;
     const int per_die = (units + kXcds - 1) / kXcds;
     const int unit = (int)(blockIdx.x % kXcds) * per_die + (int)(blockIdx.x / kXcds);
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const int g_rows = min(kRowGroup, row_tiles - grp * kRowGroup);
     const int idx = tile - grp * kRowGroup * col_tiles;
     const int tm = (grp * kRowGroup + idx % g_rows) * kPrefillTileM;   // the tile's first row
-    const int tn = (idx / g_rows) * kPrefillTileN;                     // the tile's first column
+    const int tn = (idx / g_rows) * kOutCols;                          // the tile's first column
     const int spg = p.g / kStepK;
     // the slice's K range: whole quantisation groups [gb, ge), so every group is scaled once
     const int groups = K / p.g;
@@ -89,11 +95,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         a_src = p.A16 + (size_t)min(tm + row, M - 1) * K + chunk * 8;   // rows past M: the last row
     }
     auto col = [&](int c) { return c < N ? c : 0; };   // columns past N read column 0, never stored
+    // Column c of the tile (0..255) is output column tn + c of the single matrix, or for a pair
+    // output column tn + c % 128 of the gate (c < 128) or of the up projection.
+    auto in_up = [&](int c) { return kDual && c >= kOutCols; };
+    auto out_col = [&](int c) { return col(tn + (kDual ? c % kOutCols : c)); };
     // packed weights: wave w loads word row w of the step, four columns per lane
-    const uint32_t *w_src = p.qweight + (size_t)wave * N + col(tn + lane * 4);
+    const uint32_t *w_src = (in_up(lane * 4) ? p.qweight2 : p.qweight) + (size_t)wave * N + out_col(lane * 4);
     // scales: wave w loads columns [64 w, 64 w + 64) as 32 pairs; zero words: wave w loads 8
-    const uint16_t *s_src = p.scales + col(tn + wave * 64 + (lane & 31) * 2);
-    const uint32_t *z_src = kSym ? nullptr : p.qzeros + col(tn + (wave * 8 + (lane & 7)) * 8) / 8;
+    const int sc_c = wave * 64 + (lane & 31) * 2;
+    const uint16_t *s_src = (in_up(sc_c) ? p.scales2 : p.scales) + out_col(sc_c);
+    const int zc_c = (wave * 8 + (lane & 7)) * 8;
+    const uint32_t *z_src = kSym ? nullptr : (in_up(zc_c) ? p.qzeros2 : p.qzeros) + out_col(zc_c) / 8;
     int lt = s0, lg = gb, lpos = 0;   // next step to stage, its group and position in the group
     auto issue = [&](int buf) {
         unsigned char *st = lds + buf * kStBytes;
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     };
 
     // ---- compute ------------------------------------------------------------------------------
-    const int n0 = tn + wn * 64 + cl * 4;   // the lane's 4 columns
+    const int n0 = tn + (kDual ? wn & 1 : wn) * 64 + cl * 4;   // the lane's 4 output columns
     const Masks mk = make_masks();
     float4_t acc[4][4];
     float4_t tot[4][4];
@@ -186,10 +198,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last stages' reloads land before the wave ends
 
     // Lane holds rows 4 rl + r of each row block, its 4 columns: undo the row's rescale, store
-    // (or store the slice's fp32 sums for the slice reduction).
-    if (n0 >= N) return;
-    if (p.splits > 1) {
-        float *part = p.partials + (size_t)slice * M * N;
+    // (or store the slice's fp32 sums for the slice reduction, 2N wide for a pair).
+    if (kDual && p.splits == 1) {   // up sums to LDS (over the dead ring), then silu(gate) * up
+        __syncthreads();
+        float *upl = reinterpret_cast<float *>(lds);   // [64 rows][128 columns]
+        if (wave >= 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = tm + 16 * i + 4 * rl + r;
+                    const int sh = p.shifts[min(m, M - 1)];
+                    *reinterpret_cast<float4 *>(upl + (16 * i + 4 * rl + r) * kOutCols + (wn & 1) * 64 + cl * 4) =
+                        make_float4(__builtin_amdgcn_ldexpf(tot[i][0][r], sh), __builtin_amdgcn_ldexpf(tot[i][1][r], sh),
+                                    __builtin_amdgcn_ldexpf(tot[i][2][r], sh), __builtin_amdgcn_ldexpf(tot[i][3][r], sh));
+                }
+        }
+        __syncthreads();
+        if (wave >= 2 || n0 >= N) return;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -197,7 +223,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
                 const int m = tm + 16 * i + 4 * rl + r;
                 if (m >= M) continue;
                 const int sh = p.shifts[m];
-                *reinterpret_cast<float4 *>(part + (size_t)m * N + n0) =
+                const float4 u = *reinterpret_cast<const float4 *>(upl + (16 * i + 4 * rl + r) * kOutCols + wn * 64 + cl * 4);
+                const float x0 = silu_f32(__builtin_amdgcn_ldexpf(tot[i][0][r], sh)) * u.x;
+                const float x1 = silu_f32(__builtin_amdgcn_ldexpf(tot[i][1][r], sh)) * u.y;
+                const float x2 = silu_f32(__builtin_amdgcn_ldexpf(tot[i][2][r], sh)) * u.z;
+                const float x3 = silu_f32(__builtin_amdgcn_ldexpf(tot[i][3][r], sh)) * u.w;
+                const size_t o = (size_t)m * N + n0;
+                if (p.out_bf16) {
+                    uint2 q;
+                    q.x = float_to_bf16_bits(x0) | (float_to_bf16_bits(x1) << 16);
+                    q.y = float_to_bf16_bits(x2) | (float_to_bf16_bits(x3) << 16);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o) = q;
+                } else {
+                    *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o) = make_float4(x0, x1, x2, x3);
+                }
+            }
+        return;
+    }
+    if (n0 >= N) return;
+    if (p.splits > 1) {
+        const size_t NV = kDual ? 2 * (size_t)N : (size_t)N;   // partial row: [gate | up] for a pair
+        float *part = p.partials + (size_t)slice * M * NV + (kDual && wave >= 2 ? N : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = tm + 16 * i + 4 * rl + r;
+                if (m >= M) continue;
+                const int sh = p.shifts[m];
+                *reinterpret_cast<float4 *>(part + (size_t)m * NV + n0) =
                     make_float4(__builtin_amdgcn_ldexpf(tot[i][0][r], sh), __builtin_amdgcn_ldexpf(tot[i][1][r], sh),
                                 __builtin_amdgcn_ldexpf(tot[i][2][r], sh), __builtin_amdgcn_ldexpf(tot[i][3][r], sh));
             }
@@ -224,19 +278,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         }
 }
 
-// out = the sum of the K slices in slice order (deterministic), 4 outputs per thread.
+// out = the sum of the K slices in slice order (deterministic), 4 outputs per thread; for a
+// gated pair silu(gate sum) * up sum, the slices' rows being [gate | up].
+template <bool kDual>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs p)
 {
-    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;   // float4 index of the output
     const size_t mn = (size_t)p.M * p.N;
     if (q * 4 >= mn) return;
-    float4 v = reinterpret_cast<const float4 *>(p.partials)[q];
-    for (int s = 1; s < p.splits; ++s) {
-        const float4 w = reinterpret_cast<const float4 *>(p.partials + (size_t)s * mn)[q];
-        v.x += w.x;
-        v.y += w.y;
-        v.z += w.z;
-        v.w += w.w;
+    auto slice_sum = [&](size_t at) {   // float index at of a slice, summed over the slices
+        const size_t stride = kDual ? 2 * mn : mn;
+        float4 v = *reinterpret_cast<const float4 *>(p.partials + at);
+        for (int s = 1; s < p.splits; ++s) {
+            const float4 w = *reinterpret_cast<const float4 *>(p.partials + (size_t)s * stride + at);
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        return v;
+    };
+    float4 v;
+    if constexpr (kDual) {
+        const size_t m = q * 4 / p.N, n = q * 4 - m * p.N;
+        const float4 gs = slice_sum(m * 2 * p.N + n), us = slice_sum(m * 2 * p.N + p.N + n);
+        v = make_float4(silu_f32(gs.x) * us.x, silu_f32(gs.y) * us.y, silu_f32(gs.z) * us.z, silu_f32(gs.w) * us.w);
+    } else {
+        v = slice_sum(q * 4);
     }
     if (p.out_bf16) {
         uint2 o;
@@ -252,16 +320,19 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs p)
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
-    const int units = ((a.M + kPrefillTileM - 1) / kPrefillTileM) * ((a.N + kPrefillTileN - 1) / kPrefillTileN) * a.splits;
+    const bool dual = a.qweight2 != nullptr;
+    const int out_cols = dual ? kPrefillTileN / 2 : kPrefillTileN;
+    const int units = ((a.M + kPrefillTileM - 1) / kPrefillTileM) * ((a.N + out_cols - 1) / out_cols) * a.splits;
     const dim3 grid((unsigned)((units + kXcds - 1) / kXcds * kXcds));   // whole rounds of the 8 dies
-    if (a.qzeros == nullptr)
-        hipLaunchKernelGGL(w4a16_prefill_kernel<true>, grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(w4a16_prefill_kernel<false>, grid, dim3(256), 0, stream, a);
+    const bool sym = a.qzeros == nullptr;
+    void (*kern)(PrefillArgs) = dual ? (sym ? w4a16_prefill_kernel<true, true> : w4a16_prefill_kernel<false, true>)
+                                     : (sym ? w4a16_prefill_kernel<true, false> : w4a16_prefill_kernel<false, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     const size_t quads = (size_t)a.M * a.N / 4;   // N % 8 == 0
-    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, a);
+    void (*reduce)(PrefillArgs) = dual ? prefill_reduce_kernel<true> : prefill_reduce_kernel<false>;
+    hipLaunchKernelGGL(reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
