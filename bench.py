@@ -26,6 +26,9 @@ workload's matrix with M = 512 and 2048 rows by default (activations drawn with 
 distribution): the bound is the fp16 matrix cores (2.5 PFLOP/s dense), and the line reports
 TFLOP/s (2*M*N*K per call) with an "mfma" roofline.
 
+--prefill --gate-up times the prompt-sized gated pair (w4a16_gemm_gate_up_prefill), 4*M*N*K
+flops per call.
+
 With --gate-up every call is instead the fused gated pair on the workload's shape,
 silu(A x W_gate) * (A x W_up) (w4a16_gemm_gate_up): two weight matrices per call, one [M, N]
 output, and the algorithmic bytes count both matrices.
@@ -351,9 +354,11 @@ def run_prefill(args, lib):
     from verify_matmul_amd import synth
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.argmax or args.gate_up or args.splits or args.waves_k or args.tile_cols:
+    if wl.argmax or args.splits or args.waves_k or args.tile_cols:
         print("bench.py: --prefill takes an FFN or attention workload and no launch knobs", file=sys.stderr)
         return 2
+    pair = args.gate_up   # the gated pair silu(A x W_gate) * (A x W_up): 4 M N K flops per call
+    nmat = 2 if pair else 1
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else (512, 2048)
     inp = synth.make_inputs(wl)
     K, N, g = wl.K, wl.N, wl.group
@@ -368,12 +373,22 @@ def run_prefill(args, lib):
     sc = torch.from_numpy(inp.scales.view(np.int16)).to(dev)
     qz = None if inp.qzeros is None else torch.from_numpy(inp.qzeros.view(np.int32)).to(dev)
     pool = [qw0.clone() for _ in range(R)]
+    if pair:
+        gate_inp = synth.make_gate_inputs(wl)
+        gw0 = torch.from_numpy(gate_inp.qweight.view(np.int32)).to(dev)
+        gpool = [gw0.clone() for _ in range(R)]
+        gs = torch.from_numpy(gate_inp.scales.view(np.int16)).to(dev)
+        gz = None if gate_inp.qzeros is None else torch.from_numpy(gate_inp.qzeros.view(np.int32)).to(dev)
     a = torch.from_numpy(act.view(np.int16)).to(dev)
     outs = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}
     stream = torch.cuda.current_stream()
 
     def call(i, M):
-        vm.w4a16_gemm_prefill(a[:M], pool[i % R], sc, qz, g, outs[M], stream=stream)
+        if pair:
+            vm.w4a16_gemm_gate_up_prefill(a[:M], (gpool[i % R], gs, gz), (pool[i % R], sc, qz), g, outs[M],
+                                          stream=stream)
+        else:
+            vm.w4a16_gemm_prefill(a[:M], pool[i % R], sc, qz, g, outs[M], stream=stream)
 
     def step(i, evs=None):
         for j, M in enumerate(ms):
@@ -391,7 +406,7 @@ def run_prefill(args, lib):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    flops = sum(2.0 * M * N * K for M in ms)
+    flops = sum(2.0 * nmat * M * N * K for M in ms)
     value = flops * args.steps / wall / 1e12
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
            for _ in range(args.steps)]
@@ -403,11 +418,11 @@ def run_prefill(args, lib):
     for j, M in enumerate(ms):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
         us = float(np.mean(d))
-        f = 2.0 * M * N * K
+        f = 2.0 * nmat * M * N * K
         per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "TFLOPs": round(f / us / 1e6, 1),
                          "frac_of_peak": round(f / us / 1e6 / PEAK_F16_TFLOPS, 4), "flops": f,
-                         "hbm_GBps_weights_once": round(algorithmic_bytes(M, K, N, g, wl.symmetric) / us / 1e3, 1)}
+                         "hbm_GBps_weights_once": round(algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat) / us / 1e3, 1)}
         if float(np.sum(d)) > dom_time:
             dom, dom_time = M, float(np.sum(d))
     # the dominant call alone, back to back between one event pair on its stream
@@ -419,7 +434,7 @@ def run_prefill(args, lib):
     e1.record(stream)
     torch.cuda.synchronize()
     us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
-    f_dom = 2.0 * dom * N * K
+    f_dom = 2.0 * nmat * dom * N * K
     rec = {
         "metric": "W4A16 prefill GEMM TFLOP/s (% of fp16 matrix-core peak), us/call",
         "value": round(value, 1),
@@ -433,13 +448,14 @@ def run_prefill(args, lib):
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}, prompt rows M in {','.join(map(str, ms))} (one call each per step)",
+        "config": {"workload": (f"{wl.name} gated pair silu(A x W_gate) * (A x W_up)" if pair else wl.name) +
+                               f", prompt rows M in {','.join(map(str, ms))} (one call each per step)",
                    "K": K, "N": N, "group": g, "symmetric_zero": wl.symmetric, "ms": list(ms), "out": "fp32",
                    "rotation_copies": R},
-        "roofline": {"bound": "mfma", "kernel": f"w4a16_prefill_kernel (M={dom})", "M": dom,
+        "roofline": {"bound": "mfma", "kernel": f"w4a16_prefill_kernel ({'gated pair, ' if pair else ''}M={dom})", "M": dom,
                      "achieved": round(f_dom / us_dom / 1e6, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(f_dom / us_dom / 1e6 / PEAK_F16_TFLOPS, 4),
-                     "traffic": load_traffic(args.workload, dom, "w4a16_prefill_kernel"),
+                     "traffic": None if pair else load_traffic(args.workload, dom, "w4a16_prefill_kernel"),
                      "launches": args.steps, "flops_per_launch": f_dom, "us_per_launch": round(us_dom, 3),
                      "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
         "per_m": per_m,
@@ -453,10 +469,14 @@ def run_prefill(args, lib):
         reps, elapsed = 0, 0.0
         while elapsed < args.cpu_seconds or reps == 0:
             t = time.perf_counter()
-            oracle.gemm(act[:M], inp.qweight, inp.scales, inp.qzeros, g, cols, with_bound=False)
+            if pair:
+                oracle.gate_up(act[:M], (gate_inp.qweight, gate_inp.scales, gate_inp.qzeros),
+                               (inp.qweight, inp.scales, inp.qzeros), g, cols)
+            else:
+                oracle.gemm(act[:M], inp.qweight, inp.scales, inp.qzeros, g, cols, with_bound=False)
             elapsed += time.perf_counter() - t
             reps += 1
-        rec["cpu_baseline"] = {"value": round(2.0 * M * len(cols) * K * reps / elapsed / 1e12, 6), "unit": "TFLOP/s",
+        rec["cpu_baseline"] = {"value": round(2.0 * nmat * M * len(cols) * K * reps / elapsed / 1e12, 6), "unit": "TFLOP/s",
                                "cores": threads, "kind": "oracle",
                                "sample": f"{reps} call(s) of M={M} rows on {len(cols)} of the {N} columns, "
                                          f"{elapsed:.1f} s of oracle time"}
