@@ -276,8 +276,8 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     auto load_w = [&](uint4 *dst, int t) {
 #pragma unroll
         for (int v = 0; v < kV; ++v)   // word offsets fit 32 bits (checked on the host)
-            dst[v] = kDual ? *reinterpret_cast<const uint4 *>((v ? qw2_lane : qw_lane) + (uint32_t)(t * 4 * N))
-                           : *reinterpret_cast<const uint4 *>(qw_lane + (uint32_t)(t * 4 * N) + 4 * v);
+            dst[v] = kDual ? *reinterpret_cast<const uint4 *>((v ? qw2_lane : qw_lane) + (uint32_t)t * 4u * (uint32_t)N)
+                           : *reinterpret_cast<const uint4 *>(qw_lane + (uint32_t)t * 4u * (uint32_t)N + 4 * v);
     };
 #pragma unroll
     for (int u = 0; u < kPf; ++u) {

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w
     auto issue = [&](int buf) {
         unsigned char *st = lds + buf * kStBytes;
         load_to_lds16(a_src + (size_t)lt * kStepK, st + wave * 64 * 16);
-        load_to_lds16(w_src + (uint32_t)(lt * 4 * N), st + kStA + wave * 1024);   // < 2^32 words
+        load_to_lds16(w_src + (uint32_t)lt * 4u * (uint32_t)N, st + kStA + wave * 1024);   // < 2^32 words
         if (lane < 32) load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
         if (!kSym && lane < 8) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 32);
         if (lt + 1 < s0 + steps) {   // past the slice's last step the stage reloads it (uniform)
