@@ -5,7 +5,8 @@ and the CPU-baseline leg of ``bench.py`` may import this package. The HIP librar
 imports, links or calls it, and it shares no code with the HIP library.
 
 The arithmetic lives in ``w4a16_oracle.c`` (plain C, fp32 exact dequantisation, fp64
-accumulation); this module only builds that file with gcc and marshals numpy arrays.
+accumulation; the affine form w = s * q + b of MLX checkpoints in fp64); this module only
+builds that file with gcc and marshals numpy arrays.
 """
 from __future__ import annotations
 
@@ -52,8 +53,11 @@ def _load():
         lib.w4o_silu.argtypes = [ctypes.c_double]
         lib.w4o_silu.restype = ctypes.c_double
         lib.w4o_silu_mul.argtypes = [P, P, I64, P]
+        lib.w4o_affine_unpack.argtypes = [P, ctypes.c_int, I64, I64, P]
+        lib.w4o_affine_gemm.argtypes = [P, P, ctypes.c_int, P, P, I64, I64, I64, I64, P, I64, P, P]
         for f in (lib.w4o_unpack_qweight, lib.w4o_unpack_qzeros, lib.w4o_dequant,
-                  lib.w4o_gemm, lib.w4o_argmax_rows_f32, lib.w4o_silu_mul):
+                  lib.w4o_gemm, lib.w4o_argmax_rows_f32, lib.w4o_silu_mul,
+                  lib.w4o_affine_unpack, lib.w4o_affine_gemm):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -164,3 +168,35 @@ def gate_up(act, gate, up, group: int, cols: Optional[Sequence[int]] = None):
     yg, bg = gemm(act, gate[0], gate[1], gate[2], group, cols)
     yu, bu = gemm(act, up[0], up[1], up[2], group, cols)
     return silu_mul(yg, yu), yg, bg, yu, bu
+
+
+def affine_unpack(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Codes [K, N] (uint8) of ``bits`` bits each from the column bit streams [K*bits/32, N]."""
+    pk = _c(packed, np.uint32)
+    N = pk.shape[1]
+    assert pk.shape[0] * 32 == K * bits
+    q = np.empty((K, N), dtype=np.uint8)
+    _check(_load().w4o_affine_unpack(_ptr(pk), bits, K, N, _ptr(q)), "affine_unpack")
+    return q
+
+
+def affine_gemm(act, packed, bits: int, scales, biases, group: int,
+                cols: Optional[Sequence[int]] = None):
+    """y and bound (fp64 [M, C]) of A x W with W = s * q + b, codes of ``bits`` bits.
+
+    ``act``, ``scales`` and ``biases`` are bf16 bits (uint16); the bound is
+    sum |a| * (|s * q| + |b|)."""
+    a = _c(act, np.uint16)
+    pk = _c(packed, np.uint32)
+    sc = _c(scales, np.uint16)
+    bi = _c(biases, np.uint16)
+    M, K = a.shape
+    N = pk.shape[1]
+    assert pk.shape[0] * 32 == K * bits and sc.shape == bi.shape == (K // group, N)
+    cc = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    C = N if cc is None else cc.shape[0]
+    y = np.empty((M, C), dtype=np.float64)
+    b = np.empty((M, C), dtype=np.float64)
+    _check(_load().w4o_affine_gemm(_ptr(a), _ptr(pk), bits, _ptr(sc), _ptr(bi), group, M, N, K,
+                                   _ptr(cc), C, _ptr(y), _ptr(b)), "affine_gemm")
+    return y, b

@@ -14,6 +14,8 @@
  *   y[m][n]  = sum over k ascending of (double)A[m][k] * (double)w[k][n]
  *   bound[m][n] = sum over k of |(double)A[m][k] * (double)w[k][n]|
  * with gi = k / g.
+ * The affine form w = s * q + b of MLX checkpoints (codes of 1 to 8 bits, bf16 scales and
+ * biases) has its own unpacking and matmul at the end of the file.
  *
  * Sources. The dequantisation is the exact (q - z) * scale form that the GRIMOIRE v1.7
  * release notes ('What changed') keep for their int4 single-user GEMV, with int4 weights and
@@ -211,5 +213,96 @@ int w4o_silu_mul(const double *g, const double *u, int64_t n, double *h)
         return -1;
     for (int64_t i = 0; i < n; ++i)
         h[i] = w4o_silu(g[i]) * u[i];
+    return 0;
+}
+
+/* ---- affine codes: w = s * q + b (MLX affine quantisation) ------------------------------ */
+
+/*
+ * The format of the MLX checkpoints in TensorFold PR #859 (commit messages: the affine-4
+ * checkpoint, mixed-width checkpoints of 2 to 8 bits in groups of 64): every code q of `bits`
+ * bits keeps its own value, and the weight is w = s * q + b with a scale s and a bias b per
+ * group of rows and column, both bf16.
+ *
+ * Storage read here: for column n, the codes of rows k = 0, 1, 2, ... form one little-endian
+ * bit stream, row k at stream bits [k*bits, (k+1)*bits); stream bit i is bit i % 32 of word
+ * [i / 32][n] of an array [K*bits/32, N]. At bits = 4 this is the GPTQ nibble layout above.
+ */
+static inline int affine_code_of(const uint32_t *packed, int bits, int64_t N, int64_t k, int64_t n)
+{
+    int code = 0;
+    for (int b = 0; b < bits; ++b) {           /* one stream bit at a time */
+        int64_t i = k * bits + b;
+        uint32_t word = packed[(i / 32) * N + n];
+        code |= (int)((word >> (i % 32)) & 1u) << b;
+    }
+    return code;
+}
+
+static int affine_shape_ok(int bits, int64_t K, int64_t N)
+{
+    return bits >= 1 && bits <= 8 && K > 0 && N > 0 && (K * bits) % 32 == 0;
+}
+
+/* q[k*N + n] = code of row k, column n. */
+int w4o_affine_unpack(const uint32_t *packed, int bits, int64_t K, int64_t N, uint8_t *q)
+{
+    if (!packed || !q || !affine_shape_ok(bits, K, N))
+        return -1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            q[k * N + n] = (uint8_t)affine_code_of(packed, bits, N, k, n);
+    return 0;
+}
+
+/*
+ * y[m*C + c] = sum over k ascending of a[m][k] * w[k][n], w = s * q + b in fp64 (exact: an
+ * 8-bit significand times an 8-bit code, plus an 8-bit significand), and
+ * bound[m*C + c] = sum over k of |a[m][k]| * (|s * q| + |b|): the sizes of the two terms a
+ * kernel that applies scale and bias to separate sums rounds. Columns as in w4o_gemm.
+ */
+int w4o_affine_gemm(const uint16_t *A, const uint32_t *packed, int bits, const uint16_t *scales,
+                    const uint16_t *biases, int64_t g, int64_t M, int64_t N, int64_t K,
+                    const int64_t *cols, int64_t C, double *y, double *bound)
+{
+    if (!A || !packed || !scales || !biases || !y || g <= 0 || M <= 0 || K % g ||
+        !affine_shape_ok(bits, K, N))
+        return -1;
+    if (!cols)
+        C = N;
+    if (C <= 0)
+        return -1;
+    for (int64_t c = 0; cols && c < C; ++c)
+        if (cols[c] < 0 || cols[c] >= N)
+            return -1;
+
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K));
+    if (!a)
+        return -2;
+    for (int64_t i = 0; i < M * K; ++i)
+        a[i] = (double)w4o_bf16_to_f32(A[i]);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; ++c) {
+        int64_t n = cols ? cols[c] : c;
+        for (int64_t m = 0; m < M; ++m) {
+            y[m * C + c] = 0.0;
+            if (bound)
+                bound[m * C + c] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t gi = k / g;
+            double s = (double)w4o_bf16_to_f32(scales[gi * N + n]);
+            double b = (double)w4o_bf16_to_f32(biases[gi * N + n]);
+            double sq = s * (double)affine_code_of(packed, bits, N, k, n);
+            double w = sq + b;
+            for (int64_t m = 0; m < M; ++m) {
+                y[m * C + c] += a[m * K + k] * w;
+                if (bound)
+                    bound[m * C + c] += fabs(a[m * K + k]) * (fabs(sq) + fabs(b));
+            }
+        }
+    }
+    free(a);
     return 0;
 }

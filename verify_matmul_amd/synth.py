@@ -186,3 +186,96 @@ def pack_cols(codes: np.ndarray) -> np.ndarray:
     for j in range(8):
         out |= c[:, :, j] << np.uint32(4 * j)
     return out
+
+
+# ---- affine codes (MLX affine quantisation: w = s * q + b) ------------------------------
+#
+# Storage format of an affine matrix with codes of `bits` bits (TensorFold PR #859, commit
+# messages: mixed-width MLX checkpoints, 2 to 8 bits in groups of 64):
+#   packed   uint32 [K*bits/32, N]  for column n the codes of rows 0, 1, 2, ... form one
+#                                   little-endian bit stream (row k at stream bits
+#                                   k*bits .. k*bits+bits-1); stream bit i is bit i % 32 of
+#                                   word [i / 32, n]. At 4 bits this is the qweight layout.
+#   scales   bf16   [K/g, N]        stored as uint16 bit patterns
+#   biases   bf16   [K/g, N]        stored as uint16 bit patterns
+
+_T_AFF_CODES, _T_AFF_SCALES, _T_AFF_BIASES, _T_AFF_ACT = 11, 12, 13, 14
+
+
+@dataclass
+class AffineInputs:
+    packed: np.ndarray   # uint32 [K*bits/32, N]
+    bits: int
+    scales: np.ndarray   # uint16 [K/g, N] (bf16 bits)
+    biases: np.ndarray   # uint16 [K/g, N] (bf16 bits)
+    act: np.ndarray      # uint16 [rows, K] (bf16 bits)
+    group: int
+
+    @property
+    def K(self) -> int:
+        return self.packed.shape[0] * 32 // self.bits
+
+    @property
+    def N(self) -> int:
+        return self.packed.shape[1]
+
+
+@dataclass(frozen=True)
+class AffineWorkload:
+    index: int
+    name: str
+    K: int
+    N: int
+    group: int
+    bits: int
+    ms: tuple
+
+
+# An MLX affine-4 checkpoint's FFN up/gate projection (groups of 64) at the 27B-class widths.
+AFFINE_WORKLOADS = {
+    "ffn_up_affine4": AffineWorkload(6, "FFN up/gate 5120x17408 affine-4 g64", 5120, 17408, 64, 4,
+                                     (1, 2, 4, 8, 16)),
+}
+
+
+def pack_stream(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Encode codes [K, N] (values < 2^bits) as column bit streams [K*bits/32, N]."""
+    c = np.asarray(codes, dtype=np.uint32)
+    K, N = c.shape
+    assert (K * bits) % 32 == 0 and c.max(initial=0) < (1 << bits)
+    stream = ((c[:, None, :] >> np.arange(bits, dtype=np.uint32)[None, :, None]) & 1)   # [K, bits, N]
+    stream = stream.reshape(K * bits // 32, 32, N)
+    out = np.zeros((K * bits // 32, N), dtype=np.uint32)
+    for i in range(32):
+        out |= stream[:, i, :] << np.uint32(i)
+    return out
+
+
+def draw_affine(rng_codes, rng_scales, rng_biases, K: int, N: int, group: int, bits: int):
+    """Codes uniform on 0..2^bits-1; scales uniform on [0.002, 0.02] x 15 / (2^bits - 1) (the
+    same weight spread at every width) and biases -s * (2^bits - 1) * U(0.4, 0.6) (a group's
+    minimum, as affine quantisation stores it, about half the range below zero), both rounded
+    once to bf16."""
+    top = (1 << bits) - 1
+    codes = rng_codes.integers(0, top + 1, size=(K, N), dtype=np.uint32)
+    s = rng_scales.uniform(0.002, 0.02, size=(K // group, N)) * (15.0 / top)
+    b = -s * top * rng_biases.uniform(0.4, 0.6, size=(K // group, N))
+    return pack_stream(codes, bits), f32_to_bf16_bits(s.astype(np.float32)), f32_to_bf16_bits(b.astype(np.float32))
+
+
+def make_affine_inputs(wl: AffineWorkload | str) -> AffineInputs:
+    if isinstance(wl, str):
+        wl = AFFINE_WORKLOADS[wl]
+    packed, scales, biases = draw_affine(_rng(wl.index, _T_AFF_CODES), _rng(wl.index, _T_AFF_SCALES),
+                                         _rng(wl.index, _T_AFF_BIASES), wl.K, wl.N, wl.group, wl.bits)
+    act = draw_activations(_rng(wl.index, _T_AFF_ACT), MAX_ROWS, wl.K, 1.0, 0.0, 1.0)
+    return AffineInputs(packed, wl.bits, scales, biases, act, wl.group)
+
+
+def make_affine_random(seed: int, M: int, K: int, N: int, group: int, bits: int,
+                       sigma: float = 1.0) -> AffineInputs:
+    """Free-form seeded affine inputs for parity sweeps."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    packed, scales, biases = draw_affine(rng, rng, rng, K, N, group, bits)
+    act = draw_activations(rng, M, K, sigma, 0.0, 1.0)
+    return AffineInputs(packed, bits, scales, biases, act, group)
