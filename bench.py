@@ -33,6 +33,11 @@ With --gate-up every call is instead the fused gated pair on the workload's shap
 silu(A x W_gate) * (A x W_up) (w4a16_gemm_gate_up): two weight matrices per call, one [M, N]
 output, and the algorithmic bytes count both matrices.
 
+With --affine every call is the affine-code GEMM (w4a16_gemm_affine, w = s * q + b, bf16 scales
+and biases) on the affine-4 FFN up projection 5120 x 17408 in groups of 64, M = 1, 2, 4, 8, 16.
+Algorithmic bytes per call = codes (K*N/2) + scales and biases (4*K*N/g) + activations (2*M*K)
++ outputs (4*M*N).
+
 Prints one JSON line (rank 0; this build runs on one GPU).
 """
 from __future__ import annotations
@@ -76,6 +81,8 @@ def parse():
                         "(default 512,2048)")
     p.add_argument("--gate-up", action="store_true",
                    help="time the fused gated pair silu(A x W_gate) * (A x W_up) on the workload's shape")
+    p.add_argument("--affine", action="store_true",
+                   help="time the affine-code GEMM on the affine-4 FFN up projection (w = s * q + b)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise kernel (y = 2x, fp32) over MIB MiB five times: the "
@@ -151,6 +158,8 @@ def main():
         return 0
 
     lib = vm.load()
+    if args.affine:
+        return run_affine(args, lib)
     if args.prefill:
         return run_prefill(args, lib)
     wl = synth.WORKLOADS[args.workload]
@@ -342,6 +351,125 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def affine_bytes(M, K, N, g):
+    return K * N // 2 + 4 * (K // g) * N + 2 * M * K + 4 * M * N
+
+
+def run_affine(args, lib):
+    """The affine-code GEMM at decode row counts: GB/s against HBM, as the default mode."""
+    import numpy as np
+    import torch
+    import verify_matmul_amd as vm
+    from verify_matmul_amd import synth
+
+    if args.prefill or args.gate_up or args.tile_cols:
+        print("bench.py: --affine takes no --prefill, --gate-up or --tile-cols", file=sys.stderr)
+        return 2
+    wl = synth.AFFINE_WORKLOADS["ffn_up_affine4"]
+    ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
+    x = synth.make_affine_inputs(wl)
+    K, N, g = wl.K, wl.N, wl.group
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    per_copy = affine_bytes(1, K, N, g)
+    R = max(2, math.ceil(POOL_BYTES / per_copy))
+    qw0 = torch.from_numpy(np.ascontiguousarray(x.packed).view(np.int32)).to(dev)   # 4-bit: the qweight layout
+    sc0 = torch.from_numpy(x.scales.view(np.int16)).to(dev)
+    bi0 = torch.from_numpy(x.biases.view(np.int16)).to(dev)
+    a0 = torch.from_numpy(x.act.view(np.int16)).to(dev)
+    pool = [(qw0.clone(), sc0.clone(), bi0.clone(), a0.clone(),
+             {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, args.splits, args.waves_k, 0, sp)
+              for M in ms] for qw, sc, bi, a, outs in pool]
+    fn = lib.w4a16_gemm_affine_ex
+
+    def step(i, evs=None):
+        for j, M in enumerate(ms):
+            if evs is not None:
+                evs[i][j][0].record(stream)
+            rc = fn(*calls[(i * len(ms) + j) % R][j])
+            if evs is not None:
+                evs[i][j][1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm_affine_ex failed: {lib.w4a16_last_error().decode()}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = sum(affine_bytes(M, K, N, g) for M in ms) * args.steps / wall / 1e9
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs)
+    torch.cuda.synchronize()
+    per_m, dom, dom_time = {}, None, -1.0
+    for j, M in enumerate(ms):
+        d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
+        b = affine_bytes(M, K, N, g)
+        us = float(np.mean(d))
+        per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+                         "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
+                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
+        if float(np.sum(d)) > dom_time:
+            dom, dom_time = M, float(np.sum(d))
+    jd = list(ms).index(dom)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        fn(*calls[i % R][jd])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
+    bdom = per_m[str(dom)]["bytes"]
+    achieved = bdom / us_dom / 1e3
+    rec = {
+        "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases), M in "
+                               f"{','.join(map(str, ms))} (one call each per step)",
+                   "K": K, "N": N, "group": g, "bits": wl.bits, "ms": list(ms), "out": "fp32",
+                   "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20)},
+        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine, M={dom})", "M": dom,
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": load_traffic("ffn_up_affine4", dom), "launches": args.steps,
+                     "bytes_per_launch": bdom, "us_per_launch": round(us_dom, 3),
+                     "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
+        "per_m": per_m,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        reps, elapsed, nbytes = 0, 0.0, 0
+        while elapsed < args.cpu_seconds or reps == 0:
+            for M in ms:
+                t = time.perf_counter()
+                oracle.affine_gemm(x.act[:M], x.packed, x.bits, x.scales, x.biases, g)
+                elapsed += time.perf_counter() - t
+                nbytes += affine_bytes(M, K, N, g)
+            reps += 1
+        rec["cpu_baseline"] = {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{reps} full step(s) (M={','.join(map(str, ms))}, all {N} columns), "
+                                         f"{elapsed:.1f} s of oracle time"}
     print(json.dumps(rec), flush=True)
     return 0
 

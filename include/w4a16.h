@@ -169,6 +169,41 @@ int w4a16_gemm_gate_up_prefill(const void *A, const uint32_t *qweight_gate,
                                void *out, int out_dtype, hipStream_t stream);
 
 /*
+ * Affine codes (the MLX affine format of the checkpoints in TensorFold PR #859, commit messages):
+ *
+ *   out[M, N] = A[M, K] x W[K, N],   W[k][n] = scale[k/g][n] * q[k][n] + bias[k/g][n]
+ *
+ *   qweight  uint32 [K/8, N]    4-bit codes 0..15 in the qweight layout above (nibble j of word
+ *                               [i][n] is row 8i+j); narrower codes are widened onto it first
+ *                               (w4a16_affine_widen)
+ *   scales   bf16   [K/g, N]    bit patterns
+ *   biases   bf16   [K/g, N]    bit patterns
+ * A, out, M (1..16), group_size, K, N, alignment, scratch and determinism as w4a16_gemm; there is
+ * no zero point. The sum of a group is formed as scale * sum(a * q) + bias * sum(a), so the
+ * accuracy contract is
+ *   |out - exact| <= 4e-3 * sum_k |A[m][k]| * (|scale * q| + |bias|) + 1e-6.
+ * w4a16_gemm_affine_ex takes the launch overrides of w4a16_gemm_ex (0 = the library's choice).
+ */
+int w4a16_gemm_affine(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                      const uint16_t *biases, int group_size, int M, int N, int K, void *out,
+                      int out_dtype, hipStream_t stream);
+int w4a16_gemm_affine_ex(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                         const uint16_t *biases, int group_size, int M, int N, int K, void *out,
+                         int out_dtype, int splits, int waves_k, int tile_cols, hipStream_t stream);
+
+/*
+ * Codes of `bits` = 1..4 bits rewritten as the 4-bit codes w4a16_gemm_affine reads, each keeping
+ * its value (scales and biases are unchanged), as TensorFold PR #859 first ran 2 and 3-bit
+ * checkpoints on its 4-bit tiles. Input layout: for column n the codes of rows 0, 1, 2, ... form
+ * one little-endian bit stream, row k at stream bits [k*bits, (k+1)*bits), and stream bit i is bit
+ * i % 32 of word [i/32][n] of packed (uint32 [K*bits/32, N]); at bits = 4 this is the qweight
+ * layout itself. Output qweight uint32 [K/8, N]. K % 32 == 0, N % 8 == 0, both 16-byte aligned,
+ * not overlapping. Bit-exact integer work; no scratch.
+ */
+int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight,
+                       hipStream_t stream);
+
+/*
  * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32
  * comparison, -0 == +0, NaN entries ignored; an all-NaN row gives 0).
  *   logits fp32 [M, N] device, 16-byte aligned; M in 1..65535; N in 1..2^31-1

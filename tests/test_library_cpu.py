@@ -174,3 +174,25 @@ def test_gate_up_prefill_rejects_bad_arguments(lib):
         return lib.w4a16_gemm_gate_up_prefill(A, Q, S, z, q2, S2, z2, 128, M, N, 512, O, 0, None)
     assert pre(q2=None) == -1 and pre(z=Z) == -1 and pre(z2=Z2) == -1
     assert pre(M=65537) == -1 and pre(N=260) == -1 and pre(q2=Q2 + 4) == -2
+
+
+B = 0x60000   # fake bias address
+
+
+def test_affine_rejects_bad_arguments(lib):
+    def aff(a=A, q=Q, s=S, b=B, g=64, M=1, N=256, K=512, o=O, dt=0):
+        return lib.w4a16_gemm_affine(a, q, s, b, g, M, N, K, o, dt, None)
+    assert aff(b=None) == -1 and b"biases" in lib.w4a16_last_error()
+    assert aff(q=None) == -1 and aff(M=17) == -1 and aff(g=48) == -1 and aff(N=260) == -1
+    assert aff(b=B + 2) == -2 and aff(s=S + 4) == -2 and aff(dt=2) == -1
+    ex = lambda **kw: lib.w4a16_gemm_affine_ex(A, Q, S, B, 64, 1, 256, 512, O, 0, kw.get("sp", 0),
+                                               kw.get("wk", 0), kw.get("tc", 0), None)
+    assert ex(wk=3) == -1 and ex(tc=96) == -1 and ex(sp=17, wk=1) == -1
+
+
+def test_affine_widen_rejects_bad_arguments(lib):
+    def widen(p=Q, bits=3, K=512, N=256, o=O):
+        return lib.w4a16_affine_widen(p, bits, K, N, o, None)
+    assert widen(bits=0) == -1 and widen(bits=5) == -1 and b"bits=5" in lib.w4a16_last_error()
+    assert widen(p=None) == -1 and widen(o=None) == -1 and widen(K=520) == -1 and widen(N=260) == -1
+    assert widen(p=Q + 4) == -2 and widen(o=O + 8) == -2

@@ -16,7 +16,7 @@ __all__ = [
     "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax",
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
-    "EXPORTS",
+    "w4a16_gemm_affine", "w4a16_affine_widen", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +26,8 @@ _lib = None
 # every symbol the header declares
 EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
-    "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
+    "w4a16_affine_widen", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
 
@@ -57,6 +58,9 @@ def load():
     lib.w4a16_gemm_gate_up.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_gate_up_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_gate_up_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
+    lib.w4a16_gemm_affine.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_affine_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
+    lib.w4a16_affine_widen.argtypes = [P, I, I, I, P, P]
     lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
@@ -195,6 +199,37 @@ def w4a16_argmax_rows(logits, idx, stream=None):
                                     _ptr(idx, "idx", (torch.int32,)), _stream(stream)),
            "w4a16_argmax_rows")
     return idx
+
+
+def w4a16_gemm_affine(A, qweight, scales, biases, group_size, out, splits=0, waves_k=0, tile_cols=0,
+                      stream=None):
+    """out[M,N] = A[M,K] (bf16) x W, W = scales * q + biases (4-bit codes in qweight, bf16 scales
+    and biases [K/g, N]); splits / waves_k / tile_cols as w4a16_gemm_ex (0 = default)."""
+    args = list(_gemm_args(A, qweight, scales, None, group_size, out))
+    if tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError(f"biases {tuple(biases.shape)} is not {tuple(scales.shape)}")
+    _sb = (torch.bfloat16, torch.int16, torch.uint16)
+    args[2] = _ptr(scales, "scales", _sb)
+    args[3] = _ptr(biases, "biases", _sb)
+    if splits or waves_k or tile_cols:
+        rc = load().w4a16_gemm_affine_ex(*args, int(splits), int(waves_k), int(tile_cols), _stream(stream))
+    else:
+        rc = load().w4a16_gemm_affine(*args, _stream(stream))
+    _check(rc, "w4a16_gemm_affine")
+    return out
+
+
+def w4a16_affine_widen(packed, bits, K, qweight_out, stream=None):
+    """Codes of ``bits`` (1..4) bits in column bit streams [K*bits/32, N] -> 4-bit qweight [K/8, N]."""
+    N = packed.shape[1]
+    if packed.shape[0] * 32 != K * bits:
+        raise ValueError(f"packed {tuple(packed.shape)} does not hold K={K} codes of {bits} bits")
+    if tuple(qweight_out.shape) != (K // 8, N):
+        raise ValueError("qweight_out must be [K/8, N]")
+    _check(load().w4a16_affine_widen(_ptr(packed, "packed", _I32), int(bits), int(K), N,
+                                     _ptr(qweight_out, "qweight_out", _I32), _stream(stream)),
+           "w4a16_affine_widen")
+    return qweight_out
 
 
 def w4a16_unpack_u8(qweight, q_out, stream=None):

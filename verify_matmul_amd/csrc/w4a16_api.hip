@@ -130,7 +130,7 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
 // tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
 // `splits` workgroups (summed through scratch): 4 waves per workgroup up to 32 pieces, 8 beyond
 // and for more than 8 rows. `splits` / `wk` > 0 override the choice (tuning and tests).
-int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile_cols, bool argmax,
+int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int tile_cols, bool argmax,
               GemmPlan *plan)
 {
     const int steps = K / kStepK;
@@ -177,7 +177,7 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
     // On 128-column tiles, whose registers already limit the waves per CU, the test is whether the
     // staged workgroups still fit that many waves (output layer, M = 5: 134.4 -> 127.7 us).
     GemmPlan staged{};
-    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, sym, argmax, &staged);
+    const size_t lds_staged = gemm_lds_layout(M, K, g, splits, wk, cols, true, zm, argmax, &staged);
     const bool fits = cols == 8 ? (size_t)kLdsPerCu / lds_staged >= (size_t)std::max(1, kWideTileWavesPerCu / wk)
                                 : (size_t)staged.wave_lds <= (size_t)kLdsStageBudget;
     plan->lds_a = !plan->mfma || (fits && lds_staged <= (size_t)kMaxLds);
@@ -185,7 +185,7 @@ int make_plan(int M, int N, int K, int g, bool sym, int splits, int wk, int tile
     // it each wave would run an exponent pass over its slice and convert every fragment as it
     // streams in. Staged slices are converted in the wave (cheaper than the extra launch).
     plan->prep_a = plan->mfma && !plan->lds_a;
-    plan->lds = gemm_lds_layout(M, K, g, splits, wk, cols, plan->lds_a, sym, argmax, plan);
+    plan->lds = gemm_lds_layout(M, K, g, splits, wk, cols, plan->lds_a, zm, argmax, plan);
     if (plan->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "plan needs %zu bytes of LDS per workgroup (max %d): use more splits",
                     plan->lds, kMaxLds);
@@ -215,11 +215,13 @@ int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scal
 }
 
 
-// One stored matrix: packed codes, fp16 scales, packed zeros (nullptr: symmetric).
+// One stored matrix: packed codes, scales, packed zeros (nullptr: symmetric), or for affine
+// codes bf16 scales and bf16 biases (no zeros).
 struct Matrix {
     const uint32_t *qweight;
     const uint16_t *scales;
     const uint32_t *qzeros;
+    const uint16_t *biases = nullptr;
 };
 
 // One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick;
@@ -233,6 +235,10 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     const uint32_t *qzeros = w.qzeros;
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
+    if (w.biases && (qzeros || up || idx))
+        return fail(W4A16_ERR_INVALID_ARG, "affine codes take no zero points, pair or fused pick");
+    if (w.biases && !aligned16(w.biases)) return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
+    const ZeroMode zm = w.biases ? kAffine : qzeros ? kZeroPacked : kZeroSym;
     if (up) {
         rc = check_gemm_args(A, up->qweight, up->scales, up->qzeros, group_size, M, N, K, out, out_dtype);
         if (rc != W4A16_OK) return rc;
@@ -244,7 +250,7 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     const int NV = up ? 2 * N : N;   // columns of the planned problem
     if (up) tile_cols = 128;
     GemmPlan plan{};
-    rc = make_plan(M, NV, K, group_size, qzeros == nullptr, splits, waves_k, tile_cols, idx != nullptr, &plan);
+    rc = make_plan(M, NV, K, group_size, zm, splits, waves_k, tile_cols, idx != nullptr, &plan);
     if (rc != W4A16_OK) return rc;
 
     GemmArgs a{};
@@ -252,6 +258,7 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     a.qweight = qweight;
     a.scales = scales;
     a.qzeros = qzeros;
+    a.biases = w.biases;
     if (up) {
         a.qweight2 = up->qweight;
         a.scales2 = up->scales;
@@ -421,12 +428,41 @@ int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, c
     return w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, stream);
 }
 
+int w4a16_gemm_affine_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint16_t *biases,
+                         int group_size, int M, int N, int K, void *out, int out_dtype, int splits, int waves_k,
+                         int tile_cols, hipStream_t stream)
+{
+    if (!biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
+    Matrix w{qweight, scales, nullptr};
+    w.biases = biases;
+    return gemm_call(A, w, nullptr, group_size, M, N, K, out, out_dtype, splits, waves_k, tile_cols, nullptr, stream);
+}
+
+int w4a16_gemm_affine(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint16_t *biases,
+                      int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
+{
+    return w4a16_gemm_affine_ex(A, qweight, scales, biases, group_size, M, N, K, out, out_dtype, 0, 0, 0, stream);
+}
+
+int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t stream)
+{
+    if (!packed || !qweight) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (bits < 1 || bits > 4) return fail(W4A16_ERR_INVALID_ARG, "bits=%d outside 1..4", bits);
+    if (K <= 0 || N <= 0 || K % 32 || N % 8) return fail(W4A16_ERR_INVALID_ARG, "K=%d N=%d", K, N);
+    if ((long long)(K / 8) * N > 0xFFFFFFFFLL)
+        return fail(W4A16_ERR_UNSUPPORTED, "qweight of %lld words exceeds 2^32 words", (long long)(K / 8) * N);
+    if (!aligned16(packed) || !aligned16(qweight)) return fail(W4A16_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    const hipError_t e = launch_affine_widen(packed, bits, K, N, qweight, stream);
+    if (e != hipSuccess) return hip_fail(e, "widen launch");
+    return W4A16_OK;
+}
+
 int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k, int *tile_cols)
 {
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
     GemmPlan plan{};
-    const int rc = make_plan(M, N, K, group_size, true, 0, 0, 0, false, &plan);
+    const int rc = make_plan(M, N, K, group_size, kZeroSym, 0, 0, 0, false, &plan);
     if (rc != W4A16_OK) return rc;
     if (kernel) *kernel = plan.mfma ? 1 : 0;
     if (splits) *splits = plan.splits;

@@ -129,6 +129,38 @@ __global__ void dequant_f32_kernel(const uint32_t *qweight, const uint16_t *scal
     }
 }
 
+// Codes of kBits (1..4) bits widened onto the 4-bit layout, each keeping its value, so a
+// checkpoint of narrower codes runs on the 4-bit kernels unchanged (TensorFold PR #859, commit
+// messages: 2 and 3-bit codes first ran on the affine-4 tiles this way). One thread per column
+// and 32-row block: its kBits stream words in, four 8-code words out, all loads and stores
+// coalesced along the columns.
+template <int kBits>
+__global__ void affine_widen_kernel(const uint32_t *packed, int K, int N, uint32_t *qweight)
+{
+    const long long items = (long long)(K / 32) * N;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long t = i / N;   // 32-row block
+        const int n = (int)(i - t * N);
+        uint32_t u[kBits + 1];
+#pragma unroll
+        for (int r = 0; r < kBits; ++r) u[r] = packed[(t * kBits + r) * N + n];
+        u[kBits] = 0;
+        uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {   // row 32t + j: stream bits [j * kBits, (j + 1) * kBits)
+            constexpr uint32_t kMask = (1u << kBits) - 1u;
+            const int o = j * kBits;
+            const int w = o / 32, sh = o % 32;
+            uint32_t c = u[w] >> sh;
+            if (sh + kBits > 32) c |= u[w + 1] << (32 - sh);
+            out[j / 8] |= (c & kMask) << (4 * (j % 8));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qweight[(t * 4 + r) * N + n] = out[r];
+    }
+}
+
 unsigned grid_for(long long items, int threads)
 {
     long long b = (items + threads - 1) / threads;
@@ -143,6 +175,20 @@ hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t stream)
 {
     hipLaunchKernelGGL(argmax_rows_kernel, dim3((unsigned)a.chunks, (unsigned)a.M), dim3(kArgmaxThreads), 0,
                        stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t s)
+{
+    const long long items = (long long)(K / 32) * N;
+    const dim3 grid(grid_for(items, 256)), block(256);
+    switch (bits) {
+    case 1: hipLaunchKernelGGL(affine_widen_kernel<1>, grid, block, 0, s, packed, K, N, qweight); break;
+    case 2: hipLaunchKernelGGL(affine_widen_kernel<2>, grid, block, 0, s, packed, K, N, qweight); break;
+    case 3: hipLaunchKernelGGL(affine_widen_kernel<3>, grid, block, 0, s, packed, K, N, qweight); break;
+    case 4: hipLaunchKernelGGL(affine_widen_kernel<4>, grid, block, 0, s, packed, K, N, qweight); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -119,9 +119,13 @@ __global__ __launch_bounds__(kPrepWaves * 64) void act_prep_kernel(ActPrepArgs p
 
 // Occupancy the register allocator must keep (waves per SIMD; 1 = no constraint). Left to
 // itself it moves the 64-column matrix-core kernels' accumulators into AGPRs whenever a
-// workgroup has at most 4 waves, which costs two waves per SIMD.
-template <bool kMfma, bool kSym, int kC>
-constexpr int gemm_min_waves() { return kMfma && kC == 4 ? (kSym ? 7 : 5) : 1; }
+// workgroup has at most 4 waves, which costs two waves per SIMD. Affine codes hold one more
+// accumulator and the biases: at 7 they would spill.
+template <bool kMfma, int kZM, int kC>
+constexpr int gemm_min_waves()
+{
+    return kMfma && kC == 4 ? (kZM == kZeroPacked ? 5 : kZM == kAffine ? 6 : 7) : 1;
+}
 
 // kLdsA: the wave stages its activation slice in LDS and converts it itself. Otherwise (a
 // slice too large to stage) the activations come prepared by act_prep_kernel -- fp16, slot
@@ -131,11 +135,17 @@ constexpr int gemm_min_waves() { return kMfma && kC == 4 ? (kSym ? 7 : 5) : 1; }
 // output columns of both, the activations are staged and converted once for the two, and the
 // epilogue writes silu(gate) * up. Internally the pair is a 2N-column problem whose column c of
 // a tile is output column (c / 8) * 4 + c % 4 of matrix (c / 4) % 2.
-template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kPf, int kC, bool kDual = false>
+// kZM (ZeroMode): for affine codes, w = s * q + b, the sum of a group is
+// s * sum(a * q) + b * sum(a): the codes go through the same exact conversion with zero point
+// 0, and sum(a) over the group comes from one more product per step against a fragment of ones
+// (the matrix cores are not the bound at these row counts).
+template <bool kMfma, int kZM, bool kLdsA, int kWK, int kPf, int kC, bool kDual = false>
 __global__ __launch_bounds__(kWK * 64)
-__attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a16_gemm_kernel(GemmArgs p)
+__attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a16_gemm_kernel(GemmArgs p)
 {
     static_assert(!kDual || (kMfma && kC == 8), "gated pairs run on the matrix cores, 8 columns per lane");
+    static_assert(!kDual || kZM != kAffine, "gated pairs take GPTQ codes");
+    constexpr bool kAff = kZM == kAffine;
     constexpr bool kPreA = !kLdsA;
     constexpr int kTile = 16 * kC;      // columns per tile: kC adjacent columns per lane
     constexpr int kOutTile = kDual ? kTile / 2 : kTile;   // output columns per tile
@@ -176,6 +186,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     uint4 *a_lds = reinterpret_cast<uint4 *>(wreg);                                // [word row][M]
     uint16_t *sc_lds = reinterpret_cast<uint16_t *>(wreg + p.scale_off);           // [group][64]
     uint32_t *z_lds = reinterpret_cast<uint32_t *>(wreg + p.zero_off);             // [group][8]
+    uint16_t *b_lds = reinterpret_cast<uint16_t *>(wreg + p.zero_off);             // affine: [group][64]
 
     const int n0 = tile * kOutTile + cl * (kDual ? 4 : kC);   // the lane's first output column
     const bool col_ok = n0 < N;
@@ -241,8 +252,8 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             load_to_lds4((j < 4 ? p.scales : p.scales2) + (size_t)gi * N + c, sc_lds + (size_t)b * 2);
             ++pre_loads;
         }
-    } else {   // scales: kZW items of 8 columns per group (lanes past the last item stay idle, so the
-        // LDS area holds exactly the wave's groups)
+    } else {   // scales (affine: and biases): kZW items of 8 columns per group (lanes past the last
+        // item stay idle, so the LDS area holds exactly the wave's groups)
         const int sitems = ng * kZW;
         for (int b = 0; b < sitems; b += 64) {
             const int it = b + lane;
@@ -251,9 +262,13 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             if (c >= N) c = 0;
             if (it < sitems) load_to_lds16(p.scales + (size_t)gi * N + c, sc_lds + (size_t)b * 8);
             ++pre_loads;
+            if constexpr (kAff) {
+                if (it < sitems) load_to_lds16(p.biases + (size_t)gi * N + c, b_lds + (size_t)b * 8);
+                ++pre_loads;
+            }
         }
     }
-    if (!kSym) {   // zero words: kZW per group (8 columns each; a pair: 8 gate words, 8 up words)
+    if constexpr (kZM == kZeroPacked) {   // zero words: kZW per group (8 columns each; a pair: 8 gate words, 8 up words)
         const int zitems = ng * kZW;
         for (int b = 0; b < zitems; b += 64) {
             const int it = b + lane;
@@ -348,7 +363,9 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
     }
     ZeroSub zs[kC];
 #pragma unroll
-    for (int j = 0; j < kC; ++j) zs[j] = zero_sub_sym();
+    for (int j = 0; j < kC; ++j) zs[j] = kAff ? zero_sub(0u) : zero_sub_sym();
+    float4_t acc1 = float4_t{0.f, 0.f, 0.f, 0.f};   // affine: the group's activation sums per row
+    const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
     // Position in the quantisation groups, kept by counting (all wave-uniform): step t is step
     // gpos of group gi, and `first` marks the first step of the wave's part of a group.
     int gi = g0;
@@ -371,7 +388,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             a = __builtin_bit_cast(half8_t, av);   // prepared fragment
             if (cl >= M) a = zero8;
         }
-        if (!kSym && first) {   // zero points change once per group (uniform)
+        if (kZM == kZeroPacked && first) {   // zero points change once per group (uniform)
             if constexpr (kDual) {
                 const uint32_t *zg = z_lds + (gi - g0) * kZW + (cl >> 1);
                 const uint32_t zw0 = zg[0], zw1 = zg[8];   // gate, up
@@ -396,7 +413,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
         }
 #pragma unroll
         for (int j = 0; j < kC; ++j) {
-            const half8_t b = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
+            const half8_t b = dequant_word(words[j], kZM == kZeroSym ? zero_sub_sym() : zs[j], mk);
             if (kMfma) {
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
             } else {
@@ -406,6 +423,18 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
                 s = __builtin_amdgcn_fdot2(b.hi.lo, a.hi.lo, s, false);
                 s = __builtin_amdgcn_fdot2(b.hi.hi, a.hi.hi, s, false);
                 acc[j][0] = s;
+            }
+        }
+        if constexpr (kAff) {
+            if (kMfma) {
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, acc1, 0, 0, 0);
+            } else {
+                float s = acc1[0];
+                s = __builtin_amdgcn_fdot2(ones.lo.lo, a.lo.lo, s, false);
+                s = __builtin_amdgcn_fdot2(ones.lo.hi, a.lo.hi, s, false);
+                s = __builtin_amdgcn_fdot2(ones.hi.lo, a.hi.lo, s, false);
+                s = __builtin_amdgcn_fdot2(ones.hi.hi, a.hi.hi, s, false);
+                acc1[0] = s;
             }
         }
         if (last) {
@@ -424,7 +453,23 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kSym, kC>()))) void w4a
             }
             float s4[kC];
 #pragma unroll
-            for (int j = 0; j < kC; ++j) s4[j] = half_bits_to_float((sw[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+            for (int j = 0; j < kC; ++j) {
+                const uint32_t bits = (sw[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+                s4[j] = kAff ? bf16_bits_to_float(bits) : half_bits_to_float(bits);
+            }
+            if constexpr (kAff) {   // the bias term first: b * sum(a), per row
+                const uint16_t *bp = b_lds + (gi - g0) * kTile + cl * kC;
+                uint32_t bw[kC / 2];
+#pragma unroll
+                for (int i = 0; i < kC / 2; ++i) bw[i] = reinterpret_cast<const uint32_t *>(bp)[i];
+#pragma unroll
+                for (int j = 0; j < kC; ++j) {
+                    const float bj = bf16_bits_to_float((bw[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+#pragma unroll
+                    for (int r = 0; r < (kMfma ? 4 : 1); ++r) tot[j][r] = __builtin_fmaf(acc1[r], bj, tot[j][r]);
+                }
+                acc1 = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int j = 0; j < kC; ++j) {
                 if (kMfma) {
@@ -726,12 +771,12 @@ __global__ __launch_bounds__(64) void argmax_keys_finish_kernel(unsigned long lo
 hipError_t launch_act_prep(const ActPrepArgs &pa, hipStream_t stream);
 namespace {
 
-template <bool kMfma, bool kSym, bool kLdsA, int kWK, int kC, bool kDual>
+template <bool kMfma, int kZM, bool kLdsA, int kWK, int kC, bool kDual>
 hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     constexpr int kPf = kLdsA ? kRingStaged : kRingConvert;
     constexpr int kOutTile = kDual ? 8 * kC : 16 * kC;
-    const auto kern = w4a16_gemm_kernel<kMfma, kSym, kLdsA, kWK, kPf, kC, kDual>;
+    const auto kern = w4a16_gemm_kernel<kMfma, kZM, kLdsA, kWK, kPf, kC, kDual>;
     if (!kLdsA) {
         const hipError_t e = launch_act_prep(ActPrepArgs{a.A, a.A16, a.ashift, a.M, a.K, a.splits, kWK}, stream);
         if (e != hipSuccess) return e;
@@ -749,35 +794,36 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
     return hipGetLastError();
 }
 
-template <bool kMfma, bool kSym, bool kLdsA, int kC, bool kDual = false>
+template <bool kMfma, int kZM, bool kLdsA, int kC, bool kDual = false>
 hipError_t launch_wk(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     switch (plan.wk) {
-    case 1: return launch_one<kMfma, kSym, kLdsA, 1, kC, kDual>(a, plan, stream);
-    case 2: return launch_one<kMfma, kSym, kLdsA, 2, kC, kDual>(a, plan, stream);
-    case 4: return launch_one<kMfma, kSym, kLdsA, 4, kC, kDual>(a, plan, stream);
-    case 8: return launch_one<kMfma, kSym, kLdsA, 8, kC, kDual>(a, plan, stream);
-    case 16: return launch_one<kMfma, kSym, kLdsA, 16, kC, kDual>(a, plan, stream);
+    case 1: return launch_one<kMfma, kZM, kLdsA, 1, kC, kDual>(a, plan, stream);
+    case 2: return launch_one<kMfma, kZM, kLdsA, 2, kC, kDual>(a, plan, stream);
+    case 4: return launch_one<kMfma, kZM, kLdsA, 4, kC, kDual>(a, plan, stream);
+    case 8: return launch_one<kMfma, kZM, kLdsA, 8, kC, kDual>(a, plan, stream);
+    case 16: return launch_one<kMfma, kZM, kLdsA, 16, kC, kDual>(a, plan, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 // The GEMV runs on 64-column tiles only (128-column tiles go to the matrix cores).
-template <bool kMfma, bool kSym, bool kLdsA>
+template <bool kMfma, int kZM, bool kLdsA>
 hipError_t launch_cols(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     if constexpr (kMfma)
-        return plan.cols == 8 ? launch_wk<kMfma, kSym, kLdsA, 8>(a, plan, stream)
-                              : launch_wk<kMfma, kSym, kLdsA, 4>(a, plan, stream);
+        return plan.cols == 8 ? launch_wk<kMfma, kZM, kLdsA, 8>(a, plan, stream)
+                              : launch_wk<kMfma, kZM, kLdsA, 4>(a, plan, stream);
     else
-        return plan.cols == 4 ? launch_wk<kMfma, kSym, kLdsA, 4>(a, plan, stream) : hipErrorInvalidValue;
+        return plan.cols == 4 ? launch_wk<kMfma, kZM, kLdsA, 4>(a, plan, stream) : hipErrorInvalidValue;
 }
 
 template <bool kMfma, bool kLdsA>
 hipError_t launch_sym(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
-    return a.qzeros == nullptr ? launch_cols<kMfma, true, kLdsA>(a, plan, stream)
-                               : launch_cols<kMfma, false, kLdsA>(a, plan, stream);
+    if (a.biases) return launch_cols<kMfma, kAffine, kLdsA>(a, plan, stream);
+    return a.qzeros == nullptr ? launch_cols<kMfma, kZeroSym, kLdsA>(a, plan, stream)
+                               : launch_cols<kMfma, kZeroPacked, kLdsA>(a, plan, stream);
 }
 
 // A gated pair: matrix cores on 8 columns per lane (4 of each matrix).
@@ -785,8 +831,8 @@ template <bool kLdsA>
 hipError_t launch_pair(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     if (plan.cols != 8 || !plan.mfma) return hipErrorInvalidValue;
-    return a.qzeros == nullptr ? launch_wk<true, true, kLdsA, 8, true>(a, plan, stream)
-                               : launch_wk<true, false, kLdsA, 8, true>(a, plan, stream);
+    return a.qzeros == nullptr ? launch_wk<true, kZeroSym, kLdsA, 8, true>(a, plan, stream)
+                               : launch_wk<true, kZeroPacked, kLdsA, 8, true>(a, plan, stream);
 }
 
 }  // namespace

@@ -40,11 +40,18 @@ constexpr int kRowHeader = 32;
 constexpr int kRingStaged = 3;
 constexpr int kRingConvert = 2;
 
+// How a column's weights are formed from its codes q:
+//   kZeroPacked  w = (q - z) * s, zero points z in packed words (GPTQ)
+//   kZeroSym     w = (q - 8) * s (GPTQ symmetric)
+//   kAffine      w = s * q + b, bf16 scales and biases (MLX affine)
+enum ZeroMode : int { kZeroPacked = 0, kZeroSym = 1, kAffine = 2 };
+
 struct GemmArgs {
     const uint16_t *A;
     const uint32_t *qweight;
     const uint16_t *scales;
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
+    const uint16_t *biases;   // affine codes: bf16 biases [K/g, N] (scales are then bf16 too)
     // gated pair: the up projection (same shape as qweight, the gate); out = silu(gate) * up.
     // qweight2 == nullptr: a single matrix.
     const uint32_t *qweight2;
@@ -63,7 +70,7 @@ struct GemmArgs {
     int out_bf16;
     int wave_lds;             // LDS bytes of one wave's staging area
     int scale_off;            // offset of the scales within a wave's area
-    int zero_off;             // offset of the zero words within a wave's area
+    int zero_off;             // offset of the zero words (affine: the biases) within a wave's area
 };
 
 // How one call is launched.
@@ -89,9 +96,10 @@ inline int max_wave_steps(int K, int splits, int wk)
 inline size_t round_up_sz(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // LDS layout of a plan: per-wave row shifts, then one staging area per wave (activations if
-// staged, the scales and the zero words of the wave's groups, filled by direct loads), and,
-// after the main loop, the cross-wave reduction buffer over the same bytes.
-inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols, bool lds_a, bool sym,
+// staged, the scales and the zero words -- or for affine codes the biases -- of the wave's
+// groups, filled by direct loads), and, after the main loop, the cross-wave reduction buffer
+// over the same bytes.
+inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols, bool lds_a, ZeroMode zm,
                               bool argmax, GemmPlan *pl)
 {
     const size_t tile = (size_t)tile_columns(cols);
@@ -100,7 +108,9 @@ inline size_t gemm_lds_layout(int M, int K, int g, int splits, int wk, int cols,
     const size_t groups = (size_t)(ws + spg - 1) / spg + 1;
     const size_t a_bytes = lds_a ? round_up_sz((size_t)M * ws * 4, 64) * 16 : 0;
     const size_t s_bytes = groups * (tile / 8) * 16;                         // 8 scales per item
-    const size_t z_bytes = sym ? 0 : round_up_sz(groups * (tile / 8) * 4, 16);   // 8 zeros per word
+    const size_t z_bytes = zm == kZeroSym ? 0
+                           : zm == kAffine ? s_bytes                                   // one bias per scale
+                                           : round_up_sz(groups * (tile / 8) * 4, 16);   // 8 zeros per word
     const size_t wave = a_bytes + s_bytes + z_bytes;
     const size_t header = (size_t)wk * kRowHeader * sizeof(int);
     const size_t red = (wk > 1 || splits > 1 || argmax) ? (size_t)wk * M * tile * sizeof(float) : 0;
@@ -162,6 +172,9 @@ struct ArgmaxArgs {
 constexpr int kArgmaxChunk = 4096;   // logits per argmax workgroup
 
 hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t stream);
+// Codes of 1..4 bits in column bit streams [K*bits/32, N] rewritten as 4-bit codes [K/8, N]
+// (each code keeps its value).
+hipError_t launch_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t s);
 hipError_t launch_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q, hipStream_t s);
 hipError_t launch_dequant_f32(const uint32_t *qweight, const uint16_t *scales,
                               const uint32_t *qzeros, int g, int K, int N, float *w,
