@@ -366,8 +366,8 @@ def run_affine(args, lib):
     import verify_matmul_amd as vm
     from verify_matmul_amd import synth
 
-    if args.prefill or args.gate_up or args.tile_cols:
-        print("bench.py: --affine takes no --prefill, --gate-up or --tile-cols", file=sys.stderr)
+    if args.prefill or args.gate_up:
+        print("bench.py: --affine takes no --prefill or --gate-up", file=sys.stderr)
         return 2
     wl = synth.AFFINE_WORKLOADS["ffn_up_affine4"]
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
@@ -386,7 +386,8 @@ def run_affine(args, lib):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, args.splits, args.waves_k, 0, sp)
+    calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, args.splits, args.waves_k,
+               args.tile_cols, sp)
               for M in ms] for qw, sc, bi, a, outs in pool]
     fn = lib.w4a16_gemm_affine_ex
 

@@ -139,7 +139,10 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
     // 128-column tiles for wide matrices: each wave then converts its activation slice once
     // for twice the columns (measured on the 248320-column output layer: 148 -> 130 us at
     // M = 5); narrower matrices keep 64-column tiles and the larger wave count they give.
-    const int cols = tile_cols != 0 ? tile_cols / 16 : (N >= kWideTileMinN ? 8 : 4);
+    // Affine codes above 8 rows take them too: the product against ones that forms the group
+    // sums of the activations is then shared by twice the columns (affine-4 FFN 5120 x 17408,
+    // groups of 64, M = 12 / 16: 28.4 -> 25.7 / 30.6 -> 27.9 us; at M <= 8 no gain).
+    const int cols = tile_cols != 0 ? tile_cols / 16 : (N >= kWideTileMinN || (zm == kAffine && M > 8) ? 8 : 4);
     const int tiles = (N + tile_columns(cols) - 1) / tile_columns(cols);
     if (splits == 0 || wk == 0) {
         // P pieces per tile: about 4352 waves in all, at least 8 pieces, of at least 10 steps
