@@ -39,18 +39,18 @@ constexpr int kStS = kPrefillTileN * 2;
 constexpr int kStZ = kPrefillTileN / 8 * 4;
 constexpr int kStBytes = kStA + kStB + kStS + kStZ;
 
+// Waves per SIMD the register allocator must keep: 3 for symmetric zero points (the gated pair
+// needs it: FFN 5120 x 17408 at M = 2048, 852 us against 985 with 2), 2 with stored zero
+// points, whose extra registers would spill at 3 (FFN down 17408 x 5120 at M = 2048: 1158 us
+// at 3 against 772 at 2).
+template <bool kSym>
+constexpr int prefill_min_waves() { return kSym ? 3 : 2; }
+
 // kDual: a gated pair (gate in qweight, up in qweight2). The tile's 256 columns are then 128
 // output columns of the gate followed by the same 128 of the up projection: waves 0 and 1
 // compute the gate, waves 2 and 3 the up projection, and the up waves hand their sums to the
 // gate waves through LDS, which write silu(gate) * up. Everything up to the epilogue is the
 // single-matrix kernel over those 256 columns.
-// Waves per SIMD the register allocator must keep: 3 for symmetric zero points (the gated pair
-// needs it: FFN 5120 x 17408 at M = 2048, 820-830 us against 957-981 with 2), 2 with stored
-// zero points, whose extra registers would spill at 3 (FFN down 17408 x 5120 at M = 2048: 1151
-// us at 3 against 777 at 2).
-template <bool kSym>
-constexpr int prefill_min_waves() { return kSym ? 3 : 2; }
-
 template <bool kSym, bool kDual>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_min_waves<kSym>()))) void
 w4a16_prefill_kernel(PrefillArgs p)
