@@ -35,8 +35,10 @@ output, and the algorithmic bytes count both matrices.
 
 With --affine every call is the affine-code GEMM (w4a16_gemm_affine, w = s * q + b, bf16 scales
 and biases) on the affine-4 FFN up projection 5120 x 17408 in groups of 64, M = 1, 2, 4, 8, 16.
-Algorithmic bytes per call = codes (K*N/2) + scales and biases (4*K*N/g) + activations (2*M*K)
-+ outputs (4*M*N).
+Algorithmic bytes per call = codes (K*N*bits/8) + scales and biases (4*K*N/g) + activations
+(2*M*K) + outputs (4*M*N). --affine --affine-bits 8 times the 8-bit checkpoint of the same
+projection through its split planes (w4a16_gemm_affine_split, planes prepared once before
+timing); its algorithmic bytes are those of the 8-bit format.
 
 Prints one JSON line (rank 0; this build runs on one GPU).
 """
@@ -83,6 +85,8 @@ def parse():
                    help="time the fused gated pair silu(A x W_gate) * (A x W_up) on the workload's shape")
     p.add_argument("--affine", action="store_true",
                    help="time the affine-code GEMM on the affine-4 FFN up projection (w = s * q + b)")
+    p.add_argument("--affine-bits", type=int, default=4, choices=[4, 8],
+                   help="with --affine: code width of the checkpoint (8 runs the split planes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise kernel (y = 2x, fp32) over MIB MiB five times: the "
@@ -355,8 +359,8 @@ def main():
     return 0
 
 
-def affine_bytes(M, K, N, g):
-    return K * N // 2 + 4 * (K // g) * N + 2 * M * K + 4 * M * N
+def affine_bytes(M, K, N, g, bits=4):
+    return K * N * bits // 8 + 4 * (K // g) * N + 2 * M * K + 4 * M * N
 
 
 def run_affine(args, lib):
@@ -369,27 +373,46 @@ def run_affine(args, lib):
     if args.prefill or args.gate_up:
         print("bench.py: --affine takes no --prefill or --gate-up", file=sys.stderr)
         return 2
-    wl = synth.AFFINE_WORKLOADS["ffn_up_affine4"]
+    bits = args.affine_bits
+    if bits == 8 and (args.splits or args.waves_k or args.tile_cols):
+        print("bench.py: --affine-bits 8 takes no launch knobs", file=sys.stderr)
+        return 2
+    wl = synth.AFFINE_WORKLOADS[f"ffn_up_affine{bits}"]
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
     x = synth.make_affine_inputs(wl)
     K, N, g = wl.K, wl.N, wl.group
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    per_copy = affine_bytes(1, K, N, g)
+    per_copy = affine_bytes(1, K, N, g, bits)
     R = max(2, math.ceil(POOL_BYTES / per_copy))
     qw0 = torch.from_numpy(np.ascontiguousarray(x.packed).view(np.int32)).to(dev)   # 4-bit: the qweight layout
     sc0 = torch.from_numpy(x.scales.view(np.int16)).to(dev)
     bi0 = torch.from_numpy(x.biases.view(np.int16)).to(dev)
     a0 = torch.from_numpy(x.act.view(np.int16)).to(dev)
-    pool = [(qw0.clone(), sc0.clone(), bi0.clone(), a0.clone(),
-             {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}) for _ in range(R)]
+    pool = []
+    for _ in range(R):
+        if bits == 8:   # the split planes, prepared once per copy
+            qw = torch.empty((2 * K // 8, N), dtype=torch.int32, device=dev)
+            sc = torch.empty((2 * K // g, N), dtype=torch.int16, device=dev)
+            bi = torch.empty((2 * K // g, N), dtype=torch.int16, device=dev)
+            vm.w4a16_affine_split(qw0, bits, sc0, bi0, g, K, qw, sc, bi)
+        else:
+            qw, sc, bi = qw0.clone(), sc0.clone(), bi0.clone()
+        pool.append((qw, sc, bi, a0.clone(), {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}))
+    del qw0
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, args.splits, args.waves_k,
-               args.tile_cols, sp)
-              for M in ms] for qw, sc, bi, a, outs in pool]
-    fn = lib.w4a16_gemm_affine_ex
+    if bits == 8:
+        calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, sp) for M in ms]
+                 for qw, sc, bi, a, outs in pool]
+        fn = lib.w4a16_gemm_affine_split
+    else:
+        calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, args.splits, args.waves_k,
+                   args.tile_cols, sp)
+                  for M in ms] for qw, sc, bi, a, outs in pool]
+        fn = lib.w4a16_gemm_affine_ex
 
     def step(i, evs=None):
         for j, M in enumerate(ms):
@@ -399,7 +422,7 @@ def run_affine(args, lib):
             if evs is not None:
                 evs[i][j][1].record(stream)
             if rc != 0:
-                raise RuntimeError(f"w4a16_gemm_affine_ex failed: {lib.w4a16_last_error().decode()}")
+                raise RuntimeError(f"affine GEMM failed: {lib.w4a16_last_error().decode()}")
 
     for i in range(args.warmup):
         step(i)
@@ -409,7 +432,7 @@ def run_affine(args, lib):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    value = sum(affine_bytes(M, K, N, g) for M in ms) * args.steps / wall / 1e9
+    value = sum(affine_bytes(M, K, N, g, bits) for M in ms) * args.steps / wall / 1e9
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
            for _ in range(args.steps)]
@@ -420,7 +443,7 @@ def run_affine(args, lib):
     per_m, dom, dom_time = {}, None, -1.0
     for j, M in enumerate(ms):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
-        b = affine_bytes(M, K, N, g)
+        b = affine_bytes(M, K, N, g, bits)
         us = float(np.mean(d))
         per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
@@ -443,14 +466,14 @@ def run_affine(args, lib):
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases), M in "
+        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases{'; split planes' if bits == 8 else ''}), M in "
                                f"{','.join(map(str, ms))} (one call each per step)",
                    "K": K, "N": N, "group": g, "bits": wl.bits, "ms": list(ms), "out": "fp32",
                    "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20)},
-        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine, M={dom})", "M": dom,
+        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine{', split planes' if bits == 8 else ''}, M={dom})", "M": dom,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": load_traffic("ffn_up_affine4", dom), "launches": args.steps,
+                     "traffic": load_traffic(f"ffn_up_affine{bits}", dom), "launches": args.steps,
                      "bytes_per_launch": bdom, "us_per_launch": round(us_dom, 3),
                      "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
         "per_m": per_m,
@@ -465,7 +488,7 @@ def run_affine(args, lib):
                 t = time.perf_counter()
                 oracle.affine_gemm(x.act[:M], x.packed, x.bits, x.scales, x.biases, g)
                 elapsed += time.perf_counter() - t
-                nbytes += affine_bytes(M, K, N, g)
+                nbytes += affine_bytes(M, K, N, g, bits)
             reps += 1
         rec["cpu_baseline"] = {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
                                "kind": "oracle",

@@ -204,6 +204,35 @@ int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t 
                        hipStream_t stream);
 
 /*
+ * Codes of 5..8 bits (TensorFold PR #859, commit messages: MLX checkpoints of 5 to 8 bits, each
+ * code keeping its value, scale and bias). Every code splits exactly into two 4-bit codes,
+ * q = 16 * hi + lo, so w = s * q + b = (s * lo + b) + (16 s) * hi.
+ *
+ * w4a16_affine_split (once, at load): from the column bit streams `packed` (uint32
+ * [K*bits/32, N], the layout of w4a16_affine_widen) and the bf16 scales and biases [K/g, N] it
+ * writes the two planes as one 4-bit matrix over 2K rows:
+ *   qweight_out uint32 [2K/8, N]   rows 0..K-1 the low nibbles, rows K..2K-1 the high nibbles
+ *   scales_out  bf16   [2K/g, N]   s, then 16 s (exact; a scale of magnitude 2^124 or more
+ *                                  overflows to infinity)
+ *   biases_out  bf16   [2K/g, N]   b, then 0
+ * bits in 5..8; K % 32 == 0, K % group_size == 0, group_size % 32 == 0, N % 8 == 0; 16-byte
+ * aligned, no overlap. Bit-exact; no scratch.
+ *
+ * w4a16_gemm_affine_split: out[M, N] = A[M, K] x W with W = s * q + b from those planes (qweight,
+ * scales, biases as written above, for the original K). The activations are copied twice along
+ * K into the stream's scratch buffer ([M, 2K] bf16) and the call runs as w4a16_gemm_affine over
+ * 2K rows, with its accuracy contract (the bound sum |a| (|s q| + |b|) of the original codes).
+ * M in 1..16; A, out and the other rules as w4a16_gemm_affine.
+ */
+int w4a16_affine_split(const uint32_t *packed, int bits, const uint16_t *scales,
+                       const uint16_t *biases, int group_size, int K, int N,
+                       uint32_t *qweight_out, uint16_t *scales_out, uint16_t *biases_out,
+                       hipStream_t stream);
+int w4a16_gemm_affine_split(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                            const uint16_t *biases, int group_size, int M, int N, int K, void *out,
+                            int out_dtype, hipStream_t stream);
+
+/*
  * Greedy pick per row: idx[m] = smallest n with logits[m][n] equal to the row maximum (fp32
  * comparison, -0 == +0, NaN entries ignored; an all-NaN row gives 0).
  *   logits fp32 [M, N] device, 16-byte aligned; M in 1..65535; N in 1..2^31-1

@@ -135,3 +135,59 @@ def test_affine_widened_codes_through_the_gemm(gu):
     torch.cuda.synchronize()
     y_ref, bound = oracle.affine_gemm(x.act, x.packed, 3, x.scales, x.biases, g)
     parity.check_close(out.cpu().numpy().astype(np.float64), y_ref, bound, "widened 3-bit")
+
+
+def _split_on_device(gu, x):
+    K, N, g = x.K, x.N, x.group
+    qw = torch.empty((2 * K // 8, N), dtype=torch.int32, device=gu.DEV)
+    so = torch.empty((2 * K // g, N), dtype=torch.int16, device=gu.DEV)
+    bo = torch.empty((2 * K // g, N), dtype=torch.int16, device=gu.DEV)
+    vm.w4a16_affine_split(gu.dev_u32(x.packed), x.bits, gu.dev_u16(x.scales), gu.dev_u16(x.biases), g, K, qw, so, bo)
+    torch.cuda.synchronize()
+    return qw, so, bo
+
+
+@pytest.mark.parametrize("bits", [5, 6, 7, 8])
+def test_affine_split_is_exact(gu, bits):
+    """The two 4-bit planes of every code (low nibbles, then high), the scales s then 16 s and the
+    biases b then 0, bit for bit."""
+    K, N, g = 640, 264, 64
+    x = synth.make_affine_random(500 + bits, 1, K, N, g, bits)
+    qw, so, bo = _split_on_device(gu, x)
+    codes = oracle.affine_unpack(x.packed, bits, K)
+    expect = synth.pack_rows(np.concatenate([codes & 15, codes >> 4], axis=0))
+    assert np.array_equal(qw.cpu().numpy().view(np.uint32), expect)
+    s16 = (torch.from_numpy(x.scales.view(np.int16)).view(torch.bfloat16) * 16).view(torch.int16).numpy()
+    assert np.array_equal(so.cpu().numpy(), np.concatenate([x.scales.view(np.int16), s16], axis=0))
+    assert np.array_equal(bo.cpu().numpy(), np.concatenate([x.biases.view(np.int16), np.zeros_like(s16)], axis=0))
+
+
+@pytest.mark.parametrize("K,N,g,bits", [(512, 200, 64, 8), (2048, 520, 64, 5), (1024, 1032, 128, 6), (64, 72, 32, 8)])
+def test_affine_split_gemm_parity(gu, K, N, g, bits):
+    """Codes of 5..8 bits through the split planes against the oracle on the original stream."""
+    x = synth.make_affine_random(600 + K % 251 + bits, 16, K, N, g, bits)
+    qw, so, bo = _split_on_device(gu, x)
+    act = gu.dev_u16(x.act)
+    for M in (1, 2, 5, 16):
+        gu.say(f"[affine split] K={K} N={N} g={g} bits={bits} M={M}")
+        out = torch.empty((M, N), dtype=torch.float32, device=gu.DEV)
+        vm.w4a16_gemm_affine_split(act[:M], qw, so, bo, g, out)
+        torch.cuda.synchronize()
+        y_ref, bound = oracle.affine_gemm(x.act[:M], x.packed, bits, x.scales, x.biases, g)
+        frac = parity.check_close(out.cpu().numpy().astype(np.float64), y_ref, bound, f"split bits={bits} M={M}")
+    gu.say(f"  worst err/tol {frac:.3e}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_affine8_ffn_workload(gu, M):
+    """The 8-bit affine FFN up projection 5120 x 17408 (groups of 64), sampled columns."""
+    x = synth.make_affine_inputs("ffn_up_affine8")
+    qw, so, bo = _split_on_device(gu, x)
+    out = torch.empty((M, x.N), dtype=torch.float32, device=gu.DEV)
+    vm.w4a16_gemm_affine_split(gu.dev_u16(x.act)[:M], qw, so, bo, x.group, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10 + M)
+    cols = np.unique(np.concatenate([rng.choice(x.N, 800, replace=False), np.arange(x.N - 64, x.N)]))
+    y_ref, bound = oracle.affine_gemm(x.act[:M], x.packed, 8, x.scales, x.biases, x.group, cols)
+    frac = parity.check_close(out.cpu().numpy().astype(np.float64)[:, cols], y_ref, bound, f"affine8 ffn M={M}")
+    gu.say(f"[affine8 ffn] M={M} worst err/tol {frac:.3e}")

@@ -196,3 +196,16 @@ def test_affine_widen_rejects_bad_arguments(lib):
     assert widen(bits=0) == -1 and widen(bits=5) == -1 and b"bits=5" in lib.w4a16_last_error()
     assert widen(p=None) == -1 and widen(o=None) == -1 and widen(K=520) == -1 and widen(N=260) == -1
     assert widen(p=Q + 4) == -2 and widen(o=O + 8) == -2
+
+
+def test_affine_split_rejects_bad_arguments(lib):
+    def split(p=Q, bits=8, s=S, b=B, g=64, K=512, N=256, qo=O, so=Z, bo=A):
+        return lib.w4a16_affine_split(p, bits, s, b, g, K, N, qo, so, bo, None)
+    assert split(bits=4) == -1 and split(bits=9) == -1 and b"bits=9" in lib.w4a16_last_error()
+    assert split(p=None) == -1 and split(so=None) == -1 and split(g=48) == -1 and split(K=544) == -1
+    assert split(N=260) == -1 and split(qo=O + 4) == -2 and split(b=B + 2) == -2
+
+    def gemm_split(K=512, g=64, M=1, b=B):
+        return lib.w4a16_gemm_affine_split(A, Q, S, b, g, M, 256, K, O, 0, None)
+    assert gemm_split(b=None) == -1 and gemm_split(K=96) == -1 and gemm_split(M=17) == -1
+    assert gemm_split(K=96, g=64) == -1 and b"group_size" in lib.w4a16_last_error()

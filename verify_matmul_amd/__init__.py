@@ -16,7 +16,7 @@ __all__ = [
     "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax",
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
-    "w4a16_gemm_affine", "w4a16_affine_widen", "EXPORTS",
+    "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +27,7 @@ _lib = None
 EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
     "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
-    "w4a16_affine_widen", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
 
@@ -61,6 +61,8 @@ def load():
     lib.w4a16_gemm_affine.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_affine_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_affine_widen.argtypes = [P, I, I, I, P, P]
+    lib.w4a16_affine_split.argtypes = [P, I, P, P, I, I, I, P, P, P, P]
+    lib.w4a16_gemm_affine_split.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
@@ -230,6 +232,51 @@ def w4a16_affine_widen(packed, bits, K, qweight_out, stream=None):
                                      _ptr(qweight_out, "qweight_out", _I32), _stream(stream)),
            "w4a16_affine_widen")
     return qweight_out
+
+
+def w4a16_affine_split(packed, bits, scales, biases, group_size, K, qweight_out, scales_out, biases_out,
+                       stream=None):
+    """Codes of ``bits`` (5..8) bits -> two 4-bit planes over 2K rows (low, then high) with their
+    scales (s, then 16 s) and biases (b, then 0), for w4a16_gemm_affine_split."""
+    N = packed.shape[1]
+    G = K // group_size
+    if packed.shape[0] * 32 != K * bits:
+        raise ValueError(f"packed {tuple(packed.shape)} does not hold K={K} codes of {bits} bits")
+    if tuple(scales.shape) != (G, N) or tuple(biases.shape) != (G, N):
+        raise ValueError(f"scales and biases must be [{G}, {N}]")
+    if tuple(qweight_out.shape) != (2 * K // 8, N):
+        raise ValueError("qweight_out must be [2K/8, N]")
+    if tuple(scales_out.shape) != (2 * G, N) or tuple(biases_out.shape) != (2 * G, N):
+        raise ValueError("scales_out and biases_out must be [2K/g, N]")
+    _sb = (torch.bfloat16, torch.int16, torch.uint16)
+    _check(load().w4a16_affine_split(_ptr(packed, "packed", _I32), int(bits), _ptr(scales, "scales", _sb),
+                                     _ptr(biases, "biases", _sb), int(group_size), int(K), N,
+                                     _ptr(qweight_out, "qweight_out", _I32), _ptr(scales_out, "scales_out", _sb),
+                                     _ptr(biases_out, "biases_out", _sb), _stream(stream)),
+           "w4a16_affine_split")
+    return qweight_out, scales_out, biases_out
+
+
+def w4a16_gemm_affine_split(A, qweight, scales, biases, group_size, out, stream=None):
+    """out[M,N] = A[M,K] x W, W = s * q + b from the split planes of w4a16_affine_split."""
+    M, K = A.shape
+    N = qweight.shape[1]
+    if qweight.shape[0] * 8 != 2 * K:
+        raise ValueError(f"qweight {tuple(qweight.shape)} is not the [2K/8, N] planes for K={K}")
+    if tuple(scales.shape) != (2 * K // group_size, N) or tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("scales and biases must be [2K/g, N]")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out {tuple(out.shape)} is not [{M}, {N}]")
+    dt = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}.get(out.dtype)
+    if dt is None:
+        raise TypeError("out must be float32 or bfloat16")
+    _sb = (torch.bfloat16, torch.int16, torch.uint16)
+    _check(load().w4a16_gemm_affine_split(_ptr(A, "A", _sb), _ptr(qweight, "qweight", _I32),
+                                          _ptr(scales, "scales", _sb), _ptr(biases, "biases", _sb),
+                                          int(group_size), M, N, K, _ptr(out, "out", (torch.float32, torch.bfloat16)),
+                                          dt, _stream(stream)),
+           "w4a16_gemm_affine_split")
+    return out
 
 
 def w4a16_unpack_u8(qweight, q_out, stream=None):

@@ -229,9 +229,11 @@ struct Matrix {
 
 // One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick;
 // `up` non-null makes it a gated pair (w is the gate): out = silu(A x w) * (A x up), planned as
-// one 2N-column problem on 128-column tiles (64 output columns of each matrix).
+// one 2N-column problem on 128-column tiles (64 output columns of each matrix). `dup_a`: A holds
+// K / 2 columns and is first copied twice along K into scratch (split affine planes).
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
-              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream)
+              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream,
+              bool dup_a = false)
 {
     const uint32_t *qweight = w.qweight;
     const uint16_t *scales = w.scales;
@@ -278,14 +280,16 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     a.scale_off = plan.scale_off;
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
-    if (split_k || plan.prep_a || idx) {
+    if (split_k || plan.prep_a || idx || dup_a) {
         // counters: [tile counters][argmax row keys (M x 64 bit)]
         const size_t tile = (size_t)tile_columns(plan.cols);
         const size_t tiles = ((size_t)NV + tile - 1) / tile;
         const size_t key_off = round_up(tiles * sizeof(uint32_t), 8);
         const size_t counter_bytes = key_off + 16 * sizeof(unsigned long long);
         const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
-        const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
+        const size_t prep_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
+        const size_t dup_off = round_up(prep_bytes, 256);   // the duplicated activations [M, K]
+        const size_t act_bytes = dup_a ? dup_off + a16_bytes : prep_bytes;
         ScratchView v{};
         rc = get_scratch(stream, counter_bytes, split_k ? (size_t)plan.splits * M * NV * sizeof(uint64_t) : 0,
                          act_bytes, split_k, &v);
@@ -295,6 +299,12 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
         a.stamp = v.stamp;
         a.A16 = static_cast<uint16_t *>(v.act);
         a.ashift = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
+        if (dup_a) {
+            uint16_t *dup = reinterpret_cast<uint16_t *>(static_cast<char *>(v.act) + dup_off);
+            const hipError_t e = launch_dup_halves(static_cast<const uint16_t *>(A), M, K / 2, dup, stream);
+            if (e != hipSuccess) return hip_fail(e, "activation copy launch");
+            a.A = dup;
+        }
         if (idx) {
             char *c = reinterpret_cast<char *>(v.counters);
             a.amax_keys = reinterpret_cast<unsigned long long *>(c + key_off);
@@ -445,6 +455,40 @@ int w4a16_gemm_affine(const void *A, const uint32_t *qweight, const uint16_t *sc
                       int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
 {
     return w4a16_gemm_affine_ex(A, qweight, scales, biases, group_size, M, N, K, out, out_dtype, 0, 0, 0, stream);
+}
+
+int w4a16_affine_split(const uint32_t *packed, int bits, const uint16_t *scales, const uint16_t *biases,
+                       int group_size, int K, int N, uint32_t *qweight_out, uint16_t *scales_out, uint16_t *biases_out,
+                       hipStream_t stream)
+{
+    if (!packed || !scales || !biases || !qweight_out || !scales_out || !biases_out)
+        return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (bits < 5 || bits > 8) return fail(W4A16_ERR_INVALID_ARG, "bits=%d outside 5..8", bits);
+    if (K <= 0 || N <= 0 || K % 32 || N % 8 || K > (1 << 29))
+        return fail(W4A16_ERR_INVALID_ARG, "K=%d N=%d", K, N);
+    if (group_size <= 0 || group_size % 32 || K % group_size)
+        return fail(W4A16_ERR_INVALID_ARG, "group_size=%d with K=%d", group_size, K);
+    if ((long long)(2 * (long long)K / 8) * N > 0xFFFFFFFFLL)
+        return fail(W4A16_ERR_UNSUPPORTED, "split planes of %lld words exceed 2^32 words", (long long)(K / 4) * N);
+    if (!aligned16(packed) || !aligned16(scales) || !aligned16(biases) || !aligned16(qweight_out) ||
+        !aligned16(scales_out) || !aligned16(biases_out))
+        return fail(W4A16_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+    const hipError_t e =
+        launch_affine_split(packed, bits, scales, biases, group_size, K, N, qweight_out, scales_out, biases_out, stream);
+    if (e != hipSuccess) return hip_fail(e, "split launch");
+    return W4A16_OK;
+}
+
+int w4a16_gemm_affine_split(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint16_t *biases,
+                            int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
+{
+    if (!biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
+    if (K <= 0 || K > (1 << 29)) return fail(W4A16_ERR_INVALID_ARG, "K=%d", K);
+    if (group_size <= 0 || group_size % 32 || K % group_size)   // the planes meet on a group boundary
+        return fail(W4A16_ERR_INVALID_ARG, "K=%d is not a multiple of group_size=%d (a multiple of 32)", K, group_size);
+    Matrix w{qweight, scales, nullptr};
+    w.biases = biases;
+    return gemm_call(A, w, nullptr, group_size, M, N, 2 * K, out, out_dtype, 0, 0, 0, nullptr, stream, true);
 }
 
 int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t stream)

@@ -161,6 +161,73 @@ __global__ void affine_widen_kernel(const uint32_t *packed, int K, int N, uint32
     }
 }
 
+// Codes of kBits (5..8) bits split exactly into two 4-bit planes, q = 16 * hi + lo: rows
+// 0..K-1 of the output hold lo, rows K..2K-1 hold hi, so with scales s then 16 s and biases b
+// then 0 the 4-bit affine kernel over 2K rows computes s * q + b for every code. One thread per
+// column and 32-row block, as in the widening above.
+template <int kBits>
+__global__ void affine_split_kernel(const uint32_t *packed, int K, int N, uint32_t *qweight)
+{
+    const long long items = (long long)(K / 32) * N;
+    const long long hi_off = (long long)(K / 8) * N;   // first word of the high plane
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long t = i / N;
+        const int n = (int)(i - t * N);
+        uint32_t u[kBits + 1];
+#pragma unroll
+        for (int r = 0; r < kBits; ++r) u[r] = packed[(t * kBits + r) * N + n];
+        u[kBits] = 0;
+        uint32_t lo[4] = {0u, 0u, 0u, 0u}, hi[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            constexpr uint32_t kMask = (1u << kBits) - 1u;
+            const int o = j * kBits;
+            const int w = o / 32, sh = o % 32;
+            uint32_t c = u[w] >> sh;
+            if (sh + kBits > 32) c |= u[w + 1] << (32 - sh);
+            c &= kMask;
+            lo[j / 8] |= (c & 0xFu) << (4 * (j % 8));
+            hi[j / 8] |= (c >> 4) << (4 * (j % 8));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            qweight[(t * 4 + r) * N + n] = lo[r];
+            qweight[hi_off + (t * 4 + r) * N + n] = hi[r];
+        }
+    }
+}
+
+// The group rows of the split planes: scales s then 16 s (exact in bf16: an exponent step), biases
+// b then 0. G = K / g groups of N columns each.
+__global__ void affine_split_groups_kernel(const uint16_t *scales, const uint16_t *biases, long long items,
+                                           uint16_t *scales_out, uint16_t *biases_out)
+{
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+         i += (long long)gridDim.x * blockDim.x) {
+        const uint16_t s = scales[i];
+        scales_out[i] = s;
+        scales_out[items + i] = (uint16_t)float_to_bf16_bits(bf16_bits_to_float(s) * 16.0f);
+        biases_out[i] = biases[i];
+        biases_out[items + i] = 0;
+    }
+}
+
+// dst[m][k] = src[m][k mod K] for k < 2K: the activations twice along K, 16 bytes per item.
+__global__ void dup_halves_kernel(const uint16_t *src, int M, int K, uint16_t *dst)
+{
+    const long long per_row = K / 8;
+    const long long items = (long long)M * per_row;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long m = i / per_row;
+        const long long c = i - m * per_row;
+        const uint4 v = *reinterpret_cast<const uint4 *>(src + m * K + c * 8);
+        *reinterpret_cast<uint4 *>(dst + m * 2 * K + c * 8) = v;
+        *reinterpret_cast<uint4 *>(dst + m * 2 * K + K + c * 8) = v;
+    }
+}
+
 unsigned grid_for(long long items, int threads)
 {
     long long b = (items + threads - 1) / threads;
@@ -189,6 +256,34 @@ hipError_t launch_affine_widen(const uint32_t *packed, int bits, int K, int N, u
     case 4: hipLaunchKernelGGL(affine_widen_kernel<4>, grid, block, 0, s, packed, K, N, qweight); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_affine_split(const uint32_t *packed, int bits, const uint16_t *scales, const uint16_t *biases,
+                               int g, int K, int N, uint32_t *qweight, uint16_t *scales_out, uint16_t *biases_out,
+                               hipStream_t s)
+{
+    const long long items = (long long)(K / 32) * N;
+    const dim3 grid(grid_for(items, 256)), block(256);
+    switch (bits) {
+    case 5: hipLaunchKernelGGL(affine_split_kernel<5>, grid, block, 0, s, packed, K, N, qweight); break;
+    case 6: hipLaunchKernelGGL(affine_split_kernel<6>, grid, block, 0, s, packed, K, N, qweight); break;
+    case 7: hipLaunchKernelGGL(affine_split_kernel<7>, grid, block, 0, s, packed, K, N, qweight); break;
+    case 8: hipLaunchKernelGGL(affine_split_kernel<8>, grid, block, 0, s, packed, K, N, qweight); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long gitems = (long long)(K / g) * N;
+    hipLaunchKernelGGL(affine_split_groups_kernel, dim3(grid_for(gitems, 256)), dim3(256), 0, s, scales, biases,
+                       gitems, scales_out, biases_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dup_halves(const uint16_t *src, int M, int K, uint16_t *dst, hipStream_t s)
+{
+    const long long items = (long long)M * (K / 8);
+    hipLaunchKernelGGL(dup_halves_kernel, dim3(grid_for(items, 256)), dim3(256), 0, s, src, M, K, dst);
     return hipGetLastError();
 }
 

@@ -175,6 +175,13 @@ hipError_t launch_argmax(const ArgmaxArgs &a, hipStream_t stream);
 // Codes of 1..4 bits in column bit streams [K*bits/32, N] rewritten as 4-bit codes [K/8, N]
 // (each code keeps its value).
 hipError_t launch_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t s);
+// Codes of 5..8 bits split into a low and a high 4-bit plane ([2K/8, N]: low rows, then high rows),
+// with the planes' scales [2K/g, N] (s, then 16 s) and biases (b, then 0).
+hipError_t launch_affine_split(const uint32_t *packed, int bits, const uint16_t *scales, const uint16_t *biases,
+                               int g, int K, int N, uint32_t *qweight, uint16_t *scales_out, uint16_t *biases_out,
+                               hipStream_t s);
+// dst [M, 2K] = src [M, K] twice along K (K % 8 == 0, 16-byte aligned rows).
+hipError_t launch_dup_halves(const uint16_t *src, int M, int K, uint16_t *dst, hipStream_t s);
 hipError_t launch_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q, hipStream_t s);
 hipError_t launch_dequant_f32(const uint32_t *qweight, const uint16_t *scales,
                               const uint32_t *qzeros, int g, int K, int N, float *w,

@@ -235,6 +235,9 @@ class AffineWorkload:
 AFFINE_WORKLOADS = {
     "ffn_up_affine4": AffineWorkload(6, "FFN up/gate 5120x17408 affine-4 g64", 5120, 17408, 64, 4,
                                      (1, 2, 4, 8, 16)),
+    # the same projection of an 8-bit MLX checkpoint
+    "ffn_up_affine8": AffineWorkload(7, "FFN up/gate 5120x17408 affine-8 g64", 5120, 17408, 64, 8,
+                                     (1, 2, 4, 8, 16)),
 }
 
 
