@@ -219,10 +219,11 @@ int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t 
  * aligned, no overlap. Bit-exact; no scratch.
  *
  * w4a16_gemm_affine_split: out[M, N] = A[M, K] x W with W = s * q + b from those planes (qweight,
- * scales, biases as written above, for the original K). The activations are copied twice along
- * K into the stream's scratch buffer ([M, 2K] bf16) and the call runs as w4a16_gemm_affine over
- * 2K rows, with its accuracy contract (the bound sum |a| (|s q| + |b|) of the original codes).
- * M in 1..16; A, out and the other rules as w4a16_gemm_affine.
+ * scales, biases as written above, for the original K). The two planes run as a pair of
+ * matrices over the same activations in one launch, as w4a16_gemm_gate_up does, their two sums
+ * of a column added in the epilogue; the accuracy contract is w4a16_gemm_affine's, with the bound
+ * sum |a| (|s q| + |b|) of the original codes. M in 1..16; A, out, scratch and the other rules as
+ * w4a16_gemm_affine.
  */
 int w4a16_affine_split(const uint32_t *packed, int bits, const uint16_t *scales,
                        const uint16_t *biases, int group_size, int K, int N,

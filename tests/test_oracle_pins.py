@@ -94,18 +94,21 @@ def test_dequant_exhaustive_exact(orc):
     assert N == 63488
     g = 16
     K = 16 * g                                       # group gi has zero gi; row k has code k % 16
-    qweight = np.empty((K // 8, N), dtype=np.uint32)
-    qweight[0::2] = 0x76543210
-    qweight[1::2] = 0xFEDCBA98
-    scales = np.broadcast_to(fin[:N], (K // g, N)).copy()
-    qzeros = np.repeat((np.arange(16, dtype=np.uint32) * 0x11111111)[:, None], N // 8, axis=1)
-    w = orc.dequant(qweight, scales, qzeros, g)
     k = np.arange(K)
     d = (k % 16 - k // g).astype(np.float64)         # q - z
-    s = fin[:N].view(np.float16).astype(np.float64)
-    exact = d[:, None] * s[None, :]                   # exact in fp64 (<= 5 x 11 bits)
-    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)   # fits fp32
-    assert np.array_equal(w.astype(np.float64), exact)
+    C = N // 8                                       # the scales in 8 column blocks (bounded memory)
+    qweight = np.empty((K // 8, C), dtype=np.uint32)
+    qweight[0::2] = 0x76543210
+    qweight[1::2] = 0xFEDCBA98
+    qzeros = np.repeat((np.arange(16, dtype=np.uint32) * 0x11111111)[:, None], C // 8, axis=1)
+    for c0 in range(0, N, C):
+        blk = fin[c0:c0 + C]
+        scales = np.broadcast_to(blk, (K // g, C)).copy()
+        w = orc.dequant(qweight, scales, qzeros, g)
+        s = blk.view(np.float16).astype(np.float64)
+        exact = d[:, None] * s[None, :]               # exact in fp64 (<= 5 x 11 bits)
+        assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)   # fits fp32
+        assert np.array_equal(w.astype(np.float64), exact), c0
 
 
 # ---- the matmul against exact rational arithmetic -----------------------------------------

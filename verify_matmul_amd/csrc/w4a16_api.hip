@@ -229,20 +229,22 @@ struct Matrix {
 
 // One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick;
 // `up` non-null makes it a gated pair (w is the gate): out = silu(A x w) * (A x up), planned as
-// one 2N-column problem on 128-column tiles (64 output columns of each matrix). `dup_a`: A holds
-// K / 2 columns and is first copied twice along K into scratch (split affine planes).
+// one 2N-column problem on 128-column tiles (64 output columns of each matrix). Two affine
+// matrices (w and up both with biases) are summed instead: out = (A x w) + (A x up).
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
-              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream,
-              bool dup_a = false)
+              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream)
 {
     const uint32_t *qweight = w.qweight;
     const uint16_t *scales = w.scales;
     const uint32_t *qzeros = w.qzeros;
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
-    if (w.biases && (qzeros || up || idx))
-        return fail(W4A16_ERR_INVALID_ARG, "affine codes take no zero points, pair or fused pick");
-    if (w.biases && !aligned16(w.biases)) return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
+    if (w.biases && (qzeros || idx || (up && (up->qzeros || !up->biases))))
+        return fail(W4A16_ERR_INVALID_ARG, "affine codes take no zero points or fused pick, and pair only with affine codes");
+    if (!w.biases && up && up->biases)
+        return fail(W4A16_ERR_INVALID_ARG, "a GPTQ matrix does not pair with affine codes");
+    if ((w.biases && !aligned16(w.biases)) || (up && up->biases && !aligned16(up->biases)))
+        return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
     const ZeroMode zm = w.biases ? kAffine : qzeros ? kZeroPacked : kZeroSym;
     if (up) {
         rc = check_gemm_args(A, up->qweight, up->scales, up->qzeros, group_size, M, N, K, out, out_dtype);
@@ -268,6 +270,7 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
         a.qweight2 = up->qweight;
         a.scales2 = up->scales;
         a.qzeros2 = up->qzeros;
+        a.biases2 = up->biases;
     }
     a.out = out;
     a.M = M;
@@ -280,16 +283,14 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     a.scale_off = plan.scale_off;
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
-    if (split_k || plan.prep_a || idx || dup_a) {
+    if (split_k || plan.prep_a || idx) {
         // counters: [tile counters][argmax row keys (M x 64 bit)]
         const size_t tile = (size_t)tile_columns(plan.cols);
         const size_t tiles = ((size_t)NV + tile - 1) / tile;
         const size_t key_off = round_up(tiles * sizeof(uint32_t), 8);
         const size_t counter_bytes = key_off + 16 * sizeof(unsigned long long);
         const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
-        const size_t prep_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
-        const size_t dup_off = round_up(prep_bytes, 256);   // the duplicated activations [M, K]
-        const size_t act_bytes = dup_a ? dup_off + a16_bytes : prep_bytes;
+        const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
         rc = get_scratch(stream, counter_bytes, split_k ? (size_t)plan.splits * M * NV * sizeof(uint64_t) : 0,
                          act_bytes, split_k, &v);
@@ -299,12 +300,6 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
         a.stamp = v.stamp;
         a.A16 = static_cast<uint16_t *>(v.act);
         a.ashift = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
-        if (dup_a) {
-            uint16_t *dup = reinterpret_cast<uint16_t *>(static_cast<char *>(v.act) + dup_off);
-            const hipError_t e = launch_dup_halves(static_cast<const uint16_t *>(A), M, K / 2, dup, stream);
-            if (e != hipSuccess) return hip_fail(e, "activation copy launch");
-            a.A = dup;
-        }
         if (idx) {
             char *c = reinterpret_cast<char *>(v.counters);
             a.amax_keys = reinterpret_cast<unsigned long long *>(c + key_off);
@@ -482,13 +477,16 @@ int w4a16_affine_split(const uint32_t *packed, int bits, const uint16_t *scales,
 int w4a16_gemm_affine_split(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint16_t *biases,
                             int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
 {
-    if (!biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
-    if (K <= 0 || K > (1 << 29)) return fail(W4A16_ERR_INVALID_ARG, "K=%d", K);
-    if (group_size <= 0 || group_size % 32 || K % group_size)   // the planes meet on a group boundary
-        return fail(W4A16_ERR_INVALID_ARG, "K=%d is not a multiple of group_size=%d (a multiple of 32)", K, group_size);
-    Matrix w{qweight, scales, nullptr};
-    w.biases = biases;
-    return gemm_call(A, w, nullptr, group_size, M, N, 2 * K, out, out_dtype, 0, 0, 0, nullptr, stream, true);
+    if (!qweight || !scales || !biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (qweight, scales or biases)");
+    if (N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size)
+        return fail(W4A16_ERR_INVALID_ARG, "N=%d K=%d group_size=%d", N, K, group_size);
+    // the two planes as a pair of matrices over the same activations, summed per column
+    const size_t plane = (size_t)(K / 8) * N, groups = (size_t)(K / group_size) * N;
+    Matrix lo{qweight, scales, nullptr};
+    lo.biases = biases;
+    Matrix hi{qweight + plane, scales + groups, nullptr};
+    hi.biases = biases + groups;
+    return gemm_call(A, lo, &hi, group_size, M, N, K, out, out_dtype, 0, 0, 0, nullptr, stream);
 }
 
 int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t stream)

@@ -163,7 +163,7 @@ __global__ void affine_widen_kernel(const uint32_t *packed, int K, int N, uint32
 
 // Codes of kBits (5..8) bits split exactly into two 4-bit planes, q = 16 * hi + lo: rows
 // 0..K-1 of the output hold lo, rows K..2K-1 hold hi, so with scales s then 16 s and biases b
-// then 0 the 4-bit affine kernel over 2K rows computes s * q + b for every code. One thread per
+// then 0 the sum of the two planes' affine products is s * q + b for every code. One thread per
 // column and 32-row block, as in the widening above.
 template <int kBits>
 __global__ void affine_split_kernel(const uint32_t *packed, int K, int N, uint32_t *qweight)
@@ -210,21 +210,6 @@ __global__ void affine_split_groups_kernel(const uint16_t *scales, const uint16_
         scales_out[items + i] = (uint16_t)float_to_bf16_bits(bf16_bits_to_float(s) * 16.0f);
         biases_out[i] = biases[i];
         biases_out[items + i] = 0;
-    }
-}
-
-// dst[m][k] = src[m][k mod K] for k < 2K: the activations twice along K, 16 bytes per item.
-__global__ void dup_halves_kernel(const uint16_t *src, int M, int K, uint16_t *dst)
-{
-    const long long per_row = K / 8;
-    const long long items = (long long)M * per_row;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < items;
-         i += (long long)gridDim.x * blockDim.x) {
-        const long long m = i / per_row;
-        const long long c = i - m * per_row;
-        const uint4 v = *reinterpret_cast<const uint4 *>(src + m * K + c * 8);
-        *reinterpret_cast<uint4 *>(dst + m * 2 * K + c * 8) = v;
-        *reinterpret_cast<uint4 *>(dst + m * 2 * K + K + c * 8) = v;
     }
 }
 
@@ -277,13 +262,6 @@ hipError_t launch_affine_split(const uint32_t *packed, int bits, const uint16_t 
     const long long gitems = (long long)(K / g) * N;
     hipLaunchKernelGGL(affine_split_groups_kernel, dim3(grid_for(gitems, 256)), dim3(256), 0, s, scales, biases,
                        gitems, scales_out, biases_out);
-    return hipGetLastError();
-}
-
-hipError_t launch_dup_halves(const uint16_t *src, int M, int K, uint16_t *dst, hipStream_t s)
-{
-    const long long items = (long long)M * (K / 8);
-    hipLaunchKernelGGL(dup_halves_kernel, dim3(grid_for(items, 256)), dim3(256), 0, s, src, M, K, dst);
     return hipGetLastError();
 }
 

@@ -134,7 +134,8 @@ constexpr int gemm_min_waves()
 // output columns of the gate followed by the same 4 of the up projection, so a tile covers 64
 // output columns of both, the activations are staged and converted once for the two, and the
 // epilogue writes silu(gate) * up. Internally the pair is a 2N-column problem whose column c of
-// a tile is output column (c / 8) * 4 + c % 4 of matrix (c / 4) % 2.
+// a tile is output column (c / 8) * 4 + c % 4 of matrix (c / 4) % 2. A pair of affine matrices
+// (the low and high 4-bit planes of wider codes) is summed instead: out = (A x W) + (A x W2).
 // kZM (ZeroMode): for affine codes, w = s * q + b, the sum of a group is
 // s * sum(a * q) + b * sum(a): the codes go through the same exact conversion with zero point
 // 0, and sum(a) over the group comes from one more product per step against a fragment of ones
@@ -144,8 +145,9 @@ __global__ __launch_bounds__(kWK * 64)
 __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a16_gemm_kernel(GemmArgs p)
 {
     static_assert(!kDual || (kMfma && kC == 8), "gated pairs run on the matrix cores, 8 columns per lane");
-    static_assert(!kDual || kZM != kAffine, "gated pairs take GPTQ codes");
     constexpr bool kAff = kZM == kAffine;
+    // how a pair's two sums of one output column meet
+    auto combine = [](float g, float u) { return kAff ? g + u : silu_f32(g) * u; };
     constexpr bool kPreA = !kLdsA;
     constexpr int kTile = 16 * kC;      // columns per tile: kC adjacent columns per lane
     constexpr int kOutTile = kDual ? kTile / 2 : kTile;   // output columns per tile
@@ -251,6 +253,10 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
             if (c >= N) c = 0;
             load_to_lds4((j < 4 ? p.scales : p.scales2) + (size_t)gi * N + c, sc_lds + (size_t)b * 2);
             ++pre_loads;
+            if constexpr (kAff) {   // the biases in the same order
+                load_to_lds4((j < 4 ? p.biases : p.biases2) + (size_t)gi * N + c, b_lds + (size_t)b * 2);
+                ++pre_loads;
+            }
         }
     } else {   // scales (affine: and biases): kZW items of 8 columns per group (lanes past the last
         // item stay idle, so the LDS area holds exactly the wave's groups)
@@ -549,11 +555,11 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
 #pragma unroll
             for (int v = 0; v < (kDual ? 1 : kV); ++v) {
                 float x0 = tot[4 * v][r], x1 = tot[4 * v + 1][r], x2 = tot[4 * v + 2][r], x3 = tot[4 * v + 3][r];
-                if constexpr (kDual) {   // silu(gate) * up
-                    x0 = silu_f32(x0) * tot[4][r];
-                    x1 = silu_f32(x1) * tot[5][r];
-                    x2 = silu_f32(x2) * tot[6][r];
-                    x3 = silu_f32(x3) * tot[7][r];
+                if constexpr (kDual) {   // silu(gate) * up, or the sum of an affine pair
+                    x0 = combine(x0, tot[4][r]);
+                    x1 = combine(x1, tot[5][r]);
+                    x2 = combine(x2, tot[6][r]);
+                    x3 = combine(x3, tot[7][r]);
                 }
                 if (p.out_bf16) {
                     uint2 q;
@@ -639,7 +645,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
             const int oc = idx - m * kOutTile;
             const int n = tile * kOutTile + oc;
             const float *fin = red + (size_t)m * kTile + (oc >> 2) * 8 + (oc & 3);   // gate; up 4 further
-            if (n < N) store_out(m, n, silu_f32(fin[0]) * fin[4]);
+            if (n < N) store_out(m, n, combine(fin[0], fin[4]));
         }
     };
     if (p.splits == 1) {
@@ -831,6 +837,7 @@ template <bool kLdsA>
 hipError_t launch_pair(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     if (plan.cols != 8 || !plan.mfma) return hipErrorInvalidValue;
+    if (a.biases) return launch_wk<true, kAffine, kLdsA, 8, true>(a, plan, stream);
     return a.qzeros == nullptr ? launch_wk<true, kZeroSym, kLdsA, 8, true>(a, plan, stream)
                                : launch_wk<true, kZeroPacked, kLdsA, 8, true>(a, plan, stream);
 }

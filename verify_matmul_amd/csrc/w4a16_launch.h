@@ -57,6 +57,7 @@ struct GemmArgs {
     const uint32_t *qweight2;
     const uint16_t *scales2;
     const uint32_t *qzeros2;
+    const uint16_t *biases2;  // affine pair: the second matrix's biases; out = (A x W) + (A x W2)
     void *out;
     uint16_t *A16;            // [M, K] prepared activations (matrix-core path)
     int *ashift;              // [splits * waves_k, M] their rescale per K piece and row
@@ -180,8 +181,6 @@ hipError_t launch_affine_widen(const uint32_t *packed, int bits, int K, int N, u
 hipError_t launch_affine_split(const uint32_t *packed, int bits, const uint16_t *scales, const uint16_t *biases,
                                int g, int K, int N, uint32_t *qweight, uint16_t *scales_out, uint16_t *biases_out,
                                hipStream_t s);
-// dst [M, 2K] = src [M, K] twice along K (K % 8 == 0, 16-byte aligned rows).
-hipError_t launch_dup_halves(const uint16_t *src, int M, int K, uint16_t *dst, hipStream_t s);
 hipError_t launch_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q, hipStream_t s);
 hipError_t launch_dequant_f32(const uint32_t *qweight, const uint16_t *scales,
                               const uint32_t *qzeros, int g, int K, int N, float *w,
