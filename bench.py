@@ -359,8 +359,8 @@ def main():
     return 0
 
 
-def affine_bytes(M, K, N, g, bits=4):
-    return K * N * bits // 8 + 4 * (K // g) * N + 2 * M * K + 4 * M * N
+def affine_bytes(M, K, N, g, bits=4, matrices=1):
+    return matrices * (K * N * bits // 8 + 4 * (K // g) * N) + 2 * M * K + 4 * M * N
 
 
 def run_affine(args, lib):
@@ -370,10 +370,13 @@ def run_affine(args, lib):
     import verify_matmul_amd as vm
     from verify_matmul_amd import synth
 
-    if args.prefill or args.gate_up:
-        print("bench.py: --affine takes no --prefill or --gate-up", file=sys.stderr)
-        return 2
     bits = args.affine_bits
+    pair = args.gate_up   # the affine gated pair silu(A x W_gate) * (A x W_up)
+    if args.prefill or (pair and (bits != 4 or args.splits or args.waves_k or args.tile_cols)):
+        print("bench.py: --affine takes no --prefill; --affine --gate-up takes 4-bit codes and no launch knobs",
+              file=sys.stderr)
+        return 2
+    nmat = 2 if pair else 1
     if bits == 8 and (args.splits or args.waves_k or args.tile_cols):
         print("bench.py: --affine-bits 8 takes no launch knobs", file=sys.stderr)
         return 2
@@ -383,8 +386,14 @@ def run_affine(args, lib):
     K, N, g = wl.K, wl.N, wl.group
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    per_copy = affine_bytes(1, K, N, g, bits)
+    per_copy = affine_bytes(1, K, N, g, bits, nmat)
     R = max(2, math.ceil(POOL_BYTES / per_copy))
+    if pair:
+        xg = synth.make_affine_gate_inputs(wl)
+        gq0 = torch.from_numpy(np.ascontiguousarray(xg.packed).view(np.int32)).to(dev)
+        gs0 = torch.from_numpy(xg.scales.view(np.int16)).to(dev)
+        gb0 = torch.from_numpy(xg.biases.view(np.int16)).to(dev)
+        gates = [(gq0.clone(), gs0.clone(), gb0.clone()) for _ in range(R)]
     qw0 = torch.from_numpy(np.ascontiguousarray(x.packed).view(np.int32)).to(dev)   # 4-bit: the qweight layout
     sc0 = torch.from_numpy(x.scales.view(np.int16)).to(dev)
     bi0 = torch.from_numpy(x.biases.view(np.int16)).to(dev)
@@ -404,7 +413,11 @@ def run_affine(args, lib):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    if bits == 8:
+    if pair:
+        calls = [[(vp(a), vp(gates[r][0]), vp(gates[r][1]), vp(gates[r][2]), vp(qw), vp(sc), vp(bi), g, M, N, K,
+                   vp(outs[M]), 0, sp) for M in ms] for r, (qw, sc, bi, a, outs) in enumerate(pool)]
+        fn = lib.w4a16_gemm_affine_gate_up
+    elif bits == 8:
         calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, sp) for M in ms]
                  for qw, sc, bi, a, outs in pool]
         fn = lib.w4a16_gemm_affine_split
@@ -432,7 +445,7 @@ def run_affine(args, lib):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    value = sum(affine_bytes(M, K, N, g, bits) for M in ms) * args.steps / wall / 1e9
+    value = sum(affine_bytes(M, K, N, g, bits, nmat) for M in ms) * args.steps / wall / 1e9
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
            for _ in range(args.steps)]
@@ -443,7 +456,7 @@ def run_affine(args, lib):
     per_m, dom, dom_time = {}, None, -1.0
     for j, M in enumerate(ms):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
-        b = affine_bytes(M, K, N, g, bits)
+        b = affine_bytes(M, K, N, g, bits, nmat)
         us = float(np.mean(d))
         per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
@@ -466,14 +479,16 @@ def run_affine(args, lib):
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases{'; split planes' if bits == 8 else ''}), M in "
+        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases{'; split planes' if bits == 8 else ''})"
+                               f"{' gated pair silu(A x W_gate) * (A x W_up)' if pair else ''}, M in "
                                f"{','.join(map(str, ms))} (one call each per step)",
                    "K": K, "N": N, "group": g, "bits": wl.bits, "ms": list(ms), "out": "fp32",
                    "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20)},
-        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine{', split planes' if bits == 8 else ''}, M={dom})", "M": dom,
+        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine{', split planes' if bits == 8 else ''}{', gated pair' if pair else ''}, M={dom})", "M": dom,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": load_traffic(f"ffn_up_affine{bits}", dom), "launches": args.steps,
+                     "traffic": load_traffic(f"ffn_up_affine{bits}" + ("_gate_up" if pair else ""), dom),
+                     "launches": args.steps,
                      "bytes_per_launch": bdom, "us_per_launch": round(us_dom, 3),
                      "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
         "per_m": per_m,
@@ -486,9 +501,13 @@ def run_affine(args, lib):
         while elapsed < args.cpu_seconds or reps == 0:
             for M in ms:
                 t = time.perf_counter()
-                oracle.affine_gemm(x.act[:M], x.packed, x.bits, x.scales, x.biases, g)
+                if pair:
+                    oracle.affine_gate_up(x.act[:M], (xg.packed, 4, xg.scales, xg.biases),
+                                          (x.packed, 4, x.scales, x.biases), g)
+                else:
+                    oracle.affine_gemm(x.act[:M], x.packed, x.bits, x.scales, x.biases, g)
                 elapsed += time.perf_counter() - t
-                nbytes += affine_bytes(M, K, N, g, bits)
+                nbytes += affine_bytes(M, K, N, g, bits, nmat)
             reps += 1
         rec["cpu_baseline"] = {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads,
                                "kind": "oracle",

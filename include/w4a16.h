@@ -192,6 +192,18 @@ int w4a16_gemm_affine_ex(const void *A, const uint32_t *qweight, const uint16_t 
                          int out_dtype, int splits, int waves_k, int tile_cols, hipStream_t stream);
 
 /*
+ * The gated feed-forward input of two affine matrices, out = silu(A x W_gate) * (A x W_up), each W
+ * = scale * q + bias as in w4a16_gemm_affine (4-bit codes, bf16 scales and biases, same shape):
+ * the operation, launch and scratch of w4a16_gemm_gate_up, each product under w4a16_gemm_affine's
+ * accuracy contract (carried through silu and the product as for w4a16_gemm_gate_up).
+ */
+int w4a16_gemm_affine_gate_up(const void *A, const uint32_t *qweight_gate,
+                              const uint16_t *scales_gate, const uint16_t *biases_gate,
+                              const uint32_t *qweight_up, const uint16_t *scales_up,
+                              const uint16_t *biases_up, int group_size, int M, int N, int K,
+                              void *out, int out_dtype, hipStream_t stream);
+
+/*
  * Codes of `bits` = 1..4 bits rewritten as the 4-bit codes w4a16_gemm_affine reads, each keeping
  * its value (scales and biases are unchanged), as TensorFold PR #859 first ran 2 and 3-bit
  * checkpoints on its 4-bit tiles. Input layout: for column n the codes of rows 0, 1, 2, ... form

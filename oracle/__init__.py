@@ -200,3 +200,11 @@ def affine_gemm(act, packed, bits: int, scales, biases, group: int,
     _check(_load().w4o_affine_gemm(_ptr(a), _ptr(pk), bits, _ptr(sc), _ptr(bi), group, M, N, K,
                                    _ptr(cc), C, _ptr(y), _ptr(b)), "affine_gemm")
     return y, b
+
+
+def affine_gate_up(act, gate, up, group: int, cols: Optional[Sequence[int]] = None):
+    """silu(A x W_gate) * (A x W_up) for affine matrices; gate and up are (packed, bits, scales,
+    biases). Returns (h, y_gate, bound_gate, y_up, bound_up), all fp64."""
+    yg, bg = affine_gemm(act, gate[0], gate[1], gate[2], gate[3], group, cols)
+    yu, bu = affine_gemm(act, up[0], up[1], up[2], up[3], group, cols)
+    return silu_mul(yg, yu), yg, bg, yu, bu

@@ -191,3 +191,43 @@ def test_affine8_ffn_workload(gu, M):
     y_ref, bound = oracle.affine_gemm(x.act[:M], x.packed, 8, x.scales, x.biases, x.group, cols)
     frac = parity.check_close(out.cpu().numpy().astype(np.float64)[:, cols], y_ref, bound, f"affine8 ffn M={M}")
     gu.say(f"[affine8 ffn] M={M} worst err/tol {frac:.3e}")
+
+
+def _gate_up_on_device(gu, gate, up, M, out_dtype=torch.float32):
+    dg = [gu.dev_u32(synth.pack_rows(oracle.affine_unpack(gate.packed, gate.bits, gate.K))),
+          gu.dev_u16(gate.scales), gu.dev_u16(gate.biases)]
+    du = [gu.dev_u32(synth.pack_rows(oracle.affine_unpack(up.packed, up.bits, up.K))),
+          gu.dev_u16(up.scales), gu.dev_u16(up.biases)]
+    out = torch.empty((M, up.N), dtype=out_dtype, device=gu.DEV)
+    vm.w4a16_gemm_affine_gate_up(gu.dev_u16(up.act)[:M], tuple(dg), tuple(du), up.group, out)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("K,N,g", [(512, 200, 64), (2048, 520, 64), (1024, 1032, 128)])
+def test_affine_gate_up_parity(gu, K, N, g):
+    gate = synth.make_affine_random(700 + K % 97, 16, K, N, g, 4)
+    up = synth.make_affine_random(701 + K % 97, 16, K, N, g, 4)
+    up = synth.AffineInputs(up.packed, 4, up.scales, up.biases, gate.act, g)
+    for M in (1, 2, 5, 16):
+        gu.say(f"[affine gate_up] K={K} N={N} g={g} M={M}")
+        h = _gate_up_on_device(gu, gate, up, M)
+        ref = oracle.affine_gate_up(gate.act[:M], (gate.packed, 4, gate.scales, gate.biases),
+                                    (up.packed, 4, up.scales, up.biases), g)
+        frac = parity.check_gate_up(h, *ref, f"affine gate_up K={K} M={M}")
+        hb = _gate_up_on_device(gu, gate, up, M, torch.bfloat16)
+        assert np.array_equal(hb, torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).double().numpy())
+    gu.say(f"  worst err/tol {frac:.3e}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_affine_gate_up_ffn_workload(gu, M):
+    up = synth.make_affine_inputs("ffn_up_affine4")
+    gate = synth.make_affine_gate_inputs("ffn_up_affine4")
+    h = _gate_up_on_device(gu, gate, up, M)
+    rng = np.random.default_rng(20 + M)
+    cols = np.unique(np.concatenate([rng.choice(up.N, 800, replace=False), np.arange(up.N - 64, up.N)]))
+    ref = oracle.affine_gate_up(up.act[:M], (gate.packed, 4, gate.scales, gate.biases),
+                                (up.packed, 4, up.scales, up.biases), up.group, cols)
+    frac = parity.check_gate_up(h[:, cols], *ref, f"affine ffn gate_up M={M}")
+    gu.say(f"[affine gate_up ffn] M={M} worst err/tol {frac:.3e}")

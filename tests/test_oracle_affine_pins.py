@@ -160,3 +160,21 @@ def test_affine_oracle_rejects_bad_arguments(orc):
         a = list(args)
         a[i] = bad
         assert lib.w4o_affine_gemm(*a) == -1, (i, bad)
+
+
+def test_affine_gate_up_orientation(orc):
+    """Scales 0 make every weight its bias: gate biases 1 give y_gate = sum(a), up biases 2 give
+    y_up = 2 sum(a), so h = silu(sum a) * 2 sum(a) -- and not silu(2 sum a) * sum(a)."""
+    K, N, g = 64, 8, 32
+    rng = np.random.default_rng(8)
+    act = synth.f32_to_bf16_bits(rng.standard_normal((2, K)).astype(np.float32))
+    pk = synth.pack_stream(rng.integers(0, 16, size=(K, N), dtype=np.uint8), 4)
+    zs = np.zeros((K // g, N), np.uint16)
+    one, two = np.full_like(zs, 0x3F80), np.full_like(zs, 0x4000)   # bf16 1.0 and 2.0
+    h, yg, _, yu, _ = orc.affine_gate_up(act, (pk, 4, zs, one), (pk, 4, zs, two), g)
+    sa = _bf16(act).sum(axis=1)[:, None] * np.ones((1, N))
+    assert np.allclose(yg, sa, rtol=1e-15, atol=1e-15) and np.allclose(yu, 2 * sa, rtol=1e-15, atol=1e-15)
+    expect = sa / (1 + np.exp(-sa)) * 2 * sa
+    assert np.allclose(h, expect, rtol=1e-14, atol=1e-15)
+    swapped = 2 * sa / (1 + np.exp(-2 * sa)) * sa
+    assert not np.allclose(h, swapped, rtol=1e-6)

@@ -16,7 +16,8 @@ __all__ = [
     "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax",
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
-    "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "EXPORTS",
+    "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split",
+    "w4a16_gemm_affine_gate_up", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,7 @@ _lib = None
 EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
     "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
-    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version",
 )
 
@@ -63,6 +64,7 @@ def load():
     lib.w4a16_affine_widen.argtypes = [P, I, I, I, P, P]
     lib.w4a16_affine_split.argtypes = [P, I, P, P, I, I, I, P, P, P, P]
     lib.w4a16_gemm_affine_split.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_affine_gate_up.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_plan.argtypes = [I, I, I, I, P, P, P, P]
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
@@ -218,6 +220,32 @@ def w4a16_gemm_affine(A, qweight, scales, biases, group_size, out, splits=0, wav
     else:
         rc = load().w4a16_gemm_affine(*args, _stream(stream))
     _check(rc, "w4a16_gemm_affine")
+    return out
+
+
+def w4a16_gemm_affine_gate_up(A, gate, up, group_size, out, stream=None):
+    """out = silu(A x W_gate) * (A x W_up) for affine matrices; gate and up are
+    (qweight, scales, biases) triples (4-bit codes, bf16 scales and biases)."""
+    M, K = A.shape
+    N = gate[0].shape[1]
+    _sb = (torch.bfloat16, torch.int16, torch.uint16)
+    for name, (qw, sc, bi) in (("gate", gate), ("up", up)):
+        if qw.shape[0] * 8 != K or qw.shape[1] != N:
+            raise ValueError(f"{name} qweight {tuple(qw.shape)} is not [{K // 8}, {N}]")
+        if tuple(sc.shape) != (K // group_size, N) or tuple(bi.shape) != tuple(sc.shape):
+            raise ValueError(f"{name} scales and biases must be [{K // group_size}, {N}]")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out {tuple(out.shape)} is not [{M}, {N}]")
+    dt = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}.get(out.dtype)
+    if dt is None:
+        raise TypeError("out must be float32 or bfloat16")
+    ptrs = []
+    for qw, sc, bi in (gate, up):
+        ptrs += [_ptr(qw, "qweight", _I32), _ptr(sc, "scales", _sb), _ptr(bi, "biases", _sb)]
+    _check(load().w4a16_gemm_affine_gate_up(_ptr(A, "A", _sb), *ptrs, int(group_size), M, N, K,
+                                            _ptr(out, "out", (torch.float32, torch.bfloat16)), dt,
+                                            _stream(stream)),
+           "w4a16_gemm_affine_gate_up")
     return out
 
 

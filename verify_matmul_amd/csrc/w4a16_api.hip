@@ -229,10 +229,11 @@ struct Matrix {
 
 // One GEMM call: check, plan, take scratch, launch. `idx` non-null adds the fused greedy pick;
 // `up` non-null makes it a gated pair (w is the gate): out = silu(A x w) * (A x up), planned as
-// one 2N-column problem on 128-column tiles (64 output columns of each matrix). Two affine
-// matrices (w and up both with biases) are summed instead: out = (A x w) + (A x up).
+// one 2N-column problem on 128-column tiles (64 output columns of each matrix). `pair_sum` adds
+// the pair's two products instead: out = (A x w) + (A x up).
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
-              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream)
+              int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream,
+              bool pair_sum = false)
 {
     const uint32_t *qweight = w.qweight;
     const uint16_t *scales = w.scales;
@@ -271,6 +272,7 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
         a.scales2 = up->scales;
         a.qzeros2 = up->qzeros;
         a.biases2 = up->biases;
+        a.pair_sum = pair_sum ? 1 : 0;
     }
     a.out = out;
     a.M = M;
@@ -486,7 +488,20 @@ int w4a16_gemm_affine_split(const void *A, const uint32_t *qweight, const uint16
     lo.biases = biases;
     Matrix hi{qweight + plane, scales + groups, nullptr};
     hi.biases = biases + groups;
-    return gemm_call(A, lo, &hi, group_size, M, N, K, out, out_dtype, 0, 0, 0, nullptr, stream);
+    return gemm_call(A, lo, &hi, group_size, M, N, K, out, out_dtype, 0, 0, 0, nullptr, stream, true);
+}
+
+int w4a16_gemm_affine_gate_up(const void *A, const uint32_t *qweight_gate, const uint16_t *scales_gate,
+                              const uint16_t *biases_gate, const uint32_t *qweight_up, const uint16_t *scales_up,
+                              const uint16_t *biases_up, int group_size, int M, int N, int K, void *out,
+                              int out_dtype, hipStream_t stream)
+{
+    if (!biases_gate || !biases_up) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
+    Matrix gate{qweight_gate, scales_gate, nullptr};
+    gate.biases = biases_gate;
+    Matrix up{qweight_up, scales_up, nullptr};
+    up.biases = biases_up;
+    return gemm_call(A, gate, &up, group_size, M, N, K, out, out_dtype, 0, 0, 0, nullptr, stream);
 }
 
 int w4a16_affine_widen(const uint32_t *packed, int bits, int K, int N, uint32_t *qweight, hipStream_t stream)

@@ -134,8 +134,8 @@ constexpr int gemm_min_waves()
 // output columns of the gate followed by the same 4 of the up projection, so a tile covers 64
 // output columns of both, the activations are staged and converted once for the two, and the
 // epilogue writes silu(gate) * up. Internally the pair is a 2N-column problem whose column c of
-// a tile is output column (c / 8) * 4 + c % 4 of matrix (c / 4) % 2. A pair of affine matrices
-// (the low and high 4-bit planes of wider codes) is summed instead: out = (A x W) + (A x W2).
+// a tile is output column (c / 8) * 4 + c % 4 of matrix (c / 4) % 2. With p.pair_sum the pair is
+// summed instead, out = (A x W) + (A x W2): the low and high 4-bit planes of wider affine codes.
 // kZM (ZeroMode): for affine codes, w = s * q + b, the sum of a group is
 // s * sum(a * q) + b * sum(a): the codes go through the same exact conversion with zero point
 // 0, and sum(a) over the group comes from one more product per step against a fragment of ones
@@ -146,8 +146,9 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
 {
     static_assert(!kDual || (kMfma && kC == 8), "gated pairs run on the matrix cores, 8 columns per lane");
     constexpr bool kAff = kZM == kAffine;
-    // how a pair's two sums of one output column meet
-    auto combine = [](float g, float u) { return kAff ? g + u : silu_f32(g) * u; };
+    // how a pair's two sums of one output column meet (uniform over the launch)
+    const bool pair_sum = p.pair_sum != 0;
+    auto combine = [pair_sum](float g, float u) { return pair_sum ? g + u : silu_f32(g) * u; };
     constexpr bool kPreA = !kLdsA;
     constexpr int kTile = 16 * kC;      // columns per tile: kC adjacent columns per lane
     constexpr int kOutTile = kDual ? kTile / 2 : kTile;   // output columns per tile

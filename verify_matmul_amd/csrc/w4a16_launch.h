@@ -57,7 +57,8 @@ struct GemmArgs {
     const uint32_t *qweight2;
     const uint16_t *scales2;
     const uint32_t *qzeros2;
-    const uint16_t *biases2;  // affine pair: the second matrix's biases; out = (A x W) + (A x W2)
+    const uint16_t *biases2;  // affine pair: the second matrix's biases
+    int pair_sum;             // pair: 1 -> out = (A x W) + (A x W2) (split planes); 0 -> silu(gate) * up
     void *out;
     uint16_t *A16;            // [M, K] prepared activations (matrix-core path)
     int *ashift;              // [splits * waves_k, M] their rescale per K piece and row

@@ -200,6 +200,8 @@ def pack_cols(codes: np.ndarray) -> np.ndarray:
 #   biases   bf16   [K/g, N]        stored as uint16 bit patterns
 
 _T_AFF_CODES, _T_AFF_SCALES, _T_AFF_BIASES, _T_AFF_ACT = 11, 12, 13, 14
+# the gate matrix beside an affine up projection: its own draws
+_T_AFF_CODES2, _T_AFF_SCALES2, _T_AFF_BIASES2 = 15, 16, 17
 
 
 @dataclass
@@ -282,3 +284,14 @@ def make_affine_random(seed: int, M: int, K: int, N: int, group: int, bits: int,
     packed, scales, biases = draw_affine(rng, rng, rng, K, N, group, bits)
     act = draw_activations(rng, M, K, sigma, 0.0, 1.0)
     return AffineInputs(packed, bits, scales, biases, act, group)
+
+
+def make_affine_gate_inputs(wl: AffineWorkload | str) -> AffineInputs:
+    """The gate matrix that pairs with ``make_affine_inputs(wl)`` (the up projection): same shape
+    and distributions, its own draws, the same activations."""
+    if isinstance(wl, str):
+        wl = AFFINE_WORKLOADS[wl]
+    up = make_affine_inputs(wl)
+    packed, scales, biases = draw_affine(_rng(wl.index, _T_AFF_CODES2), _rng(wl.index, _T_AFF_SCALES2),
+                                         _rng(wl.index, _T_AFF_BIASES2), wl.K, wl.N, wl.group, wl.bits)
+    return AffineInputs(packed, wl.bits, scales, biases, up.act, wl.group)
