@@ -16,7 +16,10 @@ Timed regions (all on the library's stream, inputs resident in HBM):
   1. K steps back to back -> `value` (whole-step throughput, wall clock between synchronizes);
   2. the same K steps with a HIP event pair around every launch -> `per_m` (us per call);
   3. the step's dominant call alone, K launches back to back between one event pair ->
-     `roofline.achieved` (algorithmic bytes per launch / average launch duration).
+     `roofline.achieved` (algorithmic bytes per launch / average launch duration);
+  4. context only: that call on one weight copy, cache-resident (`context.cache_resident`,
+     L2/MALL, not HBM), and a plain device copy of one weight copy per launch
+     (`context.copy_ceiling`, bytes read + written).
 `roofline.traffic` is the HBM bytes per launch of that call from the committed rocprofv3 counter
 summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or null when the
 kernel sources changed since the counters were taken.
@@ -326,6 +329,32 @@ def main():
     achieved = dm["bytes"] / us_dom / 1e3   # GB/s
     traffic = load_traffic(args.workload + ("_gate_up" if pair else ""), dom)
 
+    # context only, never `value`: (a) the dominant launch on one weight copy K times, which then
+    # stays in the L2s and the 256 MB last-level cache (a cache-resident rate, not an HBM one);
+    # (b) a plain device copy of one rotating weight copy per launch in this process (its bytes
+    # read plus written), as the streaming ceiling of plain data movement on these buffers
+    def back_to_back(launch):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for i in range(args.steps):
+            launch(i)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        return c0.elapsed_time(c1) * 1e3 / args.steps
+
+    resident_us = back_to_back(lambda i: fn(*calls[0][jd][1]))
+    sink = torch.empty_like(pool[0][0])
+    read_bytes = pool[0][0].numel() * 4
+    read_us = back_to_back(lambda i: sink.copy_(pool[1 + i % (R - 1)][0]))
+    context = {"cache_resident": {"what": "the dominant launch on one weight copy, back to back: L2/MALL, not HBM",
+                                  "us_per_launch": round(resident_us, 3),
+                                  "GBps": round(dm["bytes"] / resident_us / 1e3, 1)},
+               "copy_ceiling": {"what": "device copy of one rotating weight copy per launch (torch copy_), "
+                                        "bytes read + written",
+                                "bytes": 2 * read_bytes, "us_per_launch": round(read_us, 3),
+                                "GBps": round(2 * read_bytes / read_us / 1e3, 1)}}
+
     rec = {
         "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
         "value": round(value, 1),
@@ -352,6 +381,7 @@ def main():
                      "launches": args.steps, "bytes_per_launch": dm["bytes"],
                      "us_per_launch": round(us_dom, 3), "us_per_launch_lone_event_pair": dm["us_per_call"]},
         "per_m": per_m,
+        "context": context,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp)
