@@ -268,7 +268,8 @@ def main():
         b = algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat)
         us = float(np.mean(d))
         kern, spl, wk, tcols = vm.w4a16_plan(M, N, K, g)
-        per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+        per_m[str(M)] = {"us_per_call": round(us, 3), "us_median": round(float(np.median(d)), 3),
+                         "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
                          "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
         if pair:   # 128-column tiles of the 2N-wide pair (64 output columns of each matrix)
@@ -488,7 +489,8 @@ def run_affine(args, lib):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
         b = affine_bytes(M, K, N, g, bits, nmat)
         us = float(np.mean(d))
-        per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+        per_m[str(M)] = {"us_per_call": round(us, 3), "us_median": round(float(np.median(d)), 3),
+                         "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
                          "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
         if float(np.sum(d)) > dom_time:
@@ -620,7 +622,8 @@ def run_prefill(args, lib):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
         us = float(np.mean(d))
         f = 2.0 * nmat * M * N * K
-        per_m[str(M)] = {"us_per_call": round(us, 3), "us_p10": round(float(np.percentile(d, 10)), 3),
+        per_m[str(M)] = {"us_per_call": round(us, 3), "us_median": round(float(np.median(d)), 3),
+                         "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "TFLOPs": round(f / us / 1e6, 1),
                          "frac_of_peak": round(f / us / 1e6 / PEAK_F16_TFLOPS, 4), "flops": f,
                          "hbm_GBps_weights_once": round(algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat) / us / 1e3, 1)}
