@@ -98,7 +98,30 @@ def parse():
     return p.parse_args()
 
 
-def cpu_baseline(wl, inp, ms, seconds, gate=None):
+def cpu_one_thread(workload, ms, seconds):
+    """The same oracle on one host thread over whole steps (one call per row count in `ms`): a
+    child process started with OMP_NUM_THREADS=1 (OpenMP fixes its thread count when it starts)
+    that runs only the CPU oracle on its own copy of the seeded inputs. Returns steps, seconds."""
+    import subprocess
+    code = (f"import sys, time, json\nsys.path.insert(0, {ROOT!r})\n"
+            "import oracle\nfrom verify_matmul_amd import synth\n"
+            f"oracle._load()\ninp = synth.make_inputs(synth.WORKLOADS[{workload!r}])\n"
+            "n, el = 0, 0.0\n"
+            f"while el < {seconds} or n == 0:\n"
+            f"    for M in {tuple(ms)!r}:\n"
+            "        t = time.perf_counter()\n"
+            "        oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, inp.group)\n"
+            "        el += time.perf_counter() - t\n"
+            "    n += 1\n"
+            "print(json.dumps({'calls': n, 'seconds': el}))\n")
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"one-thread oracle run failed: {r.stderr[-500:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def cpu_baseline(wl, inp, ms, seconds, gate=None, one=None):
     """The CPU oracle, as it is, on this host's cores: the whole step repeated for ~`seconds`."""
     import oracle
     oracle._load()
@@ -115,9 +138,18 @@ def cpu_baseline(wl, inp, ms, seconds, gate=None):
             elapsed += time.perf_counter() - t
             nbytes += algorithmic_bytes(M, wl.K, wl.N, wl.group, wl.symmetric, matrices=1 if gate is None else 2)
         reps += 1
-    return {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full step(s) of the workload (M={','.join(map(str, ms))}, all {wl.N} columns), "
-                      f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)"}
+    rec = {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} full step(s) of the workload (M={','.join(map(str, ms))}, all {wl.N} columns), "
+                     f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)"}
+    if one is not None:   # the same steps on one thread (measured before any GPU work)
+        step_b = sum(algorithmic_bytes(M, wl.K, wl.N, wl.group, wl.symmetric) for M in ms)
+        v1 = step_b * one["calls"] / one["seconds"] / 1e9
+        rec["one_thread"] = {"value": round(v1, 4), "unit": "GB/s", "cores": 1,
+                             "sample": f"{one['calls']} full step(s), {one['seconds']:.1f} s of oracle time"}
+        # what the threads above actually bought on this host (its CPU share may be smaller
+        # than its thread count)
+        rec["speedup_over_one_thread"] = round(rec["value"] / v1, 2)
+    return rec
 
 
 def load_traffic(workload, M, kernel="w4a16_gemm_kernel"):
@@ -152,6 +184,15 @@ def main():
     import torch
     import verify_matmul_amd as vm
     from verify_matmul_amd import synth
+
+    # the one-thread oracle figure runs in a child process, started here before this process
+    # loads the library or touches the device
+    one_thread = None
+    if not (args.no_cpu_baseline or args.calibrate or args.affine or args.prefill or args.gate_up):
+        w0 = synth.WORKLOADS[args.workload]
+        ms0 = tuple(int(x) for x in args.ms.split(",")) if args.ms else w0.ms
+        if algorithmic_bytes(1, w0.K, w0.N, w0.group, w0.symmetric) <= 128 * 2 ** 20:   # not the output layer
+            one_thread = cpu_one_thread(args.workload, ms0, max(1.0, args.cpu_seconds / 4))
 
     if args.calibrate:
         n = args.calibrate * 2 ** 20 // 4
@@ -385,7 +426,7 @@ def main():
         "context": context,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp)
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp, one_thread)
     print(json.dumps(rec), flush=True)
     return 0
 
