@@ -22,6 +22,9 @@ FLAGS = [
     # split-K arrival count is read only at the end of the kernel), not a wave-aggregated one
     # waited for on the spot
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    # loop headers on 64-byte instruction-cache lines (the same box, the two builds alternated:
+    # FFN down M = 1 / 4 / 8 0.12-0.2 us faster, FFN up M = 2 0.15, no row count slower)
+    "-falign-loops=64",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
