@@ -30,9 +30,9 @@ FLAGS = [
 
 
 def source_hash() -> str:
-    """Hash of every HIP source and header the library is built from."""
+    """Hash of every HIP source and header the library is built from, and of its compiler flags."""
     import hashlib
-    h = hashlib.sha256()
+    h = hashlib.sha256("\0".join(FLAGS[:-1]).encode())   # the include path (last) depends on the checkout
     names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
     for n in names + ["../../include/w4a16.h"]:
         with open(os.path.join(CSRC, n), "rb") as f:
