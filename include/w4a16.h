@@ -29,12 +29,18 @@
  *     device work was enqueued. The library never aborts and never prints: w4a16_last_error()
  *     returns a description of the last non-OK status of the calling thread.
  *   - The library owns one scratch buffer per (device, stream) for split-K partial sums, tile
- *     counters, prepared activations and the fused pick's row keys. It is allocated (with
- *     hipMalloc, then zeroed) on the first call that needs it on that stream (and grown
- *     if a later call needs more), so warm a stream up before timing or capturing it. Calls on
+ *     counters and slice flags, prepared activations and the fused pick's row keys. It is
+ *     allocated (with hipMalloc, then zeroed) on the first call that needs it on that stream; a
+ *     later call that needs more gets a new, larger buffer and the old one is kept until
+ *     w4a16_release_scratch (a graph captured earlier may still use it). Every call leaves the
+ *     counters, flags and keys zero and writes every partial sum before it reads it, so no
+ *     state carries from one call to the next: calls may be captured into a HIP graph and
+ *     replayed any number of times. A call that would have to allocate while its stream is
+ *     being captured returns W4A16_ERR_UNSUPPORTED instead, so run the same calls on the stream
+ *     once before capturing it (that also keeps allocation out of timed regions). Calls on
  *     different streams never share scratch; calls on one stream are ordered, and calls that
- *     run concurrently on one stream's scratch (e.g. the same stream used from two graphs
- *     replayed at once) are not supported.
+ *     run concurrently on one stream's scratch (e.g. two graphs captured from one stream and
+ *     replayed at once on different streams) are not supported.
  *   - Results are deterministic: the same inputs and launch give bit-identical outputs (the
  *     split-K partials are summed in a fixed order, never with float atomics).
  */
@@ -51,7 +57,8 @@ extern "C" {
 typedef enum {
     W4A16_OK = 0,
     W4A16_ERR_INVALID_ARG = -1,   /* null pointer, size or divisibility violation, bad dtype */
-    W4A16_ERR_UNSUPPORTED = -2,   /* pointer not 16-byte aligned, or qweight of 2^32 words or more */
+    W4A16_ERR_UNSUPPORTED = -2,   /* pointer not 16-byte aligned, qweight of 2^32 words or more, or
+                                     scratch needed while the stream is being captured */
     W4A16_ERR_HIP = -3,           /* a HIP runtime call failed; see w4a16_last_error() */
     W4A16_ERR_NO_MEMORY = -4      /* the scratch buffer could not be allocated */
 } w4a16_status;
@@ -270,6 +277,9 @@ int w4a16_release_scratch(void);
 const char *w4a16_status_string(int status);
 const char *w4a16_last_error(void);
 int w4a16_version(void);   /* 100 * major + minor */
+/* Hash of the sources and compiler flags the library was built from (16 hex digits); the
+ * Python binding refuses a library whose hash differs from its sources'. */
+const char *w4a16_source_hash(void);
 
 #ifdef __cplusplus
 }

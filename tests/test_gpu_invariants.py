@@ -112,6 +112,34 @@ def test_wide_dynamic_range_rows(gu):
             parity.check_close(d.run(M, splits=splits, waves_k=wk), y_ref, bound, f"range M={M}")
 
 
+def test_activation_span_at_the_documented_edge(gu):
+    """The accuracy contract holds for rows whose nonzero activations span up to 2^29 within one
+    K slice. Each row carries one outlier 2^29 times larger than its other entries (which lie in
+    [1, 2)), and in about half of the columns the outlier's code equals its zero point, so the
+    outlier contributes nothing there and the bound is made of the small entries alone: they
+    must reach the matrix cores without losing a bit for those columns to pass."""
+    rng = np.random.default_rng(27)
+    K, N, g = 1024, 512, 64
+    a = (1.0 + rng.random((16, K))).astype(np.float32) * rng.choice([-1.0, 1.0], size=(16, K)).astype(np.float32)
+    pos = rng.integers(0, K, size=16)
+    a[np.arange(16), pos] *= np.float32(2.0 ** 29)
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)
+    half = rng.random(N) < 0.5
+    for m in range(16):   # the outlier's code equals the zero point in the chosen columns
+        codes[pos[m], half] = zeros[pos[m] // g, half]
+    inp = synth.Inputs(synth.pack_rows(codes), synth.draw_scales(rng, (K // g, N), 0.002, 0.02),
+                       synth.pack_cols(zeros), synth.f32_to_bf16_bits(a), g)
+    d = gu.DevInputs(inp)
+    for M in (1, 4, 16):
+        y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
+        for splits, wk, cols in ((0, 0, 0), (1, 1, 0), (4, 2, 0), (2, 4, 128)):
+            gu.say(f"[span 2^29] M={M} splits={splits} waves_k={wk} tile_cols={cols}")
+            frac = parity.check_close(d.run(M, splits=splits, waves_k=wk, tile_cols=cols), y_ref, bound,
+                                      f"span M={M} {splits}/{wk}/{cols}")
+            gu.say(f"  worst err/tol {frac:.3e}")
+
+
 def test_power_of_two_activation_scaling_is_exact(gu):
     """Scaling every activation by 2^k scales every output by exactly 2^k: the per-slice rescale
     into fp16 is exact, so it absorbs any power of two, from slices far below fp16's range to

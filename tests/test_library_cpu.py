@@ -209,3 +209,14 @@ def test_affine_split_rejects_bad_arguments(lib):
         return lib.w4a16_gemm_affine_split(A, Q, S, b, g, M, 256, K, O, 0, None)
     assert gemm_split(b=None) == -1 and gemm_split(K=96) == -1 and gemm_split(M=17) == -1
     assert gemm_split(K=96, g=64) == -1 and b"group_size" in lib.w4a16_last_error()
+
+
+def test_load_refuses_a_library_built_from_other_sources(monkeypatch):
+    """The binding compares the hash embedded at build time with the hash of the sources beside it."""
+    import verify_matmul_amd as vm
+    from verify_matmul_amd import _build
+    assert vm.load().w4a16_source_hash().decode() == _build.source_hash()
+    monkeypatch.setattr(vm, "_lib", None)
+    monkeypatch.setattr(_build, "source_hash", lambda: "0" * 16)
+    with pytest.raises(ImportError, match="other sources"):
+        vm.load()

@@ -29,7 +29,7 @@ EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
     "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
     "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
-    "w4a16_last_error", "w4a16_version",
+    "w4a16_last_error", "w4a16_version", "w4a16_source_hash",
 )
 
 OUT_F32 = 0
@@ -51,6 +51,13 @@ def load():
         raise ImportError(f"{lib_path} is missing: build it with __graft_entry__.build() "
                           f"(hipcc --offload-arch=gfx950); there is no fallback implementation")
     lib = ctypes.CDLL(lib_path)
+    from . import _build
+    lib.w4a16_source_hash.argtypes = []
+    lib.w4a16_source_hash.restype = ctypes.c_char_p
+    built, want = lib.w4a16_source_hash().decode(), _build.source_hash()
+    if built != want:
+        raise ImportError(f"{lib_path} was built from other sources (hash {built}, these sources {want}): "
+                          f"rebuild it with __graft_entry__.build()")
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]

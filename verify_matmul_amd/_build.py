@@ -50,7 +50,8 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into verify_matmul_amd/libw4a16.so (always recompiles)."""
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    cmd = [hipcc(), *FLAGS, f'-DW4A16_SOURCE_HASH="{source_hash()}"', *[os.path.join(CSRC, s) for s in SOURCES],
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 #include <utility>
+#include <vector>
 
 #include "w4a16.h"
 #include "w4a16_launch.h"
@@ -36,15 +37,22 @@ int hip_fail(hipError_t e, const char *what)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- per-(device, stream) scratch -------------------------------------------------------------
-// One block per (device, stream): [counters][stamped partials][prepared activations]. The block
-// is zeroed when it is allocated. Kernels leave every counter at zero. Split-K partials carry
-// the stamp of the call that wrote them; each split-K call takes the next stamp, and when the
-// 32-bit stamps run out the partials are zeroed again, so an old stamp never matches a new one.
-// Prepared activations are rewritten by every matrix-core call before its GEMM reads them.
+// One block per (device, stream) in three regions:
+//   [0] control words: split-K tile counters and slice flags, the fused pick's row keys and the
+//       argmax counters. Zeroed when the block is allocated; every kernel leaves them zero, so
+//       they are zero between calls whatever the previous call was.
+//   [1] fp32 partial sums: split-K slices of the small-row GEMM, K slices of the many-row GEMM.
+//       Always written before they are read within a call (the small-row reducer reads a slice
+//       only after its flag is raised), so stale contents are never used.
+//   [2] prepared activations, rewritten by every call that reads them.
+// When a call needs a larger block, a new one is allocated and zeroed and the old one is kept
+// (a graph captured earlier may still use it) until w4a16_release_scratch. A call that would
+// allocate while its stream is being captured fails instead (allocation and zeroing are not
+// captured): warm the stream up with the same shapes before capturing it.
 struct Scratch {
     void *base = nullptr;
     size_t bytes[3] = {0, 0, 0};
-    uint32_t stamp = 0;
+    std::vector<void *> retired;
 };
 
 struct Key {
@@ -62,37 +70,33 @@ std::map<Key, Scratch> g_scratch;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct ScratchView {
-    uint32_t *counters;
-    uint64_t *partials;
+    uint32_t *control;
+    float *partials;
     void *act;
-    uint32_t stamp;   // 0 unless a stamp was asked for
 };
 
 // Returns W4A16_OK and fills `view` with pointers into a block whose regions hold at least the
-// requested bytes, allocating or growing the stream's block when needed. `new_stamp` takes the
-// next stamp.
-int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, size_t act_bytes, bool new_stamp,
-                ScratchView *view)
+// requested bytes, allocating a larger block for the stream when needed.
+int get_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, size_t act_bytes, ScratchView *view)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch &s = g_scratch[Key{dev, stream}];
-    const size_t need[3] = {std::max(counter_bytes, (size_t)4096), partial_bytes, act_bytes};
+    const size_t need[3] = {std::max(control_bytes, (size_t)4096), partial_bytes, act_bytes};
     if (s.base == nullptr || s.bytes[0] < need[0] || s.bytes[1] < need[1] || s.bytes[2] < need[2]) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone)
+            return fail(W4A16_ERR_UNSUPPORTED,
+                        "this call needs more scratch than its stream holds, and the stream is being captured: "
+                        "run the same calls on the stream once before capturing it");
         size_t nb[3], total = 0;
         for (int r = 0; r < 3; ++r) {
             nb[r] = round_up(std::max(need[r], s.bytes[r]), 256);
             total += nb[r];
-        }
-        if (s.base) {
-            // the old block may still be in use by earlier work on this stream
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            e = hipFree(s.base);
-            s.base = nullptr;
-            if (e != hipSuccess) return hip_fail(e, "hipFree");
         }
         void *p = nullptr;
         e = hipMalloc(&p, total);
@@ -105,22 +109,14 @@ int get_scratch(hipStream_t stream, size_t counter_bytes, size_t partial_bytes, 
             (void)hipFree(p);
             return hip_fail(e, "hipMemsetAsync");
         }
+        if (s.base) s.retired.push_back(s.base);
         s.base = p;
         for (int r = 0; r < 3; ++r) s.bytes[r] = nb[r];
     }
     char *b = static_cast<char *>(s.base);
-    view->counters = reinterpret_cast<uint32_t *>(b);
-    view->partials = reinterpret_cast<uint64_t *>(b + s.bytes[0]);
+    view->control = reinterpret_cast<uint32_t *>(b);
+    view->partials = reinterpret_cast<float *>(b + s.bytes[0]);
     view->act = b + s.bytes[0] + s.bytes[1];
-    view->stamp = 0;
-    if (new_stamp) {
-        if (++s.stamp == 0) {   // every stamp used once: clear the partials and start over
-            e = hipMemsetAsync(view->partials, 0, s.bytes[1], stream);
-            if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
-            s.stamp = 1;
-        }
-        view->stamp = s.stamp;
-    }
     return W4A16_OK;
 }
 
@@ -286,24 +282,25 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
     if (split_k || plan.prep_a || idx) {
-        // counters: [tile counters][argmax row keys (M x 64 bit)]
+        // control words: [tile counters][slice flags, tiles x splits][argmax row keys (16 x 64 bit)]
         const size_t tile = (size_t)tile_columns(plan.cols);
         const size_t tiles = ((size_t)NV + tile - 1) / tile;
-        const size_t key_off = round_up(tiles * sizeof(uint32_t), 8);
-        const size_t counter_bytes = key_off + 16 * sizeof(unsigned long long);
+        const size_t flag_off = tiles * sizeof(uint32_t);
+        const size_t key_off = round_up(flag_off + tiles * plan.splits * sizeof(uint32_t), 8);
+        const size_t control_bytes = key_off + 16 * sizeof(unsigned long long);
         const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
         const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
-        rc = get_scratch(stream, counter_bytes, split_k ? (size_t)plan.splits * M * NV * sizeof(uint64_t) : 0,
-                         act_bytes, split_k, &v);
+        rc = get_scratch(stream, control_bytes, split_k ? (size_t)plan.splits * M * NV * sizeof(float) : 0, act_bytes,
+                         &v);
         if (rc != W4A16_OK) return rc;
-        a.counters = v.counters;
+        char *c = reinterpret_cast<char *>(v.control);
+        a.counters = v.control;
+        a.flags = reinterpret_cast<uint32_t *>(c + flag_off);
         a.partials = v.partials;
-        a.stamp = v.stamp;
         a.A16 = static_cast<uint16_t *>(v.act);
         a.ashift = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
         if (idx) {
-            char *c = reinterpret_cast<char *>(v.counters);
             a.amax_keys = reinterpret_cast<unsigned long long *>(c + key_off);
             a.amax_idx = idx;
         }
@@ -346,7 +343,7 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
     const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
     const size_t part_bytes = splits > 1 ? (size_t)splits * M * N * (up ? 2 : 1) * sizeof(float) : 0;
     ScratchView v{};
-    rc = get_scratch(stream, 0, part_bytes, a16_bytes + (size_t)M * sizeof(int), false, &v);
+    rc = get_scratch(stream, 0, part_bytes, a16_bytes + (size_t)M * sizeof(int), &v);
     if (rc != W4A16_OK) return rc;
     uint16_t *a16 = static_cast<uint16_t *>(v.act);
     int *shifts = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
@@ -364,7 +361,7 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
         pa.qzeros2 = up->qzeros;
     }
     pa.out = out;
-    pa.partials = reinterpret_cast<float *>(v.partials);
+    pa.partials = v.partials;
     pa.M = M;
     pa.N = N;
     pa.K = K;
@@ -545,9 +542,9 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
     // counters: M uint32 counters followed by M 64-bit keys, all zero between calls
     const size_t need = round_up((size_t)M * 4, 8) + (size_t)M * 8;
     ScratchView v{};
-    int rc = get_scratch(stream, need, 0, 0, false, &v);
+    int rc = get_scratch(stream, need, 0, 0, &v);
     if (rc != W4A16_OK) return rc;
-    uint32_t *ctr = v.counters;
+    uint32_t *ctr = v.control;
     a.counters = ctr;
     a.keys = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ctr) + round_up((size_t)M * 4, 8));
     const hipError_t e = launch_argmax(a, stream);
@@ -583,13 +580,16 @@ int w4a16_release_scratch(void)
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     int rc = W4A16_OK;
     for (auto &kv : g_scratch) {
-        if (!kv.second.base) continue;
+        std::vector<void *> blocks = kv.second.retired;
+        if (kv.second.base) blocks.push_back(kv.second.base);
         int cur = 0;
         (void)hipGetDevice(&cur);
         (void)hipSetDevice(kv.first.device);
-        const hipError_t e = hipFree(kv.second.base);
+        for (void *b : blocks) {
+            const hipError_t e = hipFree(b);
+            if (e != hipSuccess) rc = hip_fail(e, "hipFree");
+        }
         (void)hipSetDevice(cur);
-        if (e != hipSuccess) rc = hip_fail(e, "hipFree");
     }
     g_scratch.clear();
     return rc;
@@ -600,7 +600,7 @@ const char *w4a16_status_string(int status)
     switch (status) {
     case W4A16_OK: return "ok";
     case W4A16_ERR_INVALID_ARG: return "invalid argument";
-    case W4A16_ERR_UNSUPPORTED: return "unsupported (alignment)";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported (alignment, size, or scratch during capture)";
     case W4A16_ERR_HIP: return "HIP runtime error";
     case W4A16_ERR_NO_MEMORY: return "out of device memory";
     default: return "unknown status";
@@ -609,6 +609,11 @@ const char *w4a16_status_string(int status)
 
 const char *w4a16_last_error(void) { return g_last_error; }
 
-int w4a16_version(void) { return 100; }
+int w4a16_version(void) { return 200; }
+
+#ifndef W4A16_SOURCE_HASH
+#define W4A16_SOURCE_HASH "unknown"
+#endif
+const char *w4a16_source_hash(void) { return W4A16_SOURCE_HASH; }
 
 }  // extern "C"

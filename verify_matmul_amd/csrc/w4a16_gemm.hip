@@ -53,6 +53,10 @@ namespace {
 // Activation items (16 bytes) a lane may stage through registers: 8 KB per wave.
 constexpr int kHeld = 8;
 
+// Wait until every vector memory operation this thread issued has completed (stores included:
+// on gfx9 stores count in vmcnt).
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 
 // The K range [wb, we) (in steps) of piece `wave` of split `split`: splits cut K into
 // contiguous slices, the waves of a workgroup cut each slice again. The activation preparation
@@ -661,103 +665,70 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
     }
 
     // ---- split-K across workgroups ---------------------------------------------------------
-    // Every workgroup of the tile bumped the tile's counter when it started; the last one to
-    // start adds the slices. The others store each element of their slice as one 64-bit word,
-    // the value in the low half and this call's stamp in the high half: a single agent-scope
-    // atomic store, so value and stamp become visible together, and nothing to wait for. The
-    // reducer reads the other slices and re-reads any element whose stamp is not yet this
-    // call's (those workgroups are already running, so every wait ends), adding the slices in
-    // slice order with its own slice taken from LDS.
-    const uint64_t stamp_hi = (uint64_t)p.stamp << 32;
+    // Every workgroup of the tile counted itself in on the tile's counter when it started; the
+    // last one to start adds the slices. The others store their slice as fp32 with agent-scope
+    // atomic stores, wait until every store of the workgroup has completed, and raise their
+    // slice's flag. The reducer waits for each other slice's flag, reads the slice, adds the
+    // slices in slice order (bit-identical results from run to run), and lowers the flags and
+    // the counter again. Counters and flags are therefore zero between calls whatever the call
+    // was: no state carries from one call to the next, so a call replayed from a captured graph
+    // runs exactly as it ran when it was captured.
+    const size_t slice = (size_t)M * NV;
+    uint32_t *const tile_flags = p.flags + (size_t)tile * p.splits;
     if (!s_last) {
         for (int idx = tid; idx < M * kTile; idx += kThreads) {
             const int m = idx / kTile;
             const int c = idx - m * kTile;
-            const int n = tile * kTile + c;
             if (col_valid(c))
-                __hip_atomic_store(p.partials + ((size_t)split * M + m) * NV + n,
-                                   stamp_hi | __builtin_bit_cast(uint32_t, wg_sum(m, c)), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.partials + (size_t)split * slice + (size_t)m * NV + tile * kTile + c, wg_sum(m, c),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        wait_vm_all();        // this thread's stores have completed ...
+        __syncthreads();      // ... and so have every other thread's
+        if (tid == 0) __hip_atomic_store(&tile_flags[split], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    // Slices are fetched a batch at a time. The batch is the smallest of 4, 8 or 16 that covers
-    // the slices, so few slices fetch no padding, and a thread issues the first batch of up to
-    // 8 / batch of its outputs (two at 16 rows with 8 waves) before it adds any: one round trip
-    // for them, overlapped with its own slice's sum from LDS.
-    auto reduce = [&](auto batch_tag) {
-        constexpr int kBatch = decltype(batch_tag)::value;
-        constexpr int kOut = kBatch >= 8 ? 1 : 8 / kBatch;
-        const size_t slice = (size_t)M * NV;
-        const int cnt0 = min(kBatch, p.splits);
-        for (int base = tid; base < M * kTile; base += kOut * kThreads) {
-            uint64_t part[kOut][kBatch];
-#pragma unroll
-            for (int o = 0; o < kOut; ++o) {
-                const int idx = base + o * kThreads;
-                const int m = idx / kTile;
-                const int n = tile * kTile + idx - m * kTile;
-                const bool ok = idx < M * kTile && col_valid(idx - m * kTile);
-                const uint64_t *col = p.partials + (ok ? (size_t)m * NV + n : 0);
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    part[o][i] = 0;
-                    if (ok)
-                        part[o][i] = __hip_atomic_load(col + (size_t)min(i, cnt0 - 1) * slice, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-#pragma unroll
-            for (int o = 0; o < kOut; ++o) {
-                const int idx = base + o * kThreads;
-                if (idx >= M * kTile) continue;   // wave-uniform: M * kTile is a multiple of 64
-                const int m = idx / kTile;
-                const int c = idx - m * kTile;
-                const int n = tile * kTile + c;
-                const bool in = col_valid(c);
-                const float own = wg_sum(m, c);
-                const uint64_t *col = p.partials + (size_t)m * NV + n;
-                float v = 0.f;
-                bool failed = false;
-                for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
-                    const int cnt = min(kBatch, p.splits - sp0);
-                    if (sp0 > 0) {   // more than 16 slices: the next batch of this output
-#pragma unroll
-                        for (int i = 0; i < kBatch; ++i)
-                            part[o][i] = __hip_atomic_load(col + (size_t)(sp0 + min(i, cnt - 1)) * slice,
-                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-#pragma unroll
-                    for (int i = 0; i < kBatch; ++i) {
-                        if (i >= cnt) continue;
-                        const int sp = sp0 + i;
-                        if (sp == split) {
-                            v += own;
-                            continue;
-                        }
-                        uint64_t w = part[o][i];
-                        uint32_t spins = 0;
-                        while ((w & 0xFFFFFFFF00000000ull) != stamp_hi) {   // not yet stored in this call
-                            __builtin_amdgcn_s_sleep(2);
-                            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
-                                failed = true;
-                                break;
-                            }
-                            w = __hip_atomic_load(col + (size_t)sp * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        v += __builtin_bit_cast(float, (uint32_t)w);
-                    }
-                }
-                put(m, c, failed ? __builtin_nanf("") : v, in);
+    __shared__ int s_failed;
+    if (tid == 0) s_failed = 0;
+    __syncthreads();
+    for (int sp = tid; sp < p.splits; sp += kThreads) {
+        if (sp == split) continue;
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&tile_flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                s_failed = 1;
+                break;
             }
         }
-    };
-    if (p.splits <= 4)
-        reduce(std::integral_constant<int, 4>{});
-    else if (p.splits <= 8)
-        reduce(std::integral_constant<int, 8>{});
-    else
-        reduce(std::integral_constant<int, 16>{});
+    }
+    __syncthreads();   // every flag seen raised: the slices' stores have completed
+    const bool failed = s_failed != 0;
+    constexpr int kBatch = 8;
+    for (int idx = tid; idx < M * kTile; idx += kThreads) {
+        const int m = idx / kTile;
+        const int c = idx - m * kTile;
+        const bool in = col_valid(c);
+        const float own = wg_sum(m, c);
+        const float *col = p.partials + (size_t)m * NV + tile * kTile + c;
+        float v = 0.f;
+        for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
+            float x[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int sp = sp0 + i;
+                x[i] = sp < p.splits && sp != split
+                           ? __hip_atomic_load(col + (size_t)sp * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : own;
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (sp0 + i < p.splits) v += x[i];
+        }
+        put(m, c, failed ? __builtin_nanf("") : v, in);
+    }
+    for (int sp = tid; sp < p.splits; sp += kThreads)
+        if (sp != split) __hip_atomic_store(&tile_flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (kDual) finish_pair();
     if (amax) finish_argmax();
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

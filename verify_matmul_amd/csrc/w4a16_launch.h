@@ -24,10 +24,9 @@ constexpr int kLdsStageBudget = 8 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kWideTileWavesPerCu = 16;
 
-// Bound on the split-K reducer's wait for another slice's element (each try sleeps about 128
-// cycles).
-// Only reached if a workgroup never finished, which a correct launch rules out; the outputs
-// of the tile are then NaN instead of a hang.
+// Bound on the split-K reducer's wait for another slice's flag (each try sleeps about 128
+// cycles). Only reached if a workgroup never finished, which a correct launch rules out; the
+// outputs of the tile are then NaN instead of a hang.
 constexpr uint32_t kSpinLimit = 1u << 24;
 
 // Ints of per-row data at the start of a GEMM workgroup's LDS, per wave: 16 rescale exponents
@@ -62,9 +61,9 @@ struct GemmArgs {
     void *out;
     uint16_t *A16;            // [M, K] prepared activations (matrix-core path)
     int *ashift;              // [splits * waves_k, M] their rescale per K piece and row
-    uint64_t *partials;       // [splits, M, N] (gated pair: [splits, M, 2N]) stamped fp32 partial sums
+    float *partials;          // [splits, M, N] (gated pair: [splits, M, 2N]) fp32 partial sums
     uint32_t *counters;       // one per column tile, zero between calls
-    uint32_t stamp;           // this call's stamp (nonzero, not used by the last 2^32 - 1 calls)
+    uint32_t *flags;          // [tiles, splits] slice-ready flags, zero between calls
     unsigned long long *amax_keys;   // fused argmax: [M] row keys, zero between calls (nullptr: off)
     int32_t *amax_idx;               // fused argmax: [M] output indices
     int M, N, K, g;
