@@ -86,6 +86,23 @@ int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales,
                void *out, int out_dtype, hipStream_t stream);
 
 /*
+ * w4a16_gemm for callers that cannot allocate device memory: code being captured into a HIP graph
+ * on a stream that has not been warmed up, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same operation, arguments, accuracy contract and determinism as w4a16_gemm; it calls
+ * no hipMalloc, hipFree or allocating routine. Its scratch is one fixed 16 MiB array in device
+ * memory per GPU (1 MiB of counters and flags, 15 MiB of partial sums and prepared activations),
+ * held until the process ends; its first call on a device takes the array's address and clears
+ * the counters with a small kernel on `stream`. A launch whose scratch would not fit takes fewer
+ * split-K workgroups per tile (so its rounding may differ from w4a16_gemm's, within the same
+ * contract); if even one does not fit, W4A16_ERR_UNSUPPORTED. Every call on a GPU uses the same
+ * array and leaves its counters and flags zero: calls that overlap on one GPU (on different
+ * streams, or graphs replayed concurrently) race and must not be made.
+ */
+int w4a16_gemm_noalloc(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                       const uint32_t *qzeros, int group_size, int M, int N, int K,
+                       void *out, int out_dtype, hipStream_t stream);
+
+/*
  * w4a16_gemm with an explicit launch: `splits` workgroups share each column tile along K
  * (their fp32 partials are added in slice order through the library's scratch buffer),
  * `waves_k` waves of each workgroup split that workgroup's K range (1, 2, 4, 8 or 16), and

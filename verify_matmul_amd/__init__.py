@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax",
+    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_argmax",
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split",
@@ -26,8 +26,8 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = (
-    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
-    "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
+    "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill",
+    "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
     "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version", "w4a16_source_hash",
 )
@@ -60,6 +60,7 @@ def load():
                           f"rebuild it with __graft_entry__.build()")
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
     lib.w4a16_gemm_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
@@ -82,7 +83,7 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
               "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill",
               "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
@@ -144,6 +145,13 @@ def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
     """out[M,N] = A[M,K] (bf16) x dequant(qweight, scales, qzeros); qzeros None = symmetric 8."""
     args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
     _check(load().w4a16_gemm(*args, _stream(stream)), "w4a16_gemm")
+    return out
+
+
+def w4a16_gemm_noalloc(A, qweight, scales, qzeros, group_size, out, stream=None):
+    """w4a16_gemm on the library's fixed per-GPU scratch array: allocates nothing."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    _check(load().w4a16_gemm_noalloc(*args, _stream(stream)), "w4a16_gemm_noalloc")
     return out
 
 

@@ -120,6 +120,59 @@ int get_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, 
     return W4A16_OK;
 }
 
+// ---- the no-allocation scratch (w4a16_gemm_noalloc) -------------------------------------------
+// For callers that cannot allocate: one fixed array in device memory per GPU, `scratch`, laid out
+// as [control words (kNoAllocControl bytes)][partials and prepared activations]. Its address is
+// taken with hipGetSymbolAddress once per device (with that device current) and kept; host code
+// passes that address, never the array's name, to kernels. The control words are cleared by a
+// fill kernel at that set-up and are zero between calls from then on (every kernel leaves them
+// zero). Every call on a GPU shares its array: calls that overlap on one GPU race.
+constexpr size_t kNoAllocBytes = 16u << 20;
+constexpr size_t kNoAllocControl = 1u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+std::mutex g_noalloc_mu;
+std::map<int, char *> g_noalloc_ptr;   // device -> address of its `scratch`
+
+__global__ void zero_words_kernel(uint32_t *p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+int noalloc_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, size_t act_bytes,
+                    ScratchView *view)
+{
+    const size_t data = round_up(partial_bytes, 256) + act_bytes;
+    if (control_bytes > kNoAllocControl || data > kNoAllocBytes - kNoAllocControl)
+        return fail(W4A16_ERR_UNSUPPORTED,
+                    "the call needs %zu control and %zu data bytes of scratch; the no-allocation buffer holds %zu and %zu",
+                    control_bytes, data, kNoAllocControl, kNoAllocBytes - kNoAllocControl);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    char *base = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_noalloc_mu);
+        auto it = g_noalloc_ptr.find(dev);
+        if (it == g_noalloc_ptr.end()) {
+            void *ptr = nullptr;
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+            hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint32_t *>(ptr),
+                               kNoAllocControl / sizeof(uint32_t));
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e, "clearing the no-allocation scratch");
+            it = g_noalloc_ptr.emplace(dev, static_cast<char *>(ptr)).first;
+        }
+        base = it->second;
+    }
+    view->control = reinterpret_cast<uint32_t *>(base);
+    view->partials = reinterpret_cast<float *>(base + kNoAllocControl);
+    view->act = base + kNoAllocControl + round_up(partial_bytes, 256);
+    return W4A16_OK;
+}
+
 // The launch plan of a shape. Measured on MI355X, the weights stream best from many short
 // waves (5-20 K steps each) with a shallow ring, 4-16 thousand waves in all: they keep HBM
 // busy from the first microsecond and the hardware dispatcher balances them. Each 64-column
@@ -229,7 +282,7 @@ struct Matrix {
 // the pair's two products instead: out = (A x w) + (A x up).
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
               int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream,
-              bool pair_sum = false)
+              bool pair_sum = false, bool noalloc = false)
 {
     const uint32_t *qweight = w.qweight;
     const uint16_t *scales = w.scales;
@@ -256,6 +309,33 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     GemmPlan plan{};
     rc = make_plan(M, NV, K, group_size, zm, splits, waves_k, tile_cols, idx != nullptr, &plan);
     if (rc != W4A16_OK) return rc;
+    // scratch of a plan: control words [tile counters][slice flags, tiles x splits][argmax row keys
+    // (16 x 64 bit)], fp32 partials [splits, M, NV], prepared activations [M, K] and their shifts
+    const size_t tile = (size_t)tile_columns(plan.cols);
+    const size_t tiles = ((size_t)NV + tile - 1) / tile;
+    const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
+    auto needs = [&](const GemmPlan &pl, size_t *control, size_t *part, size_t *act) {
+        *control = round_up(tiles * sizeof(uint32_t) + tiles * pl.splits * sizeof(uint32_t), 8) +
+                   16 * sizeof(unsigned long long);
+        *part = pl.splits > 1 ? (size_t)pl.splits * M * NV * sizeof(float) : 0;
+        *act = pl.prep_a ? a16_bytes + (size_t)pl.splits * pl.wk * M * sizeof(int) : 0;
+    };
+    size_t control_bytes, part_bytes, act_bytes;
+    needs(plan, &control_bytes, &part_bytes, &act_bytes);
+    // the no-allocation buffer: a default plan that does not fit takes fewer workgroups per tile
+    // (fewer partial slices), down to one
+    // (down to one, or to the last launch that still fits in LDS; what still does not fit is refused
+    // by noalloc_scratch)
+    while (noalloc && splits == 0 && plan.splits > 1 &&
+           (control_bytes > kNoAllocControl ||
+            round_up(part_bytes, 256) + act_bytes > kNoAllocBytes - kNoAllocControl)) {
+        GemmPlan fewer{};
+        if (make_plan(M, NV, K, group_size, zm, std::max(1, plan.splits / 2), plan.wk, tile_cols, idx != nullptr,
+                      &fewer) != W4A16_OK)
+            break;
+        plan = fewer;
+        needs(plan, &control_bytes, &part_bytes, &act_bytes);
+    }
 
     GemmArgs a{};
     a.A = static_cast<const uint16_t *>(A);
@@ -282,17 +362,11 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
     if (split_k || plan.prep_a || idx) {
-        // control words: [tile counters][slice flags, tiles x splits][argmax row keys (16 x 64 bit)]
-        const size_t tile = (size_t)tile_columns(plan.cols);
-        const size_t tiles = ((size_t)NV + tile - 1) / tile;
         const size_t flag_off = tiles * sizeof(uint32_t);
         const size_t key_off = round_up(flag_off + tiles * plan.splits * sizeof(uint32_t), 8);
-        const size_t control_bytes = key_off + 16 * sizeof(unsigned long long);
-        const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
-        const size_t act_bytes = plan.prep_a ? a16_bytes + (size_t)plan.splits * plan.wk * M * sizeof(int) : 0;
         ScratchView v{};
-        rc = get_scratch(stream, control_bytes, split_k ? (size_t)plan.splits * M * NV * sizeof(float) : 0, act_bytes,
-                         &v);
+        rc = noalloc ? noalloc_scratch(stream, control_bytes, part_bytes, act_bytes, &v)
+                     : get_scratch(stream, control_bytes, part_bytes, act_bytes, &v);
         if (rc != W4A16_OK) return rc;
         char *c = reinterpret_cast<char *>(v.control);
         a.counters = v.control;
@@ -433,6 +507,13 @@ int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales, c
                int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
 {
     return w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, stream);
+}
+
+int w4a16_gemm_noalloc(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                       int group_size, int M, int N, int K, void *out, int out_dtype, hipStream_t stream)
+{
+    return gemm_call(A, Matrix{qweight, scales, qzeros}, nullptr, group_size, M, N, K, out, out_dtype, 0, 0, 0, nullptr,
+                     stream, false, true);
 }
 
 int w4a16_gemm_affine_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint16_t *biases,
