@@ -1,0 +1,50 @@
+"""Host-side checks of the decode kernel's explicit launch (no GPU needed): refused knobs fail
+with INVALID_ARG, asked of the host-only planner w4a16_decode_plan (the checks w4a16_gemm_decode_ex
+makes before any device work)."""
+import ctypes
+import os
+
+import pytest
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import verify_matmul_amd as vm
+    if not os.path.exists(vm.lib_path):
+        from verify_matmul_amd import _build
+        _build.build()
+    return vm.load()
+
+
+def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128):
+    """The host-only planner: the same checks as w4a16_gemm_decode_ex, no device work."""
+    return lib.w4a16_decode_plan(M, N, K, g, 0, slices, tiles, kw, cols, ring, None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(slices=17), b"slices"),            # above the 16 the kernel adds
+    (dict(slices=17, K=1024), b"slices"),
+    (dict(slices=20, K=512), b"slices"),     # 512 / 32 = 16 steps
+    (dict(slices=5, tiles=2, kw=4, K=512), b"K-steps"),   # 5 x 4 pieces > 16 steps
+    (dict(tiles=9), b"waves"),
+    (dict(tiles=4, kw=3), b"waves"),         # 12 waves
+    (dict(cols=96), b"tile_cols"),
+    (dict(ring=5), b"ring"),
+    (dict(ring=3, cols=128), b"ring"),
+    (dict(slices=-1), b"must be >= 0"),
+    (dict(slices=1, tiles=1, M=16, K=8192, g=4096), b"activation items"),   # 16 rows x 1024 items on one wave
+    (dict(slices=1, tiles=4, kw=2, M=2, K=5120), b"LDS"),                  # 160 steps of 1 KB fragments
+])
+def test_decode_launch_is_checked(lib, kw, msg):
+    assert dec(lib, **kw) == -1
+    assert msg in lib.w4a16_last_error(), lib.w4a16_last_error()
+
+
+def test_default_plans_are_accepted(lib):
+    """The default launch of every workload shape and row count is one the kernel takes."""
+    out = (ctypes.c_int * 6)()
+    for K, N, g, packed in ((512, 256, 128, 0), (5120, 5120, 128, 0), (5120, 17408, 128, 0), (17408, 5120, 64, 1),
+                            (5120, 248320, 128, 0)):
+        for M in range(1, 17):
+            assert lib.w4a16_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, out) == 0, (K, N, M, lib.w4a16_last_error())
+            assert out[5] <= 160 * 1024 - 256

@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_argmax",
+    "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex",
+    "w4a16_decode_plan", "w4a16_gemm_argmax",
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split",
@@ -26,7 +27,7 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = (
-    "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill",
+    "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_prefill",
     "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
     "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version", "w4a16_source_hash",
@@ -61,6 +62,8 @@ def load():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_decode_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, I, I, P]
+    lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
     lib.w4a16_gemm_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
@@ -83,7 +86,7 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
               "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill",
               "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
@@ -146,6 +149,24 @@ def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
     args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
     _check(load().w4a16_gemm(*args, _stream(stream)), "w4a16_gemm")
     return out
+
+
+def w4a16_gemm_decode_ex(A, qweight, scales, qzeros, group_size, out, slices=0, tiles=0, kw=0, tile_cols=0, ring=0,
+                         stream=None):
+    """w4a16_gemm on the decode kernel with an explicit launch (0 = its default for that knob)."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    _check(load().w4a16_gemm_decode_ex(*args, int(slices), int(tiles), int(kw), int(tile_cols), int(ring),
+                                       _stream(stream)), "w4a16_gemm_decode_ex")
+    return out
+
+
+def w4a16_decode_plan(M, N, K, group_size, packed_zeros=False, slices=0, tiles=0, kw=0, tile_cols=0, ring=0):
+    """The decode kernel's launch for a shape (host only, no device work): a dict of slices, tiles,
+    kw, tile_cols, ring and lds bytes, or W4A16Error with the status w4a16_gemm_decode_ex would return."""
+    out = (ctypes.c_int * 6)()
+    _check(load().w4a16_decode_plan(int(M), int(N), int(K), int(group_size), int(bool(packed_zeros)), int(slices),
+                                    int(tiles), int(kw), int(tile_cols), int(ring), out), "w4a16_decode_plan")
+    return dict(zip(("slices", "tiles", "kw", "tile_cols", "ring", "lds"), list(out)))
 
 
 def w4a16_gemm_noalloc(A, qweight, scales, qzeros, group_size, out, stream=None):

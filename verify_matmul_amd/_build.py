@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["w4a16_api.hip", "w4a16_gemm.hip", "w4a16_prefill.hip", "w4a16_aux.hip"]
+SOURCES = ["w4a16_api.hip", "w4a16_gemm.hip", "w4a16_decode.hip", "w4a16_prefill.hip", "w4a16_aux.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming v_pk_{add,mul,fma}_f32 (the host pass

@@ -244,6 +244,64 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
     return W4A16_OK;
 }
 
+// The decode kernel's launch (w4a16_decode.hip). A workgroup is `tiles` x `kw` waves on adjacent
+// column tiles over one K slice; `slices` workgroups per group of columns. `slices`, `tiles`,
+// `kw`, `tile_cols` and `ring` > 0 override the defaults (tuning and tests).
+int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int tiles, int kw, int tile_cols, int ring,
+                     DecodePlan *pl)
+{
+    const int steps = K / kStepK;
+    if (tile_cols != 0 && tile_cols != 64 && tile_cols != 128)
+        return fail(W4A16_ERR_INVALID_ARG, "tile_cols=%d is not 0, 64 or 128", tile_cols);
+    pl->mfma = M > 1;
+    pl->cols = tile_cols ? tile_cols / 16 : 4;
+    pl->tiles = tiles ? tiles : 4;
+    pl->kw = kw ? kw : 1;
+    // default waves along K: more when even the most slices leave a thread too many activation
+    // items to hold
+    while (kw == 0 && pl->tiles * pl->kw * 2 <= kDecMaxWaves &&
+           decode_held(M, K, pl->tiles, pl->kw, std::max(1, std::min(kDecMaxSlices, steps / pl->kw))) > kDecHeld)
+        pl->kw *= 2;
+    if (pl->tiles < 1 || pl->kw < 1 || pl->tiles * pl->kw > kDecMaxWaves)
+        return fail(W4A16_ERR_INVALID_ARG, "tiles=%d x kw=%d waves outside 1..%d", pl->tiles, pl->kw, kDecMaxWaves);
+    const long long wc = (long long)pl->tiles * 16 * pl->cols;
+    const int groups = (int)((N + wc - 1) / wc);
+    if (slices == 0) {
+        slices = (int)std::min<long long>(kDecMaxSlices, (1024 + groups - 1) / groups);
+        slices = std::max(1, std::min(slices, steps / (4 * pl->kw)));
+        // long K: more slices until the slice's activations fit in registers and LDS
+        while (slices < std::min(kDecMaxSlices, steps / pl->kw) &&
+               (decode_held(M, K, pl->tiles, pl->kw, slices) > kDecHeld ||
+                decode_lds_layout(K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, nullptr) >
+                    (size_t)kMaxLds))
+            ++slices;
+    }
+    if (slices < 1 || slices > kDecMaxSlices || (long long)slices * pl->kw > steps)
+        return fail(W4A16_ERR_INVALID_ARG, "slices=%d outside 1..%d, or slices x kw=%d above the %d K-steps of 32",
+                    slices, kDecMaxSlices, pl->kw, steps);
+    pl->slices = slices;
+    if (decode_held(M, K, pl->tiles, pl->kw, slices) > kDecHeld)
+        return fail(W4A16_ERR_INVALID_ARG,
+                    "a K slice of %d steps puts %d activation items of 16 bytes on each thread (at most %d): "
+                    "use more slices or waves", (steps + slices - 1) / slices, decode_held(M, K, pl->tiles, pl->kw, slices),
+                    kDecHeld);
+    // the kernel addresses a slice's codes (plus the ring's reads past its end) with 32-bit byte
+    // offsets
+    const long long smax = (steps + slices - 1) / slices;
+    if ((smax + 8) * 16LL * N >= (1LL << 31))
+        return fail(W4A16_ERR_UNSUPPORTED, "a K slice of %lld steps over %d columns exceeds 2 GiB of codes: use more slices",
+                    smax, N);
+    pl->ring = ring ? ring : (pl->cols == 8 ? 2 : (M > 1 ? 4 : 3));
+    const bool ring_ok = pl->cols == 8 ? (pl->ring == 2 || pl->ring == 4)
+                                       : (pl->ring == 2 || pl->ring == 3 || pl->ring == 4 || pl->ring == 6 || pl->ring == 8);
+    if (!ring_ok) return fail(W4A16_ERR_INVALID_ARG, "ring=%d is not available for %d-column tiles", pl->ring, 16 * pl->cols);
+    pl->lds = decode_lds_layout(K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pl);
+    if (pl->lds > (size_t)kMaxLds)
+        return fail(W4A16_ERR_INVALID_ARG, "decode plan needs %zu bytes of LDS per workgroup (max %d): use more slices",
+                    pl->lds, kMaxLds);
+    return W4A16_OK;
+}
+
 int check_gemm_args(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                     int g, int M, int N, int K, void *out, int out_dtype, int max_m = 16)
 {
@@ -384,6 +442,60 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     return W4A16_OK;
 }
 
+// A decode-kernel call: check, plan, take scratch, launch.
+int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
+                int tile_cols, int ring, hipStream_t stream, bool noalloc = false)
+{
+    int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
+    if (rc != W4A16_OK) return rc;
+    if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
+        return fail(W4A16_ERR_INVALID_ARG, "slices=%d tiles=%d kw=%d ring=%d must be >= 0", slices, tiles, kw, ring);
+    DecodePlan plan{};
+    rc = make_decode_plan(M, N, K, group_size, qzeros != nullptr, slices, tiles, kw, tile_cols, ring, &plan);
+    if (rc != W4A16_OK) return rc;
+    const long long wc = (long long)plan.tiles * 16 * plan.cols;
+    const int groups = (int)((N + wc - 1) / wc);
+    DecodeArgs a{};
+    a.A = static_cast<const uint16_t *>(A);
+    a.qweight = qweight;
+    a.scales = scales;
+    a.qzeros = qzeros;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.g = group_size;
+    a.tiles = plan.tiles;
+    a.kw = plan.kw;
+    a.slices = plan.slices;
+    a.groups = groups;
+    a.out_bf16 = out_dtype == W4A16_OUT_BF16;
+    a.a_off = plan.a_off;
+    a.s_off = plan.s_off;
+    a.z_off = plan.z_off;
+    a.r_off = plan.r_off;
+    if (plan.slices > 1) {
+        // control words: [counters, one per group of columns][flags, groups x slices]
+        const size_t control_bytes = (size_t)groups * (1 + plan.slices) * sizeof(uint32_t);
+        const size_t part_bytes = (size_t)plan.slices * M * N * sizeof(float);
+        if (part_bytes >= (1ull << 31))
+            return fail(W4A16_ERR_UNSUPPORTED, "%zu bytes of partial sums exceed the 2 GiB the kernel addresses",
+                        part_bytes);
+        ScratchView v{};
+        rc = noalloc ? noalloc_scratch(stream, control_bytes, part_bytes, 0, &v)
+                     : get_scratch(stream, control_bytes, part_bytes, 0, &v);
+        if (rc != W4A16_OK) return rc;
+        a.counters = v.control;
+        a.flags = v.control + groups;
+        a.partials = v.partials;
+        a.part_bytes = (uint32_t)part_bytes;
+    }
+    const hipError_t e = launch_decode(a, plan, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode GEMM launch");
+    return W4A16_OK;
+}
+
 // A many-row call (prompt processing): check, choose the K slices, take scratch, prepare the
 // activations, launch. `up` non-null makes it a gated pair (w is the gate).
 int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
@@ -457,6 +569,14 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
 {
     return gemm_call(A, Matrix{qweight, scales, qzeros}, nullptr, group_size, M, N, K, out, out_dtype, splits,
                      waves_k, tile_cols, nullptr, stream);
+}
+
+int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                         int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
+                         int tile_cols, int ring, hipStream_t stream)
+{
+    return decode_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, slices, tiles, kw, tile_cols,
+                       ring, stream);
 }
 
 int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -606,6 +726,27 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
     if (splits) *splits = plan.splits;
     if (waves_k) *waves_k = plan.wk;
     if (tile_cols) *tile_cols = tile_columns(plan.cols);
+    return W4A16_OK;
+}
+
+int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles, int kw,
+                      int tile_cols, int ring, int *plan_out)
+{
+    if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
+        return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
+    if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
+        return fail(W4A16_ERR_INVALID_ARG, "slices=%d tiles=%d kw=%d ring=%d must be >= 0", slices, tiles, kw, ring);
+    DecodePlan plan{};
+    const int rc = make_decode_plan(M, N, K, group_size, packed_zeros != 0, slices, tiles, kw, tile_cols, ring, &plan);
+    if (rc != W4A16_OK) return rc;
+    if (plan_out) {
+        plan_out[0] = plan.slices;
+        plan_out[1] = plan.tiles;
+        plan_out[2] = plan.kw;
+        plan_out[3] = 16 * plan.cols;
+        plan_out[4] = plan.ring;
+        plan_out[5] = (int)plan.lds;
+    }
     return W4A16_OK;
 }
 

@@ -1,0 +1,518 @@
+// W4A16 decode GEMM for gfx950: one row (dot-product GEMV) or 2..16 rows (matrix cores), with
+// the activation slice of a workgroup converted once and shared by all of its column tiles.
+//
+// Work layout
+//   * A workgroup is `tiles` x `kw` waves over one K slice. Wave (w, k) owns column tile w of
+//     the workgroup (64 columns, 4 adjacent per lane, or 128, 8 per lane) and K piece k of the
+//     slice. The tiles are adjacent, so at every step the workgroup reads `tiles` x 256 (or 512)
+//     contiguous bytes of each word row it touches: measured on MI355X, reading the FFN matrix's
+//     codes with four adjacent tiles per workgroup takes 8.2-8.7 us against 9.4 us when the
+//     waves of a workgroup all split one tile's K range.
+//   * The slice's activations (all M rows) are loaded once by the whole workgroup, rescaled per
+//     row by one exact power of two, and stored in LDS as fp16 fragments in the order the dot
+//     products or the matrix cores read them. Had every wave loaded its own fragments from L2,
+//     the same read would take 14-21 us.
+//   * The `kw` pieces of a tile are added in LDS in piece order; `slices` workgroups cover each
+//     group of columns along K, their fp32 sums meeting in scratch, where the last workgroup to
+//     start adds them in slice order. Splitting K inside the workgroup moves no partial sums
+//     through memory; slices across workgroups write and read `slices - 1` copies of the output.
+//
+// Per step (32 K rows): each packed word becomes 8 exact fp16 values (q - z) (w4a16_device.h);
+// the GEMV multiplies them with v_dot2c_f32_f16, the matrix-core path with one
+// v_mfma_f32_16x16x32_f16 per word column (rows past M are zero fragments). Sums are kept per
+// quantisation group and scaled once in fp32 at the group's end, so (q - z) * scale never rounds
+// before accumulation (GRIMOIRE v1.7 release notes, 'What changed': an exact (q - z) * scale
+// dequantisation, a GEMV for one user and a matrix-engine kernel for 2-16 rows).
+//
+// The weights are loaded with non-temporal 16-byte buffer loads (each byte is read once per call)
+// into a ring of `kU` steps per wave, issued before the activation slice is converted so that
+// they are in flight from the first instructions on.
+#include "w4a16_device.h"
+#include "w4a16_launch.h"
+
+namespace w4a16 {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Buffer resource over `bytes` bytes at `base`: accesses past the end read zero and write
+// nothing, without a memory request.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kCoherent = 16;     // cache-policy operand of the buffer builtins: sc1 (agent scope)
+constexpr int kNonTemporal = 2;   // and: nt
+
+constexpr int kHeld = kDecHeld;
+
+// LDS position (in 16-byte fragments) of the matrix-core fragment of row m, word row wr of the
+// slice: step t = wr / 4 holds 64 fragments, lane q * 16 + m of the MFMA reads row m, K quarter q.
+// The row index is XOR-swizzled with 4 (t mod 4) + q so that 16 lanes writing 16 consecutive word
+// rows of one row hit 16 different bank groups; a wave reading one step still reads 64
+// consecutive fragments.
+__device__ __forceinline__ int frag_pos(int m, int wr)
+{
+    const int t = wr >> 2, q = wr & 3;
+    return t * 64 + q * 16 + (m ^ (((t & 3) << 2) | q));
+}
+
+template <bool kMfma, int kZM, int kU, int kV>
+__global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
+{
+    constexpr int kC = 4 * kV;      // adjacent columns per lane
+    constexpr int kTile = 16 * kC;  // columns per wave
+    constexpr int kRows = kMfma ? 4 : 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_last, s_failed;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int NW = p.tiles * p.kw;              // waves of the workgroup
+    const int T = NW * 64;
+    const int w_tile = wave % p.tiles;          // the wave's column tile
+    const int w_k = wave / p.tiles;             // and K piece
+    const int cl = lane & 15;   // column block of the lane (and its MFMA A row)
+    const int rl = lane >> 4;   // word row of the lane within a step
+    const int M = p.M, N = p.N, K = p.K;
+    const int spg = p.g / kStepK;
+    const int P = p.slices;
+    const int cg = blockIdx.x / P;              // group of columns
+    const int sl = blockIdx.x - cg * P;         // K slice
+    const int steps = K / kStepK;
+    const int sb = (int)((long long)sl * steps / P);
+    const int se = (int)((long long)(sl + 1) * steps / P);   // se > sb (host: slices <= steps)
+    const int wb = sb + (int)((long long)w_k * (se - sb) / p.kw);           // the wave's piece [wb, we)
+    const int we = sb + (int)((long long)(w_k + 1) * (se - sb) / p.kw);     // (host: slices * kw <= steps)
+    const int g0 = sb / spg;
+    const int ng = (se - 1) / spg - g0 + 1;
+    const int WC = p.tiles * kTile;             // columns of the workgroup
+    const int c0 = cg * WC;
+    const int lcol = w_tile * kTile + cl * kC;  // the lane's first column within the workgroup
+    const int n0 = c0 + lcol;
+    const bool col_ok = n0 < N;                 // N % 8 == 0, so a lane's columns are all in or all out
+    const int nc = col_ok ? n0 : 0;
+
+    uint32_t arrival = 0;
+    if (P > 1 && tid == 0)
+        arrival = __hip_atomic_fetch_add(&p.counters[cg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    uint32_t *rowmax = reinterpret_cast<uint32_t *>(smem);                   // [16] largest |a| bits per row
+    uint4 *a_lds = reinterpret_cast<uint4 *>(smem + p.a_off);                // fp16 fragments
+    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(smem + p.s_off);         // [group][WC] scales
+    uint32_t *z_lds = reinterpret_cast<uint32_t *>(smem + p.z_off);          // [group][WC/8] zero words
+    float *red = reinterpret_cast<float *>(smem + p.r_off);                  // [kw-1][tiles][kC*kRows][64]
+
+    // ---- 1. scales and zero words of the workgroup's columns and groups, straight into LDS ----
+    {
+        const int per = WC / 8;   // 16-byte scale items (and zero words) per group
+        const int sitems = ng * per;
+        for (int b = wave * 64; b < sitems; b += T) {
+            const int it = b + lane;
+            const int gi = g0 + it / per;
+            int c = c0 + (it - (it / per) * per) * 8;
+            if (c >= N) c = 0;
+            if (it < sitems) load_to_lds16(p.scales + (size_t)gi * N + c, sc_lds + (size_t)b * 8);
+        }
+        if constexpr (kZM == kZeroPacked) {
+            for (int b = wave * 64; b < sitems; b += T) {
+                const int it = b + lane;
+                const int gi = g0 + it / per;
+                int c = c0 + (it - (it / per) * per) * 8;
+                if (c >= N) c = 0;
+                if (it < sitems) load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
+            }
+        }
+    }
+    asm volatile("" ::: "memory");
+
+    // ---- 2. the activation slice into registers ---------------------------------------------
+    // Item = (row m, word row wr) of 8 bf16 values. With at least as many rows as waves, wave v
+    // takes whole rows v, v + NW, ...; otherwise each row is shared by `wr_w` = NW / M waves, each
+    // taking every wr_w-th block of 64 word rows. A lane takes word rows lane, lane + 64 * wr_w, ...
+    // of each of its rows. (The host keeps rows x chunks within kHeld.)
+    const int NWR = (se - sb) * 4;                        // word rows of the slice
+    const bool by_row = M >= NW;
+    const int wr_w = by_row ? 1 : NW / M;                 // waves per row
+    const int m_first = by_row ? wave : wave / wr_w;      // >= M: the wave holds no activations
+    const int part = by_row ? 0 : wave - (wave / wr_w) * wr_w;
+    const int rstep = by_row ? NW : M;                    // to the wave's next row
+    const int chunks = (NWR + 64 * wr_w - 1) / (64 * wr_w);
+    const uint16_t *a_slice = p.A + (size_t)sb * 32;
+    uint4 held[kHeld];
+    {
+        int i_m = m_first, c = 0;
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j) {
+            const int wr = (part + c * wr_w) * 64 + lane;
+            held[j] = uint4{0u, 0u, 0u, 0u};
+            if (i_m < M && wr < NWR) held[j] = *reinterpret_cast<const uint4 *>(a_slice + (size_t)i_m * K + (size_t)wr * 8);
+            if (++c == chunks) {
+                c = 0;
+                i_m += rstep;
+            }
+        }
+    }
+    asm volatile("" ::: "memory");
+
+    // ---- 3. the weight ring ----------------------------------------------------------------
+    // A buffer resource over exactly the slice's word rows: the ring reloads steps past the
+    // wave's piece unconditionally (no branch in the loop); reads past the slice return zero
+    // without a memory request. Non-temporal: every byte is read once per call.
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.qweight + (size_t)sb * 4 * N, (uint32_t)((se - sb) * 16 * N));
+    const uint32_t w_lane = ((uint32_t)rl * (uint32_t)N + (uint32_t)nc) * 4u;   // bytes (slices stay below 2 GiB)
+    uint4 ring[kU][kV];
+    auto load_w = [&](uint4 *dst, int t) {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+                wrs, (int)(w_lane + (uint32_t)(t - sb) * 16u * (uint32_t)N + 16u * v), 0, kNonTemporal);
+            dst[v] = uint4{x.x, x.y, x.z, x.w};
+        }
+    };
+    // (issued in slot order, each behind a compiler barrier: the loop waits for slot u with
+    // exactly kU - 1 later loads outstanding, which holds on its first round only if the
+    // prologue issued the slots in the same order)
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        load_w(ring[u], wb + u);
+        asm volatile("" ::: "memory");
+    }
+
+    // ---- 4. row maxima, then the fp16 fragments ---------------------------------------------
+    if (tid < 16) rowmax[tid] = 0u;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kU * kV));   // all but the ring: scales, zeros, activations
+    __syncthreads();                                  // every wave's direct loads have landed
+    {   // each wave: the largest magnitude of each of its rows, one LDS atomic per row
+        int i_m = m_first, c = 0;
+        uint32_t run = 0;
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j) {
+            run = max(run, max_mag8(held[j]));
+            if (++c == chunks || j == kHeld - 1) {
+                if (i_m < M) {
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) run = max(run, (uint32_t)__shfl_xor((int)run, o));
+                    if (lane == 0 && run) atomicMax(&rowmax[i_m], run);
+                }
+                run = 0;
+                c = 0;
+                i_m += rstep;
+            }
+        }
+    }
+    __syncthreads();
+    {
+        int i_m = m_first, c = 0;
+        float mul = i_m < M ? pow2_neg(act_shift(rowmax[i_m] >> 7)) : 0.f;
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j) {
+            const int wr = (part + c * wr_w) * 64 + lane;
+            if (i_m < M && wr < NWR)
+                a_lds[kMfma ? frag_pos(i_m, wr) : wr] = __builtin_bit_cast(uint4, act8_to_slots(held[j], mul));
+            if (++c == chunks) {
+                c = 0;
+                i_m += rstep;
+                mul = i_m < M ? pow2_neg(act_shift(rowmax[i_m] >> 7)) : 0.f;
+            }
+        }
+        if (kMfma && M < 16) {   // matrix-core rows past M: zero fragments
+            for (int i = tid; i < (16 - M) * NWR; i += T) {
+                const int mm = M + i / NWR, ww = i - (i / NWR) * NWR;
+                a_lds[frag_pos(mm, ww)] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. stream the wave's piece ------------------------------------------------------------
+    const Masks mk = make_masks();
+    float4_t acc[kC], tot[kC];
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+        acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        tot[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    ZeroSub zs[kC];
+#pragma unroll
+    for (int j = 0; j < kC; ++j) zs[j] = zero_sub_sym();
+    int gi = wb / spg, gpos = wb - (wb / spg) * spg;
+    bool first = true;
+    // the lane's matrix-core fragment within a step: lane q * 16 + m reads row m, K quarter q
+    const int lx = (lane & 48) | ((lane & 15) ^ (lane >> 4));
+
+    auto step = [&](int t, const uint4 *wv) {
+        const bool last = gpos == spg - 1 || t + 1 == we;
+        const int tt = t - sb;
+        const half8_t a = __builtin_bit_cast(half8_t, kMfma ? a_lds[tt * 64 + (lx ^ ((tt & 3) << 2))] : a_lds[tt * 4 + rl]);
+        if (kZM == kZeroPacked && first) {   // zero points change once per group (uniform)
+            const uint32_t zw = z_lds[(gi - g0) * (WC / 8) + lcol / 8];
+#pragma unroll
+            for (int j = 0; j < kC; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(lcol + j)));
+        }
+        uint32_t words[kC];
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+            words[4 * v] = wv[v].x;
+            words[4 * v + 1] = wv[v].y;
+            words[4 * v + 2] = wv[v].z;
+            words[4 * v + 3] = wv[v].w;
+        }
+#pragma unroll
+        for (int j = 0; j < kC; ++j) {
+            const half8_t b = dequant_word(words[j], kZM == kZeroSym ? zero_sub_sym() : zs[j], mk);
+            if constexpr (kMfma) {
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+            } else {
+                float s = acc[j][0];
+                s = __builtin_amdgcn_fdot2(b.lo.lo, a.lo.lo, s, false);
+                s = __builtin_amdgcn_fdot2(b.lo.hi, a.lo.hi, s, false);
+                s = __builtin_amdgcn_fdot2(b.hi.lo, a.hi.lo, s, false);
+                s = __builtin_amdgcn_fdot2(b.hi.hi, a.hi.hi, s, false);
+                acc[j][0] = s;
+            }
+        }
+        if (last) {   // the group's scale, once, on fp32 sums
+            const uint16_t *sp = sc_lds + (gi - g0) * WC + lcol;
+            uint32_t sw[kC / 2];
+            if constexpr (kC == 4) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(sp);
+                sw[0] = v.x;
+                sw[1] = v.y;
+            } else {
+                const uint4 q = *reinterpret_cast<const uint4 *>(sp);
+                sw[0] = q.x;
+                sw[1] = q.y;
+                sw[2] = q.z;
+                sw[3] = q.w;
+            }
+#pragma unroll
+            for (int j = 0; j < kC; ++j) {
+                const float s = half_bits_to_float((sw[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+                if constexpr (kMfma) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tot[j][r] = __builtin_fmaf(acc[j][r], s, tot[j][r]);
+                    acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    tot[j][0] = __builtin_fmaf(acc[j][0], s, tot[j][0]);
+                    acc[j][0] = 0.f;
+                }
+            }
+        }
+        first = last;
+        if (++gpos == spg) {
+            gpos = 0;
+            ++gi;
+        }
+    };
+
+    // Whole rounds of the ring: every step computes and reissues its slot unconditionally, so the
+    // wait before a step covers only that slot.
+    const int full_end = wb + (we - wb) / kU * kU;
+    int t0 = wb;
+    for (; t0 < full_end; t0 += kU) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            step(t0 + u, ring[u]);
+            load_w(ring[u], t0 + u + kU);   // past the slice: no memory request
+        }
+    }
+#pragma unroll
+    for (int u = 0; u + 1 < kU; ++u)
+        if (t0 + u < we) step(t0 + u, ring[u]);
+
+    // ---- 6. the K pieces of each tile, added in LDS in piece order ------------------------------
+    if (p.kw > 1) {
+        constexpr int kVals = kC * kRows;   // floats per lane
+        if (w_k > 0) {
+            float *dst = red + ((size_t)(w_k - 1) * p.tiles + w_tile) * kVals * 64 + lane;
+#pragma unroll
+            for (int j = 0; j < kC; ++j)
+#pragma unroll
+                for (int r = 0; r < kRows; ++r) dst[(j * kRows + r) * 64] = tot[j][r];
+        }
+        __syncthreads();
+        if (w_k == 0) {
+            for (int k = 1; k < p.kw; ++k) {
+                const float *src = red + ((size_t)(k - 1) * p.tiles + w_tile) * kVals * 64 + lane;
+#pragma unroll
+                for (int j = 0; j < kC; ++j)
+#pragma unroll
+                    for (int r = 0; r < kRows; ++r) tot[j][r] += src[(j * kRows + r) * 64];
+            }
+        }
+    }
+
+    // ---- 7. the tile's sums: add the word rows (GEMV), undo the activation rescale -------------
+    if constexpr (!kMfma) {
+#pragma unroll
+        for (int j = 0; j < kC; ++j) {
+            float v = tot[j][0];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            tot[j][0] = v;
+        }
+    }
+    const int row_base = kMfma ? 4 * rl : 0;
+    const bool holder = (kMfma || rl == 0) && col_ok && w_k == 0;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int m = row_base + r;
+        const int sh = m < M ? act_shift(rowmax[m] >> 7) : 0;
+#pragma unroll
+        for (int j = 0; j < kC; ++j) tot[j][r] = __builtin_amdgcn_ldexpf(tot[j][r], sh);
+    }
+
+    auto store_out = [&](int m, int v, float x0, float x1, float x2, float x3) {
+        const size_t o = (size_t)m * N + n0 + 4 * v;
+        if (p.out_bf16) {
+            uint2 q;
+            q.x = float_to_bf16_bits(x0) | (float_to_bf16_bits(x1) << 16);
+            q.y = float_to_bf16_bits(x2) | (float_to_bf16_bits(x3) << 16);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + o) = q;
+        } else {
+            *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + o) = make_float4(x0, x1, x2, x3);
+        }
+    };
+
+    if (P == 1) {
+        if (holder) {
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const int m = row_base + r;
+                if (m < M) {
+#pragma unroll
+                    for (int v = 0; v < kV; ++v)
+                        store_out(m, v, tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]);
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- 8. slices across workgroups ----------------------------------------------------------
+    // Every workgroup of the column group counted itself in when it started; the last one to
+    // start adds the slices. The others store their slice (16-byte stores with the agent-scope
+    // coherence bit), wait until every store of the workgroup has completed, and raise their
+    // slice's flag. The reducer waits for each other slice's flag, reads the slices, adds them in
+    // slice order (bit-identical results from run to run), and lowers the flags and the counter
+    // again: counters and flags are zero between calls, so no state carries from one call to
+    // the next and a replayed graph runs as it ran when it was captured.
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(p.partials, p.part_bytes);
+    uint32_t *const flags = p.flags + (size_t)cg * P;
+    if (tid == 0) {
+        s_last = arrival == (uint32_t)(P - 1);
+        s_failed = 0;
+    }
+    __syncthreads();
+    if (!s_last) {
+        if (holder) {
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                const int m = row_base + r;
+                if (m < M) {
+#pragma unroll
+                    for (int v = 0; v < kV; ++v) {
+                        const f32x4 x = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
+                        const uint32_t off = (uint32_t)((((size_t)sl * M + m) * N + n0 + 4 * v) * sizeof(float));
+                        __builtin_amdgcn_raw_buffer_store_b128(x, prs, (int)off, 0, kCoherent);
+                    }
+                }
+            }
+        }
+        wait_vm_all();     // this thread's stores have completed ...
+        __syncthreads();   // ... and so have every other thread's
+        if (tid == 0) __hip_atomic_store(&flags[sl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    for (int sp = tid; sp < P; sp += T) {
+        if (sp == sl) continue;
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                s_failed = 1;
+                break;
+            }
+        }
+    }
+    __syncthreads();   // every flag seen raised: the other slices' stores have completed
+    const bool failed = s_failed != 0;
+    if (holder) {
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int m = row_base + r;
+            if (m >= M) continue;
+#pragma unroll
+            for (int v = 0; v < kV; ++v) {
+                const f32x4 own = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
+                f32x4 x[kDecMaxSlices];
+#pragma unroll
+                for (int sp = 0; sp < kDecMaxSlices; ++sp) {
+                    x[sp] = own;
+                    if (sp < P && sp != sl) {
+                        const uint32_t off = (uint32_t)((((size_t)sp * M + m) * N + n0 + 4 * v) * sizeof(float));
+                        x[sp] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kCoherent);
+                    }
+                }
+                f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < kDecMaxSlices; ++sp)
+                    if (sp < P) sum += x[sp];
+                if (failed) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+                store_out(m, v, sum.x, sum.y, sum.z, sum.w);
+            }
+        }
+    }
+    for (int sp = tid; sp < P; sp += T)
+        if (sp != sl) __hip_atomic_store(&flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool kMfma, int kZM, int kU, int kV>
+hipError_t launch_one(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
+{
+    const auto kern = decode_kernel<kMfma, kZM, kU, kV>;
+    if (plan.lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.groups * a.slices)), dim3(a.tiles * a.kw * 64), plan.lds, stream, a);
+    return hipGetLastError();
+}
+
+template <bool kMfma, int kZM>
+hipError_t launch_ring(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
+{
+    if (plan.cols == 8) {
+        switch (plan.ring) {
+        case 2: return launch_one<kMfma, kZM, 2, 2>(a, plan, stream);
+        case 4: return launch_one<kMfma, kZM, 4, 2>(a, plan, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (plan.ring) {
+    case 2: return launch_one<kMfma, kZM, 2, 1>(a, plan, stream);
+    case 3: return launch_one<kMfma, kZM, 3, 1>(a, plan, stream);
+    case 4: return launch_one<kMfma, kZM, 4, 1>(a, plan, stream);
+    case 6: return launch_one<kMfma, kZM, 6, 1>(a, plan, stream);
+    case 8: return launch_one<kMfma, kZM, 8, 1>(a, plan, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
+{
+    if (a.qzeros)
+        return plan.mfma ? launch_ring<true, kZeroPacked>(a, plan, stream) : launch_ring<false, kZeroPacked>(a, plan, stream);
+    return plan.mfma ? launch_ring<true, kZeroSym>(a, plan, stream) : launch_ring<false, kZeroSym>(a, plan, stream);
+}
+
+}  // namespace w4a16

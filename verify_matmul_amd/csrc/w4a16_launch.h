@@ -161,6 +161,83 @@ constexpr int kPrefillTileM = 64;
 constexpr int kPrefillTileN = 256;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// Decode GEMM (w4a16_decode.hip): a workgroup is `tiles` x `kw` waves over one K slice, wave
+// (w, k) on column tile w (tiles adjacent, 64 or 128 columns each) and K piece k of the slice;
+// the workgroup's activation slice is converted once into LDS for all of them and the pieces
+// are added in LDS. `slices` workgroups share each group of columns along K; their fp32 sums
+// meet through scratch (counters and flags as in the small-row kernel).
+constexpr int kDecMaxWaves = 8;
+constexpr int kDecMaxSlices = 16;
+// Activation items (8 bf16 values) each thread of a decode workgroup holds between the row
+// maximum and the conversion: rows per wave x 64-item chunks per row must not exceed it.
+constexpr int kDecHeld = 8;
+struct DecodeArgs {
+    const uint16_t *A;
+    const uint32_t *qweight;
+    const uint16_t *scales;
+    const uint32_t *qzeros;   // nullptr: symmetric zero point 8
+    void *out;
+    float *partials;          // [slices, M, N] fp32 (slices > 1)
+    uint32_t *counters;       // [groups] zero between calls
+    uint32_t *flags;          // [groups, slices] zero between calls
+    int M, N, K, g;
+    int tiles;                // adjacent column tiles per workgroup
+    int kw;                   // K pieces per tile (waves per tile) in a workgroup
+    int slices;               // workgroups along K per group of columns
+    int groups;               // groups of columns (tiles adjacent tiles each)
+    int out_bf16;
+    int a_off, s_off, z_off, r_off;   // LDS offsets: fragments, scales, zero words, piece sums
+    uint32_t part_bytes;      // bytes of the partials region (bounds the buffer accesses)
+};
+struct DecodePlan {
+    bool mfma;                // false: the one-row dot-product GEMV
+    int cols;                 // adjacent columns per lane: 4 or 8 (tiles of 64 or 128 columns)
+    int tiles;
+    int kw;
+    int slices;
+    int ring;                 // steps of packed weights in flight per wave (template instance)
+    size_t lds;
+    int a_off, s_off, z_off, r_off;
+};
+// Activation items each thread holds under a plan: rows per wave x 64-item chunks per row.
+inline int decode_held(int M, int K, int tiles, int kw, int slices)
+{
+    const int steps = K / kStepK;
+    const int nwr = (steps + slices - 1) / slices * 4;   // word rows of the longest slice
+    const int nw = tiles * kw;
+    if (M >= nw) return (M + nw - 1) / nw * ((nwr + 63) / 64);
+    const int per = nw / M;                              // waves per row
+    return (nwr + 64 * per - 1) / (64 * per);
+}
+// LDS of a decode plan: 16 row maxima, the activation slice as fp16 fragments (MFMA: 1 KB per
+// step, 16 rows padded with zeros; GEMV: 64 bytes per step), the workgroup's scales and zero
+// words of its groups, and the K pieces' sums (kw - 1 pieces of every tile).
+inline size_t decode_lds_layout(int K, int g, bool mfma, int cols, int tiles, int kw, int slices, bool packed,
+                                DecodePlan *pl)
+{
+    const int steps = K / kStepK;
+    const int smax = (steps + slices - 1) / slices;
+    const int spg = g / kStepK;
+    const size_t groups = (size_t)(smax + spg - 1) / spg + 1;
+    const size_t wc = (size_t)tiles * 16 * cols;
+    const size_t a_off = 128;
+    const size_t a_bytes = (size_t)smax * (mfma ? 1024 : 64);
+    const size_t s_off = a_off + a_bytes;
+    const size_t s_bytes = groups * wc * 2;
+    const size_t z_off = s_off + round_up_sz(s_bytes, 16);
+    const size_t z_bytes = packed ? groups * (wc / 8) * 4 : 0;
+    const size_t r_off = round_up_sz(z_off + z_bytes, 16);
+    const size_t r_bytes = (size_t)(kw - 1) * tiles * 64 * cols * (mfma ? 4 : 1) * sizeof(float);
+    if (pl) {
+        pl->a_off = (int)a_off;
+        pl->s_off = (int)s_off;
+        pl->z_off = (int)z_off;
+        pl->r_off = (int)r_off;
+    }
+    return r_off + r_bytes;
+}
+hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream);
+
 struct ArgmaxArgs {
     const float *logits;
     int32_t *idx;
