@@ -123,16 +123,17 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
  * split each group of columns along K (their fp32 sums are added in slice order through the
  * library's scratch buffer); slices * kw must not exceed K/32. `ring` is the number of 32-row steps
  * of packed weights each wave keeps in flight (2, 3, 4, 6 or 8 on 64-column tiles, 2 or 4 on
- * 128-column tiles). 0 picks the kernel's default for that knob. A launch whose K slice would put
- * more than 8 activation items of 16 bytes on a thread (M rows x 4 items per step, shared by the
- * workgroup's waves) is refused with W4A16_ERR_INVALID_ARG. Same operation, arguments, accuracy
- * contract (with the activations rescaled per row and K slice) and determinism as w4a16_gemm.
- * Meant for tests and tuning sweeps.
+ * 128-column tiles). 0 picks the kernel's default for that knob. A launch whose activation slice
+ * or scales would not fit in a workgroup's LDS is refused with W4A16_ERR_INVALID_ARG. Same
+ * operation, arguments, accuracy contract (with the activations rescaled per row and K slice) and
+ * determinism as w4a16_gemm.
+ * idx: NULL, or int32 [M] device for the fused greedy pick of w4a16_gemm_argmax. Meant for tests
+ * and tuning sweeps.
  */
 int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t *scales,
                          const uint32_t *qzeros, int group_size, int M, int N, int K,
                          void *out, int out_dtype, int slices, int tiles, int kw, int tile_cols,
-                         int ring, hipStream_t stream);
+                         int ring, int32_t *idx, hipStream_t stream);
 
 /* The decode kernel's launch for a shape and explicit knobs (0 = default), checked exactly as
  * w4a16_gemm_decode_ex checks it, without any device work: W4A16_OK and, if plan_out is not NULL,
@@ -142,9 +143,11 @@ int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t 
 int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles,
                       int kw, int tile_cols, int ring, int *plan_out);
 
-/* The launch w4a16_gemm picks for a shape: *kernel = 0 for the one-row GEMV, 1 for the MFMA
- * GEMM; *splits, *waves_k and *tile_cols as in w4a16_gemm_ex. Any output pointer may be NULL.
- * Host only. */
+/* The launch w4a16_gemm picks for a shape (symmetric zero points): *kernel = 0 for the small-row
+ * kernel's one-row GEMV, 1 for its MFMA GEMM, with *splits, *waves_k and *tile_cols as in
+ * w4a16_gemm_ex; or 2 (one row) / 3 (matrix cores) for the decode kernel of w4a16_gemm_decode_ex,
+ * which w4a16_gemm takes for matrices of 65536 columns or more (an output layer), with *splits =
+ * its slices, *waves_k = its kw and *tile_cols. Any output pointer may be NULL. Host only. */
 int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, int *waves_k,
                int *tile_cols);
 

@@ -136,3 +136,29 @@ def test_decode_workloads(gu, name, M):
     y = run(gu, d, M)
     frac = parity.check_close(y, y_ref, bound, f"{name} M={M}")
     gu.say(f"[decode workload] {name} M={M} worst err/tol {frac:.3e}")
+
+
+@pytest.mark.parametrize("K,N,g,sym", [(512, 1000, 128, True), (1024, 4104, 64, False), (512, 131072, 128, True)])
+def test_decode_fused_pick(gu, K, N, g, sym):
+    """The greedy pick fused into the decode kernel's epilogue, single-slice and through the slice
+    reducer: logits bit-identical to the same launch without the pick, indices equal to the
+    separate pick (w4a16_argmax_rows) over those fp32 logits, logits within the bar."""
+    inp = synth.make_random(K + N + 7, 16, K, N, g, symmetric=sym)
+    d = gu.DevInputs(inp)
+    for M in (1, 2, 5, 16):
+        y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
+        for launch in ((0, 0, 0, 0, 0), (1, 4, 1, 64, 4), (3, 2, 2, 64, 3), (4, 4, 1, 128, 2)):
+            if refused(launch, M, N, K, g, not sym):
+                continue
+            gu.say(f"[decode pick] K={K} N={N} M={M} launch={launch}")
+            plain = run(gu, d, M, *launch)
+            out = torch.full((M, N), float("nan"), dtype=torch.float32, device=gu.DEV)
+            idx = torch.full((M,), -5, dtype=torch.int32, device=gu.DEV)
+            vm.w4a16_gemm_decode_ex(d.act[:M], d.qweight, d.scales, d.qzeros, g, out, *launch, idx=idx)
+            sep = torch.empty((M,), dtype=torch.int32, device=gu.DEV)
+            vm.w4a16_argmax_rows(out, sep)
+            torch.cuda.synchronize()
+            y = out.double().cpu().numpy()
+            assert np.array_equal(y, plain)
+            assert idx.cpu().tolist() == sep.cpu().tolist() == np.argmax(y, axis=1).tolist()
+            parity.check_close(y, y_ref, bound, f"pick K={K} N={N} M={M} {launch}")

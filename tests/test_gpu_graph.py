@@ -95,6 +95,65 @@ def test_graph_replay_matches_the_oracle(gu):
         parity.check_gate_up(o_pair.cpu().numpy(), *h, f"replay {r}: gated pair")
 
 
+def test_graph_replay_of_the_wide_matrix_kernel(gu):
+    """The same on a matrix wide enough for the decode kernel (the output layer's path): default
+    launches at one, five and sixteen rows (K slices exchanged through slice flags), the fused pick
+    on it (the finishing kernel clears the row keys in every replay), and an explicit launch of
+    three slices with the pick."""
+    K, N, g = 1024, 70000, 128           # 137 groups of 512 columns, the last one ragged
+    w = synth.make_random(9201, 16, K, N, g, symmetric=False)
+    d = gu.DevInputs(w)
+    a_buf = torch.zeros((16, K), dtype=torch.int16, device=gu.DEV)
+    outs = {M: torch.empty((M, N), dtype=torch.float32, device=gu.DEV) for M in (1, 5, 16)}
+    o_pick = torch.empty((5, N), dtype=torch.float32, device=gu.DEV)
+    o_ex = torch.empty((16, N), dtype=torch.float32, device=gu.DEV)
+    idx = torch.full((5,), -1, dtype=torch.int32, device=gu.DEV)
+    idx_ex = torch.full((16,), -1, dtype=torch.int32, device=gu.DEV)
+    for M in (1, 5, 16):
+        kern, slices, kw, cols = vm.w4a16_plan(M, N, K, g)
+        gu.say(f"[graph wide] default plan M={M}: kernel={kern} slices={slices} kw={kw} tile_cols={cols}")
+        assert kern == (2 if M == 1 else 3)
+
+    def calls():
+        for M in (1, 5, 16):
+            vm.w4a16_gemm(a_buf[:M], d.qweight, d.scales, d.qzeros, g, outs[M])
+        vm.w4a16_gemm_argmax(a_buf[:5], d.qweight, d.scales, d.qzeros, g, o_pick, idx)
+        vm.w4a16_gemm_decode_ex(a_buf[:16], d.qweight, d.scales, d.qzeros, g, o_ex, 3, 8, 1, 64, 4, idx=idx_ex)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        calls()
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(9202)
+    for r in range(REPLAYS):
+        act = synth.f32_to_bf16_bits(rng.standard_normal((16, K)).astype(np.float32) * np.float32(1 + r))
+        a_buf.copy_(torch.from_numpy(act.view(np.int16)))
+        for t in (*outs.values(), o_pick, o_ex):
+            t.fill_(float("nan"))
+        idx.fill_(-1)
+        idx_ex.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        gu.say(f"[graph wide] replay {r}")
+        y16, b16 = oracle.gemm(act, w.qweight, w.scales, w.qzeros, g)
+        for M in (1, 5, 16):
+            y, b = (y16, b16) if M == 16 else oracle.gemm(act[:M], w.qweight, w.scales, w.qzeros, g)
+            parity.check_close(outs[M].cpu().numpy(), y, b, f"replay {r}: {M}-row GEMM")
+        y5, b5 = oracle.gemm(act[:5], w.qweight, w.scales, w.qzeros, g)
+        logits = o_pick.cpu().numpy()
+        parity.check_close(logits, y5, b5, f"replay {r}: fused pick's logits")
+        assert np.array_equal(idx.cpu().numpy().astype(np.int64), oracle.argmax_rows_f32(logits)), f"replay {r}"
+        logits = o_ex.cpu().numpy()
+        parity.check_close(logits, y16, b16, f"replay {r}: three-slice launch")
+        assert np.array_equal(idx_ex.cpu().numpy().astype(np.int64), oracle.argmax_rows_f32(logits)), f"replay {r}"
+
+
 def test_capture_that_needs_scratch_is_refused(gu):
     """A call that would have to allocate scratch during capture fails cleanly instead."""
     K, N, g = 1024, 512, 128

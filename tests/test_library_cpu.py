@@ -95,10 +95,16 @@ def test_plan_host_only(lib):
     import ctypes
     k, s, w, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     for M, N, K, g in ((1, 17408, 5120, 128), (16, 17408, 5120, 128), (5, 248320, 5120, 128),
-                       (1, 5120, 5120, 128), (16, 5120, 17408, 64), (1, 256, 512, 128), (16, 8, 64, 32)):
+                       (1, 248320, 5120, 128), (16, 248320, 5120, 128), (9, 65536, 4096, 64),
+                       (1, 65528, 4096, 64), (1, 5120, 5120, 128), (16, 5120, 17408, 64), (1, 256, 512, 128),
+                       (16, 8, 64, 32)):
         assert lib.w4a16_plan(M, N, K, g, ctypes.byref(k), ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)) == 0
-        assert k.value == (0 if M == 1 and c.value == 64 else 1)   # one row on 128 columns: matrix cores
-        assert s.value >= 1 and w.value in (1, 2, 4, 8, 16) and s.value * w.value <= K // 32
+        assert (k.value >= 2) == (N >= 65536)   # the decode kernel takes the widest matrices
+        if k.value >= 2:
+            assert k.value == (2 if M == 1 else 3) and 1 <= s.value <= 16 and w.value == 1
+        else:
+            assert k.value == (0 if M == 1 and c.value == 64 else 1)   # one row on 128 columns: matrix cores
+            assert s.value >= 1 and w.value in (1, 2, 4, 8, 16) and s.value * w.value <= K // 32
         assert c.value in (64, 128)
     assert lib.w4a16_plan(0, 256, 512, 128, None, None, None, None) == -1
     assert lib.w4a16_plan(1, 256, 512, 48, None, None, None, None) == -1

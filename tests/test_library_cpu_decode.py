@@ -32,8 +32,8 @@ def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128):
     (dict(ring=5), b"ring"),
     (dict(ring=3, cols=128), b"ring"),
     (dict(slices=-1), b"must be >= 0"),
-    (dict(slices=1, tiles=1, M=16, K=8192, g=4096), b"activation items"),   # 16 rows x 1024 items on one wave
-    (dict(slices=1, tiles=4, kw=2, M=2, K=5120), b"LDS"),                  # 160 steps of 1 KB fragments
+    (dict(slices=1, tiles=1, M=16, K=8192, g=4096), b"LDS"),   # 256 steps of 1 KB fragments
+    (dict(slices=1, tiles=4, kw=2, M=16, K=5120), b"LDS"),                 # 160 steps of 1 KB fragments
 ])
 def test_decode_launch_is_checked(lib, kw, msg):
     assert dec(lib, **kw) == -1

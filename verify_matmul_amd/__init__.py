@@ -62,7 +62,7 @@ def load():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
-    lib.w4a16_gemm_decode_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, I, I, P]
+    lib.w4a16_gemm_decode_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, I, I, P, P]
     lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
@@ -152,11 +152,14 @@ def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
 
 
 def w4a16_gemm_decode_ex(A, qweight, scales, qzeros, group_size, out, slices=0, tiles=0, kw=0, tile_cols=0, ring=0,
-                         stream=None):
-    """w4a16_gemm on the decode kernel with an explicit launch (0 = its default for that knob)."""
+                         idx=None, stream=None):
+    """w4a16_gemm on the decode kernel with an explicit launch (0 = its default for that knob); idx
+    (int32 [M]) adds the fused greedy pick."""
     args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    if idx is not None and tuple(idx.shape) != (A.shape[0],):
+        raise ValueError("idx must be [M]")
     _check(load().w4a16_gemm_decode_ex(*args, int(slices), int(tiles), int(kw), int(tile_cols), int(ring),
-                                       _stream(stream)), "w4a16_gemm_decode_ex")
+                                       _ptr(idx, "idx", (torch.int32,)), _stream(stream)), "w4a16_gemm_decode_ex")
     return out
 
 

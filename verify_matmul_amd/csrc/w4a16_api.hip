@@ -245,8 +245,10 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
 }
 
 // The decode kernel's launch (w4a16_decode.hip). A workgroup is `tiles` x `kw` waves on adjacent
-// column tiles over one K slice; `slices` workgroups per group of columns. `slices`, `tiles`,
-// `kw`, `tile_cols` and `ring` > 0 override the defaults (tuning and tests).
+// column tiles over one K slice; `slices` workgroups per group of columns. Defaults: 4 tiles of 64
+// columns, one wave each; slices for about 512 workgroups (at most 16, at least 4 K steps per
+// slice, more while the slice's activations would not fit in LDS). `slices`, `tiles`, `kw`,
+// `tile_cols` and `ring` > 0 override the defaults (tuning and tests).
 int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int tiles, int kw, int tile_cols, int ring,
                      DecodePlan *pl)
 {
@@ -255,47 +257,39 @@ int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int ti
         return fail(W4A16_ERR_INVALID_ARG, "tile_cols=%d is not 0, 64 or 128", tile_cols);
     pl->mfma = M > 1;
     pl->cols = tile_cols ? tile_cols / 16 : 4;
-    pl->tiles = tiles ? tiles : 4;
+    // more rows stage more activations per workgroup, which leaves room for fewer workgroups per
+    // CU: give each workgroup more waves
+    pl->tiles = tiles ? tiles : (pl->mfma ? 8 : 4);
     pl->kw = kw ? kw : 1;
-    // default waves along K: more when even the most slices leave a thread too many activation
-    // items to hold
-    while (kw == 0 && pl->tiles * pl->kw * 2 <= kDecMaxWaves &&
-           decode_held(M, K, pl->tiles, pl->kw, std::max(1, std::min(kDecMaxSlices, steps / pl->kw))) > kDecHeld)
-        pl->kw *= 2;
     if (pl->tiles < 1 || pl->kw < 1 || pl->tiles * pl->kw > kDecMaxWaves)
         return fail(W4A16_ERR_INVALID_ARG, "tiles=%d x kw=%d waves outside 1..%d", pl->tiles, pl->kw, kDecMaxWaves);
     const long long wc = (long long)pl->tiles * 16 * pl->cols;
     const int groups = (int)((N + wc - 1) / wc);
     if (slices == 0) {
-        slices = (int)std::min<long long>(kDecMaxSlices, (1024 + groups - 1) / groups);
+        slices = (int)std::min<long long>(kDecMaxSlices, (512 + groups - 1) / groups);
         slices = std::max(1, std::min(slices, steps / (4 * pl->kw)));
-        // long K: more slices until the slice's activations fit in registers and LDS
+        // long K: more slices until the slice's activations fit in LDS; past 8 rows, until two
+        // workgroups fit on a CU (one workgroup of 16 rows per CU leaves the CU too few waves)
+        const size_t lds_cap = M > 8 ? (size_t)kMaxLds / 2 : (size_t)kMaxLds;
         while (slices < std::min(kDecMaxSlices, steps / pl->kw) &&
-               (decode_held(M, K, pl->tiles, pl->kw, slices) > kDecHeld ||
-                decode_lds_layout(K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, nullptr) >
-                    (size_t)kMaxLds))
+               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, nullptr) > lds_cap)
             ++slices;
     }
     if (slices < 1 || slices > kDecMaxSlices || (long long)slices * pl->kw > steps)
         return fail(W4A16_ERR_INVALID_ARG, "slices=%d outside 1..%d, or slices x kw=%d above the %d K-steps of 32",
                     slices, kDecMaxSlices, pl->kw, steps);
     pl->slices = slices;
-    if (decode_held(M, K, pl->tiles, pl->kw, slices) > kDecHeld)
-        return fail(W4A16_ERR_INVALID_ARG,
-                    "a K slice of %d steps puts %d activation items of 16 bytes on each thread (at most %d): "
-                    "use more slices or waves", (steps + slices - 1) / slices, decode_held(M, K, pl->tiles, pl->kw, slices),
-                    kDecHeld);
     // the kernel addresses a slice's codes (plus the ring's reads past its end) with 32-bit byte
     // offsets
     const long long smax = (steps + slices - 1) / slices;
     if ((smax + 8) * 16LL * N >= (1LL << 31))
         return fail(W4A16_ERR_UNSUPPORTED, "a K slice of %lld steps over %d columns exceeds 2 GiB of codes: use more slices",
                     smax, N);
-    pl->ring = ring ? ring : (pl->cols == 8 ? 2 : (M > 1 ? 4 : 3));
+    pl->ring = ring ? ring : (pl->cols == 8 ? 2 : M == 1 ? 3 : M <= 8 ? 4 : 8);
     const bool ring_ok = pl->cols == 8 ? (pl->ring == 2 || pl->ring == 4)
                                        : (pl->ring == 2 || pl->ring == 3 || pl->ring == 4 || pl->ring == 6 || pl->ring == 8);
     if (!ring_ok) return fail(W4A16_ERR_INVALID_ARG, "ring=%d is not available for %d-column tiles", pl->ring, 16 * pl->cols);
-    pl->lds = decode_lds_layout(K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pl);
+    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pl);
     if (pl->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "decode plan needs %zu bytes of LDS per workgroup (max %d): use more slices",
                     pl->lds, kMaxLds);
@@ -338,10 +332,32 @@ struct Matrix {
 // `up` non-null makes it a gated pair (w is the gate): out = silu(A x w) * (A x up), planned as
 // one 2N-column problem on 128-column tiles (64 output columns of each matrix). `pair_sum` adds
 // the pair's two products instead: out = (A x w) + (A x up).
+int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
+                int tile_cols, int ring, int32_t *idx, hipStream_t stream, bool noalloc);
+
+// Whether a plain GPTQ call takes the decode kernel by default: for matrices of at least
+// kDecodeMinN columns, wide enough to fill the chip with whole-K (or few-slice) workgroups, such
+// as the 248320-column output layer (MI355X, back-to-back launches: 101 against 115 us at one row,
+// 111 against 124 at five, 137 against 163 at sixteen). Narrower matrices need K slices, whose
+// exchange costs the decode kernel more than the small-row kernel's split-K (FFN 5120 x 17408:
+// 17 against 14 us at one row, 24 against 22 at sixteen).
+bool decode_by_default(int M, int N, int K, int g, bool packed)
+{
+    if (N < kDecodeMinN) return false;
+    DecodePlan pl{};
+    return make_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, &pl) == W4A16_OK;
+}
+
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
               int out_dtype, int splits, int waves_k, int tile_cols, int32_t *idx, hipStream_t stream,
               bool pair_sum = false, bool noalloc = false)
 {
+    if (!up && !w.biases && splits == 0 && waves_k == 0 && tile_cols == 0 && M >= 1 && M <= 16 && N > 0 && K > 0 &&
+        group_size > 0 && group_size % 32 == 0 && K % group_size == 0 && N % 8 == 0 &&
+        decode_by_default(M, N, K, group_size, w.qzeros != nullptr))
+        return decode_call(A, w.qweight, w.scales, w.qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, 0, 0, idx,
+                           stream, noalloc);
     const uint32_t *qweight = w.qweight;
     const uint16_t *scales = w.scales;
     const uint32_t *qzeros = w.qzeros;
@@ -445,7 +461,7 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
 // A decode-kernel call: check, plan, take scratch, launch.
 int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                 int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                int tile_cols, int ring, hipStream_t stream, bool noalloc = false)
+                int tile_cols, int ring, int32_t *idx, hipStream_t stream, bool noalloc)
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
@@ -475,10 +491,13 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     a.s_off = plan.s_off;
     a.z_off = plan.z_off;
     a.r_off = plan.r_off;
-    if (plan.slices > 1) {
-        // control words: [counters, one per group of columns][flags, groups x slices]
-        const size_t control_bytes = (size_t)groups * (1 + plan.slices) * sizeof(uint32_t);
-        const size_t part_bytes = (size_t)plan.slices * M * N * sizeof(float);
+    a.mp_log2 = decode_mp_log2(M);
+    if (plan.slices > 1 || idx) {
+        // control words: [counters, one per group of columns][flags, groups x slices][fused pick's
+        // row keys, 16 x 64 bit]
+        const size_t key_off = round_up((size_t)groups * (1 + plan.slices) * sizeof(uint32_t), 8);
+        const size_t control_bytes = key_off + 16 * sizeof(unsigned long long);
+        const size_t part_bytes = plan.slices > 1 ? (size_t)plan.slices * M * N * sizeof(float) : 0;
         if (part_bytes >= (1ull << 31))
             return fail(W4A16_ERR_UNSUPPORTED, "%zu bytes of partial sums exceed the 2 GiB the kernel addresses",
                         part_bytes);
@@ -490,6 +509,10 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
         a.flags = v.control + groups;
         a.partials = v.partials;
         a.part_bytes = (uint32_t)part_bytes;
+        if (idx) {
+            a.amax_keys = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(v.control) + key_off);
+            a.amax_idx = idx;
+        }
     }
     const hipError_t e = launch_decode(a, plan, stream);
     if (e != hipSuccess) return hip_fail(e, "decode GEMM launch");
@@ -573,10 +596,10 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
 
 int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                          int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                         int tile_cols, int ring, hipStream_t stream)
+                         int tile_cols, int ring, int32_t *idx, hipStream_t stream)
 {
     return decode_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, slices, tiles, kw, tile_cols,
-                       ring, stream);
+                       ring, idx, stream, false);
 }
 
 int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -719,6 +742,16 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
 {
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
+    if (decode_by_default(M, N, K, group_size, false)) {
+        DecodePlan dp{};
+        const int rc = make_decode_plan(M, N, K, group_size, false, 0, 0, 0, 0, 0, &dp);
+        if (rc != W4A16_OK) return rc;
+        if (kernel) *kernel = dp.mfma ? 3 : 2;
+        if (splits) *splits = dp.slices;
+        if (waves_k) *waves_k = dp.kw;
+        if (tile_cols) *tile_cols = 16 * dp.cols;
+        return W4A16_OK;
+    }
     GemmPlan plan{};
     const int rc = make_plan(M, N, K, group_size, kZeroSym, 0, 0, 0, false, &plan);
     if (rc != W4A16_OK) return rc;

@@ -19,7 +19,7 @@
 //
 // Per step (32 K rows): each packed word becomes 8 exact fp16 values (q - z) (w4a16_device.h);
 // the GEMV multiplies them with v_dot2c_f32_f16, the matrix-core path with one
-// v_mfma_f32_16x16x32_f16 per word column (rows past M are zero fragments). Sums are kept per
+// v_mfma_f32_16x16x32_f16 per word column (rows past M are not stored). Sums are kept per
 // quantisation group and scaled once in fp32 at the group's end, so (q - z) * scale never rounds
 // before accumulation (GRIMOIRE v1.7 release notes, 'What changed': an exact (q - z) * scale
 // dequantisation, a GEMV for one user and a matrix-engine kernel for 2-16 rows).
@@ -50,14 +50,19 @@ constexpr int kNonTemporal = 2;   // and: nt
 constexpr int kHeld = kDecHeld;
 
 // LDS position (in 16-byte fragments) of the matrix-core fragment of row m, word row wr of the
-// slice: step t = wr / 4 holds 64 fragments, lane q * 16 + m of the MFMA reads row m, K quarter q.
-// The row index is XOR-swizzled with 4 (t mod 4) + q so that 16 lanes writing 16 consecutive word
-// rows of one row hit 16 different bank groups; a wave reading one step still reads 64
-// consecutive fragments.
-__device__ __forceinline__ int frag_pos(int m, int wr)
+// slice, with the rows stored padded to mp = 4, 8 or 16 (the smallest that holds M; mp_log2 is
+// its log2): step t = wr / 4 holds 4 mp fragments, fragment q * mp + m is row m, K quarter q. The
+// row index is XOR-swizzled with the step (and K quarter) so that 16 lanes writing 16
+// consecutive word rows of one row hit 16 different LDS bank groups; the 16 lanes of a K
+// quarter reading a step read mp consecutive fragments.
+__device__ __forceinline__ int frag_swz(int t, int q, int mp_log2)
+{
+    return mp_log2 == 4 ? (((t & 3) << 2) | q) : mp_log2 == 3 ? (((t & 3) << 1) | (q >> 1)) : (t & 3);
+}
+__device__ __forceinline__ int frag_pos(int m, int wr, int mp_log2)
 {
     const int t = wr >> 2, q = wr & 3;
-    return t * 64 + q * 16 + (m ^ (((t & 3) << 2) | q));
+    return ((t * 4 + q) << mp_log2) + (m ^ frag_swz(t, q, mp_log2));
 }
 
 template <bool kMfma, int kZM, int kU, int kV>
@@ -68,6 +73,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     constexpr int kRows = kMfma ? 4 : 1;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_last, s_failed;
+    __shared__ unsigned long long s_rowkey[16];   // fused pick: the workgroup's best key per row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -134,7 +140,9 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     // Item = (row m, word row wr) of 8 bf16 values. With at least as many rows as waves, wave v
     // takes whole rows v, v + NW, ...; otherwise each row is shared by `wr_w` = NW / M waves, each
     // taking every wr_w-th block of 64 word rows. A lane takes word rows lane, lane + 64 * wr_w, ...
-    // of each of its rows. (The host keeps rows x chunks within kHeld.)
+    // of each of its rows: item j of a lane is chunk j % chunks of the wave's row j / chunks. The
+    // first kHeld items stay in registers from the row-maximum pass to the conversion; a longer
+    // slice reads the rest twice (L2 hits).
     const int NWR = (se - sb) * 4;                        // word rows of the slice
     const bool by_row = M >= NW;
     const int wr_w = by_row ? 1 : NW / M;                 // waves per row
@@ -142,15 +150,23 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     const int part = by_row ? 0 : wave - (wave / wr_w) * wr_w;
     const int rstep = by_row ? NW : M;                    // to the wave's next row
     const int chunks = (NWR + 64 * wr_w - 1) / (64 * wr_w);
+    const int rows_w = m_first >= M ? 0 : (M - 1 - m_first) / rstep + 1;   // rows of the wave
+    const int n_items = rows_w * chunks;                  // items per lane (uniform)
     const uint16_t *a_slice = p.A + (size_t)sb * 32;
+    auto item_src = [&](int i_m, int c) {
+        const int wr = (part + c * wr_w) * 64 + lane;
+        return wr < NWR ? a_slice + (size_t)i_m * K + (size_t)wr * 8 : nullptr;
+    };
     uint4 held[kHeld];
     {
         int i_m = m_first, c = 0;
 #pragma unroll
         for (int j = 0; j < kHeld; ++j) {
-            const int wr = (part + c * wr_w) * 64 + lane;
             held[j] = uint4{0u, 0u, 0u, 0u};
-            if (i_m < M && wr < NWR) held[j] = *reinterpret_cast<const uint4 *>(a_slice + (size_t)i_m * K + (size_t)wr * 8);
+            if (j < n_items) {
+                const uint16_t *src = item_src(i_m, c);
+                if (src) held[j] = *reinterpret_cast<const uint4 *>(src);
+            }
             if (++c == chunks) {
                 c = 0;
                 i_m += rstep;
@@ -184,47 +200,56 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     }
 
     // ---- 4. row maxima, then the fp16 fragments ---------------------------------------------
-    if (tid < 16) rowmax[tid] = 0u;
+    if (tid < 16) {
+        rowmax[tid] = 0u;
+        s_rowkey[tid] = 0ull;
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kU * kV));   // all but the ring: scales, zeros, activations
     __syncthreads();                                  // every wave's direct loads have landed
     {   // each wave: the largest magnitude of each of its rows, one LDS atomic per row
         int i_m = m_first, c = 0;
         uint32_t run = 0;
+        auto fold = [&](uint4 x) {   // one item of row i_m; the row's last folds the row maximum in
+            run = max(run, max_mag8(x));
+            if (++c == chunks) {
 #pragma unroll
-        for (int j = 0; j < kHeld; ++j) {
-            run = max(run, max_mag8(held[j]));
-            if (++c == chunks || j == kHeld - 1) {
-                if (i_m < M) {
-#pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) run = max(run, (uint32_t)__shfl_xor((int)run, o));
-                    if (lane == 0 && run) atomicMax(&rowmax[i_m], run);
-                }
+                for (int o = 32; o >= 1; o >>= 1) run = max(run, (uint32_t)__shfl_xor((int)run, o));
+                if (lane == 0 && run) atomicMax(&rowmax[i_m], run);
                 run = 0;
                 c = 0;
                 i_m += rstep;
             }
+        };
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j)
+            if (j < n_items) fold(held[j]);
+        for (int j = kHeld; j < n_items; ++j) {   // a long slice: items past the held ones
+            const uint16_t *src = item_src(i_m, c);
+            fold(src ? *reinterpret_cast<const uint4 *>(src) : uint4{0u, 0u, 0u, 0u});
         }
     }
     __syncthreads();
+    const int mp_log2 = p.mp_log2;
     {
         int i_m = m_first, c = 0;
         float mul = i_m < M ? pow2_neg(act_shift(rowmax[i_m] >> 7)) : 0.f;
-#pragma unroll
-        for (int j = 0; j < kHeld; ++j) {
-            const int wr = (part + c * wr_w) * 64 + lane;
-            if (i_m < M && wr < NWR)
-                a_lds[kMfma ? frag_pos(i_m, wr) : wr] = __builtin_bit_cast(uint4, act8_to_slots(held[j], mul));
+        auto put = [&](uint4 x, bool ok) {   // one item of row i_m, as an fp16 fragment
+            if (ok) {
+                const int wr = (part + c * wr_w) * 64 + lane;
+                a_lds[kMfma ? frag_pos(i_m, wr, mp_log2) : wr] = __builtin_bit_cast(uint4, act8_to_slots(x, mul));
+            }
             if (++c == chunks) {
                 c = 0;
                 i_m += rstep;
                 mul = i_m < M ? pow2_neg(act_shift(rowmax[i_m] >> 7)) : 0.f;
             }
-        }
-        if (kMfma && M < 16) {   // matrix-core rows past M: zero fragments
-            for (int i = tid; i < (16 - M) * NWR; i += T) {
-                const int mm = M + i / NWR, ww = i - (i / NWR) * NWR;
-                a_lds[frag_pos(mm, ww)] = uint4{0u, 0u, 0u, 0u};
-            }
+        };
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j)
+            if (j < n_items) put(held[j], item_src(i_m, c) != nullptr);
+        for (int j = kHeld; j < n_items; ++j) {
+            const uint16_t *src = item_src(i_m, c);
+            put(src ? *reinterpret_cast<const uint4 *>(src) : uint4{0u, 0u, 0u, 0u}, src != nullptr);
         }
     }
     __syncthreads();
@@ -242,13 +267,19 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     for (int j = 0; j < kC; ++j) zs[j] = zero_sub_sym();
     int gi = wb / spg, gpos = wb - (wb / spg) * spg;
     bool first = true;
-    // the lane's matrix-core fragment within a step: lane q * 16 + m reads row m, K quarter q
-    const int lx = (lane & 48) | ((lane & 15) ^ (lane >> 4));
+    // the lane's matrix-core fragment within a step: lane q * 16 + m reads row m, K quarter q.
+    // Lanes of rows past the stored ones read row m mod mp: an MFMA row only feeds its own output
+    // row, and output rows past M are never stored.
+    const int mp = 1 << mp_log2;
+    const int q_l = lane >> 4;
+    const int lx = (q_l << mp_log2) + ((cl & (mp - 1)) ^ (mp_log2 == 4 ? q_l : mp_log2 == 3 ? q_l >> 1 : 0));
+    const int sx = mp_log2 - 2;   // the step's swizzle: (t mod 4) << sx
 
     auto step = [&](int t, const uint4 *wv) {
         const bool last = gpos == spg - 1 || t + 1 == we;
         const int tt = t - sb;
-        const half8_t a = __builtin_bit_cast(half8_t, kMfma ? a_lds[tt * 64 + (lx ^ ((tt & 3) << 2))] : a_lds[tt * 4 + rl]);
+        const half8_t a = __builtin_bit_cast(half8_t, kMfma ? a_lds[((tt * 4) << mp_log2) + (lx ^ ((tt & 3) << sx))]
+                                                            : a_lds[tt * 4 + rl]);
         if (kZM == kZeroPacked && first) {   // zero points change once per group (uniform)
             const uint32_t zw = z_lds[(gi - g0) * (WC / 8) + lcol / 8];
 #pragma unroll
@@ -379,6 +410,40 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
         }
     };
 
+    // Fused greedy pick (output layer): each finished output folds into its row's key (the keys
+    // of argmax_rows_kernel, so the pick equals a separate one over the fp32 outputs): the 16
+    // lanes holding one row's columns reduce theirs, one LDS atomic per row and lane group folds
+    // them into the workgroup's keys, and one agent-scope atomic per row merges those into the
+    // call's keys; a one-wave kernel next on the stream turns the keys into indices and clears
+    // them. Called by every thread of the workgroup.
+    const bool amax = p.amax_keys != nullptr;
+    auto pick = [&](const float (*fin)[kRows]) {
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            const int m = row_base + r;
+            unsigned long long k = 0ull;
+            if (holder && m < M) {
+#pragma unroll
+                for (int j = 0; j < kC; ++j) {
+                    const float v = fin[j][r];
+                    if (v == v) {
+                        const unsigned long long kj = argmax_key(v, (uint32_t)(n0 + j));
+                        k = kj > k ? kj : k;
+                    }
+                }
+            }
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                const unsigned long long other = shfl_xor_u64(k, o);
+                k = other > k ? other : k;
+            }
+            if (cl == 0 && k) atomicMax(&s_rowkey[m], k);
+        }
+        __syncthreads();
+        if (tid < M && s_rowkey[tid])
+            __hip_atomic_fetch_max(&p.amax_keys[tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
     if (P == 1) {
         if (holder) {
 #pragma unroll
@@ -390,6 +455,14 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
                         store_out(m, v, tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]);
                 }
             }
+        }
+        if (amax) {
+            float fin[kC][kRows];
+#pragma unroll
+            for (int j = 0; j < kC; ++j)
+#pragma unroll
+                for (int r = 0; r < kRows; ++r) fin[j][r] = tot[j][r];
+            pick(fin);
         }
         return;
     }
@@ -442,6 +515,11 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     }
     __syncthreads();   // every flag seen raised: the other slices' stores have completed
     const bool failed = s_failed != 0;
+    float fin[kC][kRows];   // the finished sums (for the fused pick)
+#pragma unroll
+    for (int j = 0; j < kC; ++j)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) fin[j][r] = 0.f;
     if (holder) {
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
@@ -465,9 +543,14 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
                     if (sp < P) sum += x[sp];
                 if (failed) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
                 store_out(m, v, sum.x, sum.y, sum.z, sum.w);
+                fin[4 * v][r] = sum.x;
+                fin[4 * v + 1][r] = sum.y;
+                fin[4 * v + 2][r] = sum.z;
+                fin[4 * v + 3][r] = sum.w;
             }
         }
     }
+    if (amax) pick(fin);
     for (int sp = tid; sp < P; sp += T)
         if (sp != sl) __hip_atomic_store(&flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -483,7 +566,9 @@ hipError_t launch_one(const DecodeArgs &a, const DecodePlan &plan, hipStream_t s
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.groups * a.slices)), dim3(a.tiles * a.kw * 64), plan.lds, stream, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.amax_keys) return e;
+    return launch_argmax_finish(a.amax_keys, a.amax_idx, a.M, stream);
 }
 
 template <bool kMfma, int kZM>

@@ -823,6 +823,12 @@ hipError_t launch_act_prep(const ActPrepArgs &pa, hipStream_t stream)
     return hipGetLastError();
 }
 
+hipError_t launch_argmax_finish(unsigned long long *keys, int32_t *idx, int M, hipStream_t stream)
+{
+    hipLaunchKernelGGL(argmax_keys_finish_kernel, dim3(1), dim3(64), 0, stream, keys, idx, M);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
     if (a.qweight2) return plan.lds_a ? launch_pair<true>(a, plan, stream) : launch_pair<false>(a, plan, stream);

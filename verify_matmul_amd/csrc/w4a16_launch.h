@@ -167,9 +167,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // are added in LDS. `slices` workgroups share each group of columns along K; their fp32 sums
 // meet through scratch (counters and flags as in the small-row kernel).
 constexpr int kDecMaxWaves = 8;
+constexpr int kDecodeMinN = 65536;   // plain calls this wide take the decode kernel by default
 constexpr int kDecMaxSlices = 16;
-// Activation items (8 bf16 values) each thread of a decode workgroup holds between the row
-// maximum and the conversion: rows per wave x 64-item chunks per row must not exceed it.
+// Activation items (8 bf16 values) each thread of a decode workgroup keeps in registers between
+// the row maximum and the conversion; a longer slice reads the rest twice.
 constexpr int kDecHeld = 8;
 struct DecodeArgs {
     const uint16_t *A;
@@ -187,7 +188,10 @@ struct DecodeArgs {
     int groups;               // groups of columns (tiles adjacent tiles each)
     int out_bf16;
     int a_off, s_off, z_off, r_off;   // LDS offsets: fragments, scales, zero words, piece sums
+    int mp_log2;              // matrix-core fragments hold rows padded to 2^mp_log2 (4, 8 or 16)
     uint32_t part_bytes;      // bytes of the partials region (bounds the buffer accesses)
+    unsigned long long *amax_keys;   // fused pick: [M] row keys, zero between calls (nullptr: off)
+    int32_t *amax_idx;               // fused pick: [M] output indices
 };
 struct DecodePlan {
     bool mfma;                // false: the one-row dot-product GEMV
@@ -199,20 +203,12 @@ struct DecodePlan {
     size_t lds;
     int a_off, s_off, z_off, r_off;
 };
-// Activation items each thread holds under a plan: rows per wave x 64-item chunks per row.
-inline int decode_held(int M, int K, int tiles, int kw, int slices)
-{
-    const int steps = K / kStepK;
-    const int nwr = (steps + slices - 1) / slices * 4;   // word rows of the longest slice
-    const int nw = tiles * kw;
-    if (M >= nw) return (M + nw - 1) / nw * ((nwr + 63) / 64);
-    const int per = nw / M;                              // waves per row
-    return (nwr + 64 * per - 1) / (64 * per);
-}
-// LDS of a decode plan: 16 row maxima, the activation slice as fp16 fragments (MFMA: 1 KB per
-// step, 16 rows padded with zeros; GEMV: 64 bytes per step), the workgroup's scales and zero
+// Rows (4, 8 or 16, as log2) the matrix-core fragments of M rows are padded to.
+inline int decode_mp_log2(int M) { return M <= 4 ? 2 : M <= 8 ? 3 : 4; }
+// LDS of a decode plan: 16 row maxima, the activation slice as fp16 fragments (MFMA: 4 x 16 bytes
+// per row of the padded rows per step; GEMV: 64 bytes per step), the workgroup's scales and zero
 // words of its groups, and the K pieces' sums (kw - 1 pieces of every tile).
-inline size_t decode_lds_layout(int K, int g, bool mfma, int cols, int tiles, int kw, int slices, bool packed,
+inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int tiles, int kw, int slices, bool packed,
                                 DecodePlan *pl)
 {
     const int steps = K / kStepK;
@@ -221,7 +217,7 @@ inline size_t decode_lds_layout(int K, int g, bool mfma, int cols, int tiles, in
     const size_t groups = (size_t)(smax + spg - 1) / spg + 1;
     const size_t wc = (size_t)tiles * 16 * cols;
     const size_t a_off = 128;
-    const size_t a_bytes = (size_t)smax * (mfma ? 1024 : 64);
+    const size_t a_bytes = (size_t)smax * (mfma ? (size_t)64 << decode_mp_log2(M) : 64);
     const size_t s_off = a_off + a_bytes;
     const size_t s_bytes = groups * wc * 2;
     const size_t z_off = s_off + round_up_sz(s_bytes, 16);
@@ -237,6 +233,8 @@ inline size_t decode_lds_layout(int K, int g, bool mfma, int cols, int tiles, in
     return r_off + r_bytes;
 }
 hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream);
+// Ends a fused greedy pick: idx[m] from the call's row keys, and the keys cleared (one wave).
+hipError_t launch_argmax_finish(unsigned long long *keys, int32_t *idx, int M, hipStream_t stream);
 
 struct ArgmaxArgs {
     const float *logits;
