@@ -417,21 +417,20 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     // call's keys; a one-wave kernel next on the stream turns the keys into indices and clears
     // them. Called by every thread of the workgroup.
     const bool amax = p.amax_keys != nullptr;
-    auto pick = [&](const float (*fin)[kRows]) {
+    unsigned long long rkey[kRows];   // the lane's best key per row so far
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) rkey[r] = 0ull;
+    auto fold = [&](int r, int j, float v) {   // finished output (row_base + r, column n0 + j)
+        if (v == v) {
+            const unsigned long long kj = argmax_key(v, (uint32_t)(n0 + j));
+            rkey[r] = kj > rkey[r] ? kj : rkey[r];
+        }
+    };
+    auto pick = [&]() {
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const int m = row_base + r;
-            unsigned long long k = 0ull;
-            if (holder && m < M) {
-#pragma unroll
-                for (int j = 0; j < kC; ++j) {
-                    const float v = fin[j][r];
-                    if (v == v) {
-                        const unsigned long long kj = argmax_key(v, (uint32_t)(n0 + j));
-                        k = kj > k ? kj : k;
-                    }
-                }
-            }
+            unsigned long long k = holder && m < M ? rkey[r] : 0ull;
 #pragma unroll
             for (int o = 8; o >= 1; o >>= 1) {
                 const unsigned long long other = shfl_xor_u64(k, o);
@@ -457,12 +456,11 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
             }
         }
         if (amax) {
-            float fin[kC][kRows];
 #pragma unroll
             for (int j = 0; j < kC; ++j)
 #pragma unroll
-                for (int r = 0; r < kRows; ++r) fin[j][r] = tot[j][r];
-            pick(fin);
+                for (int r = 0; r < kRows; ++r) fold(r, j, tot[j][r]);
+            pick();
         }
         return;
     }
@@ -515,11 +513,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     }
     __syncthreads();   // every flag seen raised: the other slices' stores have completed
     const bool failed = s_failed != 0;
-    float fin[kC][kRows];   // the finished sums (for the fused pick)
-#pragma unroll
-    for (int j = 0; j < kC; ++j)
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) fin[j][r] = 0.f;
+    constexpr int kBatch = 8;
     if (holder) {
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
@@ -528,29 +522,36 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 #pragma unroll
             for (int v = 0; v < kV; ++v) {
                 const f32x4 own = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
-                f32x4 x[kDecMaxSlices];
-#pragma unroll
-                for (int sp = 0; sp < kDecMaxSlices; ++sp) {
-                    x[sp] = own;
-                    if (sp < P && sp != sl) {
-                        const uint32_t off = (uint32_t)((((size_t)sp * M + m) * N + n0 + 4 * v) * sizeof(float));
-                        x[sp] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kCoherent);
-                    }
-                }
                 f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int sp = 0; sp < kDecMaxSlices; ++sp)
-                    if (sp < P) sum += x[sp];
+                for (int b = 0; b < kDecMaxSlices; b += kBatch) {   // slices in order, kBatch loads in flight
+                    if (b >= P) break;
+                    f32x4 x[kBatch];
+#pragma unroll
+                    for (int i = 0; i < kBatch; ++i) {
+                        const int sp = b + i;
+                        x[i] = own;
+                        if (sp < P && sp != sl) {
+                            const uint32_t off = (uint32_t)((((size_t)sp * M + m) * N + n0 + 4 * v) * sizeof(float));
+                            x[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kCoherent);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < kBatch; ++i)
+                        if (b + i < P) sum += x[i];
+                }
                 if (failed) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
                 store_out(m, v, sum.x, sum.y, sum.z, sum.w);
-                fin[4 * v][r] = sum.x;
-                fin[4 * v + 1][r] = sum.y;
-                fin[4 * v + 2][r] = sum.z;
-                fin[4 * v + 3][r] = sum.w;
+                if (amax) {
+                    fold(r, 4 * v, sum.x);
+                    fold(r, 4 * v + 1, sum.y);
+                    fold(r, 4 * v + 2, sum.z);
+                    fold(r, 4 * v + 3, sum.w);
+                }
             }
         }
     }
-    if (amax) pick(fin);
+    if (amax) pick();
     for (int sp = tid; sp < P; sp += T)
         if (sp != sl) __hip_atomic_store(&flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
