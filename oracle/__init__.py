@@ -50,13 +50,14 @@ def _load():
         lib.w4o_dequant.argtypes = [P, P, P, I64, I64, I64, P]
         lib.w4o_gemm.argtypes = [P, P, P, P, I64, I64, I64, I64, P, I64, P, P]
         lib.w4o_argmax_rows_f32.argtypes = [P, I64, I64, P]
+        lib.w4o_topk_rows_f32.argtypes = [P, I64, I64, I64, P]
         lib.w4o_silu.argtypes = [ctypes.c_double]
         lib.w4o_silu.restype = ctypes.c_double
         lib.w4o_silu_mul.argtypes = [P, P, I64, P]
         lib.w4o_affine_unpack.argtypes = [P, ctypes.c_int, I64, I64, P]
         lib.w4o_affine_gemm.argtypes = [P, P, ctypes.c_int, P, P, I64, I64, I64, I64, P, I64, P, P]
         for f in (lib.w4o_unpack_qweight, lib.w4o_unpack_qzeros, lib.w4o_dequant,
-                  lib.w4o_gemm, lib.w4o_argmax_rows_f32, lib.w4o_silu_mul,
+                  lib.w4o_gemm, lib.w4o_argmax_rows_f32, lib.w4o_topk_rows_f32, lib.w4o_silu_mul,
                   lib.w4o_affine_unpack, lib.w4o_affine_gemm):
             f.restype = ctypes.c_int
         _lib = lib
@@ -143,6 +144,16 @@ def argmax_rows_f32(v: np.ndarray) -> np.ndarray:
     _check(_load().w4o_argmax_rows_f32(_ptr(x), M, N, _ptr(idx)), "argmax")
     return idx
 
+
+
+def topk_rows_f32(v: np.ndarray, k: int) -> np.ndarray:
+    """Per-row k best columns of fp32 values [M, N], best first (ties -> lowest index, NaN never
+    chosen, -1 once a row has nothing left): [M, k] int64."""
+    x = _c(v, np.float32)
+    M, N = x.shape
+    idx = np.empty((M, k), dtype=np.int64)
+    _check(_load().w4o_topk_rows_f32(_ptr(x), M, N, int(k), _ptr(idx)), "topk")
+    return idx
 
 
 def silu(x: float) -> float:

@@ -196,6 +196,41 @@ int w4o_argmax_rows_f32(const float *v, int64_t M, int64_t N, int64_t *idx)
     return 0;
 }
 
+/*
+ * The k best candidates of each row, best first: repeat the greedy selection above k times,
+ * each time over the entries not yet chosen. idx[m * k + r] = the r-th choice of row m (largest
+ * fp32 value first, equal values by smallest column, -0 equal to +0, NaN never chosen), or -1
+ * once the row has no entry left to choose. The pages move only the greedy choice onto the
+ * device (lucebox PR #823); the k best are that choice extended to the next candidates in the
+ * same order, so the first of them is the greedy one.
+ */
+int w4o_topk_rows_f32(const float *v, int64_t M, int64_t N, int64_t k, int64_t *idx)
+{
+    if (!v || !idx || M <= 0 || N <= 0 || k <= 0)
+        return -1;
+    unsigned char *taken = (unsigned char *)malloc((size_t)N);
+    if (!taken)
+        return -2;
+    for (int64_t m = 0; m < M; ++m) {
+        memset(taken, 0, (size_t)N);
+        for (int64_t r = 0; r < k; ++r) {
+            int64_t best = -1;
+            for (int64_t n = 0; n < N; ++n) {
+                float x = v[m * N + n];
+                if (taken[n] || isnan(x))
+                    continue;
+                if (best < 0 || x > v[m * N + best])
+                    best = n;
+            }
+            idx[m * k + r] = best;
+            if (best >= 0)
+                taken[best] = 1;
+        }
+    }
+    free(taken);
+    return 0;
+}
+
 /* ---- gated feed-forward input: SiLU(gate) * up ------------------------------------------ */
 
 /*

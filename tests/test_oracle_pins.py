@@ -257,6 +257,42 @@ def test_argmax_ties_take_lowest_index(orc):
     assert orc.argmax_rows_f32(r).tolist() == np.argmax(r, axis=1).tolist()   # numpy: first max
 
 
+def test_topk_hand_cases(orc):
+    """Worked by hand: best first, equal values by lowest column, -0 equal to +0, NaN never
+    chosen, -1 once a row has run out."""
+    v = np.array([[1, 5, 5, 2],
+                  [3, 3, 3, 3],
+                  [0.0, -0.0, 0.0, -1],
+                  [np.nan, 4, np.nan, 2],
+                  [np.nan, np.nan, np.nan, np.nan]], dtype=np.float32)
+    assert orc.topk_rows_f32(v, 3).tolist() == [[1, 2, 3], [0, 1, 2], [0, 1, 2], [1, 3, -1], [-1, -1, -1]]
+    assert orc.topk_rows_f32(v, 6).tolist()[0] == [1, 2, 3, 0, -1, -1]
+
+
+def test_topk_against_a_stable_sort(orc):
+    """Brute force on small rows by another route: numpy's stable argsort of the negated values
+    orders the non-NaN entries largest first with ties by lowest column (negation maps -0 and +0
+    to the same key as +0 and -0 do to each other); the first k of it, padded with -1, and k = 1
+    is the greedy pick."""
+    rng = np.random.default_rng(16)
+    for trial in range(40):
+        M, N = int(rng.integers(1, 5)), int(rng.integers(1, 40))
+        r = rng.integers(-3, 4, size=(M, N)).astype(np.float32)   # many ties
+        r[rng.random((M, N)) < 0.1] = np.nan
+        r[rng.random((M, N)) < 0.1] = -0.0
+        for k in (1, 2, 5, N, N + 3):
+            got = orc.topk_rows_f32(r, k)
+            for m in range(M):
+                ok = np.flatnonzero(~np.isnan(r[m]))
+                order = ok[np.argsort(-r[m][ok], kind="stable")].tolist()
+                want = (order + [-1] * k)[:k]
+                assert got[m].tolist() == want, (trial, m, k)
+            if k == 1:
+                greedy = orc.argmax_rows_f32(r)
+                has = ~np.all(np.isnan(r), axis=1)
+                assert got[has, 0].tolist() == greedy[has].tolist()
+
+
 def test_oracle_rejects_bad_arguments(orc):
     inp = synth.make_random(16, 1, 64, 16, 32, symmetric=True)
     with pytest.raises(ValueError):
