@@ -12,14 +12,23 @@ Algorithmic bytes per call = qweight (K*N/2) + scales (2*K*N/g) + qzeros (K*N/(2
 + activations (2*M*K) + outputs (4*M*N for fp32). Re-reads, padding and split-K scratch are
 not counted.
 
-Timed regions (all on the library's stream, inputs resident in HBM):
+Warm-up: W steps, then more until the device has been busy for 0.3 s (its clock ramps up over
+the first tens of milliseconds of work). Timed regions (all on the library's stream, inputs
+resident in HBM):
   1. K steps back to back -> `value` (whole-step throughput, wall clock between synchronizes);
-  2. the same K steps with a HIP event pair around every launch -> `per_m` (us per call);
-  3. the step's dominant call alone, K launches back to back between one event pair ->
-     `roofline.achieved` (algorithmic bytes per launch / average launch duration);
-  4. context only: that call on one weight copy, cache-resident (`context.cache_resident`,
-     L2/MALL, not HBM), and a plain device copy of one weight copy per launch
-     (`context.copy_ceiling`, bytes read + written).
+  2. each row count's call alone, K launches back to back (rotating weight copies) between one
+     HIP event pair -> `per_m` us_per_call (device time per call); the row count with the most
+     device time is the dominant call, whose algorithmic bytes / us_per_call is
+     `roofline.achieved`;
+  3. context only: the K steps again with an event pair around every launch (per_m
+     us_lone_event_pair, which includes the dispatch gap before each launch); each row count's
+     call captured into a HIP graph (one launch per rotating copy) and replayed (per_m
+     us_per_call_graph_replay: no host work between launches); the dominant call
+     on one weight copy, cache-resident (`context.cache_resident`, L2/MALL, not HBM); a plain
+     streaming read of one rotating copy of the packed weights per launch, replayed from a HIP
+     graph (`context.read_ceiling`, w4a16_stream_read: the measured ceiling for reading those
+     bytes);
+     a device copy of the same bytes (`context.copy`, bytes read + written).
 `roofline.traffic` is the HBM bytes per launch of that call from the committed rocprofv3 counter
 summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or null when the
 kernel sources changed since the counters were taken.
@@ -61,6 +70,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16 matrix cores
 POOL_BYTES = 768 * 2 ** 20      # rotating weight pool, 3x the 256 MB last-level cache
+WARM_SECONDS = 0.3              # minimum device-busy warm-up before any timing
 
 
 def algorithmic_bytes(M, K, N, g, symmetric, out_bytes=4, matrices=1):
@@ -152,7 +162,24 @@ def cpu_baseline(wl, inp, ms, seconds, gate=None, one=None):
     return rec
 
 
-def load_traffic(workload, M, kernel="w4a16_gemm_kernel"):
+def warm_up(step, n):
+    """n untimed steps, then more until the device has been busy for WARM_SECONDS: its clock ramps
+    up over the first tens of milliseconds of work, which a short warm-up would leave in the
+    timing."""
+    import torch
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    i, t0 = n, time.perf_counter()
+    while time.perf_counter() - t0 < WARM_SECONDS:
+        step(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def load_traffic(workload, M, kernel):
     """HBM bytes per launch of the M-row call, from the committed rocprofv3 counter summary, if it
     still matches the kernel source; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_M{M}.json")
@@ -279,9 +306,7 @@ def main():
                 raise RuntimeError(f"{'w4a16_gemm_gate_up_ex' if pair else 'w4a16_gemm_ex'} failed: "
                                    f"{lib.w4a16_last_error().decode()}")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
 
     # timed region 1: the steps back to back, as a decode loop issues them -> value
     torch.cuda.synchronize()
@@ -293,89 +318,9 @@ def main():
     step_bytes = sum(algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat) for M in ms)
     value = step_bytes * args.steps / wall / 1e9
 
-    # timed region 2: the same steps with a HIP event pair around every launch, on the stream the
-    # kernels run on -> per-row-count duration and the roofline of the dominant launch
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs)
-    torch.cuda.synchronize()
-
-    per_m = {}
-    dom, dom_time = None, -1.0
-    for j, M in enumerate(ms):
-        d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
-        b = algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat)
-        us = float(np.mean(d))
-        kern, spl, wk, tcols = vm.w4a16_plan(M, N, K, g)
-        per_m[str(M)] = {"us_per_call": round(us, 3), "us_median": round(float(np.median(d)), 3),
-                         "us_p10": round(float(np.percentile(d, 10)), 3),
-                         "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
-                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
-        if pair:   # 128-column tiles of the 2N-wide pair (64 output columns of each matrix)
-            per_m[str(M)].update({"kernel": "mfma, gated pair", "tile_cols": 128})
-            if args.splits or args.waves_k:
-                per_m[str(M)].update({"splits": args.splits or "default", "waves_k": args.waves_k or "default"})
-        else:
-            per_m[str(M)].update({"kernel": "gemv" if kern == 0 else "mfma", "splits": args.splits or spl,
-                                  "waves_k": args.waves_k or wk, "tile_cols": args.tile_cols or tcols})
-        if float(np.sum(d)) > dom_time:
-            dom, dom_time = M, float(np.sum(d))
-    # the dominant launch: the row count whose calls take the most time in a step
-    dm = per_m[str(dom)]
-
-    # output layer: the greedy pick over each row of logits, timed on its own (it re-reads the
-    # logits; not part of the algorithmic bytes of the matmul)
-    if wl.argmax:
-        for j, M in enumerate(ms):
-            logits = pool[0][4][M]
-            idx = torch.empty((M,), dtype=torch.int32, device=dev)
-            vm.w4a16_argmax_rows(logits, idx)
-            torch.cuda.synchronize()
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            for _ in range(args.steps):
-                vm.w4a16_argmax_rows(logits, idx)
-            a1.record(stream)
-            torch.cuda.synchronize()
-            us = a0.elapsed_time(a1) * 1e3 / args.steps
-            per_m[str(M)]["argmax_us_per_call"] = round(us, 3)
-            per_m[str(M)]["argmax_GBps"] = round(4 * M * N / us / 1e3, 1)
-            # the same pick fused into the GEMM's epilogue (one launch, no logits re-read),
-            # a lone event pair around each call as for us_per_call
-            fd = []
-            for i in range(args.steps):
-                qw, sc, qz, a, outs = pool[(i * len(ms) + j) % R]
-                f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                f0.record(stream)
-                vm.w4a16_gemm_argmax(a[:M], qw, sc, qz, g, outs[M], idx)
-                f1.record(stream)
-                fd.append((f0, f1))
-            torch.cuda.synchronize()
-            per_m[str(M)]["fused_gemm_argmax_us_per_call"] = round(
-                float(np.mean([e0.elapsed_time(e1) * 1e3 for e0, e1 in fd])), 3)
-
-    # timed region 3: the dominant launch alone, K times back to back (rotating weight copies)
-    # between one HIP event pair on its stream -> its average duration without the per-launch
-    # dispatch gap that a lone event pair adds
-    jd = list(ms).index(dom)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        fn(*calls[i % R][jd][1])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
-    achieved = dm["bytes"] / us_dom / 1e3   # GB/s
-    traffic = load_traffic(args.workload + ("_gate_up" if pair else ""), dom)
-
-    # context only, never `value`: (a) the dominant launch on one weight copy K times, which then
-    # stays in the L2s and the 256 MB last-level cache (a cache-resident rate, not an HBM one);
-    # (b) a plain device copy of one rotating weight copy per launch in this process (its bytes
-    # read plus written), as the streaming ceiling of plain data movement on these buffers
     def back_to_back(launch):
+        """Average device time per launch: K launches back to back between one HIP event pair on
+        the library's stream."""
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         c0.record(stream)
@@ -385,17 +330,150 @@ def main():
         torch.cuda.synchronize()
         return c0.elapsed_time(c1) * 1e3 / args.steps
 
+    # timed region 2: each row count's call alone, K launches back to back (rotating weight
+    # copies) -> per_m us_per_call (device time per call) and the roofline of the dominant call
+    per_m = {}
+    for j, M in enumerate(ms):
+        us = back_to_back(lambda i, j=j: fn(*calls[i % R][j][1]))
+        b = algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat)
+        kern, spl, wk, tcols = vm.w4a16_plan(M, N, K, g)
+        per_m[str(M)] = {"us_per_call": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
+        if pair:   # 128-column tiles of the 2N-wide pair (64 output columns of each matrix)
+            per_m[str(M)].update({"kernel": "w4a16_gemm_kernel (mfma, gated pair)", "tile_cols": 128})
+            if args.splits or args.waves_k:
+                per_m[str(M)].update({"splits": args.splits or "default", "waves_k": args.waves_k or "default"})
+        elif kern >= 2 and not (args.splits or args.waves_k or args.tile_cols):
+            per_m[str(M)].update({"kernel": "decode_kernel (" + ("gemv" if kern == 2 else "mfma") + ")",
+                                  "slices": spl, "waves_k": wk, "tile_cols": tcols})
+        else:
+            kern_old = kern if kern < 2 else (0 if M == 1 else 1)
+            per_m[str(M)].update({"kernel": "w4a16_gemm_kernel (" + ("gemv" if kern_old == 0 else "mfma") + ")",
+                                  "splits": args.splits or (spl if kern < 2 else "default"),
+                                  "waves_k": args.waves_k or (wk if kern < 2 else "default"),
+                                  "tile_cols": args.tile_cols or (tcols if kern < 2 else "default")})
+    # the dominant call: the row count whose call takes the most device time in a step
+    dom = max(ms, key=lambda M: per_m[str(M)]["us_per_call"])
+    dm = per_m[str(dom)]
+    us_dom = dm["us_per_call"]
+
+    # context: the same steps with a HIP event pair around every launch (each pair also times the
+    # dispatch gap in front of its launch)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs)
+    torch.cuda.synchronize()
+    for j, M in enumerate(ms):
+        d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
+        per_m[str(M)].update({"us_lone_event_pair": round(float(np.mean(d)), 3),
+                              "us_lone_event_pair_median": round(float(np.median(d)), 3)})
+
+    # output layer: the greedy pick over each row of logits on its own (it re-reads the logits;
+    # not part of the algorithmic bytes of the matmul), and the same pick fused into the GEMM's
+    # epilogue (one launch, no logits re-read), both back to back
+    if wl.argmax:
+        for j, M in enumerate(ms):
+            idx = torch.empty((M,), dtype=torch.int32, device=dev)
+            logits = pool[0][4][M]
+            vm.w4a16_argmax_rows(logits, idx)
+            aargs = (vp(logits), M, N, vp(idx), sp)
+            us = back_to_back(lambda i, aargs=aargs: lib.w4a16_argmax_rows(*aargs))
+            per_m[str(M)]["argmax_us_per_call"] = round(us, 3)
+            per_m[str(M)]["argmax_GBps"] = round(4 * M * N / us / 1e3, 1)
+
+            fargs = [(vp(a), vp(qw), vp(sc), vp(qz), g, M, N, K, vp(outs[M]), 0, vp(idx), sp)
+                     for qw, sc, qz, a, outs in pool]   # pre-marshalled, as the plain calls
+            for i in range(R):   # warm-up: the first call takes the call's scratch
+                if lib.w4a16_gemm_argmax(*fargs[i]) != 0:
+                    raise RuntimeError(f"w4a16_gemm_argmax failed: {lib.w4a16_last_error().decode()}")
+            per_m[str(M)]["fused_gemm_argmax_us_per_call"] = round(
+                back_to_back(lambda i, fargs=fargs: lib.w4a16_gemm_argmax(*fargs[i % R])), 3)
+            # the 8 best columns per row, picked in the same launch
+            top = torch.empty((M, 8), dtype=torch.int32, device=dev)
+            targs = [(vp(a), vp(qw), vp(sc), vp(qz), g, M, N, K, vp(outs[M]), 0, 8, vp(top), sp)
+                     for qw, sc, qz, a, outs in pool]
+            for i in range(R):
+                if lib.w4a16_gemm_topk(*targs[i]) != 0:
+                    raise RuntimeError(f"w4a16_gemm_topk failed: {lib.w4a16_last_error().decode()}")
+            per_m[str(M)]["fused_gemm_top8_us_per_call"] = round(
+                back_to_back(lambda i, targs=targs: lib.w4a16_gemm_topk(*targs[i % R])), 3)
+
+    achieved = dm["bytes"] / us_dom / 1e3   # GB/s
+    dom_kernel = dm["kernel"].split(" ")[0]
+    traffic = load_traffic(args.workload + ("_gate_up" if pair else ""), dom, dom_kernel)
+
+    # context only, never `value`: (a) the dominant launch on one weight copy K times, which then
+    # stays in the L2s and the 256 MB last-level cache (a cache-resident rate, not an HBM one);
+    # (b) a plain streaming read of one rotating copy of the packed weights per launch
+    # (w4a16_stream_read: 16-byte non-temporal loads, nothing else), the measured ceiling of
+    # reading these bytes from HBM; (c) a device copy of the same bytes per launch (read + write)
+    jd = list(ms).index(dom)
     resident_us = back_to_back(lambda i: fn(*calls[0][jd][1]))
-    sink = torch.empty_like(pool[0][0])
+
+    def graph_replayed(issue):
+        """Average device time per launch with no host work between launches: issue(stream) makes
+        R launches (one per rotating copy) on a side stream, run once eagerly (it takes its
+        scratch then), captured once into a HIP graph, and the graph replayed back to back."""
+        gs = torch.cuda.Stream()
+        gsp = ctypes.c_void_p(gs.cuda_stream)
+        with torch.cuda.stream(gs):
+            issue(gsp)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            issue(gsp)
+        torch.cuda.synchronize()
+        graph.replay()
+        reps = max(1, args.steps // R)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        return c0.elapsed_time(c1) * 1e3 / (reps * R)
+
+    def issue_calls(j):
+        def issue(gsp):
+            for r in range(R):
+                if fn(*(calls[r][j][1][:-1] + (gsp,))) != 0:
+                    raise RuntimeError(f"call failed: {lib.w4a16_last_error().decode()}")
+        return issue
+
+    for j, M in enumerate(ms):
+        try:
+            per_m[str(M)]["us_per_call_graph_replay"] = round(graph_replayed(issue_calls(j)), 3)
+        except RuntimeError as e:   # context only: a call that cannot be captured leaves it out
+            per_m[str(M)]["us_per_call_graph_replay"] = None
+            per_m[str(M)]["graph_replay_error"] = str(e)[:200]
+
+    sink = torch.zeros((4,), dtype=torch.int32, device=dev)
     read_bytes = pool[0][0].numel() * 4
-    read_us = back_to_back(lambda i: sink.copy_(pool[1 + i % (R - 1)][0]))
+
+    def issue_reads(gsp):
+        for r in range(R):
+            if lib.w4a16_stream_read(vp(pool[r][0]), ctypes.c_size_t(read_bytes), vp(sink), gsp) != 0:
+                raise RuntimeError(f"w4a16_stream_read failed: {lib.w4a16_last_error().decode()}")
+    ceil_us = graph_replayed(issue_reads)
+    dst = torch.empty_like(pool[0][0])
+    copy_us = back_to_back(lambda i: dst.copy_(pool[1 + i % (R - 1)][0]))
+    ceil_gbps = read_bytes / ceil_us / 1e3
     context = {"cache_resident": {"what": "the dominant launch on one weight copy, back to back: L2/MALL, not HBM",
                                   "us_per_launch": round(resident_us, 3),
                                   "GBps": round(dm["bytes"] / resident_us / 1e3, 1)},
-               "copy_ceiling": {"what": "device copy of one rotating weight copy per launch (torch copy_), "
-                                        "bytes read + written",
-                                "bytes": 2 * read_bytes, "us_per_launch": round(read_us, 3),
-                                "GBps": round(2 * read_bytes / read_us / 1e3, 1)}}
+               "read_ceiling": {"what": "w4a16_stream_read over one rotating copy of the packed weights per launch "
+                                        "(plain 16-byte non-temporal loads, 16 KiB per workgroup), replayed from "
+                                        "a HIP graph",
+                                "bytes": read_bytes, "us_per_launch": round(ceil_us, 3),
+                                "GBps": round(ceil_gbps, 1), "frac_of_peak": round(ceil_gbps / PEAK_HBM_GBPS, 4),
+                                "dominant_call_frac_of_ceiling": round(achieved / ceil_gbps, 4)},
+               "copy": {"what": "device copy of one rotating copy of the packed weights per launch (torch copy_), "
+                                "bytes read + written",
+                        "bytes": 2 * read_bytes, "us_per_launch": round(copy_us, 3),
+                        "GBps": round(2 * read_bytes / copy_us / 1e3, 1)}}
 
     rec = {
         "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
@@ -417,11 +495,11 @@ def main():
                    "launch": "default" if not (args.splits or args.waves_k or args.tile_cols) else
                    f"splits={args.splits or 'default'} waves_k={args.waves_k or 'default'} "
                    f"tile_cols={args.tile_cols or 'default'}"},
-        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel ({dm['kernel']}, M={dom})", "M": dom,
+        "roofline": {"bound": "hbm", "kernel": f"{dm['kernel']}, M={dom}", "M": dom,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "launches": args.steps, "bytes_per_launch": dm["bytes"],
-                     "us_per_launch": round(us_dom, 3), "us_per_launch_lone_event_pair": dm["us_per_call"]},
+                     "us_per_launch": round(us_dom, 3), "us_per_launch_lone_event_pair": dm["us_lone_event_pair"]},
         "per_m": per_m,
         "context": context,
     }
@@ -509,9 +587,7 @@ def run_affine(args, lib):
             if rc != 0:
                 raise RuntimeError(f"affine GEMM failed: {lib.w4a16_last_error().decode()}")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -560,7 +636,8 @@ def run_affine(args, lib):
         "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine{', split planes' if bits == 8 else ''}{', gated pair' if pair else ''}, M={dom})", "M": dom,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": load_traffic(f"ffn_up_affine{bits}" + ("_gate_up" if pair else ""), dom),
+                     "traffic": load_traffic(f"ffn_up_affine{bits}" + ("_gate_up" if pair else ""), dom,
+                                             "w4a16_gemm_kernel"),
                      "launches": args.steps,
                      "bytes_per_launch": bdom, "us_per_launch": round(us_dom, 3),
                      "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
@@ -642,9 +719,7 @@ def run_prefill(args, lib):
             if evs is not None:
                 evs[i][j][1].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)

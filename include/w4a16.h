@@ -127,21 +127,21 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
  * or scales would not fit in a workgroup's LDS is refused with W4A16_ERR_INVALID_ARG. Same
  * operation, arguments, accuracy contract (with the activations rescaled per row and K slice) and
  * determinism as w4a16_gemm.
- * idx: NULL, or int32 [M] device for the fused greedy pick of w4a16_gemm_argmax. Meant for tests
- * and tuning sweeps.
+ * topk, idx: 0 and NULL, or the fused pick of w4a16_gemm_topk (k = topk, idx int32 [M, topk]
+ * device). Meant for tests and tuning sweeps.
  */
 int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t *scales,
                          const uint32_t *qzeros, int group_size, int M, int N, int K,
                          void *out, int out_dtype, int slices, int tiles, int kw, int tile_cols,
-                         int ring, int32_t *idx, hipStream_t stream);
+                         int ring, int topk, int32_t *idx, hipStream_t stream);
 
 /* The decode kernel's launch for a shape and explicit knobs (0 = default), checked exactly as
  * w4a16_gemm_decode_ex checks it, without any device work: W4A16_OK and, if plan_out is not NULL,
  * plan_out[0..5] = slices, tiles, kw, tile_cols, ring, LDS bytes per workgroup; or the status and
  * w4a16_last_error() that w4a16_gemm_decode_ex would return. packed_zeros: nonzero for packed zero
- * points (qzeros given). Host only. */
+ * points (qzeros given); topk: 0, or the k of a fused pick. Host only. */
 int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles,
-                      int kw, int tile_cols, int ring, int *plan_out);
+                      int kw, int tile_cols, int ring, int topk, int *plan_out);
 
 /* The launch w4a16_gemm picks for a shape (symmetric zero points): *kernel = 0 for the small-row
  * kernel's one-row GEMV, 1 for its MFMA GEMM, with *splits, *waves_k and *tile_cols as in
@@ -152,14 +152,34 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
                int *tile_cols);
 
 /*
- * w4a16_gemm and the greedy pick in one launch (the output layer): out as in w4a16_gemm, and
- * idx[m] = smallest n with out[m][n] (in fp32, before any bf16 rounding) equal to the row
- * maximum, with the conventions of w4a16_argmax_rows. The pick is made in the GEMM's epilogue
- * from the values it writes, so the logits are not read back. idx: int32 [M] device.
+ * w4a16_gemm and the greedy pick (the output layer): out as in w4a16_gemm, and idx[m] = smallest
+ * n with out[m][n] (in fp32, before any bf16 rounding) equal to the row maximum, with the
+ * conventions of w4a16_argmax_rows. The pick is made in the GEMM's epilogue from the values it
+ * writes, so the logits are not read back. On matrices of 65536 columns or more the whole pick
+ * runs inside the GEMM's launch (w4a16_gemm_topk with k = 1); on narrower ones each column tile
+ * leaves its keys in the stream's scratch and a small kernel next on the stream reduces them.
+ * idx: int32 [M] device.
  */
 int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales,
                       const uint32_t *qzeros, int group_size, int M, int N, int K,
                       void *out, int out_dtype, int32_t *idx, hipStream_t stream);
+
+/*
+ * w4a16_gemm and the k best columns of each row in one launch (the output layer of a verify
+ * pass): out as in w4a16_gemm, and idx[m][r] (int32 [M, k] device) = the column of row m's r-th
+ * largest output, decided in fp32 before any bf16 rounding, largest first, equal values by lowest
+ * column, -0 equal to +0, NaN never chosen, -1 once the row has no column left (k > N or NaN
+ * outputs). idx[m][0] is the greedy pick of w4a16_gemm_argmax (which gives 0, not -1, for a row
+ * with no number). The lucebox PR #823 description
+ * moves the greedy choice over the vocabulary row onto the device; the k best extend that choice
+ * to the next candidates in the same order. k in 1..8. Each group of columns keeps its k best per
+ * row and the last group to finish merges them, inside the GEMM's launch: no logits read back, no
+ * second launch. Runs on the decode kernel (w4a16_gemm_decode_ex's default launch for the shape),
+ * whatever N. Uses the stream's scratch (a counter, and groups x M x k 64-bit keys). Deterministic.
+ */
+int w4a16_gemm_topk(const void *A, const uint32_t *qweight, const uint16_t *scales,
+                    const uint32_t *qzeros, int group_size, int M, int N, int K,
+                    void *out, int out_dtype, int k, int32_t *idx, hipStream_t stream);
 
 /*
  * out[M,N] = A x W for many rows (prompt processing), on the matrix cores: the same operation,
@@ -315,6 +335,15 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
 int w4a16_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q_out, hipStream_t stream);
 int w4a16_dequant_f32(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                       int group_size, int K, int N, float *w_out, hipStream_t stream);
+
+/*
+ * Measurement hook: a plain streaming read of `bytes` bytes at `buf` (16-byte non-temporal loads,
+ * each workgroup one contiguous 16 KiB chunk), the ceiling that the weight-streaming kernels'
+ * HBM rate is compared with. Reads the buffer once; stores one word to `sink` (device, 4 bytes)
+ * only if the XOR of what a thread read equals a fixed constant. bytes: a positive multiple of
+ * 16; buf 16-byte aligned.
+ */
+int w4a16_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
 /* Release every scratch buffer the library holds (all devices, all streams). The caller
  * must ensure no library work is still running. Returns W4A16_OK or W4A16_ERR_HIP. */

@@ -138,27 +138,70 @@ def test_decode_workloads(gu, name, M):
     gu.say(f"[decode workload] {name} M={M} worst err/tol {frac:.3e}")
 
 
-@pytest.mark.parametrize("K,N,g,sym", [(512, 1000, 128, True), (1024, 4104, 64, False), (512, 131072, 128, True)])
-def test_decode_fused_pick(gu, K, N, g, sym):
-    """The greedy pick fused into the decode kernel's epilogue, single-slice and through the slice
-    reducer: logits bit-identical to the same launch without the pick, indices equal to the
-    separate pick (w4a16_argmax_rows) over those fp32 logits, logits within the bar."""
+@pytest.mark.parametrize("K,N,g,sym", [(512, 1000, 128, True), (1024, 4104, 64, False), (512, 131072, 128, True),
+                                      (64, 256, 32, False)])
+def test_decode_fused_topk(gu, K, N, g, sym):
+    """The k best columns per row picked inside the decode kernel's launch, single-slice and
+    through the slice reducer, on every launch knob: logits bit-identical to the same launch
+    without the pick and within the bar against the oracle, indices equal to the oracle's k best
+    over those fp32 logits (both sides decide in fp32: bit-exact), k = 1 equal to the separate
+    greedy pick. Ragged groups of columns; K = 64 gives slices too short to hold the outputs in
+    the fragments' LDS, which the plan enlarges."""
     inp = synth.make_random(K + N + 7, 16, K, N, g, symmetric=sym)
     d = gu.DevInputs(inp)
     for M in (1, 2, 5, 16):
         y_ref, bound = oracle.gemm(inp.act[:M], inp.qweight, inp.scales, inp.qzeros, g)
-        for launch in ((0, 0, 0, 0, 0), (1, 4, 1, 64, 4), (3, 2, 2, 64, 3), (4, 4, 1, 128, 2)):
-            if refused(launch, M, N, K, g, not sym):
-                continue
-            gu.say(f"[decode pick] K={K} N={N} M={M} launch={launch}")
-            plain = run(gu, d, M, *launch)
-            out = torch.full((M, N), float("nan"), dtype=torch.float32, device=gu.DEV)
-            idx = torch.full((M,), -5, dtype=torch.int32, device=gu.DEV)
-            vm.w4a16_gemm_decode_ex(d.act[:M], d.qweight, d.scales, d.qzeros, g, out, *launch, idx=idx)
-            sep = torch.empty((M,), dtype=torch.int32, device=gu.DEV)
-            vm.w4a16_argmax_rows(out, sep)
-            torch.cuda.synchronize()
-            y = out.double().cpu().numpy()
-            assert np.array_equal(y, plain)
-            assert idx.cpu().tolist() == sep.cpu().tolist() == np.argmax(y, axis=1).tolist()
-            parity.check_close(y, y_ref, bound, f"pick K={K} N={N} M={M} {launch}")
+        for launch in ((0, 0, 0, 0, 0), (1, 4, 1, 64, 4), (3, 2, 2, 64, 3), (4, 4, 1, 128, 2), (1, 8, 1, 128, 4)):
+            for k in (1, 3, 8):
+                try:
+                    vm.w4a16_decode_plan(M, N, K, g, not sym, *launch, topk=k)
+                except vm.W4A16Error:
+                    continue   # refused on the host (K steps or LDS); tested on the CPU
+                gu.say(f"[decode topk] K={K} N={N} M={M} launch={launch} k={k}")
+                plain = run(gu, d, M, *launch)
+                out = torch.full((M, N), float("nan"), dtype=torch.float32, device=gu.DEV)
+                idx = torch.full((M, k), -5, dtype=torch.int32, device=gu.DEV)
+                vm.w4a16_gemm_decode_ex(d.act[:M], d.qweight, d.scales, d.qzeros, g, out, *launch, idx=idx)
+                torch.cuda.synchronize()
+                y = out.double().cpu().numpy()
+                assert np.array_equal(y, plain)
+                got = idx.cpu().numpy().astype(np.int64)
+                assert np.array_equal(got, oracle.topk_rows_f32(out.cpu().numpy(), k)), (M, launch, k)
+                if k == 1:
+                    sep = torch.empty((M,), dtype=torch.int32, device=gu.DEV)
+                    vm.w4a16_argmax_rows(out, sep)
+                    torch.cuda.synchronize()
+                    assert got[:, 0].tolist() == sep.cpu().tolist()
+                parity.check_close(y, y_ref, bound, f"topk K={K} N={N} M={M} {launch} k={k}")
+
+
+def test_decode_topk_rows_that_run_out(gu):
+    """Ties and rows with fewer numbers than k: all-zero activations make every output of a row
+    equal (picked by lowest column); NaN scales make their columns' outputs NaN, never picked, so a
+    row with four numbers gives four columns and then -1, and a row with none gives -1 throughout
+    (w4a16_gemm_argmax gives 0 there)."""
+    K, N, g = 32, 8, 32
+    inp = synth.make_random(4242, 4, K, N, g, symmetric=True)
+    d = gu.DevInputs(inp)
+    out = torch.empty((4, N), dtype=torch.float32, device=gu.DEV)
+    idx = torch.full((4, 8), -5, dtype=torch.int32, device=gu.DEV)
+    vm.w4a16_gemm_topk(d.act[:4], d.qweight, d.scales, None, g, out, idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), oracle.topk_rows_f32(out.cpu().numpy(), 8))
+    zero = torch.zeros((4, K), dtype=torch.int16, device=gu.DEV)
+    vm.w4a16_gemm_topk(zero, d.qweight, d.scales, None, g, out, idx)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [list(range(8))] * 4
+    nan_half = d.scales.clone()
+    nan_half[:, 1::2] = 0x7E00   # fp16 NaN scale on the odd columns
+    vm.w4a16_gemm_topk(d.act[:4], d.qweight, nan_half, None, g, out, idx)
+    torch.cuda.synchronize()
+    logits = out.cpu().numpy()
+    assert np.all(np.isnan(logits[:, 1::2])) and not np.any(np.isnan(logits[:, 0::2]))
+    got = idx.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, oracle.topk_rows_f32(logits, 8))
+    assert np.all(got[:, 4:] == -1) and np.all(got[:, :4] % 2 == 0)
+    nan_all = torch.full_like(d.scales, 0x7E00)
+    vm.w4a16_gemm_topk(d.act[:4], d.qweight, nan_all, None, g, out, idx)
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [[-1] * 8] * 4

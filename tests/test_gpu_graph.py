@@ -97,9 +97,9 @@ def test_graph_replay_matches_the_oracle(gu):
 
 def test_graph_replay_of_the_wide_matrix_kernel(gu):
     """The same on a matrix wide enough for the decode kernel (the output layer's path): default
-    launches at one, five and sixteen rows (K slices exchanged through slice flags), the fused pick
-    on it (the finishing kernel clears the row keys in every replay), and an explicit launch of
-    three slices with the pick."""
+    launches at one, five and sixteen rows (K slices exchanged through slice flags), the fused
+    greedy pick and the fused top-8 on it (the last group to finish lowers the pick's counter in
+    every replay), and an explicit launch of three slices with a top-4."""
     K, N, g = 1024, 70000, 128           # 137 groups of 512 columns, the last one ragged
     w = synth.make_random(9201, 16, K, N, g, symmetric=False)
     d = gu.DevInputs(w)
@@ -108,7 +108,9 @@ def test_graph_replay_of_the_wide_matrix_kernel(gu):
     o_pick = torch.empty((5, N), dtype=torch.float32, device=gu.DEV)
     o_ex = torch.empty((16, N), dtype=torch.float32, device=gu.DEV)
     idx = torch.full((5,), -1, dtype=torch.int32, device=gu.DEV)
-    idx_ex = torch.full((16,), -1, dtype=torch.int32, device=gu.DEV)
+    idx_ex = torch.full((16, 4), -1, dtype=torch.int32, device=gu.DEV)
+    o_top = torch.empty((5, N), dtype=torch.float32, device=gu.DEV)
+    idx_top = torch.full((5, 8), -1, dtype=torch.int32, device=gu.DEV)
     for M in (1, 5, 16):
         kern, slices, kw, cols = vm.w4a16_plan(M, N, K, g)
         gu.say(f"[graph wide] default plan M={M}: kernel={kern} slices={slices} kw={kw} tile_cols={cols}")
@@ -119,6 +121,7 @@ def test_graph_replay_of_the_wide_matrix_kernel(gu):
             vm.w4a16_gemm(a_buf[:M], d.qweight, d.scales, d.qzeros, g, outs[M])
         vm.w4a16_gemm_argmax(a_buf[:5], d.qweight, d.scales, d.qzeros, g, o_pick, idx)
         vm.w4a16_gemm_decode_ex(a_buf[:16], d.qweight, d.scales, d.qzeros, g, o_ex, 3, 8, 1, 64, 4, idx=idx_ex)
+        vm.w4a16_gemm_topk(a_buf[:5], d.qweight, d.scales, d.qzeros, g, o_top, idx_top)
 
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -133,10 +136,11 @@ def test_graph_replay_of_the_wide_matrix_kernel(gu):
     for r in range(REPLAYS):
         act = synth.f32_to_bf16_bits(rng.standard_normal((16, K)).astype(np.float32) * np.float32(1 + r))
         a_buf.copy_(torch.from_numpy(act.view(np.int16)))
-        for t in (*outs.values(), o_pick, o_ex):
+        for t in (*outs.values(), o_pick, o_ex, o_top):
             t.fill_(float("nan"))
         idx.fill_(-1)
         idx_ex.fill_(-1)
+        idx_top.fill_(-1)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -151,7 +155,10 @@ def test_graph_replay_of_the_wide_matrix_kernel(gu):
         assert np.array_equal(idx.cpu().numpy().astype(np.int64), oracle.argmax_rows_f32(logits)), f"replay {r}"
         logits = o_ex.cpu().numpy()
         parity.check_close(logits, y16, b16, f"replay {r}: three-slice launch")
-        assert np.array_equal(idx_ex.cpu().numpy().astype(np.int64), oracle.argmax_rows_f32(logits)), f"replay {r}"
+        assert np.array_equal(idx_ex.cpu().numpy().astype(np.int64), oracle.topk_rows_f32(logits, 4)), f"replay {r}"
+        logits = o_top.cpu().numpy()
+        parity.check_close(logits, y5, b5, f"replay {r}: top-8 logits")
+        assert np.array_equal(idx_top.cpu().numpy().astype(np.int64), oracle.topk_rows_f32(logits, 8)), f"replay {r}"
 
 
 def test_capture_that_needs_scratch_is_refused(gu):

@@ -200,3 +200,16 @@ def test_errors_do_not_touch_the_device(gu):
         vm.w4a16_gemm_ex(d.act[:1], d.qweight, d.scales, None, 128, out, 999, 1)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_stream_read_hook_reads_without_writing(gu):
+    """The read-ceiling hook reads any size (a ragged last workgroup included) and leaves its
+    inputs and, unless the fold hits its constant, its sink untouched."""
+    for nbytes in (16, 16 * 1024, 16 * 1024 + 48, 3 * 2 ** 20 + 16 * 77):
+        buf = torch.arange(nbytes // 4, dtype=torch.int32, device=gu.DEV)
+        before = buf.clone()
+        sink = torch.full((4,), 7, dtype=torch.int32, device=gu.DEV)
+        vm.w4a16_stream_read(buf, sink)
+        torch.cuda.synchronize()
+        assert torch.equal(buf, before)
+        assert sink.cpu().tolist() == [7, 7, 7, 7]

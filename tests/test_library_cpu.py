@@ -122,6 +122,11 @@ def test_aux_entry_points_reject_bad_arguments(lib):
     assert lib.w4a16_argmax_rows(A, 0, 10, O, None) == -1
     assert lib.w4a16_argmax_rows(A, 1, 0, O, None) == -1
     assert lib.w4a16_argmax_rows(A + 4, 1, 10, O, None) == -2
+    assert lib.w4a16_stream_read(None, 64, O, None) == -1
+    assert lib.w4a16_stream_read(A, 64, None, None) == -1
+    assert lib.w4a16_stream_read(A, 0, O, None) == -1
+    assert lib.w4a16_stream_read(A, 40, O, None) == -1
+    assert lib.w4a16_stream_read(A + 4, 64, O, None) == -2
     assert lib.w4a16_unpack_u8(Q, 12, 8, O, None) == -1
     assert lib.w4a16_unpack_u8(Q, 16, 6, O, None) == -1
     assert lib.w4a16_dequant_f32(Q, S, None, 64, 96, 8, O, None) == -1

@@ -16,9 +16,9 @@ def lib():
     return vm.load()
 
 
-def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128):
+def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128, topk=0):
     """The host-only planner: the same checks as w4a16_gemm_decode_ex, no device work."""
-    return lib.w4a16_decode_plan(M, N, K, g, 0, slices, tiles, kw, cols, ring, None)
+    return lib.w4a16_decode_plan(M, N, K, g, 0, slices, tiles, kw, cols, ring, topk, None)
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -34,6 +34,8 @@ def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128):
     (dict(slices=-1), b"must be >= 0"),
     (dict(slices=1, tiles=1, M=16, K=8192, g=4096), b"LDS"),   # 256 steps of 1 KB fragments
     (dict(slices=1, tiles=4, kw=2, M=16, K=5120), b"LDS"),                 # 160 steps of 1 KB fragments
+    (dict(topk=9), b"k=9"),
+    (dict(topk=-1), b"k=-1"),
 ])
 def test_decode_launch_is_checked(lib, kw, msg):
     assert dec(lib, **kw) == -1
@@ -46,5 +48,30 @@ def test_default_plans_are_accepted(lib):
     for K, N, g, packed in ((512, 256, 128, 0), (5120, 5120, 128, 0), (5120, 17408, 128, 0), (17408, 5120, 64, 1),
                             (5120, 248320, 128, 0)):
         for M in range(1, 17):
-            assert lib.w4a16_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, out) == 0, (K, N, M, lib.w4a16_last_error())
-            assert out[5] <= 160 * 1024 - 256
+            for topk in (0, 1, 8):
+                assert lib.w4a16_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, topk, out) == 0, \
+                    (K, N, M, topk, lib.w4a16_last_error())
+                assert out[5] <= 160 * 1024 - 256
+
+
+def test_fused_pick_reserves_lds_for_the_outputs(lib):
+    """A fused pick stages the group's finished outputs, M x (tiles x tile_cols) fp32, over the
+    activation fragments: a slice too short to hold them gets the room anyway."""
+    out = (ctypes.c_int * 6)()
+    assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 0, out) == 0
+    plain = out[5]
+    assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 1, out) == 0
+    assert out[5] - plain == 1 * 256 * 4 - 2 * 64   # two steps of one-row fragments -> one row of 256 outputs
+
+
+
+def test_topk_checks_its_arguments(lib):
+    A = O = 4096
+    assert lib.w4a16_gemm_topk(A, A, A, None, 128, 2, 256, 512, O, 0, 4, None, None) == -1
+    assert b"idx" in lib.w4a16_last_error()
+    for k in (0, 9, -3):
+        assert lib.w4a16_gemm_topk(A, A, A, None, 128, 2, 256, 512, O, 0, k, O, None) == -1
+        assert b"k=" in lib.w4a16_last_error()
+    assert lib.w4a16_gemm_topk(A, A, A, None, 128, 17, 256, 512, O, 0, 2, O, None) == -1   # M
+    assert lib.w4a16_gemm_decode_ex(A, A, A, None, 128, 2, 256, 512, O, 0, 0, 0, 0, 0, 0, 2, None, None) == -1
+    assert lib.w4a16_gemm_decode_ex(A, A, A, None, 128, 2, 256, 512, O, 0, 0, 0, 0, 0, 0, 0, O, None) == -1

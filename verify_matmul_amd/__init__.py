@@ -14,11 +14,11 @@ import torch
 
 __all__ = [
     "W4A16Error", "lib_path", "load", "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex",
-    "w4a16_decode_plan", "w4a16_gemm_argmax",
+    "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk",
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split",
-    "w4a16_gemm_affine_gate_up", "EXPORTS",
+    "w4a16_gemm_affine_gate_up", "w4a16_stream_read", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,9 +27,9 @@ _lib = None
 
 # every symbol the header declares
 EXPORTS = (
-    "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_prefill",
+    "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_prefill",
     "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
-    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version", "w4a16_source_hash",
 )
 
@@ -62,8 +62,9 @@ def load():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
-    lib.w4a16_gemm_decode_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, I, I, P, P]
-    lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, P]
+    lib.w4a16_gemm_decode_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, I, I, I, P, P]
+    lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.w4a16_gemm_topk.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
     lib.w4a16_gemm_prefill.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
@@ -80,16 +81,18 @@ def load():
     lib.w4a16_argmax_rows.argtypes = [P, I, I, P, P]
     lib.w4a16_unpack_u8.argtypes = [P, I, I, P, P]
     lib.w4a16_dequant_f32.argtypes = [P, P, P, I, I, I, P, P]
+    lib.w4a16_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.w4a16_release_scratch.argtypes = []
     lib.w4a16_status_string.argtypes = [I]
     lib.w4a16_status_string.restype = ctypes.c_char_p
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
               "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill",
               "w4a16_plan", "w4a16_argmax_rows",
-              "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch", "w4a16_version"):
+              "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch",
+              "w4a16_version"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -154,21 +157,25 @@ def w4a16_gemm(A, qweight, scales, qzeros, group_size, out, stream=None):
 def w4a16_gemm_decode_ex(A, qweight, scales, qzeros, group_size, out, slices=0, tiles=0, kw=0, tile_cols=0, ring=0,
                          idx=None, stream=None):
     """w4a16_gemm on the decode kernel with an explicit launch (0 = its default for that knob); idx
-    (int32 [M]) adds the fused greedy pick."""
+    (int32 [M, k]) adds the fused pick of the k best columns per row."""
     args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
-    if idx is not None and tuple(idx.shape) != (A.shape[0],):
-        raise ValueError("idx must be [M]")
-    _check(load().w4a16_gemm_decode_ex(*args, int(slices), int(tiles), int(kw), int(tile_cols), int(ring),
+    k = 0
+    if idx is not None:
+        if idx.dim() != 2 or idx.shape[0] != A.shape[0]:
+            raise ValueError("idx must be [M, k]")
+        k = int(idx.shape[1])
+    _check(load().w4a16_gemm_decode_ex(*args, int(slices), int(tiles), int(kw), int(tile_cols), int(ring), k,
                                        _ptr(idx, "idx", (torch.int32,)), _stream(stream)), "w4a16_gemm_decode_ex")
     return out
 
 
-def w4a16_decode_plan(M, N, K, group_size, packed_zeros=False, slices=0, tiles=0, kw=0, tile_cols=0, ring=0):
+def w4a16_decode_plan(M, N, K, group_size, packed_zeros=False, slices=0, tiles=0, kw=0, tile_cols=0, ring=0, topk=0):
     """The decode kernel's launch for a shape (host only, no device work): a dict of slices, tiles,
     kw, tile_cols, ring and lds bytes, or W4A16Error with the status w4a16_gemm_decode_ex would return."""
     out = (ctypes.c_int * 6)()
     _check(load().w4a16_decode_plan(int(M), int(N), int(K), int(group_size), int(bool(packed_zeros)), int(slices),
-                                    int(tiles), int(kw), int(tile_cols), int(ring), out), "w4a16_decode_plan")
+                                    int(tiles), int(kw), int(tile_cols), int(ring), int(topk), out),
+           "w4a16_decode_plan")
     return dict(zip(("slices", "tiles", "kw", "tile_cols", "ring", "lds"), list(out)))
 
 
@@ -185,6 +192,17 @@ def w4a16_gemm_ex(A, qweight, scales, qzeros, group_size, out, splits=0, waves_k
     _check(load().w4a16_gemm_ex(*args, int(splits), int(waves_k), int(tile_cols), _stream(stream)),
            "w4a16_gemm_ex")
     return out
+
+
+def w4a16_gemm_topk(A, qweight, scales, qzeros, group_size, out, idx, stream=None):
+    """w4a16_gemm plus the k best columns per row (fp32 values, best first; -1 when a row runs out)
+    in the same launch; idx: int32 [M, k], k in 1..8."""
+    args = _gemm_args(A, qweight, scales, qzeros, group_size, out)
+    if idx.dim() != 2 or idx.shape[0] != A.shape[0]:
+        raise ValueError("idx must be [M, k]")
+    _check(load().w4a16_gemm_topk(*args, int(idx.shape[1]), _ptr(idx, "idx", (torch.int32,)), _stream(stream)),
+           "w4a16_gemm_topk")
+    return out, idx
 
 
 def w4a16_gemm_argmax(A, qweight, scales, qzeros, group_size, out, idx, stream=None):
@@ -232,6 +250,12 @@ def w4a16_plan(M, N, K, group_size):
     _check(load().w4a16_plan(int(M), int(N), int(K), int(group_size), ctypes.byref(k), ctypes.byref(s),
                              ctypes.byref(w), ctypes.byref(c)), "w4a16_plan")
     return k.value, s.value, w.value, c.value
+
+
+def w4a16_stream_read(buf, sink, stream=None):
+    """Measurement hook: one plain streaming read of the tensor's bytes (sink: int32 [>= 1])."""
+    _check(load().w4a16_stream_read(_ptr(buf, "buf", (buf.dtype,)), buf.numel() * buf.element_size(),
+                                    _ptr(sink, "sink", (torch.int32,)), _stream(stream)), "w4a16_stream_read")
 
 
 def w4a16_argmax_rows(logits, idx, stream=None):

@@ -250,7 +250,7 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
 // slice, more while the slice's activations would not fit in LDS). `slices`, `tiles`, `kw`,
 // `tile_cols` and `ring` > 0 override the defaults (tuning and tests).
 int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int tiles, int kw, int tile_cols, int ring,
-                     DecodePlan *pl)
+                     bool pick, DecodePlan *pl)
 {
     const int steps = K / kStepK;
     if (tile_cols != 0 && tile_cols != 64 && tile_cols != 128)
@@ -272,7 +272,8 @@ int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int ti
         // workgroups fit on a CU (one workgroup of 16 rows per CU leaves the CU too few waves)
         const size_t lds_cap = M > 8 ? (size_t)kMaxLds / 2 : (size_t)kMaxLds;
         while (slices < std::min(kDecMaxSlices, steps / pl->kw) &&
-               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, nullptr) > lds_cap)
+               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, nullptr) >
+                   lds_cap)
             ++slices;
     }
     if (slices < 1 || slices > kDecMaxSlices || (long long)slices * pl->kw > steps)
@@ -289,7 +290,7 @@ int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int ti
     const bool ring_ok = pl->cols == 8 ? (pl->ring == 2 || pl->ring == 4)
                                        : (pl->ring == 2 || pl->ring == 3 || pl->ring == 4 || pl->ring == 6 || pl->ring == 8);
     if (!ring_ok) return fail(W4A16_ERR_INVALID_ARG, "ring=%d is not available for %d-column tiles", pl->ring, 16 * pl->cols);
-    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pl);
+    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, pl);
     if (pl->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "decode plan needs %zu bytes of LDS per workgroup (max %d): use more slices",
                     pl->lds, kMaxLds);
@@ -334,7 +335,7 @@ struct Matrix {
 // the pair's two products instead: out = (A x w) + (A x up).
 int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                 int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                int tile_cols, int ring, int32_t *idx, hipStream_t stream, bool noalloc);
+                int tile_cols, int ring, int topk, int32_t *idx, int pick_none, hipStream_t stream, bool noalloc);
 
 // Whether a plain GPTQ call takes the decode kernel by default: for matrices of at least
 // kDecodeMinN columns, wide enough to fill the chip with whole-K (or few-slice) workgroups, such
@@ -342,11 +343,11 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
 // 111 against 124 at five, 137 against 163 at sixteen). Narrower matrices need K slices, whose
 // exchange costs the decode kernel more than the small-row kernel's split-K (FFN 5120 x 17408:
 // 17 against 14 us at one row, 24 against 22 at sixteen).
-bool decode_by_default(int M, int N, int K, int g, bool packed)
+bool decode_by_default(int M, int N, int K, int g, bool packed, bool pick)
 {
     if (N < kDecodeMinN) return false;
     DecodePlan pl{};
-    return make_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, &pl) == W4A16_OK;
+    return make_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, pick, &pl) == W4A16_OK;
 }
 
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
@@ -355,9 +356,9 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
 {
     if (!up && !w.biases && splits == 0 && waves_k == 0 && tile_cols == 0 && M >= 1 && M <= 16 && N > 0 && K > 0 &&
         group_size > 0 && group_size % 32 == 0 && K % group_size == 0 && N % 8 == 0 &&
-        decode_by_default(M, N, K, group_size, w.qzeros != nullptr))
-        return decode_call(A, w.qweight, w.scales, w.qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, 0, 0, idx,
-                           stream, noalloc);
+        decode_by_default(M, N, K, group_size, w.qzeros != nullptr, idx != nullptr))
+        return decode_call(A, w.qweight, w.scales, w.qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, 0, 0,
+                           idx ? 1 : 0, idx, 0, stream, noalloc);
     const uint32_t *qweight = w.qweight;
     const uint16_t *scales = w.scales;
     const uint32_t *qzeros = w.qzeros;
@@ -383,14 +384,15 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     GemmPlan plan{};
     rc = make_plan(M, NV, K, group_size, zm, splits, waves_k, tile_cols, idx != nullptr, &plan);
     if (rc != W4A16_OK) return rc;
-    // scratch of a plan: control words [tile counters][slice flags, tiles x splits][argmax row keys
-    // (16 x 64 bit)], fp32 partials [splits, M, NV], prepared activations [M, K] and their shifts
+    // scratch of a plan: control words [tile counters][slice flags, tiles x splits][fused pick's
+    // row keys, one slot of 16 x 64 bit per tile], fp32 partials [splits, M, NV], prepared
+    // activations [M, K] and their shifts
     const size_t tile = (size_t)tile_columns(plan.cols);
     const size_t tiles = ((size_t)NV + tile - 1) / tile;
     const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
     auto needs = [&](const GemmPlan &pl, size_t *control, size_t *part, size_t *act) {
         *control = round_up(tiles * sizeof(uint32_t) + tiles * pl.splits * sizeof(uint32_t), 8) +
-                   16 * sizeof(unsigned long long);
+                   (idx ? tiles * 16 * sizeof(unsigned long long) : 0);
         *part = pl.splits > 1 ? (size_t)pl.splits * M * NV * sizeof(float) : 0;
         *act = pl.prep_a ? a16_bytes + (size_t)pl.splits * pl.wk * M * sizeof(int) : 0;
     };
@@ -461,14 +463,17 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
 // A decode-kernel call: check, plan, take scratch, launch.
 int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                 int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                int tile_cols, int ring, int32_t *idx, hipStream_t stream, bool noalloc)
+                int tile_cols, int ring, int topk, int32_t *idx, int pick_none, hipStream_t stream, bool noalloc)
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
     if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
         return fail(W4A16_ERR_INVALID_ARG, "slices=%d tiles=%d kw=%d ring=%d must be >= 0", slices, tiles, kw, ring);
+    if (topk < 0 || topk > kDecMaxTopK || (topk > 0) != (idx != nullptr))
+        return fail(W4A16_ERR_INVALID_ARG, "k=%d outside 1..%d, or idx %s", topk, kDecMaxTopK,
+                    idx ? "given without k" : "missing (null pointer)");
     DecodePlan plan{};
-    rc = make_decode_plan(M, N, K, group_size, qzeros != nullptr, slices, tiles, kw, tile_cols, ring, &plan);
+    rc = make_decode_plan(M, N, K, group_size, qzeros != nullptr, slices, tiles, kw, tile_cols, ring, topk > 0, &plan);
     if (rc != W4A16_OK) return rc;
     const long long wc = (long long)plan.tiles * 16 * plan.cols;
     const int groups = (int)((N + wc - 1) / wc);
@@ -492,26 +497,31 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     a.z_off = plan.z_off;
     a.r_off = plan.r_off;
     a.mp_log2 = decode_mp_log2(M);
-    if (plan.slices > 1 || idx) {
-        // control words: [counters, one per group of columns][flags, groups x slices][fused pick's
-        // row keys, 16 x 64 bit]
-        const size_t key_off = round_up((size_t)groups * (1 + plan.slices) * sizeof(uint32_t), 8);
-        const size_t control_bytes = key_off + 16 * sizeof(unsigned long long);
+    if (plan.slices > 1 || topk > 0) {
+        // control words: [counters, one per group of columns][flags, groups x slices][the fused
+        // pick's counter]; data: [fp32 partials, slices x M x N][the fused pick's slots, groups x
+        // M x k keys]
+        const size_t control_bytes = (size_t)groups * (1 + plan.slices) * sizeof(uint32_t) + sizeof(uint32_t);
         const size_t part_bytes = plan.slices > 1 ? (size_t)plan.slices * M * N * sizeof(float) : 0;
         if (part_bytes >= (1ull << 31))
             return fail(W4A16_ERR_UNSUPPORTED, "%zu bytes of partial sums exceed the 2 GiB the kernel addresses",
                         part_bytes);
+        const size_t slot_off = round_up(part_bytes, 256);
+        const size_t data_bytes = slot_off + (size_t)groups * M * topk * sizeof(unsigned long long);
         ScratchView v{};
-        rc = noalloc ? noalloc_scratch(stream, control_bytes, part_bytes, 0, &v)
-                     : get_scratch(stream, control_bytes, part_bytes, 0, &v);
+        rc = noalloc ? noalloc_scratch(stream, control_bytes, data_bytes, 0, &v)
+                     : get_scratch(stream, control_bytes, data_bytes, 0, &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.control;
         a.flags = v.control + groups;
         a.partials = v.partials;
         a.part_bytes = (uint32_t)part_bytes;
-        if (idx) {
-            a.amax_keys = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(v.control) + key_off);
-            a.amax_idx = idx;
+        if (topk > 0) {
+            a.topk = topk;
+            a.pick_none = pick_none;
+            a.pick_counter = v.control + (size_t)groups * (1 + plan.slices);
+            a.pick_slots = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(v.partials) + slot_off);
+            a.pick_idx = idx;
         }
     }
     const hipError_t e = launch_decode(a, plan, stream);
@@ -596,10 +606,20 @@ int w4a16_gemm_ex(const void *A, const uint32_t *qweight, const uint16_t *scales
 
 int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                          int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                         int tile_cols, int ring, int32_t *idx, hipStream_t stream)
+                         int tile_cols, int ring, int topk, int32_t *idx, hipStream_t stream)
 {
     return decode_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, slices, tiles, kw, tile_cols,
-                       ring, idx, stream, false);
+                       ring, topk, idx, -1, stream, false);
+}
+
+int w4a16_gemm_topk(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                    int group_size, int M, int N, int K, void *out, int out_dtype, int k, int32_t *idx,
+                    hipStream_t stream)
+{
+    if (!idx) return fail(W4A16_ERR_INVALID_ARG, "null pointer (idx)");
+    if (k < 1 || k > kDecMaxTopK) return fail(W4A16_ERR_INVALID_ARG, "k=%d outside 1..%d", k, kDecMaxTopK);
+    return decode_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, 0, 0, 0, 0, 0, k, idx, -1,
+                       stream, false);
 }
 
 int w4a16_gemm_argmax(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -742,9 +762,9 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
 {
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
-    if (decode_by_default(M, N, K, group_size, false)) {
+    if (decode_by_default(M, N, K, group_size, false, false)) {
         DecodePlan dp{};
-        const int rc = make_decode_plan(M, N, K, group_size, false, 0, 0, 0, 0, 0, &dp);
+        const int rc = make_decode_plan(M, N, K, group_size, false, 0, 0, 0, 0, 0, false, &dp);
         if (rc != W4A16_OK) return rc;
         if (kernel) *kernel = dp.mfma ? 3 : 2;
         if (splits) *splits = dp.slices;
@@ -763,14 +783,16 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
 }
 
 int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles, int kw,
-                      int tile_cols, int ring, int *plan_out)
+                      int tile_cols, int ring, int topk, int *plan_out)
 {
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
     if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
         return fail(W4A16_ERR_INVALID_ARG, "slices=%d tiles=%d kw=%d ring=%d must be >= 0", slices, tiles, kw, ring);
+    if (topk < 0 || topk > kDecMaxTopK) return fail(W4A16_ERR_INVALID_ARG, "k=%d outside 0..%d", topk, kDecMaxTopK);
     DecodePlan plan{};
-    const int rc = make_decode_plan(M, N, K, group_size, packed_zeros != 0, slices, tiles, kw, tile_cols, ring, &plan);
+    const int rc = make_decode_plan(M, N, K, group_size, packed_zeros != 0, slices, tiles, kw, tile_cols, ring,
+                                    topk > 0, &plan);
     if (rc != W4A16_OK) return rc;
     if (plan_out) {
         plan_out[0] = plan.slices;
@@ -804,6 +826,18 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
     a.keys = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ctr) + round_up((size_t)M * 4, 8));
     const hipError_t e = launch_argmax(a, stream);
     if (e != hipSuccess) return hip_fail(e, "argmax launch");
+    return W4A16_OK;
+}
+
+int w4a16_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (!buf || !sink) return fail(W4A16_ERR_INVALID_ARG, "null pointer");
+    if (bytes == 0 || bytes % 16) return fail(W4A16_ERR_INVALID_ARG, "bytes=%zu is not a positive multiple of 16", bytes);
+    if (bytes / (16 * 1024) >= 0x7FFFFFFFull)
+        return fail(W4A16_ERR_UNSUPPORTED, "bytes=%zu needs more than 2^31 - 1 workgroups", bytes);
+    if (!aligned16(buf)) return fail(W4A16_ERR_UNSUPPORTED, "buf must be 16-byte aligned");
+    const hipError_t e = launch_stream_read(buf, (long long)bytes, sink, stream);
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
     return W4A16_OK;
 }
 

@@ -72,8 +72,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     constexpr int kTile = 16 * kC;  // columns per wave
     constexpr int kRows = kMfma ? 4 : 1;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_last, s_failed;
-    __shared__ unsigned long long s_rowkey[16];   // fused pick: the workgroup's best key per row
+    __shared__ int s_last, s_failed, s_pick_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -200,10 +199,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     }
 
     // ---- 4. row maxima, then the fp16 fragments ---------------------------------------------
-    if (tid < 16) {
-        rowmax[tid] = 0u;
-        s_rowkey[tid] = 0ull;
-    }
+    if (tid < 16) rowmax[tid] = 0u;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kU * kV));   // all but the ring: scales, zeros, activations
     __syncthreads();                                  // every wave's direct loads have landed
     {   // each wave: the largest magnitude of each of its rows, one LDS atomic per row
@@ -410,37 +406,126 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
         }
     };
 
-    // Fused greedy pick (output layer): each finished output folds into its row's key (the keys
-    // of argmax_rows_kernel, so the pick equals a separate one over the fp32 outputs): the 16
-    // lanes holding one row's columns reduce theirs, one LDS atomic per row and lane group folds
-    // them into the workgroup's keys, and one agent-scope atomic per row merges those into the
-    // call's keys; a one-wave kernel next on the stream turns the keys into indices and clears
-    // them. Called by every thread of the workgroup.
-    const bool amax = p.amax_keys != nullptr;
-    unsigned long long rkey[kRows];   // the lane's best key per row so far
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) rkey[r] = 0ull;
-    auto fold = [&](int r, int j, float v) {   // finished output (row_base + r, column n0 + j)
-        if (v == v) {
-            const unsigned long long kj = argmax_key(v, (uint32_t)(n0 + j));
-            rkey[r] = kj > rkey[r] ? kj : rkey[r];
-        }
+    // Fused pick of the k best columns per row (the output layer's greedy pick is k = 1), in this
+    // launch: the column group's finished fp32 outputs go to LDS (over the fragments, no longer
+    // read); one wave per row takes the group's k best keys (the keys of argmax_rows_kernel: larger
+    // value first, then lower column; NaN never) and stores them to the group's slot with the
+    // agent-scope coherence bit; the workgroup waits until its stores have completed and counts
+    // itself in. The last group to count in merges every group's keys per row into the call's k
+    // picks and lowers the counter again (zero between calls). Called by every thread of the
+    // workgroup that finished the column group.
+    const int KP = p.topk;
+    float *vals = reinterpret_cast<float *>(smem + p.a_off);   // [M][WC] finished outputs
+    auto stage = [&](int r, int j, float v) {                   // a holder's finished output
+        vals[(size_t)(row_base + r) * WC + lcol + j] = v;
     };
     auto pick = [&]() {
+        __syncthreads();   // every output of the group is in LDS
+        constexpr int kPer = 2 * kC;   // keys per lane: WC / 64, at most 8 tiles of 16 * kC columns
+        for (int m = wave; m < M; m += NW) {
+            unsigned long long kk[kPer];
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-            const int m = row_base + r;
-            unsigned long long k = holder && m < M ? rkey[r] : 0ull;
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) {
-                const unsigned long long other = shfl_xor_u64(k, o);
-                k = other > k ? other : k;
+            for (int i = 0; i < kPer; ++i) {
+                const int c = lane + 64 * i;
+                const float v = c < WC ? vals[(size_t)m * WC + c] : 0.f;
+                kk[i] = c < WC && c0 + c < N && v == v ? argmax_key(v, (uint32_t)(c0 + c)) : 0ull;
             }
-            if (cl == 0 && k) atomicMax(&s_rowkey[m], k);
+            for (int r = 0; r < KP; ++r) {
+                unsigned long long best = 0ull;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) best = kk[i] > best ? kk[i] : best;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const unsigned long long other = shfl_xor_u64(best, o);
+                    best = other > best ? other : best;
+                }
+#pragma unroll
+                for (int i = 0; i < kPer; ++i)   // keys are distinct (they hold the column): one lane drops it
+                    if (kk[i] == best) kk[i] = 0ull;
+                if (lane == 0)
+                    __hip_atomic_store(&p.pick_slots[((size_t)m * p.groups + cg) * KP + r], best, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
+        wait_vm_all();     // this thread's slot stores have completed ...
+        __syncthreads();   // ... and so have every other thread's
+        if (tid == 0)
+            s_pick_last = __hip_atomic_fetch_add(p.pick_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                          (uint32_t)(p.groups - 1);
         __syncthreads();
-        if (tid < M && s_rowkey[tid])
-            __hip_atomic_fetch_max(&p.amax_keys[tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!s_pick_last) return;
+        // the last group merges the rows, min(M, waves) at a time, each row on waves / that many
+        // waves: each lane keeps the KP best of its share of the row's groups x KP keys (contiguous
+        // in the slots), sorted; each wave takes its KP best in KP rounds of the wave's largest
+        // head, and the row's first wave the KP best of its waves'
+        const int cand = p.groups * KP;
+        unsigned long long *wbest = reinterpret_cast<unsigned long long *>(vals);   // [NW][KP], over the outputs
+        const int rows_at_once = M < NW ? M : NW;
+        const int wpr = NW / rows_at_once;    // waves per row
+        const int part = wave % wpr;          // the wave's share of its row
+        unsigned long long top[kDecMaxTopK];
+        auto insert = [&](unsigned long long x) {   // x sinks to its place; the smallest falls off
+#pragma unroll
+            for (int j = 0; j < kDecMaxTopK; ++j) {
+                if (j < KP && x > top[j]) {
+                    const unsigned long long t = top[j];
+                    top[j] = x;
+                    x = t;
+                }
+            }
+        };
+        auto wave_take = [&](auto &&emit) {   // KP rounds of the wave's largest head
+            for (int r = 0; r < KP; ++r) {
+                unsigned long long best = top[0];
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const unsigned long long other = shfl_xor_u64(best, o);
+                    best = other > best ? other : best;
+                }
+                if (best != 0ull && top[0] == best) {   // the lane holding it moves to its next
+#pragma unroll
+                    for (int j = 0; j + 1 < kDecMaxTopK; ++j) top[j] = top[j + 1];
+                    top[kDecMaxTopK - 1] = 0ull;
+                }
+                emit(r, best);
+            }
+        };
+        for (int m0 = 0; m0 < M; m0 += rows_at_once) {
+            const int m = m0 + wave / wpr;
+            const bool mine = wave / wpr < rows_at_once && m < M;   // wave-uniform
+#pragma unroll
+            for (int j = 0; j < kDecMaxTopK; ++j) top[j] = 0ull;
+            if (mine) {
+                const unsigned long long *row = p.pick_slots + (size_t)m * cand;
+                constexpr int kB = 8;   // loads in flight per lane
+                const int stride = wpr * 64;
+                for (int i0 = part * 64 + lane; i0 < cand; i0 += stride * kB) {
+                    unsigned long long x[kB];
+#pragma unroll
+                    for (int b = 0; b < kB; ++b) {
+                        const int i = i0 + stride * b;
+                        x[b] = i < cand ? __hip_atomic_load(row + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+                    }
+#pragma unroll
+                    for (int b = 0; b < kB; ++b) insert(x[b]);
+                }
+                wave_take([&](int r, unsigned long long best) {
+                    if (lane == 0) wbest[wave * KP + r] = best;
+                });
+            }
+            __syncthreads();
+            if (mine && part == 0) {
+#pragma unroll
+                for (int j = 0; j < kDecMaxTopK; ++j) top[j] = 0ull;
+                for (int i = lane; i < wpr * KP; i += 64) insert(wbest[wave * KP + i]);
+                wave_take([&](int r, unsigned long long best) {
+                    if (lane == 0)
+                        p.pick_idx[(size_t)m * KP + r] = best ? (int32_t)(0xFFFFFFFFu - (uint32_t)best) : p.pick_none;
+                });
+            }
+            __syncthreads();   // wbest is read before the next rows reuse it
+        }
+        if (tid == 0) __hip_atomic_store(p.pick_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 
     if (P == 1) {
@@ -455,11 +540,16 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
                 }
             }
         }
-        if (amax) {
+        if (KP > 0) {
+            __syncthreads();   // every wave is past the main loop: the fragments are no longer read
+            if (holder) {
 #pragma unroll
-            for (int j = 0; j < kC; ++j)
+                for (int r = 0; r < kRows; ++r)
+                    if (row_base + r < M) {
 #pragma unroll
-                for (int r = 0; r < kRows; ++r) fold(r, j, tot[j][r]);
+                        for (int j = 0; j < kC; ++j) stage(r, j, tot[j][r]);
+                    }
+            }
             pick();
         }
         return;
@@ -542,16 +632,16 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
                 }
                 if (failed) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
                 store_out(m, v, sum.x, sum.y, sum.z, sum.w);
-                if (amax) {
-                    fold(r, 4 * v, sum.x);
-                    fold(r, 4 * v + 1, sum.y);
-                    fold(r, 4 * v + 2, sum.z);
-                    fold(r, 4 * v + 3, sum.w);
+                if (KP > 0) {   // every wave is past the main loop (the flag wait ended in a barrier)
+                    stage(r, 4 * v, sum.x);
+                    stage(r, 4 * v + 1, sum.y);
+                    stage(r, 4 * v + 2, sum.z);
+                    stage(r, 4 * v + 3, sum.w);
                 }
             }
         }
     }
-    if (amax) pick();
+    if (KP > 0) pick();
     for (int sp = tid; sp < P; sp += T)
         if (sp != sl) __hip_atomic_store(&flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -567,9 +657,7 @@ hipError_t launch_one(const DecodeArgs &a, const DecodePlan &plan, hipStream_t s
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.groups * a.slices)), dim3(a.tiles * a.kw * 64), plan.lds, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !a.amax_keys) return e;
-    return launch_argmax_finish(a.amax_keys, a.amax_idx, a.M, stream);
+    return hipGetLastError();
 }
 
 template <bool kMfma, int kZM>

@@ -605,13 +605,12 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
         for (int w = 1; w < kWK; ++w) v += red[((size_t)w * M + m) * kTile + c];
         return v;
     };
-    // Fused greedy pick: every finished output of the tile folds into its row's key in LDS;
-    // the tile then merges its keys into the call's row keys and exits without waiting, and
-    // argmax_keys_finish_kernel, next on the stream, turns the keys into indices and clears
-    // them (the same keys as argmax_rows_kernel, so the result equals its pick over the fp32
-    // outputs). A tile that waited for its merge to land, or counted itself out on a shared
-    // counter, would hold its compute unit a memory round trip longer. All lanes of a wave hold
-    // outputs of one row (a tile's width is a multiple of 64), so the keys are first reduced
+    // Fused greedy pick: every finished output of the tile folds into its row's key in LDS, and
+    // the tile stores its keys to its own slot of the call's keys (plain stores: no atomics on
+    // shared words, which serialise when many tiles merge into the same few rows); the finishing
+    // kernel next on the stream takes each row's largest key over the slots (the keys of
+    // argmax_rows_kernel, so the pick equals its pick over the fp32 outputs). All lanes of a wave
+    // hold outputs of one row (a tile's width is a multiple of 64), so the keys are first reduced
     // across the wave and one LDS atomic per wave folds them in: emit is called by every lane of
     // the wave together, with `ok` false for columns past N.
     auto emit = [&](int m, int n, float v, bool ok) {
@@ -628,8 +627,7 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
     };
     auto finish_argmax = [&]() {
         __syncthreads();
-        if (tid < M && s_rowkey[tid])
-            __hip_atomic_fetch_max(&p.amax_keys[tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid < M) p.amax_keys[(size_t)tile * 16 + tid] = s_rowkey[tid];
     };
     // Column c of the tile: its place in the split-K partials (2N wide for a gated pair),
     // whether it holds an output, and where its finished sum goes -- out, or for a gated pair
@@ -734,15 +732,44 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Ends a fused greedy pick: row m's index from its key, and the key cleared for the next call.
-// Runs after the GEMM on its stream, so every tile's merge has landed.
-__global__ __launch_bounds__(64) void argmax_keys_finish_kernel(unsigned long long *keys, int32_t *idx, int M)
+// Ends a fused greedy pick: one workgroup per row takes the largest key over the slots of the
+// tiles (or column groups), turns it into an index (0 when the row held no number), and clears
+// the row's slots (the control words are zero between calls). Runs after the GEMM on its stream,
+// so every slot has been stored.
+constexpr int kFinishThreads = 256;
+constexpr int kFinishBatch = 8;
+__global__ __launch_bounds__(kFinishThreads) void argmax_slots_finish_kernel(unsigned long long *keys, int slots,
+                                                                            int32_t *idx)
 {
-    const int m = threadIdx.x;
-    if (m >= M) return;
-    const unsigned long long k = keys[m];
-    idx[m] = k ? (int32_t)(0xFFFFFFFFu - (uint32_t)k) : 0;
-    keys[m] = 0;
+    __shared__ unsigned long long s_best[kFinishThreads / 64];
+    const int m = blockIdx.x;
+    unsigned long long best = 0ull;
+    // each thread reads its own slots, kFinishBatch loads in flight, then clears them
+    for (int s0 = threadIdx.x; s0 < slots; s0 += kFinishBatch * kFinishThreads) {
+        unsigned long long k[kFinishBatch];
+#pragma unroll
+        for (int b = 0; b < kFinishBatch; ++b) {
+            const int s = s0 + b * kFinishThreads;
+            k[b] = s < slots ? keys[(size_t)s * 16 + m] : 0ull;
+        }
+#pragma unroll
+        for (int b = 0; b < kFinishBatch; ++b) {
+            const int s = s0 + b * kFinishThreads;
+            best = k[b] > best ? k[b] : best;
+            if (s < slots) keys[(size_t)s * 16 + m] = 0ull;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long other = shfl_xor_u64(best, o);
+        best = other > best ? other : best;
+    }
+    if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kFinishThreads / 64; ++w) best = s_best[w] > best ? s_best[w] : best;
+        idx[m] = best ? (int32_t)(0xFFFFFFFFu - (uint32_t)best) : 0;
+    }
 }
 
 }  // namespace
@@ -768,8 +795,7 @@ hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t strea
     hipLaunchKernelGGL(kern, grid, dim3(kWK * 64), plan.lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_keys) return e;
-    hipLaunchKernelGGL(argmax_keys_finish_kernel, dim3(1), dim3(64), 0, stream, a.amax_keys, a.amax_idx, a.M);
-    return hipGetLastError();
+    return launch_argmax_finish(a.amax_keys, (int)grid.x, a.amax_idx, a.M, stream);
 }
 
 template <bool kMfma, int kZM, bool kLdsA, int kC, bool kDual = false>
@@ -823,9 +849,10 @@ hipError_t launch_act_prep(const ActPrepArgs &pa, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_argmax_finish(unsigned long long *keys, int32_t *idx, int M, hipStream_t stream)
+hipError_t launch_argmax_finish(unsigned long long *keys, int slots, int32_t *idx, int M, hipStream_t stream)
 {
-    hipLaunchKernelGGL(argmax_keys_finish_kernel, dim3(1), dim3(64), 0, stream, keys, idx, M);
+    hipLaunchKernelGGL(argmax_slots_finish_kernel, dim3((unsigned)M), dim3(kFinishThreads), 0, stream, keys, slots,
+                       idx);
     return hipGetLastError();
 }
 

@@ -64,8 +64,9 @@ struct GemmArgs {
     float *partials;          // [splits, M, N] (gated pair: [splits, M, 2N]) fp32 partial sums
     uint32_t *counters;       // one per column tile, zero between calls
     uint32_t *flags;          // [tiles, splits] slice-ready flags, zero between calls
-    unsigned long long *amax_keys;   // fused argmax: [M] row keys, zero between calls (nullptr: off)
-    int32_t *amax_idx;               // fused argmax: [M] output indices
+    unsigned long long *amax_keys;   // fused pick: [tiles, 16] row keys, one slot per column tile, zero between
+                                     // calls (nullptr: off)
+    int32_t *amax_idx;               // fused pick: [M] output indices
     int M, N, K, g;
     int splits;               // workgroups along K per column tile
     int out_bf16;
@@ -169,6 +170,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 constexpr int kDecMaxWaves = 8;
 constexpr int kDecodeMinN = 65536;   // plain calls this wide take the decode kernel by default
 constexpr int kDecMaxSlices = 16;
+constexpr int kDecMaxTopK = 8;       // largest k of the fused pick
 // Activation items (8 bf16 values) each thread of a decode workgroup keeps in registers between
 // the row maximum and the conversion; a longer slice reads the rest twice.
 constexpr int kDecHeld = 8;
@@ -190,8 +192,12 @@ struct DecodeArgs {
     int a_off, s_off, z_off, r_off;   // LDS offsets: fragments, scales, zero words, piece sums
     int mp_log2;              // matrix-core fragments hold rows padded to 2^mp_log2 (4, 8 or 16)
     uint32_t part_bytes;      // bytes of the partials region (bounds the buffer accesses)
-    unsigned long long *amax_keys;   // fused pick: [M] row keys, zero between calls (nullptr: off)
-    int32_t *amax_idx;               // fused pick: [M] output indices
+    // fused pick of the k best columns per row (topk = 0: off)
+    int topk;                       // k, 1..kDecMaxTopK
+    int pick_none;                  // index written where a row has no candidate left
+    unsigned long long *pick_slots; // [M, groups, topk] each column group's best keys (written before read)
+    uint32_t *pick_counter;         // column groups done, zero between calls
+    int32_t *pick_idx;              // [M, topk] the call's picks
 };
 struct DecodePlan {
     bool mfma;                // false: the one-row dot-product GEMV
@@ -209,7 +215,7 @@ inline int decode_mp_log2(int M) { return M <= 4 ? 2 : M <= 8 ? 3 : 4; }
 // per row of the padded rows per step; GEMV: 64 bytes per step), the workgroup's scales and zero
 // words of its groups, and the K pieces' sums (kw - 1 pieces of every tile).
 inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int tiles, int kw, int slices, bool packed,
-                                DecodePlan *pl)
+                                bool pick, DecodePlan *pl)
 {
     const int steps = K / kStepK;
     const int smax = (steps + slices - 1) / slices;
@@ -217,7 +223,12 @@ inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int ti
     const size_t groups = (size_t)(smax + spg - 1) / spg + 1;
     const size_t wc = (size_t)tiles * 16 * cols;
     const size_t a_off = 128;
-    const size_t a_bytes = (size_t)smax * (mfma ? (size_t)64 << decode_mp_log2(M) : 64);
+    // the fragments; after the main loop the fused pick reuses the region for the finished
+    // outputs, [M][wc] fp32, and then for each wave's best keys, [waves][kDecMaxTopK] 64-bit
+    const size_t a_frag = (size_t)smax * (mfma ? (size_t)64 << decode_mp_log2(M) : 64);
+    const size_t a_out = (size_t)M * wc * sizeof(float), a_keys = (size_t)tiles * kw * kDecMaxTopK * 8;
+    const size_t a_pick = pick ? (a_out > a_keys ? a_out : a_keys) : 0;
+    const size_t a_bytes = a_frag > a_pick ? a_frag : a_pick;
     const size_t s_off = a_off + a_bytes;
     const size_t s_bytes = groups * wc * 2;
     const size_t z_off = s_off + round_up_sz(s_bytes, 16);
@@ -233,8 +244,9 @@ inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int ti
     return r_off + r_bytes;
 }
 hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream);
-// Ends a fused greedy pick: idx[m] from the call's row keys, and the keys cleared (one wave).
-hipError_t launch_argmax_finish(unsigned long long *keys, int32_t *idx, int M, hipStream_t stream);
+// Ends the small-row kernel's fused greedy pick: idx[m] from the largest of keys[s * 16 + m] over
+// the slots s < slots, and those keys cleared.
+hipError_t launch_argmax_finish(unsigned long long *keys, int slots, int32_t *idx, int M, hipStream_t stream);
 
 struct ArgmaxArgs {
     const float *logits;
@@ -256,6 +268,7 @@ hipError_t launch_affine_widen(const uint32_t *packed, int bits, int K, int N, u
 hipError_t launch_affine_split(const uint32_t *packed, int bits, const uint16_t *scales, const uint16_t *biases,
                                int g, int K, int N, uint32_t *qweight, uint16_t *scales_out, uint16_t *biases_out,
                                hipStream_t s);
+hipError_t launch_stream_read(const void *buf, long long bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_unpack_u8(const uint32_t *qweight, int K, int N, uint8_t *q, hipStream_t s);
 hipError_t launch_dequant_f32(const uint32_t *qweight, const uint16_t *scales,
                               const uint32_t *qzeros, int g, int K, int N, float *w,
