@@ -101,6 +101,9 @@ def parse():
     p.add_argument("--affine-bits", type=int, default=4, choices=[4, 8],
                    help="with --affine: code width of the checkpoint (8 runs the split planes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-context", action="store_true",
+                   help="time only regions 1 and 2 (no lone event pairs, graph replays, read ceiling or copies): "
+                        "for counter collection")
     p.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise kernel (y = 2x, fp32) over MIB MiB five times: the "
                         "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes")
@@ -177,6 +180,7 @@ def warm_up(step, n):
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return i
 
 
 def load_traffic(workload, M, kernel):
@@ -306,7 +310,9 @@ def main():
                 raise RuntimeError(f"{'w4a16_gemm_gate_up_ex' if pair else 'w4a16_gemm_ex'} failed: "
                                    f"{lib.w4a16_last_error().decode()}")
 
-    warm_up(step, args.warmup)
+    # the library calls in the order this run makes them, as (phase, calls): a kernel trace of the
+    # run splits its dispatches by these counts
+    phases = [("warm-up", warm_up(step, args.warmup) * len(ms))]
 
     # timed region 1: the steps back to back, as a decode loop issues them -> value
     torch.cuda.synchronize()
@@ -317,6 +323,7 @@ def main():
     wall = time.perf_counter() - t0
     step_bytes = sum(algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat) for M in ms)
     value = step_bytes * args.steps / wall / 1e9
+    phases.append(("region 1: steps back to back", args.steps * len(ms)))
 
     def back_to_back(launch):
         """Average device time per launch: K launches back to back between one HIP event pair on
@@ -335,6 +342,7 @@ def main():
     per_m = {}
     for j, M in enumerate(ms):
         us = back_to_back(lambda i, j=j: fn(*calls[i % R][j][1]))
+        phases.append((f"region 2: M={M} back to back", args.steps))
         b = algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat)
         kern, spl, wk, tcols = vm.w4a16_plan(M, N, K, g)
         per_m[str(M)] = {"us_per_call": round(us, 3), "GBps": round(b / us / 1e3, 1),
@@ -357,6 +365,16 @@ def main():
     dm = per_m[str(dom)]
     us_dom = dm["us_per_call"]
 
+    achieved = dm["bytes"] / us_dom / 1e3   # GB/s
+    dom_kernel = dm["kernel"].split(" ")[0]
+    traffic = load_traffic(args.workload + ("_gate_up" if pair else ""), dom, dom_kernel)
+    if args.no_context:
+        print(json.dumps({"metric": "W4A16 GEMV/small-M GEMM device time per call (counter run, no context)",
+                          "value": round(value, 1), "unit": "GB/s", "steps": args.steps, "per_m": per_m,
+                          "roofline": {"kernel": f"{dm['kernel']}, M={dom}", "achieved": round(achieved, 1),
+                                       "us_per_launch": us_dom}, "phases": phases}), flush=True)
+        return 0
+
     # context: the same steps with a HIP event pair around every launch (each pair also times the
     # dispatch gap in front of its launch)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ms]
@@ -365,6 +383,7 @@ def main():
     for i in range(args.steps):
         step(i, evs)
     torch.cuda.synchronize()
+    phases.append(("context: steps with an event pair per launch", args.steps * len(ms)))
     for j, M in enumerate(ms):
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])   # us
         per_m[str(M)].update({"us_lone_event_pair": round(float(np.mean(d)), 3),
@@ -390,6 +409,7 @@ def main():
                     raise RuntimeError(f"w4a16_gemm_argmax failed: {lib.w4a16_last_error().decode()}")
             per_m[str(M)]["fused_gemm_argmax_us_per_call"] = round(
                 back_to_back(lambda i, fargs=fargs: lib.w4a16_gemm_argmax(*fargs[i % R])), 3)
+            phases.append((f"pick: M={M} fused greedy pick, warm-up and back to back", R + args.steps))
             # the 8 best columns per row, picked in the same launch
             top = torch.empty((M, 8), dtype=torch.int32, device=dev)
             targs = [(vp(a), vp(qw), vp(sc), vp(qz), g, M, N, K, vp(outs[M]), 0, 8, vp(top), sp)
@@ -399,10 +419,7 @@ def main():
                     raise RuntimeError(f"w4a16_gemm_topk failed: {lib.w4a16_last_error().decode()}")
             per_m[str(M)]["fused_gemm_top8_us_per_call"] = round(
                 back_to_back(lambda i, targs=targs: lib.w4a16_gemm_topk(*targs[i % R])), 3)
-
-    achieved = dm["bytes"] / us_dom / 1e3   # GB/s
-    dom_kernel = dm["kernel"].split(" ")[0]
-    traffic = load_traffic(args.workload + ("_gate_up" if pair else ""), dom, dom_kernel)
+            phases.append((f"pick: M={M} fused top-8, warm-up and back to back", R + args.steps))
 
     # context only, never `value`: (a) the dominant launch on one weight copy K times, which then
     # stays in the L2s and the 256 MB last-level cache (a cache-resident rate, not an HBM one);
@@ -411,6 +428,7 @@ def main():
     # reading these bytes from HBM; (c) a device copy of the same bytes per launch (read + write)
     jd = list(ms).index(dom)
     resident_us = back_to_back(lambda i: fn(*calls[0][jd][1]))
+    phases.append((f"context: M={dom} on one cache-resident weight copy", args.steps))
 
     def graph_replayed(issue):
         """Average device time per launch with no host work between launches: issue(stream) makes
@@ -434,7 +452,9 @@ def main():
             graph.replay()
         c1.record(stream)
         torch.cuda.synchronize()
+        graph_replay_launches[0] = R * (2 + reps)   # eager, first replay, timed replays
         return c0.elapsed_time(c1) * 1e3 / (reps * R)
+    graph_replay_launches = [0]
 
     def issue_calls(j):
         def issue(gsp):
@@ -446,6 +466,8 @@ def main():
     for j, M in enumerate(ms):
         try:
             per_m[str(M)]["us_per_call_graph_replay"] = round(graph_replayed(issue_calls(j)), 3)
+            phases.append((f"context: M={M} from a HIP graph (eager, first replay, timed replays)",
+                           graph_replay_launches[0]))
         except RuntimeError as e:   # context only: a call that cannot be captured leaves it out
             per_m[str(M)]["us_per_call_graph_replay"] = None
             per_m[str(M)]["graph_replay_error"] = str(e)[:200]
@@ -502,6 +524,7 @@ def main():
                      "us_per_launch": round(us_dom, 3), "us_per_launch_lone_event_pair": dm["us_lone_event_pair"]},
         "per_m": per_m,
         "context": context,
+        "phases": phases,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, inp, ms, args.cpu_seconds, gate_inp, one_thread)
