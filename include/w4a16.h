@@ -75,8 +75,10 @@ typedef enum { W4A16_OUT_F32 = 0, W4A16_OUT_BF16 = 1 } w4a16_out_dtype;
  *   M in 1..16; N > 0 and a multiple of 8; K > 0 and a multiple of g
  *   out       [M, N] fp32 (out_dtype W4A16_OUT_F32) or bf16 (W4A16_OUT_BF16, round to
  *             nearest even), 16-byte aligned
- * M = 1 on 64-column tiles runs the single-row GEMV; everything else (M = 2..16, and M = 1 on
- * the 128-column tiles of matrices with N >= 32768) runs the matrix-core GEMM. Accuracy: every output
+ * On matrices of fewer than 65536 columns, M = 1 on 64-column tiles runs the single-row GEMV and
+ * everything else (M = 2..16, and M = 1 on the 128-column tiles of matrices with N >= 32768) the
+ * matrix-core GEMM; wider matrices run the decode kernel of w4a16_gemm_decode_ex (its GEMV at one
+ * row, its matrix-core GEMM beyond), with its default launch. Accuracy: every output
  * is within 4e-3 * sum_k |a_k * w_kn| + 1e-6 of the exact value for finite inputs whose
  * nonzero activations within one row span less than 2^30 in magnitude (activations enter the
  * fp16 matrix cores through an exact power-of-two rescale per row and K-slice).
@@ -93,8 +95,9 @@ int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales,
  * memory per GPU (1 MiB of counters and flags, 15 MiB of partial sums and prepared activations),
  * held until the process ends; its first call on a device takes the array's address and clears
  * the counters with a small kernel on `stream`. A launch whose scratch would not fit takes fewer
- * split-K workgroups per tile (so its rounding may differ from w4a16_gemm's, within the same
- * contract); if even one does not fit, W4A16_ERR_UNSUPPORTED. Every call on a GPU uses the same
+ * split-K workgroups per column tile (or, on matrices of 65536 columns or more, fewer K slices)
+ * so its rounding may differ from w4a16_gemm's, within the same contract; if even one does not
+ * fit (or the K slice then no longer fits in LDS), W4A16_ERR_UNSUPPORTED. Every call on a GPU uses the same
  * array and leaves its counters and flags zero: calls that overlap on one GPU (on different
  * streams, or graphs replayed concurrently) race and must not be made.
  */

@@ -24,9 +24,13 @@ def gu():
     return gpu_util
 
 
-# (seed, M, K, N, group, symmetric): the first needs split-K partials of 1 MiB at 16 rows and
-# packed zero points; the second is smaller, ragged in N, one-row GEMV
-CALLS = [(9201, 16, 2048, 8192, 128, False), (9202, 3, 1024, 520, 64, True), (9203, 1, 512, 256, 128, True)]
+# (seed, M, K, N, group, symmetric), each call smaller than the one before: two matrices wide
+# enough for the decode kernel (the first, 16 rows over 70000 columns, needs fewer K slices than
+# its default launch to fit the array; the second is one row of 65536 columns), then the
+# small-row kernel: split-K partials of 1 MiB at 16 rows with packed zero points, a ragged N,
+# and the one-row GEMV
+CALLS = [(9204, 16, 1024, 70000, 128, False), (9205, 1, 512, 65536, 64, True), (9201, 16, 2048, 8192, 128, False),
+         (9202, 3, 1024, 520, 64, True), (9203, 1, 512, 256, 128, True)]
 
 
 def test_noalloc_matches_gemm_on_consecutive_calls(gu):

@@ -477,6 +477,20 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     if (rc != W4A16_OK) return rc;
     const long long wc = (long long)plan.tiles * 16 * plan.cols;
     const int groups = (int)((N + wc - 1) / wc);
+    // the data a launch keeps in scratch: fp32 slices, then the fused pick's slots
+    auto data_need = [&](int sl) {
+        const size_t part = sl > 1 ? (size_t)sl * M * N * sizeof(float) : 0;
+        return round_up(part, 256) + (size_t)groups * M * topk * sizeof(unsigned long long);
+    };
+    // the no-allocation array: a default launch whose slices do not fit takes fewer slices while
+    // its activation slice still fits in LDS (what still does not fit is refused below)
+    while (noalloc && slices == 0 && plan.slices > 1 && data_need(plan.slices) > kNoAllocBytes - kNoAllocControl) {
+        DecodePlan fewer{};
+        if (make_decode_plan(M, N, K, group_size, qzeros != nullptr, plan.slices - 1, tiles, kw, tile_cols, ring,
+                             topk > 0, &fewer) != W4A16_OK)
+            break;
+        plan = fewer;
+    }
     DecodeArgs a{};
     a.A = static_cast<const uint16_t *>(A);
     a.qweight = qweight;
