@@ -48,9 +48,11 @@ output, and the algorithmic bytes count both matrices.
 With --affine every call is the affine-code GEMM (w4a16_gemm_affine, w = s * q + b, bf16 scales
 and biases) on the affine-4 FFN up projection 5120 x 17408 in groups of 64, M = 1, 2, 4, 8, 16.
 Algorithmic bytes per call = codes (K*N*bits/8) + scales and biases (4*K*N/g) + activations
-(2*M*K) + outputs (4*M*N). --affine --affine-bits 8 times the 8-bit checkpoint of the same
-projection through its split planes (w4a16_gemm_affine_split, planes prepared once before
-timing); its algorithmic bytes are those of the 8-bit format.
+(2*M*K) + outputs (4*M*N). --affine-bits 2, 3, 5, 6 or 8 takes the checkpoint of that width of the
+same projection: 2 and 3-bit codes widened onto the 4-bit layout once (w4a16_affine_widen), 5, 6
+and 8-bit codes split into two 4-bit planes once (w4a16_affine_split, w4a16_gemm_affine_split);
+--affine-native reads the codes of any of these widths as stored (w4a16_gemm_affine_bits). The
+algorithmic bytes are always those of the stored format.
 
 Prints one JSON line (rank 0; this build runs on one GPU).
 """
@@ -98,8 +100,11 @@ def parse():
                    help="time the fused gated pair silu(A x W_gate) * (A x W_up) on the workload's shape")
     p.add_argument("--affine", action="store_true",
                    help="time the affine-code GEMM on the affine-4 FFN up projection (w = s * q + b)")
-    p.add_argument("--affine-bits", type=int, default=4, choices=[4, 8],
-                   help="with --affine: code width of the checkpoint (8 runs the split planes)")
+    p.add_argument("--affine-bits", type=int, default=4, choices=[2, 3, 4, 5, 6, 8],
+                   help="with --affine: code width of the checkpoint (2 and 3 are widened to 4 bits once, 5, 6 "
+                        "and 8 split into two 4-bit planes once, unless --affine-native)")
+    p.add_argument("--affine-native", action="store_true",
+                   help="with --affine: read the codes at their own width (w4a16_gemm_affine_bits)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-context", action="store_true",
                    help="time only regions 1 and 2 (no lone event pairs, graph replays, read ceiling or copies): "
@@ -544,14 +549,17 @@ def run_affine(args, lib):
     from verify_matmul_amd import synth
 
     bits = args.affine_bits
+    native = args.affine_native
     pair = args.gate_up   # the affine gated pair silu(A x W_gate) * (A x W_up)
-    if args.prefill or (pair and (bits != 4 or args.splits or args.waves_k or args.tile_cols)):
-        print("bench.py: --affine takes no --prefill; --affine --gate-up takes 4-bit codes and no launch knobs",
-              file=sys.stderr)
+    if args.prefill or (pair and (bits != 4 or native or args.splits or args.waves_k or args.tile_cols)):
+        print("bench.py: --affine takes no --prefill; --affine --gate-up takes 4-bit codes, no --affine-native and "
+              "no launch knobs", file=sys.stderr)
         return 2
     nmat = 2 if pair else 1
-    if bits == 8 and (args.splits or args.waves_k or args.tile_cols):
-        print("bench.py: --affine-bits 8 takes no launch knobs", file=sys.stderr)
+    split = bits >= 5 and not native   # two 4-bit planes
+    widen = bits < 4 and not native    # widened onto 4 bits
+    if (bits != 4 or native) and (args.splits or args.waves_k or args.tile_cols):
+        print("bench.py: launch knobs apply to 4-bit codes on the small-row kernel only", file=sys.stderr)
         return 2
     wl = synth.AFFINE_WORKLOADS[f"ffn_up_affine{bits}"]
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
@@ -573,12 +581,16 @@ def run_affine(args, lib):
     a0 = torch.from_numpy(x.act.view(np.int16)).to(dev)
     pool = []
     for _ in range(R):
-        if bits == 8:   # the split planes, prepared once per copy
+        if split:   # the split planes, prepared once per copy
             qw = torch.empty((2 * K // 8, N), dtype=torch.int32, device=dev)
             sc = torch.empty((2 * K // g, N), dtype=torch.int16, device=dev)
             bi = torch.empty((2 * K // g, N), dtype=torch.int16, device=dev)
             vm.w4a16_affine_split(qw0, bits, sc0, bi0, g, K, qw, sc, bi)
-        else:
+        elif widen:   # widened onto the 4-bit layout once per copy
+            qw = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+            vm.w4a16_affine_widen(qw0, bits, K, qw)
+            sc, bi = sc0.clone(), bi0.clone()
+        else:   # 4-bit codes (the qweight layout), or the stream as stored (native)
             qw, sc, bi = qw0.clone(), sc0.clone(), bi0.clone()
         pool.append((qw, sc, bi, a0.clone(), {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in ms}))
     del qw0
@@ -590,7 +602,11 @@ def run_affine(args, lib):
         calls = [[(vp(a), vp(gates[r][0]), vp(gates[r][1]), vp(gates[r][2]), vp(qw), vp(sc), vp(bi), g, M, N, K,
                    vp(outs[M]), 0, sp) for M in ms] for r, (qw, sc, bi, a, outs) in enumerate(pool)]
         fn = lib.w4a16_gemm_affine_gate_up
-    elif bits == 8:
+    elif native:
+        calls = [[(vp(a), vp(qw), bits, vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, sp) for M in ms]
+                 for qw, sc, bi, a, outs in pool]
+        fn = lib.w4a16_gemm_affine_bits
+    elif split:
         calls = [[(vp(a), vp(qw), vp(sc), vp(bi), g, M, N, K, vp(outs[M]), 0, sp) for M in ms]
                  for qw, sc, bi, a, outs in pool]
         fn = lib.w4a16_gemm_affine_split
@@ -624,46 +640,46 @@ def run_affine(args, lib):
     for i in range(args.steps):
         step(i, evs)
     torch.cuda.synchronize()
-    per_m, dom, dom_time = {}, None, -1.0
-    for j, M in enumerate(ms):
+    per_m = {}
+    for j, M in enumerate(ms):   # device time per call: K launches of the call back to back
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(*calls[i % R][j])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
         d = np.array([evs[i][j][0].elapsed_time(evs[i][j][1]) * 1e3 for i in range(args.steps)])
         b = affine_bytes(M, K, N, g, bits, nmat)
-        us = float(np.mean(d))
-        per_m[str(M)] = {"us_per_call": round(us, 3), "us_median": round(float(np.median(d)), 3),
-                         "us_p10": round(float(np.percentile(d, 10)), 3),
-                         "us_p90": round(float(np.percentile(d, 90)), 3), "GBps": round(b / us / 1e3, 1),
-                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b}
-        if float(np.sum(d)) > dom_time:
-            dom, dom_time = M, float(np.sum(d))
-    jd = list(ms).index(dom)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        fn(*calls[i % R][jd])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us_dom = e0.elapsed_time(e1) * 1e3 / args.steps
+        per_m[str(M)] = {"us_per_call": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                         "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4), "bytes": b,
+                         "us_lone_event_pair": round(float(np.mean(d)), 3)}
+    dom = max(ms, key=lambda M: per_m[str(M)]["us_per_call"])
+    us_dom = per_m[str(dom)]["us_per_call"]
     bdom = per_m[str(dom)]["bytes"]
     achieved = bdom / us_dom / 1e3
+    form = "codes read at their own width" if native else "split planes" if split else \
+        "widened to 4 bits" if widen else "4-bit codes"
+    kern = "decode_kernel" if native else "w4a16_gemm_kernel"
     rec = {
         "metric": "W4A16 GEMV/small-M GEMM achieved HBM GB/s (% of peak) and us/call, M=1..16",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases{'; split planes' if bits == 8 else ''})"
+        "config": {"workload": f"{wl.name} (w = s*q + b, bf16 scales and biases; {form})"
                                f"{' gated pair silu(A x W_gate) * (A x W_up)' if pair else ''}, M in "
                                f"{','.join(map(str, ms))} (one call each per step)",
                    "K": K, "N": N, "group": g, "bits": wl.bits, "ms": list(ms), "out": "fp32",
                    "rotation_copies": R, "pool_MiB": round(R * per_copy / 2 ** 20)},
-        "roofline": {"bound": "hbm", "kernel": f"w4a16_gemm_kernel (affine{', split planes' if bits == 8 else ''}{', gated pair' if pair else ''}, M={dom})", "M": dom,
+        "roofline": {"bound": "hbm", "kernel": f"{kern} (affine, {form}{', gated pair' if pair else ''}, M={dom})", "M": dom,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": load_traffic(f"ffn_up_affine{bits}" + ("_gate_up" if pair else ""), dom,
-                                             "w4a16_gemm_kernel"),
+                     "traffic": load_traffic(f"ffn_up_affine{bits}" + ("_native" if native else "") +
+                                             ("_gate_up" if pair else ""), dom, kern),
                      "launches": args.steps,
                      "bytes_per_launch": bdom, "us_per_launch": round(us_dom, 3),
-                     "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
+                     "us_per_launch_lone_event_pair": per_m[str(dom)]["us_lone_event_pair"]},
         "per_m": per_m,
     }
     if not args.no_cpu_baseline:

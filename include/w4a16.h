@@ -142,9 +142,10 @@ int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t 
  * w4a16_gemm_decode_ex checks it, without any device work: W4A16_OK and, if plan_out is not NULL,
  * plan_out[0..5] = slices, tiles, kw, tile_cols, ring, LDS bytes per workgroup; or the status and
  * w4a16_last_error() that w4a16_gemm_decode_ex would return. packed_zeros: nonzero for packed zero
- * points (qzeros given); topk: 0, or the k of a fused pick. Host only. */
+ * points (qzeros given); topk: 0, or the k of a fused pick; affine_bits: 0 for GPTQ codes, or the
+ * width of the affine codes of w4a16_gemm_affine_bits_ex. Host only. */
 int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles,
-                      int kw, int tile_cols, int ring, int topk, int *plan_out);
+                      int kw, int tile_cols, int ring, int topk, int affine_bits, int *plan_out);
 
 /* The launch w4a16_gemm picks for a shape (symmetric zero points): *kernel = 0 for the small-row
  * kernel's one-row GEMV, 1 for its MFMA GEMM, with *splits, *waves_k and *tile_cols as in
@@ -266,6 +267,32 @@ int w4a16_gemm_affine(const void *A, const uint32_t *qweight, const uint16_t *sc
 int w4a16_gemm_affine_ex(const void *A, const uint32_t *qweight, const uint16_t *scales,
                          const uint16_t *biases, int group_size, int M, int N, int K, void *out,
                          int out_dtype, int splits, int waves_k, int tile_cols, hipStream_t stream);
+
+/*
+ * Affine codes read at their own width (TensorFold PR #859, commit messages: 2, 3, 5 and 6-bit
+ * codes get tiles of their own width, 8-bit codes their own GEMV, so that a mostly 2-bit
+ * checkpoint does not stream as many bytes as a 4-bit one):
+ *
+ *   out[M, N] = A[M, K] x W[K, N],   W[k][n] = scale[k/g][n] * q[k][n] + bias[k/g][n]
+ *
+ *   packed   uint32 [K*bits/32, N]  the codes as column bit streams, the input layout of
+ *                                   w4a16_affine_widen (row k of column n at stream bits
+ *                                   [k*bits, (k+1)*bits)); bits = 1, 2, 3, 4, 5, 6 or 8 (7-bit
+ *                                   codes: w4a16_affine_split)
+ *   scales, biases  bf16 [K/g, N]   bit patterns
+ * Each call streams K*N*bits/8 bytes of codes: nothing is widened or split. A, out, M (1..16),
+ * group_size, K, N, alignment, scratch, determinism and the accuracy contract as
+ * w4a16_gemm_affine. Runs on the decode kernel (w4a16_gemm_decode_ex), whose code reader pulls
+ * each lane's 8 codes out of one or two words of the stream. w4a16_gemm_affine_bits_ex takes
+ * that kernel's launch knobs (0 = its default; 64-column tiles; ring 4).
+ */
+int w4a16_gemm_affine_bits(const void *A, const uint32_t *packed, int bits, const uint16_t *scales,
+                           const uint16_t *biases, int group_size, int M, int N, int K, void *out,
+                           int out_dtype, hipStream_t stream);
+int w4a16_gemm_affine_bits_ex(const void *A, const uint32_t *packed, int bits,
+                              const uint16_t *scales, const uint16_t *biases, int group_size,
+                              int M, int N, int K, void *out, int out_dtype, int slices, int tiles,
+                              int kw, int ring, hipStream_t stream);
 
 /*
  * The gated feed-forward input of two affine matrices, out = silu(A x W_gate) * (A x W_up), each W

@@ -16,9 +16,9 @@ def lib():
     return vm.load()
 
 
-def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128, topk=0):
+def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128, topk=0, bits=0):
     """The host-only planner: the same checks as w4a16_gemm_decode_ex, no device work."""
-    return lib.w4a16_decode_plan(M, N, K, g, 0, slices, tiles, kw, cols, ring, topk, None)
+    return lib.w4a16_decode_plan(M, N, K, g, 0, slices, tiles, kw, cols, ring, topk, bits, None)
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -36,6 +36,12 @@ def dec(lib, slices=0, tiles=0, kw=0, cols=0, ring=0, M=4, N=256, K=512, g=128, 
     (dict(slices=1, tiles=4, kw=2, M=16, K=5120), b"LDS"),                 # 160 steps of 1 KB fragments
     (dict(topk=9), b"k=9"),
     (dict(topk=-1), b"k=-1"),
+    (dict(bits=7), b"affine_bits=7"),
+    (dict(bits=9), b"affine_bits=9"),
+    (dict(bits=2, cols=128), b"64-column"),
+    (dict(bits=3, ring=2), b"ring"),
+    (dict(bits=2, ring=3), b"ring"),
+    (dict(bits=5, ring=8), b"ring"),
 ])
 def test_decode_launch_is_checked(lib, kw, msg):
     assert dec(lib, **kw) == -1
@@ -49,7 +55,7 @@ def test_default_plans_are_accepted(lib):
                             (5120, 248320, 128, 0)):
         for M in range(1, 17):
             for topk in (0, 1, 8):
-                assert lib.w4a16_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, topk, out) == 0, \
+                assert lib.w4a16_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, topk, 0, out) == 0, \
                     (K, N, M, topk, lib.w4a16_last_error())
                 assert out[5] <= 160 * 1024 - 256
 
@@ -58,9 +64,9 @@ def test_fused_pick_reserves_lds_for_the_outputs(lib):
     """A fused pick stages the group's finished outputs, M x (tiles x tile_cols) fp32, over the
     activation fragments: a slice too short to hold them gets the room anyway."""
     out = (ctypes.c_int * 6)()
-    assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 0, out) == 0
+    assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 0, 0, out) == 0
     plain = out[5]
-    assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 1, out) == 0
+    assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 1, 0, out) == 0
     assert out[5] - plain == 1 * 256 * 4 - 2 * 64   # two steps of one-row fragments -> one row of 256 outputs
 
 
@@ -75,3 +81,32 @@ def test_topk_checks_its_arguments(lib):
     assert lib.w4a16_gemm_topk(A, A, A, None, 128, 17, 256, 512, O, 0, 2, O, None) == -1   # M
     assert lib.w4a16_gemm_decode_ex(A, A, A, None, 128, 2, 256, 512, O, 0, 0, 0, 0, 0, 0, 2, None, None) == -1
     assert lib.w4a16_gemm_decode_ex(A, A, A, None, 128, 2, 256, 512, O, 0, 0, 0, 0, 0, 0, 0, O, None) == -1
+
+
+def test_affine_bits_plans(lib):
+    """Affine codes read at their own width: every width the kernel takes, at the affine
+    workloads' shapes and every row count, has a default launch that fits; its scales and biases
+    both sit in LDS (more than the GPTQ launch of the same shape)."""
+    out = (ctypes.c_int * 6)()
+    for K, N, g in ((5120, 17408, 64), (512, 256, 64), (1024, 520, 32), (5120, 248320, 64)):
+        for bits in (1, 2, 3, 4, 5, 6, 8):
+            for M in (1, 2, 5, 9, 16):
+                assert lib.w4a16_decode_plan(M, N, K, g, 0, 0, 0, 0, 0, 0, 0, bits, out) == 0, \
+                    (K, N, bits, M, lib.w4a16_last_error())
+                assert out[3] == 64 and out[4] == 4 and out[5] <= 160 * 1024 - 256
+    assert lib.w4a16_decode_plan(4, 256, 512, 64, 1, 0, 0, 0, 0, 0, 0, 2, out) == -1   # no zero points
+
+
+def test_affine_bits_checks_its_arguments(lib):
+    A = O = 4096
+    f = lib.w4a16_gemm_affine_bits
+    assert f(A, A, 2, A, None, 64, 2, 256, 512, O, 0, None) == -1
+    assert b"biases" in lib.w4a16_last_error()
+    for bits in (0, 7, 9, -1):
+        assert f(A, A, bits, A, A, 64, 2, 256, 512, O, 0, None) == -1
+        assert b"bits=" in lib.w4a16_last_error()
+    assert f(A, A, 2, A, A + 8, 64, 2, 256, 512, O, 0, None) == -2   # biases not 16-byte aligned
+    assert f(A, A, 2, A, A, 48, 2, 256, 512, O, 0, None) == -1       # group size
+    assert f(A, A, 2, A, A, 64, 17, 256, 512, O, 0, None) == -1      # M
+    assert lib.w4a16_gemm_affine_bits_ex(A, A, 3, A, A, 64, 2, 256, 512, O, 0, 0, 0, 0, 3, None) == -1
+    assert b"ring" in lib.w4a16_last_error()

@@ -18,6 +18,7 @@ __all__ = [
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split",
+    "w4a16_gemm_affine_bits",
     "w4a16_gemm_affine_gate_up", "w4a16_stream_read", "EXPORTS",
 ]
 
@@ -29,7 +30,8 @@ _lib = None
 EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_prefill",
     "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
-    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_bits",
+    "w4a16_gemm_affine_bits_ex", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version", "w4a16_source_hash",
 )
 
@@ -63,7 +65,9 @@ def load():
     lib.w4a16_gemm.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_noalloc.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_decode_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, I, I, I, P, P]
-    lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, I, I, P]
+    lib.w4a16_gemm_affine_bits.argtypes = [P, P, I, P, P, I, I, I, I, P, I, P]
+    lib.w4a16_gemm_affine_bits_ex.argtypes = [P, P, I, P, P, I, I, I, I, P, I, I, I, I, I, P]
     lib.w4a16_gemm_topk.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
@@ -88,7 +92,7 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_affine_bits", "w4a16_gemm_affine_bits_ex", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
               "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill",
               "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch",
@@ -169,12 +173,13 @@ def w4a16_gemm_decode_ex(A, qweight, scales, qzeros, group_size, out, slices=0, 
     return out
 
 
-def w4a16_decode_plan(M, N, K, group_size, packed_zeros=False, slices=0, tiles=0, kw=0, tile_cols=0, ring=0, topk=0):
+def w4a16_decode_plan(M, N, K, group_size, packed_zeros=False, slices=0, tiles=0, kw=0, tile_cols=0, ring=0, topk=0,
+                      affine_bits=0):
     """The decode kernel's launch for a shape (host only, no device work): a dict of slices, tiles,
     kw, tile_cols, ring and lds bytes, or W4A16Error with the status w4a16_gemm_decode_ex would return."""
     out = (ctypes.c_int * 6)()
     _check(load().w4a16_decode_plan(int(M), int(N), int(K), int(group_size), int(bool(packed_zeros)), int(slices),
-                                    int(tiles), int(kw), int(tile_cols), int(ring), int(topk), out),
+                                    int(tiles), int(kw), int(tile_cols), int(ring), int(topk), int(affine_bits), out),
            "w4a16_decode_plan")
     return dict(zip(("slices", "tiles", "kw", "tile_cols", "ring", "lds"), list(out)))
 
@@ -367,6 +372,31 @@ def w4a16_gemm_affine_split(A, qweight, scales, biases, group_size, out, stream=
                                           int(group_size), M, N, K, _ptr(out, "out", (torch.float32, torch.bfloat16)),
                                           dt, _stream(stream)),
            "w4a16_gemm_affine_split")
+    return out
+
+
+def w4a16_gemm_affine_bits(A, packed, bits, scales, biases, group_size, out, slices=0, tiles=0, kw=0, ring=0,
+                           stream=None):
+    """out[M,N] = A[M,K] (bf16) x W, W = scales * q + biases, the codes read at their own width
+    from the column bit streams `packed` (uint32 [K*bits/32, N]; bits 1..6 or 8), bf16 scales and
+    biases [K/g, N]; slices / tiles / kw / ring as w4a16_gemm_decode_ex (0 = default)."""
+    M, K = A.shape
+    N = packed.shape[1]
+    if packed.shape[0] * 32 != K * bits:
+        raise ValueError(f"packed {tuple(packed.shape)} is not [{K * bits // 32}, {N}] for {bits}-bit codes")
+    if tuple(scales.shape) != (K // group_size, N) or tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("scales and biases must be [K/g, N]")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out {tuple(out.shape)} is not [{M}, {N}]")
+    dt = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}.get(out.dtype)
+    if dt is None:
+        raise TypeError("out must be float32 or bfloat16")
+    _sb = (torch.bfloat16, torch.int16, torch.uint16)
+    _check(load().w4a16_gemm_affine_bits_ex(_ptr(A, "A", _sb), _ptr(packed, "packed", _I32), int(bits),
+                                            _ptr(scales, "scales", _sb), _ptr(biases, "biases", _sb), int(group_size),
+                                            M, N, K, _ptr(out, "out", (torch.float32, torch.bfloat16)), dt,
+                                            int(slices), int(tiles), int(kw), int(ring), _stream(stream)),
+           "w4a16_gemm_affine_bits")
     return out
 
 

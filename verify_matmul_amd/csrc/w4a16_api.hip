@@ -249,30 +249,40 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
 // columns, one wave each; slices for about 512 workgroups (at most 16, at least 4 K steps per
 // slice, more while the slice's activations would not fit in LDS). `slices`, `tiles`, `kw`,
 // `tile_cols` and `ring` > 0 override the defaults (tuning and tests).
+// `bits`: 0 for GPTQ codes, else the width of affine codes (64-column tiles, a ring of 4)
 int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int tiles, int kw, int tile_cols, int ring,
-                     bool pick, DecodePlan *pl)
+                     bool pick, DecodePlan *pl, int bits = 0)
 {
     const int steps = K / kStepK;
+    const bool affine = bits > 0;
     if (tile_cols != 0 && tile_cols != 64 && tile_cols != 128)
         return fail(W4A16_ERR_INVALID_ARG, "tile_cols=%d is not 0, 64 or 128", tile_cols);
+    if (affine && tile_cols == 128)
+        return fail(W4A16_ERR_INVALID_ARG, "affine codes run on 64-column tiles (tile_cols=%d)", tile_cols);
     pl->mfma = M > 1;
     pl->cols = tile_cols ? tile_cols / 16 : 4;
     // more rows stage more activations per workgroup, which leaves room for fewer workgroups per
     // CU: give each workgroup more waves
-    pl->tiles = tiles ? tiles : (pl->mfma ? 8 : 4);
+    // (affine codes below kDecodeMinN columns: 4 tiles at every row count, measured on the
+    // 5120 x 17408 projection at 2, 4 and 8 bits, where 8 tiles with more K slices lost 10-30%)
+    pl->tiles = tiles ? tiles : (pl->mfma && (!affine || N >= kDecodeMinN) ? 8 : 4);
     pl->kw = kw ? kw : 1;
     if (pl->tiles < 1 || pl->kw < 1 || pl->tiles * pl->kw > kDecMaxWaves)
         return fail(W4A16_ERR_INVALID_ARG, "tiles=%d x kw=%d waves outside 1..%d", pl->tiles, pl->kw, kDecMaxWaves);
     const long long wc = (long long)pl->tiles * 16 * pl->cols;
     const int groups = (int)((N + wc - 1) / wc);
     if (slices == 0) {
-        slices = (int)std::min<long long>(kDecMaxSlices, (512 + groups - 1) / groups);
+        // about 512 workgroups (affine codes: 400, which measured 8-10% faster than 512)
+        const int target = affine ? 400 : 512;
+        slices = (int)std::min<long long>(kDecMaxSlices, (target + groups - 1) / groups);
         slices = std::max(1, std::min(slices, steps / (4 * pl->kw)));
-        // long K: more slices until the slice's activations fit in LDS; past 8 rows, until two
-        // workgroups fit on a CU (one workgroup of 16 rows per CU leaves the CU too few waves)
-        const size_t lds_cap = M > 8 ? (size_t)kMaxLds / 2 : (size_t)kMaxLds;
+        // long K: more slices until the slice's activations fit in LDS; past 8 rows (affine codes:
+        // past one row, whose scales and biases of groups of 64 take 4x the LDS of GPTQ's groups
+        // of 128), until two workgroups fit on a CU (one workgroup of 16 rows per CU leaves the CU
+        // too few waves)
+        const size_t lds_cap = M > 8 || (affine && M > 1) ? (size_t)kMaxLds / 2 : (size_t)kMaxLds;
         while (slices < std::min(kDecMaxSlices, steps / pl->kw) &&
-               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, nullptr) >
+               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, nullptr, affine) >
                    lds_cap)
             ++slices;
     }
@@ -283,14 +293,18 @@ int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int ti
     // the kernel addresses a slice's codes (plus the ring's reads past its end) with 32-bit byte
     // offsets
     const long long smax = (steps + slices - 1) / slices;
-    if ((smax + 8) * 16LL * N >= (1LL << 31))
+    const long long step_bytes = 4LL * (affine ? bits : 4) * N;   // a step's codes over all columns
+    if ((smax + 8) * step_bytes >= (1LL << 31))
         return fail(W4A16_ERR_UNSUPPORTED, "a K slice of %lld steps over %d columns exceeds 2 GiB of codes: use more slices",
                     smax, N);
-    pl->ring = ring ? ring : (pl->cols == 8 ? 2 : M == 1 ? 3 : M <= 8 ? 4 : 8);
-    const bool ring_ok = pl->cols == 8 ? (pl->ring == 2 || pl->ring == 4)
-                                       : (pl->ring == 2 || pl->ring == 3 || pl->ring == 4 || pl->ring == 6 || pl->ring == 8);
-    if (!ring_ok) return fail(W4A16_ERR_INVALID_ARG, "ring=%d is not available for %d-column tiles", pl->ring, 16 * pl->cols);
-    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, pl);
+    pl->ring = ring ? ring : affine ? 4 : (pl->cols == 8 ? 2 : M == 1 ? 3 : M <= 8 ? 4 : 8);
+    const bool ring_ok = affine ? pl->ring == 4
+                         : pl->cols == 8 ? (pl->ring == 2 || pl->ring == 4)
+                                         : (pl->ring == 2 || pl->ring == 3 || pl->ring == 4 || pl->ring == 6 || pl->ring == 8);
+    if (!ring_ok)
+        return fail(W4A16_ERR_INVALID_ARG, "ring=%d is not available for %s", pl->ring,
+                    affine ? "affine codes (4)" : pl->cols == 8 ? "128-column tiles" : "64-column tiles");
+    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, pl, affine);
     if (pl->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "decode plan needs %zu bytes of LDS per workgroup (max %d): use more slices",
                     pl->lds, kMaxLds);
@@ -335,7 +349,8 @@ struct Matrix {
 // the pair's two products instead: out = (A x w) + (A x up).
 int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                 int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                int tile_cols, int ring, int topk, int32_t *idx, int pick_none, hipStream_t stream, bool noalloc);
+                int tile_cols, int ring, int topk, int32_t *idx, int pick_none, hipStream_t stream, bool noalloc,
+                const uint16_t *biases = nullptr, int bits = 0);
 
 // Whether a plain GPTQ call takes the decode kernel by default: for matrices of at least
 // kDecodeMinN columns, wide enough to fill the chip with whole-K (or few-slice) workgroups, such
@@ -463,17 +478,29 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
 // A decode-kernel call: check, plan, take scratch, launch.
 int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                 int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
-                int tile_cols, int ring, int topk, int32_t *idx, int pick_none, hipStream_t stream, bool noalloc)
+                int tile_cols, int ring, int topk, int32_t *idx, int pick_none, hipStream_t stream, bool noalloc,
+                const uint16_t *biases, int bits)
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
+    if (bits) {   // affine codes: column bit streams [K * bits / 32, N], bf16 scales and biases
+        if (!biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
+        if (qzeros) return fail(W4A16_ERR_INVALID_ARG, "affine codes take no zero points");
+        if (!(bits >= 1 && bits <= 6) && bits != 8)
+            return fail(W4A16_ERR_INVALID_ARG, "bits=%d is not 1, 2, 3, 4, 5, 6 or 8 (7-bit codes: w4a16_affine_split)",
+                        bits);
+        if (!aligned16(biases)) return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
+        if ((long long)(K / 32) * bits * N > 0xFFFFFFFFLL)
+            return fail(W4A16_ERR_UNSUPPORTED, "codes of %lld words exceed 2^32 words", (long long)(K / 32) * bits * N);
+    }
     if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
         return fail(W4A16_ERR_INVALID_ARG, "slices=%d tiles=%d kw=%d ring=%d must be >= 0", slices, tiles, kw, ring);
     if (topk < 0 || topk > kDecMaxTopK || (topk > 0) != (idx != nullptr))
         return fail(W4A16_ERR_INVALID_ARG, "k=%d outside 1..%d, or idx %s", topk, kDecMaxTopK,
                     idx ? "given without k" : "missing (null pointer)");
     DecodePlan plan{};
-    rc = make_decode_plan(M, N, K, group_size, qzeros != nullptr, slices, tiles, kw, tile_cols, ring, topk > 0, &plan);
+    rc = make_decode_plan(M, N, K, group_size, qzeros != nullptr, slices, tiles, kw, tile_cols, ring, topk > 0, &plan,
+                          bits);
     if (rc != W4A16_OK) return rc;
     const long long wc = (long long)plan.tiles * 16 * plan.cols;
     const int groups = (int)((N + wc - 1) / wc);
@@ -487,7 +514,7 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     while (noalloc && slices == 0 && plan.slices > 1 && data_need(plan.slices) > kNoAllocBytes - kNoAllocControl) {
         DecodePlan fewer{};
         if (make_decode_plan(M, N, K, group_size, qzeros != nullptr, plan.slices - 1, tiles, kw, tile_cols, ring,
-                             topk > 0, &fewer) != W4A16_OK)
+                             topk > 0, &fewer, bits) != W4A16_OK)
             break;
         plan = fewer;
     }
@@ -496,6 +523,8 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     a.qweight = qweight;
     a.scales = scales;
     a.qzeros = qzeros;
+    a.biases = bits ? biases : nullptr;
+    a.bits = bits;
     a.out = out;
     a.M = M;
     a.N = N;
@@ -624,6 +653,23 @@ int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t 
 {
     return decode_call(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype, slices, tiles, kw, tile_cols,
                        ring, topk, idx, -1, stream, false);
+}
+
+int w4a16_gemm_affine_bits_ex(const void *A, const uint32_t *packed, int bits, const uint16_t *scales,
+                              const uint16_t *biases, int group_size, int M, int N, int K, void *out, int out_dtype,
+                              int slices, int tiles, int kw, int ring, hipStream_t stream)
+{
+    if (bits == 0) return fail(W4A16_ERR_INVALID_ARG, "bits=0 is not 1, 2, 3, 4, 5, 6 or 8");
+    return decode_call(A, packed, scales, nullptr, group_size, M, N, K, out, out_dtype, slices, tiles, kw, 0, ring, 0,
+                       nullptr, 0, stream, false, biases, bits);
+}
+
+int w4a16_gemm_affine_bits(const void *A, const uint32_t *packed, int bits, const uint16_t *scales,
+                           const uint16_t *biases, int group_size, int M, int N, int K, void *out, int out_dtype,
+                           hipStream_t stream)
+{
+    return w4a16_gemm_affine_bits_ex(A, packed, bits, scales, biases, group_size, M, N, K, out, out_dtype, 0, 0, 0, 0,
+                                     stream);
 }
 
 int w4a16_gemm_topk(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -797,8 +843,11 @@ int w4a16_plan(int M, int N, int K, int group_size, int *kernel, int *splits, in
 }
 
 int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles, int kw,
-                      int tile_cols, int ring, int topk, int *plan_out)
+                      int tile_cols, int ring, int topk, int affine_bits, int *plan_out)
 {
+    if (affine_bits && ((!(affine_bits >= 1 && affine_bits <= 6) && affine_bits != 8) || packed_zeros))
+        return fail(W4A16_ERR_INVALID_ARG, "affine_bits=%d is not 0, 1, 2, 3, 4, 5, 6 or 8, or comes with zero points",
+                    affine_bits);
     if (M < 1 || M > 16 || N <= 0 || K <= 0 || group_size <= 0 || group_size % 32 || K % group_size || N % 8)
         return fail(W4A16_ERR_INVALID_ARG, "invalid shape M=%d N=%d K=%d group_size=%d", M, N, K, group_size);
     if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
@@ -806,7 +855,7 @@ int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int
     if (topk < 0 || topk > kDecMaxTopK) return fail(W4A16_ERR_INVALID_ARG, "k=%d outside 0..%d", topk, kDecMaxTopK);
     DecodePlan plan{};
     const int rc = make_decode_plan(M, N, K, group_size, packed_zeros != 0, slices, tiles, kw, tile_cols, ring,
-                                    topk > 0, &plan);
+                                    topk > 0, &plan, affine_bits);
     if (rc != W4A16_OK) return rc;
     if (plan_out) {
         plan_out[0] = plan.slices;

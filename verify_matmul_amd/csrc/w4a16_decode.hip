@@ -65,9 +65,65 @@ __device__ __forceinline__ int frag_pos(int m, int wr, int mp_log2)
     return ((t * 4 + q) << mp_log2) + (m ^ frag_swz(t, q, mp_log2));
 }
 
-template <bool kMfma, int kZM, int kU, int kV>
+// kLd: 16-byte weight loads per lane and step. GPTQ codes: kLd = kV (one word row of 4 * kV
+// columns). Affine codes (kZM == kAffine, 4 columns per lane): each column is a bit stream of
+// kBits bits per row, so a step's 32 rows are kBits word rows, and a lane's 8 rows are 8 * kBits
+// bits that start at bit 8 * kBits * (lane's K quarter) of the step: in one word row for 1, 2 and
+// 4 bits (kLd = 1), in two consecutive ones otherwise (kLd = 2; 3, 5, 6 and 8 bits).
+// The 8 codes of one column that a lane reads from an affine bit stream, as exact fp16 values q
+// in the slot order of dequant_word (pairs (k0, k4), (k1, k5), (k2, k6), (k3, k7)). The lane's
+// rows k0..k3 start at bit a_off of (w1:w0), rows k4..k7 at bit a_off4. Each pair is built in one
+// word, a code in the low bits of each half, read as fp16 1024 + q and less 1024 (exact: q < 256).
+template <int kBits>
+__device__ __forceinline__ half8_t affine_codes(uint32_t w0, uint32_t w1, int a_off, int a_off4, Masks mk)
+{
+    if constexpr (kBits == 4) {   // the 4-bit stream is the GPTQ word layout: zero point 0
+        return dequant_word(w0, zero_sub(0u), mk);
+    }
+    half2_t pr[4];
+    const half2_t sub = as_half2(0xE400E400u);   // -1024 in both halves
+    if constexpr (kBits == 8) {   // k0..k3: the bytes of w0, k4..k7: the bytes of w1
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + r) << 16) | (uint32_t)r;   // (w0 byte r, 0, w1 byte r, 0)
+            pr[r] = as_half2(__builtin_amdgcn_perm(w1, w0, sel) | 0x64006400u) + sub;
+        }
+    } else if constexpr (kBits == 2) {   // 16 bits from a_off: bytes (k0..k3), (k4..k7)
+        const uint32_t x = w0 >> (uint32_t)a_off;
+        const uint32_t y = __builtin_amdgcn_perm(0u, x, 0x0C010C00u);   // k0..k3 in the low half, k4..k7 in the high
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = as_half2(((y >> (2 * r)) & 0x00030003u) | 0x64006400u) + sub;
+    } else {   // 1, 3, 5 and 6 bits: two 32-bit windows of (w1:w0)
+        const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)a_off);
+        const uint32_t hi = a_off4 >= 32 ? w1 >> (uint32_t)(a_off4 - 32) : __builtin_amdgcn_alignbit(w1, w0, (uint32_t)a_off4);
+        constexpr uint32_t kMask2 = ((1u << kBits) - 1u) * 0x10001u;   // a code in both halves
+        if constexpr (kBits <= 4) {   // k0..k3 in the low half of y, k4..k7 in the high half
+            constexpr uint32_t kHalf = (1u << (4 * kBits)) - 1u;
+            const uint32_t y = (lo & kHalf) | ((hi & kHalf) << 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = as_half2(((y >> (kBits * r)) & kMask2) | 0x64006400u) + sub;
+        } else {                      // (k0, k1 | k4, k5) and (k2, k3 | k6, k7)
+            constexpr uint32_t kHalf = (1u << (2 * kBits)) - 1u;
+            const uint32_t y0 = (lo & kHalf) | ((hi & kHalf) << 16);
+            const uint32_t y1 = ((lo >> (2 * kBits)) & kHalf) | (((hi >> (2 * kBits)) & kHalf) << 16);
+            pr[0] = as_half2((y0 & kMask2) | 0x64006400u) + sub;
+            pr[1] = as_half2(((y0 >> kBits) & kMask2) | 0x64006400u) + sub;
+            pr[2] = as_half2((y1 & kMask2) | 0x64006400u) + sub;
+            pr[3] = as_half2(((y1 >> kBits) & kMask2) | 0x64006400u) + sub;
+        }
+    }
+    half8_t b;
+    b[0] = pr[0][0]; b[1] = pr[0][1]; b[2] = pr[1][0]; b[3] = pr[1][1];
+    b[4] = pr[2][0]; b[5] = pr[2][1]; b[6] = pr[3][0]; b[7] = pr[3][1];
+    return b;
+}
+
+template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4>
 __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 {
+    constexpr bool kAff = kZM == kAffine;
+    static_assert(!kAff || kLd == ((kBits == 1 || kBits == 2 || kBits == 4) ? 1 : 2), "word rows per lane and step");
+    static_assert(!kAff || kV == 1, "affine codes run on 64-column tiles");
     constexpr int kC = 4 * kV;      // adjacent columns per lane
     constexpr int kTile = 16 * kC;  // columns per wave
     constexpr int kRows = kMfma ? 4 : 1;
@@ -132,6 +188,16 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
                 if (it < sitems) load_to_lds4(p.qzeros + (size_t)gi * (N / 8) + c / 8, z_lds + b);
             }
         }
+        if constexpr (kAff) {   // the biases, laid out as the scales, over the zero words' region
+            uint16_t *bi_lds = reinterpret_cast<uint16_t *>(z_lds);
+            for (int b = wave * 64; b < sitems; b += T) {
+                const int it = b + lane;
+                const int gi = g0 + it / per;
+                int c = c0 + (it - (it / per) * per) * 8;
+                if (c >= N) c = 0;
+                if (it < sitems) load_to_lds16(p.biases + (size_t)gi * N + c, bi_lds + (size_t)b * 8);
+            }
+        }
     }
     asm volatile("" ::: "memory");
 
@@ -178,14 +244,18 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     // A buffer resource over exactly the slice's word rows: the ring reloads steps past the
     // wave's piece unconditionally (no branch in the loop); reads past the slice return zero
     // without a memory request. Non-temporal: every byte is read once per call.
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.qweight + (size_t)sb * 4 * N, (uint32_t)((se - sb) * 16 * N));
-    const uint32_t w_lane = ((uint32_t)rl * (uint32_t)N + (uint32_t)nc) * 4u;   // bytes (slices stay below 2 GiB)
-    uint4 ring[kU][kV];
+    constexpr int R = kAff ? kBits : 4;   // word rows per step
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.qweight + (size_t)sb * R * N, (uint32_t)((se - sb) * R * 4 * N));
+    // affine codes: the lane's 8 rows start at bit `a_bit` of the step, in word row a_bit / 32
+    const int a_bit = kAff ? 8 * kBits * rl : 0;
+    const uint32_t w_lane = ((uint32_t)(kAff ? a_bit >> 5 : rl) * (uint32_t)N + (uint32_t)nc) * 4u;   // bytes (< 2 GiB)
+    uint4 ring[kU][kLd];
     auto load_w = [&](uint4 *dst, int t) {
 #pragma unroll
-        for (int v = 0; v < kV; ++v) {
+        for (int v = 0; v < kLd; ++v) {   // GPTQ: the next 4 columns; affine: the next word row
             const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-                wrs, (int)(w_lane + (uint32_t)(t - sb) * 16u * (uint32_t)N + 16u * v), 0, kNonTemporal);
+                wrs, (int)(w_lane + (uint32_t)(t - sb) * (uint32_t)R * 4u * (uint32_t)N + (kAff ? 4u * (uint32_t)N : 16u) * v),
+                0, kNonTemporal);
             dst[v] = uint4{x.x, x.y, x.z, x.w};
         }
     };
@@ -200,7 +270,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 
     // ---- 4. row maxima, then the fp16 fragments ---------------------------------------------
     if (tid < 16) rowmax[tid] = 0u;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kU * kV));   // all but the ring: scales, zeros, activations
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kU * kLd));   // all but the ring: scales, zeros or biases, activations
     __syncthreads();                                  // every wave's direct loads have landed
     {   // each wave: the largest magnitude of each of its rows, one LDS atomic per row
         int i_m = m_first, c = 0;
@@ -261,6 +331,12 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     ZeroSub zs[kC];
 #pragma unroll
     for (int j = 0; j < kC; ++j) zs[j] = zero_sub_sym();
+    // affine codes: the sums of the activations themselves (times the group's bias), from one
+    // more product per step against ones; and the bit positions of the lane's 8 codes (rows k0..k3
+    // from bit a_off of its first word, rows k4..k7 from a_off + 4 * bits)
+    float4_t acc_one = float4_t{0.f, 0.f, 0.f, 0.f};
+    const int a_off = a_bit & 31, a_off4 = a_off + 4 * kBits;
+    const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
     int gi = wb / spg, gpos = wb - (wb / spg) * spg;
     bool first = true;
     // the lane's matrix-core fragment within a step: lane q * 16 + m reads row m, K quarter q.
@@ -281,7 +357,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 #pragma unroll
             for (int j = 0; j < kC; ++j) zs[j] = zero_sub(zero_of(zw, (uint32_t)(lcol + j)));
         }
-        uint32_t words[kC];
+        uint32_t words[kC], words1[kC];
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
             words[4 * v] = wv[v].x;
@@ -289,9 +365,32 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
             words[4 * v + 2] = wv[v].z;
             words[4 * v + 3] = wv[v].w;
         }
+        if constexpr (kAff && kLd == 2) {
+            words1[0] = wv[1].x;
+            words1[1] = wv[1].y;
+            words1[2] = wv[1].z;
+            words1[3] = wv[1].w;
+        }
+        if constexpr (kAff) {   // the activations' own sums, for the bias
+            if constexpr (kMfma) {
+                acc_one = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, acc_one, 0, 0, 0);
+            } else {
+                float s = acc_one[0];
+                s = __builtin_amdgcn_fdot2(ones.lo.lo, a.lo.lo, s, false);
+                s = __builtin_amdgcn_fdot2(ones.lo.hi, a.lo.hi, s, false);
+                s = __builtin_amdgcn_fdot2(ones.hi.lo, a.hi.lo, s, false);
+                s = __builtin_amdgcn_fdot2(ones.hi.hi, a.hi.hi, s, false);
+                acc_one[0] = s;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kC; ++j) {
-            const half8_t b = dequant_word(words[j], kZM == kZeroSym ? zero_sub_sym() : zs[j], mk);
+            half8_t b;
+            if constexpr (kAff) {
+                b = affine_codes<kBits>(words[j], kLd == 2 ? words1[j] : 0u, a_off, a_off4, mk);
+            } else {
+                b = dequant_word(words[j], kZM == kZeroSym ? zero_sub_sym() : zs[j], mk);
+            }
             if constexpr (kMfma) {
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
             } else {
@@ -317,18 +416,32 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
                 sw[2] = q.z;
                 sw[3] = q.w;
             }
+            uint32_t bw[kC / 2];   // affine: the group's biases, laid out as the scales
+            if constexpr (kAff) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(z_lds) +
+                                                                 (gi - g0) * WC + lcol);
+                bw[0] = v.x;
+                bw[1] = v.y;
+            }
 #pragma unroll
             for (int j = 0; j < kC; ++j) {
-                const float s = half_bits_to_float((sw[j / 2] >> (16 * (j & 1))) & 0xFFFFu);
+                const uint32_t sbits = (sw[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+                const float s = kAff ? bf16_bits_to_float(sbits) : half_bits_to_float(sbits);
+                const float bias = kAff ? bf16_bits_to_float((bw[j / 2] >> (16 * (j & 1))) & 0xFFFFu) : 0.f;
                 if constexpr (kMfma) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[j][r] = __builtin_fmaf(acc[j][r], s, tot[j][r]);
+                    for (int r = 0; r < 4; ++r) {
+                        tot[j][r] = __builtin_fmaf(acc[j][r], s, tot[j][r]);
+                        if constexpr (kAff) tot[j][r] = __builtin_fmaf(acc_one[r], bias, tot[j][r]);
+                    }
                     acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
                 } else {
                     tot[j][0] = __builtin_fmaf(acc[j][0], s, tot[j][0]);
+                    if constexpr (kAff) tot[j][0] = __builtin_fmaf(acc_one[0], bias, tot[j][0]);
                     acc[j][0] = 0.f;
                 }
             }
+            if constexpr (kAff) acc_one = float4_t{0.f, 0.f, 0.f, 0.f};
         }
         first = last;
         if (++gpos == spg) {
@@ -647,10 +760,10 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool kMfma, int kZM, int kU, int kV>
+template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4>
 hipError_t launch_one(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
 {
-    const auto kern = decode_kernel<kMfma, kZM, kU, kV>;
+    const auto kern = decode_kernel<kMfma, kZM, kU, kV, kLd, kBits>;
     if (plan.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
@@ -680,10 +793,28 @@ hipError_t launch_ring(const DecodeArgs &a, const DecodePlan &plan, hipStream_t 
     }
 }
 
+// affine codes: 64-column tiles, a ring of 4 steps, one instance per code width
+template <bool kMfma>
+hipError_t launch_affine(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
+{
+    if (plan.ring != 4) return hipErrorInvalidValue;
+    switch (a.bits) {
+    case 1: return launch_one<kMfma, kAffine, 4, 1, 1, 1>(a, plan, stream);
+    case 2: return launch_one<kMfma, kAffine, 4, 1, 1, 2>(a, plan, stream);
+    case 3: return launch_one<kMfma, kAffine, 4, 1, 2, 3>(a, plan, stream);
+    case 4: return launch_one<kMfma, kAffine, 4, 1, 1, 4>(a, plan, stream);
+    case 5: return launch_one<kMfma, kAffine, 4, 1, 2, 5>(a, plan, stream);
+    case 6: return launch_one<kMfma, kAffine, 4, 1, 2, 6>(a, plan, stream);
+    case 8: return launch_one<kMfma, kAffine, 4, 1, 2, 8>(a, plan, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
 {
+    if (a.biases) return plan.mfma ? launch_affine<true>(a, plan, stream) : launch_affine<false>(a, plan, stream);
     if (a.qzeros)
         return plan.mfma ? launch_ring<true, kZeroPacked>(a, plan, stream) : launch_ring<false, kZeroPacked>(a, plan, stream);
     return plan.mfma ? launch_ring<true, kZeroSym>(a, plan, stream) : launch_ring<false, kZeroSym>(a, plan, stream);

@@ -176,9 +176,11 @@ constexpr int kDecMaxTopK = 8;       // largest k of the fused pick
 constexpr int kDecHeld = 8;
 struct DecodeArgs {
     const uint16_t *A;
-    const uint32_t *qweight;
-    const uint16_t *scales;
+    const uint32_t *qweight;  // GPTQ [K/8, N]; affine codes: column bit streams [K * bits / 32, N]
+    const uint16_t *scales;   // fp16 (GPTQ) or bf16 (affine) [K/g, N]
     const uint32_t *qzeros;   // nullptr: symmetric zero point 8
+    const uint16_t *biases;   // affine codes: bf16 [K/g, N] (nullptr: GPTQ)
+    int bits;                 // affine codes: bits per code (1, 2, 3, 4, 5, 6 or 8)
     void *out;
     float *partials;          // [slices, M, N] fp32 (slices > 1)
     uint32_t *counters;       // [groups] zero between calls
@@ -215,7 +217,7 @@ inline int decode_mp_log2(int M) { return M <= 4 ? 2 : M <= 8 ? 3 : 4; }
 // per row of the padded rows per step; GEMV: 64 bytes per step), the workgroup's scales and zero
 // words of its groups, and the K pieces' sums (kw - 1 pieces of every tile).
 inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int tiles, int kw, int slices, bool packed,
-                                bool pick, DecodePlan *pl)
+                                bool pick, DecodePlan *pl, bool affine = false)
 {
     const int steps = K / kStepK;
     const int smax = (steps + slices - 1) / slices;
@@ -232,7 +234,8 @@ inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int ti
     const size_t s_off = a_off + a_bytes;
     const size_t s_bytes = groups * wc * 2;
     const size_t z_off = s_off + round_up_sz(s_bytes, 16);
-    const size_t z_bytes = packed ? groups * (wc / 8) * 4 : 0;
+    // the zero words, or for affine codes the biases (laid out as the scales)
+    const size_t z_bytes = affine ? s_bytes : packed ? groups * (wc / 8) * 4 : 0;
     const size_t r_off = round_up_sz(z_off + z_bytes, 16);
     const size_t r_bytes = (size_t)(kw - 1) * tiles * 64 * cols * (mfma ? 4 : 1) * sizeof(float);
     if (pl) {

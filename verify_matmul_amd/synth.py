@@ -240,6 +240,15 @@ AFFINE_WORKLOADS = {
     # the same projection of an 8-bit MLX checkpoint
     "ffn_up_affine8": AffineWorkload(7, "FFN up/gate 5120x17408 affine-8 g64", 5120, 17408, 64, 8,
                                      (1, 2, 4, 8, 16)),
+    # and of 2, 3, 5 and 6-bit ones (mixed-width checkpoints)
+    "ffn_up_affine2": AffineWorkload(8, "FFN up/gate 5120x17408 affine-2 g64", 5120, 17408, 64, 2,
+                                     (1, 2, 4, 8, 16)),
+    "ffn_up_affine3": AffineWorkload(9, "FFN up/gate 5120x17408 affine-3 g64", 5120, 17408, 64, 3,
+                                     (1, 2, 4, 8, 16)),
+    "ffn_up_affine5": AffineWorkload(10, "FFN up/gate 5120x17408 affine-5 g64", 5120, 17408, 64, 5,
+                                     (1, 2, 4, 8, 16)),
+    "ffn_up_affine6": AffineWorkload(11, "FFN up/gate 5120x17408 affine-6 g64", 5120, 17408, 64, 6,
+                                     (1, 2, 4, 8, 16)),
 }
 
 
