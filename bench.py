@@ -39,7 +39,9 @@ distribution): the bound is the fp16 matrix cores (2.5 PFLOP/s dense), and the l
 TFLOP/s (2*M*N*K per call) with an "mfma" roofline.
 
 --prefill --gate-up times the prompt-sized gated pair (w4a16_gemm_gate_up_prefill), 4*M*N*K
-flops per call.
+flops per call. --prefill --affine [--affine-bits B] times the affine prompt GEMM
+(w4a16_gemm_affine_bits_prefill) on the affine FFN up projection of that width (codes read as
+stored), activations N(0, 1).
 
 With --gate-up every call is instead the fused gated pair on the workload's shape,
 silu(A x W_gate) * (A x W_up) (w4a16_gemm_gate_up): two weight matrices per call, one [M, N]
@@ -242,10 +244,10 @@ def main():
         return 0
 
     lib = vm.load()
-    if args.affine:
-        return run_affine(args, lib)
     if args.prefill:
         return run_prefill(args, lib)
+    if args.affine:
+        return run_affine(args, lib)
     wl = synth.WORKLOADS[args.workload]
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else wl.ms
     inp = synth.make_inputs(wl)
@@ -713,25 +715,39 @@ def run_prefill(args, lib):
     import verify_matmul_amd as vm
     from verify_matmul_amd import synth
 
-    wl = synth.WORKLOADS[args.workload]
-    if wl.argmax or args.splits or args.waves_k or args.tile_cols:
-        print("bench.py: --prefill takes an FFN or attention workload and no launch knobs", file=sys.stderr)
+    aff = args.affine   # affine codes read at their own width
+    wl = synth.AFFINE_WORKLOADS[f"ffn_up_affine{args.affine_bits}"] if aff else synth.WORKLOADS[args.workload]
+    if (not aff and wl.argmax) or args.splits or args.waves_k or args.tile_cols or (aff and args.gate_up):
+        print("bench.py: --prefill takes an FFN or attention workload (or --affine, a single matrix) and no launch "
+              "knobs", file=sys.stderr)
+        return 2
+    if aff and args.affine_bits == 7:
+        print("bench.py: the affine prompt GEMM reads 1-6 and 8-bit codes", file=sys.stderr)
         return 2
     pair = args.gate_up   # the gated pair silu(A x W_gate) * (A x W_up): 4 M N K flops per call
     nmat = 2 if pair else 1
     ms = tuple(int(x) for x in args.ms.split(",")) if args.ms else (512, 2048)
-    inp = synth.make_inputs(wl)
     K, N, g = wl.K, wl.N, wl.group
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     # prompt-sized activations with the workload's distribution (its own seeded draw)
     rng = np.random.Generator(np.random.PCG64(1000 * wl.index + 8))
-    act = synth.draw_activations(rng, max(ms), K, wl.act_sigma, wl.outlier_frac, wl.outlier_mul)
-    per_copy = algorithmic_bytes(0, K, N, g, wl.symmetric)
+    if aff:
+        xa = synth.make_affine_inputs(wl)
+        act = synth.draw_activations(rng, max(ms), K, 1.0, 0.0, 1.0)
+        per_copy = affine_bytes(0, K, N, g, wl.bits)
+        qw0 = torch.from_numpy(np.ascontiguousarray(xa.packed).view(np.int32)).to(dev)
+        sc = torch.from_numpy(xa.scales.view(np.int16)).to(dev)
+        bi = torch.from_numpy(xa.biases.view(np.int16)).to(dev)
+        qz = None
+    else:
+        inp = synth.make_inputs(wl)
+        act = synth.draw_activations(rng, max(ms), K, wl.act_sigma, wl.outlier_frac, wl.outlier_mul)
+        per_copy = algorithmic_bytes(0, K, N, g, wl.symmetric)
+        qw0 = torch.from_numpy(inp.qweight.view(np.int32)).to(dev)
+        sc = torch.from_numpy(inp.scales.view(np.int16)).to(dev)
+        qz = None if inp.qzeros is None else torch.from_numpy(inp.qzeros.view(np.int32)).to(dev)
     R = max(2, math.ceil(POOL_BYTES / per_copy))
-    qw0 = torch.from_numpy(inp.qweight.view(np.int32)).to(dev)
-    sc = torch.from_numpy(inp.scales.view(np.int16)).to(dev)
-    qz = None if inp.qzeros is None else torch.from_numpy(inp.qzeros.view(np.int32)).to(dev)
     pool = [qw0.clone() for _ in range(R)]
     if pair:
         gate_inp = synth.make_gate_inputs(wl)
@@ -747,6 +763,8 @@ def run_prefill(args, lib):
         if pair:
             vm.w4a16_gemm_gate_up_prefill(a[:M], (gpool[i % R], gs, gz), (pool[i % R], sc, qz), g, outs[M],
                                           stream=stream)
+        elif aff:
+            vm.w4a16_gemm_affine_bits_prefill(a[:M], pool[i % R], wl.bits, sc, bi, g, outs[M], stream=stream)
         else:
             vm.w4a16_gemm_prefill(a[:M], pool[i % R], sc, qz, g, outs[M], stream=stream)
 
@@ -781,7 +799,9 @@ def run_prefill(args, lib):
                          "us_p10": round(float(np.percentile(d, 10)), 3),
                          "us_p90": round(float(np.percentile(d, 90)), 3), "TFLOPs": round(f / us / 1e6, 1),
                          "frac_of_peak": round(f / us / 1e6 / PEAK_F16_TFLOPS, 4), "flops": f,
-                         "hbm_GBps_weights_once": round(algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat) / us / 1e3, 1)}
+                         "hbm_GBps_weights_once": round((affine_bytes(M, K, N, g, wl.bits) if aff else
+                                                         algorithmic_bytes(M, K, N, g, wl.symmetric, matrices=nmat))
+                                                        / us / 1e3, 1)}
         if float(np.sum(d)) > dom_time:
             dom, dom_time = M, float(np.sum(d))
     # the dominant call alone, back to back between one event pair on its stream
@@ -809,12 +829,13 @@ def run_prefill(args, lib):
         "data": "synthetic",
         "config": {"workload": (f"{wl.name} gated pair silu(A x W_gate) * (A x W_up)" if pair else wl.name) +
                                f", prompt rows M in {','.join(map(str, ms))} (one call each per step)",
-                   "K": K, "N": N, "group": g, "symmetric_zero": wl.symmetric, "ms": list(ms), "out": "fp32",
-                   "rotation_copies": R},
-        "roofline": {"bound": "mfma", "kernel": f"w4a16_prefill_kernel ({'gated pair, ' if pair else ''}M={dom})", "M": dom,
+                   "K": K, "N": N, "group": g, "ms": list(ms), "out": "fp32", "rotation_copies": R,
+                   **({"affine_bits": wl.bits, "scales_biases": "bf16"} if aff else {"symmetric_zero": wl.symmetric})},
+        "roofline": {"bound": "mfma", "kernel": f"w4a16_prefill_kernel ({'gated pair, ' if pair else ''}"
+                                                f"{f'affine-{wl.bits}, ' if aff else ''}M={dom})", "M": dom,
                      "achieved": round(f_dom / us_dom / 1e6, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(f_dom / us_dom / 1e6 / PEAK_F16_TFLOPS, 4),
-                     "traffic": None if pair else load_traffic(args.workload, dom, "w4a16_prefill_kernel"),
+                     "traffic": None if pair or aff else load_traffic(args.workload, dom, "w4a16_prefill_kernel"),
                      "launches": args.steps, "flops_per_launch": f_dom, "us_per_launch": round(us_dom, 3),
                      "us_per_launch_lone_event_pair": per_m[str(dom)]["us_per_call"]},
         "per_m": per_m,
@@ -831,6 +852,8 @@ def run_prefill(args, lib):
             if pair:
                 oracle.gate_up(act[:M], (gate_inp.qweight, gate_inp.scales, gate_inp.qzeros),
                                (inp.qweight, inp.scales, inp.qzeros), g, cols)
+            elif aff:
+                oracle.affine_gemm(act[:M], xa.packed, wl.bits, xa.scales, xa.biases, g, cols)
             else:
                 oracle.gemm(act[:M], inp.qweight, inp.scales, inp.qzeros, g, cols, with_bound=False)
             elapsed += time.perf_counter() - t

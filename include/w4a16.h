@@ -295,6 +295,21 @@ int w4a16_gemm_affine_bits_ex(const void *A, const uint32_t *packed, int bits,
                               int kw, int ring, hipStream_t stream);
 
 /*
+ * The same product for many rows (prompt processing), on the prompt GEMM of w4a16_gemm_prefill
+ * (TensorFold PR #859, PR description: a prompt GEMM for the affine codes beside their GEMV):
+ * packed, bits, scales and biases as w4a16_gemm_affine_bits, each code read at its own width;
+ * A, out, M (1..W4A16_PREFILL_MAX_M), the per-row rescale of A, scratch and determinism as
+ * w4a16_gemm_prefill; the accuracy contract of w4a16_gemm_affine. Every group adds
+ * scale * sum(a q) + bias * sum(a) in fp32, sum(a) taken on the matrix cores from the same fp16
+ * activations. Errors as w4a16_gemm_affine_bits (bits outside 1..6 and 8, a missing bias
+ * pointer, codes beyond 2^32 words), then as w4a16_gemm_prefill.
+ */
+int w4a16_gemm_affine_bits_prefill(const void *A, const uint32_t *packed, int bits,
+                                   const uint16_t *scales, const uint16_t *biases, int group_size,
+                                   int M, int N, int K, void *out, int out_dtype,
+                                   hipStream_t stream);
+
+/*
  * The gated feed-forward input of two affine matrices, out = silu(A x W_gate) * (A x W_up), each W
  * = scale * q + bias as in w4a16_gemm_affine (4-bit codes, bf16 scales and biases, same shape):
  * the operation, launch and scratch of w4a16_gemm_gate_up, each product under w4a16_gemm_affine's

@@ -110,3 +110,22 @@ def test_affine_bits_checks_its_arguments(lib):
     assert f(A, A, 2, A, A, 64, 17, 256, 512, O, 0, None) == -1      # M
     assert lib.w4a16_gemm_affine_bits_ex(A, A, 3, A, A, 64, 2, 256, 512, O, 0, 0, 0, 0, 3, None) == -1
     assert b"ring" in lib.w4a16_last_error()
+
+
+def test_affine_bits_prefill_checks_its_arguments(lib):
+    """The affine prompt GEMM refuses what w4a16_gemm_affine_bits refuses, with M up to
+    W4A16_PREFILL_MAX_M, before any device work."""
+    A = O = 4096
+    f = lib.w4a16_gemm_affine_bits_prefill
+    assert f(A, A, 2, A, None, 64, 300, 256, 512, O, 0, None) == -1
+    assert b"biases" in lib.w4a16_last_error()
+    for bits in (0, 7, 9, -1):
+        assert f(A, A, bits, A, A, 64, 300, 256, 512, O, 0, None) == -1
+        assert b"bits=" in lib.w4a16_last_error()
+    assert f(A, A, 2, A, A + 8, 64, 300, 256, 512, O, 0, None) == -2   # biases not 16-byte aligned
+    assert f(A, A, 2, A, A, 48, 300, 256, 512, O, 0, None) == -1       # group size
+    assert f(A, A, 2, A, A, 64, 0, 256, 512, O, 0, None) == -1         # M
+    assert f(A, A, 2, A, A, 64, 65537, 256, 512, O, 0, None) == -1
+    assert b"M=65537" in lib.w4a16_last_error()
+    assert f(A, A, 8, A, A, 64, 300, 260, 512, O, 0, None) == -1       # N % 8
+    assert f(A, A, 8, A, A, 64, 300, 256, 512, O, 2, None) == -1       # out_dtype

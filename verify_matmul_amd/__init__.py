@@ -18,7 +18,7 @@ __all__ = [
     "w4a16_gemm_gate_up", "w4a16_gemm_prefill", "w4a16_gemm_gate_up_prefill", "w4a16_plan",
     "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_release_scratch",
     "w4a16_gemm_affine", "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split",
-    "w4a16_gemm_affine_bits",
+    "w4a16_gemm_affine_bits", "w4a16_gemm_affine_bits_prefill",
     "w4a16_gemm_affine_gate_up", "w4a16_stream_read", "EXPORTS",
 ]
 
@@ -31,7 +31,7 @@ EXPORTS = (
     "w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_prefill",
     "w4a16_gemm_gate_up", "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill", "w4a16_gemm_affine", "w4a16_gemm_affine_ex",
     "w4a16_affine_widen", "w4a16_affine_split", "w4a16_gemm_affine_split", "w4a16_gemm_affine_bits",
-    "w4a16_gemm_affine_bits_ex", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch", "w4a16_status_string",
+    "w4a16_gemm_affine_bits_ex", "w4a16_gemm_affine_bits_prefill", "w4a16_gemm_affine_gate_up", "w4a16_plan", "w4a16_argmax_rows", "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch", "w4a16_status_string",
     "w4a16_last_error", "w4a16_version", "w4a16_source_hash",
 )
 
@@ -68,6 +68,7 @@ def load():
     lib.w4a16_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, I, I, P]
     lib.w4a16_gemm_affine_bits.argtypes = [P, P, I, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_affine_bits_ex.argtypes = [P, P, I, P, P, I, I, I, I, P, I, I, I, I, I, P]
+    lib.w4a16_gemm_affine_bits_prefill.argtypes = [P, P, I, P, P, I, I, I, I, P, I, P]
     lib.w4a16_gemm_topk.argtypes = [P, P, P, P, I, I, I, I, P, I, I, P, P]
     lib.w4a16_gemm_ex.argtypes = [P, P, P, P, I, I, I, I, P, I, I, I, I, P]
     lib.w4a16_gemm_argmax.argtypes = [P, P, P, P, I, I, I, I, P, I, P, P]
@@ -92,7 +93,7 @@ def load():
     lib.w4a16_last_error.argtypes = []
     lib.w4a16_last_error.restype = ctypes.c_char_p
     lib.w4a16_version.argtypes = []
-    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_affine_bits", "w4a16_gemm_affine_bits_ex", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
+    for f in ("w4a16_gemm", "w4a16_gemm_noalloc", "w4a16_gemm_ex", "w4a16_gemm_decode_ex", "w4a16_decode_plan", "w4a16_gemm_argmax", "w4a16_gemm_topk", "w4a16_gemm_affine_bits", "w4a16_gemm_affine_bits_ex", "w4a16_gemm_affine_bits_prefill", "w4a16_gemm_prefill", "w4a16_gemm_gate_up",
               "w4a16_gemm_gate_up_ex", "w4a16_gemm_gate_up_prefill",
               "w4a16_plan", "w4a16_argmax_rows",
               "w4a16_unpack_u8", "w4a16_dequant_f32", "w4a16_stream_read", "w4a16_release_scratch",
@@ -397,6 +398,29 @@ def w4a16_gemm_affine_bits(A, packed, bits, scales, biases, group_size, out, sli
                                             M, N, K, _ptr(out, "out", (torch.float32, torch.bfloat16)), dt,
                                             int(slices), int(tiles), int(kw), int(ring), _stream(stream)),
            "w4a16_gemm_affine_bits")
+    return out
+
+
+def w4a16_gemm_affine_bits_prefill(A, packed, bits, scales, biases, group_size, out, stream=None):
+    """The product of w4a16_gemm_affine_bits for many rows (M up to 65536), on the prompt GEMM."""
+    M, K = A.shape
+    N = packed.shape[1]
+    if packed.shape[0] * 32 != K * bits:
+        raise ValueError(f"packed {tuple(packed.shape)} is not [{K * bits // 32}, {N}] for {bits}-bit codes")
+    if tuple(scales.shape) != (K // group_size, N) or tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("scales and biases must be [K/g, N]")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out {tuple(out.shape)} is not [{M}, {N}]")
+    dt = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}.get(out.dtype)
+    if dt is None:
+        raise TypeError("out must be float32 or bfloat16")
+    _sb = (torch.bfloat16, torch.int16, torch.uint16)
+    _check(load().w4a16_gemm_affine_bits_prefill(_ptr(A, "A", _sb), _ptr(packed, "packed", _I32), int(bits),
+                                                 _ptr(scales, "scales", _sb), _ptr(biases, "biases", _sb),
+                                                 int(group_size), M, N, K,
+                                                 _ptr(out, "out", (torch.float32, torch.bfloat16)), dt,
+                                                 _stream(stream)),
+           "w4a16_gemm_affine_bits_prefill")
     return out
 
 

@@ -475,6 +475,21 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     return W4A16_OK;
 }
 
+// Affine codes read at their own width: column bit streams [K * bits / 32, N] (addressed with
+// 32-bit word offsets), bf16 scales and biases, no zero points.
+int check_affine_bits_args(const uint32_t *qzeros, const uint16_t *biases, int bits, int N, int K)
+{
+    if (!biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
+    if (qzeros) return fail(W4A16_ERR_INVALID_ARG, "affine codes take no zero points");
+    if (!(bits >= 1 && bits <= 6) && bits != 8)
+        return fail(W4A16_ERR_INVALID_ARG, "bits=%d is not 1, 2, 3, 4, 5, 6 or 8 (7-bit codes: w4a16_affine_split)",
+                    bits);
+    if (!aligned16(biases)) return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
+    if ((long long)(K / 32) * bits * N > 0xFFFFFFFFLL)
+        return fail(W4A16_ERR_UNSUPPORTED, "codes of %lld words exceed 2^32 words", (long long)(K / 32) * bits * N);
+    return W4A16_OK;
+}
+
 // A decode-kernel call: check, plan, take scratch, launch.
 int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                 int group_size, int M, int N, int K, void *out, int out_dtype, int slices, int tiles, int kw,
@@ -483,15 +498,9 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
 {
     int rc = check_gemm_args(A, qweight, scales, qzeros, group_size, M, N, K, out, out_dtype);
     if (rc != W4A16_OK) return rc;
-    if (bits) {   // affine codes: column bit streams [K * bits / 32, N], bf16 scales and biases
-        if (!biases) return fail(W4A16_ERR_INVALID_ARG, "null pointer (biases)");
-        if (qzeros) return fail(W4A16_ERR_INVALID_ARG, "affine codes take no zero points");
-        if (!(bits >= 1 && bits <= 6) && bits != 8)
-            return fail(W4A16_ERR_INVALID_ARG, "bits=%d is not 1, 2, 3, 4, 5, 6 or 8 (7-bit codes: w4a16_affine_split)",
-                        bits);
-        if (!aligned16(biases)) return fail(W4A16_ERR_UNSUPPORTED, "every pointer must be 16-byte aligned");
-        if ((long long)(K / 32) * bits * N > 0xFFFFFFFFLL)
-            return fail(W4A16_ERR_UNSUPPORTED, "codes of %lld words exceed 2^32 words", (long long)(K / 32) * bits * N);
+    if (bits) {
+        rc = check_affine_bits_args(qzeros, biases, bits, N, K);
+        if (rc != W4A16_OK) return rc;
     }
     if (slices < 0 || tiles < 0 || kw < 0 || ring < 0)
         return fail(W4A16_ERR_INVALID_ARG, "slices=%d tiles=%d kw=%d ring=%d must be >= 0", slices, tiles, kw, ring);
@@ -573,12 +582,17 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
 }
 
 // A many-row call (prompt processing): check, choose the K slices, take scratch, prepare the
-// activations, launch. `up` non-null makes it a gated pair (w is the gate).
+// activations, launch. `up` non-null makes it a gated pair (w is the gate); bits > 0 makes w
+// affine codes of that width (w.biases given), a single matrix.
 int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
-                 int out_dtype, hipStream_t stream)
+                 int out_dtype, hipStream_t stream, int bits = 0)
 {
     int rc = check_gemm_args(A, w.qweight, w.scales, w.qzeros, group_size, M, N, K, out, out_dtype, W4A16_PREFILL_MAX_M);
     if (rc != W4A16_OK) return rc;
+    if (bits) {
+        rc = check_affine_bits_args(w.qzeros, w.biases, bits, N, K);
+        if (rc != W4A16_OK) return rc;
+    }
     if (up) {
         rc = check_gemm_args(A, up->qweight, up->scales, up->qzeros, group_size, M, N, K, out, out_dtype,
                              W4A16_PREFILL_MAX_M);
@@ -622,6 +636,8 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
         pa.scales2 = up->scales;
         pa.qzeros2 = up->qzeros;
     }
+    pa.biases = bits ? w.biases : nullptr;
+    pa.bits = bits;
     pa.out = out;
     pa.partials = v.partials;
     pa.M = M;
@@ -670,6 +686,16 @@ int w4a16_gemm_affine_bits(const void *A, const uint32_t *packed, int bits, cons
 {
     return w4a16_gemm_affine_bits_ex(A, packed, bits, scales, biases, group_size, M, N, K, out, out_dtype, 0, 0, 0, 0,
                                      stream);
+}
+
+int w4a16_gemm_affine_bits_prefill(const void *A, const uint32_t *packed, int bits, const uint16_t *scales,
+                                   const uint16_t *biases, int group_size, int M, int N, int K, void *out,
+                                   int out_dtype, hipStream_t stream)
+{
+    if (bits == 0) return fail(W4A16_ERR_INVALID_ARG, "bits=0 is not 1, 2, 3, 4, 5, 6 or 8");
+    Matrix w{packed, scales, nullptr};
+    w.biases = biases;
+    return prefill_call(A, w, nullptr, group_size, M, N, K, out, out_dtype, stream, bits);
 }
 
 int w4a16_gemm_topk(const void *A, const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,

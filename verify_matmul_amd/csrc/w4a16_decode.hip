@@ -70,54 +70,6 @@ __device__ __forceinline__ int frag_pos(int m, int wr, int mp_log2)
 // kBits bits per row, so a step's 32 rows are kBits word rows, and a lane's 8 rows are 8 * kBits
 // bits that start at bit 8 * kBits * (lane's K quarter) of the step: in one word row for 1, 2 and
 // 4 bits (kLd = 1), in two consecutive ones otherwise (kLd = 2; 3, 5, 6 and 8 bits).
-// The 8 codes of one column that a lane reads from an affine bit stream, as exact fp16 values q
-// in the slot order of dequant_word (pairs (k0, k4), (k1, k5), (k2, k6), (k3, k7)). The lane's
-// rows k0..k3 start at bit a_off of (w1:w0), rows k4..k7 at bit a_off4. Each pair is built in one
-// word, a code in the low bits of each half, read as fp16 1024 + q and less 1024 (exact: q < 256).
-template <int kBits>
-__device__ __forceinline__ half8_t affine_codes(uint32_t w0, uint32_t w1, int a_off, int a_off4, Masks mk)
-{
-    if constexpr (kBits == 4) {   // the 4-bit stream is the GPTQ word layout: zero point 0
-        return dequant_word(w0, zero_sub(0u), mk);
-    }
-    half2_t pr[4];
-    const half2_t sub = as_half2(0xE400E400u);   // -1024 in both halves
-    if constexpr (kBits == 8) {   // k0..k3: the bytes of w0, k4..k7: the bytes of w1
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + r) << 16) | (uint32_t)r;   // (w0 byte r, 0, w1 byte r, 0)
-            pr[r] = as_half2(__builtin_amdgcn_perm(w1, w0, sel) | 0x64006400u) + sub;
-        }
-    } else if constexpr (kBits == 2) {   // 16 bits from a_off: bytes (k0..k3), (k4..k7)
-        const uint32_t x = w0 >> (uint32_t)a_off;
-        const uint32_t y = __builtin_amdgcn_perm(0u, x, 0x0C010C00u);   // k0..k3 in the low half, k4..k7 in the high
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = as_half2(((y >> (2 * r)) & 0x00030003u) | 0x64006400u) + sub;
-    } else {   // 1, 3, 5 and 6 bits: two 32-bit windows of (w1:w0)
-        const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)a_off);
-        const uint32_t hi = a_off4 >= 32 ? w1 >> (uint32_t)(a_off4 - 32) : __builtin_amdgcn_alignbit(w1, w0, (uint32_t)a_off4);
-        constexpr uint32_t kMask2 = ((1u << kBits) - 1u) * 0x10001u;   // a code in both halves
-        if constexpr (kBits <= 4) {   // k0..k3 in the low half of y, k4..k7 in the high half
-            constexpr uint32_t kHalf = (1u << (4 * kBits)) - 1u;
-            const uint32_t y = (lo & kHalf) | ((hi & kHalf) << 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = as_half2(((y >> (kBits * r)) & kMask2) | 0x64006400u) + sub;
-        } else {                      // (k0, k1 | k4, k5) and (k2, k3 | k6, k7)
-            constexpr uint32_t kHalf = (1u << (2 * kBits)) - 1u;
-            const uint32_t y0 = (lo & kHalf) | ((hi & kHalf) << 16);
-            const uint32_t y1 = ((lo >> (2 * kBits)) & kHalf) | (((hi >> (2 * kBits)) & kHalf) << 16);
-            pr[0] = as_half2((y0 & kMask2) | 0x64006400u) + sub;
-            pr[1] = as_half2(((y0 >> kBits) & kMask2) | 0x64006400u) + sub;
-            pr[2] = as_half2((y1 & kMask2) | 0x64006400u) + sub;
-            pr[3] = as_half2(((y1 >> kBits) & kMask2) | 0x64006400u) + sub;
-        }
-    }
-    half8_t b;
-    b[0] = pr[0][0]; b[1] = pr[0][1]; b[2] = pr[1][0]; b[3] = pr[1][1];
-    b[4] = pr[2][0]; b[5] = pr[2][1]; b[6] = pr[3][0]; b[7] = pr[3][1];
-    return b;
-}
-
 template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4>
 __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 {

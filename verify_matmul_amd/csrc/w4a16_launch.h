@@ -151,6 +151,10 @@ struct PrefillArgs {
     const uint32_t *qweight2;
     const uint16_t *scales2;
     const uint32_t *qzeros2;
+    // affine codes (bits > 0): qweight is the column bit stream [K * bits / 32, N], scales and
+    // biases bf16 [K / g, N], no zero points, a single matrix
+    const uint16_t *biases;
+    int bits;
     void *out;
     float *partials;          // [splits, M, N] fp32 slices when splits > 1 ([splits, M, 2N] for a pair)
     int M, N, K, g;

@@ -32,29 +32,56 @@ constexpr int kRowGroup = 4; // row tiles that visit the column tiles together
 
 // One stage of LDS: the activation tile [64 rows][4 chunks of 16 B] (a row's chunk c sits in
 // slot c ^ ((row / 4) % 4): the 16 rows a wave reads at once then fall into 16 different bank
-// groups), the packed weights [4 word rows][256 columns], 256 fp16 scales, 32 zero words.
-constexpr int kStA = kPrefillTileM * 64;
-constexpr int kStB = 4 * kPrefillTileN * 4;
-constexpr int kStS = kPrefillTileN * 2;
-constexpr int kStZ = kPrefillTileN / 8 * 4;
-constexpr int kStBytes = kStA + kStB + kStS + kStZ;
+// groups), the codes [R word rows][256 columns], then for GPTQ codes 256 fp16 scales and 32 zero
+// words, for affine codes per wave w the bf16 scales of columns [64 w, 64 w + 64) followed by
+// their bf16 biases. R = 4 for GPTQ words; R = the code width for affine bit streams (a step's
+// 32 rows of a column are that many words).
+template <int kBits>
+struct Stage {
+    static constexpr int R = kBits ? kBits : 4;
+    static constexpr int A = kPrefillTileM * 64;
+    static constexpr int B = R * kPrefillTileN * 4;
+    static constexpr int S = kPrefillTileN * 2;
+    static constexpr int Z = kBits ? kPrefillTileN * 2 : kPrefillTileN / 8 * 4;
+    static constexpr int bytes = A + B + S + Z;
+};
 
 // Waves per SIMD the register allocator must keep: 3 for symmetric zero points (the gated pair
 // needs it: FFN 5120 x 17408 at M = 2048, 852 us against 985 with 2), 2 with stored zero
 // points, whose extra registers would spill at 3 (FFN down 17408 x 5120 at M = 2048: 1158 us
-// at 3 against 772 at 2).
-template <bool kSym>
-constexpr int prefill_min_waves() { return kSym ? 3 : 2; }
+// at 3 against 772 at 2), and 2 for affine codes (16 more accumulators: the bias sums).
+template <bool kSym, int kBits>
+constexpr int prefill_min_waves() { return kSym && !kBits ? 3 : 2; }
 
 // kDual: a gated pair (gate in qweight, up in qweight2). The tile's 256 columns are then 128
 // output columns of the gate followed by the same 128 of the up projection: waves 0 and 1
 // compute the gate, waves 2 and 3 the up projection, and the up waves hand their sums to the
 // gate waves through LDS, which write silu(gate) * up. Everything up to the epilogue is the
 // single-matrix kernel over those 256 columns.
-template <bool kSym, bool kDual>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_min_waves<kSym>()))) void
+//
+// kBits > 0: affine codes w = s * q + b (MLX affine checkpoints, TensorFold PR #859, commit
+// messages and PR description: codes of their own width, and a prompt GEMM for them), stored as
+// column bit streams [K * kBits / 32, N] with bf16 scales and biases [K / g, N]. A step stages
+// its kBits word rows; each lane pulls its column's 8 codes out of one or two words as exact
+// fp16 values (affine_codes), and one more matrix-core product per row block against ones gives
+// the activations' own sums, so every group adds s * sum(a q) + b * sum(a) in fp32.
+template <bool kSym, bool kDual, int kBits = 0>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(prefill_min_waves<kSym, kBits>()))) void
 w4a16_prefill_kernel(PrefillArgs p)
 {
+    constexpr bool kAff = kBits > 0;
+    static_assert(!(kAff && kDual), "the affine prompt GEMM is a single matrix");
+    using St = Stage<kBits>;
+    constexpr int kStA = St::A;
+    constexpr int kStB = St::B;
+    constexpr int kStS = St::S;
+    constexpr int kStBytes = St::bytes;
+    constexpr int R = St::R;
+    // codes staged with 16-byte loads (word rows w, w + 4 of the step by wave w: GPTQ words and
+    // 4- and 8-bit streams) or 4-byte loads (column t of every word row by thread t: widths 1, 2,
+    // 3, 5 and 6), so that every wave issues the same number of loads per stage
+    constexpr bool kWide = !kAff || kBits % 4 == 0;
+    constexpr int kWLoads = !kAff ? 1 : kWide ? kBits / 4 : kBits;
     constexpr int kOutCols = kDual ? kPrefillTileN / 2 : kPrefillTileN;   // output columns per tile
     __shared__ __align__(16) unsigned char lds[kStages * kStBytes];
     const int tid = threadIdx.x;
@@ -93,7 +120,7 @@ w4a16_prefill_kernel(PrefillArgs p)
     const int steps = (ge - gb) * spg;    // steps of the slice (>= 1: splits <= groups)
 
     // ---- loads of one stage: every wave issues the same kLoads direct loads -------------------
-    constexpr int kLoads = kSym ? 3 : 4;
+    constexpr int kLoads = 2 + kWLoads + (!kAff && !kSym ? 1 : 0);
     // activation tile: wave w fills slots [64 w, 64 w + 64), rows 16 w .. 16 w + 15
     const uint16_t *a_src;
     {
@@ -107,19 +134,35 @@ w4a16_prefill_kernel(PrefillArgs p)
     // output column tn + c % 128 of the gate (c < 128) or of the up projection.
     auto in_up = [&](int c) { return kDual && c >= kOutCols; };
     auto out_col = [&](int c) { return col(tn + (kDual ? c % kOutCols : c)); };
-    // packed weights: wave w loads word row w of the step, four columns per lane
-    const uint32_t *w_src = (in_up(lane * 4) ? p.qweight2 : p.qweight) + (size_t)wave * N + out_col(lane * 4);
-    // scales: wave w loads columns [64 w, 64 w + 64) as 32 pairs; zero words: wave w loads 8
+    // packed weights: wave w loads word row w of the step (and w + 4 of an 8-bit stream), four
+    // columns per lane; or thread t loads column t of every word row of the step
+    const uint32_t *w_src = kWide ? (in_up(lane * 4) ? p.qweight2 : p.qweight) + (size_t)wave * N + out_col(lane * 4)
+                                  : p.qweight + out_col(tid);
+    // scales: wave w loads columns [64 w, 64 w + 64) as 32 pairs; zero words: wave w loads 8;
+    // affine biases: lanes 32..63 load the same columns' biases right after the scales
     const int sc_c = wave * 64 + (lane & 31) * 2;
-    const uint16_t *s_src = (in_up(sc_c) ? p.scales2 : p.scales) + out_col(sc_c);
+    const uint16_t *s_src = kAff ? (lane < 32 ? p.scales : p.biases) + out_col(sc_c)
+                                 : (in_up(sc_c) ? p.scales2 : p.scales) + out_col(sc_c);
     const int zc_c = (wave * 8 + (lane & 7)) * 8;
     const uint32_t *z_src = kSym ? nullptr : (in_up(zc_c) ? p.qzeros2 : p.qzeros) + out_col(zc_c) / 8;
     int lt = s0, lg = gb, lpos = 0;   // next step to stage, its group and position in the group
     auto issue = [&](int buf) {
         unsigned char *st = lds + buf * kStBytes;
         load_to_lds16(a_src + (size_t)lt * kStepK, st + wave * 64 * 16);
-        load_to_lds16(w_src + (uint32_t)lt * 4u * (uint32_t)N, st + kStA + wave * 1024);   // < 2^32 words
-        if (lane < 32) load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
+        // word offsets < 2^32 (host)
+#pragma unroll
+        for (int j = 0; j < kWLoads; ++j) {
+            if constexpr (kWide)
+                load_to_lds16(w_src + ((uint32_t)lt * (uint32_t)R + 4u * (uint32_t)j) * (uint32_t)N,
+                              st + kStA + (wave + 4 * j) * 1024);
+            else
+                load_to_lds4(w_src + ((uint32_t)lt * (uint32_t)R + (uint32_t)j) * (uint32_t)N,
+                             st + kStA + j * 1024 + wave * 256);
+        }
+        if constexpr (kAff)
+            load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 256);
+        else if (lane < 32)
+            load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
         if (!kSym && lane < 8) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 32);
         if (lt + 1 < s0 + steps) {   // past the slice's last step the stage reloads it (uniform)
             ++lt;
@@ -145,6 +188,19 @@ w4a16_prefill_kernel(PrefillArgs p)
     ZeroSub zs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) zs[j] = zero_sub_sym();
+    // affine codes: the activations' own sums per row block (times the group's bias), and the
+    // words holding the lane's 8 codes: bit a_bit = 8 * kBits * rl of the step's column stream
+    // onwards, in word row w_row0 and, for widths that cross a word, w_row1 (a row of the step
+    // whose bits are not used when the codes end in w_row0)
+    float4_t acc_one[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc_one[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const half8_t ones = half8_t{1, 1, 1, 1, 1, 1, 1, 1};
+    constexpr bool kTwoWords = kAff && !(kBits == 1 || kBits == 2 || kBits == 4);
+    const int a_bit = kAff ? 8 * kBits * rl : 0;
+    const int c_off = a_bit & 31, c_off4 = c_off + 4 * kBits;   // bit positions of rows k0 and k4
+    const int w_row0 = kAff ? a_bit >> 5 : rl;
+    const int w_row1 = min(w_row0 + 1, R - 1);
     int cpos = 0;   // position of the computed step in its group
     int a_off[4];   // the lane's A fragment of each row block within a stage
 #pragma unroll
@@ -152,8 +208,9 @@ w4a16_prefill_kernel(PrefillArgs p)
         const int row = 16 * i + cl;
         a_off[i] = row * 64 + ((rl ^ ((row >> 2) & 3)) * 16);
     }
-    const int b_off = kStA + rl * 1024 + (wn * 64 + cl * 4) * 4;
-    const int s_off = kStA + kStB + (wn * 64 + cl * 4) * 2;
+    const int b_off = kStA + w_row0 * 1024 + (wn * 64 + cl * 4) * 4;
+    const int b_off1 = kStA + w_row1 * 1024 + (wn * 64 + cl * 4) * 4;
+    const int s_off = kAff ? kStA + kStB + wn * 256 + cl * 8 : kStA + kStB + (wn * 64 + cl * 4) * 2;
     const int z_off = kStA + kStB + kStS + (wn * 8 + (cl >> 1)) * 4;
 
     auto step = [&](int buf) {
@@ -165,31 +222,62 @@ w4a16_prefill_kernel(PrefillArgs p)
         }
         const uint4 w = *reinterpret_cast<const uint4 *>(st + b_off);
         const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+        uint32_t words1[4] = {0u, 0u, 0u, 0u};
+        if constexpr (kTwoWords) {
+            const uint4 w1 = *reinterpret_cast<const uint4 *>(st + b_off1);
+            words1[0] = w1.x;
+            words1[1] = w1.y;
+            words1[2] = w1.z;
+            words1[3] = w1.w;
+        }
         half8_t b[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (kAff)
+                b[j] = affine_codes<kBits>(words[j], words1[j], c_off, c_off4, mk);
+            else
+                b[j] = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const half8_t a = *reinterpret_cast<const half8_t *>(st + a_off[i]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+            if constexpr (kAff) acc_one[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, acc_one[i], 0, 0, 0);
         }
         if (++cpos == spg) {   // the group's end: scale its sums once (uniform)
             cpos = 0;
             const uint2 sv = *reinterpret_cast<const uint2 *>(st + s_off);
-            float sc[4];
-            sc[0] = half_bits_to_float(sv.x & 0xFFFFu);
-            sc[1] = half_bits_to_float(sv.x >> 16);
-            sc[2] = half_bits_to_float(sv.y & 0xFFFFu);
-            sc[3] = half_bits_to_float(sv.y >> 16);
+            float sc[4], bi[4];
+            if constexpr (kAff) {
+                const uint2 bv = *reinterpret_cast<const uint2 *>(st + s_off + 128);
+                sc[0] = bf16_bits_to_float(sv.x & 0xFFFFu);
+                sc[1] = bf16_bits_to_float(sv.x >> 16);
+                sc[2] = bf16_bits_to_float(sv.y & 0xFFFFu);
+                sc[3] = bf16_bits_to_float(sv.y >> 16);
+                bi[0] = bf16_bits_to_float(bv.x & 0xFFFFu);
+                bi[1] = bf16_bits_to_float(bv.x >> 16);
+                bi[2] = bf16_bits_to_float(bv.y & 0xFFFFu);
+                bi[3] = bf16_bits_to_float(bv.y >> 16);
+            } else {
+                sc[0] = half_bits_to_float(sv.x & 0xFFFFu);
+                sc[1] = half_bits_to_float(sv.x >> 16);
+                sc[2] = half_bits_to_float(sv.y & 0xFFFFu);
+                sc[3] = half_bits_to_float(sv.y >> 16);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) tot[i][j][r] = __builtin_fmaf(acc[i][j][r], sc[j], tot[i][j][r]);
+                    for (int r = 0; r < 4; ++r) {
+                        tot[i][j][r] = __builtin_fmaf(acc[i][j][r], sc[j], tot[i][j][r]);
+                        if constexpr (kAff) tot[i][j][r] = __builtin_fmaf(acc_one[i][r], bi[j], tot[i][j][r]);
+                    }
                     acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
                 }
+                if constexpr (kAff) acc_one[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
         }
     };
 
@@ -335,6 +423,17 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
     const bool sym = a.qzeros == nullptr;
     void (*kern)(PrefillArgs) = dual ? (sym ? w4a16_prefill_kernel<true, true> : w4a16_prefill_kernel<false, true>)
                                      : (sym ? w4a16_prefill_kernel<true, false> : w4a16_prefill_kernel<false, false>);
+    switch (a.bits) {   // affine codes (the host admits these widths only)
+    case 0: break;
+    case 1: kern = w4a16_prefill_kernel<true, false, 1>; break;
+    case 2: kern = w4a16_prefill_kernel<true, false, 2>; break;
+    case 3: kern = w4a16_prefill_kernel<true, false, 3>; break;
+    case 4: kern = w4a16_prefill_kernel<true, false, 4>; break;
+    case 5: kern = w4a16_prefill_kernel<true, false, 5>; break;
+    case 6: kern = w4a16_prefill_kernel<true, false, 6>; break;
+    case 8: kern = w4a16_prefill_kernel<true, false, 8>; break;
+    default: return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
