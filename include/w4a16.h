@@ -140,8 +140,10 @@ int w4a16_gemm_decode_ex(const void *A, const uint32_t *qweight, const uint16_t 
 
 /* The decode kernel's launch for a shape and explicit knobs (0 = default), checked exactly as
  * w4a16_gemm_decode_ex checks it, without any device work: W4A16_OK and, if plan_out is not NULL,
- * plan_out[0..5] = slices, tiles, kw, tile_cols, ring, LDS bytes per workgroup; or the status and
- * w4a16_last_error() that w4a16_gemm_decode_ex would return. packed_zeros: nonzero for packed zero
+ * plan_out[0..6] = slices, tiles, kw, tile_cols, ring, LDS bytes per workgroup, and the 32-row
+ * K-steps per ring slot (1; or 2 and 4 for 2- and 1-bit affine codes whose groups hold whole
+ * blocks of 64 and 128 rows, read a word per lane; slices and K pieces are then whole blocks);
+ * or the status and w4a16_last_error() that w4a16_gemm_decode_ex would return. packed_zeros: nonzero for packed zero
  * points (qzeros given); topk: 0, or the k of a fused pick; affine_bits: 0 for GPTQ codes, or the
  * width of the affine codes of w4a16_gemm_affine_bits_ex. Host only. */
 int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int slices, int tiles,

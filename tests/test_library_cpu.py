@@ -94,14 +94,22 @@ def test_explicit_launch_is_checked(lib):
 def test_plan_host_only(lib):
     import ctypes
     k, s, w, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    for M, N, K, g in ((1, 17408, 5120, 128), (16, 17408, 5120, 128), (5, 248320, 5120, 128),
-                       (1, 248320, 5120, 128), (16, 248320, 5120, 128), (9, 65536, 4096, 64),
-                       (1, 65528, 4096, 64), (1, 5120, 5120, 128), (16, 5120, 17408, 64), (1, 256, 512, 128),
-                       (16, 8, 64, 32)):
+    # (M, N, K, g, whether the decode kernel takes it): the widest matrices at every row count; from
+    # 16384 columns 9-16 rows when its launch of 4 tiles x 2 K pieces runs in one round (FFN 5120 x
+    # 17408: 3 slices, 204 workgroups; 8192 x 28672 has none and stays on the small-row kernel)
+    for M, N, K, g, dec in ((1, 17408, 5120, 128, False), (8, 17408, 5120, 128, False), (9, 17408, 5120, 128, True),
+                            (16, 17408, 5120, 128, True), (5, 248320, 5120, 128, True), (1, 248320, 5120, 128, True),
+                            (16, 248320, 5120, 128, True), (9, 65536, 4096, 64, True), (1, 65528, 4096, 64, False),
+                            (16, 32768, 5120, 128, True), (16, 28672, 8192, 128, False), (1, 5120, 5120, 128, False),
+                            (16, 5120, 17408, 64, False), (16, 5120, 5120, 128, False), (1, 256, 512, 128, False),
+                            (16, 8, 64, 32, False)):
         assert lib.w4a16_plan(M, N, K, g, ctypes.byref(k), ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)) == 0
-        assert (k.value >= 2) == (N >= 65536)   # the decode kernel takes the widest matrices
+        assert (k.value >= 2) == dec, (M, N, K)
         if k.value >= 2:
-            assert k.value == (2 if M == 1 else 3) and 1 <= s.value <= 16 and w.value == 1
+            assert k.value == (2 if M == 1 else 3) and 1 <= s.value <= 16
+            assert w.value == (2 if 8 < M and N < 65536 else 1)
+            if N < 65536:   # one round of at least 192 workgroups of 4 x 64 columns
+                assert s.value * -(-N // 256) >= 192 and c.value == 64
         else:
             assert k.value == (0 if M == 1 and c.value == 64 else 1)   # one row on 128 columns: matrix cores
             assert s.value >= 1 and w.value in (1, 2, 4, 8, 16) and s.value * w.value <= K // 32

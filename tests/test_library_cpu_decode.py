@@ -50,7 +50,7 @@ def test_decode_launch_is_checked(lib, kw, msg):
 
 def test_default_plans_are_accepted(lib):
     """The default launch of every workload shape and row count is one the kernel takes."""
-    out = (ctypes.c_int * 6)()
+    out = (ctypes.c_int * 7)()
     for K, N, g, packed in ((512, 256, 128, 0), (5120, 5120, 128, 0), (5120, 17408, 128, 0), (17408, 5120, 64, 1),
                             (5120, 248320, 128, 0)):
         for M in range(1, 17):
@@ -63,7 +63,7 @@ def test_default_plans_are_accepted(lib):
 def test_fused_pick_reserves_lds_for_the_outputs(lib):
     """A fused pick stages the group's finished outputs, M x (tiles x tile_cols) fp32, over the
     activation fragments: a slice too short to hold them gets the room anyway."""
-    out = (ctypes.c_int * 6)()
+    out = (ctypes.c_int * 7)()
     assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 0, 0, out) == 0
     plain = out[5]
     assert lib.w4a16_decode_plan(1, 256, 64, 32, 0, 1, 4, 1, 64, 2, 1, 0, out) == 0
@@ -87,7 +87,7 @@ def test_affine_bits_plans(lib):
     """Affine codes read at their own width: every width the kernel takes, at the affine
     workloads' shapes and every row count, has a default launch that fits; its scales and biases
     both sit in LDS (more than the GPTQ launch of the same shape)."""
-    out = (ctypes.c_int * 6)()
+    out = (ctypes.c_int * 7)()
     for K, N, g in ((5120, 17408, 64), (512, 256, 64), (1024, 520, 32), (5120, 248320, 64)):
         for bits in (1, 2, 3, 4, 5, 6, 8):
             for M in (1, 2, 5, 9, 16):
@@ -129,3 +129,22 @@ def test_affine_bits_prefill_checks_its_arguments(lib):
     assert b"M=65537" in lib.w4a16_last_error()
     assert f(A, A, 8, A, A, 64, 300, 260, 512, O, 0, None) == -1       # N % 8
     assert f(A, A, 8, A, A, 64, 300, 256, 512, O, 2, None) == -1       # out_dtype
+
+
+def test_affine_word_per_lane_blocks(lib):
+    """1- and 2-bit codes read a word per lane over blocks of 4 and 2 steps when the quantisation
+    groups hold whole blocks; otherwise (and for every other width) one step per ring slot. A
+    block is never split: slices and K pieces are whole blocks."""
+    import verify_matmul_amd as vm
+    for bits, g, sub in ((2, 64, 2), (2, 128, 2), (2, 32, 1), (1, 128, 4), (1, 256, 4), (1, 64, 1), (1, 32, 1),
+                         (3, 128, 1), (4, 128, 1), (8, 64, 1)):
+        assert vm.w4a16_decode_plan(4, 512, 1024, g, affine_bits=bits)["sub"] == sub, (bits, g)
+    assert vm.w4a16_decode_plan(4, 512, 1024, 128, packed_zeros=True)["sub"] == 1   # GPTQ codes
+    # K = 512: 16 steps = 8 blocks of 2-bit codes or 4 of 1-bit codes
+    assert vm.w4a16_decode_plan(4, 512, 512, 64, slices=8, affine_bits=2)["slices"] == 8
+    with pytest.raises(vm.W4A16Error):
+        vm.w4a16_decode_plan(4, 512, 512, 64, slices=9, affine_bits=2)
+    with pytest.raises(vm.W4A16Error):
+        vm.w4a16_decode_plan(4, 512, 512, 128, slices=5, affine_bits=1)
+    with pytest.raises(vm.W4A16Error):
+        vm.w4a16_decode_plan(4, 512, 512, 128, slices=2, kw=4, affine_bits=1)

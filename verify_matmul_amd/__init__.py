@@ -177,12 +177,13 @@ def w4a16_gemm_decode_ex(A, qweight, scales, qzeros, group_size, out, slices=0, 
 def w4a16_decode_plan(M, N, K, group_size, packed_zeros=False, slices=0, tiles=0, kw=0, tile_cols=0, ring=0, topk=0,
                       affine_bits=0):
     """The decode kernel's launch for a shape (host only, no device work): a dict of slices, tiles,
-    kw, tile_cols, ring and lds bytes, or W4A16Error with the status w4a16_gemm_decode_ex would return."""
-    out = (ctypes.c_int * 6)()
+    kw, tile_cols, ring, lds bytes and sub (32-row steps per ring slot), or W4A16Error with the status
+    w4a16_gemm_decode_ex would return."""
+    out = (ctypes.c_int * 7)()
     _check(load().w4a16_decode_plan(int(M), int(N), int(K), int(group_size), int(bool(packed_zeros)), int(slices),
                                     int(tiles), int(kw), int(tile_cols), int(ring), int(topk), int(affine_bits), out),
            "w4a16_decode_plan")
-    return dict(zip(("slices", "tiles", "kw", "tile_cols", "ring", "lds"), list(out)))
+    return dict(zip(("slices", "tiles", "kw", "tile_cols", "ring", "lds", "sub"), list(out)))
 
 
 def w4a16_gemm_noalloc(A, qweight, scales, qzeros, group_size, out, stream=None):

@@ -253,24 +253,50 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
 int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int tiles, int kw, int tile_cols, int ring,
                      bool pick, DecodePlan *pl, int bits = 0)
 {
-    const int steps = K / kStepK;
     const bool affine = bits > 0;
     if (tile_cols != 0 && tile_cols != 64 && tile_cols != 128)
         return fail(W4A16_ERR_INVALID_ARG, "tile_cols=%d is not 0, 64 or 128", tile_cols);
     if (affine && tile_cols == 128)
         return fail(W4A16_ERR_INVALID_ARG, "affine codes run on 64-column tiles (tile_cols=%d)", tile_cols);
+    // 1- and 2-bit codes: a word per lane, blocks of 4 / bits steps, where the quantisation groups
+    // hold whole blocks (otherwise the 8-row reader, 2 or 4 lanes per word)
+    pl->sub = affine && bits <= 2 && g % (kStepK * 4 / bits) == 0 ? 4 / bits : 1;
+    const int steps = K / kStepK / pl->sub;   // in blocks: slices and pieces take whole ones
     pl->mfma = M > 1;
     pl->cols = tile_cols ? tile_cols / 16 : 4;
+    pl->one_round = false;
+    // GPTQ codes, 9-16 rows, fewer than kDecodeMinN columns: 4 tiles x 2 K pieces per workgroup, a
+    // ring of 4, and the fewest K slices that give at least kDecodeMidWgs workgroups which all run
+    // at once (measured on MI355X, back to back, at 16 rows: FFN 5120 x 17408 3 slices 20.5-20.7
+    // us against 21.8-23.4 for the small-row kernel, 8 tiles x 1 piece 23.1-23.4, ring 8 21.6;
+    // 5120 x 32768 2 slices 25.5 against 29.6; 8192 x 28672 with 3 slices, one and a third rounds
+    // of workgroups, 48.4 against 41.9)
+    const bool mid = !affine && M > 8 && N < kDecodeMinN;
     // more rows stage more activations per workgroup, which leaves room for fewer workgroups per
     // CU: give each workgroup more waves
     // (affine codes below kDecodeMinN columns: 4 tiles at every row count, measured on the
     // 5120 x 17408 projection at 2, 4 and 8 bits, where 8 tiles with more K slices lost 10-30%)
-    pl->tiles = tiles ? tiles : (pl->mfma && (!affine || N >= kDecodeMinN) ? 8 : 4);
-    pl->kw = kw ? kw : 1;
+    pl->tiles = tiles ? tiles : (pl->mfma && (!affine || N >= kDecodeMinN) && !mid ? 8 : 4);
+    pl->kw = kw ? kw : mid ? 2 : 1;
     if (pl->tiles < 1 || pl->kw < 1 || pl->tiles * pl->kw > kDecMaxWaves)
         return fail(W4A16_ERR_INVALID_ARG, "tiles=%d x kw=%d waves outside 1..%d", pl->tiles, pl->kw, kDecMaxWaves);
     const long long wc = (long long)pl->tiles * 16 * pl->cols;
     const int groups = (int)((N + wc - 1) / wc);
+    if (slices == 0 && mid) {
+        // workgroups per CU: by waves (3 with the 77 registers of the ring-4 instance) and by LDS
+        const int by_waves = 3 * 8 / (pl->tiles * pl->kw);
+        for (int s = std::max(1, (kDecodeMidWgs + groups - 1) / groups);
+             s <= std::min(kDecMaxSlices, steps / pl->kw); ++s) {
+            const size_t lds =
+                decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, s, packed, pick, nullptr, false);
+            const long long per_cu = std::min<long long>(by_waves, (long long)(kLdsPerCu / lds));
+            if (lds <= (size_t)kMaxLds && (long long)groups * s <= (long long)kCus * per_cu) {
+                slices = s;
+                pl->one_round = true;
+                break;
+            }
+        }
+    }
     if (slices == 0) {
         // about 512 workgroups (affine codes: 400, which measured 8-10% faster than 512)
         const int target = affine ? 400 : 512;
@@ -282,29 +308,29 @@ int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int ti
         // too few waves)
         const size_t lds_cap = M > 8 || (affine && M > 1) ? (size_t)kMaxLds / 2 : (size_t)kMaxLds;
         while (slices < std::min(kDecMaxSlices, steps / pl->kw) &&
-               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, nullptr, affine) >
-                   lds_cap)
+               decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, nullptr, affine,
+                                 pl->sub) > lds_cap)
             ++slices;
     }
     if (slices < 1 || slices > kDecMaxSlices || (long long)slices * pl->kw > steps)
-        return fail(W4A16_ERR_INVALID_ARG, "slices=%d outside 1..%d, or slices x kw=%d above the %d K-steps of 32",
-                    slices, kDecMaxSlices, pl->kw, steps);
+        return fail(W4A16_ERR_INVALID_ARG, "slices=%d outside 1..%d, or slices x kw=%d above the %d K-%s",
+                    slices, kDecMaxSlices, pl->kw, steps, pl->sub > 1 ? "blocks" : "steps of 32");
     pl->slices = slices;
     // the kernel addresses a slice's codes (plus the ring's reads past its end) with 32-bit byte
     // offsets
-    const long long smax = (steps + slices - 1) / slices;
+    const long long smax = (long long)(steps + slices - 1) / slices * pl->sub;
     const long long step_bytes = 4LL * (affine ? bits : 4) * N;   // a step's codes over all columns
-    if ((smax + 8) * step_bytes >= (1LL << 31))
+    if ((smax + 8LL * pl->sub) * step_bytes >= (1LL << 31))
         return fail(W4A16_ERR_UNSUPPORTED, "a K slice of %lld steps over %d columns exceeds 2 GiB of codes: use more slices",
                     smax, N);
-    pl->ring = ring ? ring : affine ? 4 : (pl->cols == 8 ? 2 : M == 1 ? 3 : M <= 8 ? 4 : 8);
+    pl->ring = ring ? ring : affine || mid ? 4 : (pl->cols == 8 ? 2 : M == 1 ? 3 : M <= 8 ? 4 : 8);
     const bool ring_ok = affine ? pl->ring == 4
                          : pl->cols == 8 ? (pl->ring == 2 || pl->ring == 4)
                                          : (pl->ring == 2 || pl->ring == 3 || pl->ring == 4 || pl->ring == 6 || pl->ring == 8);
     if (!ring_ok)
         return fail(W4A16_ERR_INVALID_ARG, "ring=%d is not available for %s", pl->ring,
                     affine ? "affine codes (4)" : pl->cols == 8 ? "128-column tiles" : "64-column tiles");
-    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, pl, affine);
+    pl->lds = decode_lds_layout(M, K, g, pl->mfma, pl->cols, pl->tiles, pl->kw, slices, packed, pick, pl, affine, pl->sub);
     if (pl->lds > (size_t)kMaxLds)
         return fail(W4A16_ERR_INVALID_ARG, "decode plan needs %zu bytes of LDS per workgroup (max %d): use more slices",
                     pl->lds, kMaxLds);
@@ -355,14 +381,17 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
 // Whether a plain GPTQ call takes the decode kernel by default: for matrices of at least
 // kDecodeMinN columns, wide enough to fill the chip with whole-K (or few-slice) workgroups, such
 // as the 248320-column output layer (MI355X, back-to-back launches: 101 against 115 us at one row,
-// 111 against 124 at five, 137 against 163 at sixteen). Narrower matrices need K slices, whose
-// exchange costs the decode kernel more than the small-row kernel's split-K (FFN 5120 x 17408:
-// 17 against 14 us at one row, 24 against 22 at sixteen).
+// 111 against 124 at five, 137 against 163 at sixteen); and for 9-16 rows on matrices of
+// kDecodeMidN columns or more when its launch for them runs in one round (see make_decode_plan).
+// Narrower matrices, and fewer rows, need more K slices, whose exchange costs the decode kernel
+// more than the small-row kernel's split-K (FFN 5120 x 17408: 17 against 14 us at one row, 18.0
+// against 16.7 at eight; attention 5120 x 5120 at sixteen: 17.2 against 13.6).
 bool decode_by_default(int M, int N, int K, int g, bool packed, bool pick)
 {
-    if (N < kDecodeMinN) return false;
+    if (N < kDecodeMidN || (N < kDecodeMinN && M <= 8)) return false;
     DecodePlan pl{};
-    return make_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, pick, &pl) == W4A16_OK;
+    if (make_decode_plan(M, N, K, g, packed, 0, 0, 0, 0, 0, pick, &pl) != W4A16_OK) return false;
+    return N >= kDecodeMinN || pl.one_round;
 }
 
 int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, int N, int K, void *out,
@@ -889,6 +918,7 @@ int w4a16_decode_plan(int M, int N, int K, int group_size, int packed_zeros, int
         plan_out[2] = plan.kw;
         plan_out[3] = 16 * plan.cols;
         plan_out[4] = plan.ring;
+        plan_out[6] = plan.sub;
         plan_out[5] = (int)plan.lds;
     }
     return W4A16_OK;

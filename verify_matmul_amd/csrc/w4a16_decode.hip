@@ -70,12 +70,19 @@ __device__ __forceinline__ int frag_pos(int m, int wr, int mp_log2)
 // kBits bits per row, so a step's 32 rows are kBits word rows, and a lane's 8 rows are 8 * kBits
 // bits that start at bit 8 * kBits * (lane's K quarter) of the step: in one word row for 1, 2 and
 // 4 bits (kLd = 1), in two consecutive ones otherwise (kLd = 2; 3, 5, 6 and 8 bits).
-template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4>
+// kSub: 32-row steps per ring slot. 1, or for 1- and 2-bit affine codes 4 / kBits: then lane q
+// loads word q of a block of kSub steps (each lane a word of its own, where at kSub = 1 two or
+// four lanes would load the same word for 8 rows each) and holds rows 32 q / kBits onwards, i.e.
+// 8-row chunks kSub * q .. kSub * q + kSub - 1 of the block; the block takes kSub matrix-core
+// products (or dot-product rounds) per column, product h pairing each lane's chunk kSub * q + h
+// of the codes with the same chunk of the activations. Slices and pieces are whole blocks.
+template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4, int kSub = 1>
 __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 {
     constexpr bool kAff = kZM == kAffine;
     static_assert(!kAff || kLd == ((kBits == 1 || kBits == 2 || kBits == 4) ? 1 : 2), "word rows per lane and step");
     static_assert(!kAff || kV == 1, "affine codes run on 64-column tiles");
+    static_assert(kSub == 1 || (kAff && kSub * kBits == 4), "blocks of steps: 1- and 2-bit affine codes");
     constexpr int kC = 4 * kV;      // adjacent columns per lane
     constexpr int kTile = 16 * kC;  // columns per wave
     constexpr int kRows = kMfma ? 4 : 1;
@@ -97,10 +104,12 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     const int cg = blockIdx.x / P;              // group of columns
     const int sl = blockIdx.x - cg * P;         // K slice
     const int steps = K / kStepK;
-    const int sb = (int)((long long)sl * steps / P);
-    const int se = (int)((long long)(sl + 1) * steps / P);   // se > sb (host: slices <= steps)
-    const int wb = sb + (int)((long long)w_k * (se - sb) / p.kw);           // the wave's piece [wb, we)
-    const int we = sb + (int)((long long)(w_k + 1) * (se - sb) / p.kw);     // (host: slices * kw <= steps)
+    const int units = steps / kSub;   // blocks of kSub steps (host: K % (32 kSub) == 0)
+    const int sb = kSub * (int)((long long)sl * units / P);
+    const int se = kSub * (int)((long long)(sl + 1) * units / P);   // se > sb (host: slices <= units)
+    const int su = (se - sb) / kSub;
+    const int wb = sb + kSub * (int)((long long)w_k * su / p.kw);          // the wave's piece [wb, we)
+    const int we = sb + kSub * (int)((long long)(w_k + 1) * su / p.kw);    // (host: slices * kw <= units)
     const int g0 = sb / spg;
     const int ng = (se - 1) / spg - g0 + 1;
     const int WC = p.tiles * kTile;             // columns of the workgroup
@@ -199,8 +208,9 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     constexpr int R = kAff ? kBits : 4;   // word rows per step
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.qweight + (size_t)sb * R * N, (uint32_t)((se - sb) * R * 4 * N));
     // affine codes: the lane's 8 rows start at bit `a_bit` of the step, in word row a_bit / 32
-    const int a_bit = kAff ? 8 * kBits * rl : 0;
-    const uint32_t w_lane = ((uint32_t)(kAff ? a_bit >> 5 : rl) * (uint32_t)N + (uint32_t)nc) * 4u;   // bytes (< 2 GiB)
+    // (blocks of kSub > 1 steps: word row rl of the block)
+    const int a_bit = kAff && kSub == 1 ? 8 * kBits * rl : 0;
+    const uint32_t w_lane = ((uint32_t)(kAff && kSub == 1 ? a_bit >> 5 : rl) * (uint32_t)N + (uint32_t)nc) * 4u;   // bytes (< 2 GiB)
     uint4 ring[kU][kLd];
     auto load_w = [&](uint4 *dst, int t) {
 #pragma unroll
@@ -216,7 +226,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     // prologue issued the slots in the same order)
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-        load_w(ring[u], wb + u);
+        load_w(ring[u], wb + u * kSub);
         asm volatile("" ::: "memory");
     }
 
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     const int sx = mp_log2 - 2;   // the step's swizzle: (t mod 4) << sx
 
     auto step = [&](int t, const uint4 *wv) {
-        const bool last = gpos == spg - 1 || t + 1 == we;
+        const bool last = gpos + kSub == spg || t + kSub == we;   // (host: spg % kSub == 0)
         const int tt = t - sb;
         const half8_t a = __builtin_bit_cast(half8_t, kMfma ? a_lds[((tt * 4) << mp_log2) + (lx ^ ((tt & 3) << sx))]
                                                             : a_lds[tt * 4 + rl]);
@@ -323,35 +333,39 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
             words1[2] = wv[1].z;
             words1[3] = wv[1].w;
         }
-        if constexpr (kAff) {   // the activations' own sums, for the bias
+        auto mac = [&](const half8_t &x, const half8_t &b, float4_t &c) {
             if constexpr (kMfma) {
-                acc_one = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, acc_one, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(x, b, c, 0, 0, 0);
             } else {
-                float s = acc_one[0];
-                s = __builtin_amdgcn_fdot2(ones.lo.lo, a.lo.lo, s, false);
-                s = __builtin_amdgcn_fdot2(ones.lo.hi, a.lo.hi, s, false);
-                s = __builtin_amdgcn_fdot2(ones.hi.lo, a.hi.lo, s, false);
-                s = __builtin_amdgcn_fdot2(ones.hi.hi, a.hi.hi, s, false);
-                acc_one[0] = s;
+                float s = c[0];
+                s = __builtin_amdgcn_fdot2(b.lo.lo, x.lo.lo, s, false);
+                s = __builtin_amdgcn_fdot2(b.lo.hi, x.lo.hi, s, false);
+                s = __builtin_amdgcn_fdot2(b.hi.lo, x.hi.lo, s, false);
+                s = __builtin_amdgcn_fdot2(b.hi.hi, x.hi.hi, s, false);
+                c[0] = s;
             }
-        }
+        };
+        if constexpr (kSub > 1) {   // a block of kSub steps: one product per 8-row chunk of the lane's word
 #pragma unroll
-        for (int j = 0; j < kC; ++j) {
-            half8_t b;
-            if constexpr (kAff) {
-                b = affine_codes<kBits>(words[j], kLd == 2 ? words1[j] : 0u, a_off, a_off4, mk);
-            } else {
-                b = dequant_word(words[j], kZM == kZeroSym ? zero_sub_sym() : zs[j], mk);
+            for (int h = 0; h < kSub; ++h) {
+                const int wr = tt * 4 + kSub * rl + h;   // the chunk's word row of the slice
+                const half8_t x = __builtin_bit_cast(half8_t, kMfma ? a_lds[frag_pos(cl & (mp - 1), wr, mp_log2)] : a_lds[wr]);
+                mac(x, ones, acc_one);   // the activations' own sums, for the bias
+#pragma unroll
+                for (int j = 0; j < kC; ++j)
+                    mac(x, affine_codes<kBits>(words[j], 0u, 8 * kBits * h, 8 * kBits * h + 4 * kBits, mk), acc[j]);
             }
-            if constexpr (kMfma) {
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
-            } else {
-                float s = acc[j][0];
-                s = __builtin_amdgcn_fdot2(b.lo.lo, a.lo.lo, s, false);
-                s = __builtin_amdgcn_fdot2(b.lo.hi, a.lo.hi, s, false);
-                s = __builtin_amdgcn_fdot2(b.hi.lo, a.hi.lo, s, false);
-                s = __builtin_amdgcn_fdot2(b.hi.hi, a.hi.hi, s, false);
-                acc[j][0] = s;
+        } else {
+            if constexpr (kAff) mac(a, ones, acc_one);   // the activations' own sums, for the bias
+#pragma unroll
+            for (int j = 0; j < kC; ++j) {
+                half8_t b;
+                if constexpr (kAff) {
+                    b = affine_codes<kBits>(words[j], kLd == 2 ? words1[j] : 0u, a_off, a_off4, mk);
+                } else {
+                    b = dequant_word(words[j], kZM == kZeroSym ? zero_sub_sym() : zs[j], mk);
+                }
+                mac(a, b, acc[j]);
             }
         }
         if (last) {   // the group's scale, once, on fp32 sums
@@ -396,7 +410,8 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
             if constexpr (kAff) acc_one = float4_t{0.f, 0.f, 0.f, 0.f};
         }
         first = last;
-        if (++gpos == spg) {
+        gpos += kSub;
+        if (gpos == spg) {
             gpos = 0;
             ++gi;
         }
@@ -404,18 +419,18 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 
     // Whole rounds of the ring: every step computes and reissues its slot unconditionally, so the
     // wait before a step covers only that slot.
-    const int full_end = wb + (we - wb) / kU * kU;
+    const int full_end = wb + (we - wb) / (kU * kSub) * (kU * kSub);
     int t0 = wb;
-    for (; t0 < full_end; t0 += kU) {
+    for (; t0 < full_end; t0 += kU * kSub) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            step(t0 + u, ring[u]);
-            load_w(ring[u], t0 + u + kU);   // past the slice: no memory request
+            step(t0 + u * kSub, ring[u]);
+            load_w(ring[u], t0 + (u + kU) * kSub);   // past the slice: no memory request
         }
     }
 #pragma unroll
     for (int u = 0; u + 1 < kU; ++u)
-        if (t0 + u < we) step(t0 + u, ring[u]);
+        if (t0 + u * kSub < we) step(t0 + u * kSub, ring[u]);
 
     // ---- 6. the K pieces of each tile, added in LDS in piece order ------------------------------
     if (p.kw > 1) {
@@ -712,10 +727,10 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4>
+template <bool kMfma, int kZM, int kU, int kV, int kLd = kV, int kBits = 4, int kSub = 1>
 hipError_t launch_one(const DecodeArgs &a, const DecodePlan &plan, hipStream_t stream)
 {
-    const auto kern = decode_kernel<kMfma, kZM, kU, kV, kLd, kBits>;
+    const auto kern = decode_kernel<kMfma, kZM, kU, kV, kLd, kBits, kSub>;
     if (plan.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
@@ -751,8 +766,10 @@ hipError_t launch_affine(const DecodeArgs &a, const DecodePlan &plan, hipStream_
 {
     if (plan.ring != 4) return hipErrorInvalidValue;
     switch (a.bits) {
-    case 1: return launch_one<kMfma, kAffine, 4, 1, 1, 1>(a, plan, stream);
-    case 2: return launch_one<kMfma, kAffine, 4, 1, 1, 2>(a, plan, stream);
+    case 1: return plan.sub == 4 ? launch_one<kMfma, kAffine, 4, 1, 1, 1, 4>(a, plan, stream)
+                                 : launch_one<kMfma, kAffine, 4, 1, 1, 1>(a, plan, stream);
+    case 2: return plan.sub == 2 ? launch_one<kMfma, kAffine, 4, 1, 1, 2, 2>(a, plan, stream)
+                                 : launch_one<kMfma, kAffine, 4, 1, 1, 2>(a, plan, stream);
     case 3: return launch_one<kMfma, kAffine, 4, 1, 2, 3>(a, plan, stream);
     case 4: return launch_one<kMfma, kAffine, 4, 1, 1, 4>(a, plan, stream);
     case 5: return launch_one<kMfma, kAffine, 4, 1, 2, 5>(a, plan, stream);

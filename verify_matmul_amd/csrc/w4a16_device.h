@@ -234,12 +234,29 @@ __device__ __forceinline__ half8_t affine_codes(uint32_t w0, uint32_t w1, int a_
             const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + r) << 16) | (uint32_t)r;   // (w0 byte r, 0, w1 byte r, 0)
             pr[r] = as_half2(__builtin_amdgcn_perm(w1, w0, sel) | 0x64006400u) + sub;
         }
-    } else if constexpr (kBits == 2) {   // 16 bits from a_off: bytes (k0..k3), (k4..k7)
-        const uint32_t x = w0 >> (uint32_t)a_off;
-        const uint32_t y = __builtin_amdgcn_perm(0u, x, 0x0C010C00u);   // k0..k3 in the low half, k4..k7 in the high
+    } else if constexpr (kBits == 2) {
+        // The 16 bits from a_off (0 or 16) are bytes (k0..k3) and (k4..k7): one byte permute puts
+        // them in the two halves. Code r of each byte sits at bit 2r; read in place as the mantissa
+        // of an fp16 whose unit is that bit (exponent 2^(10 - 2r)), it is 2^(10 - 2r) + q, so each
+        // pair takes one and-or and one packed subtract, with no shift.
+        const uint32_t y = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u + 0x00020002u * ((uint32_t)a_off >> 4));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = as_half2(((y >> (2 * r)) & 0x00030003u) | 0x64006400u) + sub;
-    } else {   // 1, 3, 5 and 6 bits: two 32-bit windows of (w1:w0)
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t magic = (uint32_t)(25 - 2 * r) << 10;   // fp16 2^(10 - 2r)
+            pr[r] = as_half2((y & (0x00030003u << (2 * r))) | (magic * 0x10001u)) - as_half2(magic * 0x10001u);
+        }
+    } else if constexpr (kBits == 1) {
+        // The byte at a_off (a multiple of 8) holds k0..k7 at bits 0..7; permuted into both halves,
+        // pair r takes bit r of the low half and bit r + 4 of the high one, each read in place as
+        // the mantissa of an fp16 whose unit is that bit.
+        const uint32_t bsel = (uint32_t)a_off >> 3;
+        const uint32_t y = __builtin_amdgcn_perm(0u, w0, 0x0C000C00u | (bsel << 16) | bsel);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t magic = ((uint32_t)(25 - r) << 10) | ((uint32_t)(21 - r) << 26);   // 2^(10 - r), 2^(6 - r)
+            pr[r] = as_half2((y & ((1u << r) | (1u << (20 + r)))) | magic) - as_half2(magic);
+        }
+    } else {   // 3, 5 and 6 bits: two 32-bit windows of (w1:w0)
         const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)a_off);
         const uint32_t hi = a_off4 >= 32 ? w1 >> (uint32_t)(a_off4 - 32) : __builtin_amdgcn_alignbit(w1, w0, (uint32_t)a_off4);
         constexpr uint32_t kMask2 = ((1u << kBits) - 1u) * 0x10001u;   // a code in both halves

@@ -173,6 +173,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // meet through scratch (counters and flags as in the small-row kernel).
 constexpr int kDecMaxWaves = 8;
 constexpr int kDecodeMinN = 65536;   // plain calls this wide take the decode kernel by default
+constexpr int kDecodeMidN = 16384;   // and from this width, plain calls of more than 8 rows
+constexpr int kDecodeMidWgs = 192;   // their workgroups: at least this many, in one round
+constexpr int kCus = 256;            // compute units of an MI355X (the planner is host-only)
 constexpr int kDecMaxSlices = 16;
 constexpr int kDecMaxTopK = 8;       // largest k of the fused pick
 // Activation items (8 bf16 values) each thread of a decode workgroup keeps in registers between
@@ -211,7 +214,9 @@ struct DecodePlan {
     int tiles;
     int kw;
     int slices;
-    int ring;                 // steps of packed weights in flight per wave (template instance)
+    int ring;                 // ring slots of packed weights in flight per wave (template instance)
+    int sub;                  // 32-row steps per ring slot: 1, or 4 / bits for 1- and 2-bit affine codes
+    bool one_round;           // the default launch of 9-16 rows below kDecodeMinN columns found its slices
     size_t lds;
     int a_off, s_off, z_off, r_off;
 };
@@ -221,10 +226,10 @@ inline int decode_mp_log2(int M) { return M <= 4 ? 2 : M <= 8 ? 3 : 4; }
 // per row of the padded rows per step; GEMV: 64 bytes per step), the workgroup's scales and zero
 // words of its groups, and the K pieces' sums (kw - 1 pieces of every tile).
 inline size_t decode_lds_layout(int M, int K, int g, bool mfma, int cols, int tiles, int kw, int slices, bool packed,
-                                bool pick, DecodePlan *pl, bool affine = false)
+                                bool pick, DecodePlan *pl, bool affine = false, int sub = 1)
 {
-    const int steps = K / kStepK;
-    const int smax = (steps + slices - 1) / slices;
+    const int units = K / kStepK / sub;   // slices are whole blocks of `sub` steps
+    const int smax = (units + slices - 1) / slices * sub;
     const int spg = g / kStepK;
     const size_t groups = (size_t)(smax + spg - 1) / spg + 1;
     const size_t wc = (size_t)tiles * 16 * cols;
