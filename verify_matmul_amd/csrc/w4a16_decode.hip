@@ -240,8 +240,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
         auto fold = [&](uint4 x) {   // one item of row i_m; the row's last folds the row maximum in
             run = max(run, max_mag8(x));
             if (++c == chunks) {
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) run = max(run, (uint32_t)__shfl_xor((int)run, o));
+                run = wave_max_u32(run);
                 if (lane == 0 && run) atomicMax(&rowmax[i_m], run);
                 run = 0;
                 c = 0;
@@ -683,34 +682,44 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     }
     __syncthreads();   // every flag seen raised: the other slices' stores have completed
     const bool failed = s_failed != 0;
-    constexpr int kBatch = 8;
+    // Each output adds the slices in slice order. The loads of a batch of slices for all of the
+    // lane's rows are in flight together (one round trip per batch, not one per row: a slice
+    // read from another die's stores takes about half a microsecond to arrive).
+    constexpr int kOut = kRows * kV;                      // float4 outputs per lane
+    constexpr int kBatch = kOut >= 8 ? 1 : 8 / kOut;      // slices per batch: at most 8 loads in flight
     if (holder) {
+        f32x4 sum[kOut];
+#pragma unroll
+        for (int o = 0; o < kOut; ++o) sum[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < P; b += kBatch) {   // slices in order
+            f32x4 x[kBatch][kOut];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+                for (int o = 0; o < kOut; ++o) {
+                    const int r = o / kV, v = o - (o / kV) * kV;
+                    const int sp = b + i, m = row_base + r;
+                    x[i][o] = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
+                    if (sp < P && sp != sl && m < M) {
+                        const uint32_t off = (uint32_t)((((size_t)sp * M + m) * N + n0 + 4 * v) * sizeof(float));
+                        x[i][o] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kCoherent);
+                    }
+                }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+                for (int o = 0; o < kOut; ++o)
+                    if (b + i < P) sum[o] += x[i][o];
+        }
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
             const int m = row_base + r;
             if (m >= M) continue;
 #pragma unroll
             for (int v = 0; v < kV; ++v) {
-                const f32x4 own = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
-                f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int b = 0; b < kDecMaxSlices; b += kBatch) {   // slices in order, kBatch loads in flight
-                    if (b >= P) break;
-                    f32x4 x[kBatch];
-#pragma unroll
-                    for (int i = 0; i < kBatch; ++i) {
-                        const int sp = b + i;
-                        x[i] = own;
-                        if (sp < P && sp != sl) {
-                            const uint32_t off = (uint32_t)((((size_t)sp * M + m) * N + n0 + 4 * v) * sizeof(float));
-                            x[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kCoherent);
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < kBatch; ++i)
-                        if (b + i < P) sum += x[i];
-                }
-                if (failed) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+                f32x4 sm = sum[r * kV + v];
+                if (failed) sm = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+                const f32x4 sum = sm;
                 store_out(m, v, sum.x, sum.y, sum.z, sum.w);
                 if (KP > 0) {   // every wave is past the main loop (the flag wait ended in a barrier)
                     stage(r, 4 * v, sum.x);

@@ -205,6 +205,20 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t n)
     return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - n);
 }
 
+// The largest of v over the wave's 64 lanes, in every lane: rotations within each row of 16
+// lanes (DPP row_ror 8, 4, 2, 1; VALU operands, no LDS round trip as a lane shuffle takes), then
+// the four rows' results read as scalars. Every lane must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
     const uint32_t lo = __shfl_xor((uint32_t)v, m);
