@@ -141,6 +141,21 @@ def cpu_one_thread(workload, ms, seconds):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
+def host_cpu():
+    """This host's processor model and logical CPU count, recorded beside the oracle's timing."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def cpu_baseline(wl, inp, ms, seconds, gate=None, one=None):
     """The CPU oracle, as it is, on this host's cores: the whole step repeated for ~`seconds`."""
     import oracle
@@ -160,7 +175,8 @@ def cpu_baseline(wl, inp, ms, seconds, gate=None, one=None):
         reps += 1
     rec = {"value": round(nbytes / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
            "sample": f"{reps} full step(s) of the workload (M={','.join(map(str, ms))}, all {wl.N} columns), "
-                     f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)"}
+                     f"{elapsed:.1f} s of oracle time (unpack + exact dequant + fp64 accumulate)",
+           "host": host_cpu()}
     if one is not None:   # the same steps on one thread (measured before any GPU work)
         step_b = sum(algorithmic_bytes(M, wl.K, wl.N, wl.group, wl.symmetric) for M in ms)
         v1 = step_b * one["calls"] / one["seconds"] / 1e9
