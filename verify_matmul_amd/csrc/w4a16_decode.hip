@@ -57,7 +57,9 @@ constexpr int kHeld = kDecHeld;
 // quarter reading a step read mp consecutive fragments.
 __device__ __forceinline__ int frag_swz(int t, int q, int mp_log2)
 {
-    return mp_log2 == 4 ? (((t & 3) << 2) | q) : mp_log2 == 3 ? (((t & 3) << 1) | (q >> 1)) : (t & 3);
+    // mp = 16: ((t & 3) << 2) | q; mp = 8: ((t & 3) << 1) | (q >> 1); mp = 4: t & 3 (q < 4), in one
+    // form without branches (mp_log2 is uniform)
+    return ((t & 3) << (mp_log2 - 2)) | (q >> (4 - mp_log2));
 }
 __device__ __forceinline__ int frag_pos(int m, int wr, int mp_log2)
 {
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     // row, and output rows past M are never stored.
     const int mp = 1 << mp_log2;
     const int q_l = lane >> 4;
-    const int lx = (q_l << mp_log2) + ((cl & (mp - 1)) ^ (mp_log2 == 4 ? q_l : mp_log2 == 3 ? q_l >> 1 : 0));
+    const int lx = (q_l << mp_log2) + ((cl & (mp - 1)) ^ (q_l >> (4 - mp_log2)));
     const int sx = mp_log2 - 2;   // the step's swizzle: (t mod 4) << sx
 
     auto step = [&](int t, const uint4 *wv) {
