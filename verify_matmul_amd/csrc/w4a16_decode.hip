@@ -204,11 +204,12 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     asm volatile("" ::: "memory");
 
     // ---- 3. the weight ring ----------------------------------------------------------------
-    // A buffer resource over exactly the slice's word rows: the ring reloads steps past the
-    // wave's piece unconditionally (no branch in the loop); reads past the slice return zero
-    // without a memory request. Non-temporal: every byte is read once per call.
+    // A buffer resource over exactly the word rows of the wave's piece: the ring reloads steps
+    // past the piece unconditionally (no branch in the loop), and those reads return zero without
+    // a memory request (over the whole slice they would fetch the next piece's first steps
+    // again). Non-temporal: every byte is read once per call.
     constexpr int R = kAff ? kBits : 4;   // word rows per step
-    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.qweight + (size_t)sb * R * N, (uint32_t)((se - sb) * R * 4 * N));
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.qweight + (size_t)wb * R * N, (uint32_t)((we - wb) * R * 4 * N));
     // affine codes: the lane's 8 rows start at bit `a_bit` of the step, in word row a_bit / 32
     // (blocks of kSub > 1 steps: word row rl of the block)
     const int a_bit = kAff && kSub == 1 ? 8 * kBits * rl : 0;
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 #pragma unroll
         for (int v = 0; v < kLd; ++v) {   // GPTQ: the next 4 columns; affine: the next word row
             const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-                wrs, (int)(w_lane + (uint32_t)(t - sb) * (uint32_t)R * 4u * (uint32_t)N + (kAff ? 4u * (uint32_t)N : 16u) * v),
+                wrs, (int)(w_lane + (uint32_t)(t - wb) * (uint32_t)R * 4u * (uint32_t)N + (kAff ? 4u * (uint32_t)N : 16u) * v),
                 0, kNonTemporal);
             dst[v] = uint4{x.x, x.y, x.z, x.w};
         }
