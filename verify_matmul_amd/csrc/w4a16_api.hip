@@ -37,21 +37,25 @@ int hip_fail(hipError_t e, const char *what)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- per-(device, stream) scratch -------------------------------------------------------------
-// One block per (device, stream) in three regions:
-//   [0] control words: split-K tile counters and slice flags, the fused pick's row keys and the
-//       argmax counters. Zeroed when the block is allocated; every kernel leaves them zero, so
-//       they are zero between calls whatever the previous call was.
-//   [1] fp32 partial sums: split-K slices of the small-row GEMM, K slices of the many-row GEMM.
-//       Always written before they are read within a call (the small-row reducer reads a slice
-//       only after its flag is raised), so stale contents are never used.
-//   [2] prepared activations, rewritten by every call that reads them.
-// When a call needs a larger block, a new one is allocated and zeroed and the old one is kept
+// One block per (device, stream) in four regions:
+//   [0] control words: split-K tile counters, the fused pick's row keys and the argmax counters.
+//       Zeroed when the block is allocated; every kernel leaves them zero, so they are zero
+//       between calls whatever the previous call was.
+//   [1] the split-K exchange of the small-row and decode kernels: fp32 slots for their slices,
+//       every word kSliceEmpty when the block is allocated. Each reducer writes the pattern back
+//       into the slots it took, so the region is all kSliceEmpty between calls whatever the
+//       previous call was. Nothing else is stored there.
+//   [2] data written before it is read within a call: the many-row GEMM's fp32 K slices, the
+//       fused k-best pick's slots.
+//   [3] prepared activations, rewritten by every call that reads them.
+// When a call needs a larger block, a new one is allocated and set up and the old one is kept
 // (a graph captured earlier may still use it) until w4a16_release_scratch. A call that would
 // allocate while its stream is being captured fails instead (allocation and zeroing are not
 // captured): warm the stream up with the same shapes before capturing it.
+constexpr int kRegions = 4;
 struct Scratch {
     void *base = nullptr;
-    size_t bytes[3] = {0, 0, 0};
+    size_t bytes[kRegions] = {0, 0, 0, 0};
     std::vector<void *> retired;
 };
 
@@ -71,21 +75,37 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct ScratchView {
     uint32_t *control;
+    float *exchange;
     float *partials;
     void *act;
 };
 
+__global__ void fill_words_kernel(uint32_t *p, size_t n, uint32_t value)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+hipError_t fill_words(uint32_t *p, size_t n, uint32_t value, hipStream_t stream)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_words_kernel, dim3(256), dim3(256), 0, stream, p, n, value);
+    return hipGetLastError();
+}
+
 // Returns W4A16_OK and fills `view` with pointers into a block whose regions hold at least the
 // requested bytes, allocating a larger block for the stream when needed.
-int get_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, size_t act_bytes, ScratchView *view)
+int get_scratch(hipStream_t stream, size_t control_bytes, size_t exchange_bytes, size_t partial_bytes,
+                size_t act_bytes, ScratchView *view)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch &s = g_scratch[Key{dev, stream}];
-    const size_t need[3] = {std::max(control_bytes, (size_t)4096), partial_bytes, act_bytes};
-    if (s.base == nullptr || s.bytes[0] < need[0] || s.bytes[1] < need[1] || s.bytes[2] < need[2]) {
+    const size_t need[kRegions] = {std::max(control_bytes, (size_t)4096), exchange_bytes, partial_bytes, act_bytes};
+    if (s.base == nullptr || s.bytes[0] < need[0] || s.bytes[1] < need[1] || s.bytes[2] < need[2] ||
+        s.bytes[3] < need[3]) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         e = hipStreamIsCapturing(stream, &cap);
         if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
@@ -93,8 +113,8 @@ int get_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, 
             return fail(W4A16_ERR_UNSUPPORTED,
                         "this call needs more scratch than its stream holds, and the stream is being captured: "
                         "run the same calls on the stream once before capturing it");
-        size_t nb[3], total = 0;
-        for (int r = 0; r < 3; ++r) {
+        size_t nb[kRegions], total = 0;
+        for (int r = 0; r < kRegions; ++r) {
             nb[r] = round_up(std::max(need[r], s.bytes[r]), 256);
             total += nb[r];
         }
@@ -105,49 +125,58 @@ int get_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, 
             return fail(W4A16_ERR_NO_MEMORY, "hipMalloc of %zu scratch bytes: %s", total, hipGetErrorString(e));
         }
         e = hipMemsetAsync(p, 0, total, stream);
+        if (e == hipSuccess)
+            e = fill_words(reinterpret_cast<uint32_t *>(static_cast<char *>(p) + nb[0]), nb[1] / sizeof(uint32_t),
+                           kSliceEmpty, stream);
         if (e != hipSuccess) {
             (void)hipFree(p);
-            return hip_fail(e, "hipMemsetAsync");
+            return hip_fail(e, "setting up scratch");
         }
         if (s.base) s.retired.push_back(s.base);
         s.base = p;
-        for (int r = 0; r < 3; ++r) s.bytes[r] = nb[r];
+        for (int r = 0; r < kRegions; ++r) s.bytes[r] = nb[r];
     }
     char *b = static_cast<char *>(s.base);
     view->control = reinterpret_cast<uint32_t *>(b);
-    view->partials = reinterpret_cast<float *>(b + s.bytes[0]);
-    view->act = b + s.bytes[0] + s.bytes[1];
+    view->exchange = reinterpret_cast<float *>(b + s.bytes[0]);
+    view->partials = reinterpret_cast<float *>(b + s.bytes[0] + s.bytes[1]);
+    view->act = b + s.bytes[0] + s.bytes[1] + s.bytes[2];
     return W4A16_OK;
 }
 
 // ---- the no-allocation scratch (w4a16_gemm_noalloc) -------------------------------------------
 // For callers that cannot allocate: one fixed array in device memory per GPU, `scratch`, laid out
-// as [control words (kNoAllocControl bytes)][partials and prepared activations]. Its address is
-// taken with hipGetSymbolAddress once per device (with that device current) and kept; host code
-// passes that address, never the array's name, to kernels. The control words are cleared by a
-// fill kernel at that set-up and are zero between calls from then on (every kernel leaves them
-// zero). Every call on a GPU shares its array: calls that overlap on one GPU race.
+// as [control words (kNoAllocControl bytes)][split-K exchange (kNoAllocExchange bytes)][data and
+// prepared activations (kNoAllocData bytes)]. Its address is taken with hipGetSymbolAddress once
+// per device (with that device current) and kept; host code passes that address, never the
+// array's name, to kernels. At that set-up fill kernels zero the control words and set every
+// word of the exchange to kSliceEmpty; every kernel leaves them so from then on. Every call on a
+// GPU shares its array: calls that overlap on one GPU race.
 constexpr size_t kNoAllocBytes = 16u << 20;
 constexpr size_t kNoAllocControl = 1u << 20;
+constexpr size_t kNoAllocExchange = 11u << 20;
+constexpr size_t kNoAllocData = kNoAllocBytes - kNoAllocControl - kNoAllocExchange;
 static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
 std::mutex g_noalloc_mu;
 std::map<int, char *> g_noalloc_ptr;   // device -> address of its `scratch`
 
-__global__ void zero_words_kernel(uint32_t *p, size_t n)
+// Whether a call's scratch fits the no-allocation array's regions.
+bool noalloc_fits(size_t control_bytes, size_t exchange_bytes, size_t partial_bytes, size_t act_bytes)
 {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
+    return control_bytes <= kNoAllocControl && exchange_bytes <= kNoAllocExchange &&
+           round_up(partial_bytes, 256) + act_bytes <= kNoAllocData;
 }
 
-int noalloc_scratch(hipStream_t stream, size_t control_bytes, size_t partial_bytes, size_t act_bytes,
-                    ScratchView *view)
+int noalloc_scratch(hipStream_t stream, size_t control_bytes, size_t exchange_bytes, size_t partial_bytes,
+                    size_t act_bytes, ScratchView *view)
 {
-    const size_t data = round_up(partial_bytes, 256) + act_bytes;
-    if (control_bytes > kNoAllocControl || data > kNoAllocBytes - kNoAllocControl)
+    if (!noalloc_fits(control_bytes, exchange_bytes, partial_bytes, act_bytes))
         return fail(W4A16_ERR_UNSUPPORTED,
-                    "the call needs %zu control and %zu data bytes of scratch; the no-allocation buffer holds %zu and %zu",
-                    control_bytes, data, kNoAllocControl, kNoAllocBytes - kNoAllocControl);
+                    "the call needs %zu control, %zu exchange and %zu data bytes of scratch; the no-allocation "
+                    "buffer holds %zu, %zu and %zu",
+                    control_bytes, exchange_bytes, round_up(partial_bytes, 256) + act_bytes, kNoAllocControl,
+                    kNoAllocExchange, kNoAllocData);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -159,17 +188,20 @@ int noalloc_scratch(hipStream_t stream, size_t control_bytes, size_t partial_byt
             void *ptr = nullptr;
             e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
             if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
-            hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint32_t *>(ptr),
-                               kNoAllocControl / sizeof(uint32_t));
-            e = hipGetLastError();
-            if (e != hipSuccess) return hip_fail(e, "clearing the no-allocation scratch");
+            uint32_t *words = static_cast<uint32_t *>(ptr);
+            e = fill_words(words, kNoAllocControl / sizeof(uint32_t), 0u, stream);
+            if (e == hipSuccess)
+                e = fill_words(words + kNoAllocControl / sizeof(uint32_t), kNoAllocExchange / sizeof(uint32_t),
+                               kSliceEmpty, stream);
+            if (e != hipSuccess) return hip_fail(e, "setting up the no-allocation scratch");
             it = g_noalloc_ptr.emplace(dev, static_cast<char *>(ptr)).first;
         }
         base = it->second;
     }
     view->control = reinterpret_cast<uint32_t *>(base);
-    view->partials = reinterpret_cast<float *>(base + kNoAllocControl);
-    view->act = base + kNoAllocControl + round_up(partial_bytes, 256);
+    view->exchange = reinterpret_cast<float *>(base + kNoAllocControl);
+    view->partials = reinterpret_cast<float *>(base + kNoAllocControl + kNoAllocExchange);
+    view->act = base + kNoAllocControl + kNoAllocExchange + round_up(partial_bytes, 256);
     return W4A16_OK;
 }
 
@@ -428,33 +460,30 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     GemmPlan plan{};
     rc = make_plan(M, NV, K, group_size, zm, splits, waves_k, tile_cols, idx != nullptr, &plan);
     if (rc != W4A16_OK) return rc;
-    // scratch of a plan: control words [tile counters][slice flags, tiles x splits][fused pick's
-    // row keys, one slot of 16 x 64 bit per tile], fp32 partials [splits, M, NV], prepared
-    // activations [M, K] and their shifts
+    // scratch of a plan: control words [tile counters][fused pick's row keys, one slot of 16 x 64
+    // bit per tile], the split-K exchange [splits, M, NV], prepared activations [M, K] and their
+    // shifts
     const size_t tile = (size_t)tile_columns(plan.cols);
     const size_t tiles = ((size_t)NV + tile - 1) / tile;
     const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
-    auto needs = [&](const GemmPlan &pl, size_t *control, size_t *part, size_t *act) {
-        *control = round_up(tiles * sizeof(uint32_t) + tiles * pl.splits * sizeof(uint32_t), 8) +
-                   (idx ? tiles * 16 * sizeof(unsigned long long) : 0);
-        *part = pl.splits > 1 ? (size_t)pl.splits * M * NV * sizeof(float) : 0;
+    auto needs = [&](const GemmPlan &pl, size_t *control, size_t *exch, size_t *act) {
+        *control = round_up(tiles * sizeof(uint32_t), 8) + (idx ? tiles * 16 * sizeof(unsigned long long) : 0);
+        *exch = pl.splits > 1 ? (size_t)pl.splits * M * NV * sizeof(float) : 0;
         *act = pl.prep_a ? a16_bytes + (size_t)pl.splits * pl.wk * M * sizeof(int) : 0;
     };
-    size_t control_bytes, part_bytes, act_bytes;
-    needs(plan, &control_bytes, &part_bytes, &act_bytes);
+    size_t control_bytes, exchange_bytes, act_bytes;
+    needs(plan, &control_bytes, &exchange_bytes, &act_bytes);
     // the no-allocation buffer: a default plan that does not fit takes fewer workgroups per tile
     // (fewer partial slices), down to one
     // (down to one, or to the last launch that still fits in LDS; what still does not fit is refused
     // by noalloc_scratch)
-    while (noalloc && splits == 0 && plan.splits > 1 &&
-           (control_bytes > kNoAllocControl ||
-            round_up(part_bytes, 256) + act_bytes > kNoAllocBytes - kNoAllocControl)) {
+    while (noalloc && splits == 0 && plan.splits > 1 && !noalloc_fits(control_bytes, exchange_bytes, 0, act_bytes)) {
         GemmPlan fewer{};
         if (make_plan(M, NV, K, group_size, zm, std::max(1, plan.splits / 2), plan.wk, tile_cols, idx != nullptr,
                       &fewer) != W4A16_OK)
             break;
         plan = fewer;
-        needs(plan, &control_bytes, &part_bytes, &act_bytes);
+        needs(plan, &control_bytes, &exchange_bytes, &act_bytes);
     }
 
     GemmArgs a{};
@@ -482,16 +511,14 @@ int gemm_call(const void *A, Matrix w, const Matrix *up, int group_size, int M, 
     a.zero_off = plan.zero_off;
     const bool split_k = plan.splits > 1;
     if (split_k || plan.prep_a || idx) {
-        const size_t flag_off = tiles * sizeof(uint32_t);
-        const size_t key_off = round_up(flag_off + tiles * plan.splits * sizeof(uint32_t), 8);
+        const size_t key_off = round_up(tiles * sizeof(uint32_t), 8);
         ScratchView v{};
-        rc = noalloc ? noalloc_scratch(stream, control_bytes, part_bytes, act_bytes, &v)
-                     : get_scratch(stream, control_bytes, part_bytes, act_bytes, &v);
+        rc = noalloc ? noalloc_scratch(stream, control_bytes, exchange_bytes, 0, act_bytes, &v)
+                     : get_scratch(stream, control_bytes, exchange_bytes, 0, act_bytes, &v);
         if (rc != W4A16_OK) return rc;
         char *c = reinterpret_cast<char *>(v.control);
         a.counters = v.control;
-        a.flags = reinterpret_cast<uint32_t *>(c + flag_off);
-        a.partials = v.partials;
+        a.partials = v.exchange;
         a.A16 = static_cast<uint16_t *>(v.act);
         a.ashift = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
         if (idx) {
@@ -542,14 +569,12 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     if (rc != W4A16_OK) return rc;
     const long long wc = (long long)plan.tiles * 16 * plan.cols;
     const int groups = (int)((N + wc - 1) / wc);
-    // the data a launch keeps in scratch: fp32 slices, then the fused pick's slots
-    auto data_need = [&](int sl) {
-        const size_t part = sl > 1 ? (size_t)sl * M * N * sizeof(float) : 0;
-        return round_up(part, 256) + (size_t)groups * M * topk * sizeof(unsigned long long);
-    };
+    // what a launch keeps in scratch: its fp32 slices in the split-K exchange, the fused pick's slots
+    auto exchange_need = [&](int sl) { return sl > 1 ? (size_t)sl * M * N * sizeof(float) : (size_t)0; };
+    const size_t slot_bytes = (size_t)groups * M * topk * sizeof(unsigned long long);
     // the no-allocation array: a default launch whose slices do not fit takes fewer slices while
     // its activation slice still fits in LDS (what still does not fit is refused below)
-    while (noalloc && slices == 0 && plan.slices > 1 && data_need(plan.slices) > kNoAllocBytes - kNoAllocControl) {
+    while (noalloc && slices == 0 && plan.slices > 1 && !noalloc_fits(0, exchange_need(plan.slices), slot_bytes, 0)) {
         DecodePlan fewer{};
         if (make_decode_plan(M, N, K, group_size, qzeros != nullptr, plan.slices - 1, tiles, kw, tile_cols, ring,
                              topk > 0, &fewer, bits) != W4A16_OK)
@@ -579,29 +604,25 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     a.r_off = plan.r_off;
     a.mp_log2 = decode_mp_log2(M);
     if (plan.slices > 1 || topk > 0) {
-        // control words: [counters, one per group of columns][flags, groups x slices][the fused
-        // pick's counter]; data: [fp32 partials, slices x M x N][the fused pick's slots, groups x
-        // M x k keys]
-        const size_t control_bytes = (size_t)groups * (1 + plan.slices) * sizeof(uint32_t) + sizeof(uint32_t);
-        const size_t part_bytes = plan.slices > 1 ? (size_t)plan.slices * M * N * sizeof(float) : 0;
-        if (part_bytes >= (1ull << 31))
+        // control words: [counters, one per group of columns][the fused pick's counter]; the split-K
+        // exchange [slices, M, N]; data: the fused pick's slots [groups, M, k]
+        const size_t control_bytes = (size_t)groups * sizeof(uint32_t) + sizeof(uint32_t);
+        const size_t exchange_bytes = exchange_need(plan.slices);
+        if (exchange_bytes >= (1ull << 31))
             return fail(W4A16_ERR_UNSUPPORTED, "%zu bytes of partial sums exceed the 2 GiB the kernel addresses",
-                        part_bytes);
-        const size_t slot_off = round_up(part_bytes, 256);
-        const size_t data_bytes = slot_off + (size_t)groups * M * topk * sizeof(unsigned long long);
+                        exchange_bytes);
         ScratchView v{};
-        rc = noalloc ? noalloc_scratch(stream, control_bytes, data_bytes, 0, &v)
-                     : get_scratch(stream, control_bytes, data_bytes, 0, &v);
+        rc = noalloc ? noalloc_scratch(stream, control_bytes, exchange_bytes, slot_bytes, 0, &v)
+                     : get_scratch(stream, control_bytes, exchange_bytes, slot_bytes, 0, &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.control;
-        a.flags = v.control + groups;
-        a.partials = v.partials;
-        a.part_bytes = (uint32_t)part_bytes;
+        a.partials = v.exchange;
+        a.part_bytes = (uint32_t)exchange_bytes;
         if (topk > 0) {
             a.topk = topk;
             a.pick_none = pick_none;
-            a.pick_counter = v.control + (size_t)groups * (1 + plan.slices);
-            a.pick_slots = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(v.partials) + slot_off);
+            a.pick_counter = v.control + groups;
+            a.pick_slots = reinterpret_cast<unsigned long long *>(v.partials);
             a.pick_idx = idx;
         }
     }
@@ -648,7 +669,7 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
     const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
     const size_t part_bytes = splits > 1 ? (size_t)splits * M * N * (up ? 2 : 1) * sizeof(float) : 0;
     ScratchView v{};
-    rc = get_scratch(stream, 0, part_bytes, a16_bytes + (size_t)M * sizeof(int), &v);
+    rc = get_scratch(stream, 0, 0, part_bytes, a16_bytes + (size_t)M * sizeof(int), &v);
     if (rc != W4A16_OK) return rc;
     uint16_t *a16 = static_cast<uint16_t *>(v.act);
     int *shifts = reinterpret_cast<int *>(static_cast<char *>(v.act) + a16_bytes);
@@ -938,7 +959,7 @@ int w4a16_argmax_rows(const float *logits, int M, int N, int32_t *idx, hipStream
     // counters: M uint32 counters followed by M 64-bit keys, all zero between calls
     const size_t need = round_up((size_t)M * 4, 8) + (size_t)M * 8;
     ScratchView v{};
-    int rc = get_scratch(stream, need, 0, 0, &v);
+    int rc = get_scratch(stream, need, 0, 0, 0, &v);
     if (rc != W4A16_OK) return rc;
     uint32_t *ctr = v.control;
     a.counters = ctr;

@@ -53,11 +53,6 @@ namespace {
 // Activation items (16 bytes) a lane may stage through registers: 8 KB per wave.
 constexpr int kHeld = 8;
 
-// Wait until every vector memory operation this thread issued has completed (stores included:
-// on gfx9 stores count in vmcnt).
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-
 // The K range [wb, we) (in steps) of piece `wave` of split `split`: splits cut K into
 // contiguous slices, the waves of a workgroup cut each slice again. The activation preparation
 // kernel and the GEMM compute the same ranges.
@@ -664,69 +659,71 @@ __attribute__((amdgpu_waves_per_eu(gemm_min_waves<kMfma, kZM, kC>()))) void w4a1
 
     // ---- split-K across workgroups ---------------------------------------------------------
     // Every workgroup of the tile counted itself in on the tile's counter when it started; the
-    // last one to start adds the slices. The others store their slice as fp32 with agent-scope
-    // atomic stores, wait until every store of the workgroup has completed, and raise their
-    // slice's flag. The reducer waits for each other slice's flag, reads the slice, adds the
-    // slices in slice order (bit-identical results from run to run), and lowers the flags and
-    // the counter again. Counters and flags are therefore zero between calls whatever the call
-    // was: no state carries from one call to the next, so a call replayed from a captured graph
-    // runs exactly as it ran when it was captured.
+    // last one to start adds the slices. The others store their slice into the split-K
+    // exchange as fp32 with agent-scope atomic stores and are done: nothing to wait for, no
+    // flag. The reducer reads each other slice's slot again until it no longer holds
+    // kSliceEmpty, adds the slices in slice order (bit-identical results from run to run), writes
+    // kSliceEmpty back into every slot it took and lowers the counter. The exchange and the
+    // counters are therefore as they were before the call whatever the call was: no state
+    // carries from one call to the next, so a call replayed from a captured graph runs exactly as
+    // it ran when it was captured.
     const size_t slice = (size_t)M * NV;
-    uint32_t *const tile_flags = p.flags + (size_t)tile * p.splits;
+    uint32_t *const ex = reinterpret_cast<uint32_t *>(p.partials);   // slots as bits
     if (!s_last) {
         for (int idx = tid; idx < M * kTile; idx += kThreads) {
             const int m = idx / kTile;
             const int c = idx - m * kTile;
             if (col_valid(c))
-                __hip_atomic_store(p.partials + (size_t)split * slice + (size_t)m * NV + tile * kTile + c, wg_sum(m, c),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ex + (size_t)split * slice + (size_t)m * NV + tile * kTile + c,
+                                   __builtin_bit_cast(uint32_t, wg_sum(m, c)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        wait_vm_all();        // this thread's stores have completed ...
-        __syncthreads();      // ... and so have every other thread's
-        if (tid == 0) __hip_atomic_store(&tile_flags[split], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    __shared__ int s_failed;
-    if (tid == 0) s_failed = 0;
-    __syncthreads();
-    for (int sp = tid; sp < p.splits; sp += kThreads) {
-        if (sp == split) continue;
-        uint32_t spins = 0;
-        while (__hip_atomic_load(&tile_flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
-                s_failed = 1;
-                break;
-            }
-        }
-    }
-    __syncthreads();   // every flag seen raised: the slices' stores have completed
-    const bool failed = s_failed != 0;
     constexpr int kBatch = 8;
     for (int idx = tid; idx < M * kTile; idx += kThreads) {
         const int m = idx / kTile;
         const int c = idx - m * kTile;
         const bool in = col_valid(c);
         const float own = wg_sum(m, c);
-        const float *col = p.partials + (size_t)m * NV + tile * kTile + c;
+        uint32_t *const col = ex + (size_t)m * NV + tile * kTile + c;
         float v = 0.f;
+        bool failed = false;
         for (int sp0 = 0; in && sp0 < p.splits; sp0 += kBatch) {
-            float x[kBatch];
+            auto taken = [&](int i) { return sp0 + i < p.splits && sp0 + i != split; };
+            uint32_t x[kBatch];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int sp = sp0 + i;
-                x[i] = sp < p.splits && sp != split
-                           ? __hip_atomic_load(col + (size_t)sp * slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : own;
+            for (int i = 0; i < kBatch; ++i)
+                x[i] = taken(i) ? __hip_atomic_load(col + (size_t)(sp0 + i) * slice, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : __builtin_bit_cast(uint32_t, own);
+            for (uint32_t spins = 0;;) {   // until every slot of the batch has arrived
+                bool wait = false;
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) wait |= taken(i) && x[i] == kSliceEmpty;
+                if (!wait) break;
+                if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                    failed = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (taken(i) && x[i] == kSliceEmpty)
+                        x[i] = __hip_atomic_load(col + (size_t)(sp0 + i) * slice, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
             }
 #pragma unroll
             for (int i = 0; i < kBatch; ++i)
-                if (sp0 + i < p.splits) v += x[i];
+                if (sp0 + i < p.splits) v += __builtin_bit_cast(float, x[i]);
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)   // the slots are empty again
+                if (taken(i))
+                    __hip_atomic_store(col + (size_t)(sp0 + i) * slice, kSliceEmpty, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
         put(m, c, failed ? __builtin_nanf("") : v, in);
     }
-    for (int sp = tid; sp < p.splits; sp += kThreads)
-        if (sp != split) __hip_atomic_store(&tile_flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (kDual) finish_pair();
     if (amax) finish_argmax();
     if (tid == 0) __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -24,10 +24,18 @@ constexpr int kLdsStageBudget = 8 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kWideTileWavesPerCu = 16;
 
-// Bound on the split-K reducer's wait for another slice's flag (each try sleeps about 128
-// cycles). Only reached if a workgroup never finished, which a correct launch rules out; the
-// outputs of the tile are then NaN instead of a hang.
+// Bound on the split-K reducer's wait for another slice's sums (each try sleeps about 128
+// cycles). Only reached if a workgroup never finished, which a correct launch rules out; those
+// outputs are then NaN instead of a hang.
 constexpr uint32_t kSpinLimit = 1u << 24;
+
+// The split-K exchange: fp32 slots [slices, M, N] that hold this bit pattern (a signalling NaN)
+// between calls. A workgroup publishes its slice by storing it; the reducer takes each slot
+// once it no longer holds the pattern and writes the pattern back. The kernels publish only
+// results of floating-point arithmetic, which never produce a signalling NaN, so a slot changes
+// exactly when its slice arrives. (Were a published value a NaN of this very payload, the
+// reducer would wait out kSpinLimit and output NaN: the sum it stands for is NaN anyway.)
+constexpr uint32_t kSliceEmpty = 0x7FBADBADu;
 
 // Ints of per-row data at the start of a GEMM workgroup's LDS, per wave: 16 rescale exponents
 // and 16 rescale multipliers.
@@ -61,9 +69,8 @@ struct GemmArgs {
     void *out;
     uint16_t *A16;            // [M, K] prepared activations (matrix-core path)
     int *ashift;              // [splits * waves_k, M] their rescale per K piece and row
-    float *partials;          // [splits, M, N] (gated pair: [splits, M, 2N]) fp32 partial sums
+    float *partials;          // split-K exchange [splits, M, N] (gated pair: [splits, M, 2N]), kSliceEmpty between calls
     uint32_t *counters;       // one per column tile, zero between calls
-    uint32_t *flags;          // [tiles, splits] slice-ready flags, zero between calls
     unsigned long long *amax_keys;   // fused pick: [tiles, 16] row keys, one slot per column tile, zero between
                                      // calls (nullptr: off)
     int32_t *amax_idx;               // fused pick: [M] output indices
@@ -170,7 +177,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // (w, k) on column tile w (tiles adjacent, 64 or 128 columns each) and K piece k of the slice;
 // the workgroup's activation slice is converted once into LDS for all of them and the pieces
 // are added in LDS. `slices` workgroups share each group of columns along K; their fp32 sums
-// meet through scratch (counters and flags as in the small-row kernel).
+// meet through the split-K exchange (a counter per group of columns, as in the small-row kernel).
 constexpr int kDecMaxWaves = 8;
 constexpr int kDecodeMinN = 65536;   // plain calls this wide take the decode kernel by default
 constexpr int kDecodeMidN = 16384;   // and from this width, plain calls of more than 8 rows
@@ -189,9 +196,8 @@ struct DecodeArgs {
     const uint16_t *biases;   // affine codes: bf16 [K/g, N] (nullptr: GPTQ)
     int bits;                 // affine codes: bits per code (1, 2, 3, 4, 5, 6 or 8)
     void *out;
-    float *partials;          // [slices, M, N] fp32 (slices > 1)
+    float *partials;          // split-K exchange [slices, M, N] (slices > 1), kSliceEmpty between calls
     uint32_t *counters;       // [groups] zero between calls
-    uint32_t *flags;          // [groups, slices] zero between calls
     int M, N, K, g;
     int tiles;                // adjacent column tiles per workgroup
     int kw;                   // K pieces per tile (waves per tile) in a workgroup
