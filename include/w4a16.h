@@ -28,14 +28,14 @@
  *   - Arguments are checked on the host before any device work; a non-OK status means no
  *     device work was enqueued. The library never aborts and never prints: w4a16_last_error()
  *     returns a description of the last non-OK status of the calling thread.
- *   - The library owns one scratch buffer per (device, stream) for tile counters, the split-K
- *     exchange of partial sums, the many-row GEMM's K slices, prepared activations and the fused
- *     pick's row keys. It is allocated (with hipMalloc, then set up by small kernels on the
- *     stream) on the first call that needs it on that stream; a later call that needs more gets
- *     a new, larger buffer and the old one is kept until w4a16_release_scratch (a graph captured
- *     earlier may still use it). Every call leaves the counters and keys zero and the exchange
- *     empty, and writes its other data before it reads it, so no state carries from one call to
- *     the next: calls may be captured into a HIP graph and
+ *   - The library owns one scratch buffer per (device, stream) for tile counters and slice
+ *     flags, split-K partial sums, prepared activations and the fused pick's row keys. It is
+ *     allocated (with hipMalloc, then set up by small kernels on the stream) on the first call
+ *     that needs it on that stream; a later call that needs more gets a new, larger buffer and
+ *     the old one is kept until w4a16_release_scratch (a graph captured earlier may still use
+ *     it). Every call leaves the counters, flags and keys zero and the small-row kernel's
+ *     split-K exchange empty, and writes its other data before it reads it, so no state carries
+ *     from one call to the next: calls may be captured into a HIP graph and
  *     replayed any number of times. A call that would have to allocate while its stream is
  *     being captured returns W4A16_ERR_UNSUPPORTED instead, so run the same calls on the stream
  *     once before capturing it (that also keeps allocation out of timed regions). Calls on
@@ -93,15 +93,15 @@ int w4a16_gemm(const void *A, const uint32_t *qweight, const uint16_t *scales,
  * on a stream that has not been warmed up, tight serving loops, and harnesses that forbid
  * hipMalloc. Same operation, arguments, accuracy contract and determinism as w4a16_gemm; it calls
  * no hipMalloc, hipFree or allocating routine. Its scratch is one fixed 16 MiB array in device
- * memory per GPU (1 MiB of counters, 11 MiB of split-K exchange for partial sums, 4 MiB of
- * prepared activations), held until the process ends; its first call on a device takes the
+ * memory per GPU (1 MiB of counters and flags, 6 MiB of split-K exchange, 9 MiB of partial sums
+ * and prepared activations), held until the process ends; its first call on a device takes the
  * array's address and sets up the counters and the exchange with small kernels on `stream`. A
- * launch whose scratch would not fit takes fewer
- * split-K workgroups per column tile (or, on matrices of 65536 columns or more, fewer K slices)
- * so its rounding may differ from w4a16_gemm's, within the same contract; if even one does not
- * fit (or the K slice then no longer fits in LDS), W4A16_ERR_UNSUPPORTED. Every call on a GPU uses the same
- * array and leaves its counters zero and its exchange empty: calls that overlap on one GPU (on different
- * streams, or graphs replayed concurrently) race and must not be made.
+ * launch whose scratch would not fit takes fewer split-K workgroups per column tile (or, on
+ * matrices of 65536 columns or more, fewer K slices) so its rounding may differ from
+ * w4a16_gemm's, within the same contract; if even one does not fit (or the K slice then no
+ * longer fits in LDS), W4A16_ERR_UNSUPPORTED. Every call on a GPU uses the same array and leaves
+ * its counters and flags zero and its exchange empty: calls that overlap on one GPU (on
+ * different streams, or graphs replayed concurrently) race and must not be made.
  */
 int w4a16_gemm_noalloc(const void *A, const uint32_t *qweight, const uint16_t *scales,
                        const uint32_t *qzeros, int group_size, int M, int N, int K,

@@ -38,15 +38,15 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---- per-(device, stream) scratch -------------------------------------------------------------
 // One block per (device, stream) in four regions:
-//   [0] control words: split-K tile counters, the fused pick's row keys and the argmax counters.
-//       Zeroed when the block is allocated; every kernel leaves them zero, so they are zero
-//       between calls whatever the previous call was.
-//   [1] the split-K exchange of the small-row and decode kernels: fp32 slots for their slices,
-//       every word kSliceEmpty when the block is allocated. Each reducer writes the pattern back
-//       into the slots it took, so the region is all kSliceEmpty between calls whatever the
-//       previous call was. Nothing else is stored there.
-//   [2] data written before it is read within a call: the many-row GEMM's fp32 K slices, the
-//       fused k-best pick's slots.
+//   [0] control words: split-K tile counters, the decode kernel's slice flags, the fused pick's
+//       row keys and the argmax counters. Zeroed when the block is allocated; every kernel leaves
+//       them zero, so they are zero between calls whatever the previous call was.
+//   [1] the small-row kernel's split-K exchange: fp32 slots for its slices, every word
+//       kSliceEmpty when the block is allocated. Each reducer writes the pattern back into the
+//       slots it took, so the region is all kSliceEmpty between calls whatever the previous call
+//       was. Nothing else is stored there.
+//   [2] data written before it is read within a call: the decode kernel's fp32 slices (read only
+//       after their flags are raised) and fused k-best slots, the many-row GEMM's K slices.
 //   [3] prepared activations, rewritten by every call that reads them.
 // When a call needs a larger block, a new one is allocated and set up and the old one is kept
 // (a graph captured earlier may still use it) until w4a16_release_scratch. A call that would
@@ -146,15 +146,15 @@ int get_scratch(hipStream_t stream, size_t control_bytes, size_t exchange_bytes,
 
 // ---- the no-allocation scratch (w4a16_gemm_noalloc) -------------------------------------------
 // For callers that cannot allocate: one fixed array in device memory per GPU, `scratch`, laid out
-// as [control words (kNoAllocControl bytes)][split-K exchange (kNoAllocExchange bytes)][data and
-// prepared activations (kNoAllocData bytes)]. Its address is taken with hipGetSymbolAddress once
+// as [control words (kNoAllocControl bytes)][split-K exchange (kNoAllocExchange bytes)][data:
+// the decode kernel's slices, prepared activations (kNoAllocData bytes)]. Its address is taken with hipGetSymbolAddress once
 // per device (with that device current) and kept; host code passes that address, never the
 // array's name, to kernels. At that set-up fill kernels zero the control words and set every
 // word of the exchange to kSliceEmpty; every kernel leaves them so from then on. Every call on a
 // GPU shares its array: calls that overlap on one GPU race.
 constexpr size_t kNoAllocBytes = 16u << 20;
 constexpr size_t kNoAllocControl = 1u << 20;
-constexpr size_t kNoAllocExchange = 11u << 20;
+constexpr size_t kNoAllocExchange = 6u << 20;
 constexpr size_t kNoAllocData = kNoAllocBytes - kNoAllocControl - kNoAllocExchange;
 static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
@@ -569,12 +569,14 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     if (rc != W4A16_OK) return rc;
     const long long wc = (long long)plan.tiles * 16 * plan.cols;
     const int groups = (int)((N + wc - 1) / wc);
-    // what a launch keeps in scratch: its fp32 slices in the split-K exchange, the fused pick's slots
-    auto exchange_need = [&](int sl) { return sl > 1 ? (size_t)sl * M * N * sizeof(float) : (size_t)0; };
-    const size_t slot_bytes = (size_t)groups * M * topk * sizeof(unsigned long long);
+    // the data a launch keeps in scratch: fp32 slices, then the fused pick's slots
+    auto data_need = [&](int sl) {
+        const size_t part = sl > 1 ? (size_t)sl * M * N * sizeof(float) : 0;
+        return round_up(part, 256) + (size_t)groups * M * topk * sizeof(unsigned long long);
+    };
     // the no-allocation array: a default launch whose slices do not fit takes fewer slices while
     // its activation slice still fits in LDS (what still does not fit is refused below)
-    while (noalloc && slices == 0 && plan.slices > 1 && !noalloc_fits(0, exchange_need(plan.slices), slot_bytes, 0)) {
+    while (noalloc && slices == 0 && plan.slices > 1 && !noalloc_fits(0, 0, data_need(plan.slices), 0)) {
         DecodePlan fewer{};
         if (make_decode_plan(M, N, K, group_size, qzeros != nullptr, plan.slices - 1, tiles, kw, tile_cols, ring,
                              topk > 0, &fewer, bits) != W4A16_OK)
@@ -604,25 +606,31 @@ int decode_call(const void *A, const uint32_t *qweight, const uint16_t *scales, 
     a.r_off = plan.r_off;
     a.mp_log2 = decode_mp_log2(M);
     if (plan.slices > 1 || topk > 0) {
-        // control words: [counters, one per group of columns][the fused pick's counter]; the split-K
-        // exchange [slices, M, N]; data: the fused pick's slots [groups, M, k]
-        const size_t control_bytes = (size_t)groups * sizeof(uint32_t) + sizeof(uint32_t);
-        const size_t exchange_bytes = exchange_need(plan.slices);
-        if (exchange_bytes >= (1ull << 31))
+        // control words: [counters, one per group of columns][flags, groups x slices][the fused
+        // pick's counter]; data: [fp32 partials, slices x M x N][the fused pick's slots, groups x
+        // M x k keys]. (The decode kernel keeps per-slice flags: the small-row kernel's exchange,
+        // whose reducer writes the empty pattern back, would add the slices' bytes again in
+        // writes, 2.2 MB per call at 16 rows on FFN 5120 x 17408, for no measured gain here.)
+        const size_t control_bytes = (size_t)groups * (1 + plan.slices) * sizeof(uint32_t) + sizeof(uint32_t);
+        const size_t part_bytes = plan.slices > 1 ? (size_t)plan.slices * M * N * sizeof(float) : 0;
+        if (part_bytes >= (1ull << 31))
             return fail(W4A16_ERR_UNSUPPORTED, "%zu bytes of partial sums exceed the 2 GiB the kernel addresses",
-                        exchange_bytes);
+                        part_bytes);
+        const size_t slot_off = round_up(part_bytes, 256);
+        const size_t data_bytes = slot_off + (size_t)groups * M * topk * sizeof(unsigned long long);
         ScratchView v{};
-        rc = noalloc ? noalloc_scratch(stream, control_bytes, exchange_bytes, slot_bytes, 0, &v)
-                     : get_scratch(stream, control_bytes, exchange_bytes, slot_bytes, 0, &v);
+        rc = noalloc ? noalloc_scratch(stream, control_bytes, 0, data_bytes, 0, &v)
+                     : get_scratch(stream, control_bytes, 0, data_bytes, 0, &v);
         if (rc != W4A16_OK) return rc;
         a.counters = v.control;
-        a.partials = v.exchange;
-        a.part_bytes = (uint32_t)exchange_bytes;
+        a.flags = v.control + groups;
+        a.partials = v.partials;
+        a.part_bytes = (uint32_t)part_bytes;
         if (topk > 0) {
             a.topk = topk;
             a.pick_none = pick_none;
-            a.pick_counter = v.control + groups;
-            a.pick_slots = reinterpret_cast<unsigned long long *>(v.partials);
+            a.pick_counter = v.control + (size_t)groups * (1 + plan.slices);
+            a.pick_slots = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(v.partials) + slot_off);
             a.pick_idx = idx;
         }
     }

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
     constexpr int kTile = 16 * kC;  // columns per wave
     constexpr int kRows = kMfma ? 4 : 1;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_last, s_pick_last;
+    __shared__ int s_last, s_failed, s_pick_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -639,115 +639,80 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
 
     // ---- 8. slices across workgroups ----------------------------------------------------------
     // Every workgroup of the column group counted itself in when it started; the last one to
-    // start adds the slices. The others store their slice into the split-K exchange (16-byte
-    // stores with the agent-scope coherence bit) and are done: nothing to wait for, no flag. The
-    // reducer reads each other slice's slots again until none of their words holds kSliceEmpty,
-    // adds the slices in slice order (bit-identical results from run to run), writes kSliceEmpty
-    // back into every slot it took and lowers the counter: the exchange and the counters are as
-    // they were before the call, so no state carries from one call to the next and a replayed
-    // graph runs as it ran when it was captured.
+    // start adds the slices. The others store their slice (16-byte stores with the agent-scope
+    // coherence bit), wait until every store of the workgroup has completed, and raise their
+    // slice's flag. The reducer waits for each other slice's flag, reads the slices, adds them in
+    // slice order (bit-identical results from run to run), and lowers the flags and the counter
+    // again: counters and flags are zero between calls, so no state carries from one call to
+    // the next and a replayed graph runs as it ran when it was captured.
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(p.partials, p.part_bytes);
-    if (tid == 0) s_last = arrival == (uint32_t)(P - 1);
-    __syncthreads();   // (every wave is past the main loop: the fragments' LDS is free for the pick)
-    auto word = [&](int sp, int r, int v) {   // a lane's output in slice sp's slots, in words
-        return (((size_t)sp * M + row_base + r) * N + n0 + 4 * v);
-    };
-    auto slot = [&](int sp, int r, int v) { return (int)(uint32_t)(word(sp, r, v) * sizeof(float)); };   // in bytes
-    // Waits re-read a slot with atomic loads, which the compiler keeps in the loop (a buffer
-    // load there could be hoisted out of it as a plain read of unchanged memory).
-    const uint32_t *const ex = reinterpret_cast<const uint32_t *>(p.partials);
-    auto poll = [&](size_t w) { return __hip_atomic_load(ex + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    uint32_t *const flags = p.flags + (size_t)cg * P;
+    if (tid == 0) {
+        s_last = arrival == (uint32_t)(P - 1);
+        s_failed = 0;
+    }
+    __syncthreads();
     if (!s_last) {
         if (holder) {
 #pragma unroll
             for (int r = 0; r < kRows; ++r) {
-                if (row_base + r < M) {
+                const int m = row_base + r;
+                if (m < M) {
 #pragma unroll
                     for (int v = 0; v < kV; ++v) {
                         const f32x4 x = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), prs, slot(sl, r, v), 0,
-                                                               kCoherent);
+                        const uint32_t off = (uint32_t)((((size_t)sl * M + m) * N + n0 + 4 * v) * sizeof(float));
+                        __builtin_amdgcn_raw_buffer_store_b128(x, prs, (int)off, 0, kCoherent);
                     }
                 }
             }
         }
+        wait_vm_all();     // this thread's stores have completed ...
+        __syncthreads();   // ... and so have every other thread's
+        if (tid == 0) __hip_atomic_store(&flags[sl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
+    for (int sp = tid; sp < P; sp += T) {
+        if (sp == sl) continue;
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
+                s_failed = 1;
+                break;
+            }
+        }
+    }
+    __syncthreads();   // every flag seen raised: the other slices' stores have completed
+    const bool failed = s_failed != 0;
     // Each output adds the slices in slice order. The loads of a batch of slices for all of the
     // lane's rows are in flight together (one round trip per batch, not one per row: a slice
-    // written on another die takes about half a microsecond to arrive).
+    // read from another die's stores takes about half a microsecond to arrive).
     constexpr int kOut = kRows * kV;                      // float4 outputs per lane
     constexpr int kBatch = kOut >= 8 ? 1 : 8 / kOut;      // slices per batch: at most 8 loads in flight
     if (holder) {
-        auto taken = [&](int sp, int o) { return sp < P && sp != sl && row_base + o / kV < M; };
-        auto empty = [](u32x4 x) { return x.x == kSliceEmpty || x.y == kSliceEmpty || x.z == kSliceEmpty || x.w == kSliceEmpty; };
-        bool failed = false;
-        // First one lane of the wave waits for one word per slice (its first output's first
-        // word): once that has arrived, the writer has issued the stores of all of the wave's
-        // slots, and the rest arrive within a round trip. Polling every slot while the writers
-        // still stream their weights would load the memory system for nothing.
-        if (lane == 0) {
-            for (int sp = 0; sp < P; ++sp) {
-                if (sp == sl) continue;
-                for (uint32_t spins = 0; poll(word(sp, 0, 0)) == kSliceEmpty;) {
-                    if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
-                        failed = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
-            }
-        }
         f32x4 sum[kOut];
 #pragma unroll
         for (int o = 0; o < kOut; ++o) sum[o] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int b = 0; b < P; b += kBatch) {   // slices in order
-            u32x4 x[kBatch][kOut];
+            f32x4 x[kBatch][kOut];
 #pragma unroll
             for (int i = 0; i < kBatch; ++i)
 #pragma unroll
                 for (int o = 0; o < kOut; ++o) {
                     const int r = o / kV, v = o - (o / kV) * kV;
-                    x[i][o] = __builtin_bit_cast(
-                        u32x4, f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]});
-                    if (taken(b + i, o)) x[i][o] = __builtin_amdgcn_raw_buffer_load_b128(prs, slot(b + i, r, v), 0, kCoherent);
+                    const int sp = b + i, m = row_base + r;
+                    x[i][o] = f32x4{tot[4 * v][r], tot[4 * v + 1][r], tot[4 * v + 2][r], tot[4 * v + 3][r]};
+                    if (sp < P && sp != sl && m < M) {
+                        const uint32_t off = (uint32_t)((((size_t)sp * M + m) * N + n0 + 4 * v) * sizeof(float));
+                        x[i][o] = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kCoherent);
+                    }
                 }
-            for (uint32_t spins = 0;;) {   // until every slot of the batch has arrived
-                bool wait = false;
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-#pragma unroll
-                    for (int o = 0; o < kOut; ++o) wait |= taken(b + i, o) && empty(x[i][o]);
-                if (!wait) break;
-                if (++spins == kSpinLimit) {   // cannot happen while every workgroup runs to its end
-                    failed = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-#pragma unroll
-                    for (int o = 0; o < kOut; ++o)
-                        if (taken(b + i, o) && empty(x[i][o])) {
-                            const int r = o / kV, v = o - (o / kV) * kV;
-                            const size_t w = word(b + i, r, v);
-                            x[i][o] = u32x4{poll(w), poll(w + 1), poll(w + 2), poll(w + 3)};
-                        }
-            }
 #pragma unroll
             for (int i = 0; i < kBatch; ++i)
 #pragma unroll
                 for (int o = 0; o < kOut; ++o)
-                    if (b + i < P) sum[o] += __builtin_bit_cast(f32x4, x[i][o]);
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i)   // the slots are empty again
-#pragma unroll
-                for (int o = 0; o < kOut; ++o)
-                    if (taken(b + i, o)) {
-                        const int r = o / kV, v = o - (o / kV) * kV;
-                        __builtin_amdgcn_raw_buffer_store_b128(u32x4{kSliceEmpty, kSliceEmpty, kSliceEmpty, kSliceEmpty},
-                                                               prs, slot(b + i, r, v), 0, kCoherent);
-                    }
+                    if (b + i < P) sum[o] += x[i][o];
         }
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
@@ -757,17 +722,20 @@ __global__ __launch_bounds__(kDecMaxWaves * 64) void decode_kernel(DecodeArgs p)
             for (int v = 0; v < kV; ++v) {
                 f32x4 sm = sum[r * kV + v];
                 if (failed) sm = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-                store_out(m, v, sm.x, sm.y, sm.z, sm.w);
-                if (KP > 0) {
-                    stage(r, 4 * v, sm.x);
-                    stage(r, 4 * v + 1, sm.y);
-                    stage(r, 4 * v + 2, sm.z);
-                    stage(r, 4 * v + 3, sm.w);
+                const f32x4 sum = sm;
+                store_out(m, v, sum.x, sum.y, sum.z, sum.w);
+                if (KP > 0) {   // every wave is past the main loop (the flag wait ended in a barrier)
+                    stage(r, 4 * v, sum.x);
+                    stage(r, 4 * v + 1, sum.y);
+                    stage(r, 4 * v + 2, sum.z);
+                    stage(r, 4 * v + 3, sum.w);
                 }
             }
         }
     }
     if (KP > 0) pick();
+    for (int sp = tid; sp < P; sp += T)
+        if (sp != sl) __hip_atomic_store(&flags[sp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(&p.counters[cg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -177,7 +177,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // (w, k) on column tile w (tiles adjacent, 64 or 128 columns each) and K piece k of the slice;
 // the workgroup's activation slice is converted once into LDS for all of them and the pieces
 // are added in LDS. `slices` workgroups share each group of columns along K; their fp32 sums
-// meet through the split-K exchange (a counter per group of columns, as in the small-row kernel).
+// meet through scratch: a counter per group of columns and a flag per slice (the writers wait for
+// their stores to complete and raise the slice's flag; the reducer waits for the flags).
 constexpr int kDecMaxWaves = 8;
 constexpr int kDecodeMinN = 65536;   // plain calls this wide take the decode kernel by default
 constexpr int kDecodeMidN = 16384;   // and from this width, plain calls of more than 8 rows
@@ -196,8 +197,9 @@ struct DecodeArgs {
     const uint16_t *biases;   // affine codes: bf16 [K/g, N] (nullptr: GPTQ)
     int bits;                 // affine codes: bits per code (1, 2, 3, 4, 5, 6 or 8)
     void *out;
-    float *partials;          // split-K exchange [slices, M, N] (slices > 1), kSliceEmpty between calls
+    float *partials;          // [slices, M, N] fp32 (slices > 1), written before they are read
     uint32_t *counters;       // [groups] zero between calls
+    uint32_t *flags;          // [groups, slices] zero between calls
     int M, N, K, g;
     int tiles;                // adjacent column tiles per workgroup
     int kw;                   // K pieces per tile (waves per tile) in a workgroup
