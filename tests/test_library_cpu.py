@@ -118,6 +118,36 @@ def test_plan_host_only(lib):
     assert lib.w4a16_plan(1, 256, 512, 48, None, None, None, None) == -1
 
 
+def test_plan_balances_narrow_matrices(lib):
+    """At most 256 column tiles (one per compute unit): the default launch takes the workgroups
+    per tile s that minimise ceil(tiles * s / 256) / s (the busiest CU's share of the work), the
+    fewest on a tie, with at most two workgroups per CU; 16 waves per workgroup, or 8 for up to 8
+    rows when the pieces would be shorter than 8 steps."""
+    import ctypes
+    k, s, w, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+
+    def plan(M, N, K, g):
+        assert lib.w4a16_plan(M, N, K, g, ctypes.byref(k), ctypes.byref(s), ctypes.byref(w), ctypes.byref(c)) == 0
+        return k.value, s.value, w.value, c.value
+
+    # (M, N, K, g) -> (splits, waves_k): attention and FFN down (80 tiles), 5120 x 4096 (64 tiles),
+    # 5120 x 8192 (128), 5120 x 13824 (216: whole K in a workgroup), 3072 x 2048 (32)
+    for M, N, K, g, want in ((1, 5120, 5120, 128, (3, 8)), (8, 5120, 5120, 128, (3, 8)),
+                             (16, 5120, 5120, 128, (3, 16)), (1, 5120, 17408, 64, (3, 16)),
+                             (16, 5120, 17408, 64, (3, 16)), (1, 4096, 5120, 128, (4, 8)),
+                             (16, 4096, 5120, 128, (4, 16)), (4, 8192, 5120, 128, (2, 8)),
+                             (16, 8192, 5120, 128, (2, 16)), (1, 13824, 5120, 128, (1, 16)),
+                             (16, 13824, 5120, 128, (1, 16)), (1, 2048, 3072, 64, (8, 8))):
+        kern, splits, wk, cols = plan(M, N, K, g)
+        assert kern == (0 if M == 1 else 1) and cols == 64, (M, N, K)
+        assert (splits, wk) == want, (M, N, K, (splits, wk))
+        tiles = -(-N // 64)
+        cost = lambda x: -(-tiles * x // 256) / x
+        assert all(cost(splits) <= cost(x) for x in range(1, min(16, 512 // tiles) + 1)), (M, N, K)
+    # more than 256 tiles keep the wave-count rule (FFN up 5120 x 17408: 4 workgroups of 4 waves)
+    assert plan(1, 17408, 5120, 128)[1:3] == (4, 4)
+
+
 def test_fused_pick_checks_its_arguments(lib):
     assert lib.w4a16_gemm_argmax(A, Q, S, None, 128, 1, 256, 512, O, 0, None, None) == -1
     assert b"idx" in lib.w4a16_last_error()

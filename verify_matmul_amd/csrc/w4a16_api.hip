@@ -225,6 +225,27 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
     // groups of 64, M = 12 / 16: 28.4 -> 25.7 / 30.6 -> 27.9 us; at M <= 8 no gain).
     const int cols = tile_cols != 0 ? tile_cols / 16 : (N >= kWideTileMinN || (zm == kAffine && M > 8) ? 8 : 4);
     const int tiles = (N + tile_columns(cols) - 1) / tile_columns(cols);
+    if ((splits == 0 || wk == 0) && tiles <= kCus) {
+        // At most one column tile per compute unit: the launch is balanced by its workgroup
+        // count, not its wave count. `s` workgroups per tile put ceil(tiles * s / kCus) of them on
+        // the busiest CU, each with 1/s of the tile's work: take the s (up to two workgroups per
+        // CU) that minimises that, the fewest on a tie (each slice more adds to the exchange),
+        // and 16 waves per workgroup (8 for up to 8 rows when the pieces would be shorter than 8
+        // steps). Measured on MI355X, back to back, us: attention 5120 x 5120 (80 tiles) M = 1 /
+        // 8 / 16 9.4 / 10.6 / 13.4 -> 8.5 / 9.2 / 10.6 (3 workgroups per tile, 4 before); FFN down
+        // 17408 x 5120 M = 1 / 4 / 8 / 16 16.5 / 18.8 / 21.2 / 25.4 -> 14.7 / 15.3 / 17.5 / 23.1;
+        // 5120 x 4096 (64 tiles) M = 1 / 16 8.3 / 9.9 -> 7.6 / 8.8; 5120 x 13824 (216 tiles) M = 1
+        // / 16 12.4 / 20.4 -> 11.1 / 18.5 (whole K in a workgroup); 5120 x 8192 (128 tiles) M = 16
+        // 13.6 -> 12.4. Matrices of more tiles keep the wave-count rule below.
+        int s = 1;
+        for (int c = 2; c <= std::min(16, 2 * kCus / tiles); ++c)
+            if ((long long)((tiles * c + kCus - 1) / kCus) * s < (long long)((tiles * s + kCus - 1) / kCus) * c) s = c;
+        int w = M > 8 || steps / (s * 16) >= 8 ? 16 : 8;
+        while (w > 1 && s * w > steps) w /= 2;
+        s = std::max(1, std::min(s, steps / w));
+        if (wk == 0) wk = w;
+        if (splits == 0) splits = std::max(1, std::min(s, steps / wk));
+    }
     if (splits == 0 || wk == 0) {
         // P pieces per tile: about 4352 waves in all, at least 8 pieces, of at least 10 steps
         // up to 4 rows (attention, M = 1: 16 pieces of 10 steps 10.2 us, 32 of 5 10.6 us) and
