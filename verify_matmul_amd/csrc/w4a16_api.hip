@@ -693,7 +693,18 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     const long long tiles = (long long)((M + kPrefillTileM - 1) / kPrefillTileM) * ((N + out_cols - 1) / out_cols);
     const long long slots = 2LL * std::max(cus, 1);
-    const int splits = tiles >= slots ? 1 : (int)std::min<long long>({16LL, (long long)(K / group_size), slots / tiles});
+    int splits = tiles >= slots ? 1 : (int)std::min<long long>({16LL, (long long)(K / group_size), slots / tiles});
+    // From one round on, two slices when they cut the rounds the tiles take by a fifth or more,
+    // counted with the workgroups a CU really holds (3 for GPTQ codes with symmetric zero points,
+    // 2 otherwise): FFN down 17408 x 5120 (stored zero points) at M = 2048, 640 tiles, 1.25
+    // rounds of 512: 750-767 us whole, 632 in 2 slices (659 in 3, 651 in 4); FFN up 5120 x 17408
+    // and attention at M = 2048 (symmetric, 3 a CU) stay whole (2 slices: 469 -> 528 us).
+    if (tiles >= slots && K / group_size >= 2) {
+        const long long resident = (w.qzeros == nullptr && bits == 0 ? 3LL : 2LL) * std::max(cus, 1);
+        const long long whole = (tiles + resident - 1) / resident;        // rounds, in whole-K tiles
+        const long long halves = (2 * tiles + resident - 1) / resident;   // rounds of half-K tiles
+        if (5 * halves <= 8 * whole) splits = 2;                          // halves / 2 <= 0.8 whole
+    }
     // scratch: the prepared activations (fp16, [M, K]), one rescale per row, the K slices
     const size_t a16_bytes = round_up((size_t)M * K * sizeof(uint16_t), 256);
     const size_t part_bytes = splits > 1 ? (size_t)splits * M * N * (up ? 2 : 1) * sizeof(float) : 0;
