@@ -324,11 +324,15 @@ int make_decode_plan(int M, int N, int K, int g, bool packed, int slices, int ti
     // us against 21.8-23.4 for the small-row kernel, 8 tiles x 1 piece 23.1-23.4, ring 8 21.6;
     // 5120 x 32768 2 slices 25.5 against 29.6; 8192 x 28672 with 3 slices, one and a third rounds
     // of workgroups, 48.4 against 41.9)
-    const bool mid = !affine && M > 8 && N < kDecodeMinN;
+    // Affine codes from kDecodeMidN to kDecodeMinN columns take the same launch at every row count
+    // (affine FFN 5120 x 17408, groups of 64, us back to back, 6 slices of 4 tiles x 1 piece ->
+    // 3 slices of 4 x 2: 4-bit M = 1 / 8 / 16 18.0 / 20.9 / 22.7 -> 16.7 / 19.4 / 21.1; 8-bit
+    // 21.9 / 25.0 / 26.5 -> 20.5 / 23.0 / 24.9; 2-bit 18.2 / 21.4 / 22.6 -> 17.0 / 20.0 / 21.9).
+    const bool mid = N < kDecodeMinN && (affine ? N >= kDecodeMidN : M > 8);
     // more rows stage more activations per workgroup, which leaves room for fewer workgroups per
     // CU: give each workgroup more waves
-    // (affine codes below kDecodeMinN columns: 4 tiles at every row count, measured on the
-    // 5120 x 17408 projection at 2, 4 and 8 bits, where 8 tiles with more K slices lost 10-30%)
+    // (narrower affine matrices: 4 tiles at every row count; on the 5120 x 17408 projection at
+    // 2, 4 and 8 bits 8 tiles with more K slices lost 10-30%)
     pl->tiles = tiles ? tiles : (pl->mfma && (!affine || N >= kDecodeMinN) && !mid ? 8 : 4);
     pl->kw = kw ? kw : mid ? 2 : 1;
     if (pl->tiles < 1 || pl->kw < 1 || pl->tiles * pl->kw > kDecMaxWaves)
