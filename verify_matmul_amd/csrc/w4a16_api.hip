@@ -231,16 +231,19 @@ int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int t
         // the busiest CU, each with 1/s of the tile's work: take the s (up to two workgroups per
         // CU) that minimises that, the fewest on a tie (each slice more adds to the exchange),
         // and 16 waves per workgroup (8 for up to 8 rows when the pieces would be shorter than 8
-        // steps). Measured on MI355X, back to back, us: attention 5120 x 5120 (80 tiles) M = 1 /
-        // 8 / 16 9.4 / 10.6 / 13.4 -> 8.5 / 9.2 / 10.6 (3 workgroups per tile, 4 before); FFN down
-        // 17408 x 5120 M = 1 / 4 / 8 / 16 16.5 / 18.8 / 21.2 / 25.4 -> 14.7 / 15.3 / 17.5 / 23.1;
+        // steps, and 8 on 128-column tiles, whose registers already hold a CU to 4 waves per SIMD:
+        // affine-4 FFN 5120 x 17408, 136 tiles, M = 9 / 12 / 16 24.0 / 24.7 / 27.2 us with 4 x 8,
+        // 24.9 / 25.8 / 27.1 with 3 x 16, 21.4 / 23.0 / 25.2 with 3 x 8). Measured on MI355X, back
+        // to back, us: attention 5120 x 5120 (80 tiles) M = 1 / 8 / 16 9.4 / 10.6 / 13.4 -> 8.5 /
+        // 9.2 / 10.6 (3 workgroups per tile, 4 before); FFN down 17408 x 5120 M = 1 / 4 / 8 / 16
+        // 16.5 / 18.8 / 21.2 / 25.4 -> 14.7 / 15.3 / 17.5 / 23.1;
         // 5120 x 4096 (64 tiles) M = 1 / 16 8.3 / 9.9 -> 7.6 / 8.8; 5120 x 13824 (216 tiles) M = 1
         // / 16 12.4 / 20.4 -> 11.1 / 18.5 (whole K in a workgroup); 5120 x 8192 (128 tiles) M = 16
         // 13.6 -> 12.4. Matrices of more tiles keep the wave-count rule below.
         int s = 1;
         for (int c = 2; c <= std::min(16, 2 * kCus / tiles); ++c)
             if ((long long)((tiles * c + kCus - 1) / kCus) * s < (long long)((tiles * s + kCus - 1) / kCus) * c) s = c;
-        int w = M > 8 || steps / (s * 16) >= 8 ? 16 : 8;
+        int w = cols == 4 && (M > 8 || steps / (s * 16) >= 8) ? 16 : 8;
         while (w > 1 && s * w > steps) w /= 2;
         s = std::max(1, std::min(s, steps / w));
         if (wk == 0) wk = w;
