@@ -20,6 +20,8 @@
 //     into the B fragments of its 4 column blocks;
 //   * sums are kept per quantisation group and scaled once at the group's end in fp32, so the
 //     exact (q - z) * scale product never rounds before accumulation.
+#include <type_traits>
+
 #include "w4a16_device.h"
 #include "w4a16_launch.h"
 
@@ -86,7 +88,7 @@ w4a16_prefill_kernel(PrefillArgs p)
     __shared__ __align__(16) unsigned char lds[kStages * kStBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS and load bases stay scalar
     const int cl = lane & 15;   // A row / B column of the lane within a 16 x 16 block
     const int rl = lane >> 4;   // word row (8 K rows) of the lane within a 32-row step
     const int wn = wave;   // the wave's 64 columns of the tile
@@ -213,7 +215,9 @@ w4a16_prefill_kernel(PrefillArgs p)
     const int s_off = kAff ? kStA + kStB + wn * 256 + cl * 8 : kStA + kStB + (wn * 64 + cl * 4) * 2;
     const int z_off = kStA + kStB + kStS + (wn * 8 + (cl >> 1)) * 4;
 
-    auto step = [&](int buf) {
+    constexpr bool kZeroStart = prefill_min_waves<kSym, kBits>() == 2;
+    auto step = [&](int buf, auto first_tag) {
+        constexpr bool kFirst = decltype(first_tag)::value;   // the group's first step
         const unsigned char *st = lds + buf * kStBytes;
         if (!kSym && cpos == 0) {   // a new group's zero points (uniform)
             const uint32_t zw = *reinterpret_cast<const uint32_t *>(st + z_off);
@@ -238,12 +242,18 @@ w4a16_prefill_kernel(PrefillArgs p)
             else
                 b[j] = dequant_word(words[j], kSym ? zero_sub_sym() : zs[j], mk);
         }
+        // With registers to spare (the 2-wave instances), a group's first step starts its sums
+        // from zero in the products themselves (a zero C operand), so the group's end needs no
+        // clearing moves; the 3-wave instances would spill for it and clear at the group's end.
+        const float4_t zero4 = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const half8_t a = *reinterpret_cast<const half8_t *>(st + a_off[i]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
-            if constexpr (kAff) acc_one[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, acc_one[i], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], kFirst ? zero4 : acc[i][j], 0, 0, 0);
+            if constexpr (kAff)
+                acc_one[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, kFirst ? zero4 : acc_one[i], 0, 0, 0);
         }
         if (++cpos == spg) {   // the group's end: scale its sums once (uniform)
             cpos = 0;
@@ -274,9 +284,9 @@ w4a16_prefill_kernel(PrefillArgs p)
                         tot[i][j][r] = __builtin_fmaf(acc[i][j][r], sc[j], tot[i][j][r]);
                         if constexpr (kAff) tot[i][j][r] = __builtin_fmaf(acc_one[i][r], bi[j], tot[i][j][r]);
                     }
-                    acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!kZeroStart) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
                 }
-                if constexpr (kAff) acc_one[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (kAff && !kZeroStart) acc_one[i] = float4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
     };
@@ -289,7 +299,10 @@ w4a16_prefill_kernel(PrefillArgs p)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoads));
         __syncthreads();
         issue((t + kStages - 1) % kStages);
-        step(t % kStages);
+        if (kZeroStart && cpos == 0)   // uniform
+            step(t % kStages, std::true_type{});
+        else
+            step(t % kStages, std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last stages' reloads land before the wave ends
 
