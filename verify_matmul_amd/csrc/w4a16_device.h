@@ -159,6 +159,20 @@ __device__ __forceinline__ void load_to_lds4(const void *src, void *lds_base)
     asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_offset(lds_base)) : "memory");
 }
 
+// The same loads from a base address held in scalar registers plus a 32-bit byte offset per lane
+// (the instruction's scalar-base form). A loop that moves the base by the same amount in every
+// lane then keeps that arithmetic off the vector unit. `base` must be equal in all lanes of the
+// wave (it is computed from kernel arguments and wave-uniform values only).
+__device__ __forceinline__ void load_to_lds16_s(const void *base, uint32_t off, void *lds_base)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_offset(lds_base)) : "memory");
+}
+
+__device__ __forceinline__ void load_to_lds4_s(const void *base, uint32_t off, void *lds_base)
+{
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_offset(lds_base)) : "memory");
+}
+
 // SiLU, the gate of a gated feed-forward pair: x * logistic(x) = x / (1 + e^-x). Large
 // negative x give e^-x = inf and a signed zero.
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }

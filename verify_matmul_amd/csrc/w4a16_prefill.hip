@@ -124,12 +124,17 @@ w4a16_prefill_kernel(PrefillArgs p)
     // ---- loads of one stage: every wave issues the same kLoads direct loads -------------------
     constexpr int kLoads = 2 + kWLoads + (!kAff && !kSym ? 1 : 0);
     // activation tile: wave w fills slots [64 w, 64 w + 64), rows 16 w .. 16 w + 15
-    const uint16_t *a_src;
+    // (all operands of a single GPTQ matrix, and the activations of every instance, load from a
+    // wave-uniform base in scalar registers plus a byte offset per lane; the gated pair and affine
+    // codes pick between two arrays per lane, and those loads keep a full address per lane)
+    constexpr bool kSBase = !kDual && !kAff;
+    const uint16_t *const a_base = p.A16 + (size_t)tm * K;   // the tile's first row
+    uint32_t a_off_b;                                         // bytes (< 64 rows x K x 2)
     {
         const int slot = wave * 64 + lane;
         const int row = slot >> 2;
         const int chunk = (slot & 3) ^ ((row >> 2) & 3);
-        a_src = p.A16 + (size_t)min(tm + row, M - 1) * K + chunk * 8;   // rows past M: the last row
+        a_off_b = (uint32_t)(((min(tm + row, M - 1) - tm) * K + chunk * 8) * 2);   // rows past M: the last row
     }
     auto col = [&](int c) { return c < N ? c : 0; };   // columns past N read column 0, never stored
     // Column c of the tile (0..255) is output column tn + c of the single matrix, or for a pair
@@ -147,14 +152,21 @@ w4a16_prefill_kernel(PrefillArgs p)
                                  : (in_up(sc_c) ? p.scales2 : p.scales) + out_col(sc_c);
     const int zc_c = (wave * 8 + (lane & 7)) * 8;
     const uint32_t *z_src = kSym ? nullptr : (in_up(zc_c) ? p.qzeros2 : p.qzeros) + out_col(zc_c) / 8;
+    // their byte offsets from the matrices' starts, for the scalar-base loads
+    const uint32_t w_off_b = (uint32_t)(((size_t)wave * N + out_col(lane * 4)) * 4);
+    const uint32_t s_off_b = (uint32_t)out_col(sc_c) * 2;
+    const uint32_t z_off_b = (uint32_t)(out_col(zc_c) / 8) * 4;
     int lt = s0, lg = gb, lpos = 0;   // next step to stage, its group and position in the group
     auto issue = [&](int buf) {
         unsigned char *st = lds + buf * kStBytes;
-        load_to_lds16(a_src + (size_t)lt * kStepK, st + wave * 64 * 16);
+        load_to_lds16_s(a_base + (size_t)lt * kStepK, a_off_b, st + wave * 64 * 16);
         // word offsets < 2^32 (host)
 #pragma unroll
         for (int j = 0; j < kWLoads; ++j) {
-            if constexpr (kWide)
+            if constexpr (kSBase)
+                load_to_lds16_s(p.qweight + (size_t)((uint32_t)lt * (uint32_t)R + 4u * (uint32_t)j) * (uint32_t)N,
+                                w_off_b, st + kStA + (wave + 4 * j) * 1024);
+            else if constexpr (kWide)
                 load_to_lds16(w_src + ((uint32_t)lt * (uint32_t)R + 4u * (uint32_t)j) * (uint32_t)N,
                               st + kStA + (wave + 4 * j) * 1024);
             else
@@ -163,9 +175,18 @@ w4a16_prefill_kernel(PrefillArgs p)
         }
         if constexpr (kAff)
             load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 256);
-        else if (lane < 32)
-            load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
-        if (!kSym && lane < 8) load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 32);
+        else if (lane < 32) {
+            if constexpr (kSBase)
+                load_to_lds4_s(p.scales + (size_t)lg * N, s_off_b, st + kStA + kStB + wave * 128);
+            else
+                load_to_lds4(s_src + (size_t)lg * N, st + kStA + kStB + wave * 128);
+        }
+        if (!kSym && lane < 8) {
+            if constexpr (kSBase)
+                load_to_lds4_s(p.qzeros + (size_t)lg * (N / 8), z_off_b, st + kStA + kStB + kStS + wave * 32);
+            else
+                load_to_lds4(z_src + (size_t)lg * (N / 8), st + kStA + kStB + kStS + wave * 32);
+        }
         if (lt + 1 < s0 + steps) {   // past the slice's last step the stage reloads it (uniform)
             ++lt;
             if (++lpos == spg) {
