@@ -207,10 +207,11 @@ int noalloc_scratch(hipStream_t stream, size_t control_bytes, size_t exchange_by
 
 // The launch plan of a shape. Measured on MI355X, the weights stream best from many short
 // waves (5-20 K steps each) with a shallow ring, 4-16 thousand waves in all: they keep HBM
-// busy from the first microsecond and the hardware dispatcher balances them. Each 64-column
-// tile is cut into P pieces along K, `waves_k` of them inside one workgroup (summed in LDS) and
-// `splits` workgroups (summed through scratch): 4 waves per workgroup up to 32 pieces, 8 beyond
-// and for more than 8 rows. `splits` / `wk` > 0 override the choice (tuning and tests).
+// busy from the first microsecond. Each column tile is cut into pieces along K, `waves_k` of
+// them inside one workgroup (summed in LDS) and `splits` workgroups (summed through scratch).
+// Matrices of at most one tile per compute unit take the splits that balance the CUs' work
+// (below); wider ones 4 waves per workgroup up to 32 pieces, 8 beyond and for more than 8 rows.
+// `splits` / `wk` > 0 override the choice (tuning and tests).
 int make_plan(int M, int N, int K, int g, ZeroMode zm, int splits, int wk, int tile_cols, bool argmax,
               GemmPlan *plan)
 {

@@ -162,15 +162,25 @@ __device__ __forceinline__ void load_to_lds4(const void *src, void *lds_base)
 // The same loads from a base address held in scalar registers plus a 32-bit byte offset per lane
 // (the instruction's scalar-base form). A loop that moves the base by the same amount in every
 // lane then keeps that arithmetic off the vector unit. `base` must be equal in all lanes of the
-// wave (it is computed from kernel arguments and wave-uniform values only).
+// wave (it is computed from kernel arguments and wave-uniform values only). The optimiser's
+// uniformity analysis is what places such a base in scalar registers; an unoptimised build (the
+// host-sanitizer build compiles the device code at -O0) takes the full-address form instead.
 __device__ __forceinline__ void load_to_lds16_s(const void *base, uint32_t off, void *lds_base)
 {
+#if defined(__OPTIMIZE__)
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_offset(lds_base)) : "memory");
+#else
+    load_to_lds16(static_cast<const unsigned char *>(base) + off, lds_base);
+#endif
 }
 
 __device__ __forceinline__ void load_to_lds4_s(const void *base, uint32_t off, void *lds_base)
 {
+#if defined(__OPTIMIZE__)
     asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_offset(lds_base)) : "memory");
+#else
+    load_to_lds4(static_cast<const unsigned char *>(base) + off, lds_base);
+#endif
 }
 
 // SiLU, the gate of a gated feed-forward pair: x * logistic(x) = x / (1 + e^-x). Large
