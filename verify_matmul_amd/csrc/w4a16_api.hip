@@ -701,14 +701,23 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     const long long tiles = (long long)((M + kPrefillTileM - 1) / kPrefillTileM) * ((N + out_cols - 1) / out_cols);
     const long long slots = 2LL * std::max(cus, 1);
+    // Workgroups a CU holds at once: 3 for GPTQ codes with symmetric zero points, 2 otherwise.
+    const bool three = w.qzeros == nullptr && bits == 0;
+    const long long resident = (three ? 3LL : 2LL) * std::max(cus, 1);
     int splits = tiles >= slots ? 1 : (int)std::min<long long>({16LL, (long long)(K / group_size), slots / tiles});
-    // From one round on, two slices when they cut the rounds the tiles take by a fifth or more,
-    // counted with the workgroups a CU really holds (3 for GPTQ codes with symmetric zero points,
-    // 2 otherwise): FFN down 17408 x 5120 (stored zero points) at M = 2048, 640 tiles, 1.25
-    // rounds of 512: 750-767 us whole, 632 in 2 slices (659 in 3, 651 in 4); FFN up 5120 x 17408
-    // and attention at M = 2048 (symmetric, 3 a CU) stay whole (2 slices: 469 -> 528 us).
-    if (tiles >= slots && K / group_size >= 2) {
-        const long long resident = (w.qzeros == nullptr && bits == 0 ? 3LL : 2LL) * std::max(cus, 1);
+    // The symmetric kernel, which holds 3 workgroups a CU, takes up to that many when the count
+    // above is 1 or 2 (FFN up 5120 x 17408 at M = 256, 272 tiles: 107.5 us whole, 89.4 in 2
+    // slices; attention at M = 1024, 320 tiles: 111 -> 93). More slices than the 2-a-CU count
+    // lost on attention at M = 128 and 256 (12 -> 16 slices 32.4 -> 34.6 us, 6 -> 9 40.2 -> 41.3).
+    if (three && tiles < resident)
+        splits = (int)std::min<long long>({16LL, (long long)(K / group_size), resident / tiles,
+                                           std::max<long long>(2, splits)});
+    // From one round on, the 2-workgroup kernels take two slices when they cut the rounds the tiles
+    // need by a fifth or more: FFN down 17408 x 5120 (stored zero points) at M = 2048, 640 tiles,
+    // 1.25 rounds of 512: 750-767 us whole, 632 in 2 slices (659 in 3, 651 in 4). The symmetric
+    // kernel, whose third workgroup a CU makes the last round cheaper, stays whole (FFN up at M =
+    // 1024, 1088 tiles: 259 us whole, 281 in 2 slices; at M = 2048 469 -> 528).
+    if (!three && tiles >= slots && K / group_size >= 2) {
         const long long whole = (tiles + resident - 1) / resident;        // rounds, in whole-K tiles
         const long long halves = (2 * tiles + resident - 1) / resident;   // rounds of half-K tiles
         if (5 * halves <= 8 * whole) splits = 2;                          // halves / 2 <= 0.8 whole
