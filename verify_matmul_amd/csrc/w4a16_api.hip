@@ -706,12 +706,15 @@ int prefill_call(const void *A, Matrix w, const Matrix *up, int group_size, int 
     const long long resident = (three ? 3LL : 2LL) * std::max(cus, 1);
     int splits = tiles >= slots ? 1 : (int)std::min<long long>({16LL, (long long)(K / group_size), slots / tiles});
     // The symmetric kernel, which holds 3 workgroups a CU, takes up to that many when the count
-    // above is 1 or 2 (FFN up 5120 x 17408 at M = 256, 272 tiles: 107.5 us whole, 89.4 in 2
-    // slices; attention at M = 1024, 320 tiles: 111 -> 93). More slices than the 2-a-CU count
-    // lost on attention at M = 128 and 256 (12 -> 16 slices 32.4 -> 34.6 us, 6 -> 9 40.2 -> 41.3).
+    // above is 1 or 2, or while each slice keeps at least 8 quantisation groups (FFN up 5120 x
+    // 17408 at M = 256, 272 tiles: 107.5 us whole, 89.4 in 2 slices; at M = 128, 136 tiles, 57.0
+    // in 3 slices, 53.3 in 5; attention at M = 1024, 320 tiles: 111 -> 93). Shorter slices past
+    // the 2-a-CU count lost on attention at M = 128 and 256 (12 -> 16 slices 32.4 -> 34.6 us,
+    // 6 -> 9 40.2 -> 41.3).
     if (three && tiles < resident)
         splits = (int)std::min<long long>({16LL, (long long)(K / group_size), resident / tiles,
-                                           std::max<long long>(2, splits)});
+                                           std::max<long long>({2LL, (long long)splits,
+                                                                (long long)(K / group_size) / 8})});
     // From one round on, the 2-workgroup kernels take two slices when they cut the rounds the tiles
     // need by a fifth or more: FFN down 17408 x 5120 (stored zero points) at M = 2048, 640 tiles,
     // 1.25 rounds of 512: 750-767 us whole, 632 in 2 slices (659 in 3, 651 in 4). The symmetric
