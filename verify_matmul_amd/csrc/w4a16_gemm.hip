@@ -776,7 +776,7 @@ namespace {
 template <bool kMfma, int kZM, bool kLdsA, int kWK, int kC, bool kDual>
 hipError_t launch_one(const GemmArgs &a, const GemmPlan &plan, hipStream_t stream)
 {
-    constexpr int kPf = kLdsA ? kRingStaged : kRingConvert;
+    constexpr int kPf = kLdsA ? kRingStaged : ring_unstaged<kZM, kC>();
     constexpr int kOutTile = kDual ? 8 * kC : 16 * kC;
     const auto kern = w4a16_gemm_kernel<kMfma, kZM, kLdsA, kWK, kPf, kC, kDual>;
     if (!kLdsA) {

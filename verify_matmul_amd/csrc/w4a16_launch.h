@@ -43,7 +43,10 @@ constexpr int kRowHeader = 32;
 // Ring depth (steps of packed weights in flight per wave). Shallow rings measure best: with
 // thousands of short waves in flight, HBM is kept busy by the number of waves, and a deep ring
 // only lengthens each wave's start. One step deeper when activations are staged in LDS (a slot
-// is one 16-byte load) than when each slot also carries an activation fragment.
+// is one 16-byte load) than when each slot also carries an activation fragment, except for
+// packed zero points on 64-column tiles: their register floor (5 waves per SIMD) leaves room for a
+// third slot (89 VGPRs), which measured 0.3-0.6 us faster at 11-16 rows on the 17408 x 5120
+// projection; the other unstaged instances would spill or lose a wave per SIMD with it.
 constexpr int kRingStaged = 3;
 constexpr int kRingConvert = 2;
 
@@ -52,6 +55,13 @@ constexpr int kRingConvert = 2;
 //   kZeroSym     w = (q - 8) * s (GPTQ symmetric)
 //   kAffine      w = s * q + b, bf16 scales and biases (MLX affine)
 enum ZeroMode : int { kZeroPacked = 0, kZeroSym = 1, kAffine = 2 };
+
+// Ring depth of a matrix-core instance whose activations come prepared (see kRingConvert).
+template <int kZM, int kC>
+constexpr int ring_unstaged()
+{
+    return kZM == kZeroPacked && kC == 4 ? 3 : kRingConvert;
+}
 
 struct GemmArgs {
     const uint16_t *A;
